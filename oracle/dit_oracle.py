@@ -1,0 +1,334 @@
+"""fp64 CPU oracle for the FLUX-style joint text+image DiT block forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+``bench.py``'s CPU-baseline leg may import this module.  The product path
+(``attention_dit_block_amd``) never imports, calls or falls back to it, and it
+shares no code with that path: the only common code is ``dit_inputs`` (seeded
+draws, no arithmetic of the method).
+
+What it computes is the plain definition of each stage, in float64, reading
+the same storage bits the GPU gets (bf16 widened exactly, or float32) and
+never rounding in between.  numpy's matmul serves as the matrix-product
+primitive; everything else is written out.
+
+Sources (the "CUDA codepath !" thread, antirez/iris.c issue #15):
+  * the cuBLAS/custom-kernel reply lists the operations of the transformer:
+    QKV projections, FFN, attention scores (matrix products) and RMSNorm,
+    RoPE, AdaLN modulation, softmax and activations;
+  * the GGML update, item 3, fixes RoPE: 4 axes of [32, 32, 32, 32] dims,
+    separate text/image positions, pairs formed by repeat-interleave;
+  * the GGML update's bottom line names the block: AdaLN + custom RoPE +
+    joint attention.
+The remaining details are the FLUX double-/single-stream block convention
+(the readings are listed in the design notes and in each function below):
+SiLU before the modulation linear, chunk order shift/scale/gate, modulation
+(1 + scale) * RMSNorm(x) + shift, no biases, per-head RMSNorm of q and k with
+a per-stream weight, RoPE frequency theta^(-2j/dim_axis) with theta = 1e4 and
+rotation by +angle on interleaved pairs, softmax scale 1/sqrt(head_dim), no
+mask, text tokens first, SwiGLU with the gate half first.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
+(closed forms, invariants, library special cases, brute force) except the
+composition of the whole block, which is pinned only through its stages and
+block-level special cases (identity modulation, constant scores, zero FFN).
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+F64 = np.float64
+
+
+# --- storage -----------------------------------------------------------------
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage (bf16 bit pattern as uint16, or float32) -> exact float64."""
+    if dtype == "bf16":
+        u = np.ascontiguousarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return u.view(np.float32).astype(F64)
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(F64)
+    if dtype == "f64":
+        return np.asarray(a, dtype=F64)
+    raise ValueError(dtype)
+
+
+def store(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Value of x after being stored in ``dtype`` (round-to-nearest-even), as
+    float64.  'f64' keeps x exact.  bf16 keeps 8 significant bits and the
+    float32 exponent range; the rounding is taken directly from the float64
+    value (no double rounding).  Inputs are finite and far from the float32
+    overflow / underflow limits."""
+    x = np.asarray(x, dtype=F64)
+    if dtype == "f64":
+        return x
+    if dtype == "f32":
+        return x.astype(np.float32).astype(F64)
+    if dtype == "bf16":
+        u = np.ascontiguousarray(x).view(np.uint64)
+        drop = np.uint64(45)                       # 52 - 7 mantissa bits dropped
+        lsb = (u >> drop) & np.uint64(1)
+        r = ((u + (np.uint64(1) << np.uint64(44)) - np.uint64(1) + lsb) >> drop) << drop
+        return r.view(F64)
+    raise ValueError(dtype)
+
+
+# --- elementwise ---------------------------------------------------------------
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z)) (the thread's 'activations')."""
+    z = np.asarray(z, dtype=F64)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """SwiGLU gating f = SiLU(g) * u, g being the first half of the FFN-in output."""
+    return silu(g) * u
+
+
+# --- AdaLN ------------------------------------------------------------------------
+
+def adaln_modulation(w_mod: np.ndarray, cond: np.ndarray) -> np.ndarray:
+    """m = W_mod . SiLU(c).  W_mod is [n_chunks*d, d_cond] ([out, in]); the result
+    is read as n_chunks vectors of d in the order shift, scale, gate (repeated)."""
+    return np.asarray(w_mod, F64) @ silu(cond)
+
+
+def rms_norm(x: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) over the last axis; no learnable weight."""
+    x = np.asarray(x, F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps)
+
+
+def modulate(x: np.ndarray, shift: np.ndarray, scale: np.ndarray, eps: float) -> np.ndarray:
+    """AdaLN modulation of a pre-norm: (1 + scale) * RMSNorm(x) + shift.
+    shift = scale = 0 gives the plain RMSNorm (identity modulation)."""
+    return (1.0 + np.asarray(scale, F64)) * rms_norm(x, eps) + np.asarray(shift, F64)
+
+
+def adaln_modulate(cond, w_mod, n_chunks: int, d: int, x=None, shift_chunk: int = 0,
+                   scale_chunk: int = 1, eps: float = 1e-6):
+    """Counterpart of the library's standalone AdaLN call: returns the modulation
+    vectors m [n_chunks, d] and, if x is given, (1+scale)*RMSNorm(x)+shift."""
+    m = adaln_modulation(w_mod, cond).reshape(n_chunks, d)
+    if x is None:
+        return m, None
+    return m, modulate(x, m[shift_chunk], m[scale_chunk], eps)
+
+
+# --- RoPE ---------------------------------------------------------------------------
+
+def rope_frequencies(axis_dim: int, theta: float) -> np.ndarray:
+    """omega_j = theta^(-2j/axis_dim), j = 0 .. axis_dim/2 - 1."""
+    j = np.arange(axis_dim // 2, dtype=F64)
+    return np.power(F64(theta), -2.0 * j / axis_dim)
+
+
+def rope_angles(pos: np.ndarray, axes_dim: Sequence[int], theta: float) -> np.ndarray:
+    """phi[n, p] for every pair p of the head (pairs of all axes, in axis order):
+    phi = pos[n, a] * omega_j for the pair j of axis a."""
+    pos = np.asarray(pos, dtype=F64)
+    cols = []
+    for a, dim in enumerate(axes_dim):
+        cols.append(pos[:, a:a + 1] * rope_frequencies(dim, theta)[None, :])
+    return np.concatenate(cols, axis=1)
+
+
+def rope_rotate(x: np.ndarray, pos: np.ndarray, axes_dim: Sequence[int], theta: float) -> np.ndarray:
+    """Rotate every interleaved pair (x[2p], x[2p+1]) of the last axis by +phi[n, p]:
+    (u, v) -> (u cos - v sin, u sin + v cos).  x is [n, ..., head_dim] with the
+    token on axis 0; axis a of the position owns dims [sum(axes_dim[:a]), +axes_dim[a])."""
+    x = np.asarray(x, F64)
+    phi = rope_angles(pos, axes_dim, theta)               # [n, head_dim/2]
+    shape = (x.shape[0],) + (1,) * (x.ndim - 2) + (phi.shape[1],)
+    c = np.cos(phi).reshape(shape)
+    s = np.sin(phi).reshape(shape)
+    u = x[..., 0::2]
+    v = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = u * c - v * s
+    out[..., 1::2] = u * s + v * c
+    return out
+
+
+def qk_rmsnorm_rope(q, k, n_heads: int, head_dim: int, qk_w, n_first: int, eps: float,
+                    pos, axes_dim: Sequence[int], theta: float):
+    """Per token and head: q <- RoPE(RMSNorm(q_head) * w_q), k likewise with w_k.
+    q, k are [n, n_heads*head_dim]; qk_w is [2 sets, 2 (q, k), head_dim]: rows
+    n < n_first use set 0 (text), the others set 1 (image)."""
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    n = q.shape[0]
+    w = np.asarray(qk_w, F64).reshape(-1, 2, head_dim)
+    set_of_row = np.where(np.arange(n) < n_first, 0, min(1, w.shape[0] - 1))
+    outs = []
+    for which, t in ((0, q), (1, k)):
+        th = t.reshape(n, n_heads, head_dim)
+        wrow = w[set_of_row, which, :][:, None, :]         # [n, 1, head_dim]
+        normed = rms_norm(th, eps) * wrow
+        outs.append(rope_rotate(normed, pos, axes_dim, theta).reshape(n, n_heads * head_dim))
+    return outs[0], outs[1]
+
+
+# --- attention ----------------------------------------------------------------------
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Exact softmax over the last axis (max-subtracted)."""
+    s = np.asarray(s, F64)
+    e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def joint_attention(q, k, v, n_heads: int, head_dim: int, scale: Optional[float] = None,
+                    q_rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """For every head h: O_h = softmax(Q_h K_h^T * scale) V_h over ALL tokens
+    (text and image in one softmax, no mask).  q, k, v are [n, n_heads*head_dim]
+    with head h in columns h*head_dim .. h*head_dim + head_dim - 1.
+    ``q_rows`` restricts the query rows (the keys and values are always all)."""
+    if scale is None:
+        scale = 1.0 / np.sqrt(F64(head_dim))
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    if q_rows is not None:
+        q = q[q_rows]
+    out = np.empty((q.shape[0], n_heads * head_dim), dtype=F64)
+    for h in range(n_heads):
+        c = slice(h * head_dim, (h + 1) * head_dim)
+        p = softmax_rows((q[:, c] @ k[:, c].T) * scale)
+        out[:, c] = p @ v[:, c]
+    return out
+
+
+# --- blocks ---------------------------------------------------------------------------
+
+def _w(ws: Dict[str, np.ndarray], name: str, dtype: str) -> np.ndarray:
+    return widen(ws[name], dtype)
+
+
+def storage_plan(cfg, exact: bool = False) -> Dict[str, str]:
+    """Storage type of each tensor a stage hands to the next.
+
+    The bf16 workloads are bf16 weights and activations with float32
+    accumulation; the float32 workload is float32 throughout.  So every
+    activation handed from one step to the next (the modulated pre-norm a and
+    b, qkv, q/k after QK-norm + RoPE, the attention output O, the SwiGLU
+    output f) is stored in the workload's type, the AdaLN vectors in float32,
+    and the residual stream (the mid-block h and the block output y) in
+    float32.  Arithmetic itself is exact float64.  ``exact=True`` stores
+    nothing (every tensor exact) to measure drift from exact arithmetic."""
+    if exact:
+        return {k: "f64" for k in ("act", "mod", "res")}
+    act = "bf16" if cfg.dtype == "bf16" else "f32"
+    return {"act": act, "mod": "f32", "res": "f32"}
+
+
+def double_block(cfg, inputs: Dict[str, object], rows_txt=None, rows_img=None,
+                 mods=None, keep: bool = False, exact: bool = False) -> Dict[str, np.ndarray]:
+    """Double-stream block (text and image keep their own weights, attention is joint).
+
+    1. m_s = W_mod,s . SiLU(c) -> shift1, scale1, gate1, shift2, scale2, gate2
+    2. a_s = (1 + scale1) * RMSNorm(x_s) + shift1
+    3. [q | k | v]_s = a_s W_qkv,s^T
+    4. q, k <- RMSNorm per head * w_{q,k},s ; RoPE at the token's position
+    5. O = joint attention over [text; image]
+    6. h_s = x_s + gate1 * (O_s W_o,s^T)
+    7. b_s = (1 + scale2) * RMSNorm(h_s) + shift2 ; [g | u] = b_s W_in,s^T
+    8. y_s = h_s + gate2 * ((SiLU(g) * u) W_down,s^T)
+
+    Each step's output is stored per ``storage_plan``.  The inputs x_s are read
+    in their own storage type (``x_dtype``: the workload type for a first
+    block, float32 for a block fed by another block's output).
+    ``rows_txt`` / ``rows_img`` select output rows (index arrays within each
+    stream); all tokens still enter the keys and values.  ``mods`` replaces
+    the AdaLN vectors by given [6, d] arrays (special-case pins).  ``keep``
+    returns the intermediates too."""
+    t = cfg.dtype
+    st = storage_plan(cfg, exact)
+    d, H, D, F = cfg.d, cfg.n_heads, cfg.head_dim, cfg.ffn_inner
+    nt, ni = cfg.n_txt, cfg.n_img
+    xdt = inputs.get("x_dtype", t)
+    cond = widen(inputs["cond"], t)
+    xs = {"txt": widen(inputs["x_txt"], xdt), "img": widen(inputs["x_img"], xdt)}
+    pos = np.asarray(inputs["pos"])
+    ws = {"txt": inputs["txt"], "img": inputs["img"]}
+    m = {}
+    for s in ("txt", "img"):
+        if mods is not None:
+            m[s] = np.asarray(mods[s], F64).reshape(6, d)
+        else:
+            m[s] = store(adaln_modulation(_w(ws[s], "w_mod", t), cond), st["mod"]).reshape(6, d)
+    qkv = {}
+    for s in ("txt", "img"):
+        a = store(modulate(xs[s], m[s][0], m[s][1], cfg.eps), st["act"])
+        qkv[s] = store(a @ _w(ws[s], "w_qkv", t).T, st["act"])
+    q = np.concatenate([qkv["txt"][:, :d], qkv["img"][:, :d]], axis=0)
+    k = np.concatenate([qkv["txt"][:, d:2 * d], qkv["img"][:, d:2 * d]], axis=0)
+    v = np.concatenate([qkv["txt"][:, 2 * d:], qkv["img"][:, 2 * d:]], axis=0)
+    qk_w = np.stack([widen(ws["txt"]["qk_norm_w"], t).reshape(2, D),
+                     widen(ws["img"]["qk_norm_w"], t).reshape(2, D)])
+    q, k = qk_rmsnorm_rope(q, k, H, D, qk_w, nt, cfg.eps_qk, pos, cfg.axes_dim, cfg.theta)
+    q, k = store(q, st["act"]), store(k, st["act"])
+    rows = {"txt": np.arange(nt) if rows_txt is None else np.asarray(rows_txt),
+            "img": np.arange(ni) if rows_img is None else np.asarray(rows_img)}
+    q_rows = np.concatenate([rows["txt"], nt + rows["img"]])
+    o = store(joint_attention(q, k, v, H, D, q_rows=q_rows), st["act"])
+    o_s = {"txt": o[:len(rows["txt"])], "img": o[len(rows["txt"]):]}
+    out: Dict[str, np.ndarray] = {}
+    for s in ("txt", "img"):
+        x_r = xs[s][rows[s]]
+        h = store(x_r + m[s][2] * (o_s[s] @ _w(ws[s], "w_o", t).T), st["res"])
+        b = store(modulate(h, m[s][3], m[s][4], cfg.eps), st["act"])
+        gu = b @ _w(ws[s], "w_ffn_in", t).T
+        f = store(swiglu(gu[:, :F], gu[:, F:]), st["act"])
+        y = store(h + m[s][5] * (f @ _w(ws[s], "w_ffn_out", t).T), st["res"])
+        out["y_" + s] = y
+        if keep:
+            out.update({"mod_" + s: m[s], "h_" + s: h, "f_" + s: f, "o_" + s: o_s[s]})
+    if keep:
+        out.update({"q": q, "k": k, "v": v, "qkv_txt": qkv["txt"], "qkv_img": qkv["img"]})
+    return out
+
+
+def single_block(cfg, inputs: Dict[str, object], rows=None, mods=None,
+                 keep: bool = False, exact: bool = False) -> Dict[str, np.ndarray]:
+    """Single-stream block over the concatenated sequence x = [text; image]:
+
+    m = W_mod . SiLU(c) -> shift, scale, gate
+    a = (1 + scale) * RMSNorm(x) + shift
+    [q | k | v | g | u] = a W_1^T
+    q, k <- RMSNorm per head * w ; RoPE ; O = joint attention
+    y = x + gate * ([O | SiLU(g) * u] W_2^T)
+
+    Storage as in ``double_block``; x is read in ``x_dtype``."""
+    t = cfg.dtype
+    st = storage_plan(cfg, exact)
+    d, H, D, F = cfg.d, cfg.n_heads, cfg.head_dim, cfg.ffn_inner
+    n = cfg.n_tok
+    cond = widen(inputs["cond"], t)
+    x = widen(inputs["x"], inputs.get("x_dtype", t))
+    pos = np.asarray(inputs["pos"])
+    ws = inputs["w"]
+    if mods is not None:
+        m = np.asarray(mods, F64).reshape(3, d)
+    else:
+        m = store(adaln_modulation(_w(ws, "w_mod", t), cond), st["mod"]).reshape(3, d)
+    a = store(modulate(x, m[0], m[1], cfg.eps), st["act"])
+    w1 = _w(ws, "w_1", t)
+    qkv = store(a @ w1[:3 * d].T, st["act"])
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    qk_w = widen(ws["qk_norm_w"], t).reshape(1, 2, D)
+    q, k = qk_rmsnorm_rope(q, k, H, D, qk_w, n, cfg.eps_qk, pos, cfg.axes_dim, cfg.theta)
+    q, k = store(q, st["act"]), store(k, st["act"])
+    r = np.arange(n) if rows is None else np.asarray(rows)
+    o = store(joint_attention(q, k, v, H, D, q_rows=r), st["act"])
+    gu = a[r] @ w1[3 * d:].T
+    f = store(swiglu(gu[:, :F], gu[:, F:]), st["act"])
+    y = store(x[r] + m[2] * (np.concatenate([o, f], axis=1) @ _w(ws, "w_2", t).T), st["res"])
+    out = {"y": y}
+    if keep:
+        out.update({"mod": m, "q": q, "k": k, "v": v, "o": o, "f": f, "a": a})
+    return out
