@@ -1,0 +1,327 @@
+"""MI355X (gfx950) forward pass of a FLUX-style joint text+image DiT block.
+
+Thin ctypes binding over the C-ABI library ``libdit.so`` (``include/dit.h``):
+argument marshalling only -- every step of the computation runs in the HIP
+kernels of the library.  torch tensors provide device memory and the stream.
+There is no CPU fallback: importing this package fails if the library is not
+built (``python attention_dit_block_amd/build.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+
+__all__ = [
+    "DIT_F32", "DIT_BF16", "DIT_OK", "DitError", "lib", "library_path",
+    "BlockConfig", "StreamWeights", "SingleWeights",
+    "adaln_modulate", "qk_rmsnorm_rope", "joint_attention",
+    "block_workspace_size", "block_forward", "single_block_forward",
+    "last_error", "launch_count", "abi_version",
+    "timing_begin", "timing_end", "timing_read",
+]
+
+DIT_F32, DIT_BF16 = 0, 1
+DIT_OK, DIT_ERR_INVALID_ARG, DIT_ERR_UNSUPPORTED, DIT_ERR_WORKSPACE, DIT_ERR_HIP = 0, 1, 2, 3, 4
+STATUS_NAMES = {0: "DIT_OK", 1: "DIT_ERR_INVALID_ARG", 2: "DIT_ERR_UNSUPPORTED",
+                3: "DIT_ERR_WORKSPACE", 4: "DIT_ERR_HIP"}
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdit.so")
+if not os.path.exists(library_path):
+    raise ImportError(f"{library_path} is not built: run `python attention_dit_block_amd/build.py`")
+lib = ctypes.CDLL(library_path)
+
+_vp, _i, _l, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_float, ctypes.c_size_t
+
+
+class BlockConfig(ctypes.Structure):
+    _fields_ = [("dtype", _i), ("x_dtype", _i), ("y_dtype", _i), ("d", _i), ("n_heads", _i),
+                ("head_dim", _i), ("ffn_inner", _i), ("d_cond", _i), ("n_txt", _i), ("n_img", _i),
+                ("eps", _f), ("eps_qk", _f), ("theta", _f), ("n_axes", _i), ("axes_dim", _i * 4)]
+
+
+class StreamWeights(ctypes.Structure):
+    _fields_ = [("w_mod", _vp), ("w_qkv", _vp), ("qk_norm_w", _vp), ("w_o", _vp),
+                ("w_ffn_in", _vp), ("w_ffn_out", _vp)]
+
+
+class SingleWeights(ctypes.Structure):
+    _fields_ = [("w_mod", _vp), ("w_1", _vp), ("qk_norm_w", _vp), ("w_2", _vp)]
+
+
+def _sig(name, res, args):
+    f = getattr(lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_adaln = _sig("dit_adaln_modulate", _i, [_i, _vp, _vp, _i, _vp, _i, _i, _vp, _vp, _i, _i, _l, _i, _i, _f, _vp, _l])
+_qkrope = _sig("dit_qk_rmsnorm_rope", _i, [_i, _vp, _vp, _l, _vp, _l, _i, _i, _i, _vp, _i, _f, _vp, _i,
+                                           ctypes.POINTER(_i), _f])
+_attn = _sig("dit_joint_attention", _i, [_i, _vp, _vp, _l, _vp, _l, _vp, _l, _vp, _l, _i, _i, _i, _f])
+_wsize = _sig("dit_block_workspace_size", _sz, [ctypes.POINTER(BlockConfig), _i])
+_block = _sig("dit_block_forward", _i, [ctypes.POINTER(BlockConfig), ctypes.POINTER(StreamWeights),
+                                        ctypes.POINTER(StreamWeights), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+_single = _sig("dit_single_block_forward", _i, [ctypes.POINTER(BlockConfig), ctypes.POINTER(SingleWeights),
+                                                _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+_last_error = _sig("dit_last_error", ctypes.c_char_p, [])
+_launch_count = _sig("dit_launch_count", ctypes.c_uint64, [])
+_abi = _sig("dit_abi_version", _i, [])
+_tbegin = _sig("dit_timing_begin", _i, [_i])
+_tend = _sig("dit_timing_end", _i, [])
+_tread = _sig("dit_timing_read", _i, [_i, ctypes.c_char_p, _i, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_double)])
+
+EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", "dit_block_workspace_size",
+            "dit_block_forward", "dit_single_block_forward", "dit_last_error", "dit_launch_count",
+            "dit_abi_version", "dit_timing_begin", "dit_timing_end", "dit_timing_read"]
+
+
+class DitError(RuntimeError):
+    def __init__(self, code: int, fn: str):
+        self.code = code
+        self.status = STATUS_NAMES.get(code, str(code))
+        super().__init__(f"{fn}: {self.status}: {last_error()}")
+
+
+def last_error() -> str:
+    return _last_error().decode()
+
+
+def launch_count() -> int:
+    return int(_launch_count())
+
+
+def abi_version() -> int:
+    return int(_abi())
+
+
+def _check(rc: int, fn: str) -> None:
+    if rc != DIT_OK:
+        raise DitError(rc, fn)
+
+
+# --- marshalling helpers -------------------------------------------------------------------
+
+def _ptr(t, what: str, dtype=None) -> Optional[int]:
+    """Device pointer of a torch tensor (None -> NULL).  Host tensors are refused, so a host
+    address can never reach a kernel."""
+    if t is None:
+        return None
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{what} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _need(t, n: int, what: str, contiguous: bool = True) -> None:
+    """Refuse a tensor smaller than the call reads or writes (the C ABI sees only pointers)."""
+    if t is None:
+        return
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() < n:
+        raise ValueError(f"{what} has {t.numel()} elements, the call needs {n}")
+
+
+def _rows(t, rows: int, width: int, what: str) -> None:
+    """A strided 2-D view must cover rows x width with its own row stride."""
+    if rows == 0:
+        return
+    if t.dim() != 2 or t.shape[0] < rows or t.shape[1] < width or t.stride(1) != 1:
+        raise ValueError(f"{what} must be a [>= {rows}, >= {width}] view with unit column stride")
+
+
+def _ld(t, what: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{what} must be a 2-D view with unit column stride")
+    return t.stride(0)
+
+
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DIT_BF16
+    if t.dtype == torch.float32:
+        return DIT_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# --- entry points ------------------------------------------------------------------------------
+
+def adaln_modulate(cond, w_mod, n_chunks: int, d: int, mod_out, x=None, x_out=None, shift_chunk: int = 0,
+                   scale_chunk: int = 1, eps: float = 1e-6, stream=None) -> None:
+    """mod_out = W_mod SiLU(cond) (fp32); optionally x_out = (1+scale) RMSNorm(x) + shift."""
+    import torch
+    dtype = _dt(w_mod)
+    n_tok, ld_x, ld_o, xdt = 0, 0, 0, dtype
+    _need(w_mod, n_chunks * d * cond.numel(), "w_mod")
+    _need(cond, cond.numel(), "cond")
+    _need(mod_out, n_chunks * d, "mod_out")
+    if x is not None:
+        if x_out is None:
+            raise ValueError("x_out is required with x")
+        n_tok, ld_x, ld_o, xdt = x.shape[0], _ld(x, "x"), _ld(x_out, "x_out"), _dt(x)
+        _rows(x, n_tok, d, "x")
+        _rows(x_out, n_tok, d, "x_out")
+    rc = _adaln(dtype, _stream(stream), _ptr(cond, "cond"), cond.numel(), _ptr(w_mod, "w_mod"), n_chunks, d,
+                _ptr(mod_out, "mod_out", torch.float32), _ptr(x, "x"), xdt, n_tok, ld_x, shift_chunk, scale_chunk,
+                eps, _ptr(x_out, "x_out"), ld_o)
+    _check(rc, "dit_adaln_modulate")
+
+
+def qk_rmsnorm_rope(q, k, n_heads: int, qk_w, n_first: int, pos, eps: float = 1e-6,
+                    axes_dim: Sequence[int] = (32, 32, 32, 32), theta: float = 1e4, head_dim: int = 128,
+                    stream=None) -> None:
+    """In place on the q and k views: per-head RMSNorm * weight, then 4-axis RoPE."""
+    import torch
+    axes = (_i * len(axes_dim))(*axes_dim)
+    n = q.shape[0]
+    _rows(q, n, n_heads * head_dim, "q")
+    _rows(k, n, n_heads * head_dim, "k")
+    _need(qk_w, (2 if n_first < n else 1) * 2 * head_dim, "qk_w")
+    _need(pos, n * len(axes_dim), "pos")
+    rc = _qkrope(_dt(q), _stream(stream), _ptr(q, "q"), _ld(q, "q"), _ptr(k, "k"), _ld(k, "k"), q.shape[0],
+                 n_heads, head_dim, _ptr(qk_w, "qk_w"), n_first, eps, _ptr(pos, "pos", torch.int32),
+                 len(axes_dim), axes, theta)
+    _check(rc, "dit_qk_rmsnorm_rope")
+
+
+def joint_attention(q, k, v, o, n_heads: int, softmax_scale: Optional[float] = None, head_dim: int = 128,
+                    stream=None) -> None:
+    """o = softmax(q k^T * scale) v per head, over all rows (joint text+image attention)."""
+    if softmax_scale is None:
+        softmax_scale = head_dim ** -0.5
+    n = q.shape[0]
+    for t, what in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _rows(t, n, n_heads * head_dim, what)
+    rc = _attn(_dt(q), _stream(stream), _ptr(q, "q"), _ld(q, "q"), _ptr(k, "k"), _ld(k, "k"), _ptr(v, "v"),
+               _ld(v, "v"), _ptr(o, "o"), _ld(o, "o"), q.shape[0], n_heads, head_dim, softmax_scale)
+    _check(rc, "dit_joint_attention")
+
+
+@dataclass
+class Shape:
+    """Python-side block shape (mirrors dit_block_config)."""
+    dtype: int
+    d: int
+    n_heads: int
+    ffn_inner: int
+    n_txt: int
+    n_img: int
+    d_cond: int = 0
+    x_dtype: Optional[int] = None
+    y_dtype: int = DIT_F32
+    head_dim: int = 128
+    eps: float = 1e-6
+    eps_qk: float = 1e-6
+    theta: float = 1e4
+    axes_dim: Sequence[int] = (32, 32, 32, 32)
+
+    def c_config(self) -> BlockConfig:
+        c = BlockConfig()
+        c.dtype = self.dtype
+        c.x_dtype = self.dtype if self.x_dtype is None else self.x_dtype
+        c.y_dtype = self.y_dtype
+        c.d, c.n_heads, c.head_dim, c.ffn_inner = self.d, self.n_heads, self.head_dim, self.ffn_inner
+        c.d_cond = self.d_cond or self.d
+        c.n_txt, c.n_img = self.n_txt, self.n_img
+        c.eps, c.eps_qk, c.theta = self.eps, self.eps_qk, self.theta
+        c.n_axes = len(self.axes_dim)
+        for i, a in enumerate(self.axes_dim):
+            c.axes_dim[i] = a
+        return c
+
+
+def block_workspace_size(shape: Shape, single_stream: bool = False) -> int:
+    c = shape.c_config()
+    n = _wsize(ctypes.byref(c), 1 if single_stream else 0)
+    if n == 0:
+        raise DitError(DIT_ERR_INVALID_ARG, "dit_block_workspace_size")
+    return int(n)
+
+
+def _stream_weights(shape: "Shape", w: dict, what: str) -> StreamWeights:
+    d, F, dc, hd = shape.d, shape.ffn_inner, shape.d_cond or shape.d, shape.head_dim
+    sizes = {"w_mod": 6 * d * dc, "w_qkv": 3 * d * d, "qk_norm_w": 2 * hd, "w_o": d * d,
+             "w_ffn_in": 2 * F * d, "w_ffn_out": d * F}
+    s = StreamWeights()
+    for name, n in sizes.items():
+        _need(w[name], n, f"{what}.{name}")
+        setattr(s, name, _ptr(w[name], f"{what}.{name}"))
+    return s
+
+
+def _check_block_io(shape: "Shape", cond, pos, pairs) -> None:
+    _need(cond, shape.d_cond or shape.d, "cond")
+    _need(pos, (shape.n_txt + shape.n_img) * len(shape.axes_dim), "pos")
+    for t, n, what in pairs:
+        if n:
+            _need(t, n * shape.d, what)
+
+
+def block_forward(shape: Shape, txt: dict, img: dict, cond, pos, x_txt, x_img, y_txt, y_img, workspace,
+                  stream=None) -> None:
+    """Double-stream block: y_txt, y_img from x_txt, x_img (see include/dit.h)."""
+    import torch
+    c = shape.c_config()
+    wt, wi = _stream_weights(shape, txt, "txt"), _stream_weights(shape, img, "img")
+    _check_block_io(shape, cond, pos, ((x_txt, shape.n_txt, "x_txt"), (x_img, shape.n_img, "x_img"),
+                                       (y_txt, shape.n_txt, "y_txt"), (y_img, shape.n_img, "y_img")))
+    rc = _block(ctypes.byref(c), ctypes.byref(wt), ctypes.byref(wi), _ptr(cond, "cond"),
+                _ptr(pos, "pos", torch.int32), _ptr(x_txt, "x_txt"), _ptr(x_img, "x_img"), _ptr(y_txt, "y_txt"),
+                _ptr(y_img, "y_img"), _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                _stream(stream))
+    _check(rc, "dit_block_forward")
+
+
+def single_block_forward(shape: Shape, w: dict, cond, pos, x, y, workspace, stream=None) -> None:
+    """Single-stream block over x = [text; image] (see include/dit.h)."""
+    import torch
+    c = shape.c_config()
+    d, F, dc, hd = shape.d, shape.ffn_inner, shape.d_cond or shape.d, shape.head_dim
+    n = shape.n_txt + shape.n_img
+    sw = SingleWeights()
+    for name, size in (("w_mod", 3 * d * dc), ("w_1", (3 * d + 2 * F) * d), ("qk_norm_w", 2 * hd),
+                       ("w_2", d * (d + F))):
+        _need(w[name], size, name)
+        setattr(sw, name, _ptr(w[name], name))
+    _check_block_io(shape, cond, pos, ((x, n, "x"), (y, n, "y")))
+    rc = _single(ctypes.byref(c), ctypes.byref(sw), _ptr(cond, "cond"), _ptr(pos, "pos", torch.int32),
+                 _ptr(x, "x"), _ptr(y, "y"), _ptr(workspace, "workspace"),
+                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "dit_single_block_forward")
+
+
+# --- kernel timing -----------------------------------------------------------------------------
+
+def timing_begin(capacity: int) -> None:
+    _check(_tbegin(capacity), "dit_timing_begin")
+
+
+def timing_end() -> None:
+    _tend()
+
+
+def timing_read() -> dict:
+    """{kernel launch-site name: (launches, total_ms)} for the launches recorded on this thread."""
+    out = {}
+    n = _tread(-1, None, 0, None, None)
+    if n < 0:
+        raise DitError(DIT_ERR_HIP, "dit_timing_read")
+    for i in range(n):
+        buf = ctypes.create_string_buffer(128)
+        cnt = _i()
+        ms = ctypes.c_double()
+        _tread(i, buf, 128, ctypes.byref(cnt), ctypes.byref(ms))
+        out[buf.value.decode()] = (cnt.value, ms.value)
+    return out

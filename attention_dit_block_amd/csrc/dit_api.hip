@@ -1,0 +1,561 @@
+// C ABI of the DiT block library (declared in include/dit.h): argument validation on the host,
+// workspace planning and the launch sequence of each entry point.  Validation happens before
+// any HIP call, so an invalid call launches nothing and needs no GPU.  The pattern of a flat C
+// ABI that carries device pointers and shapes and re-validates them at the boundary follows the
+// fak GPU backend page ("GPU -- the in-kernel forward pass, on the GPU", section 2).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dit.h"
+#include "launch.h"
+
+using namespace dit;
+
+namespace {
+
+// ---- thread-local state -----------------------------------------------------------------
+struct TimingState {
+    bool on = false;
+    int capacity = 0, used = 0;
+    std::vector<hipEvent_t> ev;         // 2 per slot
+    std::vector<const char*> name;
+};
+thread_local char tl_err[512] = "";
+thread_local uint64_t tl_launches = 0;
+thread_local TimingState tl_timing;
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(tl_err, sizeof(tl_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+void clear_err() { tl_err[0] = 0; }
+
+template <typename F>
+int launch(const char* name, hipStream_t s, F&& fn) {
+    TimingState& T = tl_timing;
+    const bool timed = T.on && T.used < T.capacity;
+    if (timed && hipEventRecord(T.ev[2 * T.used], s) != hipSuccess)
+        return fail(DIT_ERR_HIP, "hipEventRecord failed before %s", name);
+    const hipError_t e = fn();
+    if (e != hipSuccess) return fail(DIT_ERR_HIP, "launch of %s failed: %s", name, hipGetErrorString(e));
+    if (timed) {
+        if (hipEventRecord(T.ev[2 * T.used + 1], s) != hipSuccess)
+            return fail(DIT_ERR_HIP, "hipEventRecord failed after %s", name);
+        T.name[T.used++] = name;
+    }
+    ++tl_launches;
+    return DIT_OK;
+}
+#define DIT_TRY(x)                     \
+    do {                               \
+        const int _rc = (x);           \
+        if (_rc != DIT_OK) return _rc; \
+    } while (0)
+
+// ---- validation helpers ------------------------------------------------------------------------
+size_t esize(int dt) { return dt == DIT_BF16 ? 2 : 4; }
+bool valid_dtype(int dt) { return dt == DIT_BF16 || dt == DIT_F32; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_ptr(const void* p, const char* what) {
+    if (!p) return fail(DIT_ERR_INVALID_ARG, "%s is NULL", what);
+    if (!aligned16(p)) return fail(DIT_ERR_INVALID_ARG, "%s is not 16-byte aligned", what);
+    return DIT_OK;
+}
+int check_ld(long ld, long width, int dt, const char* what) {
+    if (ld < width) return fail(DIT_ERR_INVALID_ARG, "%s = %ld is smaller than the row width %ld", what, ld, width);
+    if ((ld * (long)esize(dt)) % 16 != 0)
+        return fail(DIT_ERR_INVALID_ARG, "%s = %ld: row stride is not a multiple of 16 bytes", what, ld);
+    return DIT_OK;
+}
+// Byte range [lo, hi) of a strided matrix.
+struct Range { uintptr_t lo, hi; };
+Range range_of(const void* p, long rows, long ld, long width, int dt) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    if (rows <= 0) return {lo, lo};
+    return {lo, lo + (uintptr_t)(((rows - 1) * ld + width) * (long)esize(dt))};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+int build_rope_table(int head_dim, int n_axes, const int* axes_dim, float theta, RopeTable& t) {
+    if (!axes_dim) return fail(DIT_ERR_INVALID_ARG, "axes_dim is NULL");
+    if (n_axes < 1 || n_axes > 4) return fail(DIT_ERR_UNSUPPORTED, "n_axes = %d (1..4 supported)", n_axes);
+    if (!(theta > 0.0f) || !std::isfinite(theta)) return fail(DIT_ERR_INVALID_ARG, "theta must be positive");
+    int sum = 0, p = 0;
+    for (int a = 0; a < n_axes; ++a) {
+        const int dim = axes_dim[a];
+        if (dim <= 0 || dim % 2) return fail(DIT_ERR_INVALID_ARG, "axes_dim[%d] = %d must be even and positive", a, dim);
+        sum += dim;
+        if (sum > head_dim) break;
+        for (int j = 0; j < dim / 2; ++j, ++p) {
+            const double om = std::pow((double)theta, -2.0 * j / dim);
+            t.omega_d[p] = om;
+            t.omega[p] = (float)om;
+            t.axis[p] = (int8_t)a;
+        }
+    }
+    if (sum != head_dim) return fail(DIT_ERR_INVALID_ARG, "axes_dim sum to %d, head_dim is %d", sum, head_dim);
+    return DIT_OK;
+}
+
+int validate_config(const dit_block_config* c) {
+    if (!c) return fail(DIT_ERR_INVALID_ARG, "cfg is NULL");
+    if (!valid_dtype(c->dtype) || !valid_dtype(c->x_dtype) || !valid_dtype(c->y_dtype))
+        return fail(DIT_ERR_INVALID_ARG, "dtype / x_dtype / y_dtype must be DIT_F32 or DIT_BF16");
+    if (c->dtype == DIT_F32 && (c->x_dtype != DIT_F32 || c->y_dtype != DIT_F32))
+        return fail(DIT_ERR_UNSUPPORTED, "an fp32 block needs fp32 x and y");
+    if (c->head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim = %d (only 128 is supported)", c->head_dim);
+    if (c->n_heads < 1 || c->d != c->n_heads * c->head_dim)
+        return fail(DIT_ERR_INVALID_ARG, "d = %d must equal n_heads * head_dim = %d * %d", c->d, c->n_heads, c->head_dim);
+    if (c->d > 8192) return fail(DIT_ERR_UNSUPPORTED, "d = %d (at most 8192)", c->d);
+    if (c->ffn_inner < 128 || c->ffn_inner % 128)
+        return fail(DIT_ERR_INVALID_ARG, "ffn_inner = %d must be a positive multiple of 128", c->ffn_inner);
+    if (c->d_cond < 8 || c->d_cond % 8 || c->d_cond > 16384)
+        return fail(DIT_ERR_INVALID_ARG, "d_cond = %d must be a multiple of 8 in [8, 16384]", c->d_cond);
+    if (c->n_txt < 0 || c->n_img < 0 || c->n_txt + c->n_img < 1)
+        return fail(DIT_ERR_INVALID_ARG, "n_txt = %d, n_img = %d: need n_txt, n_img >= 0 and at least one token",
+                    c->n_txt, c->n_img);
+    if (!(c->eps >= 0.0f) || !(c->eps_qk >= 0.0f)) return fail(DIT_ERR_INVALID_ARG, "eps must be >= 0");
+    RopeTable t;
+    return build_rope_table(c->head_dim, c->n_axes, c->axes_dim, c->theta, t);
+}
+
+// Workspace plan: 256-byte aligned sub-buffers.
+struct WsPlan {
+    size_t mod, act, qkv, o, h, f, of, total;
+};
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+WsPlan plan_workspace(const dit_block_config* c, int single) {
+    const size_t n = (size_t)c->n_txt + c->n_img, d = c->d, F = c->ffn_inner, es = esize(c->dtype);
+    WsPlan p{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
+    if (!single) {
+        p.mod = take(2 * 6 * d * 4);
+        p.act = take(n * d * es);
+        p.qkv = take(n * 3 * d * es);
+        p.o = take(n * d * es);
+        p.h = take(n * d * 4);
+        p.f = take(n * F * es);
+    } else {
+        p.mod = take(3 * d * 4);
+        p.act = take(n * d * es);
+        p.qkv = take(n * 3 * d * es);
+        p.of = take(n * (d + F) * es);
+    }
+    p.total = off;
+    return p;
+}
+
+}  // namespace
+
+// =========================================================================================
+extern "C" {
+
+const char* dit_last_error(void) { return tl_err; }
+uint64_t dit_launch_count(void) { return tl_launches; }
+int dit_abi_version(void) { return DIT_ABI_VERSION; }
+
+int dit_adaln_modulate(int dtype, void* stream, const void* cond, int d_cond, const void* w_mod, int n_chunks,
+                       int d, float* mod_out, const void* x, int x_dtype, int n_tok, long ld_x, int shift_chunk,
+                       int scale_chunk, float eps, void* x_out, long ld_out) {
+    clear_err();
+    if (!valid_dtype(dtype)) return fail(DIT_ERR_INVALID_ARG, "dtype %d", dtype);
+    DIT_TRY(check_ptr(cond, "cond"));
+    DIT_TRY(check_ptr(w_mod, "w_mod"));
+    DIT_TRY(check_ptr(mod_out, "mod_out"));
+    if (d < 8 || d % 8 || d > 8192) return fail(DIT_ERR_INVALID_ARG, "d = %d must be a multiple of 8 in [8, 8192]", d);
+    if (d_cond < 8 || d_cond % 8 || d_cond > 16384)
+        return fail(DIT_ERR_INVALID_ARG, "d_cond = %d must be a multiple of 8 in [8, 16384]", d_cond);
+    if (n_chunks < 1) return fail(DIT_ERR_INVALID_ARG, "n_chunks = %d", n_chunks);
+    if ((long)n_chunks * d > (1L << 30)) return fail(DIT_ERR_UNSUPPORTED, "n_chunks * d too large");
+    if (x) {
+        if (!valid_dtype(x_dtype)) return fail(DIT_ERR_INVALID_ARG, "x_dtype %d", x_dtype);
+        if (dtype == DIT_F32 && x_dtype != DIT_F32) return fail(DIT_ERR_UNSUPPORTED, "fp32 call needs fp32 x");
+        if (n_tok < 0) return fail(DIT_ERR_INVALID_ARG, "n_tok = %d", n_tok);
+        if (shift_chunk < 0 || shift_chunk >= n_chunks || scale_chunk < 0 || scale_chunk >= n_chunks)
+            return fail(DIT_ERR_INVALID_ARG, "shift_chunk / scale_chunk out of [0, n_chunks)");
+        if (!(eps >= 0.0f)) return fail(DIT_ERR_INVALID_ARG, "eps must be >= 0");
+        DIT_TRY(check_ptr(x, "x"));
+        DIT_TRY(check_ptr(x_out, "x_out"));
+        DIT_TRY(check_ld(ld_x, d, x_dtype, "ld_x"));
+        DIT_TRY(check_ld(ld_out, d, dtype, "ld_out"));
+        if (overlap(range_of(x, n_tok, ld_x, d, x_dtype), range_of(x_out, n_tok, ld_out, d, dtype)))
+            return fail(DIT_ERR_INVALID_ARG, "x_out overlaps x");
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    GemvBatch g{};
+    g.p[0] = {w_mod, mod_out, n_chunks * d};
+    g.n = 1;
+    g.cond = cond;
+    g.d_cond = d_cond;
+    g.dtype = dtype;
+    DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
+    if (x && n_tok > 0) {
+        ModBatch m{};
+        m.p[0] = {x, ld_x, x_dtype, x_out, ld_out, mod_out + (size_t)shift_chunk * d,
+                  mod_out + (size_t)scale_chunk * d, n_tok};
+        m.n = 1;
+        m.d = d;
+        m.eps = eps;
+        m.dtype = dtype;
+        DIT_TRY(launch("modulate", s, [&] { return launch_modulate(m, s); }));
+    }
+    return DIT_OK;
+}
+
+int dit_qk_rmsnorm_rope(int dtype, void* stream, void* q, long ld_q, void* k, long ld_k, int n_tok, int n_heads,
+                        int head_dim, const void* qk_w, int n_first, float eps, const int32_t* pos, int n_axes,
+                        const int* axes_dim, float theta) {
+    clear_err();
+    if (!valid_dtype(dtype)) return fail(DIT_ERR_INVALID_ARG, "dtype %d", dtype);
+    if (head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim = %d (only 128 is supported)", head_dim);
+    if (n_heads < 1) return fail(DIT_ERR_INVALID_ARG, "n_heads = %d", n_heads);
+    if (n_tok < 0) return fail(DIT_ERR_INVALID_ARG, "n_tok = %d", n_tok);
+    if (!(eps >= 0.0f)) return fail(DIT_ERR_INVALID_ARG, "eps must be >= 0");
+    QkRopeArgs a{};
+    DIT_TRY(build_rope_table(head_dim, n_axes, axes_dim, theta, a.tab));
+    if (n_tok == 0) return DIT_OK;          // nothing is read or written
+    DIT_TRY(check_ptr(q, "q"));
+    DIT_TRY(check_ptr(k, "k"));
+    DIT_TRY(check_ptr(qk_w, "qk_w"));
+    DIT_TRY(check_ptr(pos, "pos"));
+    const long width = (long)n_heads * head_dim;
+    DIT_TRY(check_ld(ld_q, width, dtype, "ld_q"));
+    DIT_TRY(check_ld(ld_k, width, dtype, "ld_k"));
+    if (overlap(range_of(q, n_tok, ld_q, width, dtype), range_of(k, n_tok, ld_k, width, dtype))) {
+        // q and k may be column views of one buffer: they must not share an element.
+        const uintptr_t qa = reinterpret_cast<uintptr_t>(q), ka = reinterpret_cast<uintptr_t>(k);
+        const uintptr_t dist = qa > ka ? qa - ka : ka - qa;
+        if (ld_q != ld_k || dist < (uintptr_t)width * esize(dtype) ||
+            dist + (uintptr_t)width * esize(dtype) > (uintptr_t)ld_q * esize(dtype))
+            return fail(DIT_ERR_INVALID_ARG, "q and k overlap");
+    }
+    if (n_tok == 0) return DIT_OK;
+    a.q = q; a.ld_q = ld_q; a.k = k; a.ld_k = ld_k;
+    a.n_tok = n_tok; a.n_heads = n_heads; a.n_first = n_first; a.eps = eps;
+    a.qk_w0 = qk_w;
+    a.qk_w1 = reinterpret_cast<const char*>(qk_w) + (n_first < n_tok ? 2 * (size_t)head_dim * esize(dtype) : 0);
+    a.pos = pos; a.n_axes = n_axes; a.dtype = dtype;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(a, s); });
+}
+
+int dit_joint_attention(int dtype, void* stream, const void* q, long ld_q, const void* k, long ld_k, const void* v,
+                        long ld_v, void* o, long ld_o, int n_tok, int n_heads, int head_dim, float softmax_scale) {
+    clear_err();
+    if (!valid_dtype(dtype)) return fail(DIT_ERR_INVALID_ARG, "dtype %d", dtype);
+    if (head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim = %d (only 128 is supported)", head_dim);
+    if (n_heads < 1) return fail(DIT_ERR_INVALID_ARG, "n_heads = %d", n_heads);
+    if (n_tok < 0) return fail(DIT_ERR_INVALID_ARG, "n_tok = %d", n_tok);
+    if (!std::isfinite(softmax_scale)) return fail(DIT_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (n_tok == 0) return DIT_OK;          // nothing is read or written
+    DIT_TRY(check_ptr(q, "q"));
+    DIT_TRY(check_ptr(k, "k"));
+    DIT_TRY(check_ptr(v, "v"));
+    DIT_TRY(check_ptr(o, "o"));
+    const long width = (long)n_heads * head_dim;
+    DIT_TRY(check_ld(ld_q, width, dtype, "ld_q"));
+    DIT_TRY(check_ld(ld_k, width, dtype, "ld_k"));
+    DIT_TRY(check_ld(ld_v, width, dtype, "ld_v"));
+    DIT_TRY(check_ld(ld_o, width, dtype, "ld_o"));
+    const Range ro = range_of(o, n_tok, ld_o, width, dtype);
+    if (overlap(ro, range_of(q, n_tok, ld_q, width, dtype)) || overlap(ro, range_of(k, n_tok, ld_k, width, dtype)) ||
+        overlap(ro, range_of(v, n_tok, ld_v, width, dtype)))
+        return fail(DIT_ERR_INVALID_ARG, "o overlaps q, k or v");
+    if ((long)n_tok * n_heads > (1L << 30)) return fail(DIT_ERR_UNSUPPORTED, "n_tok * n_heads too large");
+    if (n_tok == 0) return DIT_OK;
+    AttnArgs a{q, ld_q, k, ld_k, v, ld_v, o, ld_o, n_tok, n_heads, softmax_scale, dtype};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("joint_attention", s, [&] { return launch_attention(a, s); });
+}
+
+size_t dit_block_workspace_size(const dit_block_config* cfg, int single_stream) {
+    clear_err();
+    if (validate_config(cfg) != DIT_OK) return 0;
+    return plan_workspace(cfg, single_stream ? 1 : 0).total;
+}
+
+static int check_stream_weights(const dit_stream_weights* w, const char* s) {
+    if (!w) return fail(DIT_ERR_INVALID_ARG, "%s weights are NULL", s);
+    const void* p[6] = {w->w_mod, w->w_qkv, w->qk_norm_w, w->w_o, w->w_ffn_in, w->w_ffn_out};
+    const char* n[6] = {"w_mod", "w_qkv", "qk_norm_w", "w_o", "w_ffn_in", "w_ffn_out"};
+    for (int i = 0; i < 6; ++i) {
+        if (!p[i]) return fail(DIT_ERR_INVALID_ARG, "%s.%s is NULL", s, n[i]);
+        if (!aligned16(p[i])) return fail(DIT_ERR_INVALID_ARG, "%s.%s is not 16-byte aligned", s, n[i]);
+    }
+    return DIT_OK;
+}
+
+int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt, const dit_stream_weights* img,
+                      const void* cond, const int32_t* pos, const void* x_txt, const void* x_img, void* y_txt,
+                      void* y_img, void* workspace, size_t ws_bytes, void* stream) {
+    clear_err();
+    DIT_TRY(validate_config(cfg));
+    const dit_block_config& c = *cfg;
+    const int nt = c.n_txt, ni = c.n_img, n = nt + ni, d = c.d, F = c.ffn_inner;
+    DIT_TRY(check_stream_weights(txt, "txt"));
+    DIT_TRY(check_stream_weights(img, "img"));
+    DIT_TRY(check_ptr(cond, "cond"));
+    DIT_TRY(check_ptr(pos, "pos"));
+    if (nt > 0) { DIT_TRY(check_ptr(x_txt, "x_txt")); DIT_TRY(check_ptr(y_txt, "y_txt")); }
+    if (ni > 0) { DIT_TRY(check_ptr(x_img, "x_img")); DIT_TRY(check_ptr(y_img, "y_img")); }
+    DIT_TRY(check_ptr(workspace, "workspace"));
+    const WsPlan W = plan_workspace(cfg, 0);
+    if (ws_bytes < W.total)
+        return fail(DIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
+    // y may alias x (same dtype); otherwise no overlap; nothing may overlap the workspace.
+    const Range rws{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + W.total};
+    const Range rxt = range_of(x_txt, nt, d, d, c.x_dtype), rxi = range_of(x_img, ni, d, d, c.x_dtype);
+    const Range ryt = range_of(y_txt, nt, d, d, c.y_dtype), ryi = range_of(y_img, ni, d, d, c.y_dtype);
+    if (overlap(rws, rxt) || overlap(rws, rxi) || overlap(rws, ryt) || overlap(rws, ryi))
+        return fail(DIT_ERR_INVALID_ARG, "workspace overlaps an input or output");
+    if (overlap(ryt, ryi)) return fail(DIT_ERR_INVALID_ARG, "y_txt overlaps y_img");
+    const bool same = c.x_dtype == c.y_dtype;
+    if ((overlap(ryt, rxt) && !(same && ryt.lo == rxt.lo)) || (overlap(ryi, rxi) && !(same && ryi.lo == rxi.lo)) ||
+        overlap(ryt, rxi) || overlap(ryi, rxt))
+        return fail(DIT_ERR_INVALID_ARG, "y overlaps x other than as an exact alias of the same dtype");
+
+    char* ws = reinterpret_cast<char*>(workspace);
+    float* mod_t = reinterpret_cast<float*>(ws + W.mod);
+    float* mod_i = mod_t + 6 * (size_t)d;
+    char* act = ws + W.act;
+    char* qkv = ws + W.qkv;
+    char* ob = ws + W.o;
+    float* h = reinterpret_cast<float*>(ws + W.h);
+    char* f = ws + W.f;
+    const size_t es = esize(c.dtype), xs = esize(c.x_dtype);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    // 1. AdaLN vectors of both streams
+    GemvBatch g{};
+    g.p[0] = {txt->w_mod, mod_t, 6 * d};
+    g.p[1] = {img->w_mod, mod_i, 6 * d};
+    g.n = 2;
+    g.cond = cond;
+    g.d_cond = c.d_cond;
+    g.dtype = c.dtype;
+    DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
+
+    // 2. a = (1 + scale1) RMSNorm(x) + shift1   (text rows, then image rows)
+    ModBatch m{};
+    int nm = 0;
+    if (nt) m.p[nm++] = {x_txt, d, c.x_dtype, act, d, mod_t + 0 * d, mod_t + 1 * (size_t)d, nt};
+    if (ni) m.p[nm++] = {x_img, d, c.x_dtype, act + (size_t)nt * d * es, d, mod_i + 0 * d, mod_i + 1 * (size_t)d, ni};
+    m.n = nm; m.d = d; m.eps = c.eps; m.dtype = c.dtype;
+    DIT_TRY(launch("modulate_x", s, [&] { return launch_modulate(m, s); }));
+
+    // 3. qkv = a W_qkv^T
+    GemmBatch gq{};
+    gq.dtype = c.dtype;
+    {
+        int k = 0;
+        if (nt) gq.p[k++] = {act, d, txt->w_qkv, d, qkv, 3L * d, c.dtype, nullptr, 0, 0, nullptr, 0, nt, 3 * d, d, EPI_STORE};
+        if (ni) gq.p[k++] = {act + (size_t)nt * d * es, d, img->w_qkv, d, qkv + (size_t)nt * 3 * d * es, 3L * d, c.dtype,
+                             nullptr, 0, 0, nullptr, 0, ni, 3 * d, d, EPI_STORE};
+        gq.n = k;
+    }
+    DIT_TRY(launch("gemm_qkv", s, [&] { return launch_gemm(gq, s); }));
+
+    // 4. QK RMSNorm + RoPE in place (text rows use the text weights)
+    QkRopeArgs r{};
+    DIT_TRY(build_rope_table(c.head_dim, c.n_axes, c.axes_dim, c.theta, r.tab));
+    r.q = qkv; r.ld_q = 3L * d; r.k = qkv + (size_t)d * es; r.ld_k = 3L * d;
+    r.n_tok = n; r.n_heads = c.n_heads; r.qk_w0 = txt->qk_norm_w; r.qk_w1 = img->qk_norm_w; r.n_first = nt;
+    r.eps = c.eps_qk; r.pos = pos; r.n_axes = c.n_axes; r.dtype = c.dtype;
+    DIT_TRY(launch("qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(r, s); }));
+
+    // 5. O = joint attention over all n tokens
+    AttnArgs at{qkv, 3L * d, qkv + (size_t)d * es, 3L * d, qkv + (size_t)2 * d * es, 3L * d, ob, d, n, c.n_heads,
+                1.0f / std::sqrt((float)c.head_dim), c.dtype};
+    DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
+
+    // 6. h = x + gate1 * (O W_o^T)   (fp32)
+    GemmBatch go{};
+    go.dtype = c.dtype;
+    {
+        int k = 0;
+        if (nt) go.p[k++] = {ob, d, txt->w_o, d, h, d, DIT_F32, x_txt, d, c.x_dtype, mod_t + 2 * (size_t)d, 0, nt, d, d,
+                             EPI_GATED_RES};
+        if (ni) go.p[k++] = {ob + (size_t)nt * d * es, d, img->w_o, d, h + (size_t)nt * d, d, DIT_F32, x_img, d,
+                             c.x_dtype, mod_i + 2 * (size_t)d, 0, ni, d, d, EPI_GATED_RES};
+        go.n = k;
+    }
+    DIT_TRY(launch("gemm_out_proj", s, [&] { return launch_gemm(go, s); }));
+
+    // 7. b = (1 + scale2) RMSNorm(h) + shift2
+    ModBatch m2{};
+    nm = 0;
+    if (nt) m2.p[nm++] = {h, d, DIT_F32, act, d, mod_t + 3 * (size_t)d, mod_t + 4 * (size_t)d, nt};
+    if (ni) m2.p[nm++] = {h + (size_t)nt * d, d, DIT_F32, act + (size_t)nt * d * es, d, mod_i + 3 * (size_t)d,
+                          mod_i + 4 * (size_t)d, ni};
+    m2.n = nm; m2.d = d; m2.eps = c.eps; m2.dtype = c.dtype;
+    DIT_TRY(launch("modulate_h", s, [&] { return launch_modulate(m2, s); }));
+
+    // 8. f = SiLU(b W_gate^T) * (b W_up^T)
+    GemmBatch gf{};
+    gf.dtype = c.dtype;
+    {
+        int k = 0;
+        if (nt) gf.p[k++] = {act, d, txt->w_ffn_in, d, f, F, c.dtype, nullptr, 0, 0, nullptr, F, nt, F, d, EPI_SWIGLU};
+        if (ni) gf.p[k++] = {act + (size_t)nt * d * es, d, img->w_ffn_in, d, f + (size_t)nt * F * es, F, c.dtype, nullptr,
+                             0, 0, nullptr, F, ni, F, d, EPI_SWIGLU};
+        gf.n = k;
+    }
+    DIT_TRY(launch("gemm_ffn_in_swiglu", s, [&] { return launch_gemm(gf, s); }));
+
+    // 9. y = h + gate2 * (f W_down^T)
+    GemmBatch gd{};
+    gd.dtype = c.dtype;
+    {
+        int k = 0;
+        if (nt) gd.p[k++] = {f, F, txt->w_ffn_out, F, y_txt, d, c.y_dtype, h, d, DIT_F32, mod_t + 5 * (size_t)d, 0, nt, d,
+                             F, EPI_GATED_RES};
+        if (ni) gd.p[k++] = {f + (size_t)nt * F * es, F, img->w_ffn_out, F, y_img, d, c.y_dtype, h + (size_t)nt * d, d,
+                             DIT_F32, mod_i + 5 * (size_t)d, 0, ni, d, F, EPI_GATED_RES};
+        gd.n = k;
+    }
+    DIT_TRY(launch("gemm_ffn_down", s, [&] { return launch_gemm(gd, s); }));
+    (void)xs;
+    return DIT_OK;
+}
+
+int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weights* w, const void* cond,
+                             const int32_t* pos, const void* x, void* y, void* workspace, size_t ws_bytes,
+                             void* stream) {
+    clear_err();
+    DIT_TRY(validate_config(cfg));
+    const dit_block_config& c = *cfg;
+    const int n = c.n_txt + c.n_img, d = c.d, F = c.ffn_inner;
+    if (!w) return fail(DIT_ERR_INVALID_ARG, "weights are NULL");
+    DIT_TRY(check_ptr(w->w_mod, "w_mod"));
+    DIT_TRY(check_ptr(w->w_1, "w_1"));
+    DIT_TRY(check_ptr(w->qk_norm_w, "qk_norm_w"));
+    DIT_TRY(check_ptr(w->w_2, "w_2"));
+    DIT_TRY(check_ptr(cond, "cond"));
+    DIT_TRY(check_ptr(pos, "pos"));
+    DIT_TRY(check_ptr(x, "x"));
+    DIT_TRY(check_ptr(y, "y"));
+    DIT_TRY(check_ptr(workspace, "workspace"));
+    const WsPlan W = plan_workspace(cfg, 1);
+    if (ws_bytes < W.total)
+        return fail(DIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
+    const Range rws{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + W.total};
+    const Range rx = range_of(x, n, d, d, c.x_dtype), ry = range_of(y, n, d, d, c.y_dtype);
+    if (overlap(rws, rx) || overlap(rws, ry)) return fail(DIT_ERR_INVALID_ARG, "workspace overlaps x or y");
+    if (overlap(rx, ry) && !(c.x_dtype == c.y_dtype && rx.lo == ry.lo))
+        return fail(DIT_ERR_INVALID_ARG, "y overlaps x other than as an exact alias of the same dtype");
+
+    char* ws = reinterpret_cast<char*>(workspace);
+    float* mod = reinterpret_cast<float*>(ws + W.mod);
+    char* act = ws + W.act;
+    char* qkv = ws + W.qkv;
+    char* of = ws + W.of;
+    const size_t es = esize(c.dtype);
+    const long ldof = (long)d + F;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    GemvBatch g{};
+    g.p[0] = {w->w_mod, mod, 3 * d};
+    g.n = 1; g.cond = cond; g.d_cond = c.d_cond; g.dtype = c.dtype;
+    DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
+
+    ModBatch m{};
+    m.p[0] = {x, d, c.x_dtype, act, d, mod, mod + d, n};
+    m.n = 1; m.d = d; m.eps = c.eps; m.dtype = c.dtype;
+    DIT_TRY(launch("modulate_x", s, [&] { return launch_modulate(m, s); }));
+
+    // [q|k|v] = a W_1[0:3d]^T  and  f = SiLU(a W_1[3d:3d+F]^T) * (a W_1[3d+F:]^T), written next to O
+    GemmBatch g1{};
+    g1.dtype = c.dtype;
+    g1.p[0] = {act, d, w->w_1, d, qkv, 3L * d, c.dtype, nullptr, 0, 0, nullptr, 0, n, 3 * d, d, EPI_STORE};
+    g1.p[1] = {act, d, reinterpret_cast<const char*>(w->w_1) + (size_t)3 * d * d * es, d, of + (size_t)d * es, ldof,
+               c.dtype, nullptr, 0, 0, nullptr, F, n, F, d, EPI_SWIGLU};
+    g1.n = 2;
+    DIT_TRY(launch("gemm_linear1", s, [&] { return launch_gemm(g1, s); }));
+
+    QkRopeArgs r{};
+    DIT_TRY(build_rope_table(c.head_dim, c.n_axes, c.axes_dim, c.theta, r.tab));
+    r.q = qkv; r.ld_q = 3L * d; r.k = qkv + (size_t)d * es; r.ld_k = 3L * d;
+    r.n_tok = n; r.n_heads = c.n_heads; r.qk_w0 = w->qk_norm_w; r.qk_w1 = w->qk_norm_w; r.n_first = n;
+    r.eps = c.eps_qk;
+    r.pos = pos; r.n_axes = c.n_axes; r.dtype = c.dtype;
+    DIT_TRY(launch("qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(r, s); }));
+
+    AttnArgs at{qkv, 3L * d, qkv + (size_t)d * es, 3L * d, qkv + (size_t)2 * d * es, 3L * d, of, ldof, n, c.n_heads,
+                1.0f / std::sqrt((float)c.head_dim), c.dtype};
+    DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
+
+    GemmBatch g2{};
+    g2.dtype = c.dtype;
+    g2.p[0] = {of, ldof, w->w_2, ldof, y, d, c.y_dtype, x, d, c.x_dtype, mod + 2 * (size_t)d, 0, n, d, d + F,
+               EPI_GATED_RES};
+    g2.n = 1;
+    DIT_TRY(launch("gemm_linear2", s, [&] { return launch_gemm(g2, s); }));
+    return DIT_OK;
+}
+
+// ---- kernel timing --------------------------------------------------------------------------
+int dit_timing_begin(int capacity) {
+    clear_err();
+    TimingState& T = tl_timing;
+    if (capacity < 1 || capacity > (1 << 20)) return fail(DIT_ERR_INVALID_ARG, "capacity = %d", capacity);
+    for (hipEvent_t e : T.ev) (void)hipEventDestroy(e);
+    T.ev.assign(2 * (size_t)capacity, nullptr);
+    T.name.assign(capacity, nullptr);
+    for (auto& e : T.ev)
+        if (hipEventCreate(&e) != hipSuccess) return fail(DIT_ERR_HIP, "hipEventCreate failed");
+    T.capacity = capacity;
+    T.used = 0;
+    T.on = true;
+    return DIT_OK;
+}
+
+int dit_timing_end(void) {
+    tl_timing.on = false;
+    return DIT_OK;
+}
+
+int dit_timing_read(int i, char* name_buf, int name_len, int* launches, double* total_ms) {
+    clear_err();
+    TimingState& T = tl_timing;
+    std::vector<const char*> names;
+    std::vector<double> sums;
+    std::vector<int> counts;
+    for (int u = 0; u < T.used; ++u) {
+        if (hipEventSynchronize(T.ev[2 * u + 1]) != hipSuccess) {
+            fail(DIT_ERR_HIP, "hipEventSynchronize failed");
+            return -1;
+        }
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, T.ev[2 * u], T.ev[2 * u + 1]) != hipSuccess) {
+            fail(DIT_ERR_HIP, "hipEventElapsedTime failed");
+            return -1;
+        }
+        size_t k = 0;
+        while (k < names.size() && std::strcmp(names[k], T.name[u]) != 0) ++k;
+        if (k == names.size()) { names.push_back(T.name[u]); sums.push_back(0.0); counts.push_back(0); }
+        sums[k] += ms;
+        counts[k] += 1;
+    }
+    if (i >= 0 && i < (int)names.size()) {
+        if (name_buf && name_len > 0) {
+            std::strncpy(name_buf, names[i], (size_t)name_len - 1);
+            name_buf[name_len - 1] = 0;
+        }
+        if (launches) *launches = counts[i];
+        if (total_ms) *total_ms = sums[i];
+    }
+    return (int)names.size();
+}
+
+}  // extern "C"

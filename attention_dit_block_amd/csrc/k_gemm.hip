@@ -1,0 +1,335 @@
+// Grouped GEMMs of the DiT block on gfx950: C = epilogue(A . B^T), A = activations [M, K],
+// B = weights [N, K] ([out, in]).  These are the thread's "heavy matrix multiplications"
+// (QKV projections, FFN; the "CUDA codepath !" thread, antirez/iris.c issue #15), with the
+// per-block elementwise work fused into the epilogue:
+//   EPI_STORE     C = acc                                   (QKV)
+//   EPI_GATED_RES C = R + gate[col] * acc                   (out-proj, FFN-down: gated residual)
+//   EPI_SWIGLU    C = SiLU(acc_gate) * acc_up               (FFN-in)
+// One launch covers several problems (text and image streams, or the two halves of the
+// single-stream block's first linear).
+//
+// bf16 path: 256-thread workgroups (4 waves, 2 x 2), a 256 x 256 x 64 block tile, each wave a
+// 128 x 128 sub-tile of 4 x 4 v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators.  Both
+// operands go global -> LDS with global_load_lds_dwordx4 (no VGPR staging), double-buffered;
+// LDS rows are 128 B with the 16-byte chunk index XOR-swizzled by (row & 7) so the fragment
+// reads are bank-conflict free.  The MFMA computes D[n][m], so each lane ends with four
+// consecutive output columns of one row and the epilogue reads / writes 8-16 B per lane.
+// Workgroups are remapped so each XCD gets a contiguous range of tiles, grouped along M.
+//
+// fp32 path: a plain LDS-tiled FMA kernel (no reduced-precision matrix math).
+#include "dev_common.h"
+#include "launch.h"
+
+namespace dit {
+
+enum GemmMode { MODE_STORE = 0, MODE_RES = 1, MODE_SWIGLU = 2, MODE_MIXED = 3 };
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kGroupM = 4;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void tile_of(const GemmBatch& b, int L, int& pi, int& tm, int& tn) {
+    pi = (b.n > 1 && L >= b.p[1].tile_begin) ? 1 : 0;
+    const GemmProblem& P = b.p[pi];
+    const int t = L - P.tile_begin;
+    const int per_group = kGroupM * P.tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * kGroupM;
+    const int gsize = min(P.tiles_m - first_m, kGroupM);
+    const int r = t - g * per_group;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+}
+
+// XCD-aware remap: consecutive workgroup ids go round-robin over the 8 XCDs; give each XCD a
+// contiguous range of tile indices instead.
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+    const int x = bid & 7, idx = bid >> 3;
+    const int q = nwg >> 3, r = nwg & 7;
+    return x * q + min(x, r) + idx;
+}
+
+__device__ __forceinline__ float silu_acc(float g) { return g / (1.0f + __expf(-g)); }
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmBatch b) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * (BM + BN) * BK * 2];
+    constexpr int kStage = (BM + BN) * BK * 2;     // bytes of one A+B stage
+    constexpr int kBOff = BM * BK * 2;             // B tile offset within a stage
+
+    int pi, tm, tn;
+    tile_of(b, xcd_remap(blockIdx.x, gridDim.x), pi, tm, tn);
+    const GemmProblem& P = b.p[pi];
+    const int epi = MODE == MODE_MIXED ? P.epi : (MODE == MODE_SWIGLU ? EPI_SWIGLU
+                                                  : (MODE == MODE_RES ? EPI_GATED_RES : EPI_STORE));
+    const bool swiglu = epi == EPI_SWIGLU;
+    const int m0 = tm * BM;
+    const int n0 = swiglu ? tn * (BN / 2) : tn * BN;   // first output column
+    const int M = P.M, K = P.K;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // ---- global -> LDS load plan: wave w, instruction i covers tile rows (w*8+i)*8 .. +7
+    const bf16_t* gA[8];
+    const bf16_t* gB[8];
+    {
+        const int lr = lane >> 3, lc = lane & 7;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = (wave * 8 + i) * 8 + lr;
+            const int chunk = lc ^ (row & 7);
+            int am = m0 + row;
+            am = am < M ? am : M - 1;
+            gA[i] = reinterpret_cast<const bf16_t*>(P.A) + (size_t)am * P.lda + chunk * 8;
+            long bn;
+            if (swiglu) bn = row < BN / 2 ? (long)n0 + row : P.up_off + n0 + (row - BN / 2);
+            else bn = n0 + row;
+            const long nmax = swiglu ? P.up_off + P.N - 1 : P.N - 1;
+            if (!swiglu && bn > nmax) bn = nmax;
+            if (swiglu) {
+                const long lim = row < BN / 2 ? P.N - 1 : P.up_off + P.N - 1;
+                if (bn > lim) bn = lim;
+            }
+            gB[i] = reinterpret_cast<const bf16_t*>(P.B) + (size_t)bn * P.ldb + chunk * 8;
+        }
+    }
+    auto issue_loads = [&](int buf, int k0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_global_load_lds(gA[i] + k0, (lds_void*)(smem + buf * kStage + (wave * 8 + i) * 1024),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gB[i] + k0,
+                                             (lds_void*)(smem + buf * kStage + kBOff + (wave * 8 + i) * 1024),
+                                             16, 0, 0);
+        }
+    };
+
+    // ---- fragment read offsets (bytes within a tile buffer)
+    // A fragment (m-block mb): row wm*128 + mb*32 + (lane & 31); B fragment (n-block nb): see below.
+    int a_row[4], b_row[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        a_row[j] = wm * 128 + j * 32 + (lane & 31);
+        if (swiglu) b_row[j] = (j < 2 ? wn * 64 + j * 32 : BN / 2 + wn * 64 + (j - 2) * 32) + (lane & 31);
+        else b_row[j] = wn * 128 + j * 32 + (lane & 31);
+    }
+    const int khalf = lane >> 5;
+
+    f32x16_v acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    const int nk = K / BK;
+    issue_loads(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int it = 0; it < nk; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < nk) issue_loads(buf ^ 1, (it + 1) * BK);
+        const char* la = smem + buf * kStage;
+        const char* lb = la + kBOff;
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            const int c = 2 * s + khalf;
+            bf16x8_v fa[4], fb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                fa[j] = *reinterpret_cast<const bf16x8_v*>(la + a_row[j] * 128 + ((c ^ (a_row[j] & 7)) << 4));
+                fb[j] = *reinterpret_cast<const bf16x8_v*>(lb + b_row[j] * 128 + ((c ^ (b_row[j] & 7)) << 4));
+            }
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // ---- epilogue.  acc[nb][mb][q]: row m = m0 + wm*128 + mb*32 + (lane & 31),
+    //      B-row offset within the n-block: 8*(q>>2) + 4*khalf + (q&3).
+    const int mlane = lane & 31;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int m = m0 + wm * 128 + mb * 32 + mlane;
+        if (m >= M) continue;
+        if (swiglu) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int col = n0 + wn * 64 + nb * 32 + 8 * i + 4 * khalf;
+                    if (col >= P.N) continue;
+                    float f[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float g = acc[nb][mb][4 * i + j];
+                        const float u = acc[nb + 2][mb][4 * i + j];
+                        f[j] = silu_acc(g) * u;
+                    }
+                    u32x2_v w = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+                    *reinterpret_cast<u32x2_v*>(reinterpret_cast<bf16_t*>(P.C) + (size_t)m * P.ldc + col) = w;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int col = n0 + wn * 128 + nb * 32 + 8 * i + 4 * khalf;
+                    if (col >= P.N) continue;
+                    float o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] = acc[nb][mb][4 * i + j];
+                    if (epi == EPI_GATED_RES) {
+                        const f32x4_v gt = ldf4(P.gate + col);
+                        float r[4];
+                        if (P.r_dtype == BF16) {
+                            const u32x2_v rv = *reinterpret_cast<const u32x2_v*>(
+                                reinterpret_cast<const bf16_t*>(P.R) + (size_t)m * P.ldr + col);
+                            r[0] = bf_lo(rv[0]); r[1] = bf_hi(rv[0]); r[2] = bf_lo(rv[1]); r[3] = bf_hi(rv[1]);
+                        } else {
+                            const f32x4_v rv = ldf4(reinterpret_cast<const float*>(P.R) + (size_t)m * P.ldr + col);
+                            r[0] = rv[0]; r[1] = rv[1]; r[2] = rv[2]; r[3] = rv[3];
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) o[j] = fmaf(gt[j], o[j], r[j]);
+                    }
+                    if (P.c_dtype == BF16) {
+                        u32x2_v w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                        *reinterpret_cast<u32x2_v*>(reinterpret_cast<bf16_t*>(P.C) + (size_t)m * P.ldc + col) = w;
+                    } else {
+                        f32x4_v w = {o[0], o[1], o[2], o[3]};
+                        stf4(reinterpret_cast<float*>(P.C) + (size_t)m * P.ldc + col, w);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// fp32 GEMM: 64 x 64 block tile, K step 16, 256 threads each owning a 4 x 4 output patch.
+// SwiGLU problems load a second B tile (the up rows) and keep a second accumulator.
+// ------------------------------------------------------------------------------------------
+constexpr int FBM = 64, FBN = 64, FBK = 16;
+
+template <bool SWIGLU>
+__device__ __forceinline__ void gemm_f32_tile(const GemmProblem& P, int tm, int tn) {
+    __shared__ float sA[FBK][FBM + 4];
+    __shared__ float sB[FBK][FBN + 4];
+    __shared__ float sU[SWIGLU ? FBK : 1][FBN + 4];
+    const int tid = threadIdx.x;
+    const int m0 = tm * FBM, n0 = tn * FBN;
+    const int lr = tid >> 2, lk = (tid & 3) * 4;          // loader: row, k offset
+    const int ty = tid >> 4, tx = tid & 15;               // compute: 4 rows, 4 cols
+    float acc[4][4] = {}, accu[4][4] = {};
+    const int am = min(m0 + lr, P.M - 1);
+    const int bn = min(n0 + lr, P.N - 1);
+    const float* Ap = reinterpret_cast<const float*>(P.A) + (size_t)am * P.lda;
+    const float* Bp = reinterpret_cast<const float*>(P.B) + (size_t)bn * P.ldb;
+    const float* Up = reinterpret_cast<const float*>(P.B) + (size_t)(P.up_off + bn) * P.ldb;
+    for (int k0 = 0; k0 < P.K; k0 += FBK) {
+        const f32x4_v a = ldf4(Ap + k0 + lk), bb = ldf4(Bp + k0 + lk);
+        f32x4_v uu = {0, 0, 0, 0};
+        if (SWIGLU) uu = ldf4(Up + k0 + lk);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            sA[lk + t][lr] = a[t];
+            sB[lk + t][lr] = bb[t];
+            if (SWIGLU) sU[lk + t][lr] = uu[t];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < FBK; ++kk) {
+            float av[4], bv[4], uv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                av[i] = sA[kk][ty * 4 + i];
+                bv[i] = sB[kk][tx * 4 + i];
+                if (SWIGLU) uv[i] = sU[kk][tx * 4 + i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+                    if (SWIGLU) accu[i][j] = fmaf(av[i], uv[j], accu[i][j]);
+                }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + ty * 4 + i;
+        if (m >= P.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + tx * 4 + j;
+            if (n >= P.N) continue;
+            float o = acc[i][j];
+            if (SWIGLU) o = (o / (1.0f + expf(-o))) * accu[i][j];
+            if (P.epi == EPI_GATED_RES) {
+                const float r = reinterpret_cast<const float*>(P.R)[(size_t)m * P.ldr + n];
+                o = fmaf(P.gate[n], o, r);
+            }
+            reinterpret_cast<float*>(P.C)[(size_t)m * P.ldc + n] = o;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmBatch b) {
+    const int L = blockIdx.x;
+    const int pi = (b.n > 1 && L >= b.p[1].tile_begin) ? 1 : 0;
+    const GemmProblem& P = b.p[pi];
+    const int t = L - P.tile_begin;
+    const int tm = t / P.tiles_n, tn = t % P.tiles_n;
+    if (P.epi == EPI_SWIGLU) gemm_f32_tile<true>(P, tm, tn);
+    else gemm_f32_tile<false>(P, tm, tn);
+}
+
+hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
+    int total = 0;
+    bool any_swiglu = false, all_swiglu = true, all_res = true, all_store = true;
+    for (int i = 0; i < b.n; ++i) {
+        GemmProblem& P = b.p[i];
+        const bool sw = P.epi == EPI_SWIGLU;
+        any_swiglu |= sw;
+        all_swiglu &= sw;
+        all_res &= P.epi == EPI_GATED_RES;
+        all_store &= P.epi == EPI_STORE;
+        if (b.dtype == BF16) {
+            P.tiles_m = (P.M + BM - 1) / BM;
+            P.tiles_n = sw ? (P.N + BN / 2 - 1) / (BN / 2) : (P.N + BN - 1) / BN;
+        } else {
+            P.tiles_m = (P.M + FBM - 1) / FBM;
+            P.tiles_n = (P.N + FBN - 1) / FBN;
+        }
+        if (P.M == 0) P.tiles_m = 0;
+        P.tile_begin = total;
+        total += P.tiles_m * P.tiles_n;
+    }
+    (void)any_swiglu;
+    b.total_tiles = total;
+    if (total == 0) return hipSuccess;
+    if (b.dtype == BF16) {
+        if (all_store) hipLaunchKernelGGL(gemm_bf16_kernel<MODE_STORE>, dim3(total), dim3(256), 0, s, b);
+        else if (all_res) hipLaunchKernelGGL(gemm_bf16_kernel<MODE_RES>, dim3(total), dim3(256), 0, s, b);
+        else if (all_swiglu) hipLaunchKernelGGL(gemm_bf16_kernel<MODE_SWIGLU>, dim3(total), dim3(256), 0, s, b);
+        else hipLaunchKernelGGL(gemm_bf16_kernel<MODE_MIXED>, dim3(total), dim3(256), 0, s, b);
+    } else {
+        hipLaunchKernelGGL(gemm_f32_kernel, dim3(total), dim3(256), 0, s, b);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dit

@@ -1,0 +1,100 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Every launcher assumes its arguments were validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+enum DType { F32 = 0, BF16 = 1 };
+
+// ---- AdaLN GEMV: out_p[r] = sum_k W_p[r, k] * SiLU(cond[k]) ------------------
+struct GemvProblem {
+    const void* w;      // [rows, d_cond]
+    float* out;         // [rows]
+    int rows;
+};
+struct GemvBatch {
+    GemvProblem p[2];
+    int n;
+    const void* cond;   // [d_cond]
+    int d_cond;
+    int dtype;          // dtype of w and cond
+};
+hipError_t launch_adaln_gemv(const GemvBatch& b, hipStream_t s);
+
+// ---- modulate: out = (1 + scale) * RMSNorm(x) + shift, per row ---------------
+struct ModProblem {
+    const void* x; long ld_x; int x_dtype;
+    void* out; long ld_out;           // dtype of the launch
+    const float* shift; const float* scale;   // [d] fp32
+    int rows;
+};
+struct ModBatch {
+    ModProblem p[2];
+    int n;
+    int d;
+    float eps;
+    int dtype;          // output storage type
+};
+hipError_t launch_modulate(const ModBatch& b, hipStream_t s);
+
+// ---- QK RMSNorm + RoPE, in place -----------------------------------------------
+struct RopeTable {
+    float omega[64];        // frequency of pair p (float of the host's double)
+    double omega_d[64];     // same, double precision
+    int8_t axis[64];        // position axis of pair p
+};
+struct QkRopeArgs {
+    void* q; long ld_q;
+    void* k; long ld_k;
+    int n_tok, n_heads;
+    const void* qk_w0;      // [2 (q, k)][128] for rows n < n_first
+    const void* qk_w1;      // [2 (q, k)][128] for rows n >= n_first
+    int n_first;
+    float eps;
+    const int32_t* pos; int n_axes;
+    RopeTable tab;
+    int dtype;
+};
+hipError_t launch_qk_rmsnorm_rope(const QkRopeArgs& a, hipStream_t s);
+
+// ---- grouped GEMM  C = epilogue(A . B^T) -----------------------------------------
+enum Epilogue {
+    EPI_STORE = 0,        // C (dtype) = acc
+    EPI_GATED_RES = 1,    // C (c_dtype) = R (r_dtype) + gate[col] * acc
+    EPI_SWIGLU = 2        // C (dtype) = SiLU(acc_gate) * acc_up; B rows [n] gate, [up_off + n] up
+};
+struct GemmProblem {
+    const void* A; long lda;        // [M, K]
+    const void* B; long ldb;        // [N_b, K]   (weights, [out, in])
+    void* C; long ldc; int c_dtype;
+    const void* R; long ldr; int r_dtype;
+    const float* gate;              // [N]
+    long up_off;                    // SwiGLU: row offset of the up half in B
+    int M, N, K;                    // N = output columns
+    int epi;
+    int tiles_m, tiles_n, tile_begin;   // filled by the launcher
+};
+struct GemmBatch {
+    GemmProblem p[2];
+    int n;
+    int dtype;          // dtype of A and B
+    int total_tiles;    // filled by the launcher
+};
+hipError_t launch_gemm(GemmBatch& b, hipStream_t s);
+
+// ---- joint attention ---------------------------------------------------------------
+struct AttnArgs {
+    const void* q; long ld_q;
+    const void* k; long ld_k;
+    const void* v; long ld_v;
+    void* o; long ld_o;
+    int n_tok, n_heads;
+    float scale;
+    int dtype;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace dit

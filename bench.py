@@ -1,0 +1,215 @@
+"""Benchmark: forward pass of one FLUX-style double-stream DiT block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c4|c3] [--no-cpu-baseline]
+
+A step is one dit_block_forward call (all 9 kernels of the block) over the
+workload's synthetic inputs, already resident in HBM.  Prints ONE JSON line.
+Throughput (``value``) is algorithmic TFLOP/s: 26 N d^2 (GEMMs) + 4 N^2 d
+(attention QK^T and PV) per block, 2 flop per multiply-add.
+
+``roofline`` covers the kernel with the largest total time, timed with HIP
+events the library records on the launch stream around each of its launches
+(dit_timing_*).  ``cpu_baseline`` times the fp64 oracle on one block of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DiT block fwd ms & TFLOP/s (bf16, 4096 img+512 txt tok), % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c2", choices=["c0", "c1", "c2", "c3", "c4"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--seed", type=int, default=0)
+    return p.parse_args()
+
+
+def kernel_work(cfg, name):
+    """Algorithmic work of one launch of a launch site: (flops, bytes, bound)."""
+    n, d, F, dc = cfg.n_tok, cfg.d, cfg.ffn_inner, cfg.dc
+    es = 2 if cfg.dtype == "bf16" else 4
+    table = {
+        "gemm_qkv": (2.0 * n * d * 3 * d, None, "mfma"),
+        "gemm_out_proj": (2.0 * n * d * d, None, "mfma"),
+        "gemm_ffn_in_swiglu": (2.0 * n * d * 2 * F, None, "mfma"),
+        "gemm_ffn_down": (2.0 * n * F * d, None, "mfma"),
+        "gemm_linear1": (2.0 * n * d * (3 * d + 2 * F), None, "mfma"),
+        "gemm_linear2": (2.0 * n * (d + F) * d, None, "mfma"),
+        "joint_attention": (4.0 * n * n * d, None, "mfma"),
+        # HBM-bound: bytes read + written
+        "qk_rmsnorm_rope": (None, 4.0 * n * d * es + 16.0 * n, "hbm"),
+        "adaln_gemv": (None, 2.0 * 6 * d * dc * es, "hbm"),
+        "modulate_x": (None, 1.0 * n * d * (es + es), "hbm"),     # x (workload type) -> a
+        "modulate_h": (None, 1.0 * n * d * (4 + es), "hbm"),      # h (fp32) -> b
+    }
+    return table.get(name, (None, None, "?"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the block is not sharded across GPUs "
+              f"in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dit_inputs as di
+    import attention_dit_block_amd as dit
+
+    cfg = di.config_by_name(args.workload)
+    dev = torch.device("cuda:0")
+    t = cfg.dtype
+
+    def up(a, dt):
+        a = np.ascontiguousarray(a)
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        if dt == "i32":
+            return torch.from_numpy(a).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    tdt = dit.DIT_BF16 if t == "bf16" else dit.DIT_F32
+    step_blocks = []            # callables, one per block of the step
+    t0 = time.time()
+    inp = di.double_block_inputs(cfg, seed=args.seed)
+    cond, pos = up(inp["cond"], t), up(inp["pos"], "i32")
+    x_txt, x_img = up(inp["x_txt"], t), up(inp["x_img"], t)
+    shape = dit.Shape(dtype=tdt, d=cfg.d, n_heads=cfg.n_heads, ffn_inner=cfg.ffn_inner, n_txt=cfg.n_txt,
+                      n_img=cfg.n_img, d_cond=cfg.dc, x_dtype=tdt, y_dtype=dit.DIT_F32)
+    ws = torch.empty(max(dit.block_workspace_size(shape), dit.block_workspace_size(shape, True)),
+                     dtype=torch.uint8, device=dev)
+    y_txt = torch.empty(cfg.n_txt, cfg.d, dtype=torch.float32, device=dev)
+    y_img = torch.empty(cfg.n_img, cfg.d, dtype=torch.float32, device=dev)
+    if cfg.n_double == 1 and cfg.n_single == 0:
+        wt = {k: up(v, t) for k, v in inp["txt"].items()}
+        wi = {k: up(v, t) for k, v in inp["img"].items()}
+        step_blocks.append(lambda: dit.block_forward(shape, wt, wi, cond, pos, x_txt, x_img, y_txt, y_img, ws))
+    else:
+        # the full step: n_double double-stream blocks, then n_single single-stream blocks over [txt; img]
+        shape32 = dit.Shape(**{**shape.__dict__, "x_dtype": dit.DIT_F32})
+        state = torch.empty(cfg.n_tok, cfg.d, dtype=torch.float32, device=dev)
+        st_t, st_i = state[:cfg.n_txt], state[cfg.n_txt:]
+        for b in range(cfg.n_double):
+            bi = di.double_block_inputs(cfg, seed=args.seed, block=b)
+            wt = {k: up(v, t) for k, v in bi["txt"].items()}
+            wi = {k: up(v, t) for k, v in bi["img"].items()}
+            if b == 0:
+                step_blocks.append(lambda wt=wt, wi=wi: dit.block_forward(shape, wt, wi, cond, pos, x_txt, x_img,
+                                                                          st_t, st_i, ws))
+            else:
+                step_blocks.append(lambda wt=wt, wi=wi: dit.block_forward(shape32, wt, wi, cond, pos, st_t, st_i,
+                                                                          st_t, st_i, ws))
+        for b in range(cfg.n_single):
+            w = {k: up(v, t) for k, v in di.single_weights(cfg, args.seed, cfg.n_double + b).items()}
+            step_blocks.append(lambda w=w: dit.single_block_forward(shape32, w, cond, pos, state, state, ws))
+    setup_s = time.time() - t0
+
+    def step():
+        for f in step_blocks:
+            f()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    flops = cfg.flops_step()
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    # per-kernel durations: HIP events around every launch of the library, same stream
+    dit.timing_begin(args.steps * 16 * len(step_blocks))
+    for _ in range(args.steps):
+        step()
+    dit.timing_end()
+    torch.cuda.synchronize()
+    kt = dit.timing_read()
+    kernels = {}
+    for name, (cnt, tot) in kt.items():
+        avg = tot / cnt
+        fl, by, bound = kernel_work(cfg, name)
+        e = {"launches_per_step": cnt / args.steps, "avg_ms": round(avg, 5),
+             "share": round(tot / sum(v[1] for v in kt.values()), 4), "bound": bound}
+        if fl:
+            e["tflops"] = round(fl / (avg * 1e-3) / 1e12, 1)
+            e["frac_mfma"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+        if by:
+            e["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
+            e["frac_hbm"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[name] = e
+    dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
+    fl, by, bound = kernel_work(cfg, dom)
+    avg = kt[dom][1] / kt[dom][0]
+    if fl:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(fl / (avg * 1e-3) / 1e12, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(by / (avg * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if t == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "blocks": cfg.n_double + cfg.n_single, "d": cfg.d, "heads": cfg.n_heads,
+                   "ffn_inner": cfg.ffn_inner, "n_txt": cfg.n_txt, "n_img": cfg.n_img, "tokens": cfg.n_tok,
+                   "gflop_per_step": round(flops / 1e9, 1)},
+        "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "ms_per_step_hip_events": round(ev_ms, 4),
+        "roofline": roof,
+        "kernels": kernels,
+        "setup_s": round(setup_s, 1),
+    }
+
+    if not args.no_cpu_baseline and cfg.n_single == 0:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, inp):
+    """The fp64 oracle, as it stands, on one full block of the same workload."""
+    from oracle import dit_oracle as o
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = os.cpu_count()
+    t0 = time.perf_counter()
+    o.double_block(cfg, inp)
+    dt = time.perf_counter() - t0
+    return {"value": round(cfg.flops_double() / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "sample": f"one full double block of {cfg.name} in float64 (numpy, {dt:.1f} s)",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

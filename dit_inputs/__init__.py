@@ -25,7 +25,9 @@ row r, column c (row-major raster, token index n_txt + r*W + c) -> (0, r, c, 0).
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field, replace
+import concurrent.futures as _cf
+import os as _os
+from dataclasses import dataclass, replace
 from typing import Dict, Optional, Tuple
 
 import numpy as np
@@ -176,30 +178,50 @@ def _qk_norm_weights(cfg: BlockConfig, seed: int, block: int, stream: str, mode:
     return a if cfg.dtype == "f32" else bf16_bits_from_f32(a)
 
 
+_POOL = None
+
+
+def _pool():
+    """Thread pool for independent draws (numpy's generators release the GIL)."""
+    global _POOL
+    if _POOL is None:
+        n = min(16, max(1, len(_os.sched_getaffinity(0))))
+        _POOL = _cf.ThreadPoolExecutor(max_workers=n)
+    return _POOL
+
+
+def _draw_many(specs) -> Dict[str, np.ndarray]:
+    """specs: {key: (shape, std, dtype, seed, name, block, stream)} drawn concurrently."""
+    futs = {k: _pool().submit(draw, *v) for k, v in specs.items()}
+    return {k: f.result() for k, f in futs.items()}
+
+
 def stream_weights(cfg: BlockConfig, seed: int, block: int, stream: str,
                    qk_norm: str = "ones", std: float = 0.02) -> Dict[str, np.ndarray]:
     """Weights of one stream of a double block; Linear weights are [out, in]."""
     d, f, dc, t = cfg.d, cfg.ffn_inner, cfg.dc, cfg.dtype
-    return {
-        "w_mod": draw((6 * d, dc), std, t, seed, "w_mod", block, stream),
-        "w_qkv": draw((3 * d, d), std, t, seed, "w_qkv", block, stream),
-        "qk_norm_w": _qk_norm_weights(cfg, seed, block, stream, qk_norm),
-        "w_o": draw((d, d), std, t, seed, "w_o", block, stream),
-        "w_ffn_in": draw((2 * f, d), std, t, seed, "w_ffn_in", block, stream),
-        "w_ffn_out": draw((d, f), std, t, seed, "w_ffn_out", block, stream),
-    }
+    out = _draw_many({
+        "w_mod": ((6 * d, dc), std, t, seed, "w_mod", block, stream),
+        "w_qkv": ((3 * d, d), std, t, seed, "w_qkv", block, stream),
+        "w_o": ((d, d), std, t, seed, "w_o", block, stream),
+        "w_ffn_in": ((2 * f, d), std, t, seed, "w_ffn_in", block, stream),
+        "w_ffn_out": ((d, f), std, t, seed, "w_ffn_out", block, stream),
+    })
+    out["qk_norm_w"] = _qk_norm_weights(cfg, seed, block, stream, qk_norm)
+    return out
 
 
 def single_weights(cfg: BlockConfig, seed: int, block: int, qk_norm: str = "ones",
                    std: float = 0.02) -> Dict[str, np.ndarray]:
     """Weights of a single-stream block: W1 rows [q|k|v|gate|up], W2 input [O|f]."""
     d, f, dc, t = cfg.d, cfg.ffn_inner, cfg.dc, cfg.dtype
-    return {
-        "w_mod": draw((3 * d, dc), std, t, seed, "w_mod", block, "single"),
-        "w_1": draw((3 * d + 2 * f, d), std, t, seed, "w_1", block, "single"),
-        "qk_norm_w": _qk_norm_weights(cfg, seed, block, "single", qk_norm),
-        "w_2": draw((d, d + f), std, t, seed, "w_2", block, "single"),
-    }
+    out = _draw_many({
+        "w_mod": ((3 * d, dc), std, t, seed, "w_mod", block, "single"),
+        "w_1": ((3 * d + 2 * f, d), std, t, seed, "w_1", block, "single"),
+        "w_2": ((d, d + f), std, t, seed, "w_2", block, "single"),
+    })
+    out["qk_norm_w"] = _qk_norm_weights(cfg, seed, block, "single", qk_norm)
+    return out
 
 
 def activation_inputs(cfg: BlockConfig, seed: int) -> Dict[str, np.ndarray]:

@@ -1,0 +1,241 @@
+/*
+ * dit.h -- C ABI of the MI355X (gfx950) forward pass of a FLUX-style joint
+ * text+image DiT transformer block.
+ *
+ * The block (antirez/iris.c issue #15, "CUDA codepath !"): the transformer of
+ * the FLUX Klein image model, whose operations are the QKV projections, the
+ * FFN and the attention scores (matrix products) plus RMSNorm, RoPE, AdaLN
+ * modulation, softmax and activations (ServeurpersoCom's reply on the
+ * cuBLAS / custom-kernel split); its RoPE has 4 axes of [32, 32, 32, 32] dims
+ * with separate text and image positions (the GGML update, item 3); and it is
+ * "AdaLN + custom RoPE + joint attention" (the GGML update's bottom line).
+ * The remaining conventions are FLUX's and are stated per call below.
+ *
+ * Conventions shared by every call
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller allocates
+ *    and frees every buffer; the library keeps no device memory and no caches.
+ *  - Every call enqueues its kernels on `stream` (a hipStream_t; NULL = the
+ *    default stream), returns without synchronising, allocates nothing and
+ *    never writes an input buffer.
+ *  - Matrices are row-major.  Linear weights are [out, in], so y = x W^T.
+ *    `ld*` arguments are row strides in ELEMENTS.
+ *  - dtype: DIT_BF16 (bf16 storage, fp32 accumulation) or DIT_F32 (fp32
+ *    storage and arithmetic, no reduced-precision matrix math).
+ *  - Alignment: every pointer 16-byte aligned, every row stride a multiple of
+ *    16 bytes.
+ *  - Errors: arguments are validated on the host before any launch.  On a
+ *    failed check the call returns a dit_status code, sets the thread-local
+ *    message returned by dit_last_error() and launches nothing.  A HIP launch
+ *    error after validation returns DIT_ERR_HIP.  No call aborts or throws.
+ *  - Threading: reentrant; the only state is thread-local (error text,
+ *    launch counter, kernel timing).
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIT_ABI_VERSION 1
+
+enum dit_dtype { DIT_F32 = 0, DIT_BF16 = 1 };
+
+enum dit_status {
+    DIT_OK = 0,
+    DIT_ERR_INVALID_ARG = 1,   /* null / misaligned pointer, bad size or stride */
+    DIT_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. head_dim != 128) */
+    DIT_ERR_WORKSPACE = 3,     /* workspace smaller than dit_block_workspace_size() */
+    DIT_ERR_HIP = 4            /* a HIP runtime call failed */
+};
+
+/*
+ * AdaLN modulation (the thread's "AdaLN modulation" kernel).
+ *
+ *   mod_out = W_mod . SiLU(cond)                       [n_chunks * d] fp32
+ *   x_out   = (1 + mod[scale_chunk]) * RMSNorm(x) + mod[shift_chunk]
+ *
+ * RMSNorm(x) = x / sqrt(mean_j x_j^2 + eps) over the d features of a row
+ * (no learnable weight).  Chunk c of mod_out is mod_out[c*d .. c*d + d - 1];
+ * the FLUX order is shift, scale, gate (twice for a double-stream block).
+ *
+ *  dtype     storage type of cond, w_mod and x_out
+ *  cond      [d_cond]
+ *  w_mod     [n_chunks * d, d_cond]
+ *  mod_out   [n_chunks * d] fp32
+ *  x         optional, [n_tok rows, stride ld_x] of x_dtype (DIT_BF16 or
+ *            DIT_F32 for a bf16 call, DIT_F32 for an fp32 call).  NULL: only
+ *            mod_out is computed.
+ *  x_out     [n_tok rows, stride ld_out] of dtype; must not overlap x.
+ * Limits: 8 <= d <= 8192, d % 8 == 0, 8 <= d_cond <= 16384, d_cond % 8 == 0, n_tok >= 0.
+ */
+int dit_adaln_modulate(int dtype, void* stream,
+                       const void* cond, int d_cond,
+                       const void* w_mod, int n_chunks, int d,
+                       float* mod_out,
+                       const void* x, int x_dtype, int n_tok, long ld_x,
+                       int shift_chunk, int scale_chunk, float eps,
+                       void* x_out, long ld_out);
+
+/*
+ * Per-head QK RMSNorm followed by 4-axis RoPE, in place
+ * (the thread's "RMSNorm" and "RoPE" kernels; RoPE as in the GGML update,
+ * item 3).
+ *
+ * For every token n and head h, with u = q[n, h*128 .. h*128+127]:
+ *   u <- u / sqrt(mean(u^2) + eps) * w_q          (w_k for k)
+ *   then every interleaved pair (u[2p], u[2p+1]) is rotated by +phi:
+ *   (a, b) -> (a cos phi - b sin phi, a sin phi + b cos phi),
+ *   phi = pos[n, ax] * theta^(-2j / axes_dim[ax]) for pair j of axis ax,
+ *   axis ax owning dims [sum(axes_dim[:ax]), + axes_dim[ax]).
+ *
+ *  q, k      [n_tok rows, stride ld_q / ld_k], n_heads*head_dim columns each
+ *            (may be column views of one qkv buffer)
+ *  qk_w      [2 sets][2 (q, k)][head_dim] of dtype: rows n < n_first use set
+ *            0 (text), the others set 1 (image).  If n_first >= n_tok only
+ *            set 0 is read.
+ *  pos       int32 [n_tok, n_axes]
+ *  axes_dim  (host) [n_axes], each even, summing to head_dim
+ * Limits: head_dim == 128, 1 <= n_axes <= 4, n_heads >= 1, n_tok >= 0.
+ */
+int dit_qk_rmsnorm_rope(int dtype, void* stream,
+                        void* q, long ld_q, void* k, long ld_k,
+                        int n_tok, int n_heads, int head_dim,
+                        const void* qk_w, int n_first, float eps,
+                        const int32_t* pos, int n_axes, const int* axes_dim, float theta);
+
+/*
+ * Joint softmax attention over all n_tok tokens (text and image in one
+ * softmax, no mask, not causal) -- the thread's "attention scores" product
+ * and "softmax" kernel, here fused (flash style: the scores are never
+ * stored).
+ *
+ *   O_h = softmax(Q_h K_h^T * softmax_scale) V_h       for every head h
+ *
+ *  q, k, v   [n_tok rows, stride ld_q/ld_k/ld_v]; head h = columns
+ *            h*head_dim .. h*head_dim + head_dim - 1
+ *  o         [n_tok rows, stride ld_o] of dtype; must not overlap q, k, v
+ *  softmax_scale  usually 1/sqrt(head_dim)
+ * Limits: head_dim == 128, n_heads >= 1, n_tok >= 0.
+ */
+int dit_joint_attention(int dtype, void* stream,
+                        const void* q, long ld_q, const void* k, long ld_k,
+                        const void* v, long ld_v,
+                        void* o, long ld_o, int n_tok, int n_heads, int head_dim,
+                        float softmax_scale);
+
+/* Shapes and constants of one block. */
+typedef struct dit_block_config {
+    int dtype;          /* DIT_BF16 or DIT_F32: weights and inner activations */
+    int x_dtype;        /* storage of the block input x (residual stream) */
+    int y_dtype;        /* storage of the block output y */
+    int d;              /* hidden size = n_heads * head_dim */
+    int n_heads;
+    int head_dim;       /* must be 128 */
+    int ffn_inner;      /* F, SwiGLU inner width; multiple of 128 */
+    int d_cond;         /* conditioning vector length; multiple of 8 */
+    int n_txt;          /* text tokens (first in the joint sequence) */
+    int n_img;          /* image tokens */
+    float eps;          /* pre-norm RMSNorm epsilon */
+    float eps_qk;       /* QK-norm epsilon */
+    float theta;        /* RoPE base (1e4 for FLUX) */
+    int n_axes;         /* RoPE axes (4) */
+    int axes_dim[4];    /* dims per axis ({32,32,32,32}) */
+} dit_block_config;
+
+/* Weights of one stream of a double-stream block ([out, in], dtype). */
+typedef struct dit_stream_weights {
+    const void* w_mod;      /* [6d, d_cond]: shift1, scale1, gate1, shift2, scale2, gate2 */
+    const void* w_qkv;      /* [3d, d]: rows q | k | v, head-major inside each */
+    const void* qk_norm_w;  /* [2][head_dim]: q weight, k weight */
+    const void* w_o;        /* [d, d] */
+    const void* w_ffn_in;   /* [2F, d]: rows 0..F-1 gate (SiLU), F..2F-1 up */
+    const void* w_ffn_out;  /* [d, F] */
+} dit_stream_weights;
+
+/* Weights of a single-stream block (fused parallel attention + SwiGLU MLP). */
+typedef struct dit_single_weights {
+    const void* w_mod;      /* [3d, d_cond]: shift, scale, gate */
+    const void* w_1;        /* [3d + 2F, d]: rows q | k | v | gate | up */
+    const void* qk_norm_w;  /* [2][head_dim]: q weight, k weight */
+    const void* w_2;        /* [d, d + F]: input columns [O | f] */
+} dit_single_weights;
+
+/* Workspace bytes needed by dit_block_forward (single_stream = 0) or
+ * dit_single_block_forward (single_stream = 1).  (host) cfg.  Returns 0 for
+ * an invalid config (see dit_last_error()). */
+size_t dit_block_workspace_size(const dit_block_config* cfg, int single_stream);
+
+/*
+ * Double-stream block forward (text and image streams with their own weights,
+ * one joint attention):
+ *   m_s = W_mod,s SiLU(c);  a_s = (1+scale1) RMSNorm(x_s) + shift1
+ *   [q|k|v]_s = a_s W_qkv,s^T;  q,k <- RoPE(RMSNorm_head(.) * w_{q,k},s)
+ *   O = joint attention over [text; image];  h_s = x_s + gate1 (O_s W_o,s^T)
+ *   b_s = (1+scale2) RMSNorm(h_s) + shift2;  [g|u] = b_s W_in,s^T
+ *   y_s = h_s + gate2 ((SiLU(g) * u) W_down,s^T)
+ * Storage: the AdaLN vectors and h are fp32; a, qkv, O, b and f are dtype;
+ * x is x_dtype and y is y_dtype.
+ *
+ *  cfg, txt, img (host)
+ *  cond      [d_cond] of dtype (shared by both streams)
+ *  pos       int32 [n_txt + n_img, n_axes], text tokens first
+ *  x_txt     [n_txt, d], x_img [n_img, d] of x_dtype (contiguous rows)
+ *  y_txt     [n_txt, d], y_img [n_img, d] of y_dtype; y may alias x when
+ *            x_dtype == y_dtype, otherwise must not overlap it
+ *  workspace >= dit_block_workspace_size(cfg, 0) bytes, scratch (never
+ *            zeroed, contents undefined afterwards); must not overlap any
+ *            other argument.  Calls sharing a workspace must be ordered on
+ *            one stream.
+ */
+int dit_block_forward(const dit_block_config* cfg,
+                      const dit_stream_weights* txt, const dit_stream_weights* img,
+                      const void* cond, const int32_t* pos,
+                      const void* x_txt, const void* x_img, void* y_txt, void* y_img,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Single-stream block forward over the concatenated sequence x = [text; image]:
+ *   m = W_mod SiLU(c);  a = (1+scale) RMSNorm(x) + shift
+ *   [q|k|v|g|u] = a W_1^T;  q,k <- RoPE(RMSNorm_head(.) * w_{q,k})
+ *   O = joint attention;  y = x + gate ([O | SiLU(g) * u] W_2^T)
+ *  x, y      [n_txt + n_img, d] of x_dtype / y_dtype; aliasing as above
+ *  Other arguments as for dit_block_forward (one qk_norm_w set).
+ */
+int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weights* w,
+                             const void* cond, const int32_t* pos,
+                             const void* x, void* y,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/* Thread-local text of the last error of this thread (never NULL). */
+const char* dit_last_error(void);
+
+/* Thread-local count of kernels this thread has launched successfully (a test
+ * hook: a parity test checks that the GPU path really ran). */
+uint64_t dit_launch_count(void);
+
+/* DIT_ABI_VERSION of the built library. */
+int dit_abi_version(void);
+
+/*
+ * Kernel timing for measurement tools.  dit_timing_begin(capacity) makes the
+ * calling thread bracket each of its next `capacity` launches with a pair of
+ * HIP events recorded on the launch stream (the events are created here, not
+ * per launch).  dit_timing_end() stops recording.  dit_timing_read(i, ...)
+ * waits for the recorded events and reports, for the i-th distinct kernel
+ * seen, its name, its number of launches and the sum of their durations in
+ * milliseconds; it returns the number of distinct kernels, or -1 on error.
+ * name_buf (host) receives a NUL-terminated name of at most name_len bytes.
+ */
+int dit_timing_begin(int capacity);
+int dit_timing_end(void);
+int dit_timing_read(int i, char* name_buf, int name_len, int* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_H */

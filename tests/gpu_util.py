@@ -1,0 +1,59 @@
+"""Helpers for the GPU parity tests: move the generator's storage bits to the GPU,
+bring results back as float64, and the parity metric max|gpu - oracle| / RMS(oracle)."""
+import sys
+
+import numpy as np
+import torch
+
+import dit_inputs as di
+
+
+def dev(a, dtype: str):
+    """numpy storage (bf16 bits as uint16, float32, int32) -> cuda tensor with the same bits."""
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    if dtype == "f32":
+        return torch.from_numpy(a.astype(np.float32, copy=False)).cuda()
+    if dtype == "i32":
+        return torch.from_numpy(a.astype(np.int32, copy=False)).cuda()
+    raise ValueError(dtype)
+
+
+def host(t) -> np.ndarray:
+    """cuda tensor -> float64 numpy (exact widening)."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def tdtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def metric(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max |gpu - oracle| / RMS(oracle)."""
+    rms = float(np.sqrt(np.mean(np.asarray(ref, np.float64) ** 2)))
+    return float(np.max(np.abs(np.asarray(gpu, np.float64) - ref))) / rms
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def upload_stream_weights(w: dict, dtype: str) -> dict:
+    return {k: dev(v, dtype) for k, v in w.items()}
+
+
+def shape_of(cfg: di.BlockConfig, mod, x_dtype=None, y_dtype=None, n_txt=None, n_img=None):
+    """attention_dit_block_amd.Shape for a generator config."""
+    dt = mod.DIT_BF16 if cfg.dtype == "bf16" else mod.DIT_F32
+    return mod.Shape(dtype=dt, d=cfg.d, n_heads=cfg.n_heads, ffn_inner=cfg.ffn_inner,
+                     n_txt=cfg.n_txt if n_txt is None else n_txt, n_img=cfg.n_img if n_img is None else n_img,
+                     d_cond=cfg.dc, x_dtype=dt if x_dtype is None else x_dtype,
+                     y_dtype=mod.DIT_F32 if y_dtype is None else y_dtype, eps=cfg.eps, eps_qk=cfg.eps_qk,
+                     theta=cfg.theta, axes_dim=cfg.axes_dim)

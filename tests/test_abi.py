@@ -1,0 +1,244 @@
+"""The C-ABI library loads, exports every symbol include/dit.h declares, and rejects
+invalid arguments on the host with the documented status, an error text and no
+launch (CPU only: every call here fails validation before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _build_module():
+    import importlib.util
+    path = os.path.join(ROOT, "attention_dit_block_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("dit_build", path)
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+@pytest.fixture(scope="module")
+def dit():
+    b = _build_module()
+    if not os.path.exists(b.LIB):
+        b.build()
+    import attention_dit_block_amd as m
+    return m
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "dit.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dit_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", "dit_block_forward",
+                     "dit_single_block_forward", "dit_block_workspace_size", "dit_last_error",
+                     "dit_launch_count", "dit_abi_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(dit):
+    lib = ctypes.CDLL(dit.library_path)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(dit.EXPORTED) == declared_functions()
+
+
+def test_abi_version(dit):
+    assert dit.abi_version() == 1
+
+
+def _cfg(dit, **kw):
+    s = dit.Shape(dtype=dit.DIT_BF16, d=3072, n_heads=24, ffn_inner=9216, n_txt=512, n_img=4096)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def test_workspace_size_matches_plan(dit):
+    s = _cfg(dit)
+    n, d, F = 4608, 3072, 9216
+
+    def up(x):
+        return (x + 255) // 256 * 256
+    want = up(2 * 6 * d * 4) + up(n * d * 2) + up(n * 3 * d * 2) + up(n * d * 2) + up(n * d * 4) + up(n * F * 2)
+    assert dit.block_workspace_size(s) == want
+    want1 = up(3 * d * 4) + up(n * d * 2) + up(n * 3 * d * 2) + up(n * (d + F) * 2)
+    assert dit.block_workspace_size(s, single_stream=True) == want1
+
+
+@pytest.mark.parametrize("kw, status, text", [
+    (dict(head_dim=64, d=64 * 24), "DIT_ERR_UNSUPPORTED", "head_dim"),
+    (dict(d=3000), "DIT_ERR_INVALID_ARG", "n_heads"),
+    (dict(ffn_inner=9200), "DIT_ERR_INVALID_ARG", "ffn_inner"),
+    (dict(n_txt=0, n_img=0), "DIT_ERR_INVALID_ARG", "token"),
+    (dict(n_txt=-1), "DIT_ERR_INVALID_ARG", "n_txt"),
+    (dict(axes_dim=(32, 32, 32, 30)), "DIT_ERR_INVALID_ARG", "sum"),
+    (dict(axes_dim=(32, 32, 31, 33)), "DIT_ERR_INVALID_ARG", "even"),
+    (dict(theta=0.0), "DIT_ERR_INVALID_ARG", "theta"),
+    (dict(d_cond=3071), "DIT_ERR_INVALID_ARG", "d_cond"),
+    (dict(dtype=0, y_dtype=1), "DIT_ERR_UNSUPPORTED", "fp32"),
+    (dict(eps=-1.0), "DIT_ERR_INVALID_ARG", "eps"),
+])
+def test_invalid_config_rejected(dit, kw, status, text):
+    s = _cfg(dit, **kw)
+    with pytest.raises(dit.DitError) as e:
+        dit.block_workspace_size(s)
+    assert text in str(e.value)
+
+
+class FakeDev:
+    """Stands in for a device tensor: the calls below fail validation before any use."""
+    is_cuda = True
+
+    def __init__(self, addr, shape=(16, 3072), stride=None, dtype=None, esize=2):
+        import torch
+        self.addr, self.shape = addr, shape
+        self._stride = stride or (shape[-1], 1)
+        self.dtype = dtype or torch.bfloat16
+        self._es = esize
+
+    def data_ptr(self):
+        return self.addr
+
+    def dim(self):
+        return len(self.shape)
+
+    def stride(self, i):
+        return self._stride[i]
+
+    def numel(self):
+        n = 1
+        for s in self.shape:
+            n *= s
+        return n
+
+    def element_size(self):
+        return self._es
+
+    def is_contiguous(self):
+        return True
+
+
+def _no_launch(dit, fn):
+    before = dit.launch_count()
+    with pytest.raises(dit.DitError) as e:
+        fn()
+    assert dit.launch_count() == before
+    assert dit.last_error()
+    return e.value
+
+
+def test_attention_validation(dit):
+    import torch
+    q = FakeDev(0x100000)
+    o = FakeDev(0x900000)
+    # misaligned pointer
+    e = _no_launch(dit, lambda: dit.joint_attention(FakeDev(0x100008), q, q, o, n_heads=24, stream=FakeStream()))
+    assert e.status == "DIT_ERR_INVALID_ARG" and "aligned" in str(e)
+    # head_dim other than 128
+    e = _no_launch(dit, lambda: dit.joint_attention(q, q, q, o, n_heads=48, head_dim=64, stream=FakeStream()))
+    assert e.status == "DIT_ERR_UNSUPPORTED"
+    # row stride smaller than the width
+    e = _no_launch(dit, lambda: dit.joint_attention(FakeDev(0x100000, stride=(1024, 1)), q, q, o, n_heads=24,
+                                                    stream=FakeStream()))
+    assert "smaller than the row width" in str(e)
+    # output overlapping the input
+    e = _no_launch(dit, lambda: dit.joint_attention(q, q, q, FakeDev(0x100000 + 4096), n_heads=24,
+                                                    stream=FakeStream()))
+    assert "overlaps" in str(e)
+    # stride not a multiple of 16 bytes
+    e = _no_launch(dit, lambda: dit.joint_attention(FakeDev(0x100000, stride=(3073, 1)), q, q, o, n_heads=24,
+                                                    stream=FakeStream()))
+    assert "16 bytes" in str(e)
+
+
+class FakeStream:
+    cuda_stream = 0
+
+
+def test_rope_validation(dit):
+    import torch
+    q = FakeDev(0x100000, stride=(9216, 1))
+    k = FakeDev(0x100000 + 3072 * 2, stride=(9216, 1))
+    pos = FakeDev(0x800000, shape=(16, 8), dtype=torch.int32, esize=4)
+    w = FakeDev(0x700000, shape=(2, 2, 128))
+    e = _no_launch(dit, lambda: dit.qk_rmsnorm_rope(q, k, 24, w, 16, pos, axes_dim=(32, 32, 32, 34),
+                                                    stream=FakeStream()))
+    assert "sum" in str(e)
+    e = _no_launch(dit, lambda: dit.qk_rmsnorm_rope(q, k, 24, w, 16, pos, axes_dim=(32, 32, 32, 32, 0),
+                                                    stream=FakeStream()))
+    assert e.status == "DIT_ERR_UNSUPPORTED"
+    # q and k overlapping columns of one buffer
+    k2 = FakeDev(0x100000 + 3000 * 2, stride=(9216, 1))
+    e = _no_launch(dit, lambda: dit.qk_rmsnorm_rope(q, k2, 24, w, 16, pos, stream=FakeStream()))
+    assert "overlap" in str(e)
+
+
+def test_adaln_validation(dit):
+    import torch
+    cond = FakeDev(0x100000, shape=(3072,))
+    w = FakeDev(0x200000, shape=(1 << 27,))
+    mod = FakeDev(0x300000, shape=(1 << 16,), dtype=torch.float32, esize=4)
+    x = FakeDev(0x400000, shape=(16, 3072))
+    e = _no_launch(dit, lambda: dit.adaln_modulate(cond, w, 6, 3072, mod, x=x, x_out=FakeDev(0x400000 + 64),
+                                                   stream=FakeStream()))
+    assert "overlaps" in str(e)
+    e = _no_launch(dit, lambda: dit.adaln_modulate(cond, w, 6, 3072, mod, x=x, x_out=FakeDev(0x900000),
+                                                   shift_chunk=6, stream=FakeStream()))
+    assert "chunk" in str(e)
+    e = _no_launch(dit, lambda: dit.adaln_modulate(cond, w, 6, 3076, mod, stream=FakeStream()))
+    assert "multiple of 8" in str(e)
+
+
+def test_block_validation_workspace_and_alias(dit):
+    import torch
+    s = _cfg(dit, n_txt=16, n_img=64, d=256, n_heads=2, ffn_inner=768)
+    need = dit.block_workspace_size(s)
+    wts = {n: FakeDev(0x1000000 * (i + 1), shape=(1 << 20,)) for i, n in enumerate(
+        ("w_mod", "w_qkv", "qk_norm_w", "w_o", "w_ffn_in", "w_ffn_out"))}
+    cond = FakeDev(0x10000000, shape=(256,))
+    pos = FakeDev(0x11000000, shape=(80, 4), dtype=torch.int32, esize=4)
+    xt, xi = FakeDev(0x12000000, shape=(16, 256)), FakeDev(0x13000000, shape=(64, 256))
+    yt, yi = FakeDev(0x14000000, shape=(16, 256)), FakeDev(0x15000000, shape=(64, 256))
+    small = FakeDev(0x20000000, shape=(need - 256,), dtype=torch.uint8, esize=1)
+    e = _no_launch(dit, lambda: dit.block_forward(s, wts, wts, cond, pos, xt, xi, yt, yi, small,
+                                                  stream=FakeStream()))
+    assert e.status == "DIT_ERR_WORKSPACE"
+    ws = FakeDev(0x20000000, shape=(need,), dtype=torch.uint8, esize=1)
+    # y (fp32) partly overlapping x (bf16): not an exact alias of the same dtype
+    e = _no_launch(dit, lambda: dit.block_forward(s, wts, wts, cond, pos, xt, xi, FakeDev(0x12000000 + 256), yi,
+                                                  ws, stream=FakeStream()))
+    assert "alias" in str(e)
+    bad = dict(wts)
+    bad["w_o"] = FakeDev(0x1000004, shape=(1 << 20,))
+    e = _no_launch(dit, lambda: dit.block_forward(s, wts, bad, cond, pos, xt, xi, yt, yi, ws, stream=FakeStream()))
+    assert "img.w_o" in str(e)
+
+
+def test_host_tensor_refused_by_binding(dit):
+    import torch
+    q = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dit.joint_attention(q, q, q, q, n_heads=1, stream=FakeStream())
+
+
+def test_undersized_tensor_refused_by_binding(dit):
+    # the binding refuses buffers smaller than the call would touch
+    q = FakeDev(0x100000, shape=(16, 3072))
+    o = FakeDev(0x900000, shape=(15, 3072))
+    with pytest.raises(ValueError):
+        dit.joint_attention(q, q, q, o, n_heads=24, stream=FakeStream())
+    s = _cfg(dit, n_txt=16, n_img=64, d=256, n_heads=2, ffn_inner=768)
+    wts = {n: FakeDev(0x1000000 * (i + 1), shape=(1 << 20,)) for i, n in enumerate(
+        ("w_mod", "w_qkv", "qk_norm_w", "w_o", "w_ffn_in", "w_ffn_out"))}
+    wts["w_ffn_in"] = FakeDev(0x7000000, shape=(2 * 768 * 256 - 1,))
+    x = FakeDev(0x12000000, shape=(80, 256))
+    with pytest.raises(ValueError):
+        dit.block_forward(s, wts, wts, x, x, x, x, x, x, x, stream=FakeStream())
