@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 
 
 __all__ = [
-    "DIT_F32", "DIT_BF16", "DIT_OK", "DitError", "lib", "library_path",
+    "DIT_F32", "DIT_BF16", "DIT_F16", "DIT_OK", "DitError", "lib", "library_path",
     "BlockConfig", "StreamWeights", "SingleWeights",
     "adaln_modulate", "qk_rmsnorm_rope", "joint_attention",
     "block_workspace_size", "block_forward", "single_block_forward",
@@ -23,7 +23,7 @@ __all__ = [
     "timing_begin", "timing_end", "timing_read",
 ]
 
-DIT_F32, DIT_BF16 = 0, 1
+DIT_F32, DIT_BF16, DIT_F16 = 0, 1, 2
 DIT_OK, DIT_ERR_INVALID_ARG, DIT_ERR_UNSUPPORTED, DIT_ERR_WORKSPACE, DIT_ERR_HIP = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "DIT_OK", 1: "DIT_ERR_INVALID_ARG", 2: "DIT_ERR_UNSUPPORTED",
                 3: "DIT_ERR_WORKSPACE", 4: "DIT_ERR_HIP"}
@@ -37,7 +37,7 @@ _vp, _i, _l, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_fl
 
 
 class BlockConfig(ctypes.Structure):
-    _fields_ = [("dtype", _i), ("x_dtype", _i), ("y_dtype", _i), ("d", _i), ("n_heads", _i),
+    _fields_ = [("dtype", _i), ("act_dtype", _i), ("x_dtype", _i), ("y_dtype", _i), ("d", _i), ("n_heads", _i),
                 ("head_dim", _i), ("ffn_inner", _i), ("d_cond", _i), ("n_txt", _i), ("n_img", _i),
                 ("eps", _f), ("eps_qk", _f), ("theta", _f), ("n_axes", _i), ("axes_dim", _i * 4)]
 
@@ -58,8 +58,9 @@ def _sig(name, res, args):
     return f
 
 
-_adaln = _sig("dit_adaln_modulate", _i, [_i, _vp, _vp, _i, _vp, _i, _i, _vp, _vp, _i, _i, _l, _i, _i, _f, _vp, _l])
-_qkrope = _sig("dit_qk_rmsnorm_rope", _i, [_i, _vp, _vp, _l, _vp, _l, _i, _i, _i, _vp, _i, _f, _vp, _i,
+_adaln = _sig("dit_adaln_modulate", _i, [_i, _vp, _vp, _i, _vp, _i, _i, _vp, _vp, _i, _i, _l, _i, _i, _f, _vp, _i,
+                                         _l])
+_qkrope = _sig("dit_qk_rmsnorm_rope", _i, [_i, _vp, _vp, _l, _vp, _l, _i, _i, _i, _vp, _i, _i, _f, _vp, _i,
                                            ctypes.POINTER(_i), _f])
 _attn = _sig("dit_joint_attention", _i, [_i, _vp, _vp, _l, _vp, _l, _vp, _l, _vp, _l, _i, _i, _i, _f])
 _wsize = _sig("dit_block_workspace_size", _sz, [ctypes.POINTER(BlockConfig), _i])
@@ -147,6 +148,8 @@ def _dt(t) -> int:
         return DIT_BF16
     if t.dtype == torch.float32:
         return DIT_F32
+    if t.dtype == torch.float16:
+        return DIT_F16
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
@@ -163,19 +166,19 @@ def adaln_modulate(cond, w_mod, n_chunks: int, d: int, mod_out, x=None, x_out=No
     """mod_out = W_mod SiLU(cond) (fp32); optionally x_out = (1+scale) RMSNorm(x) + shift."""
     import torch
     dtype = _dt(w_mod)
-    n_tok, ld_x, ld_o, xdt = 0, 0, 0, dtype
+    n_tok, ld_x, ld_o, xdt, odt = 0, 0, 0, dtype, dtype
     _need(w_mod, n_chunks * d * cond.numel(), "w_mod")
     _need(cond, cond.numel(), "cond")
     _need(mod_out, n_chunks * d, "mod_out")
     if x is not None:
         if x_out is None:
             raise ValueError("x_out is required with x")
-        n_tok, ld_x, ld_o, xdt = x.shape[0], _ld(x, "x"), _ld(x_out, "x_out"), _dt(x)
+        n_tok, ld_x, ld_o, xdt, odt = x.shape[0], _ld(x, "x"), _ld(x_out, "x_out"), _dt(x), _dt(x_out)
         _rows(x, n_tok, d, "x")
         _rows(x_out, n_tok, d, "x_out")
     rc = _adaln(dtype, _stream(stream), _ptr(cond, "cond"), cond.numel(), _ptr(w_mod, "w_mod"), n_chunks, d,
                 _ptr(mod_out, "mod_out", torch.float32), _ptr(x, "x"), xdt, n_tok, ld_x, shift_chunk, scale_chunk,
-                eps, _ptr(x_out, "x_out"), ld_o)
+                eps, _ptr(x_out, "x_out"), odt, ld_o)
     _check(rc, "dit_adaln_modulate")
 
 
@@ -191,7 +194,7 @@ def qk_rmsnorm_rope(q, k, n_heads: int, qk_w, n_first: int, pos, eps: float = 1e
     _need(qk_w, (2 if n_first < n else 1) * 2 * head_dim, "qk_w")
     _need(pos, n * len(axes_dim), "pos")
     rc = _qkrope(_dt(q), _stream(stream), _ptr(q, "q"), _ld(q, "q"), _ptr(k, "k"), _ld(k, "k"), q.shape[0],
-                 n_heads, head_dim, _ptr(qk_w, "qk_w"), n_first, eps, _ptr(pos, "pos", torch.int32),
+                 n_heads, head_dim, _ptr(qk_w, "qk_w"), _dt(qk_w), n_first, eps, _ptr(pos, "pos", torch.int32),
                  len(axes_dim), axes, theta)
     _check(rc, "dit_qk_rmsnorm_rope")
 
@@ -211,7 +214,8 @@ def joint_attention(q, k, v, o, n_heads: int, softmax_scale: Optional[float] = N
 
 @dataclass
 class Shape:
-    """Python-side block shape (mirrors dit_block_config)."""
+    """Python-side block shape (mirrors dit_block_config).  act_dtype None: fp16
+    activations for bf16 weights, fp32 for fp32 weights."""
     dtype: int
     d: int
     n_heads: int
@@ -221,6 +225,7 @@ class Shape:
     d_cond: int = 0
     x_dtype: Optional[int] = None
     y_dtype: int = DIT_F32
+    act_dtype: Optional[int] = None
     head_dim: int = 128
     eps: float = 1e-6
     eps_qk: float = 1e-6
@@ -230,6 +235,10 @@ class Shape:
     def c_config(self) -> BlockConfig:
         c = BlockConfig()
         c.dtype = self.dtype
+        if self.act_dtype is not None:
+            c.act_dtype = self.act_dtype
+        else:
+            c.act_dtype = DIT_F16 if self.dtype == DIT_BF16 else DIT_F32
         c.x_dtype = self.dtype if self.x_dtype is None else self.x_dtype
         c.y_dtype = self.y_dtype
         c.d, c.n_heads, c.head_dim, c.ffn_inner = self.d, self.n_heads, self.head_dim, self.ffn_inner

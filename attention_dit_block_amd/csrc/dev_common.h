@@ -4,48 +4,110 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace dit {
 
-typedef uint16_t bf16_t;  // bf16 storage: the raw 16-bit pattern
+typedef uint16_t bf16_t;  // 16-bit storage: the raw bit pattern (bf16 or fp16)
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_v __attribute__((ext_vector_type(8)));
 typedef float f32x2_v __attribute__((ext_vector_type(2)));
 typedef float f32x4_v __attribute__((ext_vector_type(4)));
 typedef float f32x16_v __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
-// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even
-// (v_cvt_pk_bf16_f32 on gfx950).
+template <int DT> struct ESize { static constexpr int v = DT == F32 ? 4 : 2; };
+
+// ---- 16-bit formats <-> fp32.  Widening is exact; narrowing rounds to nearest even
+// (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 on gfx950).
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ float h_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_v, w)[0]; }
+__device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_v, w)[1]; }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     f32x2_v f = {lo, hi};
-    bf16x2_v b = __builtin_convertvector(f, bf16x2_v);
-    return __builtin_bit_cast(uint32_t, b);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
 }
-__device__ __forceinline__ bf16_t f2bf(float f) {
-    return bf16_t(pack_bf16x2(f, 0.0f) & 0xffffu);
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f32x2_v f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_v));
+}
+// Two bf16 values -> the same two values as fp16 (exact for normal fp16 magnitudes; values
+// below 2^-14 become fp16 subnormals, rounded to nearest even).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) { return pack_f16x2(bf_lo(w), bf_hi(w)); }
+
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return DT == F16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+}
+template <int DT>
+__device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi) {
+    if (DT == F16) { lo = h_lo(w); hi = h_hi(w); }
+    else { lo = bf_lo(w); hi = bf_hi(w); }
 }
 
-// Unpack 8 bf16 (one 16-byte load) into fp32.
-__device__ __forceinline__ void unpack8(const u32x4_v& w, float* f) {
+// 16-byte global loads / stores.
+__device__ __forceinline__ u32x4_v ld16(const void* p) { return *reinterpret_cast<const u32x4_v*>(p); }
+__device__ __forceinline__ void st16(void* p, const u32x4_v& v) { *reinterpret_cast<u32x4_v*>(p) = v; }
+__device__ __forceinline__ f32x4_v ldf4(const void* p) { return *reinterpret_cast<const f32x4_v*>(p); }
+__device__ __forceinline__ void stf4(void* p, const f32x4_v& v) { *reinterpret_cast<f32x4_v*>(p) = v; }
+
+// 8 consecutive elements of type DT <-> fp32 (one 16-byte access for 16-bit types, two for fp32).
+template <int DT>
+__device__ __forceinline__ void load8(const char* p, float* f) {
+    if (DT == F32) {
+        const f32x4_v a = ldf4(p), b = ldf4(p + 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf_lo(w[i]);
-        f[2 * i + 1] = bf_hi(w[i]);
+        for (int i = 0; i < 4; ++i) { f[i] = a[i]; f[4 + i] = b[i]; }
+    } else {
+        const u32x4_v w = ld16(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) unpack2<DT>(w[i], f[2 * i], f[2 * i + 1]);
     }
 }
-__device__ __forceinline__ u32x4_v pack8(const float* f) {
-    u32x4_v w;
+template <int DT>
+__device__ __forceinline__ void store8(char* p, const float* f) {
+    if (DT == F32) {
+        f32x4_v a = {f[0], f[1], f[2], f[3]}, b = {f[4], f[5], f[6], f[7]};
+        stf4(p, a);
+        stf4(p + 16, b);
+    } else {
+        u32x4_v w;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
-    return w;
+        for (int i = 0; i < 4; ++i) w[i] = pack2<DT>(f[2 * i], f[2 * i + 1]);
+        st16(p, w);
+    }
+}
+// 4 consecutive elements (8 bytes for 16-bit types, 16 for fp32).
+template <int DT>
+__device__ __forceinline__ void load4(const char* p, float* f) {
+    if (DT == F32) {
+        const f32x4_v a = ldf4(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = a[i];
+    } else {
+        const u32x2_v w = *reinterpret_cast<const u32x2_v*>(p);
+        unpack2<DT>(w[0], f[0], f[1]);
+        unpack2<DT>(w[1], f[2], f[3]);
+    }
+}
+template <int DT>
+__device__ __forceinline__ void store4(char* p, const float* f) {
+    if (DT == F32) {
+        f32x4_v a = {f[0], f[1], f[2], f[3]};
+        stf4(p, a);
+    } else {
+        u32x2_v w = {pack2<DT>(f[0], f[1]), pack2<DT>(f[2], f[3])};
+        *reinterpret_cast<u32x2_v*>(p) = w;
+    }
 }
 
 // Wave-wide reductions (64 lanes).
@@ -61,13 +123,5 @@ __device__ __forceinline__ float group_sum(float v) {
     for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
     return v;
 }
-
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-
-// 16-byte global loads / stores.
-__device__ __forceinline__ u32x4_v ld16(const void* p) { return *reinterpret_cast<const u32x4_v*>(p); }
-__device__ __forceinline__ void st16(void* p, const u32x4_v& v) { *reinterpret_cast<u32x4_v*>(p) = v; }
-__device__ __forceinline__ f32x4_v ldf4(const void* p) { return *reinterpret_cast<const f32x4_v*>(p); }
-__device__ __forceinline__ void stf4(void* p, const f32x4_v& v) { *reinterpret_cast<f32x4_v*>(p) = v; }
 
 }  // namespace dit

@@ -62,8 +62,9 @@ int launch(const char* name, hipStream_t s, F&& fn) {
     } while (0)
 
 // ---- validation helpers ------------------------------------------------------------------------
-size_t esize(int dt) { return dt == DIT_BF16 ? 2 : 4; }
-bool valid_dtype(int dt) { return dt == DIT_BF16 || dt == DIT_F32; }
+size_t esize(int dt) { return dt == DIT_F32 ? 4 : 2; }
+bool valid_dtype(int dt) { return dt == DIT_BF16 || dt == DIT_F32 || dt == DIT_F16; }
+bool valid_wdtype(int dt) { return dt == DIT_BF16 || dt == DIT_F32; }   // weights, cond, x
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_ptr(const void* p, const char* what) {
@@ -99,7 +100,6 @@ int build_rope_table(int head_dim, int n_axes, const int* axes_dim, float theta,
         for (int j = 0; j < dim / 2; ++j, ++p) {
             const double om = std::pow((double)theta, -2.0 * j / dim);
             t.omega_d[p] = om;
-            t.omega[p] = (float)om;
             t.axis[p] = (int8_t)a;
         }
     }
@@ -109,10 +109,14 @@ int build_rope_table(int head_dim, int n_axes, const int* axes_dim, float theta,
 
 int validate_config(const dit_block_config* c) {
     if (!c) return fail(DIT_ERR_INVALID_ARG, "cfg is NULL");
-    if (!valid_dtype(c->dtype) || !valid_dtype(c->x_dtype) || !valid_dtype(c->y_dtype))
-        return fail(DIT_ERR_INVALID_ARG, "dtype / x_dtype / y_dtype must be DIT_F32 or DIT_BF16");
-    if (c->dtype == DIT_F32 && (c->x_dtype != DIT_F32 || c->y_dtype != DIT_F32))
-        return fail(DIT_ERR_UNSUPPORTED, "an fp32 block needs fp32 x and y");
+    if (!valid_wdtype(c->dtype) || !valid_wdtype(c->x_dtype) || !valid_wdtype(c->y_dtype) ||
+        !valid_dtype(c->act_dtype))
+        return fail(DIT_ERR_INVALID_ARG, "dtype / x_dtype / y_dtype must be DIT_F32 or DIT_BF16, act_dtype one of "
+                                         "DIT_F32, DIT_BF16, DIT_F16");
+    if (c->dtype == DIT_F32 && (c->x_dtype != DIT_F32 || c->y_dtype != DIT_F32 || c->act_dtype != DIT_F32))
+        return fail(DIT_ERR_UNSUPPORTED, "an fp32 block needs fp32 activations, x and y");
+    if (c->dtype == DIT_BF16 && c->act_dtype == DIT_F32)
+        return fail(DIT_ERR_UNSUPPORTED, "bf16 weights need DIT_F16 or DIT_BF16 activations");
     if (c->head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim = %d (only 128 is supported)", c->head_dim);
     if (c->n_heads < 1 || c->d != c->n_heads * c->head_dim)
         return fail(DIT_ERR_INVALID_ARG, "d = %d must equal n_heads * head_dim = %d * %d", c->d, c->n_heads, c->head_dim);
@@ -135,7 +139,7 @@ struct WsPlan {
 };
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 WsPlan plan_workspace(const dit_block_config* c, int single) {
-    const size_t n = (size_t)c->n_txt + c->n_img, d = c->d, F = c->ffn_inner, es = esize(c->dtype);
+    const size_t n = (size_t)c->n_txt + c->n_img, d = c->d, F = c->ffn_inner, es = esize(c->act_dtype);
     WsPlan p{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
@@ -167,9 +171,9 @@ int dit_abi_version(void) { return DIT_ABI_VERSION; }
 
 int dit_adaln_modulate(int dtype, void* stream, const void* cond, int d_cond, const void* w_mod, int n_chunks,
                        int d, float* mod_out, const void* x, int x_dtype, int n_tok, long ld_x, int shift_chunk,
-                       int scale_chunk, float eps, void* x_out, long ld_out) {
+                       int scale_chunk, float eps, void* x_out, int out_dtype, long ld_out) {
     clear_err();
-    if (!valid_dtype(dtype)) return fail(DIT_ERR_INVALID_ARG, "dtype %d", dtype);
+    if (!valid_wdtype(dtype)) return fail(DIT_ERR_INVALID_ARG, "dtype %d (DIT_BF16 or DIT_F32)", dtype);
     DIT_TRY(check_ptr(cond, "cond"));
     DIT_TRY(check_ptr(w_mod, "w_mod"));
     DIT_TRY(check_ptr(mod_out, "mod_out"));
@@ -179,8 +183,10 @@ int dit_adaln_modulate(int dtype, void* stream, const void* cond, int d_cond, co
     if (n_chunks < 1) return fail(DIT_ERR_INVALID_ARG, "n_chunks = %d", n_chunks);
     if ((long)n_chunks * d > (1L << 30)) return fail(DIT_ERR_UNSUPPORTED, "n_chunks * d too large");
     if (x) {
-        if (!valid_dtype(x_dtype)) return fail(DIT_ERR_INVALID_ARG, "x_dtype %d", x_dtype);
-        if (dtype == DIT_F32 && x_dtype != DIT_F32) return fail(DIT_ERR_UNSUPPORTED, "fp32 call needs fp32 x");
+        if (!valid_wdtype(x_dtype)) return fail(DIT_ERR_INVALID_ARG, "x_dtype %d (DIT_BF16 or DIT_F32)", x_dtype);
+        if (!valid_dtype(out_dtype)) return fail(DIT_ERR_INVALID_ARG, "out_dtype %d", out_dtype);
+        if (dtype == DIT_F32 && (x_dtype != DIT_F32 || out_dtype != DIT_F32))
+            return fail(DIT_ERR_UNSUPPORTED, "an fp32 call needs fp32 x and x_out");
         if (n_tok < 0) return fail(DIT_ERR_INVALID_ARG, "n_tok = %d", n_tok);
         if (shift_chunk < 0 || shift_chunk >= n_chunks || scale_chunk < 0 || scale_chunk >= n_chunks)
             return fail(DIT_ERR_INVALID_ARG, "shift_chunk / scale_chunk out of [0, n_chunks)");
@@ -188,8 +194,8 @@ int dit_adaln_modulate(int dtype, void* stream, const void* cond, int d_cond, co
         DIT_TRY(check_ptr(x, "x"));
         DIT_TRY(check_ptr(x_out, "x_out"));
         DIT_TRY(check_ld(ld_x, d, x_dtype, "ld_x"));
-        DIT_TRY(check_ld(ld_out, d, dtype, "ld_out"));
-        if (overlap(range_of(x, n_tok, ld_x, d, x_dtype), range_of(x_out, n_tok, ld_out, d, dtype)))
+        DIT_TRY(check_ld(ld_out, d, out_dtype, "ld_out"));
+        if (overlap(range_of(x, n_tok, ld_x, d, x_dtype), range_of(x_out, n_tok, ld_out, d, out_dtype)))
             return fail(DIT_ERR_INVALID_ARG, "x_out overlaps x");
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -207,17 +213,18 @@ int dit_adaln_modulate(int dtype, void* stream, const void* cond, int d_cond, co
         m.n = 1;
         m.d = d;
         m.eps = eps;
-        m.dtype = dtype;
+        m.out_dtype = out_dtype;
         DIT_TRY(launch("modulate", s, [&] { return launch_modulate(m, s); }));
     }
     return DIT_OK;
 }
 
 int dit_qk_rmsnorm_rope(int dtype, void* stream, void* q, long ld_q, void* k, long ld_k, int n_tok, int n_heads,
-                        int head_dim, const void* qk_w, int n_first, float eps, const int32_t* pos, int n_axes,
-                        const int* axes_dim, float theta) {
+                        int head_dim, const void* qk_w, int w_dtype, int n_first, float eps, const int32_t* pos,
+                        int n_axes, const int* axes_dim, float theta) {
     clear_err();
     if (!valid_dtype(dtype)) return fail(DIT_ERR_INVALID_ARG, "dtype %d", dtype);
+    if (!valid_dtype(w_dtype)) return fail(DIT_ERR_INVALID_ARG, "w_dtype %d", w_dtype);
     if (head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim = %d (only 128 is supported)", head_dim);
     if (n_heads < 1) return fail(DIT_ERR_INVALID_ARG, "n_heads = %d", n_heads);
     if (n_tok < 0) return fail(DIT_ERR_INVALID_ARG, "n_tok = %d", n_tok);
@@ -244,7 +251,8 @@ int dit_qk_rmsnorm_rope(int dtype, void* stream, void* q, long ld_q, void* k, lo
     a.q = q; a.ld_q = ld_q; a.k = k; a.ld_k = ld_k;
     a.n_tok = n_tok; a.n_heads = n_heads; a.n_first = n_first; a.eps = eps;
     a.qk_w0 = qk_w;
-    a.qk_w1 = reinterpret_cast<const char*>(qk_w) + (n_first < n_tok ? 2 * (size_t)head_dim * esize(dtype) : 0);
+    a.qk_w1 = reinterpret_cast<const char*>(qk_w) + (n_first < n_tok ? 2 * (size_t)head_dim * esize(w_dtype) : 0);
+    a.w_dtype = w_dtype;
     a.pos = pos; a.n_axes = n_axes; a.dtype = dtype;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     return launch("qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(a, s); });
@@ -333,7 +341,7 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
     char* ob = ws + W.o;
     float* h = reinterpret_cast<float*>(ws + W.h);
     char* f = ws + W.f;
-    const size_t es = esize(c.dtype), xs = esize(c.x_dtype);
+    const size_t es = esize(c.act_dtype);     // activation element size
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
     // 1. AdaLN vectors of both streams
@@ -351,16 +359,16 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
     int nm = 0;
     if (nt) m.p[nm++] = {x_txt, d, c.x_dtype, act, d, mod_t + 0 * d, mod_t + 1 * (size_t)d, nt};
     if (ni) m.p[nm++] = {x_img, d, c.x_dtype, act + (size_t)nt * d * es, d, mod_i + 0 * d, mod_i + 1 * (size_t)d, ni};
-    m.n = nm; m.d = d; m.eps = c.eps; m.dtype = c.dtype;
+    m.n = nm; m.d = d; m.eps = c.eps; m.out_dtype = c.act_dtype;
     DIT_TRY(launch("modulate_x", s, [&] { return launch_modulate(m, s); }));
 
     // 3. qkv = a W_qkv^T
     GemmBatch gq{};
-    gq.dtype = c.dtype;
+    gq.a_dtype = c.act_dtype;
     {
         int k = 0;
-        if (nt) gq.p[k++] = {act, d, txt->w_qkv, d, qkv, 3L * d, c.dtype, nullptr, 0, 0, nullptr, 0, nt, 3 * d, d, EPI_STORE};
-        if (ni) gq.p[k++] = {act + (size_t)nt * d * es, d, img->w_qkv, d, qkv + (size_t)nt * 3 * d * es, 3L * d, c.dtype,
+        if (nt) gq.p[k++] = {act, d, txt->w_qkv, d, qkv, 3L * d, c.act_dtype, nullptr, 0, 0, nullptr, 0, nt, 3 * d, d, EPI_STORE};
+        if (ni) gq.p[k++] = {act + (size_t)nt * d * es, d, img->w_qkv, d, qkv + (size_t)nt * 3 * d * es, 3L * d, c.act_dtype,
                              nullptr, 0, 0, nullptr, 0, ni, 3 * d, d, EPI_STORE};
         gq.n = k;
     }
@@ -371,17 +379,17 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
     DIT_TRY(build_rope_table(c.head_dim, c.n_axes, c.axes_dim, c.theta, r.tab));
     r.q = qkv; r.ld_q = 3L * d; r.k = qkv + (size_t)d * es; r.ld_k = 3L * d;
     r.n_tok = n; r.n_heads = c.n_heads; r.qk_w0 = txt->qk_norm_w; r.qk_w1 = img->qk_norm_w; r.n_first = nt;
-    r.eps = c.eps_qk; r.pos = pos; r.n_axes = c.n_axes; r.dtype = c.dtype;
+    r.eps = c.eps_qk; r.pos = pos; r.n_axes = c.n_axes; r.dtype = c.act_dtype; r.w_dtype = c.dtype;
     DIT_TRY(launch("qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(r, s); }));
 
     // 5. O = joint attention over all n tokens
     AttnArgs at{qkv, 3L * d, qkv + (size_t)d * es, 3L * d, qkv + (size_t)2 * d * es, 3L * d, ob, d, n, c.n_heads,
-                1.0f / std::sqrt((float)c.head_dim), c.dtype};
+                1.0f / std::sqrt((float)c.head_dim), c.act_dtype};
     DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
 
     // 6. h = x + gate1 * (O W_o^T)   (fp32)
     GemmBatch go{};
-    go.dtype = c.dtype;
+    go.a_dtype = c.act_dtype;
     {
         int k = 0;
         if (nt) go.p[k++] = {ob, d, txt->w_o, d, h, d, DIT_F32, x_txt, d, c.x_dtype, mod_t + 2 * (size_t)d, 0, nt, d, d,
@@ -398,16 +406,16 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
     if (nt) m2.p[nm++] = {h, d, DIT_F32, act, d, mod_t + 3 * (size_t)d, mod_t + 4 * (size_t)d, nt};
     if (ni) m2.p[nm++] = {h + (size_t)nt * d, d, DIT_F32, act + (size_t)nt * d * es, d, mod_i + 3 * (size_t)d,
                           mod_i + 4 * (size_t)d, ni};
-    m2.n = nm; m2.d = d; m2.eps = c.eps; m2.dtype = c.dtype;
+    m2.n = nm; m2.d = d; m2.eps = c.eps; m2.out_dtype = c.act_dtype;
     DIT_TRY(launch("modulate_h", s, [&] { return launch_modulate(m2, s); }));
 
     // 8. f = SiLU(b W_gate^T) * (b W_up^T)
     GemmBatch gf{};
-    gf.dtype = c.dtype;
+    gf.a_dtype = c.act_dtype;
     {
         int k = 0;
-        if (nt) gf.p[k++] = {act, d, txt->w_ffn_in, d, f, F, c.dtype, nullptr, 0, 0, nullptr, F, nt, F, d, EPI_SWIGLU};
-        if (ni) gf.p[k++] = {act + (size_t)nt * d * es, d, img->w_ffn_in, d, f + (size_t)nt * F * es, F, c.dtype, nullptr,
+        if (nt) gf.p[k++] = {act, d, txt->w_ffn_in, d, f, F, c.act_dtype, nullptr, 0, 0, nullptr, F, nt, F, d, EPI_SWIGLU};
+        if (ni) gf.p[k++] = {act + (size_t)nt * d * es, d, img->w_ffn_in, d, f + (size_t)nt * F * es, F, c.act_dtype, nullptr,
                              0, 0, nullptr, F, ni, F, d, EPI_SWIGLU};
         gf.n = k;
     }
@@ -415,7 +423,7 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
 
     // 9. y = h + gate2 * (f W_down^T)
     GemmBatch gd{};
-    gd.dtype = c.dtype;
+    gd.a_dtype = c.act_dtype;
     {
         int k = 0;
         if (nt) gd.p[k++] = {f, F, txt->w_ffn_out, F, y_txt, d, c.y_dtype, h, d, DIT_F32, mod_t + 5 * (size_t)d, 0, nt, d,
@@ -425,7 +433,6 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
         gd.n = k;
     }
     DIT_TRY(launch("gemm_ffn_down", s, [&] { return launch_gemm(gd, s); }));
-    (void)xs;
     return DIT_OK;
 }
 
@@ -460,7 +467,7 @@ int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weigh
     char* act = ws + W.act;
     char* qkv = ws + W.qkv;
     char* of = ws + W.of;
-    const size_t es = esize(c.dtype);
+    const size_t es = esize(c.act_dtype);     // activation element size
     const long ldof = (long)d + F;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
@@ -471,15 +478,15 @@ int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weigh
 
     ModBatch m{};
     m.p[0] = {x, d, c.x_dtype, act, d, mod, mod + d, n};
-    m.n = 1; m.d = d; m.eps = c.eps; m.dtype = c.dtype;
+    m.n = 1; m.d = d; m.eps = c.eps; m.out_dtype = c.act_dtype;
     DIT_TRY(launch("modulate_x", s, [&] { return launch_modulate(m, s); }));
 
     // [q|k|v] = a W_1[0:3d]^T  and  f = SiLU(a W_1[3d:3d+F]^T) * (a W_1[3d+F:]^T), written next to O
     GemmBatch g1{};
-    g1.dtype = c.dtype;
-    g1.p[0] = {act, d, w->w_1, d, qkv, 3L * d, c.dtype, nullptr, 0, 0, nullptr, 0, n, 3 * d, d, EPI_STORE};
-    g1.p[1] = {act, d, reinterpret_cast<const char*>(w->w_1) + (size_t)3 * d * d * es, d, of + (size_t)d * es, ldof,
-               c.dtype, nullptr, 0, 0, nullptr, F, n, F, d, EPI_SWIGLU};
+    g1.a_dtype = c.act_dtype;
+    g1.p[0] = {act, d, w->w_1, d, qkv, 3L * d, c.act_dtype, nullptr, 0, 0, nullptr, 0, n, 3 * d, d, EPI_STORE};
+    g1.p[1] = {act, d, reinterpret_cast<const char*>(w->w_1) + (size_t)3 * d * d * esize(c.dtype), d,
+               of + (size_t)d * es, ldof, c.act_dtype, nullptr, 0, 0, nullptr, F, n, F, d, EPI_SWIGLU};
     g1.n = 2;
     DIT_TRY(launch("gemm_linear1", s, [&] { return launch_gemm(g1, s); }));
 
@@ -488,15 +495,15 @@ int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weigh
     r.q = qkv; r.ld_q = 3L * d; r.k = qkv + (size_t)d * es; r.ld_k = 3L * d;
     r.n_tok = n; r.n_heads = c.n_heads; r.qk_w0 = w->qk_norm_w; r.qk_w1 = w->qk_norm_w; r.n_first = n;
     r.eps = c.eps_qk;
-    r.pos = pos; r.n_axes = c.n_axes; r.dtype = c.dtype;
+    r.pos = pos; r.n_axes = c.n_axes; r.dtype = c.act_dtype; r.w_dtype = c.dtype;
     DIT_TRY(launch("qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(r, s); }));
 
     AttnArgs at{qkv, 3L * d, qkv + (size_t)d * es, 3L * d, qkv + (size_t)2 * d * es, 3L * d, of, ldof, n, c.n_heads,
-                1.0f / std::sqrt((float)c.head_dim), c.dtype};
+                1.0f / std::sqrt((float)c.head_dim), c.act_dtype};
     DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
 
     GemmBatch g2{};
-    g2.dtype = c.dtype;
+    g2.a_dtype = c.act_dtype;
     g2.p[0] = {of, ldof, w->w_2, ldof, y, d, c.y_dtype, x, d, c.x_dtype, mod + 2 * (size_t)d, 0, n, d, d + F,
                EPI_GATED_RES};
     g2.n = 1;

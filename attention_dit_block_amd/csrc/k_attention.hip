@@ -3,7 +3,8 @@
 // kernel; "joint attention" in the GGML update's bottom line of the "CUDA codepath !" thread,
 // antirez/iris.c issue #15).  The scores are never written to memory.
 //
-// bf16 kernel.  A workgroup of 4 waves owns 128 queries of one head; each wave 32 queries.
+// 16-bit kernel (bf16 or fp16 q, k, v).  A workgroup of 4 waves owns 128 queries of one head;
+// each wave 32 queries.
 // Per key tile of 64 keys (staged in LDS, K row-major and V transposed):
 //   S^T = K Q^T  with v_mfma_f32_32x32x16_bf16 (K fragment = A operand, Q fragment = B), so a
 //                lane holds 32 scores of ONE query: row max and row sum stay in the lane plus
@@ -12,7 +13,10 @@
 //   O^T += V^T P^T  (V^T fragment = A operand, P^T = B operand).  The K fragment rows are
 //                loaded in the key order that makes each lane's 8 consecutive score registers
 //                exactly the 8 keys the P^T operand needs, so P goes from the score
-//                accumulators to the PV MFMA without any cross-lane movement.
+//                accumulators to the PV MFMA without any cross-lane movement.  With bf16
+//                operands P enters as two bf16 terms (high part + rounded remainder), so the PV
+//                product carries the fp32 probabilities to 2^-16 relative instead of bf16's
+//                2^-9; with fp16 operands one fp16 term (2^-11) is used.
 // Each lane ends with 4 consecutive output features of one query per register group.
 //
 // fp32 kernel: LDS-tiled, 4 threads per query, fp32 FMA throughout.
@@ -30,7 +34,20 @@ __device__ __forceinline__ int key_of_row(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-__global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
+template <int DT> struct AFrag;
+template <> struct AFrag<BF16> { typedef bf16x8_v T; };
+template <> struct AFrag<F16> { typedef f16x8_v T; };
+
+template <int DT>
+__device__ __forceinline__ f32x16_v amfma(const typename AFrag<DT>::T& a, const typename AFrag<DT>::T& b,
+                                          const f32x16_v& c) {
+    if constexpr (DT == F16) return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256, 2) void attention_mfma_kernel(AttnArgs a) {
+    typedef typename AFrag<DT>::T FragT;
     __shared__ __attribute__((aligned(1024))) char sK[AK * HD * 2];    // [key][e], 256 B rows
     __shared__ __attribute__((aligned(1024))) char sV[HD * AK * 2];    // [e][key], 128 B rows
 
@@ -54,11 +71,11 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
 
     // Q fragments (B operand of S^T): query l32 of this wave, features 16*es + 8*h32 .. +7.
     const int qrow = qt * AQ + wave * 32 + l32;
-    bf16x8_v qf[8];
+    FragT qf[8];
     {
         const bf16_t* qp = Qg + (size_t)min(qrow, N - 1) * a.ld_q + 8 * h32;
 #pragma unroll
-        for (int es = 0; es < 8; ++es) qf[es] = *reinterpret_cast<const bf16x8_v*>(qp + 16 * es);
+        for (int es = 0; es < 8; ++es) qf[es] = *reinterpret_cast<const FragT*>(qp + 16 * es);
     }
 
     // Loader assignment.  K: 1024 16-byte chunks per tile, chunk c = tid + 256 r (r < 4):
@@ -131,8 +148,8 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int es = 0; es < 8; ++es) {
                 const int ch = 2 * es + h32;
-                const bf16x8_v kf = *reinterpret_cast<const bf16x8_v*>(sK + key * 256 + ((ch ^ (key & 15)) << 4));
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[es], s[kb], 0, 0, 0);
+                const FragT kf = *reinterpret_cast<const FragT*>(sK + key * 256 + ((ch ^ (key & 15)) << 4));
+                s[kb] = amfma<DT>(kf, qf[es], s[kb]);
             }
         }
         // register q of block kb holds key j0 + 32 kb + 16 (q >> 3) + 8 h32 + (q & 7)
@@ -159,27 +176,45 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int q = 0; q < 16; ++q) o[i][q] *= corr;
-        uint32_t pw[2][8];
+        // bf16: P = P_hi + P_lo, both bf16: P_hi keeps the top 16 bits of the fp32 probability
+        // (truncation), P_lo = bf16(p - P_hi) (exact difference, rounded to nearest even); the
+        // pair carries p to 2^-16 relative (one bf16 term would be 2^-9).  fp16: one term,
+        // rounded to nearest even (2^-11 relative).
+        uint32_t ph[2][8], pl[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int q = 0; q < 16; q += 2) {
                 const float p0 = exp2f(s[kb][q] - m_new), p1 = exp2f(s[kb][q + 1] - m_new);
                 l_run += p0 + p1;
-                pw[kb][q >> 1] = pack_bf16x2(p0, p1);
+                if constexpr (DT == BF16) {
+                    const uint32_t u0 = __float_as_uint(p0) & 0xffff0000u, u1 = __float_as_uint(p1) & 0xffff0000u;
+                    ph[kb][q >> 1] = (u0 >> 16) | u1;
+                    pl[kb][q >> 1] = pack_bf16x2(p0 - __uint_as_float(u0), p1 - __uint_as_float(u1));
+                } else {
+                    ph[kb][q >> 1] = pack_f16x2(p0, p1);
+                }
             }
         // ---- O^T += V^T P^T: key step ks covers keys 16 ks .. 16 ks + 15 of the tile
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int kb = ks >> 1, half = ks & 1;
-            u32x4_v pv = {pw[kb][4 * half], pw[kb][4 * half + 1], pw[kb][4 * half + 2], pw[kb][4 * half + 3]};
-            const bf16x8_v pf = __builtin_bit_cast(bf16x8_v, pv);
+            u32x4_v hv = {ph[kb][4 * half], ph[kb][4 * half + 1], ph[kb][4 * half + 2], ph[kb][4 * half + 3]};
+            const FragT pfh = __builtin_bit_cast(FragT, hv);
+            FragT vf[4];
 #pragma unroll
             for (int eb = 0; eb < 4; ++eb) {
                 const int e = eb * 32 + l32;
                 const int ch = 2 * ks + h32;
-                const bf16x8_v vf = *reinterpret_cast<const bf16x8_v*>(sV + e * 128 + ((ch ^ (e & 7)) << 4));
-                o[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[eb], 0, 0, 0);
+                vf[eb] = *reinterpret_cast<const FragT*>(sV + e * 128 + ((ch ^ (e & 7)) << 4));
+            }
+#pragma unroll
+            for (int eb = 0; eb < 4; ++eb) o[eb] = amfma<DT>(vf[eb], pfh, o[eb]);
+            if constexpr (DT == BF16) {
+                u32x4_v lv = {pl[kb][4 * half], pl[kb][4 * half + 1], pl[kb][4 * half + 2], pl[kb][4 * half + 3]};
+                const FragT pfl = __builtin_bit_cast(FragT, lv);
+#pragma unroll
+                for (int eb = 0; eb < 4; ++eb) o[eb] = amfma<DT>(vf[eb], pfl, o[eb]);
             }
         }
         __syncthreads();
@@ -198,8 +233,8 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = eb * 32 + 8 * i + 4 * h32;
-                u32x2_v w = {pack_bf16x2(o[eb][4 * i] * inv, o[eb][4 * i + 1] * inv),
-                             pack_bf16x2(o[eb][4 * i + 2] * inv, o[eb][4 * i + 3] * inv)};
+                u32x2_v w = {pack2<DT>(o[eb][4 * i] * inv, o[eb][4 * i + 1] * inv),
+                             pack2<DT>(o[eb][4 * i + 2] * inv, o[eb][4 * i + 3] * inv)};
                 *reinterpret_cast<u32x2_v*>(op + e) = w;
             }
     }
@@ -263,9 +298,10 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(AttnArgs a) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     if (a.n_tok == 0) return hipSuccess;
-    if (a.dtype == BF16) {
+    if (a.dtype == BF16 || a.dtype == F16) {
         const int nq = (a.n_tok + AQ - 1) / AQ;
-        hipLaunchKernelGGL(attention_bf16_kernel, dim3(nq * a.n_heads), dim3(256), 0, s, a);
+        if (a.dtype == F16) hipLaunchKernelGGL(attention_mfma_kernel<F16>, dim3(nq * a.n_heads), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(attention_mfma_kernel<BF16>, dim3(nq * a.n_heads), dim3(256), 0, s, a);
     } else {
         const int nq = (a.n_tok + FQ - 1) / FQ;
         hipLaunchKernelGGL(attention_f32_kernel, dim3(nq * a.n_heads), dim3(256), 0, s, a);

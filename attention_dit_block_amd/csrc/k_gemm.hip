@@ -8,9 +8,12 @@
 // One launch covers several problems (text and image streams, or the two halves of the
 // single-stream block's first linear).
 //
-// bf16 path: 256-thread workgroups (4 waves, 2 x 2), a 256 x 256 x 64 block tile, each wave a
-// 128 x 128 sub-tile of 4 x 4 v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators.  Both
-// operands go global -> LDS with global_load_lds_dwordx4 (no VGPR staging), double-buffered;
+// MFMA path (bf16 weights): 256-thread workgroups (4 waves, 2 x 2), a 256 x 256 x 64 block tile,
+// each wave a 128 x 128 sub-tile of 4 x 4 v_mfma_f32_32x32x16 tiles with fp32 accumulators.
+// Activations are bf16 or fp16; with fp16 activations the bf16 weight tile is converted to fp16
+// while it is staged (the MFMA needs one operand type; the conversion is exact).  Operands go
+// global -> LDS with global_load_lds_dwordx4 (no VGPR staging) where no conversion is needed,
+// double-buffered;
 // LDS rows are 128 B with the 16-byte chunk index XOR-swizzled by (row & 7) so the fragment
 // reads are bank-conflict free.  The MFMA computes D[n][m], so each lane ends with four
 // consecutive output columns of one row and the epilogue reads / writes 8-16 B per lane.
@@ -52,11 +55,35 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
 
 __device__ __forceinline__ float silu_acc(float g) { return g / (1.0f + __expf(-g)); }
 
-template <int MODE>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmBatch b) {
+template <int AT> struct Frag;
+template <> struct Frag<BF16> { typedef bf16x8_v T; };
+template <> struct Frag<F16> { typedef f16x8_v T; };
+
+template <int AT>
+__device__ __forceinline__ f32x16_v mfma32(const typename Frag<AT>::T& a, const typename Frag<AT>::T& b,
+                                           const f32x16_v& c) {
+    if constexpr (AT == F16) return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Epilogue store of 4 consecutive columns of one row, output type chosen at run time.
+__device__ __forceinline__ void store4_dt(void* base, size_t off, int dt, const float* o) {
+    char* p = reinterpret_cast<char*>(base);
+    if (dt == F32) store4<F32>(p + off * 4, o);
+    else if (dt == F16) store4<F16>(p + off * 2, o);
+    else store4<BF16>(p + off * 2, o);
+}
+
+// A (activations, AT) is staged global -> LDS with global_load_lds_dwordx4.  B (bf16 weights)
+// goes the same way when AT == BF16; when AT == F16 it is loaded into VGPRs, converted to fp16
+// (exact: bf16 values are fp16 values in fp16's normal range) and written to the same LDS
+// layout, so both operands of the fp16 MFMA come from one swizzled layout.
+template <int MODE, int AT>
+__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmBatch b) {
     __shared__ __attribute__((aligned(1024))) char smem[2 * (BM + BN) * BK * 2];
     constexpr int kStage = (BM + BN) * BK * 2;     // bytes of one A+B stage
     constexpr int kBOff = BM * BK * 2;             // B tile offset within a stage
+    typedef typename Frag<AT>::T FragT;
 
     int pi, tm, tn;
     tile_of(b, xcd_remap(blockIdx.x, gridDim.x), pi, tm, tn);
@@ -72,7 +99,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmBatch b) {
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    // ---- global -> LDS load plan: wave w, instruction i covers tile rows (w*8+i)*8 .. +7
+    // ---- global -> LDS load plan: wave w, instruction i covers tile rows (w*8+i)*8 .. +7;
+    //      lane l writes LDS bytes l*16 .. l*16+15 of that 1 KB block = row l/8, chunk l%8,
+    //      which holds global chunk (l%8) ^ (row & 7) of the row.
     const bf16_t* gA[8];
     const bf16_t* gB[8];
     {
@@ -85,30 +114,47 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmBatch b) {
             am = am < M ? am : M - 1;
             gA[i] = reinterpret_cast<const bf16_t*>(P.A) + (size_t)am * P.lda + chunk * 8;
             long bn;
-            if (swiglu) bn = row < BN / 2 ? (long)n0 + row : P.up_off + n0 + (row - BN / 2);
-            else bn = n0 + row;
-            const long nmax = swiglu ? P.up_off + P.N - 1 : P.N - 1;
-            if (!swiglu && bn > nmax) bn = nmax;
             if (swiglu) {
-                const long lim = row < BN / 2 ? P.N - 1 : P.up_off + P.N - 1;
-                if (bn > lim) bn = lim;
+                const bool up = row >= BN / 2;
+                bn = (long)n0 + (up ? row - BN / 2 : row);
+                if (bn > P.N - 1) bn = P.N - 1;
+                if (up) bn += P.up_off;
+            } else {
+                bn = n0 + row;
+                if (bn > P.N - 1) bn = P.N - 1;
             }
             gB[i] = reinterpret_cast<const bf16_t*>(P.B) + (size_t)bn * P.ldb + chunk * 8;
         }
     }
+    u32x4_v breg[8];
     auto issue_loads = [&](int buf, int k0) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             __builtin_amdgcn_global_load_lds(gA[i] + k0, (lds_void*)(smem + buf * kStage + (wave * 8 + i) * 1024),
                                              16, 0, 0);
-            __builtin_amdgcn_global_load_lds(gB[i] + k0,
-                                             (lds_void*)(smem + buf * kStage + kBOff + (wave * 8 + i) * 1024),
-                                             16, 0, 0);
+            if constexpr (AT == BF16)
+                __builtin_amdgcn_global_load_lds(gB[i] + k0,
+                                                 (lds_void*)(smem + buf * kStage + kBOff + (wave * 8 + i) * 1024),
+                                                 16, 0, 0);
+            else
+                breg[i] = ld16(gB[i] + k0);
+        }
+    };
+    auto store_b = [&](int buf) {
+        if constexpr (AT == F16) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                u32x4_v w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(breg[i][j]);
+                *reinterpret_cast<u32x4_v*>(smem + buf * kStage + kBOff + (wave * 8 + i) * 1024 + lane * 16) = w;
+            }
         }
     };
 
-    // ---- fragment read offsets (bytes within a tile buffer)
-    // A fragment (m-block mb): row wm*128 + mb*32 + (lane & 31); B fragment (n-block nb): see below.
+    // ---- fragment read offsets.  A fragment (m-block j): row wm*128 + j*32 + (lane & 31);
+    //      B fragment (n-block j): a 32-row block of this wave's B rows (gate and up halves for
+    //      SwiGLU tiles).
     int a_row[4], b_row[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -128,29 +174,31 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmBatch b) {
 
     const int nk = K / BK;
     issue_loads(0, 0);
+    store_b(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int it = 0; it < nk; ++it) {
         const int buf = it & 1;
-        if (it + 1 < nk) issue_loads(buf ^ 1, (it + 1) * BK);
+        const bool more = it + 1 < nk;
+        if (more) issue_loads(buf ^ 1, (it + 1) * BK);
         const char* la = smem + buf * kStage;
         const char* lb = la + kBOff;
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
             const int c = 2 * s + khalf;
-            bf16x8_v fa[4], fb[4];
+            FragT fa[4], fb[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                fa[j] = *reinterpret_cast<const bf16x8_v*>(la + a_row[j] * 128 + ((c ^ (a_row[j] & 7)) << 4));
-                fb[j] = *reinterpret_cast<const bf16x8_v*>(lb + b_row[j] * 128 + ((c ^ (b_row[j] & 7)) << 4));
+                fa[j] = *reinterpret_cast<const FragT*>(la + a_row[j] * 128 + ((c ^ (a_row[j] & 7)) << 4));
+                fb[j] = *reinterpret_cast<const FragT*>(lb + b_row[j] * 128 + ((c ^ (b_row[j] & 7)) << 4));
             }
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+                for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma32<AT>(fb[nb], fa[mb], acc[nb][mb]);
         }
+        if (more) store_b(buf ^ 1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
@@ -176,8 +224,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmBatch b) {
                         const float u = acc[nb + 2][mb][4 * i + j];
                         f[j] = silu_acc(g) * u;
                     }
-                    u32x2_v w = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
-                    *reinterpret_cast<u32x2_v*>(reinterpret_cast<bf16_t*>(P.C) + (size_t)m * P.ldc + col) = w;
+                    store4_dt(P.C, (size_t)m * P.ldc + col, P.c_dtype, f);
                 }
             }
         } else {
@@ -193,24 +240,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmBatch b) {
                     if (epi == EPI_GATED_RES) {
                         const f32x4_v gt = ldf4(P.gate + col);
                         float r[4];
-                        if (P.r_dtype == BF16) {
-                            const u32x2_v rv = *reinterpret_cast<const u32x2_v*>(
-                                reinterpret_cast<const bf16_t*>(P.R) + (size_t)m * P.ldr + col);
-                            r[0] = bf_lo(rv[0]); r[1] = bf_hi(rv[0]); r[2] = bf_lo(rv[1]); r[3] = bf_hi(rv[1]);
-                        } else {
-                            const f32x4_v rv = ldf4(reinterpret_cast<const float*>(P.R) + (size_t)m * P.ldr + col);
-                            r[0] = rv[0]; r[1] = rv[1]; r[2] = rv[2]; r[3] = rv[3];
-                        }
+                        const size_t roff = (size_t)m * P.ldr + col;
+                        if (P.r_dtype == BF16) load4<BF16>(reinterpret_cast<const char*>(P.R) + roff * 2, r);
+                        else load4<F32>(reinterpret_cast<const char*>(P.R) + roff * 4, r);
 #pragma unroll
                         for (int j = 0; j < 4; ++j) o[j] = fmaf(gt[j], o[j], r[j]);
                     }
-                    if (P.c_dtype == BF16) {
-                        u32x2_v w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                        *reinterpret_cast<u32x2_v*>(reinterpret_cast<bf16_t*>(P.C) + (size_t)m * P.ldc + col) = w;
-                    } else {
-                        f32x4_v w = {o[0], o[1], o[2], o[3]};
-                        stf4(reinterpret_cast<float*>(P.C) + (size_t)m * P.ldc + col, w);
-                    }
+                    store4_dt(P.C, (size_t)m * P.ldc + col, P.c_dtype, o);
                 }
             }
         }
@@ -297,17 +333,26 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmBatch b) {
     else gemm_f32_tile<false>(P, tm, tn);
 }
 
+template <int AT>
+static void launch_mfma(GemmBatch& b, hipStream_t s, bool all_store, bool all_res, bool all_swiglu) {
+    const dim3 grid(b.total_tiles), block(256);
+    if (all_store) hipLaunchKernelGGL((gemm_mfma_kernel<MODE_STORE, AT>), grid, block, 0, s, b);
+    else if (all_res) hipLaunchKernelGGL((gemm_mfma_kernel<MODE_RES, AT>), grid, block, 0, s, b);
+    else if (all_swiglu) hipLaunchKernelGGL((gemm_mfma_kernel<MODE_SWIGLU, AT>), grid, block, 0, s, b);
+    else hipLaunchKernelGGL((gemm_mfma_kernel<MODE_MIXED, AT>), grid, block, 0, s, b);
+}
+
 hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
     int total = 0;
-    bool any_swiglu = false, all_swiglu = true, all_res = true, all_store = true;
+    bool all_swiglu = true, all_res = true, all_store = true;
+    const bool mfma = b.a_dtype != F32;
     for (int i = 0; i < b.n; ++i) {
         GemmProblem& P = b.p[i];
         const bool sw = P.epi == EPI_SWIGLU;
-        any_swiglu |= sw;
         all_swiglu &= sw;
         all_res &= P.epi == EPI_GATED_RES;
         all_store &= P.epi == EPI_STORE;
-        if (b.dtype == BF16) {
+        if (mfma) {
             P.tiles_m = (P.M + BM - 1) / BM;
             P.tiles_n = sw ? (P.N + BN / 2 - 1) / (BN / 2) : (P.N + BN - 1) / BN;
         } else {
@@ -318,17 +363,11 @@ hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
         P.tile_begin = total;
         total += P.tiles_m * P.tiles_n;
     }
-    (void)any_swiglu;
     b.total_tiles = total;
     if (total == 0) return hipSuccess;
-    if (b.dtype == BF16) {
-        if (all_store) hipLaunchKernelGGL(gemm_bf16_kernel<MODE_STORE>, dim3(total), dim3(256), 0, s, b);
-        else if (all_res) hipLaunchKernelGGL(gemm_bf16_kernel<MODE_RES>, dim3(total), dim3(256), 0, s, b);
-        else if (all_swiglu) hipLaunchKernelGGL(gemm_bf16_kernel<MODE_SWIGLU>, dim3(total), dim3(256), 0, s, b);
-        else hipLaunchKernelGGL(gemm_bf16_kernel<MODE_MIXED>, dim3(total), dim3(256), 0, s, b);
-    } else {
-        hipLaunchKernelGGL(gemm_f32_kernel, dim3(total), dim3(256), 0, s, b);
-    }
+    if (b.a_dtype == F16) launch_mfma<F16>(b, s, all_store, all_res, all_swiglu);
+    else if (b.a_dtype == BF16) launch_mfma<BF16>(b, s, all_store, all_res, all_swiglu);
+    else hipLaunchKernelGGL(gemm_f32_kernel, dim3(total), dim3(256), 0, s, b);
     return hipGetLastError();
 }
 

@@ -23,8 +23,8 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
     extern __shared__ float s_act[];
     const int tid = threadIdx.x;
     for (int i = tid; i < b.d_cond; i += 256) {
-        float c = DT == BF16 ? bf2f(reinterpret_cast<const bf16_t*>(b.cond)[i])
-                             : reinterpret_cast<const float*>(b.cond)[i];
+        const float c = DT == BF16 ? bf2f(reinterpret_cast<const bf16_t*>(b.cond)[i])
+                                   : reinterpret_cast<const float*>(b.cond)[i];
         s_act[i] = c / (1.0f + expf(-c));
     }
     __syncthreads();
@@ -33,19 +33,19 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
     const int wave = tid >> 6;
     const int total = b.p[0].rows + (b.n > 1 ? b.p[1].rows : 0);
     const int row0 = (blockIdx.x * kGemvWaves + wave) * kGemvRowsPerWave;
-    constexpr int kElems = DT == BF16 ? 8 : 4;           // elements per 16-byte slice
+    constexpr int kES = ESize<DT>::v;
+    constexpr int kElems = 16 / kES;                       // elements per 16-byte slice
     const char* wrow[kGemvRowsPerWave];
     float acc[kGemvRowsPerWave];
     bool ok[kGemvRowsPerWave];
 #pragma unroll
     for (int r = 0; r < kGemvRowsPerWave; ++r) {
-        int g = row0 + r;
+        const int g = row0 + r;
         ok[r] = g < total;
         int pi = (g >= b.p[0].rows) ? 1 : 0;
         int lr = g - (pi ? b.p[0].rows : 0);
         if (!ok[r]) { pi = 0; lr = 0; }
-        wrow[r] = reinterpret_cast<const char*>(b.p[pi].w) +
-                  (size_t)lr * b.d_cond * (DT == BF16 ? 2 : 4);
+        wrow[r] = reinterpret_cast<const char*>(b.p[pi].w) + (size_t)lr * b.d_cond * kES;
         acc[r] = 0.0f;
     }
     for (int k0 = lane * kElems; k0 < b.d_cond; k0 += 64 * kElems) {
@@ -54,15 +54,15 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
         for (int t = 0; t < kElems; ++t) sa[t] = s_act[k0 + t];
         u32x4_v w[kGemvRowsPerWave];
 #pragma unroll
-        for (int r = 0; r < kGemvRowsPerWave; ++r)
-            w[r] = ld16(wrow[r] + (size_t)k0 * (DT == BF16 ? 2 : 4));
+        for (int r = 0; r < kGemvRowsPerWave; ++r) w[r] = ld16(wrow[r] + (size_t)k0 * kES);
 #pragma unroll
         for (int r = 0; r < kGemvRowsPerWave; ++r) {
             if (DT == BF16) {
-                float f[8];
-                unpack8(w[r], f);
 #pragma unroll
-                for (int t = 0; t < 8; ++t) acc[r] = fmaf(f[t], sa[t], acc[r]);
+                for (int t = 0; t < 4; ++t) {
+                    acc[r] = fmaf(bf_lo(w[r][t]), sa[2 * t], acc[r]);
+                    acc[r] = fmaf(bf_hi(w[r][t]), sa[2 * t + 1], acc[r]);
+                }
             } else {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) acc[r] = fmaf(__uint_as_float(w[r][t]), sa[t], acc[r]);
@@ -71,20 +71,20 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
     }
 #pragma unroll
     for (int r = 0; r < kGemvRowsPerWave; ++r) {
-        float s = wave_sum(acc[r]);
-        int g = row0 + r;
+        const float s = wave_sum(acc[r]);
+        const int g = row0 + r;
         if (lane == 0 && ok[r]) {
-            int pi = (g >= b.p[0].rows) ? 1 : 0;
+            const int pi = (g >= b.p[0].rows) ? 1 : 0;
             b.p[pi].out[g - (pi ? b.p[0].rows : 0)] = s;
         }
     }
 }
 
 hipError_t launch_adaln_gemv(const GemvBatch& b, hipStream_t s) {
-    int total = b.p[0].rows + (b.n > 1 ? b.p[1].rows : 0);
-    int per_block = kGemvWaves * kGemvRowsPerWave;
-    dim3 grid((total + per_block - 1) / per_block);
-    size_t lds = (size_t)b.d_cond * sizeof(float);
+    const int total = b.p[0].rows + (b.n > 1 ? b.p[1].rows : 0);
+    const int per_block = kGemvWaves * kGemvRowsPerWave;
+    const dim3 grid((total + per_block - 1) / per_block);
+    const size_t lds = (size_t)b.d_cond * sizeof(float);
     if (b.dtype == BF16)
         hipLaunchKernelGGL(adaln_gemv_kernel<BF16>, grid, dim3(256), lds, s, b);
     else
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
     const ModProblem& P = b.p[pi];
     const int r = row - (pi ? b.p[0].rows : 0);
     const int d = b.d;
-    const char* xrow = reinterpret_cast<const char*>(P.x) + (size_t)r * P.ld_x * (XT == BF16 ? 2 : 4);
-    char* orow = reinterpret_cast<char*>(P.out) + (size_t)r * P.ld_out * (OT == BF16 ? 2 : 4);
+    const char* xrow = reinterpret_cast<const char*>(P.x) + (size_t)r * P.ld_x * ESize<XT>::v;
+    char* orow = reinterpret_cast<char*>(P.out) + (size_t)r * P.ld_out * ESize<OT>::v;
 
     float v[NC][8];
     float ss = 0.0f;
@@ -116,13 +116,7 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
     for (int i = 0; i < NC; ++i) {
         const int c = (lane + 64 * i) * 8;        // first element of this 8-element chunk
         if (c < d) {
-            if (XT == BF16) {
-                unpack8(ld16(xrow + (size_t)c * 2), v[i]);
-            } else {
-                f32x4_v a = ldf4(xrow + (size_t)c * 4), bq = ldf4(xrow + (size_t)c * 4 + 16);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) { v[i][t] = a[t]; v[i][4 + t] = bq[t]; }
-            }
+            load8<XT>(xrow + (size_t)c * ESize<XT>::v, v[i]);
 #pragma unroll
             for (int t = 0; t < 8; ++t) ss = fmaf(v[i][t], v[i][t], ss);
         }
@@ -133,21 +127,15 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
     for (int i = 0; i < NC; ++i) {
         const int c = (lane + 64 * i) * 8;
         if (c < d) {
-            f32x4_v sh0 = ldf4(P.shift + c), sh1 = ldf4(P.shift + c + 4);
-            f32x4_v sc0 = ldf4(P.scale + c), sc1 = ldf4(P.scale + c + 4);
+            const f32x4_v sh0 = ldf4(P.shift + c), sh1 = ldf4(P.shift + c + 4);
+            const f32x4_v sc0 = ldf4(P.scale + c), sc1 = ldf4(P.scale + c + 4);
             float o[8];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 o[t] = fmaf(1.0f + sc0[t], v[i][t] * rstd, sh0[t]);
                 o[4 + t] = fmaf(1.0f + sc1[t], v[i][4 + t] * rstd, sh1[t]);
             }
-            if (OT == BF16) {
-                st16(orow + (size_t)c * 2, pack8(o));
-            } else {
-                f32x4_v a = {o[0], o[1], o[2], o[3]}, bq = {o[4], o[5], o[6], o[7]};
-                stf4(orow + (size_t)c * 4, a);
-                stf4(orow + (size_t)c * 4 + 16, bq);
-            }
+            store8<OT>(orow + (size_t)c * ESize<OT>::v, o);
         }
     }
 }
@@ -162,26 +150,29 @@ static hipError_t launch_mod_nc(const ModBatch& b, hipStream_t s, dim3 grid) {
     return hipGetLastError();
 }
 
+template <int XT>
+static hipError_t launch_mod_x(const ModBatch& b, hipStream_t s, dim3 grid) {
+    if (b.out_dtype == F16) return launch_mod_nc<XT, F16>(b, s, grid);
+    if (b.out_dtype == BF16) return launch_mod_nc<XT, BF16>(b, s, grid);
+    return launch_mod_nc<XT, F32>(b, s, grid);
+}
+
 hipError_t launch_modulate(const ModBatch& b, hipStream_t s) {
     const int total = b.p[0].rows + (b.n > 1 ? b.p[1].rows : 0);
-    if (total == 0) return hipSuccess;
-    dim3 grid((total + 3) / 4);
-    // All problems of one batch share x_dtype (checked by the caller).
-    const int xt = b.p[0].x_dtype;
-    if (b.dtype == BF16)
-        return xt == BF16 ? launch_mod_nc<BF16, BF16>(b, s, grid) : launch_mod_nc<F32, BF16>(b, s, grid);
-    return launch_mod_nc<F32, F32>(b, s, grid);
+    const dim3 grid((total + 3) / 4);
+    // All problems of one batch share x_dtype (the caller builds them so).
+    return b.p[0].x_dtype == BF16 ? launch_mod_x<BF16>(b, s, grid) : launch_mod_x<F32>(b, s, grid);
 }
 
 // ------------------------------------------------------------------------------------------
 // QK RMSNorm + 4-axis RoPE, in place.  One 256-thread block per token: the first wave computes
 // the token's 64 rotation angles once (double-precision angle and range reduction, fp32 sin/cos)
-// into LDS; then groups of 16 lanes each take one 128-dim head vector of q or k (16 B per lane),
-// reduce its mean square across the 16 lanes, scale by the QK-norm weight and rotate the four
-// interleaved pairs they hold.
+// into LDS; then groups of 16 lanes each take one 128-dim head vector of q or k (16 B per lane
+// for 16-bit types), reduce its mean square across the 16 lanes, scale by the QK-norm weight
+// and rotate the four interleaved pairs they hold.
 // Bound: HBM bytes  n_tok * 2 * n_heads * 128 * sizeof(T) read + the same written.
 // ------------------------------------------------------------------------------------------
-template <int DT>
+template <int DT, int WT>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkRopeArgs a) {
     __shared__ float s_cos[64], s_sin[64];
     const int n = blockIdx.x;
@@ -198,23 +189,17 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkRopeArgs a) {
     const int set = n < a.n_first ? 0 : 1;
     const int g = tid >> 4;           // 16 groups of 16 lanes
     const int t = tid & 15;           // dims 8t .. 8t+7 of the head
-    constexpr int ES = DT == BF16 ? 2 : 4;
+    constexpr int ES = ESize<DT>::v, WS = ESize<WT>::v;
     for (int vec = g; vec < 2 * a.n_heads; vec += 16) {
         const int which = vec >= a.n_heads ? 1 : 0;
         const int h = vec - which * a.n_heads;
         char* base = which ? reinterpret_cast<char*>(a.k) + (size_t)n * a.ld_k * ES
                            : reinterpret_cast<char*>(a.q) + (size_t)n * a.ld_q * ES;
         char* p = base + (size_t)(h * 128 + t * 8) * ES;
-        const char* wp = reinterpret_cast<const char*>(set ? a.qk_w1 : a.qk_w0) + (size_t)(which * 128 + t * 8) * ES;
+        const char* wp = reinterpret_cast<const char*>(set ? a.qk_w1 : a.qk_w0) + (size_t)(which * 128 + t * 8) * WS;
         float v[8], w[8];
-        if (DT == BF16) {
-            unpack8(ld16(p), v);
-            unpack8(ld16(wp), w);
-        } else {
-            f32x4_v a0 = ldf4(p), a1 = ldf4(p + 16), w0 = ldf4(wp), w1 = ldf4(wp + 16);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { v[i] = a0[i]; v[4 + i] = a1[i]; w[i] = w0[i]; w[4 + i] = w1[i]; }
-        }
+        load8<DT>(p, v);
+        load8<WT>(wp, w);
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
@@ -230,23 +215,23 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkRopeArgs a) {
             y[2 * i] = u0 * c - u1 * s;
             y[2 * i + 1] = u0 * s + u1 * c;
         }
-        if (DT == BF16) {
-            st16(p, pack8(y));
-        } else {
-            f32x4_v o0 = {y[0], y[1], y[2], y[3]}, o1 = {y[4], y[5], y[6], y[7]};
-            stf4(p, o0);
-            stf4(p + 16, o1);
-        }
+        store8<DT>(p, y);
     }
 }
 
-hipError_t launch_qk_rmsnorm_rope(const QkRopeArgs& a, hipStream_t s) {
-    if (a.n_tok == 0) return hipSuccess;
-    if (a.dtype == BF16)
-        hipLaunchKernelGGL(qk_norm_rope_kernel<BF16>, dim3(a.n_tok), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(qk_norm_rope_kernel<F32>, dim3(a.n_tok), dim3(256), 0, s, a);
+template <int DT>
+static hipError_t launch_rope_w(const QkRopeArgs& a, hipStream_t s) {
+    const dim3 grid(a.n_tok), block(256);
+    if (a.w_dtype == F16) hipLaunchKernelGGL((qk_norm_rope_kernel<DT, F16>), grid, block, 0, s, a);
+    else if (a.w_dtype == BF16) hipLaunchKernelGGL((qk_norm_rope_kernel<DT, BF16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((qk_norm_rope_kernel<DT, F32>), grid, block, 0, s, a);
     return hipGetLastError();
+}
+
+hipError_t launch_qk_rmsnorm_rope(const QkRopeArgs& a, hipStream_t s) {
+    if (a.dtype == F16) return launch_rope_w<F16>(a, s);
+    if (a.dtype == BF16) return launch_rope_w<BF16>(a, s);
+    return launch_rope_w<F32>(a, s);
 }
 
 }  // namespace dit

@@ -1,5 +1,6 @@
 // Host-side launchers of the gfx950 kernels (internal to the library).
-// Every launcher assumes its arguments were validated by the C ABI layer.
+// Every launcher assumes its arguments were validated by the C ABI layer and launches exactly
+// one kernel.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,7 +8,7 @@
 
 namespace dit {
 
-enum DType { F32 = 0, BF16 = 1 };
+enum DType { F32 = 0, BF16 = 1, F16 = 2 };
 
 // ---- AdaLN GEMV: out_p[r] = sum_k W_p[r, k] * SiLU(cond[k]) ------------------
 struct GemvProblem {
@@ -20,14 +21,14 @@ struct GemvBatch {
     int n;
     const void* cond;   // [d_cond]
     int d_cond;
-    int dtype;          // dtype of w and cond
+    int dtype;          // dtype of w and cond (F32 or BF16)
 };
 hipError_t launch_adaln_gemv(const GemvBatch& b, hipStream_t s);
 
 // ---- modulate: out = (1 + scale) * RMSNorm(x) + shift, per row ---------------
 struct ModProblem {
-    const void* x; long ld_x; int x_dtype;
-    void* out; long ld_out;           // dtype of the launch
+    const void* x; long ld_x; int x_dtype;    // F32 or BF16
+    void* out; long ld_out;                   // out_dtype of the batch
     const float* shift; const float* scale;   // [d] fp32
     int rows;
 };
@@ -36,14 +37,13 @@ struct ModBatch {
     int n;
     int d;
     float eps;
-    int dtype;          // output storage type
+    int out_dtype;      // F32, BF16 or F16
 };
 hipError_t launch_modulate(const ModBatch& b, hipStream_t s);
 
 // ---- QK RMSNorm + RoPE, in place -----------------------------------------------
 struct RopeTable {
-    float omega[64];        // frequency of pair p (float of the host's double)
-    double omega_d[64];     // same, double precision
+    double omega_d[64];     // frequency of pair p
     int8_t axis[64];        // position axis of pair p
 };
 struct QkRopeArgs {
@@ -56,19 +56,20 @@ struct QkRopeArgs {
     float eps;
     const int32_t* pos; int n_axes;
     RopeTable tab;
-    int dtype;
+    int dtype;              // q / k: F32, BF16 or F16
+    int w_dtype;            // QK-norm weights: F32, BF16 or F16
 };
 hipError_t launch_qk_rmsnorm_rope(const QkRopeArgs& a, hipStream_t s);
 
 // ---- grouped GEMM  C = epilogue(A . B^T) -----------------------------------------
 enum Epilogue {
-    EPI_STORE = 0,        // C (dtype) = acc
+    EPI_STORE = 0,        // C (c_dtype) = acc
     EPI_GATED_RES = 1,    // C (c_dtype) = R (r_dtype) + gate[col] * acc
-    EPI_SWIGLU = 2        // C (dtype) = SiLU(acc_gate) * acc_up; B rows [n] gate, [up_off + n] up
+    EPI_SWIGLU = 2        // C (c_dtype) = SiLU(acc_gate) * acc_up; B rows [n] gate, [up_off + n] up
 };
 struct GemmProblem {
-    const void* A; long lda;        // [M, K]
-    const void* B; long ldb;        // [N_b, K]   (weights, [out, in])
+    const void* A; long lda;        // [M, K], a_dtype of the batch
+    const void* B; long ldb;        // [N_b, K] weights ([out, in]): BF16 (F32 for an F32 batch)
     void* C; long ldc; int c_dtype;
     const void* R; long ldr; int r_dtype;
     const float* gate;              // [N]
@@ -80,7 +81,8 @@ struct GemmProblem {
 struct GemmBatch {
     GemmProblem p[2];
     int n;
-    int dtype;          // dtype of A and B
+    int a_dtype;        // F32 (fp32 path, fp32 weights), BF16 (bf16 weights) or F16 (bf16 weights,
+                        // converted to fp16 while they are staged)
     int total_tiles;    // filled by the launcher
 };
 hipError_t launch_gemm(GemmBatch& b, hipStream_t s);
@@ -93,7 +95,7 @@ struct AttnArgs {
     void* o; long ld_o;
     int n_tok, n_heads;
     float scale;
-    int dtype;
+    int dtype;          // F32, BF16 or F16
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

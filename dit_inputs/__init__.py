@@ -154,7 +154,8 @@ STREAM_IDS = {"txt": 0, "img": 1, "single": 2, "none": 3}
 
 def draw(shape, std: float, dtype: str, seed: int, name: str, block: int = 0,
          stream: str = "none") -> np.ndarray:
-    """N(0, std^2) draw.  Returns float32 (dtype 'f32') or bf16 bits (dtype 'bf16')."""
+    """N(0, std^2) draw.  Returns float32 ('f32'), bf16 bits as uint16 ('bf16') or float16
+    ('f16', rounded to nearest even)."""
     rng = np.random.default_rng([int(seed), int(block), STREAM_IDS[stream], TENSOR_IDS[name]])
     a = rng.standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
@@ -163,6 +164,8 @@ def draw(shape, std: float, dtype: str, seed: int, name: str, block: int = 0,
         return a
     if dtype == "bf16":
         return bf16_bits_from_f32(a)
+    if dtype == "f16":
+        return a.astype(np.float16)      # round to nearest even
     raise ValueError(dtype)
 
 

@@ -19,8 +19,12 @@
  *    never writes an input buffer.
  *  - Matrices are row-major.  Linear weights are [out, in], so y = x W^T.
  *    `ld*` arguments are row strides in ELEMENTS.
- *  - dtype: DIT_BF16 (bf16 storage, fp32 accumulation) or DIT_F32 (fp32
- *    storage and arithmetic, no reduced-precision matrix math).
+ *  - Element types: DIT_BF16 and DIT_F16 (16-bit storage, fp32 accumulation)
+ *    and DIT_F32 (fp32 storage and arithmetic, no reduced-precision matrix
+ *    math).  A bf16 model keeps its weights and block input in bf16; the
+ *    activations handed between the block's steps may be carried in fp16
+ *    (act_dtype), whose 10-bit mantissa keeps the block output within 2e-2
+ *    (max |err| / RMS) of exact arithmetic where bf16's 7 bits do not.
  *  - Alignment: every pointer 16-byte aligned, every row stride a multiple of
  *    16 bytes.
  *  - Errors: arguments are validated on the host before any launch.  On a
@@ -42,7 +46,7 @@ extern "C" {
 
 #define DIT_ABI_VERSION 1
 
-enum dit_dtype { DIT_F32 = 0, DIT_BF16 = 1 };
+enum dit_dtype { DIT_F32 = 0, DIT_BF16 = 1, DIT_F16 = 2 };
 
 enum dit_status {
     DIT_OK = 0,
@@ -62,14 +66,14 @@ enum dit_status {
  * (no learnable weight).  Chunk c of mod_out is mod_out[c*d .. c*d + d - 1];
  * the FLUX order is shift, scale, gate (twice for a double-stream block).
  *
- *  dtype     storage type of cond, w_mod and x_out
+ *  dtype     storage type of cond and w_mod: DIT_BF16 or DIT_F32
  *  cond      [d_cond]
  *  w_mod     [n_chunks * d, d_cond]
  *  mod_out   [n_chunks * d] fp32
  *  x         optional, [n_tok rows, stride ld_x] of x_dtype (DIT_BF16 or
- *            DIT_F32 for a bf16 call, DIT_F32 for an fp32 call).  NULL: only
- *            mod_out is computed.
- *  x_out     [n_tok rows, stride ld_out] of dtype; must not overlap x.
+ *            DIT_F32).  NULL: only mod_out is computed.
+ *  x_out     [n_tok rows, stride ld_out] of out_dtype (DIT_BF16, DIT_F16 or
+ *            DIT_F32; DIT_F32 for an fp32 call); must not overlap x.
  * Limits: 8 <= d <= 8192, d % 8 == 0, 8 <= d_cond <= 16384, d_cond % 8 == 0, n_tok >= 0.
  */
 int dit_adaln_modulate(int dtype, void* stream,
@@ -78,7 +82,7 @@ int dit_adaln_modulate(int dtype, void* stream,
                        float* mod_out,
                        const void* x, int x_dtype, int n_tok, long ld_x,
                        int shift_chunk, int scale_chunk, float eps,
-                       void* x_out, long ld_out);
+                       void* x_out, int out_dtype, long ld_out);
 
 /*
  * Per-head QK RMSNorm followed by 4-axis RoPE, in place
@@ -92,19 +96,21 @@ int dit_adaln_modulate(int dtype, void* stream,
  *   phi = pos[n, ax] * theta^(-2j / axes_dim[ax]) for pair j of axis ax,
  *   axis ax owning dims [sum(axes_dim[:ax]), + axes_dim[ax]).
  *
+ *  dtype     element type of q and k (DIT_BF16, DIT_F16 or DIT_F32)
  *  q, k      [n_tok rows, stride ld_q / ld_k], n_heads*head_dim columns each
  *            (may be column views of one qkv buffer)
- *  qk_w      [2 sets][2 (q, k)][head_dim] of dtype: rows n < n_first use set
- *            0 (text), the others set 1 (image).  If n_first >= n_tok only
- *            set 0 is read.
+ *  qk_w      [2 sets][2 (q, k)][head_dim] of w_dtype: rows n < n_first use
+ *            set 0 (text), the others set 1 (image).  If n_first >= n_tok
+ *            only set 0 is read.
  *  pos       int32 [n_tok, n_axes]
  *  axes_dim  (host) [n_axes], each even, summing to head_dim
- * Limits: head_dim == 128, 1 <= n_axes <= 4, n_heads >= 1, n_tok >= 0.
+ * Limits: head_dim == 128, 1 <= n_axes <= 4, n_heads >= 1, n_tok >= 0
+ * (n_tok == 0: nothing is read or written).
  */
 int dit_qk_rmsnorm_rope(int dtype, void* stream,
                         void* q, long ld_q, void* k, long ld_k,
                         int n_tok, int n_heads, int head_dim,
-                        const void* qk_w, int n_first, float eps,
+                        const void* qk_w, int w_dtype, int n_first, float eps,
                         const int32_t* pos, int n_axes, const int* axes_dim, float theta);
 
 /*
@@ -115,11 +121,16 @@ int dit_qk_rmsnorm_rope(int dtype, void* stream,
  *
  *   O_h = softmax(Q_h K_h^T * softmax_scale) V_h       for every head h
  *
+ *  dtype     element type of q, k, v and o (DIT_BF16, DIT_F16 or DIT_F32)
  *  q, k, v   [n_tok rows, stride ld_q/ld_k/ld_v]; head h = columns
  *            h*head_dim .. h*head_dim + head_dim - 1
  *  o         [n_tok rows, stride ld_o] of dtype; must not overlap q, k, v
  *  softmax_scale  usually 1/sqrt(head_dim)
- * Limits: head_dim == 128, n_heads >= 1, n_tok >= 0.
+ * Scores, softmax and accumulation are fp32; the 16-bit paths pass the
+ * probabilities to the PV product within 2^-11 (fp16) or 2^-16 (bf16, two
+ * terms) of their fp32 values.
+ * Limits: head_dim == 128, n_heads >= 1, n_tok >= 0 (n_tok == 0: nothing is
+ * read or written).
  */
 int dit_joint_attention(int dtype, void* stream,
                         const void* q, long ld_q, const void* k, long ld_k,
@@ -129,9 +140,11 @@ int dit_joint_attention(int dtype, void* stream,
 
 /* Shapes and constants of one block. */
 typedef struct dit_block_config {
-    int dtype;          /* DIT_BF16 or DIT_F32: weights and inner activations */
-    int x_dtype;        /* storage of the block input x (residual stream) */
-    int y_dtype;        /* storage of the block output y */
+    int dtype;          /* weights and cond: DIT_BF16 or DIT_F32 */
+    int act_dtype;      /* activations between the steps (a, qkv, O, b, f): DIT_F16 or
+                           DIT_BF16 for bf16 weights, DIT_F32 for fp32 weights */
+    int x_dtype;        /* block input x (residual stream): DIT_BF16 or DIT_F32 */
+    int y_dtype;        /* block output y: DIT_F32 or DIT_BF16 */
     int d;              /* hidden size = n_heads * head_dim */
     int n_heads;
     int head_dim;       /* must be 128 */
@@ -177,8 +190,8 @@ size_t dit_block_workspace_size(const dit_block_config* cfg, int single_stream);
  *   O = joint attention over [text; image];  h_s = x_s + gate1 (O_s W_o,s^T)
  *   b_s = (1+scale2) RMSNorm(h_s) + shift2;  [g|u] = b_s W_in,s^T
  *   y_s = h_s + gate2 ((SiLU(g) * u) W_down,s^T)
- * Storage: the AdaLN vectors and h are fp32; a, qkv, O, b and f are dtype;
- * x is x_dtype and y is y_dtype.
+ * Storage: the AdaLN vectors and h are fp32; a, qkv, O, b and f are
+ * act_dtype; x is x_dtype and y is y_dtype.
  *
  *  cfg, txt, img (host)
  *  cond      [d_cond] of dtype (shared by both streams)

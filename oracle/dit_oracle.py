@@ -8,8 +8,8 @@ draws, no arithmetic of the method).
 
 What it computes is the plain definition of each stage, in float64, reading
 the same storage bits the GPU gets (bf16 widened exactly, or float32) and
-never rounding in between.  numpy's matmul serves as the matrix-product
-primitive; everything else is written out.
+never rounding in between: intermediate results stay exact float64.  numpy's
+matmul serves as the matrix-product primitive; everything else is written out.
 
 Sources (the "CUDA codepath !" thread, antirez/iris.c issue #15):
   * the cuBLAS/custom-kernel reply lists the operations of the transformer:
@@ -44,34 +44,16 @@ F64 = np.float64
 # --- storage -----------------------------------------------------------------
 
 def widen(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Storage (bf16 bit pattern as uint16, or float32) -> exact float64."""
+    """Storage (bf16 bit pattern as uint16, float16 or float32) -> exact float64."""
     if dtype == "bf16":
         u = np.ascontiguousarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return u.view(np.float32).astype(F64)
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(F64)
+    if dtype == "f16":
+        return np.asarray(a, dtype=np.float16).astype(F64)
     if dtype == "f64":
         return np.asarray(a, dtype=F64)
-    raise ValueError(dtype)
-
-
-def store(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Value of x after being stored in ``dtype`` (round-to-nearest-even), as
-    float64.  'f64' keeps x exact.  bf16 keeps 8 significant bits and the
-    float32 exponent range; the rounding is taken directly from the float64
-    value (no double rounding).  Inputs are finite and far from the float32
-    overflow / underflow limits."""
-    x = np.asarray(x, dtype=F64)
-    if dtype == "f64":
-        return x
-    if dtype == "f32":
-        return x.astype(np.float32).astype(F64)
-    if dtype == "bf16":
-        u = np.ascontiguousarray(x).view(np.uint64)
-        drop = np.uint64(45)                       # 52 - 7 mantissa bits dropped
-        lsb = (u >> drop) & np.uint64(1)
-        r = ((u + (np.uint64(1) << np.uint64(44)) - np.uint64(1) + lsb) >> drop) << drop
-        return r.view(F64)
     raise ValueError(dtype)
 
 
@@ -209,25 +191,8 @@ def _w(ws: Dict[str, np.ndarray], name: str, dtype: str) -> np.ndarray:
     return widen(ws[name], dtype)
 
 
-def storage_plan(cfg, exact: bool = False) -> Dict[str, str]:
-    """Storage type of each tensor a stage hands to the next.
-
-    The bf16 workloads are bf16 weights and activations with float32
-    accumulation; the float32 workload is float32 throughout.  So every
-    activation handed from one step to the next (the modulated pre-norm a and
-    b, qkv, q/k after QK-norm + RoPE, the attention output O, the SwiGLU
-    output f) is stored in the workload's type, the AdaLN vectors in float32,
-    and the residual stream (the mid-block h and the block output y) in
-    float32.  Arithmetic itself is exact float64.  ``exact=True`` stores
-    nothing (every tensor exact) to measure drift from exact arithmetic."""
-    if exact:
-        return {k: "f64" for k in ("act", "mod", "res")}
-    act = "bf16" if cfg.dtype == "bf16" else "f32"
-    return {"act": act, "mod": "f32", "res": "f32"}
-
-
 def double_block(cfg, inputs: Dict[str, object], rows_txt=None, rows_img=None,
-                 mods=None, keep: bool = False, exact: bool = False) -> Dict[str, np.ndarray]:
+                 mods=None, keep: bool = False) -> Dict[str, np.ndarray]:
     """Double-stream block (text and image keep their own weights, attention is joint).
 
     1. m_s = W_mod,s . SiLU(c) -> shift1, scale1, gate1, shift2, scale2, gate2
@@ -239,15 +204,14 @@ def double_block(cfg, inputs: Dict[str, object], rows_txt=None, rows_img=None,
     7. b_s = (1 + scale2) * RMSNorm(h_s) + shift2 ; [g | u] = b_s W_in,s^T
     8. y_s = h_s + gate2 * ((SiLU(g) * u) W_down,s^T)
 
-    Each step's output is stored per ``storage_plan``.  The inputs x_s are read
-    in their own storage type (``x_dtype``: the workload type for a first
-    block, float32 for a block fed by another block's output).
+    Every step is exact float64 arithmetic on the stored inputs.  The inputs x_s
+    are read in their own storage type (``x_dtype``: the workload type for a
+    first block, float32 for a block fed by another block's output).
     ``rows_txt`` / ``rows_img`` select output rows (index arrays within each
     stream); all tokens still enter the keys and values.  ``mods`` replaces
     the AdaLN vectors by given [6, d] arrays (special-case pins).  ``keep``
     returns the intermediates too."""
     t = cfg.dtype
-    st = storage_plan(cfg, exact)
     d, H, D, F = cfg.d, cfg.n_heads, cfg.head_dim, cfg.ffn_inner
     nt, ni = cfg.n_txt, cfg.n_img
     xdt = inputs.get("x_dtype", t)
@@ -260,31 +224,30 @@ def double_block(cfg, inputs: Dict[str, object], rows_txt=None, rows_img=None,
         if mods is not None:
             m[s] = np.asarray(mods[s], F64).reshape(6, d)
         else:
-            m[s] = store(adaln_modulation(_w(ws[s], "w_mod", t), cond), st["mod"]).reshape(6, d)
+            m[s] = adaln_modulation(_w(ws[s], "w_mod", t), cond).reshape(6, d)
     qkv = {}
     for s in ("txt", "img"):
-        a = store(modulate(xs[s], m[s][0], m[s][1], cfg.eps), st["act"])
-        qkv[s] = store(a @ _w(ws[s], "w_qkv", t).T, st["act"])
+        a = modulate(xs[s], m[s][0], m[s][1], cfg.eps)
+        qkv[s] = a @ _w(ws[s], "w_qkv", t).T
     q = np.concatenate([qkv["txt"][:, :d], qkv["img"][:, :d]], axis=0)
     k = np.concatenate([qkv["txt"][:, d:2 * d], qkv["img"][:, d:2 * d]], axis=0)
     v = np.concatenate([qkv["txt"][:, 2 * d:], qkv["img"][:, 2 * d:]], axis=0)
     qk_w = np.stack([widen(ws["txt"]["qk_norm_w"], t).reshape(2, D),
                      widen(ws["img"]["qk_norm_w"], t).reshape(2, D)])
     q, k = qk_rmsnorm_rope(q, k, H, D, qk_w, nt, cfg.eps_qk, pos, cfg.axes_dim, cfg.theta)
-    q, k = store(q, st["act"]), store(k, st["act"])
     rows = {"txt": np.arange(nt) if rows_txt is None else np.asarray(rows_txt),
             "img": np.arange(ni) if rows_img is None else np.asarray(rows_img)}
     q_rows = np.concatenate([rows["txt"], nt + rows["img"]])
-    o = store(joint_attention(q, k, v, H, D, q_rows=q_rows), st["act"])
+    o = joint_attention(q, k, v, H, D, q_rows=q_rows)
     o_s = {"txt": o[:len(rows["txt"])], "img": o[len(rows["txt"]):]}
     out: Dict[str, np.ndarray] = {}
     for s in ("txt", "img"):
         x_r = xs[s][rows[s]]
-        h = store(x_r + m[s][2] * (o_s[s] @ _w(ws[s], "w_o", t).T), st["res"])
-        b = store(modulate(h, m[s][3], m[s][4], cfg.eps), st["act"])
+        h = x_r + m[s][2] * (o_s[s] @ _w(ws[s], "w_o", t).T)
+        b = modulate(h, m[s][3], m[s][4], cfg.eps)
         gu = b @ _w(ws[s], "w_ffn_in", t).T
-        f = store(swiglu(gu[:, :F], gu[:, F:]), st["act"])
-        y = store(h + m[s][5] * (f @ _w(ws[s], "w_ffn_out", t).T), st["res"])
+        f = swiglu(gu[:, :F], gu[:, F:])
+        y = h + m[s][5] * (f @ _w(ws[s], "w_ffn_out", t).T)
         out["y_" + s] = y
         if keep:
             out.update({"mod_" + s: m[s], "h_" + s: h, "f_" + s: f, "o_" + s: o_s[s]})
@@ -294,7 +257,7 @@ def double_block(cfg, inputs: Dict[str, object], rows_txt=None, rows_img=None,
 
 
 def single_block(cfg, inputs: Dict[str, object], rows=None, mods=None,
-                 keep: bool = False, exact: bool = False) -> Dict[str, np.ndarray]:
+                 keep: bool = False) -> Dict[str, np.ndarray]:
     """Single-stream block over the concatenated sequence x = [text; image]:
 
     m = W_mod . SiLU(c) -> shift, scale, gate
@@ -303,9 +266,8 @@ def single_block(cfg, inputs: Dict[str, object], rows=None, mods=None,
     q, k <- RMSNorm per head * w ; RoPE ; O = joint attention
     y = x + gate * ([O | SiLU(g) * u] W_2^T)
 
-    Storage as in ``double_block``; x is read in ``x_dtype``."""
+    Exact float64 arithmetic as in ``double_block``; x is read in ``x_dtype``."""
     t = cfg.dtype
-    st = storage_plan(cfg, exact)
     d, H, D, F = cfg.d, cfg.n_heads, cfg.head_dim, cfg.ffn_inner
     n = cfg.n_tok
     cond = widen(inputs["cond"], t)
@@ -315,19 +277,18 @@ def single_block(cfg, inputs: Dict[str, object], rows=None, mods=None,
     if mods is not None:
         m = np.asarray(mods, F64).reshape(3, d)
     else:
-        m = store(adaln_modulation(_w(ws, "w_mod", t), cond), st["mod"]).reshape(3, d)
-    a = store(modulate(x, m[0], m[1], cfg.eps), st["act"])
+        m = adaln_modulation(_w(ws, "w_mod", t), cond).reshape(3, d)
+    a = modulate(x, m[0], m[1], cfg.eps)
     w1 = _w(ws, "w_1", t)
-    qkv = store(a @ w1[:3 * d].T, st["act"])
+    qkv = a @ w1[:3 * d].T
     q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
     qk_w = widen(ws["qk_norm_w"], t).reshape(1, 2, D)
     q, k = qk_rmsnorm_rope(q, k, H, D, qk_w, n, cfg.eps_qk, pos, cfg.axes_dim, cfg.theta)
-    q, k = store(q, st["act"]), store(k, st["act"])
     r = np.arange(n) if rows is None else np.asarray(rows)
-    o = store(joint_attention(q, k, v, H, D, q_rows=r), st["act"])
+    o = joint_attention(q, k, v, H, D, q_rows=r)
     gu = a[r] @ w1[3 * d:].T
-    f = store(swiglu(gu[:, :F], gu[:, F:]), st["act"])
-    y = store(x[r] + m[2] * (np.concatenate([o, f], axis=1) @ _w(ws, "w_2", t).T), st["res"])
+    f = swiglu(gu[:, :F], gu[:, F:])
+    y = x[r] + m[2] * (np.concatenate([o, f], axis=1) @ _w(ws, "w_2", t).T)
     out = {"y": y}
     if keep:
         out.update({"mod": m, "q": q, "k": k, "v": v, "o": o, "f": f, "a": a})

@@ -15,6 +15,8 @@ def dev(a, dtype: str):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
     if dtype == "f32":
         return torch.from_numpy(a.astype(np.float32, copy=False)).cuda()
+    if dtype == "f16":
+        return torch.from_numpy(a.astype(np.float16, copy=False)).cuda()
     if dtype == "i32":
         return torch.from_numpy(a.astype(np.int32, copy=False)).cuda()
     raise ValueError(dtype)
@@ -26,7 +28,7 @@ def host(t) -> np.ndarray:
 
 
 def tdtype(dtype: str):
-    return torch.bfloat16 if dtype == "bf16" else torch.float32
+    return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
 
 
 def metric(gpu: np.ndarray, ref: np.ndarray) -> float:
@@ -41,6 +43,17 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
 
 
+def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the storage type's values at |x| (bf16: 8 significant bits; fp16: 11, with
+    the subnormal spacing 2^-24 below 2^-14; fp32: 24)."""
+    ax = np.abs(np.asarray(x, np.float64))
+    if dtype == "bf16":
+        return bf16_ulp(ax)
+    if dtype == "f16":
+        return 2.0 ** (np.floor(np.log2(np.maximum(ax, 2.0 ** -14))) - 10)
+    return 2.0 ** (np.floor(np.log2(np.maximum(ax, 2.0 ** -126))) - 23)
+
+
 def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -49,10 +62,10 @@ def upload_stream_weights(w: dict, dtype: str) -> dict:
     return {k: dev(v, dtype) for k, v in w.items()}
 
 
-def shape_of(cfg: di.BlockConfig, mod, x_dtype=None, y_dtype=None, n_txt=None, n_img=None):
+def shape_of(cfg: di.BlockConfig, mod, x_dtype=None, y_dtype=None, n_txt=None, n_img=None, act_dtype=None):
     """attention_dit_block_amd.Shape for a generator config."""
     dt = mod.DIT_BF16 if cfg.dtype == "bf16" else mod.DIT_F32
-    return mod.Shape(dtype=dt, d=cfg.d, n_heads=cfg.n_heads, ffn_inner=cfg.ffn_inner,
+    return mod.Shape(dtype=dt, act_dtype=act_dtype, d=cfg.d, n_heads=cfg.n_heads, ffn_inner=cfg.ffn_inner,
                      n_txt=cfg.n_txt if n_txt is None else n_txt, n_img=cfg.n_img if n_img is None else n_img,
                      d_cond=cfg.dc, x_dtype=dt if x_dtype is None else x_dtype,
                      y_dtype=mod.DIT_F32 if y_dtype is None else y_dtype, eps=cfg.eps, eps_qk=cfg.eps_qk,

@@ -2,10 +2,9 @@
 
 The bar (per block output tensor, y_txt and y_img separately; the whole state for a
 single-stream block): max|gpu - oracle| / RMS(oracle) <= 2e-2 for the bf16 workloads
-and <= 1e-4 for the fp32 workload.  The oracle stores every stage output in the
-workload's activation type (bf16 / fp32) and keeps the residual stream in fp32, the
-storage the block itself uses; its drift from fully exact arithmetic is printed
-beside every bf16 result.
+and <= 1e-4 for the fp32 workload, against the exact float64 oracle on the same input
+bits.  The bf16 workloads keep bf16 weights and input; the library carries the
+activations between steps in fp16 (act_dtype) and the residual stream in fp32.
 """
 import numpy as np
 import pytest
@@ -13,7 +12,7 @@ import torch
 
 import dit_inputs as di
 from oracle import dit_oracle as o
-from gpu_util import dev, host, metric, say, shape_of, upload_stream_weights
+from gpu_util import bf16_ulp, dev, host, metric, say, shape_of, upload_stream_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -27,12 +26,13 @@ def dit():
     return m
 
 
-def run_double(dit, cfg, inp, x_dtype="same", y_dtype="f32"):
+def run_double(dit, cfg, inp, x_dtype="same", y_dtype="f32", act=None):
     """Run dit_block_forward on generator inputs; returns (y_txt, y_img) as float64."""
     t = cfg.dtype
     xdt = t if x_dtype == "same" else x_dtype
     sh = shape_of(cfg, dit, x_dtype=dit.DIT_BF16 if xdt == "bf16" else dit.DIT_F32,
-                  y_dtype=dit.DIT_BF16 if y_dtype == "bf16" else dit.DIT_F32)
+                  y_dtype=dit.DIT_BF16 if y_dtype == "bf16" else dit.DIT_F32,
+                  act_dtype={None: None, "bf16": dit.DIT_BF16, "f16": dit.DIT_F16}[act])
     ws = torch.empty(dit.block_workspace_size(sh), dtype=torch.uint8, device="cuda")
     yt = torch.empty(cfg.n_txt, cfg.d, dtype=torch.float32 if y_dtype == "f32" else torch.bfloat16, device="cuda")
     yi = torch.empty(cfg.n_img, cfg.d, dtype=yt.dtype, device="cuda")
@@ -45,11 +45,11 @@ def run_double(dit, cfg, inp, x_dtype="same", y_dtype="f32"):
     return host(yt), host(yi)
 
 
-def report(cfg, name, gpu, ref, exact=None):
+def report(cfg, name, gpu, ref, bar=None):
     m = metric(gpu, ref)
-    extra = "" if exact is None else f"  (oracle drift from exact arithmetic {metric(ref, exact):.4f})"
-    say(f"  {cfg.name} {name}: max|gpu-oracle|/RMS = {m:.3e}{extra}")
-    assert m <= BAR[cfg.dtype], f"{name}: {m:.3e} > {BAR[cfg.dtype]}"
+    bar = BAR[cfg.dtype] if bar is None else bar
+    say(f"  {cfg.name} {name}: max|gpu-oracle|/RMS = {m:.3e} (bar {bar:g})")
+    assert m <= bar, f"{name}: {m:.3e} > {bar}"
     return m
 
 
@@ -63,16 +63,15 @@ def test_double_block_fp32_workload(dit):
     report(cfg, "y_img", yi, ref["y_img"])
 
 
-@pytest.mark.parametrize("qk", ["ones", "random"])
-def test_double_block_bf16_small_ragged(dit, qk):
+@pytest.mark.parametrize("qk,act", [("ones", "f16"), ("random", "f16"), ("random", "bf16")])
+def test_double_block_bf16_small_ragged(dit, qk, act):
     cfg = di.BlockConfig("ragged_bf16_d384", "bf16", d=384, n_heads=3, ffn_inner=1152, n_txt=7, grid_h=5, grid_w=9)
-    say(f"double block {cfg.name} qk={qk}")
+    say(f"double block {cfg.name} qk={qk} act={act}")
     inp = di.double_block_inputs(cfg, seed=1, qk_norm=qk)
-    yt, yi = run_double(dit, cfg, inp)
+    yt, yi = run_double(dit, cfg, inp, act=act)
     ref = o.double_block(cfg, inp)
-    ex = o.double_block(cfg, inp, exact=True)
-    report(cfg, "y_txt", yt, ref["y_txt"], ex["y_txt"])
-    report(cfg, "y_img", yi, ref["y_img"], ex["y_img"])
+    report(cfg, "y_txt", yt, ref["y_txt"])
+    report(cfg, "y_img", yi, ref["y_img"])
 
 
 def test_double_block_c1(dit):
@@ -81,9 +80,21 @@ def test_double_block_c1(dit):
     inp = di.double_block_inputs(cfg, seed=0)
     yt, yi = run_double(dit, cfg, inp)
     ref = o.double_block(cfg, inp)
-    ex = o.double_block(cfg, inp, exact=True)
-    report(cfg, "y_txt", yt, ref["y_txt"], ex["y_txt"])
-    report(cfg, "y_img", yi, ref["y_img"], ex["y_img"])
+    report(cfg, "y_txt", yt, ref["y_txt"])
+    report(cfg, "y_img", yi, ref["y_img"])
+
+
+def test_double_block_c1_bf16_activations_drift(dit):
+    # bf16 activations between the steps: reported, not held to the 2e-2 bar -- bf16's 7-bit
+    # mantissa puts this workload's output 0.035-0.05 from exact arithmetic (gates up to ~2.6
+    # and scales up to ~3 amplify the rounding of the FFN operands).  Bounded at 0.1 here.
+    cfg = di.CONFIGS[1]
+    say(f"double block {cfg.name} with bf16 activations")
+    inp = di.double_block_inputs(cfg, seed=0)
+    yt, yi = run_double(dit, cfg, inp, act="bf16")
+    ref = o.double_block(cfg, inp)
+    report(cfg, "y_txt (bf16 act)", yt, ref["y_txt"], bar=0.1)
+    report(cfg, "y_img (bf16 act)", yi, ref["y_img"], bar=0.1)
 
 
 def test_double_block_c2(dit):
@@ -136,8 +147,11 @@ def test_double_block_fp32_input_bf16_output(dit):
     yt, yi = run_double(dit, cfg, inp, x_dtype="f32", y_dtype="bf16")
     ref = o.double_block(cfg, inp)
     for name, g, r in (("y_txt", yt, ref["y_txt"]), ("y_img", yi, ref["y_img"])):
-        # y is stored in bf16 here: compare with the oracle's value rounded once to bf16
-        np.testing.assert_allclose(g, o.store(r, "bf16"), rtol=2 ** -7, atol=1e-3)
+        # y is stored in bf16 here: within half a bf16 ulp of the exact value, plus the
+        # fp16-activation drift (<= 1e-3 RMS at this size)
+        rms = np.sqrt(np.mean(r ** 2))
+        bound = 0.5 * bf16_ulp(np.abs(r) + 1e-3 * rms) + 1e-3 * rms
+        assert np.all(np.abs(g - r) <= bound), name
 
 
 def test_double_block_zero_modulation_is_exact_identity(dit):

@@ -1,11 +1,17 @@
 """Per-entry-point parity of the HIP path against the fp64 oracle (GPU).
 
 Each test draws seeded inputs, runs one C-ABI entry point through the binding, and
-compares element by element with the oracle stage it implements.  Bars:
-  * fp32 calls: max|gpu - oracle| / RMS(oracle) <= 1e-4;
-  * bf16 calls: the same metric <= 2e-2, and every element within the rounding
-    the output storage allows (the output is the oracle's value rounded once to
-    bf16, up to fp32 arithmetic): |gpu - oracle| <= tol_ulp * ulp_bf16(oracle).
+compares element by element with the oracle stage it implements (exact float64 on the
+same input bits).  Bars, derived from the arithmetic of each call:
+  * fp32 outputs: max|gpu - oracle| / RMS(oracle) <= 1e-4;
+  * 16-bit outputs (bf16, fp16): the output is the exact value rounded once to the output
+    type, up to fp32 arithmetic (which can flip a rounding that falls within ~1e-6 of a
+    tie), so every element must lie within tol_ulp ulps of the exact value.  A max/RMS bar
+    cannot resolve this: one bf16 ulp at the largest magnitudes of these tensors is
+    already ~2% of their RMS;
+  * attention (16-bit): the probabilities enter the PV product rounded (fp16: 2^-11
+    relative; bf16: two terms, 2^-16), which adds at most that fraction of
+    attention(q, k, |v|) -- a quantity the oracle computes exactly.
 Every test also checks that the library really launched (dit_launch_count).
 """
 import numpy as np
@@ -14,7 +20,7 @@ import torch
 
 import dit_inputs as di
 from oracle import dit_oracle as o
-from gpu_util import dev, host, metric, bf16_ulp, say, tdtype
+from gpu_util import dev, host, metric, ulp, say, tdtype
 
 pytestmark = pytest.mark.gpu
 
@@ -38,41 +44,55 @@ def check(gpu, ref, dtype, tol_ulp=0.6, what=""):
     if dtype == "f32":
         assert m <= 1e-4, f"{what}: max/RMS {m:.3e} > 1e-4"
         return m
-    assert m <= 2e-2, f"{what}: max/RMS {m:.3e} > 2e-2"
     err = np.abs(gpu - ref)
-    bound = tol_ulp * bf16_ulp(ref) + 1e-6 * np.sqrt(np.mean(ref ** 2))
+    bound = tol_ulp * ulp(ref, dtype) + 1e-6 * np.sqrt(np.mean(ref ** 2))
     bad = err > bound
     assert not bad.any(), (f"{what}: {bad.sum()} elements beyond {tol_ulp} ulp, worst "
                            f"{np.max(err / bound):.2f}x at {np.unravel_index(np.argmax(err / bound), err.shape)}")
     return m
 
 
+def check_attention(gpu, ref, ref_abs, dtype, what="O"):
+    rel = 2.0 ** -11 if dtype == "f16" else 2.0 ** -16
+    perr = (rel + 1e-5) * ref_abs
+    bound = 0.5 * ulp(np.abs(ref) + perr, dtype) * 1.001 + perr
+    err = np.abs(gpu - ref)
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {bad.sum()} elements beyond the bound, worst "
+                           f"{np.max(err / bound):.2f}x at {np.unravel_index(np.argmax(err / bound), err.shape)}")
+    say(f"  {what}: max err/bound {np.max(err / bound):.3f}, max|gpu-oracle|/RMS {metric(gpu, ref):.2e}")
+
+
 ROPE_CASES = [
-    ("f32", 16, 8, 8, 2),       # the fp32 workload's shape
-    ("bf16", 512, 64, 64, 24),  # 512 text + 64x64 image tokens, 24 heads
-    ("bf16", 5, 3, 7, 3),       # ragged
-    ("bf16", 1, 1, 1, 1),       # one text and one image token
-    ("bf16", 0, 2, 3, 2),       # image only
+    # (q/k dtype, weight dtype, n_txt, grid h, grid w, heads)
+    ("f32", "f32", 16, 8, 8, 2),        # the fp32 workload's shape
+    ("f16", "bf16", 512, 64, 64, 24),   # the bf16 block: fp16 activations, bf16 QK-norm weights
+    ("bf16", "bf16", 512, 64, 64, 24),
+    ("f16", "bf16", 5, 3, 7, 3),        # ragged
+    ("bf16", "bf16", 1, 1, 1, 1),       # one text and one image token
+    ("f16", "f16", 0, 2, 3, 2),         # image only
 ]
 
 
-@pytest.mark.parametrize("dtype,n_txt,gh,gw,heads", ROPE_CASES)
-def test_qk_rmsnorm_rope(dit, dtype, n_txt, gh, gw, heads):
-    say(f"qk_rmsnorm_rope {dtype} n_txt={n_txt} grid={gh}x{gw} heads={heads}")
-    cfg = _cfg(dtype, n_txt, gh, gw, heads)
+@pytest.mark.parametrize("dtype,wdt,n_txt,gh,gw,heads", ROPE_CASES)
+def test_qk_rmsnorm_rope(dit, dtype, wdt, n_txt, gh, gw, heads):
+    say(f"qk_rmsnorm_rope {dtype} w={wdt} n_txt={n_txt} grid={gh}x{gw} heads={heads}")
+    cfg = _cfg("f32" if wdt == "f16" else wdt, n_txt, gh, gw, heads)
     n, d = cfg.n_tok, cfg.d
     qkv = di.draw((n, 3 * d), 1.5, dtype, 7, "q")
     w = np.stack([di._qk_norm_weights(cfg, 7, 0, "txt", "random"),
                   di._qk_norm_weights(cfg, 7, 0, "img", "random")])   # [2 sets][2][128]
+    if wdt == "f16":
+        w = w.astype(np.float16)
     pos = di.positions(n_txt, gh, gw)
     t = dev(qkv, dtype)
     before = dit.launch_count()
-    dit.qk_rmsnorm_rope(t[:, :d], t[:, d:2 * d], heads, dev(w, dtype), n_txt, dev(pos, "i32"), eps=1e-6)
+    dit.qk_rmsnorm_rope(t[:, :d], t[:, d:2 * d], heads, dev(w, wdt), n_txt, dev(pos, "i32"), eps=1e-6)
     torch.cuda.synchronize()
     assert dit.launch_count() == before + 1
     out = host(t)
     x = o.widen(qkv, dtype)
-    rq, rk = o.qk_rmsnorm_rope(x[:, :d], x[:, d:2 * d], heads, 128, o.widen(w, dtype), n_txt, 1e-6, pos, AXES, 1e4)
+    rq, rk = o.qk_rmsnorm_rope(x[:, :d], x[:, d:2 * d], heads, 128, o.widen(w, wdt), n_txt, 1e-6, pos, AXES, 1e4)
     check(out[:, :d], rq, dtype, what="q")
     check(out[:, d:2 * d], rk, dtype, what="k")
     np.testing.assert_array_equal(out[:, 2 * d:], x[:, 2 * d:])       # v untouched
@@ -95,33 +115,35 @@ def test_qk_rmsnorm_rope_large_positions(dit):
 
 
 ADALN_CASES = [
-    ("f32", "f32", 256, 6, 80),
-    ("bf16", "bf16", 3072, 6, 4608),
-    ("bf16", "f32", 3072, 6, 600),     # fp32 input (the residual stream h)
-    ("bf16", "bf16", 3072, 3, 37),     # single-stream block: 3 chunks, ragged rows
-    ("bf16", "bf16", 264, 6, 5),       # d not a multiple of 512
+    # (weight dtype, x dtype, out dtype, d, chunks, rows)
+    ("f32", "f32", "f32", 256, 6, 80),
+    ("bf16", "bf16", "f16", 3072, 6, 4608),   # the bf16 block's first pre-norm
+    ("bf16", "f32", "f16", 3072, 6, 600),     # fp32 input (the residual stream h)
+    ("bf16", "bf16", "bf16", 3072, 6, 512),
+    ("bf16", "bf16", "f16", 3072, 3, 37),     # single-stream block: 3 chunks, ragged rows
+    ("bf16", "bf16", "f16", 264, 6, 5),       # d not a multiple of 512
 ]
 
 
-@pytest.mark.parametrize("dtype,xdt,d,chunks,rows", ADALN_CASES)
-def test_adaln_modulate(dit, dtype, xdt, d, chunks, rows):
-    say(f"adaln_modulate {dtype} x={xdt} d={d} chunks={chunks} rows={rows}")
-    cond = di.draw((d,), 1.0, dtype, 9, "cond")
-    w = di.draw((chunks * d, d), 0.02, dtype, 9, "w_mod")
+@pytest.mark.parametrize("wdt,xdt,odt,d,chunks,rows", ADALN_CASES)
+def test_adaln_modulate(dit, wdt, xdt, odt, d, chunks, rows):
+    say(f"adaln_modulate w={wdt} x={xdt} out={odt} d={d} chunks={chunks} rows={rows}")
+    cond = di.draw((d,), 1.0, wdt, 9, "cond")
+    w = di.draw((chunks * d, d), 0.02, wdt, 9, "w_mod")
     x = di.draw((rows, d), 1.0, xdt, 9, "x")
     mod = torch.empty(chunks * d, dtype=torch.float32, device="cuda")
-    xo = torch.empty(rows, d, dtype=tdtype(dtype), device="cuda")
+    xo = torch.empty(rows, d, dtype=tdtype(odt), device="cuda")
     before = dit.launch_count()
-    dit.adaln_modulate(dev(cond, dtype), dev(w, dtype), chunks, d, mod, x=dev(x, xdt), x_out=xo,
+    dit.adaln_modulate(dev(cond, wdt), dev(w, wdt), chunks, d, mod, x=dev(x, xdt), x_out=xo,
                        shift_chunk=chunks - 3, scale_chunk=chunks - 2, eps=1e-6)
     torch.cuda.synchronize()
     assert dit.launch_count() == before + 2
-    m_ref, a_ref = o.adaln_modulate(o.widen(cond, dtype), o.widen(w, dtype), chunks, d, x=o.widen(x, xdt),
+    m_ref, a_ref = o.adaln_modulate(o.widen(cond, wdt), o.widen(w, wdt), chunks, d, x=o.widen(x, xdt),
                                     shift_chunk=chunks - 3, scale_chunk=chunks - 2, eps=1e-6)
     m_gpu = host(mod).reshape(chunks, d)
     assert metric(m_gpu, m_ref) <= 1e-5
-    # the bf16 output rounds the modulated value once; the fp32 vectors add < 1e-5 relative
-    check(host(xo), a_ref, dtype, tol_ulp=0.75, what="x_out")
+    # the output rounds the modulated value once; the fp32 vectors add < 1e-5 relative
+    check(host(xo), a_ref, odt, tol_ulp=0.75, what="x_out")
 
 
 def test_adaln_gemv_only(dit):
@@ -141,10 +163,12 @@ def test_adaln_gemv_only(dit):
 ATTN_CASES = [
     ("f32", 80, 2),
     ("f32", 333, 1),
-    ("bf16", 80, 2),
-    ("bf16", 1, 3),
+    ("f16", 80, 2),
+    ("f16", 1, 3),
+    ("f16", 77, 2),
+    ("f16", 1536, 24),
+    ("f16", 4608, 24),
     ("bf16", 77, 2),
-    ("bf16", 1536, 24),
     ("bf16", 4608, 24),
 ]
 
@@ -153,8 +177,6 @@ ATTN_CASES = [
 def test_joint_attention(dit, dtype, n, heads):
     say(f"joint_attention {dtype} n={n} heads={heads}")
     d = 128 * heads
-    # q, k with RMS ~1 per head after QK-norm in the block; draw N(0,1) and scale scores up
-    # to the block's range by drawing q with std 1.5
     qkv = di.draw((n, 3 * d), 1.0, dtype, 11, "q")
     t = dev(qkv, dtype)
     o_t = torch.empty(n, d, dtype=tdtype(dtype), device="cuda")
@@ -168,8 +190,11 @@ def test_joint_attention(dit, dtype, n, heads):
         rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(n).choice(n, 300, replace=False)]))
     ref = o.joint_attention(x[:, :d], x[:, d:2 * d], x[:, 2 * d:], heads, 128, q_rows=rows)
     got = host(o_t) if rows is None else host(o_t)[rows]
-    # bf16: P is rounded to bf16 before the PV product -> allow 1.5 ulp of the output
-    check(got, ref, dtype, tol_ulp=1.5, what="O")
+    if dtype == "f32":
+        check(got, ref, dtype, what="O")
+    else:
+        ref_abs = o.joint_attention(x[:, :d], x[:, d:2 * d], np.abs(x[:, 2 * d:]), heads, 128, q_rows=rows)
+        check_attention(got, ref, ref_abs, dtype)
 
 
 def test_joint_attention_strided_output_and_canary(dit):
@@ -178,16 +203,17 @@ def test_joint_attention_strided_output_and_canary(dit):
     say("joint_attention strided output")
     n, heads = 300, 4
     d = 128 * heads
-    qkv = di.draw((n, 3 * d), 1.0, "bf16", 12, "q")
-    t = dev(qkv, "bf16")
-    buf = torch.full((n, d + 640), float("nan"), dtype=torch.bfloat16, device="cuda")
+    qkv = di.draw((n, 3 * d), 1.0, "f16", 12, "q")
+    t = dev(qkv, "f16")
+    buf = torch.full((n, d + 640), float("nan"), dtype=torch.float16, device="cuda")
     dit.joint_attention(t[:, :d], t[:, d:2 * d], t[:, 2 * d:], buf[:, :d], heads)
     torch.cuda.synchronize()
     out = host(buf)
     assert np.isnan(out[:, d:]).all()
-    x = o.widen(qkv, "bf16")
+    x = o.widen(qkv, "f16")
     ref = o.joint_attention(x[:, :d], x[:, d:2 * d], x[:, 2 * d:], heads, 128)
-    check(out[:, :d], ref, "bf16", tol_ulp=1.5, what="O")
+    ref_abs = o.joint_attention(x[:, :d], x[:, d:2 * d], np.abs(x[:, 2 * d:]), heads, 128)
+    check_attention(out[:, :d], ref, ref_abs, "f16")
 
 
 def test_joint_attention_constant_scores_mean(dit):
@@ -195,20 +221,21 @@ def test_joint_attention_constant_scores_mean(dit):
     say("joint_attention constant scores")
     n, heads = 1000, 2
     d = 128 * heads
-    v = di.draw((n, d), 1.0, "bf16", 13, "v")
-    q = torch.zeros(n, d, dtype=torch.bfloat16, device="cuda")
-    k = dev(di.draw((n, d), 1.0, "bf16", 13, "k"), "bf16")
-    out = torch.empty(n, d, dtype=torch.bfloat16, device="cuda")
-    dit.joint_attention(q, k, dev(v, "bf16"), out, heads)
-    mean = o.widen(v, "bf16").mean(axis=0)
-    check(host(out), np.broadcast_to(mean, (n, d)), "bf16", tol_ulp=1.5, what="mean")
+    v = di.draw((n, d), 1.0, "f16", 13, "v")
+    q = torch.zeros(n, d, dtype=torch.float16, device="cuda")
+    k = dev(di.draw((n, d), 1.0, "f16", 13, "k"), "f16")
+    out = torch.empty(n, d, dtype=torch.float16, device="cuda")
+    dit.joint_attention(q, k, dev(v, "f16"), out, heads)
+    vv = o.widen(v, "f16")
+    mean = np.broadcast_to(vv.mean(axis=0), (n, d))
+    check_attention(host(out), mean, np.broadcast_to(np.abs(vv).mean(axis=0), (n, d)), "f16", what="mean")
 
 
 def test_empty_calls_launch_nothing(dit):
     before = dit.launch_count()
-    q = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
-    dit.joint_attention(q, q, q, torch.empty(0, 256, dtype=torch.bfloat16, device="cuda"), 2)
+    q = torch.empty(0, 256, dtype=torch.float16, device="cuda")
+    dit.joint_attention(q, q, q, torch.empty(0, 256, dtype=torch.float16, device="cuda"), 2)
     pos = torch.empty(0, 4, dtype=torch.int32, device="cuda")
     w = torch.ones(2, 2, 128, dtype=torch.bfloat16, device="cuda")
-    dit.qk_rmsnorm_rope(q, torch.empty(0, 256, dtype=torch.bfloat16, device="cuda"), 2, w, 0, pos)
+    dit.qk_rmsnorm_rope(q, torch.empty(0, 256, dtype=torch.float16, device="cuda"), 2, w, 0, pos)
     assert dit.launch_count() == before

@@ -35,22 +35,20 @@ MUTANTS = {
     "softmax_axis": ("return e / np.sum(e, axis=-1, keepdims=True)",
                      "return e / np.sum(e, axis=0, keepdims=True)"),
     "swiglu_halves": ("return silu(g) * u", "return silu(u) * g"),
-    "gate1_chunk": ("h = store(x_r + m[s][2] *", "h = store(x_r + m[s][5] *"),
-    "shift2_scale2_swapped": ("b = store(modulate(h, m[s][3], m[s][4]", "b = store(modulate(h, m[s][4], m[s][3]"),
-    "ffn_residual_from_x": ("y = store(h + m[s][5]", "y = store(x_r + m[s][5]"),
+    "gate1_chunk": ("h = x_r + m[s][2] *", "h = x_r + m[s][5] *"),
+    "shift2_scale2_swapped": ("b = modulate(h, m[s][3], m[s][4]", "b = modulate(h, m[s][4], m[s][3]"),
+    "ffn_residual_from_x": ("y = h + m[s][5]", "y = x_r + m[s][5]"),
     "qk_sets_swapped": ("np.where(np.arange(n) < n_first, 0, min(1, w.shape[0] - 1))",
                         "np.where(np.arange(n) < n_first, min(1, w.shape[0] - 1), 0)"),
     "qk_weights_swapped": ("for which, t in ((0, q), (1, k)):", "for which, t in ((1, q), (0, k)):"),
     "single_ffn_rows": ("gu = a[r] @ w1[3 * d:].T", "gu = a[r] @ w1[2 * d:2 * d + 2 * F].T"),
     "single_o_f_order": ("np.concatenate([o, f], axis=1)", "np.concatenate([f, o], axis=1)"),
-    "bf16_ties_away": ("(np.uint64(1) << np.uint64(44)) - np.uint64(1) + lsb",
-                       "(np.uint64(1) << np.uint64(44))"),
     "v_from_k_block": ('v = np.concatenate([qkv["txt"][:, 2 * d:], qkv["img"][:, 2 * d:]], axis=0)',
                        'v = np.concatenate([qkv["txt"][:, d:2 * d], qkv["img"][:, d:2 * d]], axis=0)'),
     "attention_not_joint": (
-        "o = store(joint_attention(q, k, v, H, D, q_rows=q_rows), st[\"act\"])",
-        "o = store(np.concatenate([joint_attention(q[:nt], k[:nt], v[:nt], H, D, q_rows=rows['txt']),"
-        " joint_attention(q[nt:], k[nt:], v[nt:], H, D, q_rows=rows['img'])]), st[\"act\"])"),
+        "o = joint_attention(q, k, v, H, D, q_rows=q_rows)",
+        "o = np.concatenate([joint_attention(q[:nt], k[:nt], v[:nt], H, D, q_rows=rows['txt']),"
+        " joint_attention(q[nt:], k[nt:], v[nt:], H, D, q_rows=rows['img'])])"),
 }
 
 

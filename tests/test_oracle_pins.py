@@ -40,20 +40,6 @@ def tiny_cfg(**kw):
 
 # --- storage ----------------------------------------------------------------------
 
-def test_store_bf16_ties_and_sticky_bits():
-    x = np.array([1.0, 1 + 2**-8, 1 + 2**-8 + 2**-40, 1 + 2**-7 + 2**-8, 1 + 2**-7 + 2**-9,
-                  -(1 + 2**-8 + 2**-30), 3 * 2**-130])
-    want = np.array([1.0, 1.0, 1 + 2**-7, 1 + 2**-6, 1 + 2**-7, -(1 + 2**-7), 3 * 2**-130])
-    np.testing.assert_array_equal(o.store(x, "bf16"), want)
-
-
-def test_store_bf16_matches_torch_on_float32_values():
-    rng = np.random.default_rng(5)
-    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
-    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
-    np.testing.assert_array_equal(o.store(x.astype(np.float64), "bf16"), ref)
-
-
 def test_widen_bf16_is_exact():
     bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x3C23], dtype=np.uint16)
     want = np.array([1.0, -1.0, 3.140625, 0.0, 0.0099487304688])
@@ -355,10 +341,10 @@ def _mods(cfg, rng, **fix):
 def test_block_gate_chunks(tiny_inputs):
     cfg, inp = tiny_inputs
     rng = np.random.default_rng(11)
-    out = o.double_block(cfg, inp, mods=_mods(cfg, rng, c2=0.0), keep=True, exact=True)
+    out = o.double_block(cfg, inp, mods=_mods(cfg, rng, c2=0.0), keep=True)
     np.testing.assert_array_equal(out["h_txt"], o.widen(inp["x_txt"], "f32"))   # gate1 = 0 -> h = x
     assert np.abs(out["y_txt"] - out["h_txt"]).max() > 1e-3
-    out = o.double_block(cfg, inp, mods=_mods(cfg, rng, c5=0.0), keep=True, exact=True)
+    out = o.double_block(cfg, inp, mods=_mods(cfg, rng, c5=0.0), keep=True)
     np.testing.assert_array_equal(out["y_img"], out["h_img"])                  # gate2 = 0 -> y = h
 
 
@@ -383,7 +369,7 @@ def test_block_constant_scores_is_joint_mean(tiny_inputs):
         w = inp[s]["w_qkv"].copy()
         w[:cfg.d] = 0
         z[s] = dict(inp[s], w_qkv=w)
-    out = o.double_block(cfg, z, keep=True, exact=True)
+    out = o.double_block(cfg, z, keep=True)
     mean_v = out["v"].mean(axis=0)
     np.testing.assert_allclose(out["o_txt"], np.broadcast_to(mean_v, out["o_txt"].shape), rtol=1e-12)
     np.testing.assert_allclose(out["o_img"], np.broadcast_to(mean_v, out["o_img"].shape), rtol=1e-12)
@@ -404,7 +390,7 @@ def test_block_scale_minus_one_closed_chain():
     rng = np.random.default_rng(13)
     m = _mods(cfg, rng, c1=-1.0)
     m["img"][0] = m["txt"][0]
-    out = o.double_block(cfg, inp, mods=m, keep=True, exact=True)
+    out = o.double_block(cfg, inp, mods=m, keep=True)
     v_row = m["txt"][0] @ o.widen(inp["txt"]["w_qkv"], "f32")[2 * cfg.d:].T
     for s in ("txt", "img"):
         want = o.widen(inp["x_" + s], "f32") + m[s][2] * (v_row @ o.widen(inp[s]["w_o"], "f32").T)
@@ -433,7 +419,7 @@ def test_block_one_hot_routing_layout():
         wo = np.zeros((d, d), np.float32)
         wo[j, c] = 1.0
         inp[s] = dict(inp[s], w_qkv=w, w_o=wo)
-    out = o.double_block(cfg, inp, mods=m, keep=True, exact=True)
+    out = o.double_block(cfg, inp, mods=m, keep=True)
     a_all = np.concatenate([o.rms_norm(o.widen(inp["x_txt"], "f32"), cfg.eps),
                             o.rms_norm(o.widen(inp["x_img"], "f32"), cfg.eps)])
     want = a_all[:, i].mean()
@@ -459,7 +445,7 @@ def test_block_swiglu_halves_routing():
         w[3, 0] = 1.0
         w[F + 3, 1] = 1.0
         inp[s] = dict(inp[s], w_ffn_in=w)
-    out = o.double_block(cfg, inp, mods=m, keep=True, exact=True)
+    out = o.double_block(cfg, inp, mods=m, keep=True)
     for s in ("txt", "img"):
         b = o.rms_norm(out["h_" + s], cfg.eps)
         np.testing.assert_allclose(out["f_" + s][:, 3], o.silu(b[:, 0]) * b[:, 1], rtol=1e-12)
@@ -469,14 +455,14 @@ def test_block_swiglu_halves_routing():
 def test_block_token_permutation_equivariance():
     cfg = tiny_cfg(grid_h=3, grid_w=3)
     inp = di.double_block_inputs(cfg, seed=18, qk_norm="random")
-    out = o.double_block(cfg, inp, exact=True)
+    out = o.double_block(cfg, inp)
     perm = np.random.default_rng(19).permutation(cfg.n_img)
     p2 = dict(inp)
     p2["x_img"] = inp["x_img"][perm]
     pos = inp["pos"].copy()
     pos[cfg.n_txt:] = inp["pos"][cfg.n_txt:][perm]
     p2["pos"] = pos
-    out2 = o.double_block(cfg, p2, exact=True)
+    out2 = o.double_block(cfg, p2)
     np.testing.assert_allclose(out2["y_img"], out["y_img"][perm], rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(out2["y_txt"], out["y_txt"], rtol=1e-11, atol=1e-12)
 
@@ -510,27 +496,13 @@ def test_single_block_layout_routing():
     w2[0, 4] = 1.0                               # y col 0 <- O col 4
     w2[1, d + 6] = 1.0                           # y col 1 <- f col 6
     inp["w"] = dict(inp["w"], w_1=w1, w_2=w2)
-    out = o.single_block(cfg, inp, mods=m, keep=True, exact=True)
+    out = o.single_block(cfg, inp, mods=m, keep=True)
     x = o.widen(inp["x"], "f32")
     a = o.rms_norm(x, cfg.eps)
     dy = out["y"] - x
     np.testing.assert_allclose(dy[:, 0], a[:, 8].mean(), rtol=1e-12)      # q = k = 0 -> mean of v
     np.testing.assert_allclose(dy[:, 1], o.silu(a[:, 2]) * a[:, 3], rtol=1e-12)
     assert np.abs(dy[:, 2:]).max() == 0
-
-
-def test_storage_plan_rounds_activations_only():
-    cfg = tiny_cfg(dtype="bf16")
-    inp = di.double_block_inputs(cfg, seed=23)
-    out = o.double_block(cfg, inp, keep=True)
-    for name in ("q", "k", "v", "f_txt", "o_img"):
-        np.testing.assert_array_equal(o.store(out[name], "bf16"), out[name])
-    h = out["h_img"]
-    assert np.any(o.store(h, "bf16") != h)
-    np.testing.assert_array_equal(o.store(h, "f32"), h)
-    ex = o.double_block(cfg, inp, exact=True)
-    rms = np.sqrt(np.mean(ex["y_img"] ** 2))
-    assert 0 < np.abs(ex["y_img"] - out["y_img"]).max() / rms < 0.2
 
 
 def test_block_scale2_minus_one_makes_ffn_input_constant():
@@ -541,7 +513,7 @@ def test_block_scale2_minus_one_makes_ffn_input_constant():
     inp = di.double_block_inputs(cfg, seed=24)
     rng = np.random.default_rng(25)
     m = _mods(cfg, rng, c4=-1.0)
-    out = o.double_block(cfg, inp, mods=m, keep=True, exact=True)
+    out = o.double_block(cfg, inp, mods=m, keep=True)
     F = cfg.ffn_inner
     for s in ("txt", "img"):
         gu = m[s][3] @ o.widen(inp[s]["w_ffn_in"], "f32").T
