@@ -39,6 +39,9 @@ def parse():
     p.add_argument("--workload", default="c2", choices=["c0", "c1", "c2", "c3", "c4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="first run a plain device-to-device copy of BYTES (3 times), to scale HBM "
+                        "byte counters against a kernel of known traffic")
     return p.parse_args()
 
 
@@ -77,6 +80,15 @@ def main():
     cfg = di.config_by_name(args.workload)
     dev = torch.device("cuda:0")
     t = cfg.dtype
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy calibration: 3 copies of {n * 4} bytes", file=sys.stderr, flush=True)
+        del src, dst
 
     def up(a, dt):
         a = np.ascontiguousarray(a)
