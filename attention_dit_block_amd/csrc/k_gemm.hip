@@ -14,12 +14,14 @@
 // while it is staged (the MFMA needs one operand type; the conversion is exact).  Operands go
 // global -> LDS with global_load_lds_dwordx4 (no VGPR staging) where no conversion is needed,
 // double-buffered;
-// LDS rows are 128 B with the 16-byte chunk index XOR-swizzled by (row & 7) so the fragment
+// LDS rows are 128 B with the 16-byte chunk index XOR-swizzled (swz) so the fragment
 // reads are bank-conflict free.  The MFMA computes D[n][m], so each lane ends with four
 // consecutive output columns of one row and the epilogue reads / writes 8-16 B per lane.
-// Workgroups are remapped so each XCD gets a contiguous range of tiles, grouped along M.
+// Workgroups are remapped so each XCD gets a contiguous range of tiles, in N-major order.
 //
 // fp32 path: a plain LDS-tiled FMA kernel (no reduced-precision matrix math).
+#include <type_traits>
+
 #include "dev_common.h"
 #include "launch.h"
 
@@ -28,18 +30,21 @@ namespace dit {
 enum GemmMode { MODE_STORE = 0, MODE_RES = 1, MODE_SWIGLU = 2, MODE_MIXED = 3 };
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kGroupM = 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void tile_of(const GemmBatch& b, int L, int& pi, int& tm, int& tn) {
+    // Groups of G M-tiles; inside a group, consecutive tiles walk the G M-tiles of one N column,
+    // then the next column.  The tiles one XCD runs at the same time then form a compact
+    // block of about G x (32 / G) tiles, whose A and B tiles L2 shares.
     pi = (b.n > 1 && L >= b.p[1].tile_begin) ? 1 : 0;
     const GemmProblem& P = b.p[pi];
+    const int G0 = b.group_m > 0 ? b.group_m : 8;
     const int t = L - P.tile_begin;
-    const int per_group = kGroupM * P.tiles_n;
+    const int per_group = G0 * P.tiles_n;
     const int g = t / per_group;
-    const int first_m = g * kGroupM;
-    const int gsize = min(P.tiles_m - first_m, kGroupM);
+    const int first_m = g * G0;
+    const int gsize = min(P.tiles_m - first_m, G0);
     const int r = t - g * per_group;
     tm = first_m + r % gsize;
     tn = r / gsize;
@@ -54,6 +59,13 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
 }
 
 __device__ __forceinline__ float silu_acc(float g) { return g / (1.0f + __expf(-g)); }
+
+// LDS row swizzle of the staged tiles (rows of 128 B = 8 chunks of 16 B).  gfx950 serves a
+// ds_read_b128 16 lanes per cycle from 64 banks of 4 B (two 128-B rows per bank sweep), and a
+// fragment read has 16 consecutive rows at one chunk index: XOR-ing the chunk with (row >> 1) & 7
+// gives the 8 even rows 8 distinct chunks in one half of the banks and the 8 odd rows 8 in the
+// other half.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 template <int AT> struct Frag;
 template <> struct Frag<BF16> { typedef bf16x8_v T; };
@@ -78,8 +90,15 @@ __device__ __forceinline__ void store4_dt(void* base, size_t off, int dt, const 
 // goes the same way when AT == BF16; when AT == F16 it is loaded into VGPRs, converted to fp16
 // (exact: bf16 values are fp16 values in fp16's normal range) and written to the same LDS
 // layout, so both operands of the fp16 MFMA come from one swizzled layout.
-template <int MODE, int AT>
-__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmBatch b) {
+//
+// WN = waves along N.  WN = 2: 4 waves (one per SIMD), each a 128 x 128 sub-tile (4 x 4 MFMA
+// tiles, 256 accumulators).  WN = 4: 8 waves (two per SIMD), each 128 x 64 (4 x 2 MFMA tiles,
+// 128 accumulators) -- the second wave on a SIMD issues MFMAs while the first waits on LDS.
+template <int MODE, int AT, int WN>
+__device__ __forceinline__ void gemm_mfma_body(const GemmBatch& b) {
+    constexpr int NW = 2 * WN;                     // waves per workgroup
+    constexpr int NB = 4 / (WN / 2);               // 32-wide n-blocks per wave (4 or 2)
+    constexpr int LPW = 32 / NW;                   // 1 KB load instructions per wave per operand
     __shared__ __attribute__((aligned(1024))) char smem[2 * (BM + BN) * BK * 2];
     constexpr int kStage = (BM + BN) * BK * 2;     // bytes of one A+B stage
     constexpr int kBOff = BM * BK * 2;             // B tile offset within a stage
@@ -97,19 +116,19 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmBatch b) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 
-    // ---- global -> LDS load plan: wave w, instruction i covers tile rows (w*8+i)*8 .. +7;
+    // ---- global -> LDS load plan: wave w, instruction i covers tile rows (w*LPW+i)*8 .. +7;
     //      lane l writes LDS bytes l*16 .. l*16+15 of that 1 KB block = row l/8, chunk l%8,
-    //      which holds global chunk (l%8) ^ (row & 7) of the row.
-    const bf16_t* gA[8];
-    const bf16_t* gB[8];
+    //      which holds global chunk (l%8) ^ swz(row) of the row.
+    const bf16_t* gA[LPW];
+    const bf16_t* gB[LPW];
     {
         const int lr = lane >> 3, lc = lane & 7;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = (wave * 8 + i) * 8 + lr;
-            const int chunk = lc ^ (row & 7);
+        for (int i = 0; i < LPW; ++i) {
+            const int row = (wave * LPW + i) * 8 + lr;
+            const int chunk = lc ^ swz(row);
             int am = m0 + row;
             am = am < M ? am : M - 1;
             gA[i] = reinterpret_cast<const bf16_t*>(P.A) + (size_t)am * P.lda + chunk * 8;
@@ -126,82 +145,130 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmBatch b) {
             gB[i] = reinterpret_cast<const bf16_t*>(P.B) + (size_t)bn * P.ldb + chunk * 8;
         }
     }
-    u32x4_v breg[8];
+    u32x4_v breg[LPW];
     auto issue_loads = [&](int buf, int k0) {
+        if constexpr (AT == F16) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_global_load_lds(gA[i] + k0, (lds_void*)(smem + buf * kStage + (wave * 8 + i) * 1024),
+            for (int i = 0; i < LPW; ++i) breg[i] = ld16(gB[i] + k0);  // issued first: waited on first
+        }
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            __builtin_amdgcn_global_load_lds(gA[i] + k0, (lds_void*)(smem + buf * kStage + (wave * LPW + i) * 1024),
                                              16, 0, 0);
             if constexpr (AT == BF16)
                 __builtin_amdgcn_global_load_lds(gB[i] + k0,
-                                                 (lds_void*)(smem + buf * kStage + kBOff + (wave * 8 + i) * 1024),
+                                                 (lds_void*)(smem + buf * kStage + kBOff + (wave * LPW + i) * 1024),
                                                  16, 0, 0);
-            else
-                breg[i] = ld16(gB[i] + k0);
         }
     };
     auto store_b = [&](int buf) {
         if constexpr (AT == F16) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < LPW; ++i) {
                 u32x4_v w;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(breg[i][j]);
-                *reinterpret_cast<u32x4_v*>(smem + buf * kStage + kBOff + (wave * 8 + i) * 1024 + lane * 16) = w;
+                *reinterpret_cast<u32x4_v*>(smem + buf * kStage + kBOff + (wave * LPW + i) * 1024 + lane * 16) = w;
             }
         }
     };
 
     // ---- fragment read offsets.  A fragment (m-block j): row wm*128 + j*32 + (lane & 31);
     //      B fragment (n-block j): a 32-row block of this wave's B rows (gate and up halves for
-    //      SwiGLU tiles).
-    int a_row[4], b_row[4];
+    //      SwiGLU tiles: the first NB/2 blocks gate, the last NB/2 the matching up rows).
+    int a_row[4], b_row[NB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        a_row[j] = wm * 128 + j * 32 + (lane & 31);
-        if (swiglu) b_row[j] = (j < 2 ? wn * 64 + j * 32 : BN / 2 + wn * 64 + (j - 2) * 32) + (lane & 31);
-        else b_row[j] = wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; ++j) a_row[j] = wm * 128 + j * 32 + (lane & 31);
+    constexpr int WNR = BN / WN;                   // B rows per wave
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        if (swiglu) b_row[j] = (j < NB / 2 ? wn * (WNR / 2) + j * 32 : BN / 2 + wn * (WNR / 2) + (j - NB / 2) * 32)
+                               + (lane & 31);
+        else b_row[j] = wn * WNR + j * 32 + (lane & 31);
     }
     const int khalf = lane >> 5;
 
-    f32x16_v acc[4][4];
+    f32x16_v acc[NB][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
     const int nk = K / BK;
+    // Fragments for k16 sub-step s of a staged tile (LDS byte offset `base` of its A tile).
+    auto read_frags = [&](FragT* fa, FragT* fb, int base, int s) {
+        const int c = 2 * s + khalf;
+        const char* la = smem + base;
+        const char* lb = la + kBOff;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            fa[j] = *reinterpret_cast<const FragT*>(la + a_row[j] * 128 + ((c ^ swz(a_row[j])) << 4));
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            fb[j] = *reinterpret_cast<const FragT*>(lb + b_row[j] * 128 + ((c ^ swz(b_row[j])) << 4));
+    };
+
     issue_loads(0, 0);
     store_b(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int it = 0; it < nk; ++it) {
+    FragT fa[2][4], fb[2][NB];
+    // One k-step on the staged tile `buf`.  MORE: the next tile exists -- issue its loads
+    // and (fp16) write its converted weight tile; the body is then one basic block, so the
+    // scheduling groups below apply to all of it.
+    auto kstep = [&]<bool MORE>(int it) {
+        constexpr int kMFMA = 0x008, kVALU = 0x002, kDSR = 0x100, kDSW = 0x200, kVMEM = 0x020;
+        constexpr int kReads = 4 + NB, kMfmas = 4 * NB;
         const int buf = it & 1;
-        const bool more = it + 1 < nk;
-        if (more) issue_loads(buf ^ 1, (it + 1) * BK);
-        const char* la = smem + buf * kStage;
-        const char* lb = la + kBOff;
+        // Each k16 sub-step is its own scheduling region: its MFMAs, with the next sub-step's
+        // fragment reads placed between the first of them (they then have the remaining MFMAs
+        // of time to land), the next tile's global loads spread over sub-step 0, and (fp16
+        // path) the next weight tile's conversion + LDS writes over sub-step 3.
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
-            const int c = 2 * s + khalf;
-            FragT fa[4], fb[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                fa[j] = *reinterpret_cast<const FragT*>(la + a_row[j] * 128 + ((c ^ (a_row[j] & 7)) << 4));
-                fb[j] = *reinterpret_cast<const FragT*>(lb + b_row[j] * 128 + ((c ^ (b_row[j] & 7)) << 4));
+            const int cur = s & 1;
+            if (s + 1 < BK / 16) read_frags(fa[cur ^ 1], fb[cur ^ 1], buf * kStage, s + 1);
+            if constexpr (MORE) {
+                if (s == 0) issue_loads(buf ^ 1, (it + 1) * BK);
+                if constexpr (AT == F16) {
+                    if (s == BK / 16 - 1) store_b(buf ^ 1);
+                }
             }
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma32<AT>(fb[nb], fa[mb], acc[nb][mb]);
+                for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma32<AT>(fb[cur][nb], fa[cur][mb], acc[nb][mb]);
+            if (s + 1 < BK / 16) {
+#pragma unroll
+                for (int i = 0; i < kReads; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kDSR, 1, 0);
+                    if (MORE && s == 0 && i < LPW) __builtin_amdgcn_sched_group_barrier(kVMEM, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(kMFMA, kMfmas - kReads, 0);
+            } else if (AT == F16 && MORE) {
+#pragma unroll
+                for (int i = 0; i < LPW; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kVALU, 6, 0);
+                    __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kVALU, 6, 0);
+                    __builtin_amdgcn_sched_group_barrier(kDSW, 1, 0);
+                }
+                if (kMfmas > 2 * LPW) __builtin_amdgcn_sched_group_barrier(kMFMA, kMfmas - 2 * LPW, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (more) store_b(buf ^ 1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-    }
+        if constexpr (MORE) read_frags(fa[0], fb[0], (buf ^ 1) * kStage, 0);
+    };
+    read_frags(fa[0], fb[0], 0, 0);
+    for (int it = 0; it < nk - 1; ++it) kstep.template operator()<true>(it);
+    kstep.template operator()<false>(nk - 1);
 
     // ---- epilogue.  acc[nb][mb][q]: row m = m0 + wm*128 + mb*32 + (lane & 31),
     //      B-row offset within the n-block: 8*(q>>2) + 4*khalf + (q&3).
@@ -212,16 +279,16 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmBatch b) {
         if (m >= M) continue;
         if (swiglu) {
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
+            for (int nb = 0; nb < NB / 2; ++nb) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int col = n0 + wn * 64 + nb * 32 + 8 * i + 4 * khalf;
+                    const int col = n0 + wn * (WNR / 2) + nb * 32 + 8 * i + 4 * khalf;
                     if (col >= P.N) continue;
                     float f[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float g = acc[nb][mb][4 * i + j];
-                        const float u = acc[nb + 2][mb][4 * i + j];
+                        const float u = acc[nb + NB / 2][mb][4 * i + j];
                         f[j] = silu_acc(g) * u;
                     }
                     store4_dt(P.C, (size_t)m * P.ldc + col, P.c_dtype, f);
@@ -229,10 +296,10 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmBatch b) {
             }
         } else {
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
+            for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int col = n0 + wn * 128 + nb * 32 + 8 * i + 4 * khalf;
+                    const int col = n0 + wn * WNR + nb * 32 + 8 * i + 4 * khalf;
                     if (col >= P.N) continue;
                     float o[4];
 #pragma unroll
@@ -252,6 +319,13 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmBatch b) {
         }
     }
 }
+
+// The two workgroup layouts as kernels (launch bounds must not depend on a template parameter:
+// hipcc then emits no host launch stub).
+template <int MODE, int AT>
+__global__ __launch_bounds__(256, 1) void gemm_mfma_w4(GemmBatch b) { gemm_mfma_body<MODE, AT, 2>(b); }
+template <int MODE, int AT>
+__global__ __launch_bounds__(512, 1) void gemm_mfma_w8(GemmBatch b) { gemm_mfma_body<MODE, AT, 4>(b); }
 
 // ------------------------------------------------------------------------------------------
 // fp32 GEMM: 64 x 64 block tile, K step 16, 256 threads each owning a 4 x 4 output patch.
@@ -333,13 +407,26 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmBatch b) {
     else gemm_f32_tile<false>(P, tm, tn);
 }
 
+#ifndef DIT_GEMM_WN
+#define DIT_GEMM_WN 4
+#endif
+template <int AT, bool W8>
+static void launch_mfma_w(GemmBatch& b, hipStream_t s, bool all_store, bool all_res, bool all_swiglu) {
+    const dim3 grid(b.total_tiles), block(W8 ? 512 : 256);
+#define DIT_LAUNCH(MODE)                                                                          \
+    do {                                                                                          \
+        if constexpr (W8) hipLaunchKernelGGL((gemm_mfma_w8<MODE, AT>), grid, block, 0, s, b);     \
+        else hipLaunchKernelGGL((gemm_mfma_w4<MODE, AT>), grid, block, 0, s, b);                  \
+    } while (0)
+    if (all_store) DIT_LAUNCH(MODE_STORE);
+    else if (all_res) DIT_LAUNCH(MODE_RES);
+    else if (all_swiglu) DIT_LAUNCH(MODE_SWIGLU);
+    else DIT_LAUNCH(MODE_MIXED);
+#undef DIT_LAUNCH
+}
 template <int AT>
 static void launch_mfma(GemmBatch& b, hipStream_t s, bool all_store, bool all_res, bool all_swiglu) {
-    const dim3 grid(b.total_tiles), block(256);
-    if (all_store) hipLaunchKernelGGL((gemm_mfma_kernel<MODE_STORE, AT>), grid, block, 0, s, b);
-    else if (all_res) hipLaunchKernelGGL((gemm_mfma_kernel<MODE_RES, AT>), grid, block, 0, s, b);
-    else if (all_swiglu) hipLaunchKernelGGL((gemm_mfma_kernel<MODE_SWIGLU, AT>), grid, block, 0, s, b);
-    else hipLaunchKernelGGL((gemm_mfma_kernel<MODE_MIXED, AT>), grid, block, 0, s, b);
+    launch_mfma_w<AT, DIT_GEMM_WN == 4>(b, s, all_store, all_res, all_swiglu);
 }
 
 hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {

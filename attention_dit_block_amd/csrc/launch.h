@@ -83,6 +83,7 @@ struct GemmBatch {
     int n;
     int a_dtype;        // F32 (fp32 path, fp32 weights), BF16 (bf16 weights) or F16 (bf16 weights,
                         // converted to fp16 while they are staged)
+    int group_m;        // tile raster: groups of group_m M-tiles, N-major inside a group (0: 8)
     int total_tiles;    // filled by the launcher
 };
 hipError_t launch_gemm(GemmBatch& b, hipStream_t s);

@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--workload", default="c2", choices=["c0", "c1", "c2", "c3", "c4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--act", default="f16", choices=["f16", "bf16"],
+                   help="storage of the activations between the block's steps (bf16 workloads)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="first run a plain device-to-device copy of BYTES (3 times), to scale HBM "
                         "byte counters against a kernel of known traffic")
@@ -104,8 +106,9 @@ def main():
     inp = di.double_block_inputs(cfg, seed=args.seed)
     cond, pos = up(inp["cond"], t), up(inp["pos"], "i32")
     x_txt, x_img = up(inp["x_txt"], t), up(inp["x_img"], t)
+    act = None if t != "bf16" else (dit.DIT_F16 if args.act == "f16" else dit.DIT_BF16)
     shape = dit.Shape(dtype=tdt, d=cfg.d, n_heads=cfg.n_heads, ffn_inner=cfg.ffn_inner, n_txt=cfg.n_txt,
-                      n_img=cfg.n_img, d_cond=cfg.dc, x_dtype=tdt, y_dtype=dit.DIT_F32)
+                      n_img=cfg.n_img, d_cond=cfg.dc, x_dtype=tdt, y_dtype=dit.DIT_F32, act_dtype=act)
     ws = torch.empty(max(dit.block_workspace_size(shape), dit.block_workspace_size(shape, True)),
                      dtype=torch.uint8, device=dev)
     y_txt = torch.empty(cfg.n_txt, cfg.d, dtype=torch.float32, device=dev)
@@ -192,7 +195,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if t == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "blocks": cfg.n_double + cfg.n_single, "d": cfg.d, "heads": cfg.n_heads,
+        "config": {"workload": cfg.name, "activations": args.act if t == "bf16" else "f32", "blocks": cfg.n_double + cfg.n_single, "d": cfg.d, "heads": cfg.n_heads,
                    "ffn_inner": cfg.ffn_inner, "n_txt": cfg.n_txt, "n_img": cfg.n_img, "tokens": cfg.n_tok,
                    "gflop_per_step": round(flops / 1e9, 1)},
         "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
