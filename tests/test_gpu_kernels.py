@@ -166,6 +166,10 @@ ATTN_CASES = [
     ("f16", 80, 2),
     ("f16", 1, 3),
     ("f16", 77, 2),
+    ("f16", 64, 1),         # exactly one key tile
+    ("f16", 128, 1),        # two full tiles, no tail
+    ("f16", 130, 1),        # two full tiles + a 2-key tail
+    ("bf16", 200, 1),       # three full tiles + an 8-key tail
     ("f16", 1536, 24),
     ("f16", 4608, 24),
     ("bf16", 77, 2),
@@ -229,6 +233,44 @@ def test_joint_attention_constant_scores_mean(dit):
     vv = o.widen(v, "f16")
     mean = np.broadcast_to(vv.mean(axis=0), (n, d))
     check_attention(host(out), mean, np.broadcast_to(np.abs(vv).mean(axis=0), (n, d)), "f16", what="mean")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.21, 0.35])
+def test_joint_attention_softmax_scale(dit, scale):
+    # zero scale (uniform weights), a negative scale (the row max of the scaled scores is the
+    # min of the raw ones) and a non-default positive one
+    say(f"joint_attention scale={scale}")
+    n, heads = 200, 2
+    d = 128 * heads
+    qkv = di.draw((n, 3 * d), 1.0, "f16", 14, "q")
+    t = dev(qkv, "f16")
+    out = torch.empty(n, d, dtype=torch.float16, device="cuda")
+    dit.joint_attention(t[:, :d], t[:, d:2 * d], t[:, 2 * d:], out, heads, softmax_scale=scale)
+    x = o.widen(qkv, "f16")
+    ref = o.joint_attention(x[:, :d], x[:, d:2 * d], x[:, 2 * d:], heads, 128, scale=scale)
+    ref_abs = o.joint_attention(x[:, :d], x[:, d:2 * d], np.abs(x[:, 2 * d:]), heads, 128, scale=scale)
+    check_attention(host(out), ref, ref_abs, "f16")
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+def test_joint_attention_drifting_scores(dit, direction):
+    # scores that rise (or fall) steadily along the keys, over ~100 in base-2 units: the
+    # running max is raised again and again tile after tile (or never after the first)
+    say(f"joint_attention drifting scores, direction {direction}")
+    n, heads = 1000, 1
+    rng = np.random.default_rng(15)
+    b = np.linspace(-2.0, 4.0, n) * direction
+    q = np.ones((n, 128)) + 0.3 * rng.standard_normal((n, 128))
+    k = b[:, None] * np.ones((1, 128)) + 0.3 * rng.standard_normal((n, 128))
+    v = rng.standard_normal((n, 128))
+    qh, kh, vh = (np.asarray(a, np.float16) for a in (q, k, v))
+    out = torch.empty(n, 128, dtype=torch.float16, device="cuda")
+    dit.joint_attention(torch.from_numpy(qh).cuda(), torch.from_numpy(kh).cuda(), torch.from_numpy(vh).cuda(),
+                        out, heads)
+    x = [a.astype(np.float64) for a in (qh, kh, vh)]
+    ref = o.joint_attention(x[0], x[1], x[2], heads, 128)
+    ref_abs = o.joint_attention(x[0], x[1], np.abs(x[2]), heads, 128)
+    check_attention(host(out), ref, ref_abs, "f16")
 
 
 def test_empty_calls_launch_nothing(dit):
