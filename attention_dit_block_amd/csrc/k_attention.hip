@@ -5,8 +5,9 @@
 //
 // 16-bit kernel (bf16 or fp16 q, k, v).  A workgroup of 4 waves owns 128 queries of one head;
 // each wave 32 queries.  K and V tiles of 64 keys go from HBM straight into LDS
-// (global_load_lds, no VGPR staging), double-buffered: the next tile's loads are issued at the
-// start of a tile and awaited at its end, behind one barrier per tile.
+// (global_load_lds, no VGPR staging) through two 2-slot rings: at step j the workgroup loads
+// K tile j+2 and V tile j+1 while it computes the scores of tile j+1 (MFMA) next to the softmax
+// of tile j (VALU), then O += V_j P_j; one barrier per step.
 // Per key tile:
 //   S^T = K Q^T  with v_mfma_f32_32x32x16 (K fragment = A operand, Q fragment = B), so a lane
 //                holds 32 scores of ONE query: the row max needs one swap with lane ^ 32;
@@ -47,12 +48,12 @@ typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
 __device__ __forceinline__ int key_of_row(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
-// LDS rows are 16 chunks of 16 B.  K: chunk c of row r sits at position c ^ (r & 15), so the 16
-// lanes of a ds_read_b128 (16 keys, one chunk) hit 16 different bank groups.  V: position
-// c ^ ((r & 3) << 2), so the 4 rows read by each half-wave of a transposing read land in 4
-// different 64-byte bank ranges.
-__device__ __forceinline__ int kpos(int r, int c) { return c ^ (r & 15); }
-__device__ __forceinline__ int vpos(int r, int c) { return c ^ ((r & 3) << 2); }
+// K and V tiles are four slabs of 64 rows x 64 B (4 chunks of 16 B), slab b holding features
+// 32 b .. 32 b + 31 of each key.  K: chunk c of row r sits at position c ^ ((r >> 2) & 3), so the
+// 16 lanes of a ds_read_b128 (16 keys, one chunk) hit 16 different bank groups.  V is not
+// swizzled: the rows addressed by each half-wave of a transposing read are 4 consecutive
+// 64-byte rows of one slab, 256 contiguous bytes.
+__device__ __forceinline__ int kpos(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 template <int DT> struct AFrag;
 template <> struct AFrag<BF16> { typedef bf16x8_v T; };
@@ -77,11 +78,13 @@ __device__ __forceinline__ float half_swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int DT>
+// NEG: softmax_scale < 0 (the row max of the scaled scores is then the min of the raw ones).
+template <int DT, bool NEG>
 __global__ __launch_bounds__(256, 2) void attention_mfma_kernel(AttnArgs a) {
     typedef typename AFrag<DT>::T FragT;
-    // two stages of [K tile | V tile]
-    __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kTile];
+    // K ring (2 tiles) then V ring (2 tiles)
+    __shared__ __attribute__((aligned(1024))) char smem[4 * kTile];
+    constexpr int kV = 2 * kTile;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -112,66 +115,74 @@ __global__ __launch_bounds__(256, 2) void attention_mfma_kernel(AttnArgs a) {
         for (int es = 0; es < 8; ++es) qf[es] = *reinterpret_cast<const FragT*>(qp + 16 * es);
     }
 
-    // ---- load plan.  Each tile is 16 K and 16 V load instructions of 1 KB (4 rows); wave w
-    //      issues instructions 4w .. 4w+3 of each.  Lane l writes LDS bytes l*16 .. +15 of the
-    //      1 KB block: row 4i + l/16, position l%16, which holds chunk kpos / vpos of it.
-    const int lrow = lane >> 4, lp = lane & 15;
-    int k_el[4], v_el[4];        // element offset of the lane's chunk within its row
-    int t_row[4];                // tile row of instruction r
-    uint32_t k_b[4], v_b[4];     // byte offset of the lane's chunk from the tile's first row
+    // ---- load plan.  A tile is 16 load instructions of 1 KB; wave w issues instructions
+    //      4w .. 4w+3 of the K tile and of the V tile.  Instruction i = 4w + r fills rows
+    //      16r .. 16r+15 of slab w; lane l writes LDS bytes l*16 .. +15 of the 1 KB block: row
+    //      16r + l/4, position l%4, which holds chunk kpos(row, l%4) = (l%4) ^ (l/16) (K) or
+    //      chunk l%4 (V) of the slab row.
+    const uint32_t k_b = (uint32_t)((lane >> 2) * a.ld_k + 32 * wave + 8 * ((lane & 3) ^ (lane >> 4))) * 2u;
+    const uint32_t v_b = (uint32_t)((lane >> 2) * a.ld_v + 32 * wave + 8 * (lane & 3)) * 2u;
+    const size_t k_rstep = (size_t)16 * a.ld_k * 2;          // bytes between instructions r, r+1
+    const size_t v_rstep = (size_t)16 * a.ld_v * 2;
+    // tiles starting at key j0 into ring slot `slot`; rows past the last key repeat it
+    auto load_k = [&](int slot, int j0) {
+        char* dst = smem + slot * kTile;
+        if (j0 + AK <= N) {
+            const char* t = reinterpret_cast<const char*>(Kg + (size_t)j0 * a.ld_k);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = 4 * (4 * wave + r) + lrow;
-        t_row[r] = row;
-        k_el[r] = kpos(row, lp) * 8;
-        v_el[r] = vpos(row, lp) * 8;
-        k_b[r] = (uint32_t)(row * a.ld_k + k_el[r]) * 2u;
-        v_b[r] = (uint32_t)(row * a.ld_v + v_el[r]) * 2u;
-    }
-    auto load_tile = [&](int stage, int j0, bool clamp) {
-        char* base = smem + stage * 2 * kTile;
-        if (!clamp) {
-            const char* kt = reinterpret_cast<const char*>(Kg + (size_t)j0 * a.ld_k);
-            const char* vt = reinterpret_cast<const char*>(Vg + (size_t)j0 * a.ld_v);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                __builtin_amdgcn_global_load_lds(kt + k_b[r], (lds_void*)(base + (4 * wave + r) * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vt + v_b[r], (lds_void*)(base + kTile + (4 * wave + r) * 1024),
-                                                 16, 0, 0);
-            }
+            for (int r = 0; r < 4; ++r)
+                __builtin_amdgcn_global_load_lds(t + r * k_rstep + k_b, (lds_void*)(dst + (4 * wave + r) * 1024), 16, 0, 0);
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int key = min(j0 + t_row[r], N - 1);
-                __builtin_amdgcn_global_load_lds(Kg + (size_t)key * a.ld_k + k_el[r],
-                                                 (lds_void*)(base + (4 * wave + r) * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(Vg + (size_t)key * a.ld_v + v_el[r],
-                                                 (lds_void*)(base + kTile + (4 * wave + r) * 1024), 16, 0, 0);
+                const int key = min(j0 + 16 * r + (lane >> 2), N - 1);
+                __builtin_amdgcn_global_load_lds(Kg + (size_t)key * a.ld_k + 32 * wave + 8 * ((lane & 3) ^ (lane >> 4)),
+                                                 (lds_void*)(dst + (4 * wave + r) * 1024), 16, 0, 0);
+            }
+        }
+    };
+    auto load_v = [&](int slot, int j0) {
+        char* dst = smem + kV + slot * kTile;
+        if (j0 + AK <= N) {
+            const char* t = reinterpret_cast<const char*>(Vg + (size_t)j0 * a.ld_v);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                __builtin_amdgcn_global_load_lds(t + r * v_rstep + v_b, (lds_void*)(dst + (4 * wave + r) * 1024), 16, 0, 0);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = min(j0 + 16 * r + (lane >> 2), N - 1);
+                __builtin_amdgcn_global_load_lds(Vg + (size_t)key * a.ld_v + 32 * wave + 8 * (lane & 3),
+                                                 (lds_void*)(dst + (4 * wave + r) * 1024), 16, 0, 0);
             }
         }
     };
 
-    // ---- fragment read offsets (bytes within a stage).
-    // K fragment (block kb, feature step es): row 32 kb + key_of_row(l32), chunk 2 es + h32.
-    int k_off[8];
+    // ---- fragment read offsets (bytes within a ring slot).
+    // K fragment (block kb, feature step es): row 32 kb + key_of_row(l32) of slab es / 2, chunk
+    // 2 (es % 2) + h32 of the slab row.
+    int k_off[2];
     {
         const int kr = key_of_row(l32);
-#pragma unroll
-        for (int es = 0; es < 8; ++es) k_off[es] = kr * 256 + (kpos(kr, 2 * es + h32) << 4);
+        k_off[0] = kr * 64 + (kpos(kr, h32) << 4);
+        k_off[1] = kr * 64 + (kpos(kr, 2 + h32) << 4);
     }
     // V^T fragment (feature block eb, key step ks, half hf): lane i = lane % 16 of group
-    // g = lane / 16 addresses row 16 ks + 8 (g >> 1) + 4 hf + i / 4, features
-    // 32 eb + 16 (g & 1) + 4 (i % 4) .. +3.
-    int v_off[4];
-    {
-        const int g = lane >> 4, i = lane & 15;
-        const int row = 8 * (g >> 1) + (i >> 2);                 // + 16 ks + 4 hf (row & 3 unchanged)
+    // g = lane / 16 addresses slab eb, row 16 ks + 8 (g >> 1) + 4 hf + i / 4, features
+    // 16 (g & 1) + 4 (i % 4) .. +3 of the slab.
+    const int v_off = (8 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+
+    // S^T = K Q^T for the 64 keys in K slot `slot` (two 32-key blocks)
+    auto scores = [&](f32x16_v* sd, int slot) {
+        const char* kt = smem + slot * kTile;
 #pragma unroll
-        for (int eb = 0; eb < 4; ++eb) {
-            const int e = 32 * eb + 16 * (g & 1) + 4 * (i & 3);
-            v_off[eb] = kTile + row * 256 + (vpos(row, e >> 3) << 4) + (e & 7) * 2;
-        }
-    }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int es = 0; es < 8; ++es) {
+                const FragT kf = *reinterpret_cast<const FragT*>(kt + (es >> 1) * 4096 + kb * 32 * 64 + k_off[es & 1]);
+                sd[kb] = es == 0 ? amfma<DT>(kf, qf[es], f32x16_v{}) : amfma<DT>(kf, qf[es], sd[kb]);
+            }
+    };
 
     f32x16_v o[4];
 #pragma unroll
@@ -179,139 +190,133 @@ __global__ __launch_bounds__(256, 2) void attention_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) o[i][q] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
+    const int nt = (N + AK - 1) / AK;
+    f32x16_v sA[2], sB[2];
 
-    const int ntiles = (N + AK - 1) / AK;
-    // One key tile on stage STAGE.  TAIL: the tile runs past the last key.
-    auto tile = [&]<int STAGE, bool TAIL>(int jt) {
-        const int j0 = jt * AK;
-        if (jt + 1 < ntiles) load_tile(STAGE ^ 1, j0 + AK, j0 + 2 * AK > N);
-        const char* st = smem + STAGE * 2 * kTile;
-
-        // ---- S^T = K Q^T for two 32-key blocks
-        f32x16_v s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int q = 0; q < 16; ++q) s[kb][q] = 0.0f;
-#pragma unroll
-            for (int es = 0; es < 8; ++es) {
-                const FragT kf = *reinterpret_cast<const FragT*>(st + kb * 32 * 256 + k_off[es]);
-                s[kb] = amfma<DT>(kf, qf[es], s[kb]);
-            }
+    // One pipeline step on tile j (P = j & 1): its scores are in SC; issue the loads of K tile
+    // j + 2 and V tile j + 1, compute the scores of tile j + 1 into SN (unless LAST) while the
+    // softmax of tile j runs, then O += V_j P_j.
+    auto step = [&]<int P, bool LAST>(int j, f32x16_v* SC, f32x16_v* SN) {
+        const int j0 = j * AK;
+        if constexpr (!LAST) {
+            if (j + 2 < nt) load_k(P, j0 + 2 * AK);
+            load_v(P ^ 1, j0 + AK);
         }
-        // register q of block kb holds key j0 + 32 kb + 16 (q >> 3) + 8 h32 + (q & 7).  The row
-        // max of s * c2 is c2 times the max of s (c2 >= 0) or the min of s (c2 < 0); keys past
-        // the end take the value that drops out of that reduction, and probability 0 below.
+        // ---- region 1: S(j+1) MFMAs with the softmax of tile j
+        if constexpr (!LAST) scores(SN, P ^ 1);
+        // register q of block kb holds key j0 + 32 kb + 16 (q >> 3) + 8 h32 + (q & 7)
         auto masked = [&](int kb, int q) { return j0 + 32 * kb + 16 * (q >> 3) + 8 * h32 + (q & 7) >= N; };
-        float mt;
-        if (c2 >= 0.0f) {
-            if constexpr (TAIL) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        if (masked(kb, q)) s[kb][q] = -INFINITY;
-            }
-            float mx = s[0][0];
+        if constexpr (LAST) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int q = 0; q < 16; ++q) mx = fmaxf(mx, s[kb][q]);
-            mt = half_swap_max(mx) * c2;
-        } else {
-            if constexpr (TAIL) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        if (masked(kb, q)) s[kb][q] = INFINITY;
-            }
-            float mn = s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) mn = fminf(mn, s[kb][q]);
-            mt = -half_swap_max(-mn) * c2;
+                for (int q = 0; q < 16; ++q)
+                    if (masked(kb, q)) SC[kb][q] = NEG ? INFINITY : -INFINITY;
         }
+        float e0 = SC[0][0], e1 = SC[1][0];
+#pragma unroll
+        for (int q = 1; q < 16; ++q) {
+            e0 = NEG ? fminf(e0, SC[0][q]) : fmaxf(e0, SC[0][q]);
+            e1 = NEG ? fminf(e1, SC[1][q]) : fmaxf(e1, SC[1][q]);
+        }
+        const float mt = (NEG ? -half_swap_max(-fminf(e0, e1)) : half_swap_max(fmaxf(e0, e1))) * c2;
         // raise the running max only when this tile's max exceeds it by more than 2^kLazyMax
         const bool raise = mt > m_run + kLazyMax;
+        const float m_new = raise ? mt : m_run;
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);    // 1 unless raised; 0 on tile 0
+        m_run = m_new;
+        const float nm = -m_new;
+        // probabilities, packed as the PV operand: word 4 ks + t of ph (pl) holds keys
+        // 16 ks + 8 h32 + 2t, +1 (registers 8 (ks & 1) + 2t, +1 of block ks >> 1)
+        uint32_t ph[16], pl[DT == BF16 ? 16 : 1];
+        float lsum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int q = 0; q < 16; q += 2) {
+                float p0 = __builtin_amdgcn_exp2f(fmaf(SC[kb][q], c2, nm));
+                float p1 = __builtin_amdgcn_exp2f(fmaf(SC[kb][q + 1], c2, nm));
+                if constexpr (LAST) {
+                    if (masked(kb, q)) p0 = 0.0f;
+                    if (masked(kb, q + 1)) p1 = 0.0f;
+                }
+                lsum += p0 + p1;
+                const int w = 8 * kb + (q >> 1);
+                if constexpr (DT == BF16) {
+                    const uint32_t u0 = __float_as_uint(p0) & 0xffff0000u, u1 = __float_as_uint(p1) & 0xffff0000u;
+                    ph[w] = (u0 >> 16) | u1;
+                    pl[w] = pack_bf16x2(p0 - __uint_as_float(u0), p1 - __uint_as_float(u1));
+                } else {
+                    ph[w] = pack_f16x2(p0, p1);
+                }
+            }
+        // keep the probabilities next to the score MFMAs of the following tile (they would
+        // otherwise sink past the rescale branch below, into the PV phase); emits no code
+        asm volatile("" ::"v"(ph[0]), "v"(ph[1]), "v"(ph[2]), "v"(ph[3]), "v"(ph[4]), "v"(ph[5]), "v"(ph[6]),
+                     "v"(ph[7]), "v"(ph[8]), "v"(ph[9]), "v"(ph[10]), "v"(ph[11]), "v"(ph[12]), "v"(ph[13]),
+                     "v"(ph[14]), "v"(ph[15]), "v"(lsum));
+        if constexpr (DT == BF16)
+            asm volatile("" ::"v"(pl[0]), "v"(pl[1]), "v"(pl[2]), "v"(pl[3]), "v"(pl[4]), "v"(pl[5]), "v"(pl[6]),
+                         "v"(pl[7]), "v"(pl[8]), "v"(pl[9]), "v"(pl[10]), "v"(pl[11]), "v"(pl[12]), "v"(pl[13]),
+                         "v"(pl[14]), "v"(pl[15]));
+        l_run = fmaf(l_run, corr, lsum);
         if (__builtin_amdgcn_ballot_w64(raise)) {
-            const float m_new = raise ? mt : m_run;
-            const float corr = __builtin_amdgcn_exp2f(m_run - m_new);    // 0 on the first tile
-            m_run = m_new;
-            l_run *= corr;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) o[i][q] *= corr;
         }
-        // probabilities, in place of the scores
-        const float nm = -m_run;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                s[kb][q] = __builtin_amdgcn_exp2f(fmaf(s[kb][q], c2, nm));
-                if constexpr (TAIL) {
-                    if (masked(kb, q)) s[kb][q] = 0.0f;
-                }
-            }
-        // ---- O^T += V^T P^T: key step ks covers keys 16 ks .. 16 ks + 15 of the tile, held in
-        //      registers 8 (ks & 1) .. +7 of block ks >> 1
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int kb = ks >> 1, q0 = 8 * (ks & 1);
-            u32x4_v hv, lv;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float p0 = s[kb][q0 + 2 * t], p1 = s[kb][q0 + 2 * t + 1];
-                l_run += p0 + p1;
-                if constexpr (DT == BF16) {
-                    const uint32_t u0 = __float_as_uint(p0) & 0xffff0000u, u1 = __float_as_uint(p1) & 0xffff0000u;
-                    hv[t] = (u0 >> 16) | u1;
-                    lv[t] = pack_bf16x2(p0 - __uint_as_float(u0), p1 - __uint_as_float(u1));
-                } else {
-                    hv[t] = pack_f16x2(p0, p1);
-                }
-            }
-            const FragT pfh = __builtin_bit_cast(FragT, hv);
-            FragT vf[4];
+        // ---- region 2: O^T += V^T P^T; key step ks covers keys 16 ks .. +15 of the tile
+        const char* vt = smem + kV + P * kTile;
+        auto read_v = [&](FragT* vf, int ks) {
 #pragma unroll
             for (int eb = 0; eb < 4; ++eb) {
-                const char* vp = st + v_off[eb] + ks * 16 * 256;
+                const char* vp = vt + v_off + eb * 4096 + ks * 16 * 64;
                 const s16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-                const s16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * 256));
+                const s16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * 64));
                 const s16x8_v w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 vf[eb] = __builtin_bit_cast(FragT, w);
             }
+        };
+        FragT vf[2][4];
+        read_v(vf[0], 0);
 #pragma unroll
-            for (int eb = 0; eb < 4; ++eb) o[eb] = amfma<DT>(vf[eb], pfh, o[eb]);
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks < 3) read_v(vf[(ks + 1) & 1], ks + 1);
+            const u32x4_v hv = {ph[4 * ks], ph[4 * ks + 1], ph[4 * ks + 2], ph[4 * ks + 3]};
+#pragma unroll
+            for (int eb = 0; eb < 4; ++eb) o[eb] = amfma<DT>(vf[ks & 1][eb], __builtin_bit_cast(FragT, hv), o[eb]);
             if constexpr (DT == BF16) {
-                const FragT pfl = __builtin_bit_cast(FragT, lv);
+                const u32x4_v lv = {pl[4 * ks], pl[4 * ks + 1], pl[4 * ks + 2], pl[4 * ks + 3]};
 #pragma unroll
-                for (int eb = 0; eb < 4; ++eb) o[eb] = amfma<DT>(vf[eb], pfl, o[eb]);
+                for (int eb = 0; eb < 4; ++eb) o[eb] = amfma<DT>(vf[ks & 1][eb], __builtin_bit_cast(FragT, lv), o[eb]);
             }
         }
-        // the next tile has landed in LDS (own loads), for every wave (barrier); every wave is
-        // done reading this stage before the following tile's loads overwrite it
+        // the loads issued above have landed (own: waitcnt; every wave's: barrier), and every
+        // wave is done with the slots the next step's loads overwrite
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
 
-    load_tile(0, 0, AK > N);
+    // prologue: K tiles 0 and 1, V tile 0; scores of tile 0
+    load_k(0, 0);
+    if (nt > 1) load_k(1, AK);
+    load_v(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const int nfull = N / AK;                 // tiles with no key past the end
-    int jt = 0;
-    for (; jt + 1 < nfull; jt += 2) {
-        tile.template operator()<0, false>(jt);
-        tile.template operator()<1, false>(jt + 1);
+    scores(sA, 0);
+    __syncthreads();        // K slot 0 is refilled by step 0
+
+    int j = 0;
+    for (; j + 2 < nt; j += 2) {
+        step.template operator()<0, false>(j, sA, sB);
+        step.template operator()<1, false>(j + 1, sB, sA);
     }
-    if (jt < nfull) {
-        tile.template operator()<0, false>(jt);
-        if (++jt < ntiles) tile.template operator()<1, true>(jt);
-    } else if (jt < ntiles) {
-        tile.template operator()<0, true>(jt);
+    if (j + 1 < nt) {
+        step.template operator()<0, false>(j, sA, sB);
+        step.template operator()<1, true>(j + 1, sB, sA);
+    } else {
+        step.template operator()<0, true>(j, sA, sB);
     }
 
     const float inv = 1.0f / half_swap_sum(l_run);
@@ -389,8 +394,15 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     if (a.n_tok == 0) return hipSuccess;
     if (a.dtype == BF16 || a.dtype == F16) {
         const int nq = (a.n_tok + AQ - 1) / AQ;
-        if (a.dtype == F16) hipLaunchKernelGGL(attention_mfma_kernel<F16>, dim3(nq * a.n_heads), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(attention_mfma_kernel<BF16>, dim3(nq * a.n_heads), dim3(256), 0, s, a);
+        const dim3 grid(nq * a.n_heads), block(256);
+        const bool neg = a.scale < 0.0f;
+        if (a.dtype == F16) {
+            if (neg) hipLaunchKernelGGL((attention_mfma_kernel<F16, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((attention_mfma_kernel<F16, false>), grid, block, 0, s, a);
+        } else {
+            if (neg) hipLaunchKernelGGL((attention_mfma_kernel<BF16, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((attention_mfma_kernel<BF16, false>), grid, block, 0, s, a);
+        }
     } else {
         const int nq = (a.n_tok + FQ - 1) / FQ;
         hipLaunchKernelGGL(attention_f32_kernel, dim3(nq * a.n_heads), dim3(256), 0, s, a);
