@@ -8,16 +8,17 @@
 // One launch covers several problems (text and image streams, or the two halves of the
 // single-stream block's first linear).
 //
-// MFMA path (bf16 weights): 256-thread workgroups (4 waves, 2 x 2), a 256 x 256 x 64 block tile,
-// each wave a 128 x 128 sub-tile of 4 x 4 v_mfma_f32_32x32x16 tiles with fp32 accumulators.
-// Activations are bf16 or fp16; with fp16 activations the bf16 weight tile is converted to fp16
-// while it is staged (the MFMA needs one operand type; the conversion is exact).  Operands go
-// global -> LDS with global_load_lds_dwordx4 (no VGPR staging) where no conversion is needed,
-// double-buffered;
+// MFMA path (bf16 weights): a 256 x 256 x 64 block tile, 8 waves (2 along M x 4 along N), each a
+// 128 x 64 sub-tile of 4 x 2 v_mfma_f32_32x32x16 tiles with fp32 accumulators (a 4-wave layout
+// of 128 x 128 sub-tiles is kept as an alternative).  Activations are bf16 or fp16; with fp16
+// activations the bf16 weight tile is converted to fp16 while it is staged (the MFMA needs one
+// operand type; the conversion is exact).  Operands go global -> LDS with global_load_lds_dwordx4
+// (no VGPR staging) where no conversion is needed, double-buffered.
 // LDS rows are 128 B with the 16-byte chunk index XOR-swizzled (swz) so the fragment
 // reads are bank-conflict free.  The MFMA computes D[n][m], so each lane ends with four
 // consecutive output columns of one row and the epilogue reads / writes 8-16 B per lane.
-// Workgroups are remapped so each XCD gets a contiguous range of tiles, in N-major order.
+// Workgroups are remapped so each XCD gets a contiguous range of tiles, rastered in groups of
+// 8 M-tiles.
 //
 // fp32 path: a plain LDS-tiled FMA kernel (no reduced-precision matrix math).
 #include <type_traits>
