@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c4|c3] [--no-cpu-baseline]
 
 A step is one dit_block_forward call (all 9 kernels of the block) over the
-workload's synthetic inputs, already resident in HBM.  Prints ONE JSON line.
+workload's synthetic inputs, already resident in HBM (c3: the whole denoising
+step, 5 double-stream then 20 single-stream blocks).  Prints ONE JSON line.
 Throughput (``value``) is algorithmic TFLOP/s: 26 N d^2 (GEMMs) + 4 N^2 d
 (attention QK^T and PV) per block, 2 flop per multiply-add.
 
@@ -15,6 +16,7 @@ workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import subprocess
@@ -123,6 +125,7 @@ def main():
         state = torch.empty(cfg.n_tok, cfg.d, dtype=torch.float32, device=dev)
         st_t, st_i = state[:cfg.n_txt], state[cfg.n_txt:]
         for b in range(cfg.n_double):
+            print(f"setup: double block {b + 1}/{cfg.n_double}", file=sys.stderr, flush=True)
             bi = di.double_block_inputs(cfg, seed=args.seed, block=b)
             wt = {k: up(v, t) for k, v in bi["txt"].items()}
             wi = {k: up(v, t) for k, v in bi["img"].items()}
@@ -133,6 +136,7 @@ def main():
                 step_blocks.append(lambda wt=wt, wi=wi: dit.block_forward(shape32, wt, wi, cond, pos, st_t, st_i,
                                                                           st_t, st_i, ws))
         for b in range(cfg.n_single):
+            print(f"setup: single block {b + 1}/{cfg.n_single}", file=sys.stderr, flush=True)
             w = {k: up(v, t) for k, v in di.single_weights(cfg, args.seed, cfg.n_double + b).items()}
             step_blocks.append(lambda w=w: dit.single_block_forward(shape32, w, cond, pos, state, state, ws))
     setup_s = time.time() - t0
@@ -188,7 +192,7 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(by / (avg * 1e-3) / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(cfg.name, dom, args.act if t == "bf16" else "f32")
 
     out = {
         "metric": METRIC, "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1,
@@ -208,6 +212,38 @@ def main():
     if not args.no_cpu_baseline and cfg.n_single == 0:
         out["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(out), flush=True)
+
+
+# HBM bytes per launch, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) over this
+# bench, each counter scaled by what it reads for a plain device copy of known size (FETCH_SIZE
+# x2.0, WRITE_SIZE x1.0).  Keyed by workload, activation type and kernel; each entry holds the
+# SHA-256 prefix of the kernel's source at the time of the counters and is reported only while
+# that source is unchanged.
+_C2 = "c2_bf16_d3072_t512_i4096"
+MEASURED_TRAFFIC = {
+    (_C2, "f16", "gemm_ffn_in_swiglu"): {"bytes": 1097922687, "sha256": "19c7b2e89fa0b3fb"},
+    (_C2, "f16", "gemm_qkv"): {"bytes": 591397386, "sha256": "19c7b2e89fa0b3fb"},
+    (_C2, "f16", "gemm_ffn_down"): {"bytes": 657902957, "sha256": "19c7b2e89fa0b3fb"},
+    (_C2, "f16", "gemm_out_proj"): {"bytes": 282453664, "sha256": "19c7b2e89fa0b3fb"},
+    (_C2, "f16", "joint_attention"): {"bytes": 138860195, "sha256": "c42ae268179f09c3"},
+    (_C2, "f16", "adaln_gemv"): {"bytes": 226822596, "sha256": "1e8fd8af72198dea"},
+    (_C2, "f16", "qk_rmsnorm_rope"): {"bytes": 113914559, "sha256": "1e8fd8af72198dea"},
+    (_C2, "f16", "modulate_h"): {"bytes": 85410300, "sha256": "1e8fd8af72198dea"},
+    (_C2, "f16", "modulate_x"): {"bytes": 57100337, "sha256": "1e8fd8af72198dea"},
+}
+
+KERNEL_SOURCE = {"gemm": "k_gemm.hip", "joint_attention": "k_attention.hip"}
+
+
+def measured_traffic(workload, kernel, act):
+    e = MEASURED_TRAFFIC.get((workload, act, kernel))
+    if e is None:
+        return None
+    src = next((v for k, v in KERNEL_SOURCE.items() if kernel.startswith(k)), "k_norm.hip")
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "attention_dit_block_amd", "csrc", src)
+    with open(path, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    return e["bytes"] if sha.startswith(e["sha256"]) else None
 
 
 def cpu_baseline(cfg, inp):
