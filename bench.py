@@ -49,25 +49,44 @@ def parse():
     return p.parse_args()
 
 
-def kernel_work(cfg, name):
-    """Algorithmic work of one launch of a launch site: (flops, bytes, bound)."""
+def step_work(cfg):
+    """Algorithmic work of one step per launch site: {name: (flops, bytes, bound, launches)}.
+    A step is the workload's blocks: n_double double-stream blocks (the first reads the bf16 input,
+    later ones the fp32 residual stream), then n_single single-stream blocks (fp32 stream)."""
     n, d, F, dc = cfg.n_tok, cfg.d, cfg.ffn_inner, cfg.dc
-    es = 2 if cfg.dtype == "bf16" else 4
-    table = {
-        "gemm_qkv": (2.0 * n * d * 3 * d, None, "mfma"),
-        "gemm_out_proj": (2.0 * n * d * d, None, "mfma"),
-        "gemm_ffn_in_swiglu": (2.0 * n * d * 2 * F, None, "mfma"),
-        "gemm_ffn_down": (2.0 * n * F * d, None, "mfma"),
-        "gemm_linear1": (2.0 * n * d * (3 * d + 2 * F), None, "mfma"),
-        "gemm_linear2": (2.0 * n * (d + F) * d, None, "mfma"),
-        "joint_attention": (4.0 * n * n * d, None, "mfma"),
-        # HBM-bound: bytes read + written
-        "qk_rmsnorm_rope": (None, 4.0 * n * d * es + 16.0 * n, "hbm"),
-        "adaln_gemv": (None, 2.0 * 6 * d * dc * es, "hbm"),
-        "modulate_x": (None, 1.0 * n * d * (es + es), "hbm"),     # x (workload type) -> a
-        "modulate_h": (None, 1.0 * n * d * (4 + es), "hbm"),      # h (fp32) -> b
-    }
-    return table.get(name, (None, None, "?"))
+    es = 2 if cfg.dtype == "bf16" else 4            # weights and inter-step activations
+    work = {}
+
+    def add(name, flops=0.0, nbytes=0.0, bound="mfma"):
+        f, b_, _, c = work.get(name, (0.0, 0.0, bound, 0))
+        work[name] = (f + flops, b_ + nbytes, bound, c + 1)
+
+    for blk in range(cfg.n_double + cfg.n_single):
+        double = blk < cfg.n_double
+        ex = es if blk == 0 else 4                   # block input: workload type, then fp32 stream
+        add("adaln_gemv", nbytes=(12 if double else 3) * d * dc * es, bound="hbm")
+        add("modulate_x", nbytes=n * d * (ex + es), bound="hbm")
+        add("qk_rmsnorm_rope", nbytes=4.0 * n * d * es + 16.0 * n, bound="hbm")
+        add("joint_attention", flops=4.0 * n * n * d)
+        if double:
+            add("gemm_qkv", flops=2.0 * n * d * 3 * d)
+            add("gemm_out_proj", flops=2.0 * n * d * d)
+            add("modulate_h", nbytes=n * d * (4 + es), bound="hbm")
+            add("gemm_ffn_in_swiglu", flops=2.0 * n * d * 2 * F)
+            add("gemm_ffn_down", flops=2.0 * n * F * d)
+        else:
+            add("gemm_linear1", flops=2.0 * n * d * (3 * d + 2 * F))
+            add("gemm_linear2", flops=2.0 * n * (d + F) * d)
+    return work
+
+
+def kernel_work(cfg, name):
+    """Algorithmic work of one launch of a launch site, averaged over the step: (flops, bytes, bound)."""
+    w = step_work(cfg).get(name)
+    if w is None:
+        return None, None, "?"
+    f, b, bound, cnt = w
+    return (f / cnt if f else None), (b / cnt if b else None), bound
 
 
 def main():
