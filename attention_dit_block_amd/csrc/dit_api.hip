@@ -135,7 +135,7 @@ int validate_config(const dit_block_config* c) {
 
 // Workspace plan: 256-byte aligned sub-buffers.
 struct WsPlan {
-    size_t mod, act, qkv, o, h, f, of, total;
+    size_t mod, act, qkv, o, h, f, of, sk, sk_bytes, total;
 };
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 WsPlan plan_workspace(const dit_block_config* c, int single) {
@@ -156,6 +156,9 @@ WsPlan plan_workspace(const dit_block_config* c, int single) {
         p.qkv = take(n * 3 * d * es);
         p.of = take(n * (d + F) * es);
     }
+    // the GEMMs' stream-K scratch (16-bit paths), shared by the block's GEMMs in stream order
+    p.sk_bytes = c->dtype == DIT_BF16 ? gemm_sk_scratch_bytes() : 0;
+    p.sk = take(p.sk_bytes);
     p.total = off;
     return p;
 }
@@ -364,6 +367,7 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
 
     // 3. qkv = a W_qkv^T
     GemmBatch gq{};
+    gq.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     gq.a_dtype = c.act_dtype;
     {
         int k = 0;
@@ -389,6 +393,7 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
 
     // 6. h = x + gate1 * (O W_o^T)   (fp32)
     GemmBatch go{};
+    go.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     go.a_dtype = c.act_dtype;
     {
         int k = 0;
@@ -411,6 +416,7 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
 
     // 8. f = SiLU(b W_gate^T) * (b W_up^T)
     GemmBatch gf{};
+    gf.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     gf.a_dtype = c.act_dtype;
     {
         int k = 0;
@@ -423,6 +429,7 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
 
     // 9. y = h + gate2 * (f W_down^T)
     GemmBatch gd{};
+    gd.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     gd.a_dtype = c.act_dtype;
     {
         int k = 0;
@@ -483,6 +490,7 @@ int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weigh
 
     // [q|k|v] = a W_1[0:3d]^T  and  f = SiLU(a W_1[3d:3d+F]^T) * (a W_1[3d+F:]^T), written next to O
     GemmBatch g1{};
+    g1.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     g1.a_dtype = c.act_dtype;
     g1.p[0] = {act, d, w->w_1, d, qkv, 3L * d, c.act_dtype, nullptr, 0, 0, nullptr, 0, n, 3 * d, d, EPI_STORE};
     g1.p[1] = {act, d, reinterpret_cast<const char*>(w->w_1) + (size_t)3 * d * d * esize(c.dtype), d,
@@ -503,6 +511,7 @@ int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weigh
     DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
 
     GemmBatch g2{};
+    g2.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     g2.a_dtype = c.act_dtype;
     g2.p[0] = {of, ldof, w->w_2, ldof, y, d, c.y_dtype, x, d, c.x_dtype, mod + 2 * (size_t)d, 0, n, d, d + F,
                EPI_GATED_RES};

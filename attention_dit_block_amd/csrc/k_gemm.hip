@@ -21,6 +21,8 @@
 // 8 M-tiles.
 //
 // fp32 path: a plain LDS-tiled FMA kernel (no reduced-precision matrix math).
+#include <atomic>
+#include <chrono>
 #include <type_traits>
 
 #include "dev_common.h"
@@ -95,27 +97,72 @@ __device__ __forceinline__ void store4_dt(void* base, size_t off, int dt, const 
 // WN = waves along N.  WN = 2: 4 waves (one per SIMD), each a 128 x 128 sub-tile (4 x 4 MFMA
 // tiles, 256 accumulators).  WN = 4: 8 waves (two per SIMD), each 128 x 64 (4 x 2 MFMA tiles,
 // 128 accumulators) -- the second wave on a SIMD issues MFMAs while the first waits on LDS.
+constexpr int kGemmLds = 2 * (BM + BN) * BK * 2;      // two A+B stages: 128 KB, one workgroup per CU
+constexpr int kPartialF4 = BM * BN / 4;               // float4s of one fp32 partial tile (256 KB)
+
+// How a workgroup finishes a tile it computed k-steps [kb, ke) of:
+enum TileKind {
+    TILE_FULL = 0,      // all k-steps: epilogue
+    TILE_OWNER = 1,     // k-steps from 0: add the partials of the workgroups holding the rest, epilogue
+    TILE_PARTIAL = 2    // a later run of k-steps: publish the fp32 partial for the owner
+};
+
+// Stream-K scratch: [sk_grid] partial tiles, then [sk_grid] 64-bit flags.  Partials and flags move
+// with relaxed device-scope atomics: on gfx950 these are sc1 loads and stores that go to the
+// coherence point past the XCD-private L2s, so no cache-wide writeback or invalidate (which a
+// release / acquire fence would issue, for the whole XCD's L2) is needed.  Ordering comes from
+// waiting for the partial's stores to be acknowledged before the flag is raised.
+__device__ __forceinline__ float4* sk_partial(const GemmBatch& b, int g) {
+    return reinterpret_cast<float4*>(b.sk_scratch) + (size_t)g * kPartialF4;
+}
+__device__ __forceinline__ unsigned long long* sk_flag(const GemmBatch& b, int g) {
+    return reinterpret_cast<unsigned long long*>(reinterpret_cast<float4*>(b.sk_scratch) +
+                                                 (size_t)b.sk_grid * kPartialF4) + g;
+}
+// First k-step (stream-K relative) of workgroup g's share of S k-steps.
+__device__ __forceinline__ long sk_begin(long S, int g, int G) { return S * g / G; }
+
+__device__ __forceinline__ void sk_store(float4* p, float a, float b, float c, float d) {
+    unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+    const unsigned long long lo = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+    const unsigned long long hi = (unsigned long long)__float_as_uint(c) | ((unsigned long long)__float_as_uint(d) << 32);
+    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 sk_load(const float4* p) {
+    unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<float4*>(p));
+    const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float4(__uint_as_float((unsigned)lo), __uint_as_float((unsigned)(lo >> 32)),
+                       __uint_as_float((unsigned)hi), __uint_as_float((unsigned)(hi >> 32)));
+}
+
 template <int MODE, int AT, int WN>
-__device__ __forceinline__ void gemm_mfma_body(const GemmBatch& b) {
+__device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L, int kb, int ke, int kind, int g,
+                                          long S, long t_end) {
     constexpr int NW = 2 * WN;                     // waves per workgroup
     constexpr int NB = 4 / (WN / 2);               // 32-wide n-blocks per wave (4 or 2)
     constexpr int LPW = 32 / NW;                   // 1 KB load instructions per wave per operand
-    __shared__ __attribute__((aligned(1024))) char smem[2 * (BM + BN) * BK * 2];
     constexpr int kStage = (BM + BN) * BK * 2;     // bytes of one A+B stage
     constexpr int kBOff = BM * BK * 2;             // B tile offset within a stage
     typedef typename Frag<AT>::T FragT;
 
     int pi, tm, tn;
-    tile_of(b, xcd_remap(blockIdx.x, gridDim.x), pi, tm, tn);
+    tile_of(b, L, pi, tm, tn);
     const GemmProblem& P = b.p[pi];
     const int epi = MODE == MODE_MIXED ? P.epi : (MODE == MODE_SWIGLU ? EPI_SWIGLU
                                                   : (MODE == MODE_RES ? EPI_GATED_RES : EPI_STORE));
     const bool swiglu = epi == EPI_SWIGLU;
     const int m0 = tm * BM;
     const int n0 = swiglu ? tn * (BN / 2) : tn * BN;   // first output column
-    const int M = P.M, K = P.K;
+    const int M = P.M;
 
-    const int tid = threadIdx.x;
+    // The thread index goes through an opaque zero: the per-lane address arithmetic below is then
+    // recomputed for every tile of a persistent workgroup instead of being hoisted out of the
+    // tile loop and held in registers across it.
+    int zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+    const int tid = threadIdx.x + zero;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
@@ -197,7 +244,7 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmBatch& b) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-    const int nk = K / BK;
+    const int nk = ke - kb;                        // k-steps of this run
     // Fragments for k16 sub-step s of a staged tile (LDS byte offset `base` of its A tile).
     auto read_frags = [&](FragT* fa, FragT* fb, int base, int s) {
         const int c = 2 * s + khalf;
@@ -211,7 +258,7 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmBatch& b) {
             fb[j] = *reinterpret_cast<const FragT*>(lb + b_row[j] * 128 + ((c ^ swz(b_row[j])) << 4));
     };
 
-    issue_loads(0, 0);
+    issue_loads(0, kb * BK);
     store_b(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -233,7 +280,7 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmBatch& b) {
             const int cur = s & 1;
             if (s + 1 < BK / 16) read_frags(fa[cur ^ 1], fb[cur ^ 1], buf * kStage, s + 1);
             if constexpr (MORE) {
-                if (s == 0) issue_loads(buf ^ 1, (it + 1) * BK);
+                if (s == 0) issue_loads(buf ^ 1, (kb + it + 1) * BK);
                 if constexpr (AT == F16) {
                     if (s == BK / 16 - 1) store_b(buf ^ 1);
                 }
@@ -270,6 +317,62 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmBatch& b) {
     read_frags(fa[0], fb[0], 0, 0);
     for (int it = 0; it < nk - 1; ++it) kstep.template operator()<true>(it);
     kstep.template operator()<false>(nk - 1);
+
+    // Partial tiles: lane l of wave w keeps float4 c of its accumulators at index
+    // (w * NB*16 + c) * 64 + l of its workgroup's slot.
+    constexpr int kF4 = NB * 16;                   // float4s of accumulators per lane
+    if (kind == TILE_PARTIAL) {
+        float4* dst = sk_partial(b, g);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = (nb * 4 + mb) * 4 + q;
+                    sk_store(dst + (wave * kF4 + c) * 64 + lane, acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
+                             acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
+                }
+        // every thread's stores acknowledged at the coherence point, then one thread raises the flag
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(sk_flag(b, g), b.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    if (kind == TILE_OWNER) {
+        // The rest of this tile, up to k-step t_end (stream-K relative), was split over the next
+        // workgroups g+1, g+2, ...; each published its piece first thing in its share.
+        const int G = b.sk_grid;
+        for (int j = g + 1; j < G && sk_begin(S, j, G) < t_end; ++j) {
+            if (sk_begin(S, j + 1, G) == sk_begin(S, j, G)) continue;     // empty share
+            if (tid == 0) {
+                // bounded wait (every workgroup of the grid is resident, so the piece is being
+                // computed); on expiry the tile is finished without it
+                for (int spin = 0; spin < (1 << 22); ++spin) {
+                    if (__hip_atomic_load(sk_flag(b, j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == b.epoch) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            __syncthreads();
+            const float4* src = sk_partial(b, j);
+            // 4 loads in flight at a time: the accumulators already fill the register file
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int c = (nb * 4 + mb) * 4 + q;
+                        const float4 v = sk_load(src + (wave * kF4 + c) * 64 + lane);
+                        acc[nb][mb][4 * q] += v.x;
+                        acc[nb][mb][4 * q + 1] += v.y;
+                        acc[nb][mb][4 * q + 2] += v.z;
+                        acc[nb][mb][4 * q + 3] += v.w;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        }
+    }
 
     // ---- epilogue.  acc[nb][mb][q]: row m = m0 + wm*128 + mb*32 + (lane & 31),
     //      B-row offset within the n-block: 8*(q>>2) + 4*khalf + (q&3).
@@ -318,6 +421,44 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmBatch& b) {
                 }
             }
         }
+    }
+}
+
+// Persistent stream-K driver (sk_grid > 0) or one tile per workgroup.  Workgroup g (XCD-remapped,
+// so consecutive g share an XCD) runs tiles g, g + G, ... below dp_tiles, then its even share of
+// the remaining tiles' k-steps in order: the end of a tile some earlier workgroup started
+// (published as a partial), whole tiles, and the start of a tile later workgroups finish (it
+// owns that one and adds their partials).  A tile's owner computes its piece last, after the
+// workgroups holding the other pieces computed theirs first.
+template <int MODE, int AT, int WN>
+__device__ __forceinline__ void gemm_mfma_body(const GemmBatch& b) {
+    __shared__ __attribute__((aligned(1024))) char smem[kGemmLds];
+    const int g = xcd_remap(blockIdx.x, gridDim.x);
+    const int G = b.sk_grid, I = b.k_steps;
+    const long S = G ? (long)(b.total_tiles - b.dp_tiles) * I : 0;     // stream-K k-steps
+    const long e = G ? sk_begin(S, g + 1, G) : 0;
+    long it = G ? sk_begin(S, g, G) : 0;
+    // one work item per pass, so the tile code is generated once
+    for (int w = 0;; ++w) {
+        int L, kb = 0, ke = I, kind = TILE_FULL;
+        long t_end = 0;
+        if (G == 0) {
+            if (w > 0) break;
+            L = g;
+        } else if ((long)g + (long)w * G < b.dp_tiles) {
+            L = g + w * G;
+        } else {
+            if (it >= e) break;
+            const int t = (int)(it / I);
+            kb = (int)(it - (long)t * I);
+            ke = (int)min((long)I, e - (long)t * I);
+            kind = kb > 0 ? TILE_PARTIAL : (ke == I ? TILE_FULL : TILE_OWNER);
+            L = b.dp_tiles + t;
+            t_end = (long)(t + 1) * I;
+            it = (long)t * I + ke;
+        }
+        if (w > 0) __syncthreads();                 // LDS stages are reused by the next tile
+        gemm_tile<MODE, AT, WN>(b, smem, L, kb, ke, kind, g, S, t_end);
     }
 }
 
@@ -413,7 +554,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmBatch b) {
 #endif
 template <int AT, bool W8>
 static void launch_mfma_w(GemmBatch& b, hipStream_t s, bool all_store, bool all_res, bool all_swiglu) {
-    const dim3 grid(b.total_tiles), block(W8 ? 512 : 256);
+    const dim3 grid(b.sk_grid ? b.sk_grid : b.total_tiles), block(W8 ? 512 : 256);
 #define DIT_LAUNCH(MODE)                                                                          \
     do {                                                                                          \
         if constexpr (W8) hipLaunchKernelGGL((gemm_mfma_w8<MODE, AT>), grid, block, 0, s, b);     \
@@ -429,6 +570,34 @@ template <int AT>
 static void launch_mfma(GemmBatch& b, hipStream_t s, bool all_store, bool all_res, bool all_swiglu) {
     launch_mfma_w<AT, DIT_GEMM_WN == 4>(b, s, all_store, all_res, all_swiglu);
 }
+
+#ifndef DIT_GEMM_STREAMK
+#define DIT_GEMM_STREAMK 1
+#endif
+
+// Compute units of the current device (the stream-K grid: one 128 KB-LDS workgroup per CU, all
+// resident at once); 0 if unknown.
+static int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) n = 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+size_t gemm_sk_scratch_bytes() {
+    const int G = device_cu_count();
+    return G > 0 ? (size_t)G * ((size_t)kPartialF4 * 16 + 8) : 0;
+}
+
+// Launch tags for the stream-K flags: unique per launch in this process and started from a
+// time-derived value, so flags left in a reused workspace never match a new launch.
+static std::atomic<unsigned long long> g_epoch{
+    ((unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() << 20) | 1ull};
 
 hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
     int total = 0;
@@ -453,6 +622,29 @@ hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
     }
     b.total_tiles = total;
     if (total == 0) return hipSuccess;
+    // Stream-K when at least two full rounds of tiles exist and the last round would leave at
+    // least three quarters of the CUs idle (and every problem has the same K).  Split k-ranges
+    // cost L2 reuse (co-resident workgroups then read different k-slices of shared A and B
+    // panels), so on the block's shapes a partly full last round is cheaper run as it is: at 512
+    // text + 4096 image tokens this picks FFN-in (1296 tiles on 256 CUs), not QKV (648) or the
+    // d-output GEMMs (216).
+    b.sk_grid = 0;
+    b.dp_tiles = 0;
+    b.k_steps = 0;
+    bool same_k = true;
+    for (int i = 0; i < b.n; ++i) {
+        if (b.p[i].M == 0) continue;
+        if (b.k_steps == 0) b.k_steps = b.p[i].K / BK;
+        else same_k &= b.p[i].K / BK == b.k_steps;
+    }
+    const int G = device_cu_count();
+    if (DIT_GEMM_STREAMK && mfma && b.sk_scratch && same_k && G > 0 && total >= 2 * G && total % G != 0 &&
+        4 * (total % G) <= G) {
+        const int D = total / G;
+        b.sk_grid = G;
+        b.dp_tiles = D >= 1 ? (D - 1) * G : 0;
+        b.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed);
+    }
     if (b.a_dtype == F16) launch_mfma<F16>(b, s, all_store, all_res, all_swiglu);
     else if (b.a_dtype == BF16) launch_mfma<BF16>(b, s, all_store, all_res, all_swiglu);
     else hipLaunchKernelGGL(gemm_f32_kernel, dim3(total), dim3(256), 0, s, b);

@@ -85,8 +85,16 @@ struct GemmBatch {
                         // converted to fp16 while they are staged)
     int group_m;        // tile raster: groups of group_m M-tiles, N-major inside a group (0: 8)
     int total_tiles;    // filled by the launcher
+    // Stream-K scratch (16-B-aligned device memory of gemm_sk_scratch_bytes(), or null: one
+    // workgroup per tile).  The launcher fills the rest: a persistent grid of sk_grid
+    // workgroups runs tiles [0, dp_tiles) whole and splits the k-steps of the others evenly.
+    void* sk_scratch;
+    int sk_grid, dp_tiles, k_steps;
+    unsigned long long epoch;
 };
 hipError_t launch_gemm(GemmBatch& b, hipStream_t s);
+// Bytes of stream-K scratch launch_gemm uses on the current device (0 if it cannot tell).
+size_t gemm_sk_scratch_bytes();
 
 // ---- joint attention ---------------------------------------------------------------
 struct AttnArgs {
