@@ -102,6 +102,10 @@ def test_double_block_c2(dit):
     say(f"double block {cfg.name}")
     inp = di.double_block_inputs(cfg, seed=0)
     yt, yi = run_double(dit, cfg, inp)
+    # bit-identical on a second run (the split-K reduction of the FFN-in GEMM has a fixed order)
+    yt2, yi2 = run_double(dit, cfg, inp)
+    np.testing.assert_array_equal(yt, yt2)
+    np.testing.assert_array_equal(yi, yi2)
     ref = o.double_block(cfg, inp)
     report(cfg, "y_txt", yt, ref["y_txt"])
     report(cfg, "y_img", yi, ref["y_img"])
@@ -219,3 +223,57 @@ def test_single_block_c3_shape_sampled(dit):
     rows = _sample_rows(cfg.n_tok, 384, 3)
     ref = o.single_block(cfg, inp, rows=rows)
     report(cfg, "y[sampled]", y[rows], ref["y"])
+
+
+# ---- the full c3 step -------------------------------------------------------------------------
+
+@pytest.mark.slow
+def test_c3_step_chain_teacher_forced(dit):
+    """The 25-block step as the workload runs it: 5 double-stream blocks (the first reads the bf16
+    input, the others the fp32 residual stream in place), then 20 single-stream blocks over
+    [text; image] in place.  Blocks 0, 4, 5 and 24 are checked against the oracle fed the same
+    input state the GPU block received (teacher forcing on the GPU's own trajectory), on sampled
+    rows; the bar is the per-block 2e-2."""
+    cfg = di.CONFIGS[3]
+    nd, ns = cfg.n_double, cfg.n_single
+    checked = {0, nd - 1, nd, nd + ns - 1}
+    say(f"c3 step: {nd} double + {ns} single blocks, checking blocks {sorted(checked)}")
+    act = di.activation_inputs(cfg, seed=0)
+    t = cfg.dtype
+    cond, pos = dev(act["cond"], t), dev(act["pos"], "i32")
+    sh16 = shape_of(cfg, dit)
+    sh32 = shape_of(cfg, dit, x_dtype=dit.DIT_F32)
+    ws = torch.empty(max(dit.block_workspace_size(sh16), dit.block_workspace_size(sh32, single_stream=True)),
+                     dtype=torch.uint8, device="cuda")
+    state = torch.empty(cfg.n_tok, cfg.d, dtype=torch.float32, device="cuda")
+    st_t, st_i = state[:cfg.n_txt], state[cfg.n_txt:]
+    rt, ri = _sample_rows(cfg.n_txt, 128, 11), _sample_rows(cfg.n_img, 192, 12)
+    rows = np.concatenate([rt, cfg.n_txt + ri])
+    for blk in range(nd + ns):
+        x_in = None if blk == 0 else host(state)
+        if blk < nd:
+            bi = di.double_block_inputs(cfg, seed=0, block=blk)
+            wt, wi = upload_stream_weights(bi["txt"], t), upload_stream_weights(bi["img"], t)
+            if blk == 0:
+                dit.block_forward(sh16, wt, wi, cond, pos, dev(act["x_txt"], t), dev(act["x_img"], t), st_t, st_i, ws)
+            else:
+                dit.block_forward(sh32, wt, wi, cond, pos, st_t, st_i, st_t, st_i, ws)
+        else:
+            w = di.single_weights(cfg, 0, blk)
+            dit.single_block_forward(sh32, upload_stream_weights(w, t), cond, pos, state, state, ws)
+        torch.cuda.synchronize()
+        if blk not in checked:
+            continue
+        y = host(state)
+        if blk < nd:
+            inp = dict(bi)
+            if blk > 0:
+                inp.update(x_txt=x_in[:cfg.n_txt].astype(np.float32), x_img=x_in[cfg.n_txt:].astype(np.float32),
+                           x_dtype="f32")
+            ref = o.double_block(cfg, inp, rows_txt=rt, rows_img=ri)
+            report(cfg, f"block {blk} y_txt[sampled]", y[:cfg.n_txt][rt], ref["y_txt"])
+            report(cfg, f"block {blk} y_img[sampled]", y[cfg.n_txt:][ri], ref["y_img"])
+        else:
+            inp = {"cond": act["cond"], "pos": act["pos"], "w": w, "x": x_in.astype(np.float32), "x_dtype": "f32"}
+            ref = o.single_block(cfg, inp, rows=rows)
+            report(cfg, f"block {blk} y[sampled]", y[rows], ref["y"])
