@@ -68,6 +68,10 @@ _block = _sig("dit_block_forward", _i, [ctypes.POINTER(BlockConfig), ctypes.POIN
                                         ctypes.POINTER(StreamWeights), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
 _single = _sig("dit_single_block_forward", _i, [ctypes.POINTER(BlockConfig), ctypes.POINTER(SingleWeights),
                                                 _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+_step_wsize = _sig("dit_step_workspace_size", _sz, [ctypes.POINTER(BlockConfig), _i, _i])
+_step = _sig("dit_step_forward", _i, [ctypes.POINTER(BlockConfig), _i, ctypes.POINTER(StreamWeights),
+                                      ctypes.POINTER(StreamWeights), _i, ctypes.POINTER(SingleWeights), _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _sz, _vp])
 _last_error = _sig("dit_last_error", ctypes.c_char_p, [])
 _launch_count = _sig("dit_launch_count", ctypes.c_uint64, [])
 _abi = _sig("dit_abi_version", _i, [])
@@ -76,7 +80,8 @@ _tend = _sig("dit_timing_end", _i, [])
 _tread = _sig("dit_timing_read", _i, [_i, ctypes.c_char_p, _i, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_double)])
 
 EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", "dit_block_workspace_size",
-            "dit_block_forward", "dit_single_block_forward", "dit_last_error", "dit_launch_count",
+            "dit_block_forward", "dit_single_block_forward", "dit_step_workspace_size", "dit_step_forward",
+            "dit_last_error", "dit_launch_count",
             "dit_abi_version", "dit_timing_begin", "dit_timing_end", "dit_timing_read"]
 
 
@@ -309,6 +314,44 @@ def single_block_forward(shape: Shape, w: dict, cond, pos, x, y, workspace, stre
                  _ptr(x, "x"), _ptr(y, "y"), _ptr(workspace, "workspace"),
                  workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "dit_single_block_forward")
+
+
+def _single_weights(shape: "Shape", w: dict, what: str) -> SingleWeights:
+    d, F, dc, hd = shape.d, shape.ffn_inner, shape.d_cond or shape.d, shape.head_dim
+    sw = SingleWeights()
+    for name, size in (("w_mod", 3 * d * dc), ("w_1", (3 * d + 2 * F) * d), ("qk_norm_w", 2 * hd),
+                       ("w_2", d * (d + F))):
+        _need(w[name], size, f"{what}.{name}")
+        setattr(sw, name, _ptr(w[name], f"{what}.{name}"))
+    return sw
+
+
+def step_workspace_size(shape: Shape, n_double: int, n_single: int) -> int:
+    c = shape.c_config()
+    n = int(_step_wsize(ctypes.byref(c), n_double, n_single))
+    if n == 0:
+        raise DitError(DIT_ERR_INVALID_ARG, "dit_step_workspace_size")
+    return n
+
+
+def step_forward(shape: Shape, txt: list, img: list, single: list, cond, pos, x_txt, x_img, y, workspace,
+                 stream=None) -> None:
+    """The block stack of a denoising step: len(txt) double-stream blocks, then len(single)
+    single-stream blocks; y (fp32 [n_txt + n_img, d]) ends as the stack's output (see include/dit.h)."""
+    import torch
+    if len(txt) != len(img):
+        raise ValueError("txt and img need one weight dict per double-stream block each")
+    c = shape.c_config()
+    nd, ns = len(txt), len(single)
+    wt = (StreamWeights * max(nd, 1))(*[_stream_weights(shape, w, f"txt[{i}]") for i, w in enumerate(txt)])
+    wi = (StreamWeights * max(nd, 1))(*[_stream_weights(shape, w, f"img[{i}]") for i, w in enumerate(img)])
+    sw = (SingleWeights * max(ns, 1))(*[_single_weights(shape, w, f"single[{i}]") for i, w in enumerate(single)])
+    n = shape.n_txt + shape.n_img
+    _check_block_io(shape, cond, pos, ((x_txt, shape.n_txt, "x_txt"), (x_img, shape.n_img, "x_img"), (y, n, "y")))
+    rc = _step(ctypes.byref(c), nd, wt, wi, ns, sw, _ptr(cond, "cond"), _ptr(pos, "pos", torch.int32),
+               _ptr(x_txt, "x_txt"), _ptr(x_img, "x_img"), _ptr(y, "y", torch.float32), _ptr(workspace, "workspace"),
+               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "dit_step_forward")
 
 
 # --- kernel timing -----------------------------------------------------------------------------

@@ -5,6 +5,7 @@
 // fak GPU backend page ("GPU -- the in-kernel forward pass, on the GPU", section 2).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -575,3 +576,88 @@ int dit_timing_read(int i, char* name_buf, int name_len, int* launches, double* 
 }
 
 }  // extern "C"
+
+// =========================================================================================
+// The block stack of one denoising step.
+// =========================================================================================
+static size_t step_ws(const dit_block_config* cfg, int n_double, int n_single) {
+    size_t need = 0;
+    if (n_double > 0) need = plan_workspace(cfg, 0).total;
+    if (n_single > 0) need = std::max(need, plan_workspace(cfg, 1).total);
+    return need;
+}
+
+size_t dit_step_workspace_size(const dit_block_config* cfg, int n_double, int n_single) {
+    clear_err();
+    if (validate_config(cfg) != DIT_OK || n_double < 0 || n_single < 0) return 0;
+    return step_ws(cfg, n_double, n_single);
+}
+
+int dit_step_forward(const dit_block_config* cfg, int n_double, const dit_stream_weights* txt,
+                     const dit_stream_weights* img, int n_single, const dit_single_weights* single,
+                     const void* cond, const int32_t* pos, const void* x_txt, const void* x_img, float* y,
+                     void* workspace, size_t ws_bytes, void* stream) {
+    clear_err();
+    DIT_TRY(validate_config(cfg));
+    const dit_block_config& c = *cfg;
+    if (n_double < 0 || n_single < 0 || n_double + n_single == 0)
+        return fail(DIT_ERR_INVALID_ARG, "n_double = %d, n_single = %d: need >= 0 and at least one block", n_double,
+                    n_single);
+    if (n_double > 0 && (!txt || !img)) return fail(DIT_ERR_INVALID_ARG, "txt / img weight arrays are NULL");
+    if (n_single > 0 && !single) return fail(DIT_ERR_INVALID_ARG, "single weight array is NULL");
+    // everything is checked before the first launch
+    char what[48];
+    for (int b = 0; b < n_double; ++b) {
+        snprintf(what, sizeof what, "txt[%d]", b);
+        DIT_TRY(check_stream_weights(&txt[b], what));
+        snprintf(what, sizeof what, "img[%d]", b);
+        DIT_TRY(check_stream_weights(&img[b], what));
+    }
+    for (int b = 0; b < n_single; ++b) {
+        const dit_single_weights& w = single[b];
+        const void* p[4] = {w.w_mod, w.w_1, w.qk_norm_w, w.w_2};
+        const char* nm[4] = {"w_mod", "w_1", "qk_norm_w", "w_2"};
+        for (int i = 0; i < 4; ++i) {
+            snprintf(what, sizeof what, "single[%d].%s", b, nm[i]);
+            DIT_TRY(check_ptr(p[i], what));
+        }
+    }
+    DIT_TRY(check_ptr(cond, "cond"));
+    DIT_TRY(check_ptr(pos, "pos"));
+    DIT_TRY(check_ptr(y, "y"));
+    if (c.n_txt > 0) DIT_TRY(check_ptr(x_txt, "x_txt"));
+    if (c.n_img > 0) DIT_TRY(check_ptr(x_img, "x_img"));
+    DIT_TRY(check_ptr(workspace, "workspace"));
+    const size_t need = step_ws(cfg, n_double, n_single);
+    if (ws_bytes < need) return fail(DIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+    const size_t nt = c.n_txt, ni = c.n_img, d = c.d, es = esize(c.x_dtype);
+    if (n_double == 0 && nt > 0 && ni > 0 &&
+        reinterpret_cast<const char*>(x_img) != reinterpret_cast<const char*>(x_txt) + nt * d * es)
+        return fail(DIT_ERR_INVALID_ARG, "with no double-stream block, x_img must directly follow x_txt");
+    const Range ry = range_of(y, (int)(nt + ni), (int)d, (long)d, DIT_F32);
+    const Range rws{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+    const Range rxt = range_of(x_txt, (int)nt, (int)d, (long)d, c.x_dtype);
+    const Range rxi = range_of(x_img, (int)ni, (int)d, (long)d, c.x_dtype);
+    if (overlap(rws, ry) || overlap(rws, rxt) || overlap(rws, rxi))
+        return fail(DIT_ERR_INVALID_ARG, "workspace overlaps an input or y");
+    if (overlap(ry, rxt) || overlap(ry, rxi)) return fail(DIT_ERR_INVALID_ARG, "y overlaps x_txt / x_img");
+
+    // the first block reads x (cfg->x_dtype) and writes the fp32 stream y; the others update y in place
+    dit_block_config c_first = c, c_rest = c;
+    c_first.y_dtype = DIT_F32;
+    c_rest.y_dtype = DIT_F32;
+    c_rest.x_dtype = DIT_F32;
+    float* y_txt = y;
+    float* y_img = y + nt * d;
+    for (int b = 0; b < n_double; ++b) {
+        const dit_block_config* cb = b == 0 ? &c_first : &c_rest;
+        DIT_TRY(dit_block_forward(cb, &txt[b], &img[b], cond, pos, b == 0 ? x_txt : y_txt, b == 0 ? x_img : y_img,
+                                  y_txt, y_img, workspace, ws_bytes, stream));
+    }
+    for (int b = 0; b < n_single; ++b) {
+        const bool first = n_double == 0 && b == 0;
+        DIT_TRY(dit_single_block_forward(first ? &c_first : &c_rest, &single[b], cond, pos, first ? x_txt : y, y,
+                                         workspace, ws_bytes, stream));
+    }
+    return DIT_OK;
+}

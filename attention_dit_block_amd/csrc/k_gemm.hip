@@ -354,6 +354,9 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
                 }
             }
             __syncthreads();
+            // consumed: clear the flag, so a replay of this launch (same epoch, e.g. from a
+            // captured graph) waits for the new piece instead of taking the old one
+            if (tid == 0) __hip_atomic_store(sk_flag(b, j), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const float4* src = sk_partial(b, j);
             // 4 loads in flight at a time: the accumulators already fill the register file
 #pragma unroll
@@ -594,10 +597,16 @@ size_t gemm_sk_scratch_bytes() {
     return G > 0 ? (size_t)G * ((size_t)kPartialF4 * 16 + 8) : 0;
 }
 
-// Launch tags for the stream-K flags: unique per launch in this process and started from a
-// time-derived value, so flags left in a reused workspace never match a new launch.
+// Launch tags for the stream-K flags: nonzero, unique per launch in this process and started from a
+// time-derived value, so flags left in a reused workspace never match a new launch.  An owner
+// clears each flag it consumed, so replays of one launch (one tag) work too.
 static std::atomic<unsigned long long> g_epoch{
     ((unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() << 20) | 1ull};
+static unsigned long long next_epoch() {
+    unsigned long long e;
+    do e = g_epoch.fetch_add(1, std::memory_order_relaxed); while (e == 0);
+    return e;
+}
 
 hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
     int total = 0;
@@ -643,7 +652,7 @@ hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
         const int D = total / G;
         b.sk_grid = G;
         b.dp_tiles = D >= 1 ? (D - 1) * G : 0;
-        b.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed);
+        b.epoch = next_epoch();
     }
     if (b.a_dtype == F16) launch_mfma<F16>(b, s, all_store, all_res, all_swiglu);
     else if (b.a_dtype == BF16) launch_mfma<BF16>(b, s, all_store, all_res, all_swiglu);

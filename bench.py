@@ -40,6 +40,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c2", choices=["c0", "c1", "c2", "c3", "c4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="skip timing the step replayed from a captured graph")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--act", default="f16", choices=["f16", "bf16"],
                    help="storage of the activations between the block's steps (bf16 workloads)")
@@ -139,25 +140,20 @@ def main():
         wi = {k: up(v, t) for k, v in inp["img"].items()}
         step_blocks.append(lambda: dit.block_forward(shape, wt, wi, cond, pos, x_txt, x_img, y_txt, y_img, ws))
     else:
-        # the full step: n_double double-stream blocks, then n_single single-stream blocks over [txt; img]
-        shape32 = dit.Shape(**{**shape.__dict__, "x_dtype": dit.DIT_F32})
-        state = torch.empty(cfg.n_tok, cfg.d, dtype=torch.float32, device=dev)
-        st_t, st_i = state[:cfg.n_txt], state[cfg.n_txt:]
+        # the full step through dit_step_forward: n_double double-stream blocks, then n_single
+        # single-stream blocks over [txt; img], one fp32 residual stream
+        wts, wis, sws = [], [], []
         for b in range(cfg.n_double):
             print(f"setup: double block {b + 1}/{cfg.n_double}", file=sys.stderr, flush=True)
             bi = di.double_block_inputs(cfg, seed=args.seed, block=b)
-            wt = {k: up(v, t) for k, v in bi["txt"].items()}
-            wi = {k: up(v, t) for k, v in bi["img"].items()}
-            if b == 0:
-                step_blocks.append(lambda wt=wt, wi=wi: dit.block_forward(shape, wt, wi, cond, pos, x_txt, x_img,
-                                                                          st_t, st_i, ws))
-            else:
-                step_blocks.append(lambda wt=wt, wi=wi: dit.block_forward(shape32, wt, wi, cond, pos, st_t, st_i,
-                                                                          st_t, st_i, ws))
+            wts.append({k: up(v, t) for k, v in bi["txt"].items()})
+            wis.append({k: up(v, t) for k, v in bi["img"].items()})
         for b in range(cfg.n_single):
             print(f"setup: single block {b + 1}/{cfg.n_single}", file=sys.stderr, flush=True)
-            w = {k: up(v, t) for k, v in di.single_weights(cfg, args.seed, cfg.n_double + b).items()}
-            step_blocks.append(lambda w=w: dit.single_block_forward(shape32, w, cond, pos, state, state, ws))
+            sws.append({k: up(v, t) for k, v in di.single_weights(cfg, args.seed, cfg.n_double + b).items()})
+        ws = torch.empty(dit.step_workspace_size(shape, cfg.n_double, cfg.n_single), dtype=torch.uint8, device=dev)
+        state = torch.empty(cfg.n_tok, cfg.d, dtype=torch.float32, device=dev)
+        step_blocks.append(lambda: dit.step_forward(shape, wts, wis, sws, cond, pos, x_txt, x_img, state, ws))
     setup_s = time.time() - t0
 
     def step():
@@ -180,6 +176,29 @@ def main():
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     flops = cfg.flops_step()
     tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    # the same step replayed from a captured graph (one launch per step from the host)
+    ms_graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        ms_graph = g0.elapsed_time(g1) / args.steps
+        del graph
 
     # per-kernel durations: HIP events around every launch of the library, same stream
     dit.timing_begin(args.steps * 16 * len(step_blocks))
@@ -223,6 +242,7 @@ def main():
                    "gflop_per_step": round(flops / 1e9, 1)},
         "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "ms_per_step_hip_events": round(ev_ms, 4),
+        "ms_per_step_graph_replay": None if ms_graph is None else round(ms_graph, 4),
         "roofline": roof,
         "kernels": kernels,
         "setup_s": round(setup_s, 1),

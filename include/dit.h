@@ -223,6 +223,42 @@ int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weigh
                              const void* x, void* y,
                              void* workspace, size_t ws_bytes, void* stream);
 
+/* Workspace bytes needed by dit_step_forward with n_double / n_single blocks
+ * (the larger of the two block kinds' needs).  (host) cfg.  Returns 0 for an
+ * invalid config or negative counts. */
+size_t dit_step_workspace_size(const dit_block_config* cfg, int n_double, int n_single);
+
+/*
+ * The block stack of one denoising step: n_double double-stream blocks, then
+ * n_single single-stream blocks over [text; image], all with one conditioning
+ * vector (the transformer of the FLUX-style model the "CUDA codepath !" thread
+ * runs, antirez/iris.c issue #15).  Every launch goes to `stream` and nothing
+ * synchronises or allocates, so the whole step can be captured into one graph
+ * and replayed (the reusable-graph approach of the fak GPU page, "GPU -- the
+ * in-kernel forward pass, on the GPU", section 3b).
+ *
+ *  cfg (host): x_dtype is the type of x_txt / x_img; y_dtype is ignored (the
+ *            stream y is fp32).  act_dtype as for the blocks.
+ *  txt, img  (host) arrays of n_double stream weights (block order)
+ *  single    (host) array of n_single single-block weights
+ *  x_txt, x_img  the stack's input, [n_txt, d] and [n_img, d] of x_dtype.  With
+ *            n_double = 0, x_img must directly follow x_txt.
+ *  y         fp32 [n_txt + n_img, d], text rows first: the first block writes it
+ *            from x, every later block updates it in place; it holds the stack's
+ *            output at the end.  Must not overlap x.
+ *  workspace >= dit_step_workspace_size(cfg, n_double, n_single) bytes, as for
+ *            the blocks.
+ * All arguments of all blocks are validated before the first launch; an error
+ * launches nothing.  9 launches per double-stream block, 6 per single-stream
+ * block.
+ */
+int dit_step_forward(const dit_block_config* cfg, int n_double,
+                     const dit_stream_weights* txt, const dit_stream_weights* img,
+                     int n_single, const dit_single_weights* single,
+                     const void* cond, const int32_t* pos,
+                     const void* x_txt, const void* x_img, float* y,
+                     void* workspace, size_t ws_bytes, void* stream);
+
 /* Thread-local text of the last error of this thread (never NULL). */
 const char* dit_last_error(void);
 

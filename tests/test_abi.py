@@ -242,3 +242,43 @@ def test_undersized_tensor_refused_by_binding(dit):
     x = FakeDev(0x12000000, shape=(80, 256))
     with pytest.raises(ValueError):
         dit.block_forward(s, wts, wts, x, x, x, x, x, x, x, stream=FakeStream())
+
+
+def test_step_validation_checks_every_block_first(dit):
+    """dit_step_forward validates all blocks' arguments before its first launch."""
+    import torch
+    s = _cfg(dit, n_txt=16, n_img=64, d=256, n_heads=2, ffn_inner=768)
+    need = dit.step_workspace_size(s, 2, 3)
+    assert need >= dit.block_workspace_size(s) and need >= dit.block_workspace_size(s, single_stream=True)
+    wts = {n: FakeDev(0x1000000 * (i + 1), shape=(1 << 20,)) for i, n in enumerate(
+        ("w_mod", "w_qkv", "qk_norm_w", "w_o", "w_ffn_in", "w_ffn_out"))}
+    sw = {n: FakeDev(0x8000000 * (i + 1), shape=(1 << 20,)) for i, n in enumerate(("w_mod", "w_1", "qk_norm_w", "w_2"))}
+    cond = FakeDev(0x10000000, shape=(256,))
+    pos = FakeDev(0x11000000, shape=(80, 4), dtype=torch.int32, esize=4)
+    xt, xi = FakeDev(0x12000000, shape=(16, 256)), FakeDev(0x13000000, shape=(64, 256))
+    y = FakeDev(0x14000000, shape=(80, 256), dtype=torch.float32, esize=4)
+    ws = FakeDev(0x40000000, shape=(need,), dtype=torch.uint8, esize=1)
+    run = lambda txt, img, single, **kw: dit.step_forward(s, txt, img, single, cond, pos, kw.get("xt", xt),
+                                                          kw.get("xi", xi), y, kw.get("ws", ws), stream=FakeStream())
+    # a misaligned weight in the last single-stream block: nothing of the earlier blocks launches
+    bad = dict(sw)
+    bad["w_1"] = FakeDev(0x8000000 * 2 + 8, shape=(1 << 20,))
+    e = _no_launch(dit, lambda: run([wts, wts], [wts, wts], [sw, sw, bad]))
+    assert "single[2].w_1" in str(e)
+    bad_img = dict(wts)
+    bad_img["w_qkv"] = FakeDev(0x1000000 * 2 + 4, shape=(1 << 20,))
+    e = _no_launch(dit, lambda: run([wts, wts], [wts, bad_img], [sw]))
+    assert "img[1].w_qkv" in str(e)
+    e = _no_launch(dit, lambda: run([], [], []))
+    assert e.status == "DIT_ERR_INVALID_ARG"
+    small = FakeDev(0x40000000, shape=(need - 256,), dtype=torch.uint8, esize=1)
+    e = _no_launch(dit, lambda: run([wts, wts], [wts, wts], [sw, sw, sw], ws=small))
+    assert e.status == "DIT_ERR_WORKSPACE"
+    # single-stream blocks only: the input must be one [n_txt + n_img, d] array
+    e = _no_launch(dit, lambda: run([], [], [sw], xi=FakeDev(0x13000000, shape=(64, 256))))
+    assert "directly follow" in str(e)
+    # y overlapping the input
+    e = _no_launch(dit, lambda: dit.step_forward(s, [wts], [wts], [sw], cond, pos, xt, xi,
+                                                 FakeDev(0x12000000, shape=(80, 256), dtype=torch.float32, esize=4),
+                                                 ws, stream=FakeStream()))
+    assert "overlaps" in str(e)

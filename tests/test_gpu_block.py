@@ -277,3 +277,96 @@ def test_c3_step_chain_teacher_forced(dit):
             inp = {"cond": act["cond"], "pos": act["pos"], "w": w, "x": x_in.astype(np.float32), "x_dtype": "f32"}
             ref = o.single_block(cfg, inp, rows=rows)
             report(cfg, f"block {blk} y[sampled]", y[rows], ref["y"])
+
+
+# ---- the step entry point ----------------------------------------------------------------------
+
+def _step_weights(cfg, nd, ns, seed, qk="random"):
+    t = cfg.dtype
+    dbl = [di.double_block_inputs(cfg, seed=seed, block=b, qk_norm=qk) for b in range(nd)]
+    sgl = [di.single_weights(cfg, seed, nd + b, qk_norm=qk) for b in range(ns)]
+    return dbl, sgl, ([upload_stream_weights(x["txt"], t) for x in dbl], [upload_stream_weights(x["img"], t) for x in dbl],
+                      [upload_stream_weights(w, t) for w in sgl])
+
+
+def test_step_matches_blocks_and_oracle_chain(dit):
+    """dit_step_forward = the blocks run one by one (bit-identical), and the stack's output
+    against the oracle chain (exact arithmetic from the same input) within the block bar."""
+    cfg = di.BlockConfig("step_small", "bf16", d=384, n_heads=3, ffn_inner=1152, n_txt=7, grid_h=5, grid_w=9)
+    nd, ns = 2, 3
+    say(f"step forward {nd} double + {ns} single, {cfg.name}")
+    dbl, sgl, (wt, wi, ws_) = _step_weights(cfg, nd, ns, seed=21)
+    act = dbl[0]
+    t = cfg.dtype
+    cond, pos = dev(act["cond"], t), dev(act["pos"], "i32")
+    xt, xi = dev(act["x_txt"], t), dev(act["x_img"], t)
+    sh = shape_of(cfg, dit)
+    ws = torch.empty(dit.step_workspace_size(sh, nd, ns), dtype=torch.uint8, device="cuda")
+    y = torch.empty(cfg.n_tok, cfg.d, dtype=torch.float32, device="cuda")
+    before = dit.launch_count()
+    dit.step_forward(sh, wt, wi, ws_, cond, pos, xt, xi, y, ws)
+    torch.cuda.synchronize()
+    assert dit.launch_count() == before + 9 * nd + 6 * ns
+    # the same blocks one by one
+    sh32 = shape_of(cfg, dit, x_dtype=dit.DIT_F32)
+    z = torch.empty_like(y)
+    zt, zi = z[:cfg.n_txt], z[cfg.n_txt:]
+    for b in range(nd):
+        if b == 0:
+            dit.block_forward(sh, wt[b], wi[b], cond, pos, xt, xi, zt, zi, ws)
+        else:
+            dit.block_forward(sh32, wt[b], wi[b], cond, pos, zt, zi, zt, zi, ws)
+    for b in range(ns):
+        dit.single_block_forward(sh32, ws_[b], cond, pos, z, z, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(y), host(z))
+    # oracle chain in exact arithmetic
+    st = None
+    for b in range(nd):
+        inp = dict(dbl[b])
+        if st is not None:
+            inp.update(x_txt=st[:cfg.n_txt], x_img=st[cfg.n_txt:], x_dtype="f64")
+        r = o.double_block(cfg, inp)
+        st = np.concatenate([r["y_txt"], r["y_img"]])
+    for b in range(ns):
+        st = o.single_block(cfg, {"cond": act["cond"], "pos": act["pos"], "w": sgl[b], "x": st, "x_dtype": "f64"})["y"]
+    report(cfg, "stack output", host(y), st)
+
+
+def test_step_graph_capture_replays(dit):
+    """The c2-shaped step (1 double + 1 single block; its FFN-in GEMM runs split-K) captured
+    into a graph: every replay, with eager work of the program between replays, is bit-identical
+    to the eager step."""
+    cfg = di.CONFIGS[2]
+    say("step forward under graph capture (c2 shape, 1 double + 1 single)")
+    dbl, sgl, (wt, wi, ws_) = _step_weights(cfg, 1, 1, seed=0, qk="ones")
+    act = dbl[0]
+    t = cfg.dtype
+    cond, pos = dev(act["cond"], t), dev(act["pos"], "i32")
+    xt, xi = dev(act["x_txt"], t), dev(act["x_img"], t)
+    sh = shape_of(cfg, dit)
+    ws = torch.empty(dit.step_workspace_size(sh, 1, 1), dtype=torch.uint8, device="cuda")
+    y = torch.empty(cfg.n_tok, cfg.d, dtype=torch.float32, device="cuda")
+    dit.step_forward(sh, wt, wi, ws_, cond, pos, xt, xi, y, ws)
+    torch.cuda.synchronize()
+    eager = host(y)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up on the capture stream
+        dit.step_forward(sh, wt, wi, ws_, cond, pos, xt, xi, y, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dit.step_forward(sh, wt, wi, ws_, cond, pos, xt, xi, y, ws)
+    other_y = torch.empty_like(y)
+    other_ws = torch.empty_like(ws)
+    for rep in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y), eager)
+        # eager work of the program between replays (another step on other buffers)
+        dit.step_forward(sh, wt, wi, ws_, cond, pos, xt, xi, other_y, other_ws)
+        torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(other_y), eager)
