@@ -124,4 +124,56 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// XCD-aware remap: consecutive workgroup ids go round-robin over the 8 XCDs; give each XCD a
+// contiguous range of work indices instead (workgroups sharing operands then share one L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+    const int x = bid & 7, idx = bid >> 3;
+    const int q = nwg >> 3, r = nwg & 7;
+    return x * q + min(x, r) + idx;
+}
+
+// ---- stream-K plumbing.  A persistent grid of G workgroups splits S work steps evenly; a piece
+// of a work unit that some workgroup does not finish itself is handed over through a partial
+// result and a 64-bit flag.  Partials and flags move with relaxed device-scope atomics: on gfx950
+// these are sc1 loads and stores that go to the coherence point past the XCD-private L2s, so no
+// cache-wide writeback or invalidate (which a release / acquire fence would issue, for the whole
+// XCD's L2) is needed.  Ordering comes from waiting for the partial's stores to be acknowledged
+// before the flag is raised.
+// First step of workgroup g's share.
+__device__ __forceinline__ long sk_begin(long S, int g, int G) { return S * g / G; }
+
+__device__ __forceinline__ void sk_store(float4* p, float a, float b, float c, float d) {
+    unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+    const unsigned long long lo = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+    const unsigned long long hi = (unsigned long long)__float_as_uint(c) | ((unsigned long long)__float_as_uint(d) << 32);
+    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 sk_load(const float4* p) {
+    unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<float4*>(p));
+    const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float4(__uint_as_float((unsigned)lo), __uint_as_float((unsigned)(lo >> 32)),
+                       __uint_as_float((unsigned)hi), __uint_as_float((unsigned)(hi >> 32)));
+}
+// Publish: every thread's partial stores acknowledged, then thread 0 raises the flag.
+__device__ __forceinline__ void sk_raise(unsigned long long* flag, unsigned long long tag) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flag, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Take: thread 0 waits for the flag (bounded: every workgroup of the grid is resident, so the
+// piece is being computed; on expiry the unit is finished without it), then clears it, so a replay
+// of the same launch (same tag, e.g. from a captured graph) waits for the new piece.
+__device__ __forceinline__ void sk_take(unsigned long long* flag, unsigned long long tag) {
+    if (threadIdx.x == 0) {
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+            if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace dit

@@ -136,7 +136,7 @@ int validate_config(const dit_block_config* c) {
 
 // Workspace plan: 256-byte aligned sub-buffers.
 struct WsPlan {
-    size_t mod, act, qkv, o, h, f, of, sk, sk_bytes, total;
+    size_t mod, act, qkv, o, h, f, of, sk, sk_bytes, ask, ask_bytes, total;
 };
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 WsPlan plan_workspace(const dit_block_config* c, int single) {
@@ -160,6 +160,9 @@ WsPlan plan_workspace(const dit_block_config* c, int single) {
     // the GEMMs' stream-K scratch (16-bit paths), shared by the block's GEMMs in stream order
     p.sk_bytes = c->dtype == DIT_BF16 ? gemm_sk_scratch_bytes() : 0;
     p.sk = take(p.sk_bytes);
+    // attention's stream-K scratch (16-bit paths)
+    p.ask_bytes = c->dtype == DIT_BF16 ? attention_sk_scratch_bytes() : 0;
+    p.ask = take(p.ask_bytes);
     p.total = off;
     return p;
 }
@@ -390,6 +393,7 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
     // 5. O = joint attention over all n tokens
     AttnArgs at{qkv, 3L * d, qkv + (size_t)d * es, 3L * d, qkv + (size_t)2 * d * es, 3L * d, ob, d, n, c.n_heads,
                 1.0f / std::sqrt((float)c.head_dim), c.act_dtype};
+    at.sk_scratch = W.ask_bytes ? ws + W.ask : nullptr;
     DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
 
     // 6. h = x + gate1 * (O W_o^T)   (fp32)
@@ -509,6 +513,7 @@ int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weigh
 
     AttnArgs at{qkv, 3L * d, qkv + (size_t)d * es, 3L * d, qkv + (size_t)2 * d * es, 3L * d, of, ldof, n, c.n_heads,
                 1.0f / std::sqrt((float)c.head_dim), c.act_dtype};
+    at.sk_scratch = W.ask_bytes ? ws + W.ask : nullptr;
     DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
 
     GemmBatch g2{};

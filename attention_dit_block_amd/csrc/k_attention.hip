@@ -27,6 +27,11 @@
 //                taken over the fp32 probabilities.
 // Each lane ends with 4 consecutive output features of one query per register group.
 //
+// Work units are (head, 256-query tile) pairs.  With a stream-K scratch buffer (the block path) and
+// a partly filled last round of units, a persistent grid of one workgroup per CU splits the
+// remaining units' key tiles evenly; a unit's pieces are combined exactly like two halves of the
+// online softmax (running max, running sum, unnormalised O), in a fixed order.
+//
 // fp32 kernel: LDS-tiled, 4 threads per query, fp32 FMA throughout.
 #include "dev_common.h"
 #include "launch.h"
@@ -44,6 +49,7 @@ constexpr int AK = 64;       // keys per tile
 constexpr int HD = 128;      // head dim
 constexpr int kTile = AK * HD * 2;          // bytes of one K (or V) tile: 64 rows of 256 B
 constexpr float kLazyMax = 8.0f;            // log2 of the largest unnormalised probability
+
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4_v __attribute__((ext_vector_type(4)));
@@ -84,27 +90,45 @@ __device__ __forceinline__ float half_swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// How a workgroup finishes a (head, query tile) unit it ran key tiles [kb, ke) of:
+enum UnitKind {
+    UNIT_FULL = 0,      // all key tiles: normalise and store O
+    UNIT_OWNER = 1,     // key tiles from 0: merge the partials of the workgroups holding the rest, store
+    UNIT_PARTIAL = 2    // later key tiles: publish (running max, running sum, unnormalised O)
+};
+
+// Stream-K scratch: [sk_grid] partial slots, then [sk_grid] 64-bit flags.  In a slot, lane l of
+// wave w keeps float4 c (c < 16: its O accumulators; c = 16: running max, running sum) at index
+// (w * 17 + c) * 64 + l.
+constexpr int kPartF4 = 17;
+constexpr int kSlotF4 = kAttnWaves * kPartF4 * 64;
+__device__ __forceinline__ float4* attn_partial(const AttnArgs& a, int g) {
+    return reinterpret_cast<float4*>(a.sk_scratch) + (size_t)g * kSlotF4;
+}
+__device__ __forceinline__ unsigned long long* attn_flag(const AttnArgs& a, int g) {
+    return reinterpret_cast<unsigned long long*>(reinterpret_cast<float4*>(a.sk_scratch) +
+                                                 (size_t)a.sk_grid * kSlotF4) + g;
+}
+
+// One (head, query tile) unit L = head * nq + query tile over key tiles [kb, ke).
 // NEG: softmax_scale < 0 (the row max of the scaled scores is then the min of the raw ones).
 template <int DT, bool NEG>
-__device__ __forceinline__ void attention_mfma_body(const AttnArgs& a) {
+__device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem, int L, int kb, int ke, int kind,
+                                               int g, long S, long t_end) {
     constexpr int LPW = 16 / kAttnWaves;    // 1 KB load instructions per wave per K (or V) tile
     typedef typename AFrag<DT>::T FragT;
-    // K ring (2 tiles) then V ring (2 tiles)
-    __shared__ __attribute__((aligned(1024))) char smem[4 * kTile];
+    // smem: K ring (2 tiles) then V ring (2 tiles)
     constexpr int kV = 2 * kTile;
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    // The thread index goes through an opaque zero: the per-lane address arithmetic below is then
+    // redone for each unit instead of being hoisted out of the persistent loop, where it would
+    // hold registers across the whole kernel.
+    int zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+    const int tid = threadIdx.x + zero, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h32 = lane >> 5, l32 = lane & 31;
-    // XCD-aware order: each XCD gets a contiguous range of (head, query tile) pairs, so the
-    // workgroups sharing one head's K and V run on one L2.
     const int nq = (a.n_tok + AQ - 1) / AQ;
-    const int nwg = gridDim.x;
-    int L;
-    {
-        const int x = blockIdx.x & 7, idx = blockIdx.x >> 3, q = nwg >> 3, r = nwg & 7;
-        L = x * q + min(x, r) + idx;
-    }
     const int head = L / nq, qt = L % nq;
     const int N = a.n_tok;
     const float c2 = a.scale * 1.4426950408889634f;     // scores in base 2
@@ -200,16 +224,15 @@ __device__ __forceinline__ void attention_mfma_body(const AttnArgs& a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) o[i][q] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
-    const int nt = (N + AK - 1) / AK;
     f32x16_v sA[2], sB[2];
 
-    // One pipeline step on tile j (P = j & 1): its scores are in SC; issue the loads of K tile
-    // j + 2 and V tile j + 1, compute the scores of tile j + 1 into SN (unless LAST) while the
+    // One pipeline step on tile j (P = (j - kb) & 1): its scores are in SC; issue the loads of K
+    // tile j + 2 and V tile j + 1, compute the scores of tile j + 1 into SN (unless LAST) while the
     // softmax of tile j runs, then O += V_j P_j.
     auto step = [&]<int P, bool LAST>(int j, f32x16_v* SC, f32x16_v* SN) {
         const int j0 = j * AK;
         if constexpr (!LAST) {
-            if (j + 2 < nt) load_k(P, j0 + 2 * AK);
+            if (j + 2 < ke) load_k(P, j0 + 2 * AK);
             load_v(P ^ 1, j0 + AK);
         }
         // ---- region 1: S(j+1) MFMAs with the softmax of tile j
@@ -308,25 +331,66 @@ __device__ __forceinline__ void attention_mfma_body(const AttnArgs& a) {
         __syncthreads();
     };
 
-    // prologue: K tiles 0 and 1, V tile 0; scores of tile 0
-    load_k(0, 0);
-    if (nt > 1) load_k(1, AK);
-    load_v(0, 0);
+    // prologue: K tiles kb and kb + 1, V tile kb; scores of tile kb
+    load_k(0, kb * AK);
+    if (kb + 1 < ke) load_k(1, (kb + 1) * AK);
+    load_v(0, kb * AK);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     scores(sA, 0);
     __syncthreads();        // K slot 0 is refilled by step 0
 
-    int j = 0;
-    for (; j + 2 < nt; j += 2) {
+    int j = kb;
+    for (; j + 2 < ke; j += 2) {
         step.template operator()<0, false>(j, sA, sB);
         step.template operator()<1, false>(j + 1, sB, sA);
     }
-    if (j + 1 < nt) {
+    if (j + 1 < ke) {
         step.template operator()<0, false>(j, sA, sB);
         step.template operator()<1, true>(j + 1, sB, sA);
     } else {
         step.template operator()<0, true>(j, sA, sB);
+    }
+
+    if (kind == UNIT_PARTIAL) {
+        float4* dst = attn_partial(a, g) + wave * kPartF4 * 64 + lane;
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sk_store(dst + (4 * eb + i) * 64, o[eb][4 * i], o[eb][4 * i + 1], o[eb][4 * i + 2], o[eb][4 * i + 3]);
+        sk_store(dst + 16 * 64, m_run, l_run, 0.0f, 0.0f);
+        sk_raise(attn_flag(a, g), a.epoch);
+        return;
+    }
+    if (kind == UNIT_OWNER) {
+        // The rest of this unit's key tiles, up to stream-K step t_end, went to the next
+        // workgroups g+1, g+2, ...; each published its piece first thing in its share.  Merge:
+        // m = max(m_a, m_b), O = O_a 2^(m_a - m) + O_b 2^(m_b - m), the same for the running sum.
+        const int G = a.sk_grid;
+        for (int jg = g + 1; jg < G && sk_begin(S, jg, G) < t_end; ++jg) {
+            if (sk_begin(S, jg + 1, G) == sk_begin(S, jg, G)) continue;     // empty share
+            sk_take(attn_flag(a, jg), a.epoch);
+            const float4* src = attn_partial(a, jg) + wave * kPartF4 * 64 + lane;
+            const float4 ml = sk_load(src + 16 * 64);
+            const float m_new = fmaxf(m_run, ml.x);
+            const float ca = __builtin_amdgcn_exp2f(m_run - m_new), cb = __builtin_amdgcn_exp2f(ml.x - m_new);
+            m_run = m_new;
+            l_run = fmaf(l_run, ca, ml.y * cb);
+            // 4 loads in flight at a time: O and the pipeline state fill most of the registers
+#pragma unroll
+            for (int eb = 0; eb < 4; ++eb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 v = sk_load(src + (4 * eb + i) * 64);
+                    o[eb][4 * i] = fmaf(o[eb][4 * i], ca, v.x * cb);
+                    o[eb][4 * i + 1] = fmaf(o[eb][4 * i + 1], ca, v.y * cb);
+                    o[eb][4 * i + 2] = fmaf(o[eb][4 * i + 2], ca, v.z * cb);
+                    o[eb][4 * i + 3] = fmaf(o[eb][4 * i + 3], ca, v.w * cb);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     }
 
     const float inv = 1.0f / half_swap_sum(l_run);
@@ -344,8 +408,46 @@ __device__ __forceinline__ void attention_mfma_body(const AttnArgs& a) {
     }
 }
 
-// Fixed launch bounds per layout (they must not depend on a template parameter: hipcc then emits no
-// host launch stub).
+// Persistent stream-K driver (sk_grid > 0) or one unit per workgroup.  Workgroup g (XCD-remapped,
+// so consecutive g, which share heads, share an L2) runs units g, g + G, ... below dp_units, then
+// its even share of the remaining units' key tiles in order: the end of a unit some earlier
+// workgroup started (published as a partial), whole units, and the start of a unit later
+// workgroups finish (it owns that one and merges their partials).  A unit's owner computes its
+// piece last, after the workgroups holding the other pieces computed theirs first.
+template <int DT, bool NEG>
+__device__ __forceinline__ void attention_mfma_body(const AttnArgs& a) {
+    __shared__ __attribute__((aligned(1024))) char smem[4 * kTile];
+    const int g = xcd_remap(blockIdx.x, gridDim.x);
+    const int G = a.sk_grid, I = a.k_tiles;
+    const long S = G ? (long)(a.units - a.dp_units) * I : 0;          // stream-K key tiles
+    const long e = G ? sk_begin(S, g + 1, G) : 0;
+    long it = G ? sk_begin(S, g, G) : 0;
+    // one work item per pass, so the unit code is generated once
+    for (int w = 0;; ++w) {
+        int L, kb = 0, ke = I, kind = UNIT_FULL;
+        long t_end = 0;
+        if (G == 0) {
+            if (w > 0) break;
+            L = g;
+        } else if ((long)g + (long)w * G < a.dp_units) {
+            L = g + w * G;
+        } else {
+            if (it >= e) break;
+            const int t = (int)(it / I);
+            kb = (int)(it - (long)t * I);
+            ke = (int)min((long)I, e - (long)t * I);
+            kind = kb > 0 ? UNIT_PARTIAL : (ke == I ? UNIT_FULL : UNIT_OWNER);
+            L = a.dp_units + t;
+            t_end = (long)(t + 1) * I;
+            it = (long)t * I + ke;
+        }
+        if (w > 0) __syncthreads();                 // the K / V rings are reused by the next unit
+        attention_unit<DT, NEG>(a, smem, L, kb, ke, kind, g, S, t_end);
+    }
+}
+
+// Fixed launch bounds (they must not depend on a template parameter: hipcc then emits no host
+// launch stub).
 template <int DT, bool NEG>
 __global__ __launch_bounds__(64 * kAttnWaves, 2) void attention_mfma_kernel(AttnArgs a) {
     attention_mfma_body<DT, NEG>(a);
@@ -407,18 +509,50 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(AttnArgs a) {
     }
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+#ifndef DIT_ATTN_STREAMK
+#define DIT_ATTN_STREAMK 1
+#endif
+size_t attention_sk_scratch_bytes() {
+    const int G = device_cu_count();
+    return G > 0 ? (size_t)G * ((size_t)kSlotF4 * 16 + 8) : 0;
+}
+
+hipError_t launch_attention(AttnArgs& a, hipStream_t s) {
     if (a.n_tok == 0) return hipSuccess;
     if (a.dtype == BF16 || a.dtype == F16) {
         const int nq = (a.n_tok + AQ - 1) / AQ;
-        const dim3 grid(nq * a.n_heads), block(64 * kAttnWaves);
+        // Stream-K when the last round of units leaves CUs idle for at least four key tiles on
+        // average and every workgroup's share is at least eight key tiles (each piece handed over
+        // costs a pipeline fill and a partial's round trip): at 512 text + 4096 image tokens the
+        // 432 units of 72 key tiles run on 256 CUs as 121.5 key tiles each instead of 2 x 72.
+        const int G = device_cu_count();
+        a.units = nq * a.n_heads;
+        a.k_tiles = (a.n_tok + AK - 1) / AK;
+        a.sk_grid = 0;
+        a.dp_units = 0;
+        if (DIT_ATTN_STREAMK && a.sk_scratch && G > 0 && a.units % G != 0) {
+            const long rounds = (a.units + G - 1) / G;
+            const long work = (long)a.units * a.k_tiles;
+            const long idle = rounds * G * a.k_tiles - work;
+            if (idle >= 4L * G && work >= 8L * G) {
+                const int D = a.units / G;
+                a.sk_grid = G;
+                a.dp_units = D >= 1 ? (D - 1) * G : 0;
+                a.epoch = next_launch_tag();
+            }
+        }
+        const dim3 grid(a.sk_grid ? a.sk_grid : a.units), block(64 * kAttnWaves);
+        // Stream-K: one workgroup per CU, all resident at once (owners wait for later workgroups).
+        // The register budget already allows only one per CU; unused dynamic LDS past the 64 KB
+        // rings (more than half of the CU's 160 KB taken) makes that hold whatever the budget.
+        const unsigned pad = a.sk_grid ? 32768u : 0u;
         const bool neg = a.scale < 0.0f;
         if (a.dtype == F16) {
-            if (neg) hipLaunchKernelGGL((attention_mfma_kernel<F16, true>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((attention_mfma_kernel<F16, false>), grid, block, 0, s, a);
+            if (neg) hipLaunchKernelGGL((attention_mfma_kernel<F16, true>), grid, block, pad, s, a);
+            else hipLaunchKernelGGL((attention_mfma_kernel<F16, false>), grid, block, pad, s, a);
         } else {
-            if (neg) hipLaunchKernelGGL((attention_mfma_kernel<BF16, true>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((attention_mfma_kernel<BF16, false>), grid, block, 0, s, a);
+            if (neg) hipLaunchKernelGGL((attention_mfma_kernel<BF16, true>), grid, block, pad, s, a);
+            else hipLaunchKernelGGL((attention_mfma_kernel<BF16, false>), grid, block, pad, s, a);
         }
     } else {
         const int nq = (a.n_tok + FQ - 1) / FQ;

@@ -53,14 +53,6 @@ __device__ __forceinline__ void tile_of(const GemmBatch& b, int L, int& pi, int&
     tn = r / gsize;
 }
 
-// XCD-aware remap: consecutive workgroup ids go round-robin over the 8 XCDs; give each XCD a
-// contiguous range of tile indices instead.
-__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
-    const int x = bid & 7, idx = bid >> 3;
-    const int q = nwg >> 3, r = nwg & 7;
-    return x * q + min(x, r) + idx;
-}
-
 __device__ __forceinline__ float silu_acc(float g) { return g / (1.0f + __expf(-g)); }
 
 // LDS row swizzle of the staged tiles (rows of 128 B = 8 chunks of 16 B).  gfx950 serves a
@@ -107,34 +99,13 @@ enum TileKind {
     TILE_PARTIAL = 2    // a later run of k-steps: publish the fp32 partial for the owner
 };
 
-// Stream-K scratch: [sk_grid] partial tiles, then [sk_grid] 64-bit flags.  Partials and flags move
-// with relaxed device-scope atomics: on gfx950 these are sc1 loads and stores that go to the
-// coherence point past the XCD-private L2s, so no cache-wide writeback or invalidate (which a
-// release / acquire fence would issue, for the whole XCD's L2) is needed.  Ordering comes from
-// waiting for the partial's stores to be acknowledged before the flag is raised.
+// Stream-K scratch: [sk_grid] partial tiles, then [sk_grid] 64-bit flags.
 __device__ __forceinline__ float4* sk_partial(const GemmBatch& b, int g) {
     return reinterpret_cast<float4*>(b.sk_scratch) + (size_t)g * kPartialF4;
 }
 __device__ __forceinline__ unsigned long long* sk_flag(const GemmBatch& b, int g) {
     return reinterpret_cast<unsigned long long*>(reinterpret_cast<float4*>(b.sk_scratch) +
                                                  (size_t)b.sk_grid * kPartialF4) + g;
-}
-// First k-step (stream-K relative) of workgroup g's share of S k-steps.
-__device__ __forceinline__ long sk_begin(long S, int g, int G) { return S * g / G; }
-
-__device__ __forceinline__ void sk_store(float4* p, float a, float b, float c, float d) {
-    unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
-    const unsigned long long lo = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
-    const unsigned long long hi = (unsigned long long)__float_as_uint(c) | ((unsigned long long)__float_as_uint(d) << 32);
-    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float4 sk_load(const float4* p) {
-    unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<float4*>(p));
-    const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_float4(__uint_as_float((unsigned)lo), __uint_as_float((unsigned)(lo >> 32)),
-                       __uint_as_float((unsigned)hi), __uint_as_float((unsigned)(hi >> 32)));
 }
 
 template <int MODE, int AT, int WN>
@@ -333,10 +304,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
                     sk_store(dst + (wave * kF4 + c) * 64 + lane, acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
                              acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
                 }
-        // every thread's stores acknowledged at the coherence point, then one thread raises the flag
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(sk_flag(b, g), b.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sk_raise(sk_flag(b, g), b.epoch);
         return;
     }
     if (kind == TILE_OWNER) {
@@ -345,18 +313,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
         const int G = b.sk_grid;
         for (int j = g + 1; j < G && sk_begin(S, j, G) < t_end; ++j) {
             if (sk_begin(S, j + 1, G) == sk_begin(S, j, G)) continue;     // empty share
-            if (tid == 0) {
-                // bounded wait (every workgroup of the grid is resident, so the piece is being
-                // computed); on expiry the tile is finished without it
-                for (int spin = 0; spin < (1 << 22); ++spin) {
-                    if (__hip_atomic_load(sk_flag(b, j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == b.epoch) break;
-                    __builtin_amdgcn_s_sleep(2);
-                }
-            }
-            __syncthreads();
-            // consumed: clear the flag, so a replay of this launch (same epoch, e.g. from a
-            // captured graph) waits for the new piece instead of taking the old one
-            if (tid == 0) __hip_atomic_store(sk_flag(b, j), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sk_take(sk_flag(b, j), b.epoch);
             const float4* src = sk_partial(b, j);
             // 4 loads in flight at a time: the accumulators already fill the register file
 #pragma unroll
@@ -580,7 +537,7 @@ static void launch_mfma(GemmBatch& b, hipStream_t s, bool all_store, bool all_re
 
 // Compute units of the current device (the stream-K grid: one 128 KB-LDS workgroup per CU, all
 // resident at once); 0 if unknown.
-static int device_cu_count() {
+int device_cu_count() {
     static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -602,7 +559,7 @@ size_t gemm_sk_scratch_bytes() {
 // clears each flag it consumed, so replays of one launch (one tag) work too.
 static std::atomic<unsigned long long> g_epoch{
     ((unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() << 20) | 1ull};
-static unsigned long long next_epoch() {
+unsigned long long next_launch_tag() {
     unsigned long long e;
     do e = g_epoch.fetch_add(1, std::memory_order_relaxed); while (e == 0);
     return e;
@@ -652,7 +609,7 @@ hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
         const int D = total / G;
         b.sk_grid = G;
         b.dp_tiles = D >= 1 ? (D - 1) * G : 0;
-        b.epoch = next_epoch();
+        b.epoch = next_launch_tag();
     }
     if (b.a_dtype == F16) launch_mfma<F16>(b, s, all_store, all_res, all_swiglu);
     else if (b.a_dtype == BF16) launch_mfma<BF16>(b, s, all_store, all_res, all_swiglu);

@@ -105,7 +105,18 @@ struct AttnArgs {
     int n_tok, n_heads;
     float scale;
     int dtype;          // F32, BF16 or F16
+    // Stream-K scratch (16-B-aligned device memory of attention_sk_scratch_bytes(), or null:
+    // one workgroup per (head, query tile) unit).  The launcher fills the rest.
+    void* sk_scratch;
+    int sk_grid, dp_units, units, k_tiles;
+    unsigned long long epoch;
 };
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention(AttnArgs& a, hipStream_t s);
+size_t attention_sk_scratch_bytes();
+
+// Compute units of the current device (0 if unknown), and nonzero launch tags unique in the
+// process, for the stream-K grids.
+int device_cu_count();
+unsigned long long next_launch_tag();
 
 }  // namespace dit

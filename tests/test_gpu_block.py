@@ -127,6 +127,23 @@ def test_double_block_c4_sampled_rows(dit):
     report(cfg, "y_img[sampled]", yi[ri], ref["y_img"])
 
 
+def test_double_block_attention_split_many_ways(dit):
+    # 2 heads over 77 + 64x65 tokens: 34 (head, 256-query) units of 67 key tiles, the last one
+    # ragged.  On a 256-CU device the attention splits each unit's key tiles over about eight
+    # workgroups whose partial softmax states the first one merges; the result must not depend on
+    # the split and must repeat bit for bit.
+    cfg = di.BlockConfig("attn_split", "bf16", d=256, n_heads=2, ffn_inner=768, n_txt=77, grid_h=64, grid_w=65)
+    say(f"double block {cfg.name} n={cfg.n_txt + cfg.n_img}")
+    inp = di.double_block_inputs(cfg, seed=5)
+    yt, yi = run_double(dit, cfg, inp)
+    yt2, yi2 = run_double(dit, cfg, inp)
+    np.testing.assert_array_equal(yt, yt2)
+    np.testing.assert_array_equal(yi, yi2)
+    ref = o.double_block(cfg, inp)
+    report(cfg, "y_txt", yt, ref["y_txt"])
+    report(cfg, "y_img", yi, ref["y_img"])
+
+
 def test_double_block_text_only_and_image_only(dit):
     for nt, gh, gw in ((9, 0, 0), (0, 4, 5)):
         cfg = di.BlockConfig("edge", "bf16", d=256, n_heads=2, ffn_inner=768, n_txt=nt, grid_h=gh, grid_w=gw)
