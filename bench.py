@@ -260,15 +260,15 @@ def main():
 # that source is unchanged.
 _C2 = "c2_bf16_d3072_t512_i4096"
 MEASURED_TRAFFIC = {
-    (_C2, "f16", "gemm_ffn_in_swiglu"): {"bytes": 1547205898, "sha256": "2e00b235b1314a6f"},
-    (_C2, "f16", "gemm_qkv"): {"bytes": 586260291, "sha256": "2e00b235b1314a6f"},
-    (_C2, "f16", "gemm_ffn_down"): {"bytes": 656487502, "sha256": "2e00b235b1314a6f"},
-    (_C2, "f16", "gemm_out_proj"): {"bytes": 280870865, "sha256": "2e00b235b1314a6f"},
-    (_C2, "f16", "joint_attention"): {"bytes": 132321308, "sha256": "0cc5e1a149b7d890"},
-    (_C2, "f16", "adaln_gemv"): {"bytes": 226833664, "sha256": "1e8fd8af72198dea"},
-    (_C2, "f16", "qk_rmsnorm_rope"): {"bytes": 113918890, "sha256": "1e8fd8af72198dea"},
-    (_C2, "f16", "modulate_h"): {"bytes": 85415125, "sha256": "1e8fd8af72198dea"},
-    (_C2, "f16", "modulate_x"): {"bytes": 57102008, "sha256": "1e8fd8af72198dea"},
+    (_C2, "f16", "gemm_ffn_in_swiglu"): {"bytes": 1561134722, "sha256": "c90371d260f329ae"},
+    (_C2, "f16", "gemm_qkv"): {"bytes": 583523040, "sha256": "c90371d260f329ae"},
+    (_C2, "f16", "gemm_ffn_down"): {"bytes": 654941489, "sha256": "c90371d260f329ae"},
+    (_C2, "f16", "gemm_out_proj"): {"bytes": 280684159, "sha256": "c90371d260f329ae"},
+    (_C2, "f16", "joint_attention"): {"bytes": 881432664, "sha256": "a975d5971a12db7a"},
+    (_C2, "f16", "adaln_gemv"): {"bytes": 226824570, "sha256": "1e8fd8af72198dea"},
+    (_C2, "f16", "qk_rmsnorm_rope"): {"bytes": 113916289, "sha256": "1e8fd8af72198dea"},
+    (_C2, "f16", "modulate_h"): {"bytes": 85409504, "sha256": "1e8fd8af72198dea"},
+    (_C2, "f16", "modulate_x"): {"bytes": 57100260, "sha256": "1e8fd8af72198dea"},
 }
 
 KERNEL_SOURCE = {"gemm": "k_gemm.hip", "joint_attention": "k_attention.hip"}
