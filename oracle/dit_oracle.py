@@ -27,13 +27,14 @@ a per-stream weight, RoPE frequency theta^(-2j/dim_axis) with theta = 1e4 and
 rotation by +angle on interleaved pairs, softmax scale 1/sqrt(head_dim), no
 mask, text tokens first, SwiGLU with the gate half first.
 
-Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
-(closed forms, invariants, library special cases, brute force) except the
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` or
+``tests/test_oracle_edge.py`` (closed forms, invariants, library special cases, brute force) except the
 composition of the whole block, which is pinned only through its stages and
 block-level special cases (identity modulation, constant scores, zero FFN).
 """
 from __future__ import annotations
 
+import math
 from typing import Dict, Optional, Sequence
 
 import numpy as np
@@ -293,3 +294,57 @@ def single_block(cfg, inputs: Dict[str, object], rows=None, mods=None,
     if keep:
         out.update({"mod": m, "q": q, "k": k, "v": v, "o": o, "f": f, "a": a})
     return out
+
+
+# --- the steps either side of the block stack ------------------------------------------
+# The pages name the denoising step's transformer (FLUX Klein) but print none of these layers;
+# they follow the FLUX model's conventions, without biases like the block (readings listed in the
+# design notes).
+
+def timestep_embedding(t: float, dim: int, max_period: float = 10000.0,
+                       time_factor: float = 1000.0) -> np.ndarray:
+    """Sinusoidal embedding of a scalar: s = time_factor * t, half = dim / 2,
+    f_j = max_period^(-j / half) for j = 0 .. half-1, emb = [cos(s f_j) ..., sin(s f_j) ...]
+    (the cosine half first)."""
+    half = dim // 2
+    j = np.arange(half, dtype=F64)
+    f = np.exp(-math.log(max_period) * j / half)
+    a = F64(time_factor) * F64(t) * f
+    return np.concatenate([np.cos(a), np.sin(a)])
+
+
+def mlp_embedder(v: np.ndarray, w_in: np.ndarray, w_out: np.ndarray) -> np.ndarray:
+    """Two linear layers with a SiLU between: W_out . SiLU(W_in . v)."""
+    return np.asarray(w_out, F64) @ silu(np.asarray(w_in, F64) @ np.asarray(v, F64))
+
+
+def conditioning_vector(t: float, w_t_in, w_t_out, freq_dim: int, g: Optional[float] = None,
+                        w_g_in=None, w_g_out=None, max_period: float = 10000.0,
+                        time_factor: float = 1000.0) -> np.ndarray:
+    """c = MLP_t(emb(t)) (+ MLP_g(emb(g)) when a guidance value and its weights are given)."""
+    c = mlp_embedder(timestep_embedding(t, freq_dim, max_period, time_factor), w_t_in, w_t_out)
+    if g is not None:
+        c = c + mlp_embedder(timestep_embedding(g, freq_dim, max_period, time_factor), w_g_in, w_g_out)
+    return c
+
+
+def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y = x W^T with W [out, in] (patch and text embedding, final projection)."""
+    return np.asarray(x, F64) @ np.asarray(w, F64).T
+
+
+def layer_norm(x: np.ndarray, eps: float) -> np.ndarray:
+    """(x - mean) / sqrt(var + eps) over the last axis (population variance), no affine."""
+    x = np.asarray(x, F64)
+    mu = np.mean(x, axis=-1, keepdims=True)
+    var = np.mean((x - mu) ** 2, axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps)
+
+
+def final_layer(x: np.ndarray, cond: np.ndarray, w_mod: np.ndarray, w_out: np.ndarray,
+                eps: float = 1e-6) -> np.ndarray:
+    """Last layer of the model: [shift, scale] = W_mod . SiLU(c);
+    y = ((1 + scale) * LayerNorm(x) + shift) W_out^T."""
+    d = np.asarray(x).shape[-1]
+    m = adaln_modulation(w_mod, cond).reshape(2, d)
+    return linear((1.0 + m[1]) * layer_norm(x, eps) + m[0], w_out)
