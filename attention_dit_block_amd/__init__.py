@@ -19,6 +19,9 @@ __all__ = [
     "BlockConfig", "StreamWeights", "SingleWeights",
     "adaln_modulate", "qk_rmsnorm_rope", "joint_attention",
     "block_workspace_size", "block_forward", "single_block_forward",
+    "step_workspace_size", "step_forward", "step_shared_mod_workspace_size", "step_forward_shared_mod",
+    "timestep_embedding_workspace_size", "timestep_embedding", "linear",
+    "final_layer_workspace_size", "final_layer",
     "last_error", "launch_count", "abi_version",
     "timing_begin", "timing_end", "timing_read",
 ]
@@ -72,6 +75,15 @@ _step_wsize = _sig("dit_step_workspace_size", _sz, [ctypes.POINTER(BlockConfig),
 _step = _sig("dit_step_forward", _i, [ctypes.POINTER(BlockConfig), _i, ctypes.POINTER(StreamWeights),
                                       ctypes.POINTER(StreamWeights), _i, ctypes.POINTER(SingleWeights), _vp, _vp,
                                       _vp, _vp, _vp, _vp, _sz, _vp])
+_step_sm_wsize = _sig("dit_step_shared_mod_workspace_size", _sz, [ctypes.POINTER(BlockConfig), _i, _i])
+_step_sm = _sig("dit_step_forward_shared_mod", _i, [ctypes.POINTER(BlockConfig), _i, ctypes.POINTER(StreamWeights),
+                                                    ctypes.POINTER(StreamWeights), _i, ctypes.POINTER(SingleWeights),
+                                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+_temb_wsize = _sig("dit_timestep_embedding_workspace_size", _sz, [_i, _i])
+_temb = _sig("dit_timestep_embedding", _i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _f, _vp, _vp, _sz])
+_linear = _sig("dit_linear", _i, [_i, _vp, _vp, _i, _l, _vp, _i, _i, _i, _vp, _i, _l])
+_final_wsize = _sig("dit_final_layer_workspace_size", _sz, [_i, _i, _i])
+_final = _sig("dit_final_layer", _i, [_i, _i, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _i, _f, _vp, _i, _vp, _sz])
 _last_error = _sig("dit_last_error", ctypes.c_char_p, [])
 _launch_count = _sig("dit_launch_count", ctypes.c_uint64, [])
 _abi = _sig("dit_abi_version", _i, [])
@@ -81,6 +93,9 @@ _tread = _sig("dit_timing_read", _i, [_i, ctypes.c_char_p, _i, ctypes.POINTER(_i
 
 EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", "dit_block_workspace_size",
             "dit_block_forward", "dit_single_block_forward", "dit_step_workspace_size", "dit_step_forward",
+            "dit_step_shared_mod_workspace_size", "dit_step_forward_shared_mod",
+            "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_linear",
+            "dit_final_layer_workspace_size", "dit_final_layer",
             "dit_last_error", "dit_launch_count",
             "dit_abi_version", "dit_timing_begin", "dit_timing_end", "dit_timing_read"]
 
@@ -264,14 +279,16 @@ def block_workspace_size(shape: Shape, single_stream: bool = False) -> int:
     return int(n)
 
 
-def _stream_weights(shape: "Shape", w: dict, what: str) -> StreamWeights:
+def _stream_weights(shape: "Shape", w: dict, what: str, need_mod: bool = True) -> StreamWeights:
     d, F, dc, hd = shape.d, shape.ffn_inner, shape.d_cond or shape.d, shape.head_dim
     sizes = {"w_mod": 6 * d * dc, "w_qkv": 3 * d * d, "qk_norm_w": 2 * hd, "w_o": d * d,
              "w_ffn_in": 2 * F * d, "w_ffn_out": d * F}
     s = StreamWeights()
     for name, n in sizes.items():
-        _need(w[name], n, f"{what}.{name}")
-        setattr(s, name, _ptr(w[name], f"{what}.{name}"))
+        if name == "w_mod" and not need_mod and w.get(name) is None:
+            continue
+        _need(w.get(name), n, f"{what}.{name}")
+        setattr(s, name, _ptr(w.get(name), f"{what}.{name}"))
     return s
 
 
@@ -316,13 +333,15 @@ def single_block_forward(shape: Shape, w: dict, cond, pos, x, y, workspace, stre
     _check(rc, "dit_single_block_forward")
 
 
-def _single_weights(shape: "Shape", w: dict, what: str) -> SingleWeights:
+def _single_weights(shape: "Shape", w: dict, what: str, need_mod: bool = True) -> SingleWeights:
     d, F, dc, hd = shape.d, shape.ffn_inner, shape.d_cond or shape.d, shape.head_dim
     sw = SingleWeights()
     for name, size in (("w_mod", 3 * d * dc), ("w_1", (3 * d + 2 * F) * d), ("qk_norm_w", 2 * hd),
                        ("w_2", d * (d + F))):
-        _need(w[name], size, f"{what}.{name}")
-        setattr(sw, name, _ptr(w[name], f"{what}.{name}"))
+        if name == "w_mod" and not need_mod and w.get(name) is None:
+            continue
+        _need(w.get(name), size, f"{what}.{name}")
+        setattr(sw, name, _ptr(w.get(name), f"{what}.{name}"))
     return sw
 
 
@@ -352,6 +371,109 @@ def step_forward(shape: Shape, txt: list, img: list, single: list, cond, pos, x_
                _ptr(x_txt, "x_txt"), _ptr(x_img, "x_img"), _ptr(y, "y", torch.float32), _ptr(workspace, "workspace"),
                workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "dit_step_forward")
+
+
+def step_shared_mod_workspace_size(shape: Shape, n_double: int, n_single: int) -> int:
+    c = shape.c_config()
+    n = int(_step_sm_wsize(ctypes.byref(c), n_double, n_single))
+    if n == 0:
+        raise DitError(DIT_ERR_INVALID_ARG, "dit_step_shared_mod_workspace_size")
+    return n
+
+
+def step_forward_shared_mod(shape: Shape, txt: list, img: list, single: list, w_mod_txt, w_mod_img, w_mod_single,
+                            cond, pos, x_txt, x_img, y, workspace, stream=None) -> None:
+    """step_forward with one AdaLN weight set per block kind shared by all blocks (the blocks'
+    own w_mod entries are not read and may be missing); see include/dit.h."""
+    import torch
+    if len(txt) != len(img):
+        raise ValueError("txt and img need one weight dict per double-stream block each")
+    c = shape.c_config()
+    nd, ns = len(txt), len(single)
+    d, dc = shape.d, shape.d_cond or shape.d
+    wt = (StreamWeights * max(nd, 1))(*[_stream_weights(shape, w, f"txt[{i}]", False) for i, w in enumerate(txt)])
+    wi = (StreamWeights * max(nd, 1))(*[_stream_weights(shape, w, f"img[{i}]", False) for i, w in enumerate(img)])
+    sw = (SingleWeights * max(ns, 1))(*[_single_weights(shape, w, f"single[{i}]", False)
+                                        for i, w in enumerate(single)])
+    if nd:
+        _need(w_mod_txt, 6 * d * dc, "w_mod_txt")
+        _need(w_mod_img, 6 * d * dc, "w_mod_img")
+    if ns:
+        _need(w_mod_single, 3 * d * dc, "w_mod_single")
+    n = shape.n_txt + shape.n_img
+    _check_block_io(shape, cond, pos, ((x_txt, shape.n_txt, "x_txt"), (x_img, shape.n_img, "x_img"), (y, n, "y")))
+    rc = _step_sm(ctypes.byref(c), nd, wt, wi, ns, sw, _ptr(w_mod_txt, "w_mod_txt"), _ptr(w_mod_img, "w_mod_img"),
+                  _ptr(w_mod_single, "w_mod_single"), _ptr(cond, "cond"), _ptr(pos, "pos", torch.int32),
+                  _ptr(x_txt, "x_txt"), _ptr(x_img, "x_img"), _ptr(y, "y", torch.float32),
+                  _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "dit_step_forward_shared_mod")
+
+
+# --- the layers either side of the block stack ----------------------------------------------------
+
+def timestep_embedding_workspace_size(freq_dim: int, d: int) -> int:
+    n = int(_temb_wsize(freq_dim, d))
+    if n == 0:
+        raise DitError(DIT_ERR_INVALID_ARG, "dit_timestep_embedding_workspace_size")
+    return n
+
+
+def timestep_embedding(t, w_t_in, w_t_out, cond_out, workspace, g=None, w_g_in=None, w_g_out=None,
+                       max_period: float = 1e4, time_factor: float = 1000.0, stream=None) -> None:
+    """cond_out = MLP_t(emb(t)) [+ MLP_g(emb(g))]; t and g are fp32 [1] GPU tensors (see include/dit.h)."""
+    import torch
+    d, fd = w_t_in.shape[0], w_t_in.shape[1]
+    _need(w_t_in, d * fd, "w_t_in")
+    _need(w_t_out, d * d, "w_t_out")
+    _need(cond_out, d, "cond_out")
+    _need(t, 1, "t")
+    if g is not None:
+        _need(g, 1, "g")
+        _need(w_g_in, d * fd, "w_g_in")
+        _need(w_g_out, d * d, "w_g_out")
+    rc = _temb(_dt(w_t_in), _stream(stream), _ptr(t, "t", torch.float32), _ptr(g, "g", torch.float32),
+               _ptr(w_t_in, "w_t_in"), _ptr(w_t_out, "w_t_out"), _ptr(w_g_in, "w_g_in"), _ptr(w_g_out, "w_g_out"),
+               fd, d, max_period, time_factor, _ptr(cond_out, "cond_out"), _ptr(workspace, "workspace"),
+               workspace.numel() * workspace.element_size())
+    _check(rc, "dit_timestep_embedding")
+
+
+def linear(x, w, y, stream=None) -> None:
+    """y = x w^T (x [m, k], w [n, k], y [m, n]; 2-D views with unit column stride)."""
+    m, k = x.shape
+    n = w.shape[0]
+    _rows(x, m, k, "x")
+    _rows(y, m, n, "y")
+    _need(w, n * k, "w")
+    rc = _linear(_dt(w), _stream(stream), _ptr(x, "x"), _dt(x), _ld(x, "x"), _ptr(w, "w"), m, n, k, _ptr(y, "y"),
+                 _dt(y), _ld(y, "y"))
+    _check(rc, "dit_linear")
+
+
+def final_layer_workspace_size(n_tok: int, d: int, act_dtype: int) -> int:
+    n = int(_final_wsize(n_tok, d, act_dtype))
+    if n == 0:
+        raise DitError(DIT_ERR_INVALID_ARG, "dit_final_layer_workspace_size")
+    return n
+
+
+def final_layer(x, cond, w_mod, w_out, y, workspace, act_dtype: Optional[int] = None, eps: float = 1e-6,
+                stream=None) -> None:
+    """y = ((1 + scale) LayerNorm(x) + shift) w_out^T, [shift, scale] = w_mod SiLU(cond)."""
+    n_tok, d = x.shape
+    p = w_out.shape[0]
+    dtype = _dt(w_out)
+    if act_dtype is None:
+        act_dtype = DIT_F16 if dtype == DIT_BF16 else DIT_F32
+    _need(x, n_tok * d, "x")
+    _need(y, n_tok * p, "y")
+    _need(cond, cond.numel(), "cond")
+    _need(w_mod, 2 * d * cond.numel(), "w_mod")
+    _need(w_out, p * d, "w_out")
+    rc = _final(dtype, act_dtype, _stream(stream), _ptr(x, "x"), _dt(x), n_tok, d, _ptr(cond, "cond"), cond.numel(),
+                _ptr(w_mod, "w_mod"), _ptr(w_out, "w_out"), p, eps, _ptr(y, "y"), _dt(y),
+                _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size())
+    _check(rc, "dit_final_layer")
 
 
 # --- kernel timing -----------------------------------------------------------------------------

@@ -300,27 +300,31 @@ size_t dit_block_workspace_size(const dit_block_config* cfg, int single_stream) 
     return plan_workspace(cfg, single_stream ? 1 : 0).total;
 }
 
-static int check_stream_weights(const dit_stream_weights* w, const char* s) {
+// need_mod = false: w_mod is not used (the shared-modulation step) and may be NULL
+static int check_stream_weights(const dit_stream_weights* w, const char* s, bool need_mod = true) {
     if (!w) return fail(DIT_ERR_INVALID_ARG, "%s weights are NULL", s);
     const void* p[6] = {w->w_mod, w->w_qkv, w->qk_norm_w, w->w_o, w->w_ffn_in, w->w_ffn_out};
     const char* n[6] = {"w_mod", "w_qkv", "qk_norm_w", "w_o", "w_ffn_in", "w_ffn_out"};
-    for (int i = 0; i < 6; ++i) {
+    for (int i = need_mod ? 0 : 1; i < 6; ++i) {
         if (!p[i]) return fail(DIT_ERR_INVALID_ARG, "%s.%s is NULL", s, n[i]);
         if (!aligned16(p[i])) return fail(DIT_ERR_INVALID_ARG, "%s.%s is not 16-byte aligned", s, n[i]);
     }
     return DIT_OK;
 }
 
-int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt, const dit_stream_weights* img,
-                      const void* cond, const int32_t* pos, const void* x_txt, const void* x_img, void* y_txt,
-                      void* y_img, void* workspace, size_t ws_bytes, void* stream) {
+// mod_pre: the [2][6d] fp32 AdaLN vectors (text, image) computed by the caller, or NULL (the block
+// computes them from its own w_mod; cond is then required).
+static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weights* txt,
+                              const dit_stream_weights* img, const void* cond, const int32_t* pos, const void* x_txt,
+                              const void* x_img, void* y_txt, void* y_img, void* workspace, size_t ws_bytes,
+                              void* stream, const float* mod_pre) {
     clear_err();
     DIT_TRY(validate_config(cfg));
     const dit_block_config& c = *cfg;
     const int nt = c.n_txt, ni = c.n_img, n = nt + ni, d = c.d, F = c.ffn_inner;
-    DIT_TRY(check_stream_weights(txt, "txt"));
-    DIT_TRY(check_stream_weights(img, "img"));
-    DIT_TRY(check_ptr(cond, "cond"));
+    DIT_TRY(check_stream_weights(txt, "txt", !mod_pre));
+    DIT_TRY(check_stream_weights(img, "img", !mod_pre));
+    if (!mod_pre) DIT_TRY(check_ptr(cond, "cond"));
     DIT_TRY(check_ptr(pos, "pos"));
     if (nt > 0) { DIT_TRY(check_ptr(x_txt, "x_txt")); DIT_TRY(check_ptr(y_txt, "y_txt")); }
     if (ni > 0) { DIT_TRY(check_ptr(x_img, "x_img")); DIT_TRY(check_ptr(y_img, "y_img")); }
@@ -341,7 +345,7 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
         return fail(DIT_ERR_INVALID_ARG, "y overlaps x other than as an exact alias of the same dtype");
 
     char* ws = reinterpret_cast<char*>(workspace);
-    float* mod_t = reinterpret_cast<float*>(ws + W.mod);
+    float* mod_t = mod_pre ? const_cast<float*>(mod_pre) : reinterpret_cast<float*>(ws + W.mod);
     float* mod_i = mod_t + 6 * (size_t)d;
     char* act = ws + W.act;
     char* qkv = ws + W.qkv;
@@ -352,14 +356,16 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
     // 1. AdaLN vectors of both streams
-    GemvBatch g{};
-    g.p[0] = {txt->w_mod, mod_t, 6 * d};
-    g.p[1] = {img->w_mod, mod_i, 6 * d};
-    g.n = 2;
-    g.cond = cond;
-    g.d_cond = c.d_cond;
-    g.dtype = c.dtype;
-    DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
+    if (!mod_pre) {
+        GemvBatch g{};
+        g.p[0] = {txt->w_mod, mod_t, 6 * d};
+        g.p[1] = {img->w_mod, mod_i, 6 * d};
+        g.n = 2;
+        g.cond = cond;
+        g.d_cond = c.d_cond;
+        g.dtype = c.dtype;
+        DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
+    }
 
     // 2. a = (1 + scale1) RMSNorm(x) + shift1   (text rows, then image rows)
     ModBatch m{};
@@ -448,19 +454,27 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
     return DIT_OK;
 }
 
-int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weights* w, const void* cond,
+int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt, const dit_stream_weights* img,
+                      const void* cond, const int32_t* pos, const void* x_txt, const void* x_img, void* y_txt,
+                      void* y_img, void* workspace, size_t ws_bytes, void* stream) {
+    return block_forward_impl(cfg, txt, img, cond, pos, x_txt, x_img, y_txt, y_img, workspace, ws_bytes, stream,
+                              nullptr);
+}
+
+// mod_pre: the [3d] fp32 AdaLN vectors computed by the caller, or NULL (from w->w_mod and cond).
+static int single_block_impl(const dit_block_config* cfg, const dit_single_weights* w, const void* cond,
                              const int32_t* pos, const void* x, void* y, void* workspace, size_t ws_bytes,
-                             void* stream) {
+                             void* stream, const float* mod_pre) {
     clear_err();
     DIT_TRY(validate_config(cfg));
     const dit_block_config& c = *cfg;
     const int n = c.n_txt + c.n_img, d = c.d, F = c.ffn_inner;
     if (!w) return fail(DIT_ERR_INVALID_ARG, "weights are NULL");
-    DIT_TRY(check_ptr(w->w_mod, "w_mod"));
+    if (!mod_pre) DIT_TRY(check_ptr(w->w_mod, "w_mod"));
     DIT_TRY(check_ptr(w->w_1, "w_1"));
     DIT_TRY(check_ptr(w->qk_norm_w, "qk_norm_w"));
     DIT_TRY(check_ptr(w->w_2, "w_2"));
-    DIT_TRY(check_ptr(cond, "cond"));
+    if (!mod_pre) DIT_TRY(check_ptr(cond, "cond"));
     DIT_TRY(check_ptr(pos, "pos"));
     DIT_TRY(check_ptr(x, "x"));
     DIT_TRY(check_ptr(y, "y"));
@@ -475,7 +489,7 @@ int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weigh
         return fail(DIT_ERR_INVALID_ARG, "y overlaps x other than as an exact alias of the same dtype");
 
     char* ws = reinterpret_cast<char*>(workspace);
-    float* mod = reinterpret_cast<float*>(ws + W.mod);
+    float* mod = mod_pre ? const_cast<float*>(mod_pre) : reinterpret_cast<float*>(ws + W.mod);
     char* act = ws + W.act;
     char* qkv = ws + W.qkv;
     char* of = ws + W.of;
@@ -483,10 +497,12 @@ int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weigh
     const long ldof = (long)d + F;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-    GemvBatch g{};
-    g.p[0] = {w->w_mod, mod, 3 * d};
-    g.n = 1; g.cond = cond; g.d_cond = c.d_cond; g.dtype = c.dtype;
-    DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
+    if (!mod_pre) {
+        GemvBatch g{};
+        g.p[0] = {w->w_mod, mod, 3 * d};
+        g.n = 1; g.cond = cond; g.d_cond = c.d_cond; g.dtype = c.dtype;
+        DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
+    }
 
     ModBatch m{};
     m.p[0] = {x, d, c.x_dtype, act, d, mod, mod + d, n};
@@ -524,6 +540,12 @@ int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weigh
     g2.n = 1;
     DIT_TRY(launch("gemm_linear2", s, [&] { return launch_gemm(g2, s); }));
     return DIT_OK;
+}
+
+int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weights* w, const void* cond,
+                             const int32_t* pos, const void* x, void* y, void* workspace, size_t ws_bytes,
+                             void* stream) {
+    return single_block_impl(cfg, w, cond, pos, x, y, workspace, ws_bytes, stream, nullptr);
 }
 
 // ---- kernel timing --------------------------------------------------------------------------
@@ -591,6 +613,8 @@ static size_t step_ws(const dit_block_config* cfg, int n_double, int n_single) {
     if (n_single > 0) need = std::max(need, plan_workspace(cfg, 1).total);
     return need;
 }
+// The shared-modulation step appends the step's AdaLN vectors: [2][6d] (double) then [3d] (single).
+static size_t shared_mod_bytes(const dit_block_config* cfg) { return up256((size_t)15 * cfg->d * 4); }
 
 size_t dit_step_workspace_size(const dit_block_config* cfg, int n_double, int n_single) {
     clear_err();
@@ -598,10 +622,18 @@ size_t dit_step_workspace_size(const dit_block_config* cfg, int n_double, int n_
     return step_ws(cfg, n_double, n_single);
 }
 
-int dit_step_forward(const dit_block_config* cfg, int n_double, const dit_stream_weights* txt,
-                     const dit_stream_weights* img, int n_single, const dit_single_weights* single,
-                     const void* cond, const int32_t* pos, const void* x_txt, const void* x_img, float* y,
-                     void* workspace, size_t ws_bytes, void* stream) {
+size_t dit_step_shared_mod_workspace_size(const dit_block_config* cfg, int n_double, int n_single) {
+    clear_err();
+    if (validate_config(cfg) != DIT_OK || n_double < 0 || n_single < 0) return 0;
+    return up256(step_ws(cfg, n_double, n_single)) + shared_mod_bytes(cfg);
+}
+
+// shared: NULL (every block computes its AdaLN vectors from its own w_mod), or the three shared
+// modulation matrices {text [6d, d_cond], image [6d, d_cond], single [3d, d_cond]}.
+static int step_forward_impl(const dit_block_config* cfg, int n_double, const dit_stream_weights* txt,
+                             const dit_stream_weights* img, int n_single, const dit_single_weights* single,
+                             const void* const* shared, const void* cond, const int32_t* pos, const void* x_txt,
+                             const void* x_img, float* y, void* workspace, size_t ws_bytes, void* stream) {
     clear_err();
     DIT_TRY(validate_config(cfg));
     const dit_block_config& c = *cfg;
@@ -614,18 +646,25 @@ int dit_step_forward(const dit_block_config* cfg, int n_double, const dit_stream
     char what[48];
     for (int b = 0; b < n_double; ++b) {
         snprintf(what, sizeof what, "txt[%d]", b);
-        DIT_TRY(check_stream_weights(&txt[b], what));
+        DIT_TRY(check_stream_weights(&txt[b], what, !shared));
         snprintf(what, sizeof what, "img[%d]", b);
-        DIT_TRY(check_stream_weights(&img[b], what));
+        DIT_TRY(check_stream_weights(&img[b], what, !shared));
     }
     for (int b = 0; b < n_single; ++b) {
         const dit_single_weights& w = single[b];
         const void* p[4] = {w.w_mod, w.w_1, w.qk_norm_w, w.w_2};
         const char* nm[4] = {"w_mod", "w_1", "qk_norm_w", "w_2"};
-        for (int i = 0; i < 4; ++i) {
+        for (int i = shared ? 1 : 0; i < 4; ++i) {
             snprintf(what, sizeof what, "single[%d].%s", b, nm[i]);
             DIT_TRY(check_ptr(p[i], what));
         }
+    }
+    if (shared) {
+        if (n_double > 0) {
+            DIT_TRY(check_ptr(shared[0], "w_mod_txt"));
+            DIT_TRY(check_ptr(shared[1], "w_mod_img"));
+        }
+        if (n_single > 0) DIT_TRY(check_ptr(shared[2], "w_mod_single"));
     }
     DIT_TRY(check_ptr(cond, "cond"));
     DIT_TRY(check_ptr(pos, "pos"));
@@ -633,7 +672,8 @@ int dit_step_forward(const dit_block_config* cfg, int n_double, const dit_stream
     if (c.n_txt > 0) DIT_TRY(check_ptr(x_txt, "x_txt"));
     if (c.n_img > 0) DIT_TRY(check_ptr(x_img, "x_img"));
     DIT_TRY(check_ptr(workspace, "workspace"));
-    const size_t need = step_ws(cfg, n_double, n_single);
+    const size_t blocks_need = step_ws(cfg, n_double, n_single);
+    const size_t need = shared ? up256(blocks_need) + shared_mod_bytes(cfg) : blocks_need;
     if (ws_bytes < need) return fail(DIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
     const size_t nt = c.n_txt, ni = c.n_img, d = c.d, es = esize(c.x_dtype);
     if (n_double == 0 && nt > 0 && ni > 0 &&
@@ -647,6 +687,28 @@ int dit_step_forward(const dit_block_config* cfg, int n_double, const dit_stream
         return fail(DIT_ERR_INVALID_ARG, "workspace overlaps an input or y");
     if (overlap(ry, rxt) || overlap(ry, rxi)) return fail(DIT_ERR_INVALID_ARG, "y overlaps x_txt / x_img");
 
+    // shared modulation: one AdaLN GEMV launch per block kind for the whole step
+    float* mod_d = nullptr;
+    float* mod_s = nullptr;
+    if (shared) {
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        mod_d = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + up256(blocks_need));
+        mod_s = mod_d + 12 * d;
+        if (n_double > 0) {
+            GemvBatch g{};
+            g.p[0] = {shared[0], mod_d, (int)(6 * d)};
+            g.p[1] = {shared[1], mod_d + 6 * d, (int)(6 * d)};
+            g.n = 2; g.cond = cond; g.d_cond = c.d_cond; g.dtype = c.dtype;
+            DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
+        }
+        if (n_single > 0) {
+            GemvBatch g{};
+            g.p[0] = {shared[2], mod_s, (int)(3 * d)};
+            g.n = 1; g.cond = cond; g.d_cond = c.d_cond; g.dtype = c.dtype;
+            DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
+        }
+    }
+
     // the first block reads x (cfg->x_dtype) and writes the fp32 stream y; the others update y in place
     dit_block_config c_first = c, c_rest = c;
     c_first.y_dtype = DIT_F32;
@@ -656,13 +718,182 @@ int dit_step_forward(const dit_block_config* cfg, int n_double, const dit_stream
     float* y_img = y + nt * d;
     for (int b = 0; b < n_double; ++b) {
         const dit_block_config* cb = b == 0 ? &c_first : &c_rest;
-        DIT_TRY(dit_block_forward(cb, &txt[b], &img[b], cond, pos, b == 0 ? x_txt : y_txt, b == 0 ? x_img : y_img,
-                                  y_txt, y_img, workspace, ws_bytes, stream));
+        DIT_TRY(block_forward_impl(cb, &txt[b], &img[b], cond, pos, b == 0 ? x_txt : y_txt, b == 0 ? x_img : y_img,
+                                   y_txt, y_img, workspace, blocks_need, stream, mod_d));
     }
     for (int b = 0; b < n_single; ++b) {
         const bool first = n_double == 0 && b == 0;
-        DIT_TRY(dit_single_block_forward(first ? &c_first : &c_rest, &single[b], cond, pos, first ? x_txt : y, y,
-                                         workspace, ws_bytes, stream));
+        DIT_TRY(single_block_impl(first ? &c_first : &c_rest, &single[b], cond, pos, first ? x_txt : y, y, workspace,
+                                  blocks_need, stream, mod_s));
     }
     return DIT_OK;
+}
+
+int dit_step_forward(const dit_block_config* cfg, int n_double, const dit_stream_weights* txt,
+                     const dit_stream_weights* img, int n_single, const dit_single_weights* single,
+                     const void* cond, const int32_t* pos, const void* x_txt, const void* x_img, float* y,
+                     void* workspace, size_t ws_bytes, void* stream) {
+    return step_forward_impl(cfg, n_double, txt, img, n_single, single, nullptr, cond, pos, x_txt, x_img, y,
+                             workspace, ws_bytes, stream);
+}
+
+int dit_step_forward_shared_mod(const dit_block_config* cfg, int n_double, const dit_stream_weights* txt,
+                                const dit_stream_weights* img, int n_single, const dit_single_weights* single,
+                                const void* w_mod_txt, const void* w_mod_img, const void* w_mod_single,
+                                const void* cond, const int32_t* pos, const void* x_txt, const void* x_img, float* y,
+                                void* workspace, size_t ws_bytes, void* stream) {
+    const void* shared[3] = {w_mod_txt, w_mod_img, w_mod_single};
+    return step_forward_impl(cfg, n_double, txt, img, n_single, single, shared, cond, pos, x_txt, x_img, y,
+                             workspace, ws_bytes, stream);
+}
+
+// =========================================================================================
+// The layers either side of the block stack.
+// =========================================================================================
+static size_t temb_ws(int freq_dim, int d) { return up256((size_t)freq_dim * 4) + 2 * up256((size_t)d * 4); }
+
+size_t dit_timestep_embedding_workspace_size(int freq_dim, int d) {
+    clear_err();
+    if (freq_dim < 8 || freq_dim % 8 || d < 8 || d % 8) {
+        fail(DIT_ERR_INVALID_ARG, "freq_dim = %d, d = %d: need multiples of 8, at least 8", freq_dim, d);
+        return 0;
+    }
+    return temb_ws(freq_dim, d);
+}
+
+int dit_timestep_embedding(int dtype, void* stream, const float* t, const float* g, const void* w_t_in,
+                           const void* w_t_out, const void* w_g_in, const void* w_g_out, int freq_dim, int d,
+                           float max_period, float time_factor, void* cond_out, void* workspace, size_t ws_bytes) {
+    clear_err();
+    if (!valid_wdtype(dtype)) return fail(DIT_ERR_INVALID_ARG, "dtype must be DIT_BF16 or DIT_F32");
+    if (freq_dim < 8 || freq_dim % 8 || freq_dim > 16384)
+        return fail(DIT_ERR_INVALID_ARG, "freq_dim = %d must be a multiple of 8 in [8, 16384]", freq_dim);
+    if (d < 8 || d % 8 || d > 16384) return fail(DIT_ERR_INVALID_ARG, "d = %d must be a multiple of 8 in [8, 16384]", d);
+    if (!(max_period > 1.0f) || !std::isfinite(max_period)) return fail(DIT_ERR_INVALID_ARG, "max_period must be > 1");
+    if (!std::isfinite(time_factor)) return fail(DIT_ERR_INVALID_ARG, "time_factor must be finite");
+    if (!t) return fail(DIT_ERR_INVALID_ARG, "t is NULL");
+    DIT_TRY(check_ptr(w_t_in, "w_t_in"));
+    DIT_TRY(check_ptr(w_t_out, "w_t_out"));
+    if (g) {
+        DIT_TRY(check_ptr(w_g_in, "w_g_in"));
+        DIT_TRY(check_ptr(w_g_out, "w_g_out"));
+    }
+    DIT_TRY(check_ptr(cond_out, "cond_out"));
+    DIT_TRY(check_ptr(workspace, "workspace"));
+    const size_t need = temb_ws(freq_dim, d);
+    if (ws_bytes < need) return fail(DIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+    const Range rws{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+    if (overlap(rws, range_of(cond_out, 1, d, d, dtype))) return fail(DIT_ERR_INVALID_ARG, "cond_out overlaps the workspace");
+    char* ws = reinterpret_cast<char*>(workspace);
+    float* emb = reinterpret_cast<float*>(ws);
+    float* hid = reinterpret_cast<float*>(ws + up256((size_t)freq_dim * 4));
+    float* acc = reinterpret_cast<float*>(ws + up256((size_t)freq_dim * 4) + up256((size_t)d * 4));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // c = W_out . SiLU(W_in . emb(value)), summed over the timestep and (optionally) the guidance
+    for (int pass = 0; pass < (g ? 2 : 1); ++pass) {
+        const float* val = pass ? g : t;
+        const void* wi = pass ? w_g_in : w_t_in;
+        const void* wo = pass ? w_g_out : w_t_out;
+        DIT_TRY(launch("timestep_freq", s, [&] { return launch_freq_embed(val, time_factor, max_period, freq_dim, emb, s); }));
+        DIT_TRY(launch("embed_gemv_in", s, [&] { return launch_vec_gemv(wi, dtype, d, freq_dim, emb, false, hid, false, s); }));
+        DIT_TRY(launch("embed_gemv_out", s, [&] { return launch_vec_gemv(wo, dtype, d, d, hid, true, acc, pass > 0, s); }));
+    }
+    DIT_TRY(launch("cast", s, [&] { return launch_cast(acc, cond_out, d, dtype, s); }));
+    return DIT_OK;
+}
+
+int dit_linear(int dtype, void* stream, const void* x, int x_dtype, long ld_x, const void* w, int m, int n, int k,
+               void* y, int y_dtype, long ld_y) {
+    clear_err();
+    if (!valid_wdtype(dtype)) return fail(DIT_ERR_INVALID_ARG, "dtype must be DIT_BF16 or DIT_F32");
+    if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype))
+        return fail(DIT_ERR_INVALID_ARG, "x_dtype / y_dtype must be DIT_F32, DIT_BF16 or DIT_F16");
+    if (dtype == DIT_F32 && (x_dtype != DIT_F32 || y_dtype != DIT_F32))
+        return fail(DIT_ERR_UNSUPPORTED, "fp32 weights need fp32 x and y");
+    if (dtype == DIT_BF16 && x_dtype == DIT_F32)
+        return fail(DIT_ERR_UNSUPPORTED, "bf16 weights need DIT_BF16 or DIT_F16 x");
+    if (m < 0 || n < 8 || n % 8 || k < 16)
+        return fail(DIT_ERR_INVALID_ARG, "m = %d, n = %d, k = %d: need m >= 0, n a multiple of 8", m, n, k);
+    if (dtype == DIT_BF16 ? k % 64 : k % 16)
+        return fail(DIT_ERR_UNSUPPORTED, "k = %d must be a multiple of %d", k, dtype == DIT_BF16 ? 64 : 16);
+    if ((long)m * n > (1L << 31) || (long)n * k > (1L << 31)) return fail(DIT_ERR_UNSUPPORTED, "matrix too large");
+    DIT_TRY(check_ptr(w, "w"));
+    if (m == 0) return DIT_OK;
+    DIT_TRY(check_ptr(x, "x"));
+    DIT_TRY(check_ptr(y, "y"));
+    DIT_TRY(check_ld(ld_x, k, x_dtype, "ld_x"));
+    DIT_TRY(check_ld(ld_y, n, y_dtype, "ld_y"));
+    const Range ry = range_of(y, m, ld_y, n, y_dtype);
+    if (overlap(ry, range_of(x, m, ld_x, k, x_dtype)) || overlap(ry, range_of(w, n, k, k, dtype)))
+        return fail(DIT_ERR_INVALID_ARG, "y overlaps x or w");
+    GemmBatch b{};
+    b.a_dtype = dtype == DIT_F32 ? DIT_F32 : x_dtype;
+    b.p[0] = {x, ld_x, w, k, y, ld_y, y_dtype, nullptr, 0, 0, nullptr, 0, m, n, k, EPI_STORE};
+    b.n = 1;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("gemm_linear", s, [&] { return launch_gemm(b, s); });
+}
+
+static size_t final_ws(int n_tok, int d, int act_dtype) {
+    return up256((size_t)2 * d * 4) + up256((size_t)n_tok * d * esize(act_dtype));
+}
+
+size_t dit_final_layer_workspace_size(int n_tok, int d, int act_dtype) {
+    clear_err();
+    if (n_tok < 0 || d < 8 || !valid_dtype(act_dtype)) {
+        fail(DIT_ERR_INVALID_ARG, "n_tok = %d, d = %d, act_dtype = %d", n_tok, d, act_dtype);
+        return 0;
+    }
+    return final_ws(n_tok, d, act_dtype);
+}
+
+int dit_final_layer(int dtype, int act_dtype, void* stream, const void* x, int x_dtype, int n_tok, int d,
+                    const void* cond, int d_cond, const void* w_mod, const void* w_out, int p, float eps, void* y,
+                    int y_dtype, void* workspace, size_t ws_bytes) {
+    clear_err();
+    if (!valid_wdtype(dtype) || !valid_wdtype(x_dtype) || !valid_dtype(act_dtype) || !valid_dtype(y_dtype))
+        return fail(DIT_ERR_INVALID_ARG, "dtype / x_dtype must be DIT_F32 or DIT_BF16, act_dtype / y_dtype one of "
+                                         "DIT_F32, DIT_BF16, DIT_F16");
+    if (dtype == DIT_F32 && (x_dtype != DIT_F32 || act_dtype != DIT_F32 || y_dtype != DIT_F32))
+        return fail(DIT_ERR_UNSUPPORTED, "fp32 weights need fp32 x, activations and y");
+    if (dtype == DIT_BF16 && act_dtype == DIT_F32)
+        return fail(DIT_ERR_UNSUPPORTED, "bf16 weights need DIT_F16 or DIT_BF16 activations");
+    if (n_tok < 0) return fail(DIT_ERR_INVALID_ARG, "n_tok = %d", n_tok);
+    if (d < 64 || d % 64 || d > 8192) return fail(DIT_ERR_UNSUPPORTED, "d = %d must be a multiple of 64 in [64, 8192]", d);
+    if (d_cond < 8 || d_cond % 8 || d_cond > 16384)
+        return fail(DIT_ERR_INVALID_ARG, "d_cond = %d must be a multiple of 8 in [8, 16384]", d_cond);
+    if (p < 8 || p % 8) return fail(DIT_ERR_INVALID_ARG, "p = %d must be a positive multiple of 8", p);
+    if (!(eps >= 0.0f)) return fail(DIT_ERR_INVALID_ARG, "eps must be >= 0");
+    DIT_TRY(check_ptr(cond, "cond"));
+    DIT_TRY(check_ptr(w_mod, "w_mod"));
+    DIT_TRY(check_ptr(w_out, "w_out"));
+    DIT_TRY(check_ptr(workspace, "workspace"));
+    const size_t need = final_ws(n_tok, d, act_dtype);
+    if (ws_bytes < need) return fail(DIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+    if (n_tok > 0) {
+        DIT_TRY(check_ptr(x, "x"));
+        DIT_TRY(check_ptr(y, "y"));
+    }
+    const Range rws{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+    const Range rx = range_of(x, n_tok, d, d, x_dtype), ry = range_of(y, n_tok, p, p, y_dtype);
+    if (overlap(rws, rx) || overlap(rws, ry)) return fail(DIT_ERR_INVALID_ARG, "workspace overlaps x or y");
+    if (overlap(rx, ry)) return fail(DIT_ERR_INVALID_ARG, "y overlaps x");
+    char* ws = reinterpret_cast<char*>(workspace);
+    float* mod = reinterpret_cast<float*>(ws);
+    char* act = ws + up256((size_t)2 * d * 4);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // [shift, scale] = W_mod . SiLU(c)
+    GemvBatch g{};
+    g.p[0] = {w_mod, mod, 2 * d};
+    g.n = 1; g.cond = cond; g.d_cond = d_cond; g.dtype = dtype;
+    DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
+    if (n_tok == 0) return DIT_OK;
+    DIT_TRY(launch("layernorm_modulate", s, [&] {
+        return launch_layernorm_modulate(x, x_dtype, d, act, act_dtype, d, mod, mod + d, n_tok, d, eps, s);
+    }));
+    GemmBatch b{};
+    b.a_dtype = act_dtype;
+    b.p[0] = {act, d, w_out, d, y, p, y_dtype, nullptr, 0, 0, nullptr, 0, n_tok, p, d, EPI_STORE};
+    b.n = 1;
+    return launch("gemm_final", s, [&] { return launch_gemm(b, s); });
 }

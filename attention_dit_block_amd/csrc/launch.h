@@ -114,6 +114,19 @@ struct AttnArgs {
 hipError_t launch_attention(AttnArgs& a, hipStream_t s);
 size_t attention_sk_scratch_bytes();
 
+// ---- layers either side of the block stack ---------------------------------------------
+// emb [dim] fp32 = [cos(s f_j), sin(s f_j)], s = time_factor * t[0], f_j = max_period^(-j / (dim/2))
+hipError_t launch_freq_embed(const float* t, double time_factor, double max_period, int dim, float* emb,
+                             hipStream_t s);
+// out [rows] fp32 (+)= W [rows, K] (w_dtype F32 or BF16) . act(v), act = SiLU if silu_in
+hipError_t launch_vec_gemv(const void* w, int w_dtype, int rows, int K, const float* v, bool silu_in, float* out,
+                           bool accumulate, hipStream_t s);
+hipError_t launch_cast(const float* in, void* out, int n, int dtype, hipStream_t s);
+// out = (1 + scale) * LayerNorm(x) + shift per row (x: F32 or BF16)
+hipError_t launch_layernorm_modulate(const void* x, int x_dtype, long ld_x, void* out, int out_dtype, long ld_out,
+                                     const float* shift, const float* scale, int rows, int d, float eps,
+                                     hipStream_t s);
+
 // Compute units of the current device (0 if unknown), and nonzero launch tags unique in the
 // process, for the stream-K grids.
 int device_cu_count();

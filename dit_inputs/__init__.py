@@ -148,6 +148,8 @@ TENSOR_IDS: Dict[str, int] = {
     "w_mod": 10, "w_qkv": 11, "qk_norm_w": 12, "w_o": 13, "w_ffn_in": 14, "w_ffn_out": 15,
     "w_1": 16, "w_2": 17,
     "q": 20, "k": 21, "v": 22,
+    "w_t_in": 30, "w_t_out": 31, "w_g_in": 32, "w_g_out": 33, "w_patch": 34, "latent": 35,
+    "w_final_mod": 36, "w_final_out": 37, "w_mod_shared": 38,
 }
 STREAM_IDS = {"txt": 0, "img": 1, "single": 2, "none": 3}
 
@@ -261,3 +263,31 @@ def qkv_inputs(cfg: BlockConfig, seed: int = 0, std: float = 1.0) -> Dict[str, n
     shape = (cfg.n_tok, cfg.d)
     return {"q": draw(shape, std, t, seed, "q"), "k": draw(shape, std, t, seed, "k"),
             "v": draw(shape, std, t, seed, "v")}
+
+
+def edge_inputs(cfg: BlockConfig, seed: int = 0, freq_dim: int = 256, patch: int = 64) -> Dict[str, np.ndarray]:
+    """Inputs of the layers either side of the block stack: image latents in 2x2 patches of 16
+    channels [n_img, patch] ~ N(0, 1), and weights ~ N(0, 0.02^2) in the workload's type:
+    patch embedding [d, patch], timestep and guidance MLPs [d, freq_dim] + [d, d], final
+    layer modulation [2d, d_cond] and projection [patch, d]."""
+    t, d = cfg.dtype, cfg.d
+    return {
+        "latent": draw((cfg.n_img, patch), 1.0, t, seed, "latent"),
+        "w_patch": draw((d, patch), 0.02, t, seed, "w_patch"),
+        "w_t_in": draw((d, freq_dim), 0.02, t, seed, "w_t_in"),
+        "w_t_out": draw((d, d), 0.02, t, seed, "w_t_out"),
+        "w_g_in": draw((d, freq_dim), 0.02, t, seed, "w_g_in"),
+        "w_g_out": draw((d, d), 0.02, t, seed, "w_g_out"),
+        "w_final_mod": draw((2 * d, cfg.dc), 0.02, t, seed, "w_final_mod"),
+        "w_final_out": draw((patch, d), 0.02, t, seed, "w_final_out"),
+        "cond": draw((cfg.dc,), 1.0, t, seed, "cond"),
+    }
+
+
+def shared_mod_weights(cfg: BlockConfig, seed: int = 0) -> Dict[str, np.ndarray]:
+    """One AdaLN weight set per block kind, shared by all blocks of a step: text [6d, d_cond],
+    image [6d, d_cond], single [3d, d_cond], ~ N(0, 0.02^2)."""
+    t, d = cfg.dtype, cfg.d
+    return {"txt": draw((6 * d, cfg.dc), 0.02, t, seed, "w_mod_shared", stream="txt"),
+            "img": draw((6 * d, cfg.dc), 0.02, t, seed, "w_mod_shared", stream="img"),
+            "single": draw((3 * d, cfg.dc), 0.02, t, seed, "w_mod_shared", stream="single")}

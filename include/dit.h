@@ -259,6 +259,102 @@ int dit_step_forward(const dit_block_config* cfg, int n_double,
                      const void* x_txt, const void* x_img, float* y,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/* Workspace bytes of dit_step_forward_shared_mod: dit_step_workspace_size
+ * rounded up to 256 bytes, plus 15 * d fp32 AdaLN values. */
+size_t dit_step_shared_mod_workspace_size(const dit_block_config* cfg, int n_double, int n_single);
+
+/*
+ * dit_step_forward with shared modulation: one set of AdaLN weights serves
+ * every double-stream block (one matrix per stream) and another every
+ * single-stream block, so the step computes its AdaLN vectors once -- one
+ * GEMV launch per block kind instead of one per block (the "one GEMV per
+ * step" variant of the denoising step of a FLUX-style model, the FLUX Klein
+ * transformer the "CUDA codepath !" thread runs).  The per-block w_mod fields
+ * are not read and may be NULL.
+ *  w_mod_txt, w_mod_img  [6d, d_cond] of dtype (needed when n_double > 0)
+ *  w_mod_single          [3d, d_cond] of dtype (needed when n_single > 0)
+ *  workspace >= dit_step_shared_mod_workspace_size(cfg, n_double, n_single)
+ * Other arguments and guarantees as for dit_step_forward; 8 launches per
+ * double-stream block and 5 per single-stream block, plus 1 per block kind.
+ * With every block's w_mod equal to the shared matrix the result is
+ * bit-identical to dit_step_forward's.
+ */
+int dit_step_forward_shared_mod(const dit_block_config* cfg, int n_double,
+                                const dit_stream_weights* txt, const dit_stream_weights* img,
+                                int n_single, const dit_single_weights* single,
+                                const void* w_mod_txt, const void* w_mod_img, const void* w_mod_single,
+                                const void* cond, const int32_t* pos,
+                                const void* x_txt, const void* x_img, float* y,
+                                void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The layers either side of the block stack.  The pages name the step's
+ * transformer but print none of them; they follow the FLUX model (no biases,
+ * like the block).
+ */
+
+/* Workspace bytes of dit_timestep_embedding (fp32 scratch: freq_dim + 2 d
+ * values, each part 256-byte aligned); 0 for invalid sizes. */
+size_t dit_timestep_embedding_workspace_size(int freq_dim, int d);
+
+/*
+ * Conditioning vector from the timestep (and optional guidance) value:
+ *   emb(v) = [cos(s f_0) .. cos(s f_{h-1}), sin(s f_0) .. sin(s f_{h-1})],
+ *            s = time_factor * v, h = freq_dim / 2, f_j = max_period^(-j/h)
+ *   cond   = W_t_out SiLU(W_t_in emb(t))  [+ W_g_out SiLU(W_g_in emb(g))]
+ * summed in fp32 and rounded once to dtype.  FLUX: freq_dim 256,
+ * max_period 1e4, time_factor 1000.
+ *  dtype     weights and cond_out: DIT_BF16 or DIT_F32
+ *  t         fp32 [1] on the device (a graph replay picks up a new value)
+ *  g         fp32 [1] on the device, or NULL (no guidance term; w_g_* unused)
+ *  w_t_in, w_g_in    [d, freq_dim];  w_t_out, w_g_out  [d, d]
+ *  cond_out  [d] of dtype (the cond argument of the block calls)
+ *  workspace >= dit_timestep_embedding_workspace_size(freq_dim, d) bytes
+ * Limits: freq_dim and d multiples of 8 in [8, 16384]; max_period > 1.
+ * 4 launches (7 with guidance).
+ */
+int dit_timestep_embedding(int dtype, void* stream, const float* t, const float* g,
+                           const void* w_t_in, const void* w_t_out,
+                           const void* w_g_in, const void* w_g_out,
+                           int freq_dim, int d, float max_period, float time_factor,
+                           void* cond_out, void* workspace, size_t ws_bytes);
+
+/*
+ * y = x W^T on the block's GEMM kernel: the patch embedding of the image
+ * latents ([n_img, 64] -> [n_img, d] for 16 latent channels in 2x2 patches),
+ * the text embedding, or any other projection without bias.
+ *  dtype     of w [n, k]: DIT_BF16 (x DIT_BF16 or DIT_F16, fp32 accumulation)
+ *            or DIT_F32 (x and y DIT_F32, fp32 arithmetic)
+ *  x         [m, k] of x_dtype, row stride ld_x;  y [m, n] of y_dtype, ld_y
+ * Limits: n a multiple of 8; k a multiple of 64 (bf16) or 16 (fp32); y must
+ * not overlap x or w.  One launch.
+ */
+int dit_linear(int dtype, void* stream, const void* x, int x_dtype, long ld_x,
+               const void* w, int m, int n, int k, void* y, int y_dtype, long ld_y);
+
+/* Workspace bytes of dit_final_layer: 2 d fp32 values + n_tok rows of d
+ * act_dtype values (each part 256-byte aligned). */
+size_t dit_final_layer_workspace_size(int n_tok, int d, int act_dtype);
+
+/*
+ * Last layer of the model over the image tokens:
+ *   [shift, scale] = W_mod SiLU(cond)                         (2 d, fp32)
+ *   a = (1 + scale) LayerNorm(x) + shift,  LayerNorm(x) = (x - mean) / sqrt(var + eps)
+ *       over the d features of a row (population variance, no affine)
+ *   y = a W_out^T
+ *  dtype     of cond, w_mod [2d, d_cond] and w_out [p, d]: DIT_BF16 or DIT_F32
+ *  act_dtype storage of a (DIT_F16 or DIT_BF16 for bf16 weights, DIT_F32)
+ *  x         [n_tok, d] of x_dtype (DIT_F32 or DIT_BF16), contiguous rows --
+ *            e.g. the image rows of dit_step_forward's y
+ *  y         [n_tok, p] of y_dtype, contiguous rows (p = 64 for FLUX's 2x2
+ *            patches of 16 channels); must not overlap x
+ * Limits: d a multiple of 64 in [64, 8192]; p a multiple of 8.  3 launches.
+ */
+int dit_final_layer(int dtype, int act_dtype, void* stream, const void* x, int x_dtype,
+                    int n_tok, int d, const void* cond, int d_cond, const void* w_mod,
+                    const void* w_out, int p, float eps, void* y, int y_dtype,
+                    void* workspace, size_t ws_bytes);
+
 /* Thread-local text of the last error of this thread (never NULL). */
 const char* dit_last_error(void);
 

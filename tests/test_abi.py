@@ -282,3 +282,81 @@ def test_step_validation_checks_every_block_first(dit):
                                                  FakeDev(0x12000000, shape=(80, 256), dtype=torch.float32, esize=4),
                                                  ws, stream=FakeStream()))
     assert "overlaps" in str(e)
+
+
+def _up(x):
+    return (x + 255) // 256 * 256
+
+
+def test_edge_layer_sizes_and_validation(dit):
+    import torch
+    assert dit.timestep_embedding_workspace_size(256, 3072) == _up(256 * 4) + 2 * _up(3072 * 4)
+    assert dit.final_layer_workspace_size(4096, 3072, dit.DIT_F16) == _up(2 * 3072 * 4) + _up(4096 * 3072 * 2)
+    x = FakeDev(0x100000, shape=(64, 64))
+    w = FakeDev(0x200000, shape=(3072, 64))
+    y = FakeDev(0x400000, shape=(64, 3072))
+    # linear: n not a multiple of 8; k not a multiple of the MFMA k-step; y overlapping x
+    e = _no_launch(dit, lambda: dit.linear(x, FakeDev(0x200000, shape=(3070, 64)), FakeDev(0x400000, shape=(64, 3070)),
+                                           stream=FakeStream()))
+    assert "multiple of 8" in str(e)
+    e = _no_launch(dit, lambda: dit.linear(FakeDev(0x100000, shape=(64, 48)), FakeDev(0x200000, shape=(3072, 48)), y,
+                                           stream=FakeStream()))
+    assert e.status == "DIT_ERR_UNSUPPORTED"
+    e = _no_launch(dit, lambda: dit.linear(x, w, FakeDev(0x100000 + 1024, shape=(64, 3072)), stream=FakeStream()))
+    assert "overlaps" in str(e)
+    # final layer: d not a multiple of 64; undersized workspace
+    cond = FakeDev(0x600000, shape=(3072,))
+    e = _no_launch(dit, lambda: dit.final_layer(FakeDev(0x1000000, shape=(16, 3000)), cond,
+                                                FakeDev(0x2000000, shape=(6000, 3072)),
+                                                FakeDev(0x3000000, shape=(64, 3000)),
+                                                FakeDev(0x4000000, shape=(16, 64), dtype=torch.float32, esize=4),
+                                                FakeDev(0x5000000, shape=(1 << 20,), dtype=torch.uint8, esize=1),
+                                                stream=FakeStream()))
+    assert "multiple of 64" in str(e)
+    need = dit.final_layer_workspace_size(16, 3072, dit.DIT_F16)
+    e = _no_launch(dit, lambda: dit.final_layer(FakeDev(0x1000000, shape=(16, 3072)), cond,
+                                                FakeDev(0x2000000, shape=(6144, 3072)),
+                                                FakeDev(0x3000000, shape=(64, 3072)),
+                                                FakeDev(0x4000000, shape=(16, 64), dtype=torch.float32, esize=4),
+                                                FakeDev(0x5000000, shape=(need - 256,), dtype=torch.uint8, esize=1),
+                                                stream=FakeStream()))
+    assert e.status == "DIT_ERR_WORKSPACE"
+    # timestep embedding: max_period must exceed 1; guidance needs its weights
+    t = FakeDev(0x700000, shape=(1,), dtype=torch.float32, esize=4)
+    wi, wo = FakeDev(0x800000, shape=(3072, 256)), FakeDev(0x1800000, shape=(3072, 3072))
+    c = FakeDev(0x3800000, shape=(3072,))
+    ws = FakeDev(0x4000000, shape=(1 << 20,), dtype=torch.uint8, esize=1)
+    e = _no_launch(dit, lambda: dit.timestep_embedding(t, wi, wo, c, ws, max_period=1.0, stream=FakeStream()))
+    assert "max_period" in str(e)
+    g = FakeDev(0x700100, shape=(1,), dtype=torch.float32, esize=4)
+    e = _no_launch(dit, lambda: dit.timestep_embedding(t, wi, wo, c, ws, g=g, stream=FakeStream()))
+    assert "w_g_in" in str(e)
+
+
+def test_shared_mod_step_validation(dit):
+    import torch
+    s = _cfg(dit, n_txt=16, n_img=64, d=256, n_heads=2, ffn_inner=768)
+    need = dit.step_shared_mod_workspace_size(s, 1, 1)
+    assert need == _up(dit.step_workspace_size(s, 1, 1)) + _up(15 * 256 * 4)
+    wts = {n: FakeDev(0x1000000 * (i + 1), shape=(1 << 20,)) for i, n in enumerate(
+        ("w_qkv", "qk_norm_w", "w_o", "w_ffn_in", "w_ffn_out"))}     # no per-block w_mod
+    sw = {n: FakeDev(0x8000000 * (i + 1), shape=(1 << 20,)) for i, n in enumerate(("w_1", "qk_norm_w", "w_2"))}
+    mt, mi, ms = (FakeDev(0x20000000 + i * 0x1000000, shape=(1 << 20,)) for i in range(3))
+    cond = FakeDev(0x10000000, shape=(256,))
+    pos = FakeDev(0x11000000, shape=(80, 4), dtype=torch.int32, esize=4)
+    xt, xi = FakeDev(0x12000000, shape=(16, 256)), FakeDev(0x13000000, shape=(64, 256))
+    y = FakeDev(0x14000000, shape=(80, 256), dtype=torch.float32, esize=4)
+    ws = FakeDev(0x40000000, shape=(need,), dtype=torch.uint8, esize=1)
+    # the shared single-block matrix is missing
+    e = _no_launch(dit, lambda: dit.step_forward_shared_mod(s, [wts], [wts], [sw], mt, mi, None, cond, pos, xt, xi, y,
+                                                            ws, stream=FakeStream()))
+    assert "w_mod_single" in str(e)
+    # the plain step's workspace is too small for the shared-modulation step
+    small = FakeDev(0x40000000, shape=(dit.step_workspace_size(s, 1, 1),), dtype=torch.uint8, esize=1)
+    e = _no_launch(dit, lambda: dit.step_forward_shared_mod(s, [wts], [wts], [sw], mt, mi, ms, cond, pos, xt, xi, y,
+                                                            small, stream=FakeStream()))
+    assert e.status == "DIT_ERR_WORKSPACE"
+    # the plain step still needs every block's w_mod
+    e = _no_launch(dit, lambda: dit.step_forward(s, [dict(wts, w_mod=None)], [dict(wts, w_mod=None)],
+                                                 [dict(sw, w_mod=None)], cond, pos, xt, xi, y, ws, stream=FakeStream()))
+    assert "txt[0].w_mod is NULL" in str(e)
