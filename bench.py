@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="skip timing the step replayed from a captured graph")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--shared-mod", action="store_true",
+                   help="multi-block workloads: one AdaLN weight set per block kind, computed once per step")
     p.add_argument("--act", default="f16", choices=["f16", "bf16"],
                    help="storage of the activations between the block's steps (bf16 workloads)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -50,10 +52,11 @@ def parse():
     return p.parse_args()
 
 
-def step_work(cfg):
+def step_work(cfg, shared_mod=False):
     """Algorithmic work of one step per launch site: {name: (flops, bytes, bound, launches)}.
     A step is the workload's blocks: n_double double-stream blocks (the first reads the bf16 input,
-    later ones the fp32 residual stream), then n_single single-stream blocks (fp32 stream)."""
+    later ones the fp32 residual stream), then n_single single-stream blocks (fp32 stream).
+    shared_mod: the AdaLN GEMV runs once per block kind instead of once per block."""
     n, d, F, dc = cfg.n_tok, cfg.d, cfg.ffn_inner, cfg.dc
     es = 2 if cfg.dtype == "bf16" else 4            # weights and inter-step activations
     work = {}
@@ -65,7 +68,8 @@ def step_work(cfg):
     for blk in range(cfg.n_double + cfg.n_single):
         double = blk < cfg.n_double
         ex = es if blk == 0 else 4                   # block input: workload type, then fp32 stream
-        add("adaln_gemv", nbytes=(12 if double else 3) * d * dc * es, bound="hbm")
+        if not shared_mod or blk in (0, cfg.n_double):
+            add("adaln_gemv", nbytes=(12 if double else 3) * d * dc * es, bound="hbm")
         add("modulate_x", nbytes=n * d * (ex + es), bound="hbm")
         add("qk_rmsnorm_rope", nbytes=4.0 * n * d * es + 16.0 * n, bound="hbm")
         add("joint_attention", flops=4.0 * n * n * d)
@@ -81,9 +85,9 @@ def step_work(cfg):
     return work
 
 
-def kernel_work(cfg, name):
+def kernel_work(cfg, name, shared_mod=False):
     """Algorithmic work of one launch of a launch site, averaged over the step: (flops, bytes, bound)."""
-    w = step_work(cfg).get(name)
+    w = step_work(cfg, shared_mod).get(name)
     if w is None:
         return None, None, "?"
     f, b, bound, cnt = w
@@ -151,10 +155,19 @@ def main():
         for b in range(cfg.n_single):
             print(f"setup: single block {b + 1}/{cfg.n_single}", file=sys.stderr, flush=True)
             sws.append({k: up(v, t) for k, v in di.single_weights(cfg, args.seed, cfg.n_double + b).items()})
-        ws = torch.empty(dit.step_workspace_size(shape, cfg.n_double, cfg.n_single), dtype=torch.uint8, device=dev)
         state = torch.empty(cfg.n_tok, cfg.d, dtype=torch.float32, device=dev)
-        step_blocks.append(lambda: dit.step_forward(shape, wts, wis, sws, cond, pos, x_txt, x_img, state, ws))
+        if args.shared_mod:
+            sm = {k: up(v, t) for k, v in di.shared_mod_weights(cfg, seed=args.seed).items()}
+            ws = torch.empty(dit.step_shared_mod_workspace_size(shape, cfg.n_double, cfg.n_single),
+                             dtype=torch.uint8, device=dev)
+            step_blocks.append(lambda: dit.step_forward_shared_mod(shape, wts, wis, sws, sm["txt"], sm["img"],
+                                                                   sm["single"], cond, pos, x_txt, x_img, state, ws))
+        else:
+            ws = torch.empty(dit.step_workspace_size(shape, cfg.n_double, cfg.n_single), dtype=torch.uint8,
+                             device=dev)
+            step_blocks.append(lambda: dit.step_forward(shape, wts, wis, sws, cond, pos, x_txt, x_img, state, ws))
     setup_s = time.time() - t0
+    shared = bool(args.shared_mod) and (cfg.n_double + cfg.n_single) > 1
 
     def step():
         for f in step_blocks:
@@ -201,7 +214,7 @@ def main():
         del graph
 
     # per-kernel durations: HIP events around every launch of the library, same stream
-    dit.timing_begin(args.steps * 16 * len(step_blocks))
+    dit.timing_begin(args.steps * 16 * (cfg.n_double + cfg.n_single))     # >= the launches of every step
     for _ in range(args.steps):
         step()
     dit.timing_end()
@@ -210,7 +223,7 @@ def main():
     kernels = {}
     for name, (cnt, tot) in kt.items():
         avg = tot / cnt
-        fl, by, bound = kernel_work(cfg, name)
+        fl, by, bound = kernel_work(cfg, name, shared)
         e = {"launches_per_step": cnt / args.steps, "avg_ms": round(avg, 5),
              "share": round(tot / sum(v[1] for v in kt.values()), 4), "bound": bound}
         if fl:
@@ -221,7 +234,7 @@ def main():
             e["frac_hbm"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
         kernels[name] = e
     dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
-    fl, by, bound = kernel_work(cfg, dom)
+    fl, by, bound = kernel_work(cfg, dom, shared)
     avg = kt[dom][1] / kt[dom][0]
     if fl:
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(fl / (avg * 1e-3) / 1e12, 1),
@@ -239,7 +252,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "activations": args.act if t == "bf16" else "f32", "blocks": cfg.n_double + cfg.n_single, "d": cfg.d, "heads": cfg.n_heads,
                    "ffn_inner": cfg.ffn_inner, "n_txt": cfg.n_txt, "n_img": cfg.n_img, "tokens": cfg.n_tok,
-                   "gflop_per_step": round(flops / 1e9, 1)},
+                   "gflop_per_step": round(flops / 1e9, 1),
+                   "modulation": "shared" if shared else "per_block"},
         "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "ms_per_step_hip_events": round(ev_ms, 4),
         "ms_per_step_graph_replay": None if ms_graph is None else round(ms_graph, 4),
