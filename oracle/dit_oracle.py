@@ -348,3 +348,40 @@ def final_layer(x: np.ndarray, cond: np.ndarray, w_mod: np.ndarray, w_out: np.nd
     d = np.asarray(x).shape[-1]
     m = adaln_modulation(w_mod, cond).reshape(2, d)
     return linear((1.0 + m[1]) * layer_norm(x, eps) + m[0], w_out)
+
+
+# --- windowed (neighborhood) attention ---------------------------------------------------
+# The diffusion-VAE decoder page ports a neighborhood-attention kernel: every query attends to the
+# keys of a 3-D window (odd size per axis) around its grid position, with the boundary rule of
+# NATTEN -- near an edge the window shifts inwards instead of shrinking, and an axis narrower
+# than the requested window is attended in full (the effective size per axis is min(k, extent)).
+
+def window_start(i: int, k: int, n: int) -> int:
+    """First position of the window of size min(k, n) along an axis of extent n for query
+    position i: centred on i where it fits, shifted to stay inside [0, n)."""
+    ke = min(k, n)
+    return min(max(i - k // 2, 0), n - ke)
+
+
+def neighborhood_attention(q, k, v, grid: Sequence[int], kernel: Sequence[int], n_heads: int, head_dim: int,
+                           scale: Optional[float] = None, q_rows=None) -> np.ndarray:
+    """O = softmax(q K_W^T * scale) V_W per head, K_W / V_W the tokens of the query's window.
+    Tokens are the grid positions (t, h, w) in row-major order (w fastest); q, k, v are
+    [T*H*W, n_heads*head_dim].  Returns the rows q_rows (all by default)."""
+    q, k, v = (np.asarray(a, F64) for a in (q, k, v))
+    T, H, W = grid
+    scale = head_dim ** -0.5 if scale is None else scale
+    rows = np.arange(T * H * W) if q_rows is None else np.asarray(q_rows)
+    eff = [min(kk, n) for kk, n in zip(kernel, grid)]
+    out = np.empty((len(rows), n_heads * head_dim), F64)
+    for r_i, r in enumerate(rows):
+        t, h, w = r // (H * W), (r // W) % H, r % W
+        st = [window_start(i, kk, n) for i, kk, n in zip((t, h, w), kernel, grid)]
+        tt, hh, ww = np.meshgrid(np.arange(st[0], st[0] + eff[0]), np.arange(st[1], st[1] + eff[1]),
+                                 np.arange(st[2], st[2] + eff[2]), indexing="ij")
+        keys = ((tt * H + hh) * W + ww).ravel()
+        for hd in range(n_heads):
+            sl = slice(hd * head_dim, (hd + 1) * head_dim)
+            p = softmax_rows((q[r, sl] @ k[keys, sl].T * scale)[None, :])[0]
+            out[r_i, sl] = p @ v[keys, sl]
+    return out
