@@ -21,7 +21,7 @@ __all__ = [
     "block_workspace_size", "block_forward", "single_block_forward",
     "step_workspace_size", "step_forward", "step_shared_mod_workspace_size", "step_forward_shared_mod",
     "timestep_embedding_workspace_size", "timestep_embedding", "linear",
-    "final_layer_workspace_size", "final_layer",
+    "final_layer_workspace_size", "final_layer", "neighborhood_attention",
     "last_error", "launch_count", "abi_version",
     "timing_begin", "timing_end", "timing_read",
 ]
@@ -84,6 +84,8 @@ _temb = _sig("dit_timestep_embedding", _i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _v
 _linear = _sig("dit_linear", _i, [_i, _vp, _vp, _i, _l, _vp, _i, _i, _i, _vp, _i, _l])
 _final_wsize = _sig("dit_final_layer_workspace_size", _sz, [_i, _i, _i])
 _final = _sig("dit_final_layer", _i, [_i, _i, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _i, _f, _vp, _i, _vp, _sz])
+_natten = _sig("dit_neighborhood_attention", _i, [_i, _vp, _vp, _l, _vp, _l, _vp, _l, _vp, _l, ctypes.POINTER(_i),
+                                                 ctypes.POINTER(_i), _i, _i, _f])
 _last_error = _sig("dit_last_error", ctypes.c_char_p, [])
 _launch_count = _sig("dit_launch_count", ctypes.c_uint64, [])
 _abi = _sig("dit_abi_version", _i, [])
@@ -95,7 +97,7 @@ EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", 
             "dit_block_forward", "dit_single_block_forward", "dit_step_workspace_size", "dit_step_forward",
             "dit_step_shared_mod_workspace_size", "dit_step_forward_shared_mod",
             "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_linear",
-            "dit_final_layer_workspace_size", "dit_final_layer",
+            "dit_final_layer_workspace_size", "dit_final_layer", "dit_neighborhood_attention",
             "dit_last_error", "dit_launch_count",
             "dit_abi_version", "dit_timing_begin", "dit_timing_end", "dit_timing_read"]
 
@@ -474,6 +476,21 @@ def final_layer(x, cond, w_mod, w_out, y, workspace, act_dtype: Optional[int] = 
                 _ptr(w_mod, "w_mod"), _ptr(w_out, "w_out"), p, eps, _ptr(y, "y"), _dt(y),
                 _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size())
     _check(rc, "dit_final_layer")
+
+
+def neighborhood_attention(q, k, v, o, grid: Sequence[int], kernel: Sequence[int], n_heads: int,
+                           softmax_scale: Optional[float] = None, head_dim: int = 128, stream=None) -> None:
+    """Windowed attention over a [T, H, W] token grid (see include/dit.h)."""
+    if softmax_scale is None:
+        softmax_scale = head_dim ** -0.5
+    n = int(grid[0]) * int(grid[1]) * int(grid[2])
+    for t, what in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _rows(t, n, n_heads * head_dim, what)
+    g = (_i * 3)(*grid)
+    kk = (_i * 3)(*kernel)
+    rc = _natten(_dt(q), _stream(stream), _ptr(q, "q"), _ld(q, "q"), _ptr(k, "k"), _ld(k, "k"), _ptr(v, "v"),
+                 _ld(v, "v"), _ptr(o, "o"), _ld(o, "o"), g, kk, n_heads, head_dim, softmax_scale)
+    _check(rc, "dit_neighborhood_attention")
 
 
 # --- kernel timing -----------------------------------------------------------------------------

@@ -897,3 +897,57 @@ int dit_final_layer(int dtype, int act_dtype, void* stream, const void* x, int x
     b.n = 1;
     return launch("gemm_final", s, [&] { return launch_gemm(b, s); });
 }
+
+// =========================================================================================
+// Windowed (neighborhood) attention.
+// =========================================================================================
+int dit_neighborhood_attention(int dtype, void* stream, const void* q, long ld_q, const void* k, long ld_k,
+                               const void* v, long ld_v, void* o, long ld_o, const int* grid, const int* kernel,
+                               int n_heads, int head_dim, float softmax_scale) {
+    clear_err();
+    if (!valid_dtype(dtype)) return fail(DIT_ERR_INVALID_ARG, "dtype must be DIT_F32, DIT_BF16 or DIT_F16");
+    if (!grid || !kernel) return fail(DIT_ERR_INVALID_ARG, "grid / kernel is NULL");
+    if (head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim = %d (only 128 is supported)", head_dim);
+    if (n_heads < 1) return fail(DIT_ERR_INVALID_ARG, "n_heads = %d", n_heads);
+    long n_tok = 1;
+    int keff[3];
+    for (int a = 0; a < 3; ++a) {
+        if (grid[a] < 1) return fail(DIT_ERR_INVALID_ARG, "grid[%d] = %d must be positive", a, grid[a]);
+        if (kernel[a] < 1 || kernel[a] % 2 == 0)
+            return fail(DIT_ERR_INVALID_ARG, "kernel[%d] = %d must be positive and odd", a, kernel[a]);
+        keff[a] = std::min(kernel[a], grid[a]);
+        n_tok *= grid[a];
+        if (n_tok > (1L << 24)) return fail(DIT_ERR_UNSUPPORTED, "more than 2^24 tokens");
+    }
+    if (n_tok * n_heads > (1L << 30)) return fail(DIT_ERR_UNSUPPORTED, "n_tok * n_heads too large");
+    if (!std::isfinite(softmax_scale)) return fail(DIT_ERR_INVALID_ARG, "softmax_scale must be finite");
+    if (dtype != DIT_F32) {
+        if (!(softmax_scale > 0.0f)) return fail(DIT_ERR_UNSUPPORTED, "the 16-bit kernel needs softmax_scale > 0");
+        if (keff[2] > kWinMaxKW)
+            return fail(DIT_ERR_UNSUPPORTED, "window of %d along W (at most %d on the 16-bit kernel)", keff[2], kWinMaxKW);
+    } else if ((long)keff[0] * keff[1] * keff[2] > kWinMaxKeysF32) {
+        return fail(DIT_ERR_UNSUPPORTED, "window of %ld keys (at most %d on the fp32 kernel)",
+                    (long)keff[0] * keff[1] * keff[2], kWinMaxKeysF32);
+    }
+    const long width = (long)n_heads * head_dim;
+    DIT_TRY(check_ptr(q, "q"));
+    DIT_TRY(check_ptr(k, "k"));
+    DIT_TRY(check_ptr(v, "v"));
+    DIT_TRY(check_ptr(o, "o"));
+    DIT_TRY(check_ld(ld_q, width, dtype, "ld_q"));
+    DIT_TRY(check_ld(ld_k, width, dtype, "ld_k"));
+    DIT_TRY(check_ld(ld_v, width, dtype, "ld_v"));
+    DIT_TRY(check_ld(ld_o, width, dtype, "ld_o"));
+    const Range ro = range_of(o, n_tok, ld_o, width, dtype);
+    if (overlap(ro, range_of(q, n_tok, ld_q, width, dtype)) || overlap(ro, range_of(k, n_tok, ld_k, width, dtype)) ||
+        overlap(ro, range_of(v, n_tok, ld_v, width, dtype)))
+        return fail(DIT_ERR_INVALID_ARG, "o overlaps q, k or v");
+    WinAttnArgs a{};
+    a.q = q; a.ld_q = ld_q; a.k = k; a.ld_k = ld_k; a.v = v; a.ld_v = ld_v; a.o = o; a.ld_o = ld_o;
+    a.T = grid[0]; a.H = grid[1]; a.W = grid[2];
+    a.kT = keff[0]; a.kH = keff[1]; a.kW = keff[2];
+    a.rT = kernel[0]; a.rH = kernel[1]; a.rW = kernel[2];
+    a.n_heads = n_heads; a.scale = softmax_scale; a.dtype = dtype;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("window_attention", s, [&] { return launch_window_attention(a, s); });
+}

@@ -114,6 +114,26 @@ struct AttnArgs {
 hipError_t launch_attention(AttnArgs& a, hipStream_t s);
 size_t attention_sk_scratch_bytes();
 
+// ---- windowed (neighborhood) attention over a [T, H, W] token grid --------------------------
+struct WinAttnArgs {
+    const void* q; long ld_q;
+    const void* k; long ld_k;
+    const void* v; long ld_v;
+    void* o; long ld_o;
+    int T, H, W;            // grid; token (t, h, w) is row (t * H + h) * W + w
+    int kT, kH, kW;         // effective window per axis: min(requested, extent)
+    int rT, rH, rW;         // requested (odd) window per axis, for the window start
+    int n_heads;
+    float scale;
+    int dtype;              // F32, BF16 or F16
+    int tiles_h, tiles_w;   // filled by the launcher
+};
+hipError_t launch_window_attention(WinAttnArgs& a, hipStream_t s);
+// Largest effective window along W the 16-bit kernel handles, and the most window keys the fp32
+// kernel handles.
+constexpr int kWinMaxKW = 49;
+constexpr int kWinMaxKeysF32 = 4096;
+
 // ---- layers either side of the block stack ---------------------------------------------
 // emb [dim] fp32 = [cos(s f_j), sin(s f_j)], s = time_factor * t[0], f_j = max_period^(-j / (dim/2))
 hipError_t launch_freq_embed(const float* t, double time_factor, double max_period, int dim, float* emb,

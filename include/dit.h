@@ -355,6 +355,30 @@ int dit_final_layer(int dtype, int act_dtype, void* stream, const void* x, int x
                     const void* w_out, int p, float eps, void* y, int y_dtype,
                     void* workspace, size_t ws_bytes);
 
+/*
+ * Windowed (neighborhood) attention over a [T, H, W] token grid (the
+ * neighborhood-attention kernel of the diffusion-VAE decoder page; LTX-2.5's
+ * decoder uses a [11, 11, 11] window).  Token (t, h, w) is row
+ * (t * H + h) * W + w of q, k, v and o.  Per head, the query at (t, h, w)
+ * attends to the keys of its window: along each axis the min(kernel, extent)
+ * consecutive positions starting at clamp(i - kernel / 2, 0, extent - size) --
+ * centred where it fits, shifted inwards at an edge, and the whole axis when
+ * the window is wider than the grid.
+ *   o = softmax(q K_win^T * softmax_scale) V_win
+ *  dtype     DIT_BF16 or DIT_F16 (fp32 accumulation; MFMA) or DIT_F32
+ *  q, k, v, o  [T*H*W, n_heads * head_dim] views with row strides ld_*
+ *  grid, kernel  (host) int[3]: extents T, H, W and the requested window, each
+ *            window size a positive odd number
+ * Limits: head_dim 128; at most 2^24 tokens; 16-bit: softmax_scale > 0 and at
+ * most 49 positions of window along W; fp32: at most 4096 keys per window.
+ * o must not overlap q, k or v.  One launch.
+ */
+int dit_neighborhood_attention(int dtype, void* stream,
+                               const void* q, long ld_q, const void* k, long ld_k,
+                               const void* v, long ld_v, void* o, long ld_o,
+                               const int* grid, const int* kernel,
+                               int n_heads, int head_dim, float softmax_scale);
+
 /* Thread-local text of the last error of this thread (never NULL). */
 const char* dit_last_error(void);
 
