@@ -385,3 +385,60 @@ def neighborhood_attention(q, k, v, grid: Sequence[int], kernel: Sequence[int], 
             p = softmax_rows((q[r, sl] @ k[keys, sl].T * scale)[None, :])[0]
             out[r_i, sl] = p @ v[keys, sl]
     return out
+
+
+# --- fp8 (OCP e4m3) GEMM variant -----------------------------------------------------------
+# The pages weigh speed against accuracy ("slight (invisible) loss of accuracy", the cuBLAS
+# reply's follow-up); this variant runs the block's products on 8-bit floats: OCP e4m3 (1 sign,
+# 4 exponent bits with bias 7, 3 mantissa bits; largest finite 448, no infinities), one fp32 scale
+# per row of each operand.  The quantised code is an integer decided by floating point, so the
+# oracle takes that decision in the kernel's precision (float32), as the GPU does.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """Value of e4m3 byte(s): (-1)^s 2^(e-7) (1 + m/8) for e > 0, (-1)^s 2^-6 (m/8) for e = 0;
+    0x7f / 0xff are NaN."""
+    c = np.asarray(code, dtype=np.int64)
+    sgn = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    v = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.power(2.0, e - 7))
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return sgn * v
+
+
+_E4M3_POS = e4m3_decode(np.arange(0x7f))        # the 127 finite non-negative values, ascending
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round float values to the nearest e4m3 value, ties to the even code (even mantissa);
+    |x| must not exceed 448 (the callers scale into range)."""
+    x = np.asarray(x, dtype=F64)
+    a = np.abs(x)
+    if np.any(a > E4M3_MAX):
+        raise ValueError("value beyond the e4m3 range")
+    hi = np.searchsorted(_E4M3_POS, a, side="left")          # first value >= a
+    hi = np.minimum(hi, len(_E4M3_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == _E4M3_POS[hi], hi, code)
+    return (code | np.where(np.signbit(x) & (code != 0), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_fp8_rows(x: np.ndarray):
+    """Per-row e4m3 quantisation: s = max|x_row| / 448 in float32 (1 for an all-zero row), codes of
+    float32(x / s).  Returns (codes [rows, cols] uint8, scales [rows] float32)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x / s[:, None]).astype(np.float32)
+    return e4m3_encode(y), s
+
+
+def linear_fp8(xq, sx, wq, sw) -> np.ndarray:
+    """y = diag(sx) (dec(xq) dec(wq)^T) diag(sw), exact in float64."""
+    return (np.asarray(sx, F64)[:, None] * (e4m3_decode(xq) @ e4m3_decode(wq).T)) * np.asarray(sw, F64)[None, :]
