@@ -413,11 +413,12 @@ _E4M3_POS = e4m3_decode(np.arange(0x7f))        # the 127 finite non-negative va
 
 
 def e4m3_encode(x) -> np.ndarray:
-    """Round float values to the nearest e4m3 value, ties to the even code (even mantissa);
-    |x| must not exceed 448 (the callers scale into range)."""
+    """Round float values to the nearest e4m3 value, ties to the even code (even mantissa), keeping
+    the sign (e4m3 has +0 and -0).  Magnitudes from 448 up to (not including) 464, halfway to the next binade step, round to 448;
+    larger ones have no finite code and are refused (the callers scale into range)."""
     x = np.asarray(x, dtype=F64)
     a = np.abs(x)
-    if np.any(a > E4M3_MAX):
+    if np.any(a >= 464.0):
         raise ValueError("value beyond the e4m3 range")
     hi = np.searchsorted(_E4M3_POS, a, side="left")          # first value >= a
     hi = np.minimum(hi, len(_E4M3_POS) - 1)
@@ -426,7 +427,8 @@ def e4m3_encode(x) -> np.ndarray:
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(pick_hi, hi, lo)
     code = np.where(a == _E4M3_POS[hi], hi, code)
-    return (code | np.where(np.signbit(x) & (code != 0), 0x80, 0)).astype(np.uint8)
+    # the sign survives rounding, so a negative value that rounds to zero is -0 (code 0x80)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 
 
 def quantize_fp8_rows(x: np.ndarray):
