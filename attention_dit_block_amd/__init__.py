@@ -21,7 +21,7 @@ __all__ = [
     "block_workspace_size", "block_forward", "single_block_forward",
     "step_workspace_size", "step_forward", "step_shared_mod_workspace_size", "step_forward_shared_mod",
     "timestep_embedding_workspace_size", "timestep_embedding", "linear",
-    "final_layer_workspace_size", "final_layer", "neighborhood_attention",
+    "final_layer_workspace_size", "final_layer", "neighborhood_attention", "quantize_fp8", "linear_fp8",
     "last_error", "launch_count", "abi_version",
     "timing_begin", "timing_end", "timing_read",
 ]
@@ -86,6 +86,8 @@ _final_wsize = _sig("dit_final_layer_workspace_size", _sz, [_i, _i, _i])
 _final = _sig("dit_final_layer", _i, [_i, _i, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _i, _f, _vp, _i, _vp, _sz])
 _natten = _sig("dit_neighborhood_attention", _i, [_i, _vp, _vp, _l, _vp, _l, _vp, _l, _vp, _l, ctypes.POINTER(_i),
                                                  ctypes.POINTER(_i), _i, _i, _f])
+_quant8 = _sig("dit_quantize_fp8", _i, [_i, _vp, _vp, _l, _i, _i, _vp, _l, _vp])
+_linear8 = _sig("dit_linear_fp8", _i, [_vp, _vp, _l, _vp, _vp, _l, _vp, _i, _i, _i, _vp, _i, _l])
 _last_error = _sig("dit_last_error", ctypes.c_char_p, [])
 _launch_count = _sig("dit_launch_count", ctypes.c_uint64, [])
 _abi = _sig("dit_abi_version", _i, [])
@@ -98,6 +100,7 @@ EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", 
             "dit_step_shared_mod_workspace_size", "dit_step_forward_shared_mod",
             "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_linear",
             "dit_final_layer_workspace_size", "dit_final_layer", "dit_neighborhood_attention",
+            "dit_quantize_fp8", "dit_linear_fp8",
             "dit_last_error", "dit_launch_count",
             "dit_abi_version", "dit_timing_begin", "dit_timing_end", "dit_timing_read"]
 
@@ -491,6 +494,35 @@ def neighborhood_attention(q, k, v, o, grid: Sequence[int], kernel: Sequence[int
     rc = _natten(_dt(q), _stream(stream), _ptr(q, "q"), _ld(q, "q"), _ptr(k, "k"), _ld(k, "k"), _ptr(v, "v"),
                  _ld(v, "v"), _ptr(o, "o"), _ld(o, "o"), g, kk, n_heads, head_dim, softmax_scale)
     _check(rc, "dit_neighborhood_attention")
+
+
+def quantize_fp8(x, q, scales, stream=None) -> None:
+    """Per-row e4m3 quantisation of x [rows, cols] into q (uint8 [rows, cols]) and scales (fp32
+    [rows]); see include/dit.h."""
+    import torch
+    rows, cols = x.shape
+    _rows(x, rows, cols, "x")
+    _rows(q, rows, cols, "q")
+    _need(scales, rows, "scales")
+    rc = _quant8(_dt(x), _stream(stream), _ptr(x, "x"), _ld(x, "x"), rows, cols, _ptr(q, "q", torch.uint8), _ld(q, "q"),
+                 _ptr(scales, "scales", torch.float32))
+    _check(rc, "dit_quantize_fp8")
+
+
+def linear_fp8(xq, sx, wq, sw, y, stream=None) -> None:
+    """y = diag(sx) (xq wq^T) diag(sw) on e4m3 codes (uint8 tensors); see include/dit.h."""
+    import torch
+    m, k = xq.shape
+    n = wq.shape[0]
+    _rows(xq, m, k, "xq")
+    _rows(wq, n, k, "wq")
+    _rows(y, m, n, "y")
+    _need(sx, m, "sx")
+    _need(sw, n, "sw")
+    rc = _linear8(_stream(stream), _ptr(xq, "xq", torch.uint8), _ld(xq, "xq"), _ptr(sx, "sx", torch.float32),
+                  _ptr(wq, "wq", torch.uint8), _ld(wq, "wq"), _ptr(sw, "sw", torch.float32), m, n, k, _ptr(y, "y"),
+                  _dt(y), _ld(y, "y"))
+    _check(rc, "dit_linear_fp8")
 
 
 # --- kernel timing -----------------------------------------------------------------------------

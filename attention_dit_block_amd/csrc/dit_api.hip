@@ -951,3 +951,59 @@ int dit_neighborhood_attention(int dtype, void* stream, const void* q, long ld_q
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     return launch("window_attention", s, [&] { return launch_window_attention(a, s); });
 }
+
+// =========================================================================================
+// fp8 (OCP e4m3) quantisation and linear layer.
+// =========================================================================================
+int dit_quantize_fp8(int x_dtype, void* stream, const void* x, long ld_x, int rows, int cols, void* q, long ld_q,
+                     float* scales) {
+    clear_err();
+    if (!valid_dtype(x_dtype)) return fail(DIT_ERR_INVALID_ARG, "x_dtype must be DIT_F32, DIT_BF16 or DIT_F16");
+    if (rows < 0 || cols < 8 || cols % 8) return fail(DIT_ERR_INVALID_ARG, "rows = %d, cols = %d: cols a multiple of 8", rows, cols);
+    if (rows == 0) return DIT_OK;
+    DIT_TRY(check_ptr(x, "x"));
+    DIT_TRY(check_ptr(q, "q"));
+    DIT_TRY(check_ptr(scales, "scales"));
+    DIT_TRY(check_ld(ld_x, cols, x_dtype, "ld_x"));
+    if (ld_q < cols || ld_q % 16) return fail(DIT_ERR_INVALID_ARG, "ld_q = %ld must be >= cols and a multiple of 16", ld_q);
+    const Range rq{reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(q) + (uintptr_t)((rows - 1) * ld_q + cols)};
+    const Range rs = range_of(scales, 1, rows, rows, DIT_F32);
+    if (overlap(rq, range_of(x, rows, ld_x, cols, x_dtype)) || overlap(rs, range_of(x, rows, ld_x, cols, x_dtype)) ||
+        overlap(rq, rs))
+        return fail(DIT_ERR_INVALID_ARG, "q, scales and x overlap");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("quantize_fp8", s, [&] {
+        return launch_quantize_fp8(x, x_dtype, ld_x, rows, cols, reinterpret_cast<uint8_t*>(q), ld_q, scales, s);
+    });
+}
+
+int dit_linear_fp8(void* stream, const void* xq, long ld_x, const float* sx, const void* wq, long ld_w,
+                   const float* sw, int m, int n, int k, void* y, int y_dtype, long ld_y) {
+    clear_err();
+    if (!valid_dtype(y_dtype)) return fail(DIT_ERR_INVALID_ARG, "y_dtype must be DIT_F32, DIT_BF16 or DIT_F16");
+    if (m < 0 || n < 8 || n % 8) return fail(DIT_ERR_INVALID_ARG, "m = %d, n = %d: need m >= 0, n a multiple of 8", m, n);
+    if (k < 128 || k % 128) return fail(DIT_ERR_UNSUPPORTED, "k = %d must be a positive multiple of 128", k);
+    if ((long)m * n > (1L << 31) || (long)n * k > (1L << 31)) return fail(DIT_ERR_UNSUPPORTED, "matrix too large");
+    DIT_TRY(check_ptr(wq, "wq"));
+    DIT_TRY(check_ptr(sw, "sw"));
+    if (ld_w < k || ld_w % 16) return fail(DIT_ERR_INVALID_ARG, "ld_w = %ld must be >= k and a multiple of 16", ld_w);
+    if (m == 0) return DIT_OK;
+    DIT_TRY(check_ptr(xq, "xq"));
+    DIT_TRY(check_ptr(sx, "sx"));
+    DIT_TRY(check_ptr(y, "y"));
+    if (ld_x < k || ld_x % 16) return fail(DIT_ERR_INVALID_ARG, "ld_x = %ld must be >= k and a multiple of 16", ld_x);
+    DIT_TRY(check_ld(ld_y, n, y_dtype, "ld_y"));
+    const Range ry = range_of(y, m, ld_y, n, y_dtype);
+    const Range rx{reinterpret_cast<uintptr_t>(xq), reinterpret_cast<uintptr_t>(xq) + (uintptr_t)((m - 1) * ld_x + k)};
+    const Range rw{reinterpret_cast<uintptr_t>(wq), reinterpret_cast<uintptr_t>(wq) + (uintptr_t)((n - 1) * ld_w + k)};
+    if (overlap(ry, rx) || overlap(ry, rw) || overlap(ry, range_of(sx, 1, m, m, DIT_F32)) ||
+        overlap(ry, range_of(sw, 1, n, n, DIT_F32)))
+        return fail(DIT_ERR_INVALID_ARG, "y overlaps an input");
+    Fp8GemmArgs g{};
+    g.a = reinterpret_cast<const uint8_t*>(xq); g.lda = ld_x; g.sa = sx;
+    g.b = reinterpret_cast<const uint8_t*>(wq); g.ldb = ld_w; g.sb = sw;
+    g.c = y; g.ldc = ld_y; g.c_dtype = y_dtype;
+    g.M = m; g.N = n; g.K = k;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("gemm_fp8", s, [&] { return launch_gemm_fp8(g, s); });
+}

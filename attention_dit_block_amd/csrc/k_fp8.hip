@@ -1,0 +1,196 @@
+// fp8 (OCP e4m3) variant of the block's matrix products on gfx950: per-row quantisation and a GEMM
+// on v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 operands, unit block scales), whose dense peak is
+// twice bf16's.  The pages weigh speed against accuracy (a "slight (invisible) loss of accuracy"
+// in the reply that follows the cuBLAS split of the "CUDA codepath !" thread, antirez/iris.c issue
+// #15); this is that trade on MI355X.
+//
+// Quantisation: one wave per row; s = max|x| / 448 and q = e4m3(x / s) with correctly rounded
+// fp32 divisions and the hardware's round-to-nearest-even conversion (v_cvt_pk_fp8_f32); the
+// scaling keeps every value inside e4m3's finite range.
+//
+// GEMM: the bf16 kernel's geometry with bytes for elements -- a 256 x 256 tile, K steps of 128
+// codes (rows of 128 B, the same XOR swizzle), both operands global -> LDS with
+// global_load_lds_dwordx4 into two stages, 8 waves of 128 x 64.  A 32x32x64 MFMA takes 32 codes
+// of one row per lane: lanes 0-31 codes 0-31 of the 64-code k-slice, lanes 32-63 codes 32-63, the
+// same split on both operands.  Epilogue: acc * sa[m] * sb[n], four consecutive columns per lane.
+#include "dev_common.h"
+#include "launch.h"
+
+namespace dit {
+
+constexpr float kE4M3Max = 448.0f;
+
+template <int XT>
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const void* x, long ld_x, int rows, int cols, uint8_t* q,
+                                                           long ld_q, float* scales) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + wave;
+    if (r >= rows) return;
+    constexpr int XS = XT == F32 ? 4 : 2;
+    const char* xr = reinterpret_cast<const char*>(x) + (size_t)r * ld_x * XS;
+    float f[8];
+    float amax = 0.0f;
+    for (int k0 = lane * 8; k0 < cols; k0 += 512) {
+        load8<XT>(xr + (size_t)k0 * XS, f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    const float s = amax > 0.0f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
+    if (lane == 0) scales[r] = s;
+    uint8_t* qr = q + (size_t)r * ld_q;
+    for (int k0 = lane * 8; k0 < cols; k0 += 512) {
+        load8<XT>(xr + (size_t)k0 * XS, f);
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = __fdiv_rn(f[j], s);
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+        const u32x2_v w = {(uint32_t)w0, (uint32_t)w1};
+        *reinterpret_cast<u32x2_v*>(qr + k0) = w;
+    }
+}
+
+hipError_t launch_quantize_fp8(const void* x, int x_dtype, long ld_x, int rows, int cols, uint8_t* q, long ld_q,
+                               float* scales, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    const dim3 grid((rows + 3) / 4), block(256);
+    if (x_dtype == F32) hipLaunchKernelGGL((quantize_fp8_kernel<F32>), grid, block, 0, s, x, ld_x, rows, cols, q, ld_q, scales);
+    else if (x_dtype == F16) hipLaunchKernelGGL((quantize_fp8_kernel<F16>), grid, block, 0, s, x, ld_x, rows, cols, q, ld_q, scales);
+    else hipLaunchKernelGGL((quantize_fp8_kernel<BF16>), grid, block, 0, s, x, ld_x, rows, cols, q, ld_q, scales);
+    return hipGetLastError();
+}
+
+// ---- GEMM ----------------------------------------------------------------------------------
+typedef int i32x8_v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int QBM = 256, QBN = 256, QBK = 128;          // codes (= bytes) per k-step
+constexpr int kQStage = (QBM + QBN) * QBK;              // 64 KB: A then B
+constexpr int kQLds = 2 * kQStage;
+
+__device__ __forceinline__ int qswz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ f32x16_v mfma_f8(const i32x8_v& a, const i32x8_v& b, const f32x16_v& c) {
+    // e4m3 operands (format 0), block scales 2^(127 - 127) = 1
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <int OT>
+__global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmArgs g) {
+    constexpr int NW = 8, WN = 4, NB = 2, LPW = 32 / NW;   // waves, along N, 32-col blocks, loads
+    __shared__ __attribute__((aligned(1024))) char smem[kQLds];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    // tile: XCD-contiguous, groups of 8 M-tiles walked N-major
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_group = 8 * g.tiles_n;
+    const int grp = L / per_group, first_m = grp * 8;
+    const int gsize = min(g.tiles_m - first_m, 8);
+    const int rr = L - grp * per_group;
+    const int tm = first_m + rr % gsize, tn = rr / gsize;
+    const int m0 = tm * QBM, n0 = tn * QBN;
+
+    // load plan: wave w, instruction i covers tile rows (w*LPW+i)*8 .. +7; lane l writes LDS bytes
+    // l*16 .. +15 of the 1 KB block = row l/8, position l%8, holding chunk (l%8) ^ swz(row)
+    const uint8_t* gA[LPW];
+    const uint8_t* gB[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int row = (wave * LPW + i) * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ qswz(row);
+        gA[i] = g.a + (size_t)min(m0 + row, g.M - 1) * g.lda + chunk * 16;
+        gB[i] = g.b + (size_t)min(n0 + row, g.N - 1) * g.ldb + chunk * 16;
+    }
+    auto issue = [&](int buf, int k0) {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            __builtin_amdgcn_global_load_lds(gA[i] + k0, (lds_void*)(smem + buf * kQStage + (wave * LPW + i) * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gB[i] + k0, (lds_void*)(smem + buf * kQStage + QBM * QBK + (wave * LPW + i) * 1024),
+                                             16, 0, 0);
+        }
+    };
+    const int h = lane >> 5;
+    int a_row[4], b_row[NB];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a_row[j] = wm * 128 + j * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) b_row[j] = wn * 64 + j * 32 + (lane & 31);
+    // fragment of sub-step s (codes 64 s .. 64 s + 63 of the k-step): chunks 4 s + 2 h, + 1
+    auto frag = [&](const char* base, int row, int s) -> i32x8_v {
+        const int c = 4 * s + 2 * h;
+        const u32x4_v lo = *reinterpret_cast<const u32x4_v*>(base + row * 128 + ((c ^ qswz(row)) << 4));
+        const u32x4_v hi = *reinterpret_cast<const u32x4_v*>(base + row * 128 + (((c + 1) ^ qswz(row)) << 4));
+        return i32x8_v{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+
+    f32x16_v acc[NB][4];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    const int nk = g.K / QBK;
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int it = 0; it < nk; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < nk) issue(buf ^ 1, (it + 1) * QBK);
+        const char* la = smem + buf * kQStage;
+        const char* lb = la + QBM * QBK;
+#pragma unroll
+        for (int s = 0; s < QBK / 64; ++s) {
+            i32x8_v fa[4], fb[NB];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fa[j] = frag(la, a_row[j], s);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) fb[j] = frag(lb, b_row[j], s);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma_f8(fb[nb], fa[mb], acc[nb][mb]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // epilogue: acc[nb][mb][q] -> row m0 + wm*128 + mb*32 + (lane & 31), column
+    // n0 + wn*64 + nb*32 + 8 (q >> 2) + 4 h + (q & 3)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
+        if (m >= g.M) continue;
+        const float sa = g.sa[m];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int col = n0 + wn * 64 + nb * 32 + 8 * i + 4 * h;
+                if (col >= g.N) continue;
+                const f32x4_v sb = ldf4(g.sb + col);
+                float o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = acc[nb][mb][4 * i + j] * sa * sb[j];
+                store4<OT>(reinterpret_cast<char*>(g.c) + ((size_t)m * g.ldc + col) * (OT == F32 ? 4 : 2), o);
+            }
+    }
+}
+
+hipError_t launch_gemm_fp8(Fp8GemmArgs& g, hipStream_t s) {
+    if (g.M == 0) return hipSuccess;
+    g.tiles_m = (g.M + QBM - 1) / QBM;
+    g.tiles_n = (g.N + QBN - 1) / QBN;
+    const dim3 grid(g.tiles_m * g.tiles_n), block(512);
+    if (g.c_dtype == F32) hipLaunchKernelGGL((gemm_fp8_kernel<F32>), grid, block, 0, s, g);
+    else if (g.c_dtype == F16) hipLaunchKernelGGL((gemm_fp8_kernel<F16>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((gemm_fp8_kernel<BF16>), grid, block, 0, s, g);
+    return hipGetLastError();
+}
+
+}  // namespace dit

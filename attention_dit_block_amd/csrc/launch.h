@@ -134,6 +134,20 @@ hipError_t launch_window_attention(WinAttnArgs& a, hipStream_t s);
 constexpr int kWinMaxKW = 49;
 constexpr int kWinMaxKeysF32 = 4096;
 
+// ---- fp8 (OCP e4m3) quantisation and GEMM ---------------------------------------------------
+// q [rows, cols] e4m3 codes, scales [rows] fp32: s = max|x_row| / 448 (1 for a zero row),
+// q = e4m3(x / s) rounded to nearest even.  x: F32, BF16 or F16; cols % 8 == 0.
+hipError_t launch_quantize_fp8(const void* x, int x_dtype, long ld_x, int rows, int cols, uint8_t* q, long ld_q,
+                               float* scales, hipStream_t s);
+struct Fp8GemmArgs {
+    const uint8_t* a; long lda; const float* sa;   // [M, K] codes, [M] scales
+    const uint8_t* b; long ldb; const float* sb;   // [N, K] codes, [N] scales
+    void* c; long ldc; int c_dtype;                // [M, N] = sa[m] sb[n] sum_k a b
+    int M, N, K;                                   // K % 128 == 0, N % 4 == 0
+    int tiles_m, tiles_n;                          // filled by the launcher
+};
+hipError_t launch_gemm_fp8(Fp8GemmArgs& g, hipStream_t s);
+
 // ---- layers either side of the block stack ---------------------------------------------
 // emb [dim] fp32 = [cos(s f_j), sin(s f_j)], s = time_factor * t[0], f_j = max_period^(-j / (dim/2))
 hipError_t launch_freq_embed(const float* t, double time_factor, double max_period, int dim, float* emb,

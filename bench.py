@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="skip timing the step replayed from a captured graph")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--fp8-gemm", action="store_true",
+                   help="time the fp8 (e4m3) GEMM on the block's four products at the workload's token count "
+                        "(one JSON line of its own)")
     p.add_argument("--shared-mod", action="store_true",
                    help="multi-block workloads: one AdaLN weight set per block kind, computed once per step")
     p.add_argument("--act", default="f16", choices=["f16", "bf16"],
@@ -107,6 +110,8 @@ def main():
 
     cfg = di.config_by_name(args.workload)
     dev = torch.device("cuda:0")
+    if args.fp8_gemm:
+        return fp8_gemm_bench(args, cfg, dit, torch)
     t = cfg.dtype
     if args.copy_calibration:
         n = args.copy_calibration // 4
@@ -297,6 +302,54 @@ def measured_traffic(workload, kernel, act):
     with open(path, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     return e["bytes"] if sha.startswith(e["sha256"]) else None
+
+
+def fp8_gemm_bench(args, cfg, dit, torch):
+    """The block's four products (QKV, out-proj, FFN-in, FFN-down over all n_txt + n_img tokens) as
+    fp8 e4m3 GEMMs on quantised seeded inputs, timed with HIP events on the launch stream; the
+    bf16 kernel on the same shapes beside it.  The activation quantisation is timed separately."""
+    import dit_inputs as di
+    n, d, F = cfg.n_tok, cfg.d, cfg.ffn_inner
+    shapes = {"qkv": (3 * d, d), "out_proj": (d, d), "ffn_in": (2 * F, d), "ffn_down": (d, F)}
+    s = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(args.steps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+    per, tot8, tot16, totq, flops = {}, 0.0, 0.0, 0.0, 0.0
+    for name, (nout, k) in shapes.items():
+        x = torch.from_numpy(di.draw((n, k), 1.0, "bf16", args.seed, "x").view("int16")).view(torch.bfloat16).to("cuda")
+        w = torch.from_numpy(di.draw((nout, k), 0.02, "bf16", args.seed, "w_1").view("int16")).view(torch.bfloat16).to("cuda")
+        xq = torch.empty(n, k, dtype=torch.uint8, device="cuda")
+        sx = torch.empty(n, dtype=torch.float32, device="cuda")
+        wq = torch.empty(nout, k, dtype=torch.uint8, device="cuda")
+        sw = torch.empty(nout, dtype=torch.float32, device="cuda")
+        y = torch.empty(n, nout, dtype=torch.bfloat16, device="cuda")
+        dit.quantize_fp8(w, wq, sw)
+        tq = timed(lambda: dit.quantize_fp8(x, xq, sx))
+        t8 = timed(lambda: dit.linear_fp8(xq, sx, wq, sw, y))
+        t16 = timed(lambda: dit.linear(x, w, y))
+        f = 2.0 * n * nout * k
+        per[name] = {"fp8_us": round(t8 * 1e3, 1), "fp8_tflops": round(f / t8 / 1e9, 1),
+                     "quantize_x_us": round(tq * 1e3, 1), "bf16_us": round(t16 * 1e3, 1),
+                     "bf16_tflops": round(f / t16 / 1e9, 1)}
+        tot8, tot16, totq, flops = tot8 + t8, tot16 + t16, totq + tq, flops + f
+    out = {"metric": "fp8 (e4m3) GEMM TFLOP/s on the block's four products", "value": round(flops / tot8 / 1e9, 1),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(tot8, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp8_e4m3", "data": "synthetic",
+           "config": {"workload": cfg.name + "_gemms", "tokens": n, "d": d, "ffn_inner": F},
+           "frac_fp8_peak": round(flops / tot8 / 1e9 / 5000.0, 4),
+           "ms_quantize_activations": round(totq, 4), "ms_bf16_same_products": round(tot16, 4),
+           "products": per}
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(cfg, inp):

@@ -379,6 +379,30 @@ int dit_neighborhood_attention(int dtype, void* stream,
                                const int* grid, const int* kernel,
                                int n_heads, int head_dim, float softmax_scale);
 
+/*
+ * fp8 (OCP e4m3) variant of the matrix products: 8-bit floats with 1 sign, 4
+ * exponent (bias 7) and 3 mantissa bits, largest finite 448, one fp32 scale
+ * per row of each operand -- the speed-for-accuracy trade the thread weighs
+ * ("slight (invisible) loss of accuracy"), on MI355X's fp8 MFMA (twice the
+ * dense bf16 peak).
+ *
+ * dit_quantize_fp8: per row r of x [rows, cols] (x_dtype DIT_F32, DIT_BF16 or
+ *   DIT_F16, row stride ld_x): scales[r] = max_j |x[r, j]| / 448 (1 for an
+ *   all-zero row) and q[r, j] = e4m3(x[r, j] / scales[r]), rounded to
+ *   nearest even; both divisions correctly rounded in fp32.  q is bytes with
+ *   row stride ld_q (>= cols, multiple of 16); cols a multiple of 8.
+ * dit_linear_fp8: y[i, j] = sx[i] sw[j] sum_k dec(xq[i, k]) dec(wq[j, k]),
+ *   fp32 accumulation, y of y_dtype (DIT_F32, DIT_BF16 or DIT_F16, stride
+ *   ld_y).  xq [m, k], wq [n, k] e4m3 codes with byte strides ld_x, ld_w
+ *   (multiples of 16); sx [m], sw [n] fp32.  k a multiple of 128, n a
+ *   multiple of 8.  One launch each.
+ */
+int dit_quantize_fp8(int x_dtype, void* stream, const void* x, long ld_x, int rows, int cols,
+                     void* q, long ld_q, float* scales);
+int dit_linear_fp8(void* stream, const void* xq, long ld_x, const float* sx,
+                   const void* wq, long ld_w, const float* sw, int m, int n, int k,
+                   void* y, int y_dtype, long ld_y);
+
 /* Thread-local text of the last error of this thread (never NULL). */
 const char* dit_last_error(void);
 

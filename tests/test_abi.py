@@ -32,7 +32,7 @@ def declared_functions():
     with open(os.path.join(ROOT, "include", "dit.h")) as f:
         src = f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dit_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(dit_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_boundary():
