@@ -444,3 +444,25 @@ def quantize_fp8_rows(x: np.ndarray):
 def linear_fp8(xq, sx, wq, sw) -> np.ndarray:
     """y = diag(sx) (dec(xq) dec(wq)^T) diag(sw), exact in float64."""
     return (np.asarray(sx, F64)[:, None] * (e4m3_decode(xq) @ e4m3_decode(wq).T)) * np.asarray(sw, F64)[None, :]
+
+
+# --- 2-D convolution (the diffusion-VAE decoder's layers) ----------------------------------------
+
+def conv2d_nhwc(x: np.ndarray, w: np.ndarray, bias=None) -> np.ndarray:
+    """y[b, h, w, co] = bias[co] + sum_{i, j, ci} x[b, h + i - KH//2, w + j - KW//2, ci] W[co, i, j, ci],
+    x [B, H, W, Cin] (NHWC), W [Cout, KH, KW, Cin], stride 1, zeros outside the image (odd KH, KW
+    keep the output the input's size)."""
+    x = np.asarray(x, F64)
+    w = np.asarray(w, F64)
+    B, H, W_, Cin = x.shape
+    Cout, KH, KW, _ = w.shape
+    ph, pw = KH // 2, KW // 2
+    xp = np.zeros((B, H + 2 * ph, W_ + 2 * pw, Cin), F64)
+    xp[:, ph:ph + H, pw:pw + W_, :] = x
+    y = np.zeros((B, H, W_, Cout), F64)
+    for i in range(KH):
+        for j in range(KW):
+            y += xp[:, i:i + H, j:j + W_, :] @ w[:, i, j, :].T
+    if bias is not None:
+        y += np.asarray(bias, F64)
+    return y
