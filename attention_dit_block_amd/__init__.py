@@ -22,6 +22,7 @@ __all__ = [
     "step_workspace_size", "step_forward", "step_shared_mod_workspace_size", "step_forward_shared_mod",
     "timestep_embedding_workspace_size", "timestep_embedding", "linear",
     "final_layer_workspace_size", "final_layer", "neighborhood_attention", "quantize_fp8", "linear_fp8",
+    "conv2d",
     "last_error", "launch_count", "abi_version",
     "timing_begin", "timing_end", "timing_read",
 ]
@@ -88,6 +89,7 @@ _natten = _sig("dit_neighborhood_attention", _i, [_i, _vp, _vp, _l, _vp, _l, _vp
                                                  ctypes.POINTER(_i), _i, _i, _f])
 _quant8 = _sig("dit_quantize_fp8", _i, [_i, _vp, _vp, _l, _i, _i, _vp, _l, _vp])
 _linear8 = _sig("dit_linear_fp8", _i, [_vp, _vp, _l, _vp, _vp, _l, _vp, _i, _i, _i, _vp, _i, _l])
+_conv = _sig("dit_conv2d", _i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp, _i])
 _last_error = _sig("dit_last_error", ctypes.c_char_p, [])
 _launch_count = _sig("dit_launch_count", ctypes.c_uint64, [])
 _abi = _sig("dit_abi_version", _i, [])
@@ -100,7 +102,7 @@ EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", 
             "dit_step_shared_mod_workspace_size", "dit_step_forward_shared_mod",
             "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_linear",
             "dit_final_layer_workspace_size", "dit_final_layer", "dit_neighborhood_attention",
-            "dit_quantize_fp8", "dit_linear_fp8",
+            "dit_quantize_fp8", "dit_linear_fp8", "dit_conv2d",
             "dit_last_error", "dit_launch_count",
             "dit_abi_version", "dit_timing_begin", "dit_timing_end", "dit_timing_read"]
 
@@ -523,6 +525,24 @@ def linear_fp8(xq, sx, wq, sw, y, stream=None) -> None:
                   _ptr(wq, "wq", torch.uint8), _ld(wq, "wq"), _ptr(sw, "sw", torch.float32), m, n, k, _ptr(y, "y"),
                   _dt(y), _ld(y, "y"))
     _check(rc, "dit_linear_fp8")
+
+
+def conv2d(x, weight, y, bias=None, stream=None) -> None:
+    """NHWC 2-D convolution, stride 1, zero border: x [B, H, W, Cin], weight [Cout, KH, KW, Cin],
+    y [B, H, W, Cout] (see include/dit.h)."""
+    import torch
+    B, H, W, cin = x.shape
+    cout, kh, kw, cin2 = weight.shape
+    if cin2 != cin or tuple(y.shape) != (B, H, W, cout):
+        raise ValueError("shape mismatch between x, weight and y")
+    for t, what in ((x, "x"), (weight, "weight"), (y, "y")):
+        if not t.is_contiguous():
+            raise ValueError(f"{what} must be contiguous")
+    if bias is not None:
+        _need(bias, cout, "bias")
+    rc = _conv(_dt(x), _stream(stream), _ptr(x, "x"), B, H, W, cin, _ptr(weight, "weight"), cout, kh, kw,
+               _ptr(bias, "bias", torch.float32), _ptr(y, "y"), _dt(y))
+    _check(rc, "dit_conv2d")
 
 
 # --- kernel timing -----------------------------------------------------------------------------

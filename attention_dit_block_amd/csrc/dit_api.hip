@@ -1007,3 +1007,36 @@ int dit_linear_fp8(void* stream, const void* xq, long ld_x, const float* sx, con
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     return launch("gemm_fp8", s, [&] { return launch_gemm_fp8(g, s); });
 }
+
+// =========================================================================================
+// 2-D convolution (NHWC), implicit GEMM.
+// =========================================================================================
+int dit_conv2d(int dtype, void* stream, const void* x, int batch, int height, int width, int c_in, const void* weight,
+               int c_out, int kh, int kw, const float* bias, void* y, int y_dtype) {
+    clear_err();
+    if (dtype != DIT_BF16) return fail(DIT_ERR_UNSUPPORTED, "dtype must be DIT_BF16 (x and weight)");
+    if (y_dtype != DIT_BF16 && y_dtype != DIT_F32) return fail(DIT_ERR_INVALID_ARG, "y_dtype must be DIT_BF16 or DIT_F32");
+    if (batch < 0 || height < 1 || width < 1) return fail(DIT_ERR_INVALID_ARG, "batch = %d, %d x %d", batch, height, width);
+    if (c_in < 64 || c_in % 64) return fail(DIT_ERR_UNSUPPORTED, "c_in = %d must be a positive multiple of 64", c_in);
+    if (c_out < 8 || c_out % 8) return fail(DIT_ERR_UNSUPPORTED, "c_out = %d must be a positive multiple of 8", c_out);
+    if (kh < 1 || kw < 1 || kh % 2 == 0 || kw % 2 == 0 || kh > 7 || kw > 7)
+        return fail(DIT_ERR_UNSUPPORTED, "kernel %d x %d: odd sizes up to 7", kh, kw);
+    const long M = (long)batch * height * width;
+    if (M * c_in > (1L << 31) || M * c_out > (1L << 31) || (long)c_out * kh * kw * c_in > (1L << 31))
+        return fail(DIT_ERR_UNSUPPORTED, "tensor too large");
+    DIT_TRY(check_ptr(weight, "weight"));
+    if (bias) DIT_TRY(check_ptr(bias, "bias"));
+    if (M == 0) return DIT_OK;
+    DIT_TRY(check_ptr(x, "x"));
+    DIT_TRY(check_ptr(y, "y"));
+    const Range ry = range_of(y, M, c_out, c_out, y_dtype);
+    if (overlap(ry, range_of(x, M, c_in, c_in, dtype)) ||
+        overlap(ry, range_of(weight, c_out, (long)kh * kw * c_in, (long)kh * kw * c_in, dtype)) ||
+        (bias && overlap(ry, range_of(bias, 1, c_out, c_out, DIT_F32))))
+        return fail(DIT_ERR_INVALID_ARG, "y overlaps an input");
+    ConvArgs a{};
+    a.x = x; a.w = weight; a.bias = bias; a.y = y; a.y_dtype = y_dtype;
+    a.B = batch; a.H = height; a.W = width; a.Cin = c_in; a.Cout = c_out; a.KH = kh; a.KW = kw;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("conv2d", s, [&] { return launch_conv2d(a, s); });
+}

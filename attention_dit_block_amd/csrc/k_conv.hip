@@ -1,0 +1,168 @@
+// 2-D convolution of the diffusion-VAE decoder (the second stage of the pipeline; the decoder page
+// measures its convolutions at length) on gfx950 as an implicit GEMM: no column buffer is
+// materialised -- the page's point against im2col -- each k-step stages 64 input channels of one
+// kernel tap for 256 output pixels straight from the NHWC input.
+//
+//   y[b, h, w, co] = bias[co] + sum_{i, j, ci} x[b, h + i - KH/2, w + j - KW/2, ci] W[co, i, j, ci]
+//
+// with zeros outside the image (stride 1, "same" padding).  GEMM view: M = B*H*W output pixels,
+// N = Cout, K = KH*KW*Cin in tap-major order, W read as a [Cout, K] row-major matrix.  The bf16
+// GEMM's geometry: 256 x 256 tiles, 64-channel k-steps (rows of 128 B, XOR-swizzled chunks), both
+// operands global -> LDS with global_load_lds_dwordx4 into two stages, 8 waves of 128 x 64 on
+// v_mfma_f32_32x32x16_bf16.  A row whose tap falls outside the image writes zeros to its LDS bytes
+// (ds_write) instead of loading them.
+#include "dev_common.h"
+#include "launch.h"
+
+namespace dit {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int CBM = 256, CBN = 256, CBK = 64;
+constexpr int kCStage = (CBM + CBN) * CBK * 2;      // 64 KB: A then B
+constexpr int kCLds = 2 * kCStage;
+
+__device__ __forceinline__ int cswz(int row) { return (row >> 1) & 7; }
+
+template <int DT>
+__device__ __forceinline__ f32x16_v cmfma(const u32x4_v& a, const u32x4_v& b, const f32x16_v& c) {
+    if constexpr (DT == F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_v, a), __builtin_bit_cast(f16x8_v, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_v, a), __builtin_bit_cast(bf16x8_v, b), c, 0, 0, 0);
+}
+
+template <int DT, int OT>
+__global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
+    constexpr int NW = 8, WN = 4, NB = 2, LPW = 32 / NW;
+    __shared__ __attribute__((aligned(1024))) char smem[kCLds];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_group = 8 * a.tiles_n;
+    const int grp = L / per_group, first_m = grp * 8;
+    const int gsize = min(a.tiles_m - first_m, 8);
+    const int rr = L - grp * per_group;
+    const int tm = first_m + rr % gsize, tn = rr / gsize;
+    const int M = a.B * a.H * a.W;
+    const int m0 = tm * CBM, n0 = tn * CBN;
+    const int K = a.KH * a.KW * a.Cin;
+    const int ncb = a.Cin / CBK;                 // channel blocks per tap
+    const int nk = a.KH * a.KW * ncb;
+    const int ph = a.KH / 2, pw = a.KW / 2;
+
+    // load plan: instruction i of wave w covers tile rows (w*LPW+i)*8 .. +7; lane l writes LDS
+    // bytes l*16 .. +15 of the 1 KB block = row l/8, position l%8, holding chunk (l%8) ^ swz(row)
+    int pix[LPW], ph_[LPW], pw_[LPW];
+    const bf16_t* gB[LPW];
+    int chunk[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int row = (wave * LPW + i) * 8 + (lane >> 3);
+        chunk[i] = (lane & 7) ^ cswz(row);
+        const int p = min(m0 + row, M - 1);
+        pix[i] = p;
+        pw_[i] = p % a.W;
+        ph_[i] = (p / a.W) % a.H;
+        gB[i] = reinterpret_cast<const bf16_t*>(a.w) + (size_t)min(n0 + row, a.Cout - 1) * K + chunk[i] * 8;
+    }
+    const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
+    auto issue = [&](int buf, int kk) {
+        const int tap = kk / ncb, cb = kk - tap * ncb;
+        const int ti = tap / a.KW, tj = tap - ti * a.KW;
+        const int dh = ti - ph, dw = tj - pw;
+        char* sa = smem + buf * kCStage;
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            char* dst = sa + (wave * LPW + i) * 1024;
+            const int ih = ph_[i] + dh, iw = pw_[i] + dw;
+            if ((unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W) {
+                const bf16_t* src = X + ((long)pix[i] + (long)dh * a.W + dw) * a.Cin + cb * CBK + chunk[i] * 8;
+                __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+            } else {
+                *reinterpret_cast<u32x4_v*>(dst + lane * 16) = u32x4_v{0u, 0u, 0u, 0u};
+            }
+            __builtin_amdgcn_global_load_lds(gB[i] + (size_t)kk * CBK, (lds_void*)(sa + CBM * CBK * 2 + (wave * LPW + i) * 1024),
+                                             16, 0, 0);
+        }
+    };
+    const int h = lane >> 5;
+    int a_row[4], b_row[NB];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a_row[j] = wm * 128 + j * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) b_row[j] = wn * 64 + j * 32 + (lane & 31);
+    auto frag = [&](const char* base, int row, int s) -> u32x4_v {
+        const int c = 2 * s + h;
+        return *reinterpret_cast<const u32x4_v*>(base + row * 128 + ((c ^ cswz(row)) << 4));
+    };
+
+    f32x16_v acc[NB][4];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int it = 0; it < nk; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < nk) issue(buf ^ 1, it + 1);
+        const char* la = smem + buf * kCStage;
+        const char* lb = la + CBM * CBK * 2;
+#pragma unroll
+        for (int s = 0; s < CBK / 16; ++s) {
+            u32x4_v fa[4], fb[NB];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fa[j] = frag(la, a_row[j], s);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) fb[j] = frag(lb, b_row[j], s);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = cmfma<DT>(fb[nb], fa[mb], acc[nb][mb]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // epilogue: acc[nb][mb][q] -> pixel m0 + wm*128 + mb*32 + (lane & 31), channel
+    // n0 + wn*64 + nb*32 + 8 (q >> 2) + 4 h + (q & 3)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
+        if (m >= M) continue;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int col = n0 + wn * 64 + nb * 32 + 8 * i + 4 * h;
+                if (col >= a.Cout) continue;
+                float o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = acc[nb][mb][4 * i + j];
+                if (a.bias) {
+                    const f32x4_v bv = ldf4(a.bias + col);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] += bv[j];
+                }
+                store4<OT>(reinterpret_cast<char*>(a.y) + ((size_t)m * a.Cout + col) * (OT == F32 ? 4 : 2), o);
+            }
+    }
+}
+
+hipError_t launch_conv2d(ConvArgs& a, hipStream_t s) {
+    const long M = (long)a.B * a.H * a.W;
+    if (M == 0) return hipSuccess;
+    a.tiles_m = (int)((M + CBM - 1) / CBM);
+    a.tiles_n = (a.Cout + CBN - 1) / CBN;
+    const dim3 grid(a.tiles_m * a.tiles_n), block(512);
+    if (a.y_dtype == F32) hipLaunchKernelGGL((conv2d_kernel<BF16, F32>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((conv2d_kernel<BF16, BF16>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace dit

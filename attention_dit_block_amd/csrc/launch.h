@@ -148,6 +148,17 @@ struct Fp8GemmArgs {
 };
 hipError_t launch_gemm_fp8(Fp8GemmArgs& g, hipStream_t s);
 
+// ---- 2-D convolution (NHWC), implicit GEMM ----------------------------------------------------
+struct ConvArgs {
+    const void* x;          // [B, H, W, Cin], x_dtype BF16 or F16
+    const void* w;          // [Cout, KH, KW, Cin], BF16 (F16 x: converted while staging -- not used)
+    const float* bias;      // [Cout] or null
+    void* y; int y_dtype;   // [B, H, W, Cout]
+    int B, H, W, Cin, Cout, KH, KW;     // stride 1, zero padding (K - 1) / 2
+    int tiles_m, tiles_n;   // filled by the launcher
+};
+hipError_t launch_conv2d(ConvArgs& a, hipStream_t s);
+
 // ---- layers either side of the block stack ---------------------------------------------
 // emb [dim] fp32 = [cos(s f_j), sin(s f_j)], s = time_factor * t[0], f_j = max_period^(-j / (dim/2))
 hipError_t launch_freq_embed(const float* t, double time_factor, double max_period, int dim, float* emb,

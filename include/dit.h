@@ -403,6 +403,25 @@ int dit_linear_fp8(void* stream, const void* xq, long ld_x, const float* sx,
                    const void* wq, long ld_w, const float* sw, int m, int n, int k,
                    void* y, int y_dtype, long ld_y);
 
+/*
+ * 2-D convolution of the diffusion-VAE decoder (the pipeline's second stage,
+ * whose convolutions the decoder page measures), as an implicit GEMM on MFMA:
+ * no column buffer is built.
+ *   y[b, h, w, co] = bias[co] + sum_{i, j, ci} x[b, h + i - kh/2, w + j - kw/2, ci]
+ *                                              * weight[co, i, j, ci]
+ * stride 1, zeros outside the image (the output has the input's size).
+ *  dtype     of x and weight: DIT_BF16 (fp32 accumulation)
+ *  x         [batch, height, width, c_in] (NHWC), contiguous
+ *  weight    [c_out, kh, kw, c_in], contiguous;  bias fp32 [c_out] or NULL
+ *  y         [batch, height, width, c_out] of y_dtype (DIT_BF16 or DIT_F32);
+ *            must not overlap x, weight or bias
+ * Limits: c_in a multiple of 64, c_out a multiple of 8, kh and kw odd <= 7.
+ * One launch.
+ */
+int dit_conv2d(int dtype, void* stream, const void* x, int batch, int height, int width,
+               int c_in, const void* weight, int c_out, int kh, int kw, const float* bias,
+               void* y, int y_dtype);
+
 /* Thread-local text of the last error of this thread (never NULL). */
 const char* dit_last_error(void);
 

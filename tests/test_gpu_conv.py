@@ -1,0 +1,75 @@
+"""NHWC 2-D convolution (implicit GEMM on MFMA) against the oracle's direct definition.  The bound
+per element: the bf16 products are exact in fp32 and a sum of K = kh*kw*Cin of them, in any order,
+is within (K - 1) 2^-24 sum|terms| of the exact value (2^-23 allowing truncating adds); the bias add
+one more rounding; a bf16 output adds half a bf16 ulp."""
+import numpy as np
+import pytest
+import torch
+
+import dit_inputs as di
+from oracle import dit_oracle as o
+from gpu_util import dev, host, metric, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dit():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import attention_dit_block_amd as m
+    return m
+
+
+def run(dit, B, H, W, cin, cout, k, bias, ydt, seed):
+    x = di.draw((B, H, W, cin), 1.0, "bf16", seed, "x")
+    w = di.draw((cout, k, k, cin), 0.05, "bf16", seed, "w_1")
+    b = di.draw((cout,), 1.0, "f32", seed, "cond") if bias else None
+    xt = dev(x, "bf16").view(B, H, W, cin)
+    wt = dev(w, "bf16").view(cout, k, k, cin)
+    bt = dev(b, "f32") if bias else None
+    y = torch.empty(B, H, W, cout, dtype=ydt, device="cuda")
+    before = dit.launch_count()
+    dit.conv2d(xt, wt, y, bias=bt)
+    torch.cuda.synchronize()
+    assert dit.launch_count() == before + 1
+    xf, wf = o.widen(x, "bf16"), o.widen(w, "bf16")
+    ref = o.conv2d_nhwc(xf, wf, b)
+    abs_sum = o.conv2d_nhwc(np.abs(xf), np.abs(wf), None if b is None else np.abs(b))
+    K = k * k * cin
+    bound = (K * 2.0 ** -23 + 2.0 ** -22) * abs_sum + 1e-30
+    if ydt == torch.bfloat16:
+        bound = bound + 0.5 * 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    got = host(y)
+    err = np.abs(got - ref)
+    say(f"  conv {B}x{H}x{W}x{cin} -> {cout}, {k}x{k}, bias {bias}, {ydt}: max err/bound "
+        f"{np.max(err / bound):.3f}, max|gpu-oracle|/RMS {metric(got, ref):.2e}")
+    assert np.all(err <= bound), f"{np.sum(err > bound)} elements beyond the bound"
+    return xf, got
+
+
+def test_vae_like_3x3(dit):
+    # a decoder layer at 832 x 480 / 8 latent resolution, 256 channels (6240 pixels: a ragged tile)
+    run(dit, 1, 60, 104, 256, 256, 3, True, torch.float32, 61)
+
+
+@pytest.mark.parametrize("B, H, W, cin, cout, k, bias, ydt", [
+    (2, 13, 21, 64, 72, 3, True, torch.bfloat16),      # ragged everything, bf16 output
+    (1, 32, 32, 128, 64, 1, False, torch.float32),      # 1x1 (a per-pixel linear layer)
+    (1, 9, 11, 64, 16, 5, True, torch.float32),         # 5x5 with borders wider than the image rows
+    (3, 1, 7, 64, 8, 3, False, torch.bfloat16),         # one-row images
+])
+def test_shapes(dit, B, H, W, cin, cout, k, bias, ydt):
+    run(dit, B, H, W, cin, cout, k, bias, ydt, 62)
+
+
+def test_identity_kernel_copies_input(dit):
+    B, H, W, c = 1, 10, 12, 64
+    x = di.draw((B, H, W, c), 1.0, "bf16", 63, "x")
+    wgt = np.zeros((c, 3, 3, c), np.float32)
+    wgt[:, 1, 1, :] = np.eye(c)
+    xt = dev(x, "bf16").view(B, H, W, c)
+    wt = dev(di.bf16_bits_from_f32(wgt), "bf16").view(c, 3, 3, c)
+    y = torch.empty(B, H, W, c, dtype=torch.bfloat16, device="cuda")
+    dit.conv2d(xt, wt, y)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(y), o.widen(x, "bf16"))
