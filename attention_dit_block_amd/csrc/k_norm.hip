@@ -110,25 +110,48 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
     const char* xrow = reinterpret_cast<const char*>(P.x) + (size_t)r * P.ld_x * ESize<XT>::v;
     char* orow = reinterpret_cast<char*>(P.out) + (size_t)r * P.ld_out * ESize<OT>::v;
 
+    // Up to 8 chunks per lane, the shift / scale slices are loaded together with the row (they
+    // are independent of it), so their L2 latency overlaps the row's HBM latency; wider rows load
+    // them after the reduction to keep the register count down.
+    constexpr bool kEarly = NC <= 8;
     float v[NC][8];
-    float ss = 0.0f;
+    f32x4_v sh[kEarly ? NC : 1][2], sc[kEarly ? NC : 1][2];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int c = (lane + 64 * i) * 8;        // first element of this 8-element chunk
         if (c < d) {
             load8<XT>(xrow + (size_t)c * ESize<XT>::v, v[i]);
+        } else {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) ss = fmaf(v[i][t], v[i][t], ss);
+            for (int t = 0; t < 8; ++t) v[i][t] = 0.0f;
         }
     }
+    if constexpr (kEarly) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int c = min((lane + 64 * i) * 8, d - 8);    // chunks past the row: any valid slice
+            sh[i][0] = ldf4(P.shift + c); sh[i][1] = ldf4(P.shift + c + 4);
+            sc[i][0] = ldf4(P.scale + c); sc[i][1] = ldf4(P.scale + c + 4);
+        }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ss = fmaf(v[i][t], v[i][t], ss);
     ss = wave_sum(ss);
     const float rstd = 1.0f / sqrtf(ss / (float)d + b.eps);
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int c = (lane + 64 * i) * 8;
         if (c < d) {
-            const f32x4_v sh0 = ldf4(P.shift + c), sh1 = ldf4(P.shift + c + 4);
-            const f32x4_v sc0 = ldf4(P.scale + c), sc1 = ldf4(P.scale + c + 4);
+            f32x4_v sh0, sh1, sc0, sc1;
+            if constexpr (kEarly) {
+                sh0 = sh[i][0]; sh1 = sh[i][1]; sc0 = sc[i][0]; sc1 = sc[i][1];
+            } else {
+                sh0 = ldf4(P.shift + c); sh1 = ldf4(P.shift + c + 4);
+                sc0 = ldf4(P.scale + c); sc1 = ldf4(P.scale + c + 4);
+            }
             float o[8];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -145,6 +168,7 @@ static hipError_t launch_mod_nc(const ModBatch& b, hipStream_t s, dim3 grid) {
     const int nc = (b.d + 511) / 512;
     if (nc <= 2) hipLaunchKernelGGL((modulate_kernel<XT, OT, 2>), grid, dim3(256), 0, s, b);
     else if (nc <= 4) hipLaunchKernelGGL((modulate_kernel<XT, OT, 4>), grid, dim3(256), 0, s, b);
+    else if (nc <= 6) hipLaunchKernelGGL((modulate_kernel<XT, OT, 6>), grid, dim3(256), 0, s, b);
     else if (nc <= 8) hipLaunchKernelGGL((modulate_kernel<XT, OT, 8>), grid, dim3(256), 0, s, b);
     else hipLaunchKernelGGL((modulate_kernel<XT, OT, 16>), grid, dim3(256), 0, s, b);
     return hipGetLastError();
