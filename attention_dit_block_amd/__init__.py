@@ -22,7 +22,7 @@ __all__ = [
     "step_workspace_size", "step_forward", "step_shared_mod_workspace_size", "step_forward_shared_mod",
     "timestep_embedding_workspace_size", "timestep_embedding", "linear",
     "final_layer_workspace_size", "final_layer", "neighborhood_attention", "quantize_fp8", "linear_fp8",
-    "conv2d",
+    "StreamWeightsFp8", "block_fp8_workspace_size", "block_forward_fp8", "conv2d",
     "last_error", "launch_count", "abi_version",
     "timing_begin", "timing_end", "timing_read",
 ]
@@ -53,6 +53,11 @@ class StreamWeights(ctypes.Structure):
 
 class SingleWeights(ctypes.Structure):
     _fields_ = [("w_mod", _vp), ("w_1", _vp), ("qk_norm_w", _vp), ("w_2", _vp)]
+
+
+class StreamWeightsFp8(ctypes.Structure):
+    _fields_ = [("w_mod", _vp), ("qk_norm_w", _vp), ("w_qkv", _vp), ("s_qkv", _vp), ("w_o", _vp), ("s_o", _vp),
+                ("w_ffn_in", _vp), ("s_ffn_in", _vp), ("w_ffn_out", _vp), ("s_ffn_out", _vp)]
 
 
 def _sig(name, res, args):
@@ -89,6 +94,10 @@ _natten = _sig("dit_neighborhood_attention", _i, [_i, _vp, _vp, _l, _vp, _l, _vp
                                                  ctypes.POINTER(_i), _i, _i, _f])
 _quant8 = _sig("dit_quantize_fp8", _i, [_i, _vp, _vp, _l, _i, _i, _vp, _l, _vp])
 _linear8 = _sig("dit_linear_fp8", _i, [_vp, _vp, _l, _vp, _vp, _l, _vp, _i, _i, _i, _vp, _i, _l])
+_wsize8 = _sig("dit_block_fp8_workspace_size", _sz, [ctypes.POINTER(BlockConfig)])
+_block8 = _sig("dit_block_forward_fp8", _i, [ctypes.POINTER(BlockConfig), ctypes.POINTER(StreamWeightsFp8),
+                                             ctypes.POINTER(StreamWeightsFp8), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                             _vp])
 _conv = _sig("dit_conv2d", _i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp, _i])
 _last_error = _sig("dit_last_error", ctypes.c_char_p, [])
 _launch_count = _sig("dit_launch_count", ctypes.c_uint64, [])
@@ -102,7 +111,8 @@ EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", 
             "dit_step_shared_mod_workspace_size", "dit_step_forward_shared_mod",
             "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_linear",
             "dit_final_layer_workspace_size", "dit_final_layer", "dit_neighborhood_attention",
-            "dit_quantize_fp8", "dit_linear_fp8", "dit_conv2d",
+            "dit_quantize_fp8", "dit_linear_fp8", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
+            "dit_conv2d",
             "dit_last_error", "dit_launch_count",
             "dit_abi_version", "dit_timing_begin", "dit_timing_end", "dit_timing_read"]
 
@@ -525,6 +535,48 @@ def linear_fp8(xq, sx, wq, sw, y, stream=None) -> None:
                   _ptr(wq, "wq", torch.uint8), _ld(wq, "wq"), _ptr(sw, "sw", torch.float32), m, n, k, _ptr(y, "y"),
                   _dt(y), _ld(y, "y"))
     _check(rc, "dit_linear_fp8")
+
+
+def block_fp8_workspace_size(shape: Shape) -> int:
+    c = shape.c_config()
+    n = _wsize8(ctypes.byref(c))
+    if n == 0:
+        raise DitError(DIT_ERR_INVALID_ARG, "dit_block_fp8_workspace_size")
+    return int(n)
+
+
+def _stream_weights_fp8(shape: "Shape", w: dict, what: str) -> StreamWeightsFp8:
+    """w: w_mod, qk_norm_w (16-bit) and, per product, codes (uint8) and scales (fp32): w_qkv / s_qkv,
+    w_o / s_o, w_ffn_in / s_ffn_in, w_ffn_out / s_ffn_out."""
+    import torch
+    d, F, dc, hd = shape.d, shape.ffn_inner, shape.d_cond or shape.d, shape.head_dim
+    s = StreamWeightsFp8()
+    _need(w.get("w_mod"), 6 * d * dc, f"{what}.w_mod")
+    _need(w.get("qk_norm_w"), 2 * hd, f"{what}.qk_norm_w")
+    s.w_mod = _ptr(w.get("w_mod"), f"{what}.w_mod")
+    s.qk_norm_w = _ptr(w.get("qk_norm_w"), f"{what}.qk_norm_w")
+    for name, rows, k in (("qkv", 3 * d, d), ("o", d, d), ("ffn_in", 2 * F, d), ("ffn_out", d, F)):
+        codes, scales = w.get("w_" + name), w.get("s_" + name)
+        _need(codes, rows * k, f"{what}.w_{name}")
+        _need(scales, rows, f"{what}.s_{name}")
+        setattr(s, "w_" + name, _ptr(codes, f"{what}.w_{name}", torch.uint8))
+        setattr(s, "s_" + name, _ptr(scales, f"{what}.s_{name}", torch.float32))
+    return s
+
+
+def block_forward_fp8(shape: Shape, txt: dict, img: dict, cond, pos, x_txt, x_img, y_txt, y_img, workspace,
+                      stream=None) -> None:
+    """Double-stream block with its four weight products on e4m3 codes (see include/dit.h)."""
+    import torch
+    c = shape.c_config()
+    wt, wi = _stream_weights_fp8(shape, txt, "txt"), _stream_weights_fp8(shape, img, "img")
+    _check_block_io(shape, cond, pos, ((x_txt, shape.n_txt, "x_txt"), (x_img, shape.n_img, "x_img"),
+                                       (y_txt, shape.n_txt, "y_txt"), (y_img, shape.n_img, "y_img")))
+    rc = _block8(ctypes.byref(c), ctypes.byref(wt), ctypes.byref(wi), _ptr(cond, "cond"),
+                 _ptr(pos, "pos", torch.int32), _ptr(x_txt, "x_txt"), _ptr(x_img, "x_img"), _ptr(y_txt, "y_txt"),
+                 _ptr(y_img, "y_img"), _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                 _stream(stream))
+    _check(rc, "dit_block_forward_fp8")
 
 
 def conv2d(x, weight, y, bias=None, stream=None) -> None:

@@ -136,10 +136,10 @@ int validate_config(const dit_block_config* c) {
 
 // Workspace plan: 256-byte aligned sub-buffers.
 struct WsPlan {
-    size_t mod, act, qkv, o, h, f, of, sk, sk_bytes, ask, ask_bytes, total;
+    size_t mod, act, qkv, o, h, f, of, sk, sk_bytes, ask, ask_bytes, q8, sq, total;
 };
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
-WsPlan plan_workspace(const dit_block_config* c, int single) {
+WsPlan plan_workspace(const dit_block_config* c, int single, bool fp8 = false) {
     const size_t n = (size_t)c->n_txt + c->n_img, d = c->d, F = c->ffn_inner, es = esize(c->act_dtype);
     WsPlan p{};
     size_t off = 0;
@@ -163,6 +163,11 @@ WsPlan plan_workspace(const dit_block_config* c, int single) {
     // attention's stream-K scratch (16-bit paths)
     p.ask_bytes = c->dtype == DIT_BF16 ? attention_sk_scratch_bytes() : 0;
     p.ask = take(p.ask_bytes);
+    // fp8 products: the e4m3 codes and per-row scales of the current product's activations
+    if (fp8) {
+        p.q8 = take(n * std::max(d, F));
+        p.sq = take(n * 4);
+    }
     p.total = off;
     return p;
 }
@@ -312,24 +317,56 @@ static int check_stream_weights(const dit_stream_weights* w, const char* s, bool
     return DIT_OK;
 }
 
+static int check_stream_weights_fp8(const dit_stream_weights_fp8* w, const char* s) {
+    if (!w) return fail(DIT_ERR_INVALID_ARG, "%s weights are NULL", s);
+    const void* p[10] = {w->w_mod, w->qk_norm_w, w->w_qkv, w->s_qkv, w->w_o, w->s_o, w->w_ffn_in, w->s_ffn_in,
+                         w->w_ffn_out, w->s_ffn_out};
+    const char* n[10] = {"w_mod", "qk_norm_w", "w_qkv", "s_qkv", "w_o", "s_o", "w_ffn_in", "s_ffn_in", "w_ffn_out",
+                         "s_ffn_out"};
+    for (int i = 0; i < 10; ++i) {
+        if (!p[i]) return fail(DIT_ERR_INVALID_ARG, "%s.%s is NULL", s, n[i]);
+        if (!aligned16(p[i])) return fail(DIT_ERR_INVALID_ARG, "%s.%s is not 16-byte aligned", s, n[i]);
+    }
+    return DIT_OK;
+}
+
+static int validate_fp8_config(const dit_block_config* c) {
+    DIT_TRY(validate_config(c));
+    if (c->dtype != DIT_BF16 || (c->act_dtype != DIT_F16 && c->act_dtype != DIT_BF16))
+        return fail(DIT_ERR_UNSUPPORTED, "the fp8 block needs dtype DIT_BF16 and DIT_F16 or DIT_BF16 activations");
+    return DIT_OK;
+}
+
 // mod_pre: the [2][6d] fp32 AdaLN vectors (text, image) computed by the caller, or NULL (the block
-// computes them from its own w_mod; cond is then required).
+// computes them from its own w_mod; cond is then required).  t8 / i8: fp8 weights (the four
+// products run on e4m3 codes; txt / img are then NULL).
 static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weights* txt,
                               const dit_stream_weights* img, const void* cond, const int32_t* pos, const void* x_txt,
                               const void* x_img, void* y_txt, void* y_img, void* workspace, size_t ws_bytes,
-                              void* stream, const float* mod_pre) {
+                              void* stream, const float* mod_pre, const dit_stream_weights_fp8* t8 = nullptr,
+                              const dit_stream_weights_fp8* i8 = nullptr) {
     clear_err();
-    DIT_TRY(validate_config(cfg));
+    const bool fp8 = t8 != nullptr;
+    DIT_TRY(fp8 ? validate_fp8_config(cfg) : validate_config(cfg));
     const dit_block_config& c = *cfg;
     const int nt = c.n_txt, ni = c.n_img, n = nt + ni, d = c.d, F = c.ffn_inner;
-    DIT_TRY(check_stream_weights(txt, "txt", !mod_pre));
-    DIT_TRY(check_stream_weights(img, "img", !mod_pre));
+    if (fp8) {
+        DIT_TRY(check_stream_weights_fp8(t8, "txt"));
+        DIT_TRY(check_stream_weights_fp8(i8, "img"));
+    } else {
+        DIT_TRY(check_stream_weights(txt, "txt", !mod_pre));
+        DIT_TRY(check_stream_weights(img, "img", !mod_pre));
+    }
+    const void* wmod_t = fp8 ? t8->w_mod : txt->w_mod;
+    const void* wmod_i = fp8 ? i8->w_mod : img->w_mod;
+    const void* qkw_t = fp8 ? t8->qk_norm_w : txt->qk_norm_w;
+    const void* qkw_i = fp8 ? i8->qk_norm_w : img->qk_norm_w;
     if (!mod_pre) DIT_TRY(check_ptr(cond, "cond"));
     DIT_TRY(check_ptr(pos, "pos"));
     if (nt > 0) { DIT_TRY(check_ptr(x_txt, "x_txt")); DIT_TRY(check_ptr(y_txt, "y_txt")); }
     if (ni > 0) { DIT_TRY(check_ptr(x_img, "x_img")); DIT_TRY(check_ptr(y_img, "y_img")); }
     DIT_TRY(check_ptr(workspace, "workspace"));
-    const WsPlan W = plan_workspace(cfg, 0);
+    const WsPlan W = plan_workspace(cfg, 0, fp8);
     if (ws_bytes < W.total)
         return fail(DIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
     // y may alias x (same dtype); otherwise no overlap; nothing may overlap the workspace.
@@ -358,8 +395,8 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     // 1. AdaLN vectors of both streams
     if (!mod_pre) {
         GemvBatch g{};
-        g.p[0] = {txt->w_mod, mod_t, 6 * d};
-        g.p[1] = {img->w_mod, mod_i, 6 * d};
+        g.p[0] = {wmod_t, mod_t, 6 * d};
+        g.p[1] = {wmod_i, mod_i, 6 * d};
         g.n = 2;
         g.cond = cond;
         g.d_cond = c.d_cond;
@@ -375,7 +412,33 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     m.n = nm; m.d = d; m.eps = c.eps; m.out_dtype = c.act_dtype;
     DIT_TRY(launch("modulate_x", s, [&] { return launch_modulate(m, s); }));
 
+    // fp8 products: quantise the activations [n, k] (row stride k) per row, then one grouped e4m3
+    // GEMM over the text rows and the image rows.
+    uint8_t* q8 = fp8 ? reinterpret_cast<uint8_t*>(ws + W.q8) : nullptr;
+    float* sq = fp8 ? reinterpret_cast<float*>(ws + W.sq) : nullptr;
+    auto quantize = [&](const char* name, const void* src, int k) {
+        return launch(name, s, [&] { return launch_quantize_fp8(src, c.act_dtype, k, n, k, q8, k, sq, s); });
+    };
+    // problem of `rows` rows starting at row r0 of the quantised activations (row stride k)
+    auto fp8_problem = [&](int r0, int rows, int k, const void* wq, const float* sw, void* out, long ldc, int c_dtype,
+                           int N, int epi) {
+        Fp8GemmProblem P{};
+        P.a = q8 + (size_t)r0 * k; P.lda = k; P.sa = sq + r0;
+        P.b = reinterpret_cast<const uint8_t*>(wq); P.ldb = k; P.sb = sw;
+        P.c = out; P.ldc = ldc; P.c_dtype = c_dtype;
+        P.M = rows; P.N = N; P.K = k; P.epi = epi;
+        return P;
+    };
+
     // 3. qkv = a W_qkv^T
+    if (fp8) {
+        DIT_TRY(quantize("quantize_a", act, d));
+        Fp8GemmBatch b{};
+        if (nt) b.p[b.n++] = fp8_problem(0, nt, d, t8->w_qkv, t8->s_qkv, qkv, 3L * d, c.act_dtype, 3 * d, EPI_STORE);
+        if (ni) b.p[b.n++] = fp8_problem(nt, ni, d, i8->w_qkv, i8->s_qkv, qkv + (size_t)nt * 3 * d * es, 3L * d,
+                                         c.act_dtype, 3 * d, EPI_STORE);
+        DIT_TRY(launch("gemm_fp8_qkv", s, [&] { return launch_gemm_fp8(b, s); }));
+    } else {
     GemmBatch gq{};
     gq.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     gq.a_dtype = c.act_dtype;
@@ -387,12 +450,13 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
         gq.n = k;
     }
     DIT_TRY(launch("gemm_qkv", s, [&] { return launch_gemm(gq, s); }));
+    }
 
     // 4. QK RMSNorm + RoPE in place (text rows use the text weights)
     QkRopeArgs r{};
     DIT_TRY(build_rope_table(c.head_dim, c.n_axes, c.axes_dim, c.theta, r.tab));
     r.q = qkv; r.ld_q = 3L * d; r.k = qkv + (size_t)d * es; r.ld_k = 3L * d;
-    r.n_tok = n; r.n_heads = c.n_heads; r.qk_w0 = txt->qk_norm_w; r.qk_w1 = img->qk_norm_w; r.n_first = nt;
+    r.n_tok = n; r.n_heads = c.n_heads; r.qk_w0 = qkw_t; r.qk_w1 = qkw_i; r.n_first = nt;
     r.eps = c.eps_qk; r.pos = pos; r.n_axes = c.n_axes; r.dtype = c.act_dtype; r.w_dtype = c.dtype;
     DIT_TRY(launch("qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(r, s); }));
 
@@ -403,6 +467,19 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
 
     // 6. h = x + gate1 * (O W_o^T)   (fp32)
+    if (fp8) {
+        DIT_TRY(quantize("quantize_o", ob, d));
+        Fp8GemmBatch b{};
+        if (nt) {
+            b.p[b.n] = fp8_problem(0, nt, d, t8->w_o, t8->s_o, h, d, DIT_F32, d, EPI_GATED_RES);
+            b.p[b.n].r = x_txt; b.p[b.n].ldr = d; b.p[b.n].r_dtype = c.x_dtype; b.p[b.n++].gate = mod_t + 2 * (size_t)d;
+        }
+        if (ni) {
+            b.p[b.n] = fp8_problem(nt, ni, d, i8->w_o, i8->s_o, h + (size_t)nt * d, d, DIT_F32, d, EPI_GATED_RES);
+            b.p[b.n].r = x_img; b.p[b.n].ldr = d; b.p[b.n].r_dtype = c.x_dtype; b.p[b.n++].gate = mod_i + 2 * (size_t)d;
+        }
+        DIT_TRY(launch("gemm_fp8_out_proj", s, [&] { return launch_gemm_fp8(b, s); }));
+    } else {
     GemmBatch go{};
     go.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     go.a_dtype = c.act_dtype;
@@ -415,6 +492,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
         go.n = k;
     }
     DIT_TRY(launch("gemm_out_proj", s, [&] { return launch_gemm(go, s); }));
+    }
 
     // 7. b = (1 + scale2) RMSNorm(h) + shift2
     ModBatch m2{};
@@ -426,6 +504,20 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     DIT_TRY(launch("modulate_h", s, [&] { return launch_modulate(m2, s); }));
 
     // 8. f = SiLU(b W_gate^T) * (b W_up^T)
+    if (fp8) {
+        DIT_TRY(quantize("quantize_b", act, d));
+        Fp8GemmBatch b{};
+        if (nt) {
+            b.p[b.n] = fp8_problem(0, nt, d, t8->w_ffn_in, t8->s_ffn_in, f, F, c.act_dtype, F, EPI_SWIGLU);
+            b.p[b.n++].up_off = F;
+        }
+        if (ni) {
+            b.p[b.n] = fp8_problem(nt, ni, d, i8->w_ffn_in, i8->s_ffn_in, f + (size_t)nt * F * es, F, c.act_dtype, F,
+                                   EPI_SWIGLU);
+            b.p[b.n++].up_off = F;
+        }
+        DIT_TRY(launch("gemm_fp8_ffn_in_swiglu", s, [&] { return launch_gemm_fp8(b, s); }));
+    } else {
     GemmBatch gf{};
     gf.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     gf.a_dtype = c.act_dtype;
@@ -437,8 +529,24 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
         gf.n = k;
     }
     DIT_TRY(launch("gemm_ffn_in_swiglu", s, [&] { return launch_gemm(gf, s); }));
+    }
 
     // 9. y = h + gate2 * (f W_down^T)
+    if (fp8) {
+        DIT_TRY(quantize("quantize_f", f, F));
+        Fp8GemmBatch b{};
+        if (nt) {
+            b.p[b.n] = fp8_problem(0, nt, F, t8->w_ffn_out, t8->s_ffn_out, y_txt, d, c.y_dtype, d, EPI_GATED_RES);
+            b.p[b.n].r = h; b.p[b.n].ldr = d; b.p[b.n].r_dtype = DIT_F32; b.p[b.n++].gate = mod_t + 5 * (size_t)d;
+        }
+        if (ni) {
+            b.p[b.n] = fp8_problem(nt, ni, F, i8->w_ffn_out, i8->s_ffn_out, y_img, d, c.y_dtype, d, EPI_GATED_RES);
+            b.p[b.n].r = h + (size_t)nt * d; b.p[b.n].ldr = d; b.p[b.n].r_dtype = DIT_F32;
+            b.p[b.n++].gate = mod_i + 5 * (size_t)d;
+        }
+        DIT_TRY(launch("gemm_fp8_ffn_down", s, [&] { return launch_gemm_fp8(b, s); }));
+        return DIT_OK;
+    }
     GemmBatch gd{};
     gd.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     gd.a_dtype = c.act_dtype;
@@ -459,6 +567,24 @@ int dit_block_forward(const dit_block_config* cfg, const dit_stream_weights* txt
                       void* y_img, void* workspace, size_t ws_bytes, void* stream) {
     return block_forward_impl(cfg, txt, img, cond, pos, x_txt, x_img, y_txt, y_img, workspace, ws_bytes, stream,
                               nullptr);
+}
+
+size_t dit_block_fp8_workspace_size(const dit_block_config* cfg) {
+    clear_err();
+    if (validate_fp8_config(cfg) != DIT_OK) return 0;
+    return plan_workspace(cfg, 0, true).total;
+}
+
+int dit_block_forward_fp8(const dit_block_config* cfg, const dit_stream_weights_fp8* txt,
+                          const dit_stream_weights_fp8* img, const void* cond, const int32_t* pos, const void* x_txt,
+                          const void* x_img, void* y_txt, void* y_img, void* workspace, size_t ws_bytes,
+                          void* stream) {
+    if (!txt || !img) {
+        clear_err();
+        return fail(DIT_ERR_INVALID_ARG, "fp8 weights are NULL");
+    }
+    return block_forward_impl(cfg, nullptr, nullptr, cond, pos, x_txt, x_img, y_txt, y_img, workspace, ws_bytes,
+                              stream, nullptr, txt, img);
 }
 
 // mod_pre: the [3d] fp32 AdaLN vectors computed by the caller, or NULL (from w->w_mod and cond).
@@ -999,11 +1125,13 @@ int dit_linear_fp8(void* stream, const void* xq, long ld_x, const float* sx, con
     if (overlap(ry, rx) || overlap(ry, rw) || overlap(ry, range_of(sx, 1, m, m, DIT_F32)) ||
         overlap(ry, range_of(sw, 1, n, n, DIT_F32)))
         return fail(DIT_ERR_INVALID_ARG, "y overlaps an input");
-    Fp8GemmArgs g{};
-    g.a = reinterpret_cast<const uint8_t*>(xq); g.lda = ld_x; g.sa = sx;
-    g.b = reinterpret_cast<const uint8_t*>(wq); g.ldb = ld_w; g.sb = sw;
-    g.c = y; g.ldc = ld_y; g.c_dtype = y_dtype;
-    g.M = m; g.N = n; g.K = k;
+    Fp8GemmBatch g{};
+    Fp8GemmProblem& P = g.p[0];
+    P.a = reinterpret_cast<const uint8_t*>(xq); P.lda = ld_x; P.sa = sx;
+    P.b = reinterpret_cast<const uint8_t*>(wq); P.ldb = ld_w; P.sb = sw;
+    P.c = y; P.ldc = ld_y; P.c_dtype = y_dtype;
+    P.M = m; P.N = n; P.K = k; P.epi = EPI_STORE;
+    g.n = 1;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     return launch("gemm_fp8", s, [&] { return launch_gemm_fp8(g, s); });
 }

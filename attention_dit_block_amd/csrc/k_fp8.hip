@@ -12,7 +12,10 @@
 // codes (rows of 128 B, the same XOR swizzle), both operands global -> LDS with
 // global_load_lds_dwordx4 into two stages, 8 waves of 128 x 64.  A 32x32x64 MFMA takes 32 codes
 // of one row per lane: lanes 0-31 codes 0-31 of the 64-code k-slice, lanes 32-63 codes 32-63, the
-// same split on both operands.  Epilogue: acc * sa[m] * sb[n], four consecutive columns per lane.
+// same split on both operands.  Epilogue: acc * sa[m] * sb[n], four consecutive columns per lane,
+// then the block's epilogues as in the 16-bit GEMM: plain store, gated residual R + gate[n] * (.),
+// or SwiGLU (a tile's B rows are 128 gate rows and the 128 matching up rows).  One launch covers
+// up to two problems (text and image streams).
 #include "dev_common.h"
 #include "launch.h"
 
@@ -79,23 +82,49 @@ __device__ __forceinline__ f32x16_v mfma_f8(const i32x8_v& a, const i32x8_v& b, 
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-template <int OT>
-__global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmArgs g) {
+__device__ __forceinline__ float silu_f8(float g) { return g / (1.0f + __expf(-g)); }
+
+// Four consecutive columns of one output row, output type chosen at run time.
+__device__ __forceinline__ void store4_any(void* base, size_t off, int dt, const float* o) {
+    char* p = reinterpret_cast<char*>(base);
+    if (dt == F32) store4<F32>(p + off * 4, o);
+    else if (dt == F16) store4<F16>(p + off * 2, o);
+    else store4<BF16>(p + off * 2, o);
+}
+
+// MODE: EPI_STORE, EPI_GATED_RES or EPI_SWIGLU for every problem of the batch.
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmBatch bt) {
     constexpr int NW = 8, WN = 4, NB = 2, LPW = 32 / NW;   // waves, along N, 32-col blocks, loads
+    constexpr bool kSwiglu = MODE == EPI_SWIGLU;
     __shared__ __attribute__((aligned(1024))) char smem[kQLds];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    // tile: XCD-contiguous, groups of 8 M-tiles walked N-major
+    // tile: XCD-contiguous; per problem, groups of 8 M-tiles walked N-major
     const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int pi = (bt.n > 1 && L >= bt.p[1].tile_begin) ? 1 : 0;
+    const Fp8GemmProblem& g = bt.p[pi];
+    const int t = L - g.tile_begin;
     const int per_group = 8 * g.tiles_n;
-    const int grp = L / per_group, first_m = grp * 8;
+    const int grp = t / per_group, first_m = grp * 8;
     const int gsize = min(g.tiles_m - first_m, 8);
-    const int rr = L - grp * per_group;
+    const int rr = t - grp * per_group;
     const int tm = first_m + rr % gsize, tn = rr / gsize;
-    const int m0 = tm * QBM, n0 = tn * QBN;
+    const int m0 = tm * QBM;
+    const int n0 = kSwiglu ? tn * (QBN / 2) : tn * QBN;     // first output column
 
     // load plan: wave w, instruction i covers tile rows (w*LPW+i)*8 .. +7; lane l writes LDS bytes
-    // l*16 .. +15 of the 1 KB block = row l/8, position l%8, holding chunk (l%8) ^ swz(row)
+    // l*16 .. +15 of the 1 KB block = row l/8, position l%8, holding chunk (l%8) ^ swz(row).
+    // SwiGLU tiles stage the gate rows of their 128 output columns in B rows 0-127 and the
+    // matching up rows in 128-255.
+    auto b_src = [&](int row) -> long {
+        if (kSwiglu) {
+            const bool up = row >= QBN / 2;
+            const long n = min((long)n0 + (up ? row - QBN / 2 : row), (long)g.N - 1);
+            return up ? n + g.up_off : n;
+        }
+        return min((long)n0 + row, (long)g.N - 1);
+    };
     const uint8_t* gA[LPW];
     const uint8_t* gB[LPW];
 #pragma unroll
@@ -103,7 +132,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmArgs g) {
         const int row = (wave * LPW + i) * 8 + (lane >> 3);
         const int chunk = (lane & 7) ^ qswz(row);
         gA[i] = g.a + (size_t)min(m0 + row, g.M - 1) * g.lda + chunk * 16;
-        gB[i] = g.b + (size_t)min(n0 + row, g.N - 1) * g.ldb + chunk * 16;
+        gB[i] = g.b + (size_t)b_src(row) * g.ldb + chunk * 16;
     }
     auto issue = [&](int buf, int k0) {
 #pragma unroll
@@ -118,7 +147,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) a_row[j] = wm * 128 + j * 32 + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) b_row[j] = wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < NB; ++j)
+        b_row[j] = (kSwiglu ? j * (QBN / 2) + wn * 32 : wn * 64 + j * 32) + (lane & 31);
     // fragment of sub-step s (codes 64 s .. 64 s + 63 of the k-step): chunks 4 s + 2 h, + 1
     auto frag = [&](const char* base, int row, int s) -> i32x8_v {
         const int c = 4 * s + 2 * h;
@@ -160,36 +190,68 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmArgs g) {
         __syncthreads();
     }
 
-    // epilogue: acc[nb][mb][q] -> row m0 + wm*128 + mb*32 + (lane & 31), column
-    // n0 + wn*64 + nb*32 + 8 (q >> 2) + 4 h + (q & 3)
+    // epilogue: acc[nb][mb][q] -> row m0 + wm*128 + mb*32 + (lane & 31); B row b_row[nb] - (lane & 31)
+    // + 8 (q >> 2) + 4 h + (q & 3) of the tile
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
         const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
         if (m >= g.M) continue;
         const float sa = g.sa[m];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        if constexpr (kSwiglu) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int col = n0 + wn * 64 + nb * 32 + 8 * i + 4 * h;
+                const int col = n0 + wn * 32 + 8 * i + 4 * h;
                 if (col >= g.N) continue;
-                const f32x4_v sb = ldf4(g.sb + col);
+                const f32x4_v sg = ldf4(g.sb + col), su = ldf4(g.sb + g.up_off + col);
                 float o[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) o[j] = acc[nb][mb][4 * i + j] * sa * sb[j];
-                store4<OT>(reinterpret_cast<char*>(g.c) + ((size_t)m * g.ldc + col) * (OT == F32 ? 4 : 2), o);
+                for (int j = 0; j < 4; ++j)
+                    o[j] = silu_f8(acc[0][mb][4 * i + j] * sa * sg[j]) * (acc[1][mb][4 * i + j] * sa * su[j]);
+                store4_any(g.c, (size_t)m * g.ldc + col, g.c_dtype, o);
             }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int col = n0 + wn * 64 + nb * 32 + 8 * i + 4 * h;
+                    if (col >= g.N) continue;
+                    const f32x4_v sb = ldf4(g.sb + col);
+                    float o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] = acc[nb][mb][4 * i + j] * sa * sb[j];
+                    if constexpr (MODE == EPI_GATED_RES) {
+                        const f32x4_v gt = ldf4(g.gate + col);
+                        float r[4];
+                        const size_t roff = (size_t)m * g.ldr + col;
+                        if (g.r_dtype == BF16) load4<BF16>(reinterpret_cast<const char*>(g.r) + roff * 2, r);
+                        else load4<F32>(reinterpret_cast<const char*>(g.r) + roff * 4, r);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) o[j] = fmaf(gt[j], o[j], r[j]);
+                    }
+                    store4_any(g.c, (size_t)m * g.ldc + col, g.c_dtype, o);
+                }
+        }
     }
 }
 
-hipError_t launch_gemm_fp8(Fp8GemmArgs& g, hipStream_t s) {
-    if (g.M == 0) return hipSuccess;
-    g.tiles_m = (g.M + QBM - 1) / QBM;
-    g.tiles_n = (g.N + QBN - 1) / QBN;
-    const dim3 grid(g.tiles_m * g.tiles_n), block(512);
-    if (g.c_dtype == F32) hipLaunchKernelGGL((gemm_fp8_kernel<F32>), grid, block, 0, s, g);
-    else if (g.c_dtype == F16) hipLaunchKernelGGL((gemm_fp8_kernel<F16>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((gemm_fp8_kernel<BF16>), grid, block, 0, s, g);
+hipError_t launch_gemm_fp8(Fp8GemmBatch& bt, hipStream_t s) {
+    int total = 0;
+    for (int i = 0; i < bt.n; ++i) {
+        Fp8GemmProblem& g = bt.p[i];
+        const bool sw = g.epi == EPI_SWIGLU;
+        g.tiles_m = g.M > 0 ? (g.M + QBM - 1) / QBM : 0;
+        g.tiles_n = sw ? (g.N + QBN / 2 - 1) / (QBN / 2) : (g.N + QBN - 1) / QBN;
+        g.tile_begin = total;
+        total += g.tiles_m * g.tiles_n;
+    }
+    bt.total_tiles = total;
+    if (total == 0) return hipSuccess;
+    const dim3 grid(total), block(512);
+    // every problem of a batch has the first one's epilogue (the callers build them so)
+    if (bt.p[0].epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_fp8_kernel<EPI_SWIGLU>), grid, block, 0, s, bt);
+    else if (bt.p[0].epi == EPI_GATED_RES) hipLaunchKernelGGL((gemm_fp8_kernel<EPI_GATED_RES>), grid, block, 0, s, bt);
+    else hipLaunchKernelGGL((gemm_fp8_kernel<EPI_STORE>), grid, block, 0, s, bt);
     return hipGetLastError();
 }
 

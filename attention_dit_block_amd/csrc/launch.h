@@ -139,14 +139,22 @@ constexpr int kWinMaxKeysF32 = 4096;
 // q = e4m3(x / s) rounded to nearest even.  x: F32, BF16 or F16; cols % 8 == 0.
 hipError_t launch_quantize_fp8(const void* x, int x_dtype, long ld_x, int rows, int cols, uint8_t* q, long ld_q,
                                float* scales, hipStream_t s);
-struct Fp8GemmArgs {
+struct Fp8GemmProblem {
     const uint8_t* a; long lda; const float* sa;   // [M, K] codes, [M] scales
-    const uint8_t* b; long ldb; const float* sb;   // [N, K] codes, [N] scales
-    void* c; long ldc; int c_dtype;                // [M, N] = sa[m] sb[n] sum_k a b
-    int M, N, K;                                   // K % 128 == 0, N % 4 == 0
-    int tiles_m, tiles_n;                          // filled by the launcher
+    const uint8_t* b; long ldb; const float* sb;   // [N_b, K] codes, [N_b] scales
+    void* c; long ldc; int c_dtype;                // [M, N]: epilogue(sa[m] sb[n] sum_k a b)
+    const void* r; long ldr; int r_dtype;          // EPI_GATED_RES: residual (F32 or BF16)
+    const float* gate;                             // EPI_GATED_RES: [N]
+    long up_off;                                   // EPI_SWIGLU: row offset of the up half in b and sb
+    int M, N, K, epi;                              // K % 128 == 0, N % 4 == 0
+    int tiles_m, tiles_n, tile_begin;              // filled by the launcher
 };
-hipError_t launch_gemm_fp8(Fp8GemmArgs& g, hipStream_t s);
+struct Fp8GemmBatch {
+    Fp8GemmProblem p[2];
+    int n;              // every problem has p[0].epi
+    int total_tiles;    // filled by the launcher
+};
+hipError_t launch_gemm_fp8(Fp8GemmBatch& g, hipStream_t s);
 
 // ---- 2-D convolution (NHWC), implicit GEMM ----------------------------------------------------
 struct ConvArgs {

@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--fp8-gemm", action="store_true",
                    help="time the fp8 (e4m3) GEMM on the block's four products at the workload's token count "
                         "(one JSON line of its own)")
+    p.add_argument("--fp8-block", action="store_true",
+                   help="time the fp8 double-stream block (its four weight products on e4m3 codes) at the "
+                        "workload's size (one JSON line of its own)")
     p.add_argument("--shared-mod", action="store_true",
                    help="multi-block workloads: one AdaLN weight set per block kind, computed once per step")
     p.add_argument("--act", default="f16", choices=["f16", "bf16"],
@@ -112,6 +115,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.fp8_gemm:
         return fp8_gemm_bench(args, cfg, dit, torch)
+    if args.fp8_block:
+        return fp8_block_bench(args, cfg, dit, torch)
     t = cfg.dtype
     if args.copy_calibration:
         n = args.copy_calibration // 4
@@ -302,6 +307,89 @@ def measured_traffic(workload, kernel, act):
     with open(path, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     return e["bytes"] if sha.startswith(e["sha256"]) else None
+
+
+def fp8_block_bench(args, cfg, dit, torch):
+    """One fp8 double-stream block (dit_block_forward_fp8) on the workload's seeded inputs: the four
+    weight matrices of each stream quantised once to e4m3 before timing (a weight format, like the
+    bf16 storage of the others), the activations quantised inside every step.  Times K steps like
+    the main bench and every launch with the library's HIP events."""
+    if cfg.n_double != 1 or cfg.n_single != 0 or cfg.dtype != "bf16":
+        print("--fp8-block needs a one-double-block bf16 workload", file=sys.stderr)
+        sys.exit(2)
+    import dit_inputs as di
+    dev = torch.device("cuda:0")
+
+    def up(a, dt):
+        a = np.ascontiguousarray(a)
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    inp = di.double_block_inputs(cfg, seed=args.seed)
+    ws8 = {}
+    for s in ("txt", "img"):
+        w = {"w_mod": up(inp[s]["w_mod"], "bf16"), "qk_norm_w": up(inp[s]["qk_norm_w"], "bf16")}
+        for name in ("qkv", "o", "ffn_in", "ffn_out"):
+            wt = up(inp[s]["w_" + name], "bf16")
+            q = torch.empty(wt.shape, dtype=torch.uint8, device=dev)
+            sc = torch.empty(wt.shape[0], dtype=torch.float32, device=dev)
+            dit.quantize_fp8(wt, q, sc)
+            w["w_" + name], w["s_" + name] = q, sc
+            del wt
+        ws8[s] = w
+    shape = dit.Shape(dtype=dit.DIT_BF16, d=cfg.d, n_heads=cfg.n_heads, ffn_inner=cfg.ffn_inner, n_txt=cfg.n_txt,
+                      n_img=cfg.n_img, d_cond=cfg.dc, x_dtype=dit.DIT_BF16, y_dtype=dit.DIT_F32,
+                      act_dtype=dit.DIT_F16)
+    ws = torch.empty(dit.block_fp8_workspace_size(shape), dtype=torch.uint8, device=dev)
+    cond, pos = up(inp["cond"], "bf16"), up(inp["pos"], "i32")
+    x_txt, x_img = up(inp["x_txt"], "bf16"), up(inp["x_img"], "bf16")
+    y_txt = torch.empty(cfg.n_txt, cfg.d, dtype=torch.float32, device=dev)
+    y_img = torch.empty(cfg.n_img, cfg.d, dtype=torch.float32, device=dev)
+
+    def step():
+        dit.block_forward_fp8(shape, ws8["txt"], ws8["img"], cond, pos, x_txt, x_img, y_txt, y_img, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    dit.timing_begin(args.steps * 16)
+    for _ in range(args.steps):
+        step()
+    dit.timing_end()
+    torch.cuda.synchronize()
+    kt = dit.timing_read()
+    n, d, F = cfg.n_tok, cfg.d, cfg.ffn_inner
+    gemm = {"gemm_fp8_qkv": 6.0 * n * d * d, "gemm_fp8_out_proj": 2.0 * n * d * d,
+            "gemm_fp8_ffn_in_swiglu": 4.0 * n * d * F, "gemm_fp8_ffn_down": 2.0 * n * F * d}
+    quant = {"quantize_a": n * d * 3.0, "quantize_o": n * d * 3.0, "quantize_b": n * d * 3.0,
+             "quantize_f": n * F * 3.0}                 # fp16 read + code written
+    kernels = {}
+    for name, (cnt, tot) in kt.items():
+        avg = tot / cnt
+        e = {"avg_ms": round(avg, 5), "share": round(tot / sum(v[1] for v in kt.values()), 4)}
+        if name in gemm:
+            e["tflops"] = round(gemm[name] / (avg * 1e-3) / 1e12, 1)
+            e["frac_fp8_peak"] = round(e["tflops"] / 5000.0, 4)
+        elif name in quant:
+            e["gbs"] = round(quant[name] / (avg * 1e-3) / 1e9, 1)
+            e["frac_hbm"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[name] = e
+    flops = cfg.flops_step()
+    out = {"metric": "fp8 (e4m3 products) DiT block fwd ms & TFLOP/s", "value": round(flops / (ms * 1e-3) / 1e12, 1),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3+f16",
+           "data": "synthetic",
+           "config": {"workload": cfg.name, "tokens": cfg.n_tok, "gflop_per_step": round(flops / 1e9, 1),
+                      "products": "e4m3 weights (per-row scales, quantised once) x e4m3 activations (per row, "
+                                  "every step)"},
+           "kernels": kernels}
+    print(json.dumps(out), flush=True)
 
 
 def fp8_gemm_bench(args, cfg, dit, torch):

@@ -404,6 +404,47 @@ int dit_linear_fp8(void* stream, const void* xq, long ld_x, const float* sx,
                    void* y, int y_dtype, long ld_y);
 
 /*
+ * fp8 double-stream block: dit_block_forward with its four weight products
+ * (QKV, out-projection, FFN-in, FFN-down) on e4m3 codes.  Before each product
+ * the block quantises the product's activations per row exactly as
+ * dit_quantize_fp8 does (a, O, b and f, from their act_dtype values); the
+ * weights come quantised per output row (w[j, :] = s[j] * dec(codes[j, :]), as
+ * dit_quantize_fp8 writes them from the 16-bit weights).  The AdaLN GEMV, the
+ * norms, RoPE, attention and the epilogues (gated residual, SwiGLU) are those
+ * of the 16-bit block, so the only extra error is the e4m3 rounding of both
+ * operands of each product (up to 2^-4 relative per element).
+ *  cfg       dtype DIT_BF16; act_dtype DIT_F16 or DIT_BF16
+ *  txt, img  (host) fp8 weights of each stream (below); every pointer 16-byte
+ *            aligned
+ *  workspace >= dit_block_fp8_workspace_size(cfg) bytes (the 16-bit block's
+ *            plus n * max(d, F) code bytes and n fp32 scales)
+ * Other arguments, aliasing rules and errors as for dit_block_forward.
+ * Launches: GEMV, modulate x, quantise, QKV, QK-norm + RoPE, attention,
+ * quantise, out-projection, modulate h, quantise, FFN-in, quantise, FFN-down.
+ */
+typedef struct dit_stream_weights_fp8 {
+    const void* w_mod;          /* [6d, d_cond] of dtype (shift1, scale1, gate1, shift2, scale2, gate2) */
+    const void* qk_norm_w;      /* [2][head_dim] of dtype */
+    const void* w_qkv;          /* [3d, d] e4m3 codes (row stride d) */
+    const float* s_qkv;         /* [3d] per-row scales */
+    const void* w_o;            /* [d, d] codes */
+    const float* s_o;           /* [d] */
+    const void* w_ffn_in;       /* [2F, d] codes: rows 0..F-1 gate, F..2F-1 up */
+    const float* s_ffn_in;      /* [2F] */
+    const void* w_ffn_out;      /* [d, F] codes (row stride F) */
+    const float* s_ffn_out;     /* [d] */
+} dit_stream_weights_fp8;
+
+/* Workspace bytes of dit_block_forward_fp8; 0 for an invalid config. */
+size_t dit_block_fp8_workspace_size(const dit_block_config* cfg);
+
+int dit_block_forward_fp8(const dit_block_config* cfg,
+                          const dit_stream_weights_fp8* txt, const dit_stream_weights_fp8* img,
+                          const void* cond, const int32_t* pos,
+                          const void* x_txt, const void* x_img, void* y_txt, void* y_img,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * 2-D convolution of the diffusion-VAE decoder (the pipeline's second stage,
  * whose convolutions the decoder page measures), as an implicit GEMM on MFMA:
  * no column buffer is built.

@@ -192,8 +192,19 @@ def _w(ws: Dict[str, np.ndarray], name: str, dtype: str) -> np.ndarray:
     return widen(ws[name], dtype)
 
 
+def _product(x: np.ndarray, w: np.ndarray, fp8: bool) -> np.ndarray:
+    """x w^T.  fp8: both operands first quantised per row to OCP e4m3 (``quantize_fp8_rows``: each
+    row scaled by its max |value| / 448 and rounded to the nearest e4m3 value), the product then
+    exact (``linear_fp8``) -- the fp8 variant of a weight product."""
+    if not fp8:
+        return x @ w.T
+    xq, sx = quantize_fp8_rows(x)
+    wq, sw = quantize_fp8_rows(w)
+    return linear_fp8(xq, sx, wq, sw)
+
+
 def double_block(cfg, inputs: Dict[str, object], rows_txt=None, rows_img=None,
-                 mods=None, keep: bool = False) -> Dict[str, np.ndarray]:
+                 mods=None, keep: bool = False, fp8: bool = False) -> Dict[str, np.ndarray]:
     """Double-stream block (text and image keep their own weights, attention is joint).
 
     1. m_s = W_mod,s . SiLU(c) -> shift1, scale1, gate1, shift2, scale2, gate2
@@ -211,7 +222,10 @@ def double_block(cfg, inputs: Dict[str, object], rows_txt=None, rows_img=None,
     ``rows_txt`` / ``rows_img`` select output rows (index arrays within each
     stream); all tokens still enter the keys and values.  ``mods`` replaces
     the AdaLN vectors by given [6, d] arrays (special-case pins).  ``keep``
-    returns the intermediates too."""
+    returns the intermediates too.  ``fp8`` quantises both operands of the four weight
+    products (QKV, out-projection, FFN-in, FFN-down) to e4m3 per row (``_product``); the
+    activations are rounded to float32 just before (the quantiser's input precision), everything
+    else stays exact."""
     t = cfg.dtype
     d, H, D, F = cfg.d, cfg.n_heads, cfg.head_dim, cfg.ffn_inner
     nt, ni = cfg.n_txt, cfg.n_img
@@ -229,7 +243,7 @@ def double_block(cfg, inputs: Dict[str, object], rows_txt=None, rows_img=None,
     qkv = {}
     for s in ("txt", "img"):
         a = modulate(xs[s], m[s][0], m[s][1], cfg.eps)
-        qkv[s] = a @ _w(ws[s], "w_qkv", t).T
+        qkv[s] = _product(a, _w(ws[s], "w_qkv", t), fp8)
     q = np.concatenate([qkv["txt"][:, :d], qkv["img"][:, :d]], axis=0)
     k = np.concatenate([qkv["txt"][:, d:2 * d], qkv["img"][:, d:2 * d]], axis=0)
     v = np.concatenate([qkv["txt"][:, 2 * d:], qkv["img"][:, 2 * d:]], axis=0)
@@ -244,11 +258,11 @@ def double_block(cfg, inputs: Dict[str, object], rows_txt=None, rows_img=None,
     out: Dict[str, np.ndarray] = {}
     for s in ("txt", "img"):
         x_r = xs[s][rows[s]]
-        h = x_r + m[s][2] * (o_s[s] @ _w(ws[s], "w_o", t).T)
+        h = x_r + m[s][2] * _product(o_s[s], _w(ws[s], "w_o", t), fp8)
         b = modulate(h, m[s][3], m[s][4], cfg.eps)
-        gu = b @ _w(ws[s], "w_ffn_in", t).T
+        gu = _product(b, _w(ws[s], "w_ffn_in", t), fp8)
         f = swiglu(gu[:, :F], gu[:, F:])
-        y = h + m[s][5] * (f @ _w(ws[s], "w_ffn_out", t).T)
+        y = h + m[s][5] * _product(f, _w(ws[s], "w_ffn_out", t), fp8)
         out["y_" + s] = y
         if keep:
             out.update({"mod_" + s: m[s], "h_" + s: h, "f_" + s: f, "o_" + s: o_s[s]})
@@ -397,7 +411,7 @@ def neighborhood_attention(q, k, v, grid: Sequence[int], kernel: Sequence[int], 
 E4M3_MAX = 448.0
 
 
-def e4m3_decode(code) -> np.ndarray:
+def _e4m3_value(code) -> np.ndarray:
     """Value of e4m3 byte(s): (-1)^s 2^(e-7) (1 + m/8) for e > 0, (-1)^s 2^-6 (m/8) for e = 0;
     0x7f / 0xff are NaN."""
     c = np.asarray(code, dtype=np.int64)
@@ -409,24 +423,30 @@ def e4m3_decode(code) -> np.ndarray:
     return sgn * v
 
 
-_E4M3_POS = e4m3_decode(np.arange(0x7f))        # the 127 finite non-negative values, ascending
+_E4M3_TABLE = _e4m3_value(np.arange(256))       # value of every byte
+_E4M3_POS = _E4M3_TABLE[:0x7f]                  # the 127 finite non-negative values, ascending
+_E4M3_MID = (_E4M3_POS[:-1] + _E4M3_POS[1:]) / 2  # the 126 midpoints between neighbours (exact in float64)
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """Value of e4m3 byte(s), by the closed form above (tabulated once for the 256 bytes)."""
+    return _E4M3_TABLE[np.asarray(code, dtype=np.int64)]
 
 
 def e4m3_encode(x) -> np.ndarray:
     """Round float values to the nearest e4m3 value, ties to the even code (even mantissa), keeping
     the sign (e4m3 has +0 and -0).  Magnitudes from 448 up to (not including) 464, halfway to the next binade step, round to 448;
-    larger ones have no finite code and are refused (the callers scale into range)."""
+    larger ones have no finite code and are refused (the callers scale into range).
+    The non-negative codes 0..126 are the finite values in ascending order, so the code of |x| is
+    the number of midpoints below it, moved up by one at an exact midpoint whose lower neighbour is
+    odd."""
     x = np.asarray(x, dtype=F64)
     a = np.abs(x)
     if np.any(a >= 464.0):
         raise ValueError("value beyond the e4m3 range")
-    hi = np.searchsorted(_E4M3_POS, a, side="left")          # first value >= a
-    hi = np.minimum(hi, len(_E4M3_POS) - 1)
-    lo = np.maximum(hi - 1, 0)
-    d_lo, d_hi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    code = np.where(pick_hi, hi, lo)
-    code = np.where(a == _E4M3_POS[hi], hi, code)
+    code = np.searchsorted(_E4M3_MID, a, side="left")       # midpoints strictly below a
+    at_mid = _E4M3_MID[np.minimum(code, len(_E4M3_MID) - 1)] == a
+    code = code + (at_mid & (code % 2 == 1))
     # the sign survives rounding, so a negative value that rounds to zero is -0 (code 0x80)
     return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 

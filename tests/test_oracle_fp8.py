@@ -62,3 +62,43 @@ def test_linear_fp8_brute_force():
     want = np.array([[sum(o.e4m3_decode(xq[i, k]) * o.e4m3_decode(wq[j, k]) for k in range(5)) * sx[i] * sw[j]
                       for j in range(4)] for i in range(3)])
     np.testing.assert_allclose(o.linear_fp8(xq, sx, wq, sw), want, rtol=1e-15)
+
+
+def _representable_rows(rng, rows, cols):
+    """Rows of e4m3 values times a power of two per row, each row holding +-448 * 2^k once, so the
+    per-row scale is exactly 2^k and every scaled value is an e4m3 value."""
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)])
+    vals = o.e4m3_decode(rng.choice(finite, size=(rows, cols)))
+    vals[:, rng.integers(0, cols, rows)] = 0.0
+    vals[np.arange(rows), rng.integers(0, cols, rows)] = 448.0 * rng.choice([-1.0, 1.0], rows)
+    return vals * np.power(2.0, rng.integers(-12, 4, rows))[:, None]
+
+
+def test_fp8_product_is_exact_on_representable_operands():
+    # e4m3 values scaled by powers of two survive the per-row quantisation unchanged, so the fp8
+    # product must equal the exact one there (up to float64 summation order)
+    rng = np.random.default_rng(7)
+    x, w = _representable_rows(rng, 9, 64), _representable_rows(rng, 5, 64)
+    np.testing.assert_allclose(o._product(x, w, True), x @ w.T, rtol=1e-12, atol=0)
+    np.testing.assert_array_equal(o._product(x, w, False), x @ w.T)
+
+
+def test_fp8_product_error_within_e4m3_rounding_bound():
+    # each operand element moves by at most half an e4m3 step: 2^-4 of its magnitude in the normal
+    # range, 2^-10 of its row scale in the subnormal range -- so the product error is bounded by
+    # sum_k (ex |w| + |x| ew + ex ew); a dropped scale, a transposed operand or a wrong row's scale
+    # breaks it
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((12, 96)) * np.exp(rng.uniform(-3, 3, (12, 1)))
+    w = rng.standard_normal((10, 96)) * 0.02
+    sx = np.max(np.abs(x), axis=1, keepdims=True) / 448.0
+    sw = np.max(np.abs(w), axis=1, keepdims=True) / 448.0
+    ex = np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * sx) * (1 + 1e-6)
+    ew = np.maximum(2.0 ** -4 * np.abs(w), 2.0 ** -10 * sw) * (1 + 1e-6)
+    bound = ex @ np.abs(w).T + np.abs(x) @ ew.T + ex @ ew.T
+    err = np.abs(o._product(x, w, True) - x @ w.T)
+    assert np.all(err <= bound)
+    assert np.max(err / bound) > 0.05          # the bound is not vacuous
+    # and the fp8 block differs from the exact block only through these products
+    y = o._product(x, w, True)
+    assert not np.allclose(y, x @ w.T, rtol=1e-3)
