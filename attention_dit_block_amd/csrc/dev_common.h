@@ -22,7 +22,7 @@ typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
-template <int DT> struct ESize { static constexpr int v = DT == F32 ? 4 : 2; };
+template <int DT> struct ESize { static constexpr int v = DT == F32 ? 4 : (DT == 3 ? 1 : 2); };   // 3: fp8 codes
 
 // ---- 16-bit formats <-> fp32.  Widening is exact; narrowing rounds to nearest even
 // (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 on gfx950).

@@ -410,12 +410,23 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     if (nt) m.p[nm++] = {x_txt, d, c.x_dtype, act, d, mod_t + 0 * d, mod_t + 1 * (size_t)d, nt};
     if (ni) m.p[nm++] = {x_img, d, c.x_dtype, act + (size_t)nt * d * es, d, mod_i + 0 * d, mod_i + 1 * (size_t)d, ni};
     m.n = nm; m.d = d; m.eps = c.eps; m.out_dtype = c.act_dtype;
-    DIT_TRY(launch("modulate_x", s, [&] { return launch_modulate(m, s); }));
-
-    // fp8 products: quantise the activations [n, k] (row stride k) per row, then one grouped e4m3
-    // GEMM over the text rows and the image rows.
+    // fp8 products: a goes straight to e4m3 codes with per-row scales
     uint8_t* q8 = fp8 ? reinterpret_cast<uint8_t*>(ws + W.q8) : nullptr;
     float* sq = fp8 ? reinterpret_cast<float*>(ws + W.sq) : nullptr;
+    auto to_fp8 = [&](ModBatch& mb) {
+        int r0 = 0;
+        for (int i = 0; i < mb.n; ++i) {
+            mb.p[i].out = q8 + (size_t)r0 * d;
+            mb.p[i].out_scale = sq + r0;
+            r0 += mb.p[i].rows;
+        }
+        mb.out_dtype = FP8_ROWS;
+    };
+    if (fp8) to_fp8(m);
+    DIT_TRY(launch(fp8 ? "modulate_x_fp8" : "modulate_x", s, [&] { return launch_modulate(m, s); }));
+
+    // fp8 products: quantise the activations [n, k] (row stride k) per row (a and b come quantised
+    // from the modulate kernel), then one grouped e4m3 GEMM over the text rows and the image rows.
     auto quantize = [&](const char* name, const void* src, int k) {
         return launch(name, s, [&] { return launch_quantize_fp8(src, c.act_dtype, k, n, k, q8, k, sq, s); });
     };
@@ -432,7 +443,6 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
 
     // 3. qkv = a W_qkv^T
     if (fp8) {
-        DIT_TRY(quantize("quantize_a", act, d));
         Fp8GemmBatch b{};
         if (nt) b.p[b.n++] = fp8_problem(0, nt, d, t8->w_qkv, t8->s_qkv, qkv, 3L * d, c.act_dtype, 3 * d, EPI_STORE);
         if (ni) b.p[b.n++] = fp8_problem(nt, ni, d, i8->w_qkv, i8->s_qkv, qkv + (size_t)nt * 3 * d * es, 3L * d,
@@ -501,11 +511,11 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     if (ni) m2.p[nm++] = {h + (size_t)nt * d, d, DIT_F32, act + (size_t)nt * d * es, d, mod_i + 3 * (size_t)d,
                           mod_i + 4 * (size_t)d, ni};
     m2.n = nm; m2.d = d; m2.eps = c.eps; m2.out_dtype = c.act_dtype;
-    DIT_TRY(launch("modulate_h", s, [&] { return launch_modulate(m2, s); }));
+    if (fp8) to_fp8(m2);
+    DIT_TRY(launch(fp8 ? "modulate_h_fp8" : "modulate_h", s, [&] { return launch_modulate(m2, s); }));
 
     // 8. f = SiLU(b W_gate^T) * (b W_up^T)
     if (fp8) {
-        DIT_TRY(quantize("quantize_b", act, d));
         Fp8GemmBatch b{};
         if (nt) {
             b.p[b.n] = fp8_problem(0, nt, d, t8->w_ffn_in, t8->s_ffn_in, f, F, c.act_dtype, F, EPI_SWIGLU);

@@ -141,6 +141,47 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
         for (int t = 0; t < 8; ++t) ss = fmaf(v[i][t], v[i][t], ss);
     ss = wave_sum(ss);
     const float rstd = 1.0f / sqrtf(ss / (float)d + b.eps);
+    if constexpr (OT == FP8_ROWS) {
+        // e4m3 output: the modulated row stays in registers for its max, then s = max / 448 and
+        // codes of v / s (both divisions correctly rounded, round-to-nearest-even conversion)
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int c = min((lane + 64 * i) * 8, d - 8);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                float shv, scv;
+                if constexpr (kEarly) {
+                    shv = sh[i][t >> 2][t & 3];
+                    scv = sc[i][t >> 2][t & 3];
+                } else {
+                    shv = P.shift[c + t];
+                    scv = P.scale[c + t];
+                }
+                v[i][t] = fmaf(1.0f + scv, v[i][t] * rstd, shv);
+                if ((lane + 64 * i) * 8 < d) amax = fmaxf(amax, fabsf(v[i][t]));
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+        const float qs = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+        if (lane == 0) P.out_scale[r] = qs;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int c = (lane + 64 * i) * 8;
+            if (c < d) {
+                float y[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) y[t] = __fdiv_rn(v[i][t], qs);
+                int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+                w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+                int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+                w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+                *reinterpret_cast<u32x2_v*>(orow + c) = u32x2_v{(uint32_t)w0, (uint32_t)w1};
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int c = (lane + 64 * i) * 8;
@@ -176,6 +217,7 @@ static hipError_t launch_mod_nc(const ModBatch& b, hipStream_t s, dim3 grid) {
 
 template <int XT>
 static hipError_t launch_mod_x(const ModBatch& b, hipStream_t s, dim3 grid) {
+    if (b.out_dtype == FP8_ROWS) return launch_mod_nc<XT, FP8_ROWS>(b, s, grid);
     if (b.out_dtype == F16) return launch_mod_nc<XT, F16>(b, s, grid);
     if (b.out_dtype == BF16) return launch_mod_nc<XT, BF16>(b, s, grid);
     return launch_mod_nc<XT, F32>(b, s, grid);

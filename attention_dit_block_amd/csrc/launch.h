@@ -9,6 +9,8 @@
 namespace dit {
 
 enum DType { F32 = 0, BF16 = 1, F16 = 2 };
+// Output type of the modulate kernel only: OCP e4m3 codes with a per-row fp32 scale.
+constexpr int FP8_ROWS = 3;
 
 // ---- AdaLN GEMV: out_p[r] = sum_k W_p[r, k] * SiLU(cond[k]) ------------------
 struct GemvProblem {
@@ -31,13 +33,15 @@ struct ModProblem {
     void* out; long ld_out;                   // out_dtype of the batch
     const float* shift; const float* scale;   // [d] fp32
     int rows;
+    float* out_scale;                         // FP8_ROWS: [rows] per-row scales
 };
 struct ModBatch {
     ModProblem p[2];
     int n;
     int d;
     float eps;
-    int out_dtype;      // F32, BF16 or F16
+    int out_dtype;      // F32, BF16, F16, or FP8_ROWS: e4m3 codes (bytes, row stride ld_out) quantised per
+                        // row as launch_quantize_fp8 does, from the fp32 results
 };
 hipError_t launch_modulate(const ModBatch& b, hipStream_t s);
 

@@ -367,8 +367,8 @@ def fp8_block_bench(args, cfg, dit, torch):
     n, d, F = cfg.n_tok, cfg.d, cfg.ffn_inner
     gemm = {"gemm_fp8_qkv": 6.0 * n * d * d, "gemm_fp8_out_proj": 2.0 * n * d * d,
             "gemm_fp8_ffn_in_swiglu": 4.0 * n * d * F, "gemm_fp8_ffn_down": 2.0 * n * F * d}
-    quant = {"quantize_a": n * d * 3.0, "quantize_o": n * d * 3.0, "quantize_b": n * d * 3.0,
-             "quantize_f": n * F * 3.0}                 # fp16 read + code written
+    quant = {"quantize_o": n * d * 3.0, "quantize_f": n * F * 3.0,          # fp16 read + code written
+             "modulate_x_fp8": n * d * 3.0, "modulate_h_fp8": n * d * 5.0}  # bf16 / fp32 read + code written
     kernels = {}
     for name, (cnt, tot) in kt.items():
         avg = tot / cnt

@@ -406,8 +406,9 @@ int dit_linear_fp8(void* stream, const void* xq, long ld_x, const float* sx,
 /*
  * fp8 double-stream block: dit_block_forward with its four weight products
  * (QKV, out-projection, FFN-in, FFN-down) on e4m3 codes.  Before each product
- * the block quantises the product's activations per row exactly as
- * dit_quantize_fp8 does (a, O, b and f, from their act_dtype values); the
+ * the block quantises the product's activations per row by dit_quantize_fp8's
+ * rule (a and b from their fp32 values, inside the modulation kernel; O and f
+ * from their act_dtype values); the
  * weights come quantised per output row (w[j, :] = s[j] * dec(codes[j, :]), as
  * dit_quantize_fp8 writes them from the 16-bit weights).  The AdaLN GEMV, the
  * norms, RoPE, attention and the epilogues (gated residual, SwiGLU) are those
@@ -419,8 +420,9 @@ int dit_linear_fp8(void* stream, const void* xq, long ld_x, const float* sx,
  *  workspace >= dit_block_fp8_workspace_size(cfg) bytes (the 16-bit block's
  *            plus n * max(d, F) code bytes and n fp32 scales)
  * Other arguments, aliasing rules and errors as for dit_block_forward.
- * Launches: GEMV, modulate x, quantise, QKV, QK-norm + RoPE, attention,
- * quantise, out-projection, modulate h, quantise, FFN-in, quantise, FFN-down.
+ * Launches (11): GEMV, modulate x (to e4m3), QKV, QK-norm + RoPE, attention,
+ * quantise O, out-projection, modulate h (to e4m3), FFN-in, quantise f,
+ * FFN-down.
  */
 typedef struct dit_stream_weights_fp8 {
     const void* w_mod;          /* [6d, d_cond] of dtype (shift1, scale1, gate1, shift2, scale2, gate2) */

@@ -57,7 +57,7 @@ def run_fp8(dit, cfg, inp, y_dtype="f32"):
     dit.block_forward_fp8(sh, wt, wi, dev(inp["cond"], "bf16"), dev(inp["pos"], "i32"), dev(inp["x_txt"], "bf16"),
                           dev(inp["x_img"], "bf16"), yt, yi, ws)
     torch.cuda.synchronize()
-    assert dit.launch_count() == before + 13
+    assert dit.launch_count() == before + 11
     return host(yt), host(yi)
 
 
