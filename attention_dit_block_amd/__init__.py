@@ -22,7 +22,7 @@ __all__ = [
     "step_workspace_size", "step_forward", "step_shared_mod_workspace_size", "step_forward_shared_mod",
     "timestep_embedding_workspace_size", "timestep_embedding", "linear",
     "final_layer_workspace_size", "final_layer", "neighborhood_attention", "quantize_fp8", "linear_fp8",
-    "StreamWeightsFp8", "block_fp8_workspace_size", "block_forward_fp8", "conv2d",
+    "StreamWeightsFp8", "block_fp8_workspace_size", "block_forward_fp8", "conv2d", "convert_bf16_to_f16",
     "last_error", "launch_count", "abi_version",
     "timing_begin", "timing_end", "timing_read",
 ]
@@ -43,7 +43,8 @@ _vp, _i, _l, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_fl
 class BlockConfig(ctypes.Structure):
     _fields_ = [("dtype", _i), ("act_dtype", _i), ("x_dtype", _i), ("y_dtype", _i), ("d", _i), ("n_heads", _i),
                 ("head_dim", _i), ("ffn_inner", _i), ("d_cond", _i), ("n_txt", _i), ("n_img", _i),
-                ("eps", _f), ("eps_qk", _f), ("theta", _f), ("n_axes", _i), ("axes_dim", _i * 4)]
+                ("eps", _f), ("eps_qk", _f), ("theta", _f), ("n_axes", _i), ("axes_dim", _i * 4),
+                ("gemm_w_dtype", _i)]
 
 
 class StreamWeights(ctypes.Structure):
@@ -98,6 +99,7 @@ _wsize8 = _sig("dit_block_fp8_workspace_size", _sz, [ctypes.POINTER(BlockConfig)
 _block8 = _sig("dit_block_forward_fp8", _i, [ctypes.POINTER(BlockConfig), ctypes.POINTER(StreamWeightsFp8),
                                              ctypes.POINTER(StreamWeightsFp8), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                              _vp])
+_cvt16 = _sig("dit_convert_bf16_to_f16", _i, [_vp, _vp, _vp, _sz])
 _conv = _sig("dit_conv2d", _i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp, _i])
 _last_error = _sig("dit_last_error", ctypes.c_char_p, [])
 _launch_count = _sig("dit_launch_count", ctypes.c_uint64, [])
@@ -112,7 +114,7 @@ EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", 
             "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_linear",
             "dit_final_layer_workspace_size", "dit_final_layer", "dit_neighborhood_attention",
             "dit_quantize_fp8", "dit_linear_fp8", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
-            "dit_conv2d",
+            "dit_conv2d", "dit_convert_bf16_to_f16",
             "dit_last_error", "dit_launch_count",
             "dit_abi_version", "dit_timing_begin", "dit_timing_end", "dit_timing_read"]
 
@@ -268,6 +270,7 @@ class Shape:
     eps_qk: float = 1e-6
     theta: float = 1e4
     axes_dim: Sequence[int] = (32, 32, 32, 32)
+    gemm_w_dtype: int = 0       # 0: weights of dtype; DIT_F16: fp16 copies of the product weights
 
     def c_config(self) -> BlockConfig:
         c = BlockConfig()
@@ -285,6 +288,7 @@ class Shape:
         c.n_axes = len(self.axes_dim)
         for i, a in enumerate(self.axes_dim):
             c.axes_dim[i] = a
+        c.gemm_w_dtype = self.gemm_w_dtype
         return c
 
 
@@ -577,6 +581,15 @@ def block_forward_fp8(shape: Shape, txt: dict, img: dict, cond, pos, x_txt, x_im
                  _ptr(y_img, "y_img"), _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                  _stream(stream))
     _check(rc, "dit_block_forward_fp8")
+
+
+def convert_bf16_to_f16(src, dst, stream=None) -> None:
+    """dst (fp16) = src (bf16), elementwise: the weight format of Shape.gemm_w_dtype = DIT_F16."""
+    import torch
+    if not src.is_contiguous() or not dst.is_contiguous() or dst.numel() != src.numel():
+        raise ValueError("src and dst must be contiguous tensors of the same size")
+    rc = _cvt16(_stream(stream), _ptr(src, "src", torch.bfloat16), _ptr(dst, "dst", torch.float16), src.numel())
+    _check(rc, "dit_convert_bf16_to_f16")
 
 
 def conv2d(x, weight, y, bias=None, stream=None) -> None:

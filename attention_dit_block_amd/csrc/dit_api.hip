@@ -118,6 +118,10 @@ int validate_config(const dit_block_config* c) {
         return fail(DIT_ERR_UNSUPPORTED, "an fp32 block needs fp32 activations, x and y");
     if (c->dtype == DIT_BF16 && c->act_dtype == DIT_F32)
         return fail(DIT_ERR_UNSUPPORTED, "bf16 weights need DIT_F16 or DIT_BF16 activations");
+    if (c->gemm_w_dtype != 0 && c->gemm_w_dtype != c->dtype &&
+        !(c->gemm_w_dtype == DIT_F16 && c->dtype == DIT_BF16 && c->act_dtype == DIT_F16))
+        return fail(DIT_ERR_UNSUPPORTED, "gemm_w_dtype must be 0, dtype, or DIT_F16 for a bf16 block with DIT_F16 "
+                                         "activations");
     if (c->head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim = %d (only 128 is supported)", c->head_dim);
     if (c->n_heads < 1 || c->d != c->n_heads * c->head_dim)
         return fail(DIT_ERR_INVALID_ARG, "d = %d must equal n_heads * head_dim = %d * %d", c->d, c->n_heads, c->head_dim);
@@ -452,6 +456,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     GemmBatch gq{};
     gq.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     gq.a_dtype = c.act_dtype;
+    gq.b_f16 = c.gemm_w_dtype == DIT_F16;
     {
         int k = 0;
         if (nt) gq.p[k++] = {act, d, txt->w_qkv, d, qkv, 3L * d, c.act_dtype, nullptr, 0, 0, nullptr, 0, nt, 3 * d, d, EPI_STORE};
@@ -493,6 +498,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     GemmBatch go{};
     go.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     go.a_dtype = c.act_dtype;
+    go.b_f16 = c.gemm_w_dtype == DIT_F16;
     {
         int k = 0;
         if (nt) go.p[k++] = {ob, d, txt->w_o, d, h, d, DIT_F32, x_txt, d, c.x_dtype, mod_t + 2 * (size_t)d, 0, nt, d, d,
@@ -531,6 +537,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     GemmBatch gf{};
     gf.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     gf.a_dtype = c.act_dtype;
+    gf.b_f16 = c.gemm_w_dtype == DIT_F16;
     {
         int k = 0;
         if (nt) gf.p[k++] = {act, d, txt->w_ffn_in, d, f, F, c.act_dtype, nullptr, 0, 0, nullptr, F, nt, F, d, EPI_SWIGLU};
@@ -560,6 +567,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     GemmBatch gd{};
     gd.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     gd.a_dtype = c.act_dtype;
+    gd.b_f16 = c.gemm_w_dtype == DIT_F16;
     {
         int k = 0;
         if (nt) gd.p[k++] = {f, F, txt->w_ffn_out, F, y_txt, d, c.y_dtype, h, d, DIT_F32, mod_t + 5 * (size_t)d, 0, nt, d,
@@ -649,6 +657,7 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
     GemmBatch g1{};
     g1.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     g1.a_dtype = c.act_dtype;
+    g1.b_f16 = c.gemm_w_dtype == DIT_F16;
     g1.p[0] = {act, d, w->w_1, d, qkv, 3L * d, c.act_dtype, nullptr, 0, 0, nullptr, 0, n, 3 * d, d, EPI_STORE};
     g1.p[1] = {act, d, reinterpret_cast<const char*>(w->w_1) + (size_t)3 * d * d * esize(c.dtype), d,
                of + (size_t)d * es, ldof, c.act_dtype, nullptr, 0, 0, nullptr, F, n, F, d, EPI_SWIGLU};
@@ -671,6 +680,7 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
     GemmBatch g2{};
     g2.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     g2.a_dtype = c.act_dtype;
+    g2.b_f16 = c.gemm_w_dtype == DIT_F16;
     g2.p[0] = {of, ldof, w->w_2, ldof, y, d, c.y_dtype, x, d, c.x_dtype, mod + 2 * (size_t)d, 0, n, d, d + F,
                EPI_GATED_RES};
     g2.n = 1;
@@ -1091,6 +1101,17 @@ int dit_neighborhood_attention(int dtype, void* stream, const void* q, long ld_q
 // =========================================================================================
 // fp8 (OCP e4m3) quantisation and linear layer.
 // =========================================================================================
+int dit_convert_bf16_to_f16(void* stream, const void* src, void* dst, size_t n) {
+    clear_err();
+    if (n == 0) return DIT_OK;
+    DIT_TRY(check_ptr(src, "src"));
+    DIT_TRY(check_ptr(dst, "dst"));
+    if (overlap(range_of(src, 1, (long)n, (long)n, DIT_BF16), range_of(dst, 1, (long)n, (long)n, DIT_F16)))
+        return fail(DIT_ERR_INVALID_ARG, "src and dst overlap");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("convert_bf16_to_f16", s, [&] { return launch_bf16_to_f16(src, dst, n, s); });
+}
+
 int dit_quantize_fp8(int x_dtype, void* stream, const void* x, long ld_x, int rows, int cols, void* q, long ld_q,
                      float* scales) {
     clear_err();

@@ -6,6 +6,8 @@
 //
 // All of it is small next to the blocks (a GEMV over a d x d matrix, one pass over the image
 // rows), so the kernels are plain: one wave per output row, 16-byte loads, fp32 arithmetic.
+#include <algorithm>
+
 #include "dev_common.h"
 #include "launch.h"
 
@@ -133,6 +135,31 @@ hipError_t launch_vec_gemv(const void* w, int w_dtype, int rows, int K, const fl
         if (silu_in) hipLaunchKernelGGL((vec_gemv_kernel<F32, true>), grid, block, lds, s, w, rows, K, v, out, acc);
         else hipLaunchKernelGGL((vec_gemv_kernel<F32, false>), grid, block, lds, s, w, rows, K, v, out, acc);
     }
+    return hipGetLastError();
+}
+
+// bf16 -> fp16, 8 elements per thread per step (16-byte loads and stores), grid-stride; the same
+// rounding as the GEMM's staging conversion (exact for |x| >= 2^-14, nearest even below).
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* in, uint16_t* out, size_t n) {
+    const size_t n8 = n / 8;
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n8; i += (size_t)gridDim.x * blockDim.x) {
+        const u32x4_v w = ld16(in + i * 8);
+        u32x4_v o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = bf16x2_to_f16x2(w[j]);
+        *reinterpret_cast<u32x4_v*>(out + i * 8) = o;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < n - n8 * 8) {
+        const size_t i = n8 * 8 + threadIdx.x;
+        out[i] = (uint16_t)(bf16x2_to_f16x2(in[i]) & 0xffffu);
+    }
+}
+
+hipError_t launch_bf16_to_f16(const void* in, void* out, size_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const size_t blocks = std::min<size_t>((n / 8 + 255) / 256 + 1, 8192);
+    hipLaunchKernelGGL(bf16_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t*>(in), reinterpret_cast<uint16_t*>(out), n);
     return hipGetLastError();
 }
 

@@ -81,8 +81,13 @@ __device__ __forceinline__ void store4_dt(void* base, size_t off, int dt, const 
     else store4<BF16>(p + off * 2, o);
 }
 
-// A (activations, AT) is staged global -> LDS with global_load_lds_dwordx4.  B (bf16 weights)
-// goes the same way when AT == BF16; when AT == F16 it is loaded into VGPRs, converted to fp16
+// Operand types: AT = BF16 (bf16 activations and weights), F16 (fp16 activations, bf16 weights) or
+// F16W (fp16 activations and fp16 copies of the weights).
+constexpr int F16W = 4;
+template <int AT> constexpr int mfma_type() { return AT == BF16 ? BF16 : F16; }
+
+// A (activations, AT) is staged global -> LDS with global_load_lds_dwordx4.  B (weights)
+// goes the same way when AT is BF16 or F16W; when AT == F16 it is loaded into VGPRs, converted to fp16
 // (exact: bf16 values are fp16 values in fp16's normal range) and written to the same LDS
 // layout, so both operands of the fp16 MFMA come from one swizzled layout.
 //
@@ -116,7 +121,8 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
     constexpr int LPW = 32 / NW;                   // 1 KB load instructions per wave per operand
     constexpr int kStage = (BM + BN) * BK * 2;     // bytes of one A+B stage
     constexpr int kBOff = BM * BK * 2;             // B tile offset within a stage
-    typedef typename Frag<AT>::T FragT;
+    constexpr int MT = mfma_type<AT>();           // MFMA operand type
+    typedef typename Frag<MT>::T FragT;
 
     int pi, tm, tn;
     tile_of(b, L, pi, tm, tn);
@@ -174,7 +180,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
         for (int i = 0; i < LPW; ++i) {
             __builtin_amdgcn_global_load_lds(gA[i] + k0, (lds_void*)(smem + buf * kStage + (wave * LPW + i) * 1024),
                                              16, 0, 0);
-            if constexpr (AT == BF16)
+            if constexpr (AT != F16)
                 __builtin_amdgcn_global_load_lds(gB[i] + k0,
                                                  (lds_void*)(smem + buf * kStage + kBOff + (wave * LPW + i) * 1024),
                                                  16, 0, 0);
@@ -259,7 +265,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma32<AT>(fb[cur][nb], fa[cur][mb], acc[nb][mb]);
+                for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma32<MT>(fb[cur][nb], fa[cur][mb], acc[nb][mb]);
             if (s + 1 < BK / 16) {
 #pragma unroll
                 for (int i = 0; i < kReads; ++i) {
@@ -611,7 +617,8 @@ hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
         b.dp_tiles = D >= 1 ? (D - 1) * G : 0;
         b.epoch = next_launch_tag();
     }
-    if (b.a_dtype == F16) launch_mfma<F16>(b, s, all_store, all_res, all_swiglu);
+    if (b.a_dtype == F16 && b.b_f16) launch_mfma<F16W>(b, s, all_store, all_res, all_swiglu);
+    else if (b.a_dtype == F16) launch_mfma<F16>(b, s, all_store, all_res, all_swiglu);
     else if (b.a_dtype == BF16) launch_mfma<BF16>(b, s, all_store, all_res, all_swiglu);
     else hipLaunchKernelGGL(gemm_f32_kernel, dim3(total), dim3(256), 0, s, b);
     return hipGetLastError();

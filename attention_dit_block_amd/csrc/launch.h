@@ -87,6 +87,7 @@ struct GemmBatch {
     int n;
     int a_dtype;        // F32 (fp32 path, fp32 weights), BF16 (bf16 weights) or F16 (bf16 weights,
                         // converted to fp16 while they are staged)
+    bool b_f16;         // F16 activations only: the weights are fp16 copies, staged as they are
     int group_m;        // tile raster: groups of group_m M-tiles, N-major inside a group (0: 8)
     int total_tiles;    // filled by the launcher
     // Stream-K scratch (16-B-aligned device memory of gemm_sk_scratch_bytes(), or null: one
@@ -179,6 +180,8 @@ hipError_t launch_freq_embed(const float* t, double time_factor, double max_peri
 hipError_t launch_vec_gemv(const void* w, int w_dtype, int rows, int K, const float* v, bool silu_in, float* out,
                            bool accumulate, hipStream_t s);
 hipError_t launch_cast(const float* in, void* out, int n, int dtype, hipStream_t s);
+// out[i] = fp16(in[i]) for bf16 in (16-byte aligned in and out)
+hipError_t launch_bf16_to_f16(const void* in, void* out, size_t n, hipStream_t s);
 // out = (1 + scale) * LayerNorm(x) + shift per row (x: F32 or BF16)
 hipError_t launch_layernorm_modulate(const void* x, int x_dtype, long ld_x, void* out, int out_dtype, long ld_out,
                                      const float* shift, const float* scale, int rows, int d, float eps,

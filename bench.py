@@ -6,7 +6,10 @@ A step is one dit_block_forward call (all 9 kernels of the block) over the
 workload's synthetic inputs, already resident in HBM (c3: the whole denoising
 step, 5 double-stream then 20 single-stream blocks).  Prints ONE JSON line.
 Throughput (``value``) is algorithmic TFLOP/s: 26 N d^2 (GEMMs) + 4 N^2 d
-(attention QK^T and PV) per block, 2 flop per multiply-add.
+(attention QK^T and PV) per block, 2 flop per multiply-add.  The bf16 workloads
+run with fp16 activations and, by default, the matrix-product weights as fp16
+copies of the bf16 weights made once at setup (outputs bit-identical to the bf16
+weights; ``--gemm-weights bf16`` times the weights as given).
 
 ``roofline`` covers the kernel with the largest total time, timed with HIP
 events the library records on the launch stream around each of its launches
@@ -50,6 +53,11 @@ def parse():
                         "workload's size (one JSON line of its own)")
     p.add_argument("--shared-mod", action="store_true",
                    help="multi-block workloads: one AdaLN weight set per block kind, computed once per step")
+    p.add_argument("--gemm-weights", default="f16", choices=["bf16", "f16"],
+                   help="f16 (default): the matrix-product weights as fp16 copies of the bf16 weights, converted "
+                        "once at setup by dit_convert_bf16_to_f16 (the conversion the fp16-activation GEMMs "
+                        "otherwise apply to every staged weight tile; block outputs are bit-identical); "
+                        "bf16: the bf16 weights as given")
     p.add_argument("--act", default="f16", choices=["f16", "bf16"],
                    help="storage of the activations between the block's steps (bf16 workloads)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -143,15 +151,29 @@ def main():
     cond, pos = up(inp["cond"], t), up(inp["pos"], "i32")
     x_txt, x_img = up(inp["x_txt"], t), up(inp["x_img"], t)
     act = None if t != "bf16" else (dit.DIT_F16 if args.act == "f16" else dit.DIT_BF16)
+    f16w = t == "bf16" and args.act == "f16" and args.gemm_weights == "f16"
     shape = dit.Shape(dtype=tdt, d=cfg.d, n_heads=cfg.n_heads, ffn_inner=cfg.ffn_inner, n_txt=cfg.n_txt,
-                      n_img=cfg.n_img, d_cond=cfg.dc, x_dtype=tdt, y_dtype=dit.DIT_F32, act_dtype=act)
+                      n_img=cfg.n_img, d_cond=cfg.dc, x_dtype=tdt, y_dtype=dit.DIT_F32, act_dtype=act,
+                      gemm_w_dtype=dit.DIT_F16 if f16w else 0)
+    product_weights = ("w_qkv", "w_o", "w_ffn_in", "w_ffn_out", "w_1", "w_2")
+
+    def upw(a, dt, name):
+        """Upload one weight tensor; with fp16 product weights, convert those once on the GPU."""
+        g = up(a, dt)
+        if f16w and name in product_weights:
+            h = torch.empty(g.shape, dtype=torch.float16, device=dev)
+            dit.convert_bf16_to_f16(g, h)
+            torch.cuda.synchronize()
+            del g
+            return h
+        return g
     ws = torch.empty(max(dit.block_workspace_size(shape), dit.block_workspace_size(shape, True)),
                      dtype=torch.uint8, device=dev)
     y_txt = torch.empty(cfg.n_txt, cfg.d, dtype=torch.float32, device=dev)
     y_img = torch.empty(cfg.n_img, cfg.d, dtype=torch.float32, device=dev)
     if cfg.n_double == 1 and cfg.n_single == 0:
-        wt = {k: up(v, t) for k, v in inp["txt"].items()}
-        wi = {k: up(v, t) for k, v in inp["img"].items()}
+        wt = {k: upw(v, t, k) for k, v in inp["txt"].items()}
+        wi = {k: upw(v, t, k) for k, v in inp["img"].items()}
         step_blocks.append(lambda: dit.block_forward(shape, wt, wi, cond, pos, x_txt, x_img, y_txt, y_img, ws))
     else:
         # the full step through dit_step_forward: n_double double-stream blocks, then n_single
@@ -160,11 +182,11 @@ def main():
         for b in range(cfg.n_double):
             print(f"setup: double block {b + 1}/{cfg.n_double}", file=sys.stderr, flush=True)
             bi = di.double_block_inputs(cfg, seed=args.seed, block=b)
-            wts.append({k: up(v, t) for k, v in bi["txt"].items()})
-            wis.append({k: up(v, t) for k, v in bi["img"].items()})
+            wts.append({k: upw(v, t, k) for k, v in bi["txt"].items()})
+            wis.append({k: upw(v, t, k) for k, v in bi["img"].items()})
         for b in range(cfg.n_single):
             print(f"setup: single block {b + 1}/{cfg.n_single}", file=sys.stderr, flush=True)
-            sws.append({k: up(v, t) for k, v in di.single_weights(cfg, args.seed, cfg.n_double + b).items()})
+            sws.append({k: upw(v, t, k) for k, v in di.single_weights(cfg, args.seed, cfg.n_double + b).items()})
         state = torch.empty(cfg.n_tok, cfg.d, dtype=torch.float32, device=dev)
         if args.shared_mod:
             sm = {k: up(v, t) for k, v in di.shared_mod_weights(cfg, seed=args.seed).items()}
@@ -253,14 +275,15 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(by / (avg * 1e-3) / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(cfg.name, dom, args.act if t == "bf16" else "f32")
+    roof["traffic"] = measured_traffic(cfg.name, dom, (args.act + ("/f16w" if f16w else "")) if t == "bf16" else "f32")
 
     out = {
         "metric": METRIC, "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if t == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "activations": args.act if t == "bf16" else "f32", "blocks": cfg.n_double + cfg.n_single, "d": cfg.d, "heads": cfg.n_heads,
+        "config": {"workload": cfg.name, "activations": args.act if t == "bf16" else "f32",
+                   "product_weights": "f16 copies of the bf16 weights (converted once, exact)" if f16w else t, "blocks": cfg.n_double + cfg.n_single, "d": cfg.d, "heads": cfg.n_heads,
                    "ffn_inner": cfg.ffn_inner, "n_txt": cfg.n_txt, "n_img": cfg.n_img, "tokens": cfg.n_tok,
                    "gflop_per_step": round(flops / 1e9, 1),
                    "modulation": "shared" if shared else "per_block"},
@@ -279,20 +302,21 @@ def main():
 
 # HBM bytes per launch, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) over this
 # bench, each counter scaled by what it reads for a plain device copy of known size (FETCH_SIZE
-# x2.0, WRITE_SIZE x1.0).  Keyed by workload, activation type and kernel; each entry holds the
+# x2.0, WRITE_SIZE x1.0).  Keyed by workload, activation type (/f16w: fp16 product weights) and
+# kernel; each entry holds the
 # SHA-256 prefix of the kernel's source at the time of the counters and is reported only while
 # that source is unchanged.
 _C2 = "c2_bf16_d3072_t512_i4096"
 MEASURED_TRAFFIC = {
-    (_C2, "f16", "gemm_ffn_in_swiglu"): {"bytes": 1565964122, "sha256": "c90371d260f329ae"},
-    (_C2, "f16", "gemm_qkv"): {"bytes": 584656720, "sha256": "c90371d260f329ae"},
-    (_C2, "f16", "gemm_ffn_down"): {"bytes": 654703998, "sha256": "c90371d260f329ae"},
-    (_C2, "f16", "gemm_out_proj"): {"bytes": 281208892, "sha256": "c90371d260f329ae"},
-    (_C2, "f16", "joint_attention"): {"bytes": 881344309, "sha256": "f44582844611a615"},
-    (_C2, "f16", "adaln_gemv"): {"bytes": 226824819, "sha256": "d3c9089a528c9d47"},
-    (_C2, "f16", "qk_rmsnorm_rope"): {"bytes": 113912776, "sha256": "d3c9089a528c9d47"},
-    (_C2, "f16", "modulate_h"): {"bytes": 85394629, "sha256": "d3c9089a528c9d47"},
-    (_C2, "f16", "modulate_x"): {"bytes": 57089878, "sha256": "d3c9089a528c9d47"},
+    (_C2, "f16/f16w", "gemm_ffn_in_swiglu"): {"bytes": 1565964122, "sha256": "c90371d260f329ae"},
+    (_C2, "f16/f16w", "gemm_qkv"): {"bytes": 584656720, "sha256": "c90371d260f329ae"},
+    (_C2, "f16/f16w", "gemm_ffn_down"): {"bytes": 654703998, "sha256": "c90371d260f329ae"},
+    (_C2, "f16/f16w", "gemm_out_proj"): {"bytes": 281208892, "sha256": "c90371d260f329ae"},
+    (_C2, "f16/f16w", "joint_attention"): {"bytes": 881344309, "sha256": "f44582844611a615"},
+    (_C2, "f16/f16w", "adaln_gemv"): {"bytes": 226824819, "sha256": "d3c9089a528c9d47"},
+    (_C2, "f16/f16w", "qk_rmsnorm_rope"): {"bytes": 113912776, "sha256": "d3c9089a528c9d47"},
+    (_C2, "f16/f16w", "modulate_h"): {"bytes": 85394629, "sha256": "d3c9089a528c9d47"},
+    (_C2, "f16/f16w", "modulate_x"): {"bytes": 57089878, "sha256": "d3c9089a528c9d47"},
 }
 
 KERNEL_SOURCE = {"gemm": "k_gemm.hip", "joint_attention": "k_attention.hip"}

@@ -157,6 +157,12 @@ typedef struct dit_block_config {
     float theta;        /* RoPE base (1e4 for FLUX) */
     int n_axes;         /* RoPE axes (4) */
     int axes_dim[4];    /* dims per axis ({32,32,32,32}) */
+    int gemm_w_dtype;   /* storage of the matrix-product weights (w_qkv, w_o, w_ffn_in,
+                           w_ffn_out; w_1, w_2): 0 = dtype; DIT_F16 (dtype DIT_BF16 with
+                           DIT_F16 activations only) = fp16 copies of the bf16 weights made
+                           once by dit_convert_bf16_to_f16, which the GEMMs stage without
+                           converting (results identical to the bf16 weights); w_mod,
+                           qk_norm_w and cond stay of dtype */
 } dit_block_config;
 
 /* Weights of one stream of a double-stream block ([out, in], dtype). */
@@ -464,6 +470,14 @@ int dit_block_forward_fp8(const dit_block_config* cfg,
 int dit_conv2d(int dtype, void* stream, const void* x, int batch, int height, int width,
                int c_in, const void* weight, int c_out, int kh, int kw, const float* bias,
                void* y, int y_dtype);
+
+/*
+ * Weight format conversion: dst[i] = fp16(src[i]) for n bf16 values (exact for
+ * |x| >= 2^-14 and zero; smaller magnitudes round to nearest even among fp16
+ * subnormals, as the GEMMs' own staging conversion does).  src and dst 16-byte
+ * aligned, not overlapping.  One launch on stream.  For gemm_w_dtype = DIT_F16.
+ */
+int dit_convert_bf16_to_f16(void* stream, const void* src, void* dst, size_t n);
 
 /* Thread-local text of the last error of this thread (never NULL). */
 const char* dit_last_error(void);

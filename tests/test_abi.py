@@ -360,3 +360,22 @@ def test_shared_mod_step_validation(dit):
     e = _no_launch(dit, lambda: dit.step_forward(s, [dict(wts, w_mod=None)], [dict(wts, w_mod=None)],
                                                  [dict(sw, w_mod=None)], cond, pos, xt, xi, y, ws, stream=FakeStream()))
     assert "txt[0].w_mod is NULL" in str(e)
+
+
+def test_gemm_weight_format_validation(dit):
+    import dit_inputs as di
+    from gpu_util import shape_of
+    cfg = di.CONFIGS[1]
+    sh = shape_of(cfg, dit)
+    base = dit.block_workspace_size(sh)
+    sh.gemm_w_dtype = dit.DIT_F16
+    assert dit.block_workspace_size(sh) == base
+    sh.act_dtype = dit.DIT_BF16            # fp16 weights need fp16 activations
+    with pytest.raises(dit.DitError) as e:
+        dit.block_workspace_size(sh)
+    assert "gemm_w_dtype" in dit.last_error()
+    cfg0 = di.CONFIGS[0]                   # fp32 block
+    sh0 = shape_of(cfg0, dit)
+    sh0.gemm_w_dtype = dit.DIT_F16
+    with pytest.raises(dit.DitError):
+        dit.block_workspace_size(sh0)
