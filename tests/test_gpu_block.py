@@ -387,3 +387,34 @@ def test_step_graph_capture_replays(dit):
         dit.step_forward(sh, wt, wi, ws_, cond, pos, xt, xi, other_y, other_ws)
         torch.cuda.synchronize()
     np.testing.assert_array_equal(host(other_y), eager)
+
+
+# ---- degenerate token mixes: one stream empty, one token per stream ----------------------------
+
+EDGE_MIXES = [(0, (4, 5)), (9, (0, 0)), (1, (1, 1))]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n_txt,grid", EDGE_MIXES, ids=["image_only", "text_only", "one_each"])
+def test_double_block_degenerate_streams(dit, dtype, n_txt, grid):
+    cfg = di.BlockConfig(f"edge_{n_txt}_{grid[0]}x{grid[1]}_{dtype}", dtype, d=256, n_heads=2, ffn_inner=768,
+                         n_txt=n_txt, grid_h=grid[0], grid_w=grid[1])
+    say(f"double block {cfg.name}")
+    inp = di.double_block_inputs(cfg, seed=4, qk_norm="random")
+    yt, yi = run_double(dit, cfg, inp)
+    ref = o.double_block(cfg, inp)
+    for name, g, r in (("y_txt", yt, ref["y_txt"]), ("y_img", yi, ref["y_img"])):
+        if r.size:
+            report(cfg, name, g, r)
+        else:
+            assert g.size == 0
+
+
+@pytest.mark.parametrize("n_txt,grid", EDGE_MIXES, ids=["image_only", "text_only", "one_each"])
+def test_single_block_degenerate_streams(dit, n_txt, grid):
+    cfg = di.BlockConfig(f"single_edge_{n_txt}_{grid[0]}x{grid[1]}", "bf16", d=256, n_heads=2, ffn_inner=768,
+                         n_txt=n_txt, grid_h=grid[0], grid_w=grid[1])
+    say(f"single block {cfg.name}")
+    inp = di.single_block_inputs(cfg, seed=4, qk_norm="random")
+    y = run_single(dit, cfg, inp)
+    report(cfg, "y", y, o.single_block(cfg, inp)["y"])

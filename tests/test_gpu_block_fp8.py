@@ -111,3 +111,22 @@ def test_fp8_block_c2_sampled_rows_bf16_out(dit):
     rt = np.unique(np.concatenate([[0, cfg.n_txt - 1], rng.choice(cfg.n_txt, 24, replace=False)]))
     ri = np.unique(np.concatenate([[0, cfg.n_img - 1], rng.choice(cfg.n_img, 40, replace=False)]))
     check(cfg, {"inp": inp, "y_txt": yt[rt], "y_img": yi[ri]}, rows_txt=rt, rows_img=ri, wide=True)
+
+
+@pytest.mark.parametrize("n_txt,grid", [(0, (4, 5)), (9, (0, 0)), (1, (1, 1))],
+                         ids=["image_only", "text_only", "one_each"])
+def test_fp8_block_degenerate_streams(dit, n_txt, grid):
+    cfg = di.BlockConfig(f"fp8_edge_{n_txt}_{grid[0]}x{grid[1]}", "bf16", d=256, n_heads=2, ffn_inner=768,
+                         n_txt=n_txt, grid_h=grid[0], grid_w=grid[1])
+    say(f"fp8 double block {cfg.name}")
+    inp = di.double_block_inputs(cfg, seed=4)
+    yt, yi = run_fp8(dit, cfg, inp)
+    ref8 = o.double_block(cfg, inp, fp8=True)
+    for s, g in (("txt", yt), ("img", yi)):
+        r = ref8["y_" + s]
+        if r.size:
+            m = metric(g, r)
+            say(f"  {cfg.name} y_{s}: fp8 oracle max {m:.3e}")
+            assert m <= BAR_FP8
+        else:
+            assert g.size == 0
