@@ -22,7 +22,8 @@ __all__ = [
     "step_workspace_size", "step_forward", "step_shared_mod_workspace_size", "step_forward_shared_mod",
     "timestep_embedding_workspace_size", "timestep_embedding", "linear",
     "final_layer_workspace_size", "final_layer", "neighborhood_attention", "quantize_fp8", "linear_fp8",
-    "StreamWeightsFp8", "block_fp8_workspace_size", "block_forward_fp8", "conv2d", "convert_bf16_to_f16",
+    "StreamWeightsFp8", "block_fp8_workspace_size", "block_forward_fp8", "SingleWeightsFp8",
+    "single_block_fp8_workspace_size", "single_block_forward_fp8", "conv2d", "convert_bf16_to_f16",
     "last_error", "launch_count", "abi_version",
     "timing_begin", "timing_end", "timing_read",
 ]
@@ -54,6 +55,10 @@ class StreamWeights(ctypes.Structure):
 
 class SingleWeights(ctypes.Structure):
     _fields_ = [("w_mod", _vp), ("w_1", _vp), ("qk_norm_w", _vp), ("w_2", _vp)]
+
+
+class SingleWeightsFp8(ctypes.Structure):
+    _fields_ = [("w_mod", _vp), ("qk_norm_w", _vp), ("w_1", _vp), ("s_1", _vp), ("w_2", _vp), ("s_2", _vp)]
 
 
 class StreamWeightsFp8(ctypes.Structure):
@@ -100,6 +105,9 @@ _block8 = _sig("dit_block_forward_fp8", _i, [ctypes.POINTER(BlockConfig), ctypes
                                              ctypes.POINTER(StreamWeightsFp8), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                              _vp])
 _cvt16 = _sig("dit_convert_bf16_to_f16", _i, [_vp, _vp, _vp, _sz])
+_swsize8 = _sig("dit_single_block_fp8_workspace_size", _sz, [ctypes.POINTER(BlockConfig)])
+_single8 = _sig("dit_single_block_forward_fp8", _i, [ctypes.POINTER(BlockConfig), ctypes.POINTER(SingleWeightsFp8),
+                                                     _vp, _vp, _vp, _vp, _vp, _sz, _vp])
 _conv = _sig("dit_conv2d", _i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp, _i])
 _last_error = _sig("dit_last_error", ctypes.c_char_p, [])
 _launch_count = _sig("dit_launch_count", ctypes.c_uint64, [])
@@ -114,6 +122,7 @@ EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", 
             "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_linear",
             "dit_final_layer_workspace_size", "dit_final_layer", "dit_neighborhood_attention",
             "dit_quantize_fp8", "dit_linear_fp8", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
+            "dit_single_block_fp8_workspace_size", "dit_single_block_forward_fp8",
             "dit_conv2d", "dit_convert_bf16_to_f16",
             "dit_last_error", "dit_launch_count",
             "dit_abi_version", "dit_timing_begin", "dit_timing_end", "dit_timing_read"]
@@ -590,6 +599,41 @@ def convert_bf16_to_f16(src, dst, stream=None) -> None:
         raise ValueError("src and dst must be contiguous tensors of the same size")
     rc = _cvt16(_stream(stream), _ptr(src, "src", torch.bfloat16), _ptr(dst, "dst", torch.float16), src.numel())
     _check(rc, "dit_convert_bf16_to_f16")
+
+
+def single_block_fp8_workspace_size(shape: Shape) -> int:
+    c = shape.c_config()
+    n = _swsize8(ctypes.byref(c))
+    if n == 0:
+        raise DitError(DIT_ERR_INVALID_ARG, "dit_single_block_fp8_workspace_size")
+    return int(n)
+
+
+def single_block_forward_fp8(shape: Shape, w: dict, cond, pos, x, y, workspace, stream=None) -> None:
+    """Single-stream block with its two weight products on e4m3 codes (see include/dit.h).  w: w_mod,
+    qk_norm_w (16-bit), w_1 / s_1 and w_2 / s_2 (uint8 codes, fp32 row scales)."""
+    import torch
+    c = shape.c_config()
+    d, F, dc, hd = shape.d, shape.ffn_inner, shape.d_cond or shape.d, shape.head_dim
+    n = shape.n_txt + shape.n_img
+    _need(w.get("w_mod"), 3 * d * dc, "w_mod")
+    _need(w.get("qk_norm_w"), 2 * hd, "qk_norm_w")
+    _need(w.get("w_1"), (3 * d + 2 * F) * d, "w_1")
+    _need(w.get("s_1"), 3 * d + 2 * F, "s_1")
+    _need(w.get("w_2"), d * (d + F), "w_2")
+    _need(w.get("s_2"), d, "s_2")
+    sw = SingleWeightsFp8()
+    sw.w_mod, sw.qk_norm_w = _ptr(w.get("w_mod"), "w_mod"), _ptr(w.get("qk_norm_w"), "qk_norm_w")
+    sw.w_1, sw.s_1 = _ptr(w.get("w_1"), "w_1", torch.uint8), _ptr(w.get("s_1"), "s_1", torch.float32)
+    sw.w_2, sw.s_2 = _ptr(w.get("w_2"), "w_2", torch.uint8), _ptr(w.get("s_2"), "s_2", torch.float32)
+    _need(cond, dc, "cond")
+    _need(pos, n * len(shape.axes_dim), "pos")
+    _need(x, n * d, "x")
+    _need(y, n * d, "y")
+    rc = _single8(ctypes.byref(c), ctypes.byref(sw), _ptr(cond, "cond"), _ptr(pos, "pos", torch.int32), _ptr(x, "x"),
+                  _ptr(y, "y"), _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                  _stream(stream))
+    _check(rc, "dit_single_block_forward_fp8")
 
 
 def conv2d(x, weight, y, bias=None, stream=None) -> None:

@@ -169,7 +169,7 @@ WsPlan plan_workspace(const dit_block_config* c, int single, bool fp8 = false) {
     p.ask = take(p.ask_bytes);
     // fp8 products: the e4m3 codes and per-row scales of the current product's activations
     if (fp8) {
-        p.q8 = take(n * std::max(d, F));
+        p.q8 = take(n * (single ? d + F : std::max(d, F)));
         p.sq = take(n * 4);
     }
     p.total = off;
@@ -608,22 +608,31 @@ int dit_block_forward_fp8(const dit_block_config* cfg, const dit_stream_weights_
 // mod_pre: the [3d] fp32 AdaLN vectors computed by the caller, or NULL (from w->w_mod and cond).
 static int single_block_impl(const dit_block_config* cfg, const dit_single_weights* w, const void* cond,
                              const int32_t* pos, const void* x, void* y, void* workspace, size_t ws_bytes,
-                             void* stream, const float* mod_pre) {
+                             void* stream, const float* mod_pre, const dit_single_weights_fp8* w8 = nullptr) {
     clear_err();
-    DIT_TRY(validate_config(cfg));
+    const bool fp8 = w8 != nullptr;
+    DIT_TRY(fp8 ? validate_fp8_config(cfg) : validate_config(cfg));
     const dit_block_config& c = *cfg;
     const int n = c.n_txt + c.n_img, d = c.d, F = c.ffn_inner;
-    if (!w) return fail(DIT_ERR_INVALID_ARG, "weights are NULL");
-    if (!mod_pre) DIT_TRY(check_ptr(w->w_mod, "w_mod"));
-    DIT_TRY(check_ptr(w->w_1, "w_1"));
-    DIT_TRY(check_ptr(w->qk_norm_w, "qk_norm_w"));
-    DIT_TRY(check_ptr(w->w_2, "w_2"));
+    if (!w && !w8) return fail(DIT_ERR_INVALID_ARG, "weights are NULL");
+    const void* w_mod = fp8 ? w8->w_mod : w->w_mod;
+    const void* w_1 = fp8 ? w8->w_1 : w->w_1;
+    const void* w_2 = fp8 ? w8->w_2 : w->w_2;
+    const void* qk_norm_w = fp8 ? w8->qk_norm_w : w->qk_norm_w;
+    if (!mod_pre) DIT_TRY(check_ptr(w_mod, "w_mod"));
+    DIT_TRY(check_ptr(w_1, "w_1"));
+    DIT_TRY(check_ptr(qk_norm_w, "qk_norm_w"));
+    DIT_TRY(check_ptr(w_2, "w_2"));
+    if (fp8) {
+        DIT_TRY(check_ptr(w8->s_1, "s_1"));
+        DIT_TRY(check_ptr(w8->s_2, "s_2"));
+    }
     if (!mod_pre) DIT_TRY(check_ptr(cond, "cond"));
     DIT_TRY(check_ptr(pos, "pos"));
     DIT_TRY(check_ptr(x, "x"));
     DIT_TRY(check_ptr(y, "y"));
     DIT_TRY(check_ptr(workspace, "workspace"));
-    const WsPlan W = plan_workspace(cfg, 1);
+    const WsPlan W = plan_workspace(cfg, 1, fp8);
     if (ws_bytes < W.total)
         return fail(DIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
     const Range rws{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + W.total};
@@ -637,13 +646,15 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
     char* act = ws + W.act;
     char* qkv = ws + W.qkv;
     char* of = ws + W.of;
+    uint8_t* q8 = fp8 ? reinterpret_cast<uint8_t*>(ws + W.q8) : nullptr;
+    float* sq = fp8 ? reinterpret_cast<float*>(ws + W.sq) : nullptr;
     const size_t es = esize(c.act_dtype);     // activation element size
     const long ldof = (long)d + F;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
     if (!mod_pre) {
         GemvBatch g{};
-        g.p[0] = {w->w_mod, mod, 3 * d};
+        g.p[0] = {w_mod, mod, 3 * d};
         g.n = 1; g.cond = cond; g.d_cond = c.d_cond; g.dtype = c.dtype;
         DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
     }
@@ -651,23 +662,47 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
     ModBatch m{};
     m.p[0] = {x, d, c.x_dtype, act, d, mod, mod + d, n};
     m.n = 1; m.d = d; m.eps = c.eps; m.out_dtype = c.act_dtype;
-    DIT_TRY(launch("modulate_x", s, [&] { return launch_modulate(m, s); }));
+    if (fp8) {
+        // a goes straight to e4m3 codes with per-row scales
+        m.p[0].out = q8; m.p[0].out_scale = sq; m.out_dtype = FP8_ROWS;
+    }
+    DIT_TRY(launch(fp8 ? "modulate_x_fp8" : "modulate_x", s, [&] { return launch_modulate(m, s); }));
 
     // [q|k|v] = a W_1[0:3d]^T  and  f = SiLU(a W_1[3d:3d+F]^T) * (a W_1[3d+F:]^T), written next to O
-    GemmBatch g1{};
-    g1.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
-    g1.a_dtype = c.act_dtype;
-    g1.b_f16 = c.gemm_w_dtype == DIT_F16;
-    g1.p[0] = {act, d, w->w_1, d, qkv, 3L * d, c.act_dtype, nullptr, 0, 0, nullptr, 0, n, 3 * d, d, EPI_STORE};
-    g1.p[1] = {act, d, reinterpret_cast<const char*>(w->w_1) + (size_t)3 * d * d * esize(c.dtype), d,
-               of + (size_t)d * es, ldof, c.act_dtype, nullptr, 0, 0, nullptr, F, n, F, d, EPI_SWIGLU};
-    g1.n = 2;
-    DIT_TRY(launch("gemm_linear1", s, [&] { return launch_gemm(g1, s); }));
+    if (fp8) {
+        auto prob = [&](const void* wq, const float* sw, void* out, long ldc, int N, int epi) {
+            Fp8GemmProblem P{};
+            P.a = q8; P.lda = d; P.sa = sq;
+            P.b = reinterpret_cast<const uint8_t*>(wq); P.ldb = d; P.sb = sw;
+            P.c = out; P.ldc = ldc; P.c_dtype = c.act_dtype;
+            P.M = n; P.N = N; P.K = d; P.epi = epi;
+            return P;
+        };
+        Fp8GemmBatch bq{}, bg{};
+        bq.p[0] = prob(w_1, w8->s_1, qkv, 3L * d, 3 * d, EPI_STORE);
+        bq.n = 1;
+        bg.p[0] = prob(reinterpret_cast<const uint8_t*>(w_1) + (size_t)3 * d * d, w8->s_1 + 3 * (size_t)d,
+                       of + (size_t)d * es, ldof, F, EPI_SWIGLU);
+        bg.p[0].up_off = F;
+        bg.n = 1;
+        DIT_TRY(launch("gemm_fp8_linear1_qkv", s, [&] { return launch_gemm_fp8(bq, s); }));
+        DIT_TRY(launch("gemm_fp8_linear1_gu", s, [&] { return launch_gemm_fp8(bg, s); }));
+    } else {
+        GemmBatch g1{};
+        g1.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
+        g1.a_dtype = c.act_dtype;
+        g1.b_f16 = c.gemm_w_dtype == DIT_F16;
+        g1.p[0] = {act, d, w_1, d, qkv, 3L * d, c.act_dtype, nullptr, 0, 0, nullptr, 0, n, 3 * d, d, EPI_STORE};
+        g1.p[1] = {act, d, reinterpret_cast<const char*>(w_1) + (size_t)3 * d * d * esize(c.dtype), d,
+                   of + (size_t)d * es, ldof, c.act_dtype, nullptr, 0, 0, nullptr, F, n, F, d, EPI_SWIGLU};
+        g1.n = 2;
+        DIT_TRY(launch("gemm_linear1", s, [&] { return launch_gemm(g1, s); }));
+    }
 
     QkRopeArgs r{};
     DIT_TRY(build_rope_table(c.head_dim, c.n_axes, c.axes_dim, c.theta, r.tab));
     r.q = qkv; r.ld_q = 3L * d; r.k = qkv + (size_t)d * es; r.ld_k = 3L * d;
-    r.n_tok = n; r.n_heads = c.n_heads; r.qk_w0 = w->qk_norm_w; r.qk_w1 = w->qk_norm_w; r.n_first = n;
+    r.n_tok = n; r.n_heads = c.n_heads; r.qk_w0 = qk_norm_w; r.qk_w1 = qk_norm_w; r.n_first = n;
     r.eps = c.eps_qk;
     r.pos = pos; r.n_axes = c.n_axes; r.dtype = c.act_dtype; r.w_dtype = c.dtype;
     DIT_TRY(launch("qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(r, s); }));
@@ -677,11 +712,26 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
     at.sk_scratch = W.ask_bytes ? ws + W.ask : nullptr;
     DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
 
+    if (fp8) {
+        DIT_TRY(launch("quantize_of", s, [&] {
+            return launch_quantize_fp8(of, c.act_dtype, ldof, n, d + F, q8, ldof, sq, s);
+        }));
+        Fp8GemmBatch b2{};
+        Fp8GemmProblem& P = b2.p[0];
+        P.a = q8; P.lda = ldof; P.sa = sq;
+        P.b = reinterpret_cast<const uint8_t*>(w_2); P.ldb = ldof; P.sb = w8->s_2;
+        P.c = y; P.ldc = d; P.c_dtype = c.y_dtype;
+        P.r = x; P.ldr = d; P.r_dtype = c.x_dtype; P.gate = mod + 2 * (size_t)d;
+        P.M = n; P.N = d; P.K = d + F; P.epi = EPI_GATED_RES;
+        b2.n = 1;
+        DIT_TRY(launch("gemm_fp8_linear2", s, [&] { return launch_gemm_fp8(b2, s); }));
+        return DIT_OK;
+    }
     GemmBatch g2{};
     g2.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     g2.a_dtype = c.act_dtype;
     g2.b_f16 = c.gemm_w_dtype == DIT_F16;
-    g2.p[0] = {of, ldof, w->w_2, ldof, y, d, c.y_dtype, x, d, c.x_dtype, mod + 2 * (size_t)d, 0, n, d, d + F,
+    g2.p[0] = {of, ldof, w_2, ldof, y, d, c.y_dtype, x, d, c.x_dtype, mod + 2 * (size_t)d, 0, n, d, d + F,
                EPI_GATED_RES};
     g2.n = 1;
     DIT_TRY(launch("gemm_linear2", s, [&] { return launch_gemm(g2, s); }));
@@ -692,6 +742,22 @@ int dit_single_block_forward(const dit_block_config* cfg, const dit_single_weigh
                              const int32_t* pos, const void* x, void* y, void* workspace, size_t ws_bytes,
                              void* stream) {
     return single_block_impl(cfg, w, cond, pos, x, y, workspace, ws_bytes, stream, nullptr);
+}
+
+size_t dit_single_block_fp8_workspace_size(const dit_block_config* cfg) {
+    clear_err();
+    if (validate_fp8_config(cfg) != DIT_OK) return 0;
+    return plan_workspace(cfg, 1, true).total;
+}
+
+int dit_single_block_forward_fp8(const dit_block_config* cfg, const dit_single_weights_fp8* w, const void* cond,
+                                 const int32_t* pos, const void* x, void* y, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+    if (!w) {
+        clear_err();
+        return fail(DIT_ERR_INVALID_ARG, "fp8 weights are NULL");
+    }
+    return single_block_impl(cfg, nullptr, cond, pos, x, y, workspace, ws_bytes, stream, nullptr, w);
 }
 
 // ---- kernel timing --------------------------------------------------------------------------

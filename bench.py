@@ -334,12 +334,14 @@ def measured_traffic(workload, kernel, act):
 
 
 def fp8_block_bench(args, cfg, dit, torch):
-    """One fp8 double-stream block (dit_block_forward_fp8) on the workload's seeded inputs: the four
-    weight matrices of each stream quantised once to e4m3 before timing (a weight format, like the
-    bf16 storage of the others), the activations quantised inside every step.  Times K steps like
-    the main bench and every launch with the library's HIP events."""
-    if cfg.n_double != 1 or cfg.n_single != 0 or cfg.dtype != "bf16":
-        print("--fp8-block needs a one-double-block bf16 workload", file=sys.stderr)
+    """The workload's blocks with their weight products on e4m3 codes (dit_block_forward_fp8,
+    dit_single_block_forward_fp8): the weight matrices quantised once to e4m3 before timing (a
+    weight format, like the bf16 storage of the others), the activations quantised inside every
+    step.  One double block for the one-block workloads; the whole step (double blocks on the text
+    and image streams, then single blocks over [text; image], one fp32 residual stream) otherwise.
+    Times K steps like the main bench and every launch with the library's HIP events."""
+    if cfg.dtype != "bf16":
+        print("--fp8-block needs a bf16 workload", file=sys.stderr)
         sys.exit(2)
     import dit_inputs as di
     dev = torch.device("cuda:0")
@@ -350,29 +352,49 @@ def fp8_block_bench(args, cfg, dit, torch):
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    inp = di.double_block_inputs(cfg, seed=args.seed)
-    ws8 = {}
-    for s in ("txt", "img"):
-        w = {"w_mod": up(inp[s]["w_mod"], "bf16"), "qk_norm_w": up(inp[s]["qk_norm_w"], "bf16")}
-        for name in ("qkv", "o", "ffn_in", "ffn_out"):
-            wt = up(inp[s]["w_" + name], "bf16")
+    def quantised(w, names):
+        out = {"w_mod": up(w["w_mod"], "bf16"), "qk_norm_w": up(w["qk_norm_w"], "bf16")}
+        for name, sname in names:
+            wt = up(w[name], "bf16")
             q = torch.empty(wt.shape, dtype=torch.uint8, device=dev)
             sc = torch.empty(wt.shape[0], dtype=torch.float32, device=dev)
             dit.quantize_fp8(wt, q, sc)
-            w["w_" + name], w["s_" + name] = q, sc
+            out[name], out[sname] = q, sc
             del wt
-        ws8[s] = w
-    shape = dit.Shape(dtype=dit.DIT_BF16, d=cfg.d, n_heads=cfg.n_heads, ffn_inner=cfg.ffn_inner, n_txt=cfg.n_txt,
-                      n_img=cfg.n_img, d_cond=cfg.dc, x_dtype=dit.DIT_BF16, y_dtype=dit.DIT_F32,
-                      act_dtype=dit.DIT_F16)
-    ws = torch.empty(dit.block_fp8_workspace_size(shape), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        return out
+
+    dnames = [("w_qkv", "s_qkv"), ("w_o", "s_o"), ("w_ffn_in", "s_ffn_in"), ("w_ffn_out", "s_ffn_out")]
+    inp = di.double_block_inputs(cfg, seed=args.seed)
     cond, pos = up(inp["cond"], "bf16"), up(inp["pos"], "i32")
     x_txt, x_img = up(inp["x_txt"], "bf16"), up(inp["x_img"], "bf16")
-    y_txt = torch.empty(cfg.n_txt, cfg.d, dtype=torch.float32, device=dev)
-    y_img = torch.empty(cfg.n_img, cfg.d, dtype=torch.float32, device=dev)
+    kw = dict(d=cfg.d, n_heads=cfg.n_heads, ffn_inner=cfg.ffn_inner, n_txt=cfg.n_txt, n_img=cfg.n_img,
+              d_cond=cfg.dc, y_dtype=dit.DIT_F32, act_dtype=dit.DIT_F16)
+    sh_in = dit.Shape(dtype=dit.DIT_BF16, x_dtype=dit.DIT_BF16, **kw)       # first block: bf16 input
+    sh_st = dit.Shape(dtype=dit.DIT_BF16, x_dtype=dit.DIT_F32, **kw)        # later blocks: fp32 stream
+    ws = torch.empty(max(dit.block_fp8_workspace_size(sh_in), dit.single_block_fp8_workspace_size(sh_st)),
+                     dtype=torch.uint8, device=dev)
+    state = torch.empty(cfg.n_tok, cfg.d, dtype=torch.float32, device=dev)
+    st_txt, st_img = state[:cfg.n_txt], state[cfg.n_txt:]
+    calls = []
+    for b in range(cfg.n_double):
+        print(f"setup: fp8 double block {b + 1}/{cfg.n_double}", file=sys.stderr, flush=True)
+        bi = inp if b == 0 else di.double_block_inputs(cfg, seed=args.seed, block=b)
+        wt, wi = quantised(bi["txt"], dnames), quantised(bi["img"], dnames)
+        if b == 0:
+            calls.append(lambda wt=wt, wi=wi: dit.block_forward_fp8(sh_in, wt, wi, cond, pos, x_txt, x_img, st_txt,
+                                                                     st_img, ws))
+        else:
+            calls.append(lambda wt=wt, wi=wi: dit.block_forward_fp8(sh_st, wt, wi, cond, pos, st_txt, st_img, st_txt,
+                                                                     st_img, ws))
+    for b in range(cfg.n_single):
+        print(f"setup: fp8 single block {b + 1}/{cfg.n_single}", file=sys.stderr, flush=True)
+        w = quantised(di.single_weights(cfg, args.seed, cfg.n_double + b), [("w_1", "s_1"), ("w_2", "s_2")])
+        calls.append(lambda w=w: dit.single_block_forward_fp8(sh_st, w, cond, pos, state, state, ws))
 
     def step():
-        dit.block_forward_fp8(shape, ws8["txt"], ws8["img"], cond, pos, x_txt, x_img, y_txt, y_img, ws)
+        for f in calls:
+            f()
 
     for _ in range(args.warmup):
         step()
@@ -382,7 +404,7 @@ def fp8_block_bench(args, cfg, dit, torch):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    dit.timing_begin(args.steps * 16)
+    dit.timing_begin(args.steps * 16 * len(calls))
     for _ in range(args.steps):
         step()
     dit.timing_end()
@@ -390,13 +412,16 @@ def fp8_block_bench(args, cfg, dit, torch):
     kt = dit.timing_read()
     n, d, F = cfg.n_tok, cfg.d, cfg.ffn_inner
     gemm = {"gemm_fp8_qkv": 6.0 * n * d * d, "gemm_fp8_out_proj": 2.0 * n * d * d,
-            "gemm_fp8_ffn_in_swiglu": 4.0 * n * d * F, "gemm_fp8_ffn_down": 2.0 * n * F * d}
-    quant = {"quantize_o": n * d * 3.0, "quantize_f": n * F * 3.0,          # fp16 read + code written
-             "modulate_x_fp8": n * d * 3.0, "modulate_h_fp8": n * d * 5.0}  # bf16 / fp32 read + code written
+            "gemm_fp8_ffn_in_swiglu": 4.0 * n * d * F, "gemm_fp8_ffn_down": 2.0 * n * F * d,
+            "gemm_fp8_linear1_qkv": 6.0 * n * d * d, "gemm_fp8_linear1_gu": 4.0 * n * d * F,
+            "gemm_fp8_linear2": 2.0 * n * (d + F) * d}
+    quant = {"quantize_o": n * d * 3.0, "quantize_f": n * F * 3.0, "quantize_of": n * (d + F) * 3.0,
+             "modulate_h_fp8": n * d * 5.0}              # 16-bit / fp32 read + code written
     kernels = {}
     for name, (cnt, tot) in kt.items():
         avg = tot / cnt
-        e = {"avg_ms": round(avg, 5), "share": round(tot / sum(v[1] for v in kt.values()), 4)}
+        e = {"launches_per_step": cnt / args.steps, "avg_ms": round(avg, 5),
+             "share": round(tot / sum(v[1] for v in kt.values()), 4)}
         if name in gemm:
             e["tflops"] = round(gemm[name] / (avg * 1e-3) / 1e12, 1)
             e["frac_fp8_peak"] = round(e["tflops"] / 5000.0, 4)
@@ -409,7 +434,8 @@ def fp8_block_bench(args, cfg, dit, torch):
            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3+f16",
            "data": "synthetic",
-           "config": {"workload": cfg.name, "tokens": cfg.n_tok, "gflop_per_step": round(flops / 1e9, 1),
+           "config": {"workload": cfg.name, "blocks": cfg.n_double + cfg.n_single, "tokens": cfg.n_tok,
+                      "gflop_per_step": round(flops / 1e9, 1),
                       "products": "e4m3 weights (per-row scales, quantised once) x e4m3 activations (per row, "
                                   "every step)"},
            "kernels": kernels}

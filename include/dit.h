@@ -443,6 +443,32 @@ typedef struct dit_stream_weights_fp8 {
     const float* s_ffn_out;     /* [d] */
 } dit_stream_weights_fp8;
 
+/* fp8 weights of a single-stream block: w_1 codes [3d + 2F, d] (rows q | k | v | gate | up) with
+ * [3d + 2F] row scales, w_2 codes [d, d + F] with [d] row scales; w_mod and qk_norm_w of dtype. */
+typedef struct dit_single_weights_fp8 {
+    const void* w_mod;          /* [3d, d_cond] of dtype: shift, scale, gate */
+    const void* qk_norm_w;      /* [2][head_dim] of dtype */
+    const void* w_1;            /* [3d + 2F, d] e4m3 codes */
+    const float* s_1;           /* [3d + 2F] */
+    const void* w_2;            /* [d, d + F] e4m3 codes (row stride d + F) */
+    const float* s_2;           /* [d] */
+} dit_single_weights_fp8;
+
+/* Workspace bytes of dit_single_block_forward_fp8; 0 for an invalid config. */
+size_t dit_single_block_fp8_workspace_size(const dit_block_config* cfg);
+
+/*
+ * fp8 single-stream block: dit_single_block_forward with its two weight products on e4m3 codes:
+ * a is quantised per row inside the modulation kernel, [O | f] per row (width d + F) by a
+ * separate pass; W_1 and W_2 come quantised per output row.  Arguments, aliasing and errors as for
+ * dit_single_block_forward; cfg as for dit_block_forward_fp8.  Launches (8): GEMV, modulate x (to
+ * e4m3), linear1 q|k|v, linear1 gate|up (SwiGLU), QK-norm + RoPE, attention, quantise [O | f],
+ * linear2.
+ */
+int dit_single_block_forward_fp8(const dit_block_config* cfg, const dit_single_weights_fp8* w,
+                                 const void* cond, const int32_t* pos, const void* x, void* y,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
 /* Workspace bytes of dit_block_forward_fp8; 0 for an invalid config. */
 size_t dit_block_fp8_workspace_size(const dit_block_config* cfg);
 

@@ -272,7 +272,7 @@ def double_block(cfg, inputs: Dict[str, object], rows_txt=None, rows_img=None,
 
 
 def single_block(cfg, inputs: Dict[str, object], rows=None, mods=None,
-                 keep: bool = False) -> Dict[str, np.ndarray]:
+                 keep: bool = False, fp8: bool = False) -> Dict[str, np.ndarray]:
     """Single-stream block over the concatenated sequence x = [text; image]:
 
     m = W_mod . SiLU(c) -> shift, scale, gate
@@ -281,7 +281,9 @@ def single_block(cfg, inputs: Dict[str, object], rows=None, mods=None,
     q, k <- RMSNorm per head * w ; RoPE ; O = joint attention
     y = x + gate * ([O | SiLU(g) * u] W_2^T)
 
-    Exact float64 arithmetic as in ``double_block``; x is read in ``x_dtype``."""
+    Exact float64 arithmetic as in ``double_block``; x is read in ``x_dtype``.  ``fp8``
+    quantises both operands of the two weight products (W_1 per output row, each activation row
+    over its full width) to e4m3, as ``double_block(fp8=True)`` does."""
     t = cfg.dtype
     d, H, D, F = cfg.d, cfg.n_heads, cfg.head_dim, cfg.ffn_inner
     n = cfg.n_tok
@@ -295,15 +297,15 @@ def single_block(cfg, inputs: Dict[str, object], rows=None, mods=None,
         m = adaln_modulation(_w(ws, "w_mod", t), cond).reshape(3, d)
     a = modulate(x, m[0], m[1], cfg.eps)
     w1 = _w(ws, "w_1", t)
-    qkv = a @ w1[:3 * d].T
+    qkv = _product(a, w1[:3 * d], fp8)
     q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
     qk_w = widen(ws["qk_norm_w"], t).reshape(1, 2, D)
     q, k = qk_rmsnorm_rope(q, k, H, D, qk_w, n, cfg.eps_qk, pos, cfg.axes_dim, cfg.theta)
     r = np.arange(n) if rows is None else np.asarray(rows)
     o = joint_attention(q, k, v, H, D, q_rows=r)
-    gu = a[r] @ w1[3 * d:].T
+    gu = _product(a[r], w1[3 * d:], fp8)
     f = swiglu(gu[:, :F], gu[:, F:])
-    y = x[r] + m[2] * (np.concatenate([o, f], axis=1) @ _w(ws, "w_2", t).T)
+    y = x[r] + m[2] * _product(np.concatenate([o, f], axis=1), _w(ws, "w_2", t), fp8)
     out = {"y": y}
     if keep:
         out.update({"mod": m, "q": q, "k": k, "v": v, "o": o, "f": f, "a": a})

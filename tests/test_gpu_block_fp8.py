@@ -130,3 +130,56 @@ def test_fp8_block_degenerate_streams(dit, n_txt, grid):
             assert m <= BAR_FP8
         else:
             assert g.size == 0
+
+
+# ---- the single-stream block ---------------------------------------------------------------------
+
+def run_single_fp8(dit, cfg, inp):
+    sh = shape_of(cfg, dit)
+    ws = torch.empty(dit.single_block_fp8_workspace_size(sh), dtype=torch.uint8, device="cuda")
+    y = torch.empty(cfg.n_tok, cfg.d, dtype=torch.float32, device="cuda")
+    w = inp["w"]
+    wd = {"w_mod": dev(w["w_mod"], "bf16"), "qk_norm_w": dev(w["qk_norm_w"], "bf16")}
+    for name, sname in (("w_1", "s_1"), ("w_2", "s_2")):
+        wt = dev(w[name], "bf16")
+        q = torch.empty(wt.shape, dtype=torch.uint8, device="cuda")
+        s = torch.empty(wt.shape[0], dtype=torch.float32, device="cuda")
+        dit.quantize_fp8(wt, q, s)
+        wd[name], wd[sname] = q, s
+    before = dit.launch_count()
+    dit.single_block_forward_fp8(sh, wd, dev(inp["cond"], "bf16"), dev(inp["pos"], "i32"), dev(inp["x"], "bf16"), y,
+                                 ws)
+    torch.cuda.synchronize()
+    assert dit.launch_count() == before + 8
+    return host(y)
+
+
+def check_single(cfg, inp, y, rows=None, bar=None, wide=False):
+    ref8 = o.single_block(cfg, inp, rows=rows, fp8=True)["y"]
+    ref = o.single_block(cfg, inp, rows=rows)["y"]
+    m8, e8 = metric(y, ref8), rms_rel(ref8, ref)
+    say(f"  {cfg.name} y: fp8 oracle max {m8:.3e} rms {rms_rel(y, ref8):.3e}; exact oracle rms {rms_rel(y, ref):.3e}; "
+        f"oracle fp8 vs exact rms {e8:.3e}")
+    if bar is not None:
+        assert m8 <= bar
+    if wide:
+        assert rms_rel(y, ref) <= 1.05 * e8
+        assert rms_rel(y, ref8) <= 0.7 * e8
+
+
+@pytest.mark.parametrize("n_txt,grid", [(16, (8, 8)), (0, (4, 5)), (1, (1, 1))], ids=["small", "image_only", "one_each"])
+def test_fp8_single_block_small(dit, n_txt, grid):
+    cfg = di.BlockConfig(f"fp8_single_{n_txt}_{grid[0]}x{grid[1]}", "bf16", d=256, n_heads=2, ffn_inner=768,
+                         n_txt=n_txt, grid_h=grid[0], grid_w=grid[1])
+    say(f"fp8 single block {cfg.name}")
+    inp = di.single_block_inputs(cfg, seed=7, qk_norm="random")
+    check_single(cfg, inp, run_single_fp8(dit, cfg, inp), bar=BAR_FP8)
+
+
+def test_fp8_single_block_c3_shape_sampled(dit):
+    cfg = di.CONFIGS[3]
+    say(f"fp8 single block at {cfg.name} shape (sampled rows)")
+    inp = di.single_block_inputs(cfg, seed=0)
+    y = run_single_fp8(dit, cfg, inp)
+    rows = np.unique(np.concatenate([[0, cfg.n_tok - 1], np.random.default_rng(9).choice(cfg.n_tok, 64, replace=False)]))
+    check_single(cfg, inp, y[rows], rows=rows, wide=True)
