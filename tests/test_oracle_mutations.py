@@ -1,5 +1,5 @@
 """Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
-the pins in ``test_oracle_pins.py`` catch every one of them.
+the pins in ``test_oracle_pins.py`` and ``test_oracle_fp8.py`` catch every one of them.
 
 Each mutant is a textual edit of ``oracle/dit_oracle.py``, executed as a
 separate module; the pin tests are then run against that module.  A mutant
@@ -12,7 +12,10 @@ import types
 import pytest
 
 from oracle import dit_oracle
+import test_oracle_fp8 as fp8_pins
 import test_oracle_pins as pins
+
+PIN_MODULES = (pins, fp8_pins)
 
 SRC_PATH = dit_oracle.__file__
 
@@ -41,7 +44,8 @@ MUTANTS = {
     "qk_sets_swapped": ("np.where(np.arange(n) < n_first, 0, min(1, w.shape[0] - 1))",
                         "np.where(np.arange(n) < n_first, min(1, w.shape[0] - 1), 0)"),
     "qk_weights_swapped": ("for which, t in ((0, q), (1, k)):", "for which, t in ((1, q), (0, k)):"),
-    "single_ffn_rows": ("gu = a[r] @ w1[3 * d:].T", "gu = a[r] @ w1[2 * d:2 * d + 2 * F].T"),
+    "single_ffn_rows": ("gu = _product(a[r], w1[3 * d:], fp8)", "gu = _product(a[r], w1[2 * d:2 * d + 2 * F], fp8)"),
+    "fp8_product_drops_weight_scales": ("return linear_fp8(xq, sx, wq, sw)", "return linear_fp8(xq, sx, wq, np.ones_like(sw))"),
     "single_o_f_order": ("np.concatenate([o, f], axis=1)", "np.concatenate([f, o], axis=1)"),
     "v_from_k_block": ('v = np.concatenate([qkv["txt"][:, 2 * d:], qkv["img"][:, 2 * d:]], axis=0)',
                        'v = np.concatenate([qkv["txt"][:, d:2 * d], qkv["img"][:, d:2 * d]], axis=0)'),
@@ -54,17 +58,19 @@ MUTANTS = {
 
 def _pin_tests():
     out = []
-    for name, fn in inspect.getmembers(pins, inspect.isfunction):
-        if name.startswith("test_"):
-            out.append((name, fn))
+    for mod in PIN_MODULES:
+        for name, fn in inspect.getmembers(mod, inspect.isfunction):
+            if name.startswith("test_") and fn.__module__ == mod.__name__:
+                out.append((f"{mod.__name__}.{name}", fn))
     return out
 
 
 def _run_pins(module):
     """Run every pin against ``module``; return the names of the failing pins."""
     failed = []
-    saved = pins.o
-    pins.o = module
+    saved = [m.o for m in PIN_MODULES]
+    for m in PIN_MODULES:
+        m.o = module
     try:
         cfg = pins.tiny_cfg()
         fixture_val = (cfg, pins.di.double_block_inputs(cfg, seed=3, qk_norm="random"))
@@ -78,7 +84,8 @@ def _run_pins(module):
             except Exception:       # a mutant may also break shapes: that counts as caught
                 failed.append(name)
     finally:
-        pins.o = saved
+        for m, o in zip(PIN_MODULES, saved):
+            m.o = o
     return failed
 
 
