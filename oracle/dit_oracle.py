@@ -488,3 +488,26 @@ def conv2d_nhwc(x: np.ndarray, w: np.ndarray, bias=None) -> np.ndarray:
     if bias is not None:
         y += np.asarray(bias, F64)
     return y
+
+
+def conv3d_causal_nhwc(x: np.ndarray, w: np.ndarray, bias=None) -> np.ndarray:
+    """Causal 3-D convolution over video frames (the video-VAE decoder's layers):
+    y[b, t, h, w, co] = bias[co] + sum_{s, i, j, ci} x[b, t + s - (KT-1), h + i - KH//2, w + j - KW//2, ci]
+                                                    W[co, s, i, j, ci],
+    x [B, T, H, W, Cin], W [Cout, KT, KH, KW, Cin]; frames before the first and pixels outside the
+    image are zeros, so output frame t sees frames t-KT+1 .. t only and keeps the input's size."""
+    x = np.asarray(x, F64)
+    w = np.asarray(w, F64)
+    B, T, H, W_, Cin = x.shape
+    Cout, KT, KH, KW, _ = w.shape
+    pt, ph, pw = KT - 1, KH // 2, KW // 2
+    xp = np.zeros((B, T + pt, H + 2 * ph, W_ + 2 * pw, Cin), F64)
+    xp[:, pt:, ph:ph + H, pw:pw + W_, :] = x
+    y = np.zeros((B, T, H, W_, Cout), F64)
+    for s_ in range(KT):
+        for i in range(KH):
+            for j in range(KW):
+                y += xp[:, s_:s_ + T, i:i + H, j:j + W_, :] @ w[:, s_, i, j, :].T
+    if bias is not None:
+        y += np.asarray(bias, F64)
+    return y
