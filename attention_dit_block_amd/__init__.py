@@ -23,7 +23,8 @@ __all__ = [
     "timestep_embedding_workspace_size", "timestep_embedding", "linear",
     "final_layer_workspace_size", "final_layer", "neighborhood_attention", "quantize_fp8", "linear_fp8",
     "StreamWeightsFp8", "block_fp8_workspace_size", "block_forward_fp8", "SingleWeightsFp8",
-    "single_block_fp8_workspace_size", "single_block_forward_fp8", "conv2d", "convert_bf16_to_f16",
+    "single_block_fp8_workspace_size", "single_block_forward_fp8", "conv2d", "conv3d_causal",
+    "convert_bf16_to_f16",
     "last_error", "launch_count", "abi_version",
     "timing_begin", "timing_end", "timing_read",
 ]
@@ -105,6 +106,7 @@ _block8 = _sig("dit_block_forward_fp8", _i, [ctypes.POINTER(BlockConfig), ctypes
                                              ctypes.POINTER(StreamWeightsFp8), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                              _vp])
 _cvt16 = _sig("dit_convert_bf16_to_f16", _i, [_vp, _vp, _vp, _sz])
+_conv3 = _sig("dit_conv3d_causal", _i, [_i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _vp, _vp, _i])
 _swsize8 = _sig("dit_single_block_fp8_workspace_size", _sz, [ctypes.POINTER(BlockConfig)])
 _single8 = _sig("dit_single_block_forward_fp8", _i, [ctypes.POINTER(BlockConfig), ctypes.POINTER(SingleWeightsFp8),
                                                      _vp, _vp, _vp, _vp, _vp, _sz, _vp])
@@ -123,7 +125,7 @@ EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", 
             "dit_final_layer_workspace_size", "dit_final_layer", "dit_neighborhood_attention",
             "dit_quantize_fp8", "dit_linear_fp8", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
             "dit_single_block_fp8_workspace_size", "dit_single_block_forward_fp8",
-            "dit_conv2d", "dit_convert_bf16_to_f16",
+            "dit_conv2d", "dit_conv3d_causal", "dit_convert_bf16_to_f16",
             "dit_last_error", "dit_launch_count",
             "dit_abi_version", "dit_timing_begin", "dit_timing_end", "dit_timing_read"]
 
@@ -677,3 +679,21 @@ def timing_read() -> dict:
         _tread(i, buf, 128, ctypes.byref(cnt), ctypes.byref(ms))
         out[buf.value.decode()] = (cnt.value, ms.value)
     return out
+
+
+def conv3d_causal(x, weight, y, bias=None, stream=None) -> None:
+    """Causal 3-D convolution over frames: x [B, T, H, W, Cin], weight [Cout, KT, KH, KW, Cin],
+    y [B, T, H, W, Cout] (see include/dit.h)."""
+    import torch
+    B, T, H, W, cin = x.shape
+    cout, kt, kh, kw, cin2 = weight.shape
+    if cin2 != cin or tuple(y.shape) != (B, T, H, W, cout):
+        raise ValueError("shape mismatch between x, weight and y")
+    for t, what in ((x, "x"), (weight, "weight"), (y, "y")):
+        if not t.is_contiguous():
+            raise ValueError(f"{what} must be contiguous")
+    if bias is not None:
+        _need(bias, cout, "bias")
+    rc = _conv3(_dt(x), _stream(stream), _ptr(x, "x"), B, T, H, W, cin, _ptr(weight, "weight"), cout, kt, kh, kw,
+                _ptr(bias, "bias", torch.float32), _ptr(y, "y"), _dt(y))
+    _check(rc, "dit_conv3d_causal")

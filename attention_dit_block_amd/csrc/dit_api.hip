@@ -1236,18 +1236,22 @@ int dit_linear_fp8(void* stream, const void* xq, long ld_x, const float* sx, con
 // =========================================================================================
 // 2-D convolution (NHWC), implicit GEMM.
 // =========================================================================================
-int dit_conv2d(int dtype, void* stream, const void* x, int batch, int height, int width, int c_in, const void* weight,
-               int c_out, int kh, int kw, const float* bias, void* y, int y_dtype) {
+static int conv_impl(const char* name, int dtype, void* stream, const void* x, int batch, int frames, int height,
+                     int width, int c_in, const void* weight, int c_out, int kt, int kh, int kw, const float* bias,
+                     void* y, int y_dtype) {
     clear_err();
     if (dtype != DIT_BF16) return fail(DIT_ERR_UNSUPPORTED, "dtype must be DIT_BF16 (x and weight)");
     if (y_dtype != DIT_BF16 && y_dtype != DIT_F32) return fail(DIT_ERR_INVALID_ARG, "y_dtype must be DIT_BF16 or DIT_F32");
-    if (batch < 0 || height < 1 || width < 1) return fail(DIT_ERR_INVALID_ARG, "batch = %d, %d x %d", batch, height, width);
+    if (batch < 0 || frames < 1 || height < 1 || width < 1)
+        return fail(DIT_ERR_INVALID_ARG, "batch = %d, %d frames of %d x %d", batch, frames, height, width);
     if (c_in < 64 || c_in % 64) return fail(DIT_ERR_UNSUPPORTED, "c_in = %d must be a positive multiple of 64", c_in);
     if (c_out < 8 || c_out % 8) return fail(DIT_ERR_UNSUPPORTED, "c_out = %d must be a positive multiple of 8", c_out);
     if (kh < 1 || kw < 1 || kh % 2 == 0 || kw % 2 == 0 || kh > 7 || kw > 7)
         return fail(DIT_ERR_UNSUPPORTED, "kernel %d x %d: odd sizes up to 7", kh, kw);
-    const long M = (long)batch * height * width;
-    if (M * c_in > (1L << 31) || M * c_out > (1L << 31) || (long)c_out * kh * kw * c_in > (1L << 31))
+    if (kt < 1 || kt > 7) return fail(DIT_ERR_UNSUPPORTED, "temporal kernel %d: 1 to 7 frames", kt);
+    const long M = (long)batch * frames * height * width;
+    const long K = (long)kt * kh * kw * c_in;
+    if (M * c_in > (1L << 31) || M * c_out > (1L << 31) || (long)c_out * K > (1L << 31))
         return fail(DIT_ERR_UNSUPPORTED, "tensor too large");
     DIT_TRY(check_ptr(weight, "weight"));
     if (bias) DIT_TRY(check_ptr(bias, "bias"));
@@ -1255,13 +1259,25 @@ int dit_conv2d(int dtype, void* stream, const void* x, int batch, int height, in
     DIT_TRY(check_ptr(x, "x"));
     DIT_TRY(check_ptr(y, "y"));
     const Range ry = range_of(y, M, c_out, c_out, y_dtype);
-    if (overlap(ry, range_of(x, M, c_in, c_in, dtype)) ||
-        overlap(ry, range_of(weight, c_out, (long)kh * kw * c_in, (long)kh * kw * c_in, dtype)) ||
+    if (overlap(ry, range_of(x, M, c_in, c_in, dtype)) || overlap(ry, range_of(weight, c_out, K, K, dtype)) ||
         (bias && overlap(ry, range_of(bias, 1, c_out, c_out, DIT_F32))))
         return fail(DIT_ERR_INVALID_ARG, "y overlaps an input");
     ConvArgs a{};
     a.x = x; a.w = weight; a.bias = bias; a.y = y; a.y_dtype = y_dtype;
     a.B = batch; a.H = height; a.W = width; a.Cin = c_in; a.Cout = c_out; a.KH = kh; a.KW = kw;
+    a.T = frames; a.KT = kt;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    return launch("conv2d", s, [&] { return launch_conv2d(a, s); });
+    return launch(name, s, [&] { return launch_conv2d(a, s); });
+}
+
+int dit_conv2d(int dtype, void* stream, const void* x, int batch, int height, int width, int c_in, const void* weight,
+               int c_out, int kh, int kw, const float* bias, void* y, int y_dtype) {
+    return conv_impl("conv2d", dtype, stream, x, batch, 1, height, width, c_in, weight, c_out, 1, kh, kw, bias, y,
+                     y_dtype);
+}
+
+int dit_conv3d_causal(int dtype, void* stream, const void* x, int batch, int frames, int height, int width, int c_in,
+                      const void* weight, int c_out, int kt, int kh, int kw, const float* bias, void* y, int y_dtype) {
+    return conv_impl("conv3d_causal", dtype, stream, x, batch, frames, height, width, c_in, weight, c_out, kt, kh, kw,
+                     bias, y, y_dtype);
 }

@@ -1,12 +1,15 @@
-// 2-D convolution of the diffusion-VAE decoder (the second stage of the pipeline; the decoder page
-// measures its convolutions at length) on gfx950 as an implicit GEMM: no column buffer is
-// materialised -- the page's point against im2col -- each k-step stages 64 input channels of one
-// kernel tap for 256 output pixels straight from the NHWC input.
+// 2-D and causal 3-D convolutions of the diffusion-VAE decoder (the second stage of the pipeline;
+// the decoder page measures its convolutions at length, those of a video VAE with causal 3-D
+// kernels) on gfx950 as an implicit GEMM: no column buffer is materialised -- the page's point
+// against im2col -- each k-step stages 64 input channels of one kernel tap for 256 output pixels
+// straight from the channels-last input.
 //
-//   y[b, h, w, co] = bias[co] + sum_{i, j, ci} x[b, h + i - KH/2, w + j - KW/2, ci] W[co, i, j, ci]
+//   y[b, t, h, w, co] = bias[co] + sum_{s, i, j, ci} x[b, t + s - (KT-1), h + i - KH/2, w + j - KW/2, ci]
+//                                                  W[co, s, i, j, ci]
 //
-// with zeros outside the image (stride 1, "same" padding).  GEMM view: M = B*H*W output pixels,
-// N = Cout, K = KH*KW*Cin in tap-major order, W read as a [Cout, K] row-major matrix.  The bf16
+// with zeros before the first frame and outside the image (stride 1, "same" spatial padding,
+// causal in time; KT = T = 1 is the 2-D convolution).  GEMM view: M = B*T*H*W output pixels,
+// N = Cout, K = KT*KH*KW*Cin in tap-major order, W read as a [Cout, K] row-major matrix.  The bf16
 // GEMM's geometry: 256 x 256 tiles, 64-channel k-steps (rows of 128 B, XOR-swizzled chunks), both
 // operands global -> LDS with global_load_lds_dwordx4 into two stages, 8 waves of 128 x 64 on
 // v_mfma_f32_32x32x16_bf16.  A row whose tap falls outside the image writes zeros to its LDS bytes
@@ -44,16 +47,18 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
     const int gsize = min(a.tiles_m - first_m, 8);
     const int rr = L - grp * per_group;
     const int tm = first_m + rr % gsize, tn = rr / gsize;
-    const int M = a.B * a.H * a.W;
+    const int HW = a.H * a.W;
+    const int M = a.B * a.T * HW;
     const int m0 = tm * CBM, n0 = tn * CBN;
-    const int K = a.KH * a.KW * a.Cin;
+    const int KHW = a.KH * a.KW;
+    const int K = a.KT * KHW * a.Cin;
     const int ncb = a.Cin / CBK;                 // channel blocks per tap
-    const int nk = a.KH * a.KW * ncb;
+    const int nk = a.KT * KHW * ncb;
     const int ph = a.KH / 2, pw = a.KW / 2;
 
     // load plan: instruction i of wave w covers tile rows (w*LPW+i)*8 .. +7; lane l writes LDS
     // bytes l*16 .. +15 of the 1 KB block = row l/8, position l%8, holding chunk (l%8) ^ swz(row)
-    int pix[LPW], ph_[LPW], pw_[LPW];
+    int pix[LPW], ph_[LPW], pw_[LPW], pt_[LPW];
     const bf16_t* gB[LPW];
     int chunk[LPW];
 #pragma unroll
@@ -64,20 +69,22 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
         pix[i] = p;
         pw_[i] = p % a.W;
         ph_[i] = (p / a.W) % a.H;
+        pt_[i] = (p / HW) % a.T;
         gB[i] = reinterpret_cast<const bf16_t*>(a.w) + (size_t)min(n0 + row, a.Cout - 1) * K + chunk[i] * 8;
     }
     const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
     auto issue = [&](int buf, int kk) {
         const int tap = kk / ncb, cb = kk - tap * ncb;
-        const int ti = tap / a.KW, tj = tap - ti * a.KW;
-        const int dh = ti - ph, dw = tj - pw;
+        const int ts = tap / KHW, tr = tap - ts * KHW;
+        const int ti = tr / a.KW, tj = tr - ti * a.KW;
+        const int dt = ts - (a.KT - 1), dh = ti - ph, dw = tj - pw;
         char* sa = smem + buf * kCStage;
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             char* dst = sa + (wave * LPW + i) * 1024;
             const int ih = ph_[i] + dh, iw = pw_[i] + dw;
-            if ((unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W) {
-                const bf16_t* src = X + ((long)pix[i] + (long)dh * a.W + dw) * a.Cin + cb * CBK + chunk[i] * 8;
+            if (pt_[i] + dt >= 0 && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W) {
+                const bf16_t* src = X + ((long)pix[i] + (long)dt * HW + (long)dh * a.W + dw) * a.Cin + cb * CBK + chunk[i] * 8;
                 __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
             } else {
                 *reinterpret_cast<u32x4_v*>(dst + lane * 16) = u32x4_v{0u, 0u, 0u, 0u};
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
 }
 
 hipError_t launch_conv2d(ConvArgs& a, hipStream_t s) {
-    const long M = (long)a.B * a.H * a.W;
+    const long M = (long)a.B * a.T * a.H * a.W;
     if (M == 0) return hipSuccess;
     a.tiles_m = (int)((M + CBM - 1) / CBM);
     a.tiles_n = (a.Cout + CBN - 1) / CBN;

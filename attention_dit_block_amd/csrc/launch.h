@@ -163,11 +163,13 @@ hipError_t launch_gemm_fp8(Fp8GemmBatch& g, hipStream_t s);
 
 // ---- 2-D convolution (NHWC), implicit GEMM ----------------------------------------------------
 struct ConvArgs {
-    const void* x;          // [B, H, W, Cin], x_dtype BF16 or F16
-    const void* w;          // [Cout, KH, KW, Cin], BF16 (F16 x: converted while staging -- not used)
+    const void* x;          // [B, T, H, W, Cin], BF16
+    const void* w;          // [Cout, KT, KH, KW, Cin], BF16
     const float* bias;      // [Cout] or null
-    void* y; int y_dtype;   // [B, H, W, Cout]
-    int B, H, W, Cin, Cout, KH, KW;     // stride 1, zero padding (K - 1) / 2
+    void* y; int y_dtype;   // [B, T, H, W, Cout]
+    int B, H, W, Cin, Cout, KH, KW;     // stride 1, zero padding (K - 1) / 2 in h and w
+    int T, KT;              // frames per clip and temporal taps: frames t-KT+1 .. t (zeros before 0);
+                            // T = KT = 1: the 2-D convolution
     int tiles_m, tiles_n;   // filled by the launcher
 };
 hipError_t launch_conv2d(ConvArgs& a, hipStream_t s);

@@ -498,6 +498,22 @@ int dit_conv2d(int dtype, void* stream, const void* x, int batch, int height, in
                void* y, int y_dtype);
 
 /*
+ * Causal 3-D convolution over video frames (the layers of a video VAE's decoder, whose
+ * convolutions the decoder page measures per latent frame), as the same implicit GEMM:
+ *   y[b, t, h, w, co] = bias[co] + sum_{s, i, j, ci} x[b, t + s - (kt-1), h + i - kh/2, w + j - kw/2, ci]
+ *                                                    * weight[co, s, i, j, ci]
+ * zeros before the first frame of each clip and outside the image, so output frame t depends on
+ * frames t-kt+1 .. t only; stride 1, output the input's size.
+ *  x         [batch, frames, height, width, c_in] (channels last), contiguous
+ *  weight    [c_out, kt, kh, kw, c_in], contiguous;  bias fp32 [c_out] or NULL
+ *  y         [batch, frames, height, width, c_out] of y_dtype; must not overlap the inputs
+ * Limits as for dit_conv2d, kt from 1 to 7 (kt = frames = 1 is dit_conv2d).  One launch.
+ */
+int dit_conv3d_causal(int dtype, void* stream, const void* x, int batch, int frames, int height,
+                      int width, int c_in, const void* weight, int c_out, int kt, int kh, int kw,
+                      const float* bias, void* y, int y_dtype);
+
+/*
  * Weight format conversion: dst[i] = fp16(src[i]) for n bf16 values (exact for
  * |x| >= 2^-14 and zero; smaller magnitudes round to nearest even among fp16
  * subnormals, as the GEMMs' own staging conversion does).  src and dst 16-byte

@@ -73,3 +73,70 @@ def test_identity_kernel_copies_input(dit):
     dit.conv2d(xt, wt, y)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(y), o.widen(x, "bf16"))
+
+
+# ---- causal 3-D convolution over frames (same derived bound, K = kt*kh*kw*Cin) --------------------
+
+def run3(dit, B, T, H, W, cin, cout, kt, k, bias, ydt, seed, sample=None):
+    x = di.draw((B, T, H, W, cin), 1.0, "bf16", seed, "x")
+    w = di.draw((cout, kt, k, k, cin), 0.05, "bf16", seed, "w_1")
+    b = di.draw((cout,), 1.0, "f32", seed, "cond") if bias else None
+    xt = dev(x, "bf16").view(B, T, H, W, cin)
+    wt = dev(w, "bf16").view(cout, kt, k, k, cin)
+    bt = dev(b, "f32") if bias else None
+    y = torch.empty(B, T, H, W, cout, dtype=ydt, device="cuda")
+    before = dit.launch_count()
+    dit.conv3d_causal(xt, wt, y, bias=bt)
+    torch.cuda.synchronize()
+    assert dit.launch_count() == before + 1
+    xf, wf = o.widen(x, "bf16"), o.widen(w, "bf16")
+    got = host(y)
+    if sample is not None:
+        # frames t-kt+1 .. t of the sampled output frames only
+        t0 = max(0, sample - kt + 1)
+        xs = xf[:, t0:sample + 1]
+        ref = o.conv3d_causal_nhwc(xs, wf, b)[:, -1]
+        abs_sum = o.conv3d_causal_nhwc(np.abs(xs), np.abs(wf), None if b is None else np.abs(b))[:, -1]
+        got = got[:, sample]
+    else:
+        ref = o.conv3d_causal_nhwc(xf, wf, b)
+        abs_sum = o.conv3d_causal_nhwc(np.abs(xf), np.abs(wf), None if b is None else np.abs(b))
+    K = kt * k * k * cin
+    bound = (K * 2.0 ** -23 + 2.0 ** -22) * abs_sum + 1e-30
+    if ydt == torch.bfloat16:
+        bound = bound + 0.5 * 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    err = np.abs(got - ref)
+    say(f"  conv3d {B}x{T}x{H}x{W}x{cin} -> {cout}, {kt}x{k}x{k}, bias {bias}, {ydt}"
+        f"{'' if sample is None else f', frame {sample}'}: max err/bound {np.max(err / bound):.3f}, "
+        f"max|gpu-oracle|/RMS {metric(got, ref):.2e}")
+    assert np.all(err <= bound), f"{np.sum(err > bound)} elements beyond the bound"
+    return got
+
+
+@pytest.mark.parametrize("B, T, H, W, cin, cout, kt, k, bias, ydt", [
+    (2, 3, 5, 7, 64, 40, 3, 3, True, torch.float32),     # ragged, clips of 3 frames
+    (1, 5, 9, 6, 128, 72, 2, 3, False, torch.bfloat16),  # kt = 2
+    (1, 2, 4, 4, 64, 16, 3, 1, True, torch.float32),     # more taps than frames: the first reach before 0
+])
+def test_conv3d_causal_shapes(dit, B, T, H, W, cin, cout, kt, k, bias, ydt):
+    run3(dit, B, T, H, W, cin, cout, kt, k, bias, ydt, 64)
+
+
+def test_conv3d_one_frame_tap_equals_conv2d(dit):
+    # kt = 1: frames are independent images -- bit-identical to dit_conv2d on the frames as a batch
+    B, T, H, W, c = 2, 3, 6, 10, 64
+    x = dev(di.draw((B, T, H, W, c), 1.0, "bf16", 65, "x"), "bf16").view(B, T, H, W, c)
+    w = dev(di.draw((c, 1, 3, 3, c), 0.05, "bf16", 65, "w_1"), "bf16").view(c, 1, 3, 3, c)
+    y3 = torch.empty(B, T, H, W, c, dtype=torch.float32, device="cuda")
+    y2 = torch.empty(B * T, H, W, c, dtype=torch.float32, device="cuda")
+    dit.conv3d_causal(x, w, y3)
+    dit.conv2d(x.view(B * T, H, W, c), w.view(c, 3, 3, c), y2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(y3).reshape(B * T, H, W, c), host(y2))
+
+
+def test_conv3d_video_vae_layer_sampled_frames(dit):
+    # a video-decoder layer at a quarter of 832 x 480 (120 x 208 pixels), 256 channels, 3x3x3
+    # causal taps over 5 frames; frames 0 (taps before the clip) and 4 checked in full
+    for t in (0, 4):
+        run3(dit, 1, 5, 120, 208, 256, 256, 3, 3, True, torch.float32, 66, sample=t)
