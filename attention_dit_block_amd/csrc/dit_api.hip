@@ -128,6 +128,7 @@ int validate_config(const dit_block_config* c) {
     if (c->d > 8192) return fail(DIT_ERR_UNSUPPORTED, "d = %d (at most 8192)", c->d);
     if (c->ffn_inner < 128 || c->ffn_inner % 128)
         return fail(DIT_ERR_INVALID_ARG, "ffn_inner = %d must be a positive multiple of 128", c->ffn_inner);
+    if (c->ffn_inner > (1 << 20)) return fail(DIT_ERR_UNSUPPORTED, "ffn_inner = %d (at most 2^20)", c->ffn_inner);
     if (c->d_cond < 8 || c->d_cond % 8 || c->d_cond > 16384)
         return fail(DIT_ERR_INVALID_ARG, "d_cond = %d must be a multiple of 8 in [8, 16384]", c->d_cond);
     if (c->n_txt < 0 || c->n_img < 0 || c->n_txt + c->n_img < 1)
@@ -1029,6 +1030,8 @@ int dit_linear(int dtype, void* stream, const void* x, int x_dtype, long ld_x, c
     if (dtype == DIT_BF16 ? k % 64 : k % 16)
         return fail(DIT_ERR_UNSUPPORTED, "k = %d must be a multiple of %d", k, dtype == DIT_BF16 ? 64 : 16);
     if ((long)m * n > (1L << 31) || (long)n * k > (1L << 31)) return fail(DIT_ERR_UNSUPPORTED, "matrix too large");
+    if (dtype != DIT_F32 && (k >= kGemmMaxLd || ld_x >= kGemmMaxLd))
+        return fail(DIT_ERR_UNSUPPORTED, "k = %d, ld_x = %ld: row strides of 2^22 elements or more", k, ld_x);
     DIT_TRY(check_ptr(w, "w"));
     if (m == 0) return DIT_OK;
     DIT_TRY(check_ptr(x, "x"));

@@ -140,7 +140,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
     int zero;
     asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
     const int tid = threadIdx.x + zero;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
     // ---- global -> LDS load plan: wave w, instruction i covers tile rows (w*LPW+i)*8 .. +7;
@@ -148,6 +148,14 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
     //      which holds global chunk (l%8) ^ swz(row) of the row.
     const bf16_t* gA[LPW];
     const bf16_t* gB[LPW];
+    // The same plan as a uniform tile base plus a 32-bit per-lane byte offset (the loads then take
+    // the scalar-base addressing form, with no per-load 64-bit address arithmetic).  A wave's B
+    // rows are all gate rows or all up rows of a SwiGLU tile.  Offsets stay below 2^32 because row
+    // strides are below 2^22 elements (checked on the host).
+    const char* tA = reinterpret_cast<const char*>(P.A) + (size_t)m0 * P.lda * 2;
+    const bool wup = swiglu && wave * LPW * 8 >= BN / 2;
+    const char* tB = reinterpret_cast<const char*>(P.B) + ((size_t)n0 + (wup ? P.up_off : 0)) * P.ldb * 2;
+    uint32_t oA[LPW], oB[LPW];
     {
         const int lr = lane >> 3, lc = lane & 7;
 #pragma unroll
@@ -168,6 +176,8 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
                 if (bn > P.N - 1) bn = P.N - 1;
             }
             gB[i] = reinterpret_cast<const bf16_t*>(P.B) + (size_t)bn * P.ldb + chunk * 8;
+            oA[i] = (uint32_t)(((long)(am - m0) * P.lda + chunk * 8) * 2);
+            oB[i] = (uint32_t)(((bn - (wup ? P.up_off : 0) - n0) * P.ldb + chunk * 8) * 2);
         }
     }
     u32x4_v breg[LPW];
@@ -185,6 +195,12 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
                                                  (lds_void*)(smem + buf * kStage + kBOff + (wave * LPW + i) * 1024),
                                                  16, 0, 0);
         }
+    };
+    auto issue_load_pair = [&](int buf, int k0, int i) {
+        __builtin_amdgcn_global_load_lds(tA + (long)k0 * 2 + oA[i],
+                                         (lds_void*)(smem + buf * kStage + (wave * LPW + i) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(tB + (long)k0 * 2 + oB[i],
+                                         (lds_void*)(smem + buf * kStage + kBOff + (wave * LPW + i) * 1024), 16, 0, 0);
     };
     auto store_b = [&](int buf) {
         if constexpr (AT == F16) {
@@ -291,9 +307,69 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
         __syncthreads();
         if constexpr (MORE) read_frags(fa[0], fb[0], (buf ^ 1) * kStage, 0);
     };
-    read_frags(fa[0], fb[0], 0, 0);
-    for (int it = 0; it < nk - 1; ++it) kstep.template operator()<true>(it);
-    kstep.template operator()<false>(nk - 1);
+    // Rotated pipeline for operands that both travel global -> LDS directly (AT != F16): the
+    // barrier sits after sub-step 2, so the first fragment reads of the next staged tile and the
+    // global loads of the tile after it are issued right behind the barrier and sub-step 3's
+    // MFMAs (whose fragments are already in registers) cover their latency.  The loads of tile
+    // it + 2 go into the stage tile it was read from: every wave finished reading it before the
+    // barrier.  MORE: 2 = tiles it + 1 and it + 2 exist, 1 = only it + 1, 0 = last tile.
+    auto kstep_rot = [&]<int MORE>(int it) {
+        constexpr int kMFMA = 0x008, kDSR = 0x100;
+        constexpr int kReads = 4 + NB, kMfmas = 4 * NB;
+        const int buf = it & 1;
+#pragma unroll
+        for (int s = 0; s < BK / 16 - 1; ++s) {
+            const int cur = s & 1;
+            read_frags(fa[cur ^ 1], fb[cur ^ 1], buf * kStage, s + 1);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma32<MT>(fb[cur][nb], fa[cur][mb], acc[nb][mb]);
+#pragma unroll
+            for (int i = 0; i < kReads; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kDSR, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kMFMA, kMfmas - kReads, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (MORE > 0) {
+            // tile it + 1 has landed (own loads: waitcnt; every wave's: barrier) and no wave
+            // reads stage `buf` any more
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(fa[0], fb[0], (buf ^ 1) * kStage, 0);
+        }
+        // sub-step 3; the next tile's global loads go one A / B pair after each of the first LPW
+        // MFMAs (fenced, so the issue of the loads and their address arithmetic overlaps MFMAs
+        // instead of leaving the matrix pipe idle behind a burst of them)
+#pragma unroll
+        for (int q = 0; q < kMfmas; ++q) {
+            const int nb = q / 4, mb = q % 4;
+            acc[nb][mb] = mfma32<MT>(fb[1][nb], fa[1][mb], acc[nb][mb]);
+            if constexpr (MORE > 1) {
+                if (q < LPW) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue_load_pair(buf, (kb + it + 2) * BK, q);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (AT != F16) {
+        read_frags(fa[0], fb[0], 0, 0);
+        if (nk > 1) issue_loads(1, (kb + 1) * BK);
+        int it = 0;
+        for (; it < nk - 2; ++it) kstep_rot.template operator()<2>(it);
+        if (nk > 1) kstep_rot.template operator()<1>(it++);
+        kstep_rot.template operator()<0>(it);
+    } else {
+        read_frags(fa[0], fb[0], 0, 0);
+        for (int it = 0; it < nk - 1; ++it) kstep.template operator()<true>(it);
+        kstep.template operator()<false>(nk - 1);
+    }
 
     // Partial tiles: lane l of wave w keeps float4 c of its accumulators at index
     // (w * NB*16 + c) * 64 + l of its workgroup's slot.
@@ -589,6 +665,8 @@ hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
             P.tiles_n = (P.N + FBN - 1) / FBN;
         }
         if (P.M == 0) P.tiles_m = 0;
+        // the MFMA kernel addresses a tile's rows by 32-bit byte offsets from the tile's first row
+        if (mfma && P.M > 0 && (P.lda >= kGemmMaxLd || P.ldb >= kGemmMaxLd)) return hipErrorInvalidValue;
         P.tile_begin = total;
         total += P.tiles_m * P.tiles_n;
     }

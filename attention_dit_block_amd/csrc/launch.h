@@ -97,6 +97,9 @@ struct GemmBatch {
     int sk_grid, dp_tiles, k_steps;
     unsigned long long epoch;
 };
+// Row strides (lda, ldb) of the 16-bit GEMMs are below this many elements (launch_gemm returns
+// hipErrorInvalidValue otherwise; the entry points reject such strides first).
+constexpr long kGemmMaxLd = 1L << 22;
 hipError_t launch_gemm(GemmBatch& b, hipStream_t s);
 // Bytes of stream-K scratch launch_gemm uses on the current device (0 if it cannot tell).
 size_t gemm_sk_scratch_bytes();

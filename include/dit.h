@@ -148,7 +148,7 @@ typedef struct dit_block_config {
     int d;              /* hidden size = n_heads * head_dim */
     int n_heads;
     int head_dim;       /* must be 128 */
-    int ffn_inner;      /* F, SwiGLU inner width; multiple of 128 */
+    int ffn_inner;      /* F, SwiGLU inner width; multiple of 128, at most 2^20 */
     int d_cond;         /* conditioning vector length; multiple of 8 */
     int n_txt;          /* text tokens (first in the joint sequence) */
     int n_img;          /* image tokens */
@@ -332,8 +332,9 @@ int dit_timestep_embedding(int dtype, void* stream, const float* t, const float*
  *  dtype     of w [n, k]: DIT_BF16 (x DIT_BF16 or DIT_F16, fp32 accumulation)
  *            or DIT_F32 (x and y DIT_F32, fp32 arithmetic)
  *  x         [m, k] of x_dtype, row stride ld_x;  y [m, n] of y_dtype, ld_y
- * Limits: n a multiple of 8; k a multiple of 64 (bf16) or 16 (fp32); y must
- * not overlap x or w.  One launch.
+ * Limits: n a multiple of 8; k a multiple of 64 (bf16) or 16 (fp32); bf16:
+ * k and ld_x below 2^22 (DIT_ERR_UNSUPPORTED otherwise); y must not overlap
+ * x or w.  One launch.
  */
 int dit_linear(int dtype, void* stream, const void* x, int x_dtype, long ld_x,
                const void* w, int m, int n, int k, void* y, int y_dtype, long ld_y);

@@ -77,6 +77,7 @@ def test_workspace_size_matches_plan(dit):
     (dict(head_dim=64, d=64 * 24), "DIT_ERR_UNSUPPORTED", "head_dim"),
     (dict(d=3000), "DIT_ERR_INVALID_ARG", "n_heads"),
     (dict(ffn_inner=9200), "DIT_ERR_INVALID_ARG", "ffn_inner"),
+    (dict(ffn_inner=(1 << 20) + 128), "DIT_ERR_UNSUPPORTED", "ffn_inner"),
     (dict(n_txt=0, n_img=0), "DIT_ERR_INVALID_ARG", "token"),
     (dict(n_txt=-1), "DIT_ERR_INVALID_ARG", "n_txt"),
     (dict(axes_dim=(32, 32, 32, 30)), "DIT_ERR_INVALID_ARG", "sum"),
@@ -379,3 +380,13 @@ def test_gemm_weight_format_validation(dit):
     sh0.gemm_w_dtype = dit.DIT_F16
     with pytest.raises(dit.DitError):
         dit.block_workspace_size(sh0)
+
+
+def test_linear_row_stride_limit(dit):
+    """The 16-bit GEMM addresses a tile's rows by 32-bit offsets: row strides of 2^22 elements or
+    more are refused before any launch."""
+    x = FakeDev(0x100000, shape=(2, 64), stride=(1 << 22, 1))
+    w = FakeDev(0x200000, shape=(8, 64))
+    y = FakeDev(0x300000, shape=(2, 8))
+    e = _no_launch(dit, lambda: dit.linear(x, w, y, stream=FakeStream()))
+    assert e.status == "DIT_ERR_UNSUPPORTED" and "2^22" in str(e)
