@@ -69,12 +69,14 @@ __device__ __forceinline__ unsigned long long* attn_flag(const AttnArgs& a, int 
 // One (head, query tile) unit L = head * nq + query tile over key tiles [kb, ke).
 // NEG: softmax_scale < 0 (the row max of the scaled scores is then the min of the raw ones).
 template <int DT, bool NEG>
-__device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem, int L, int kb, int ke, int kind,
+__device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem_k0, char* smem_k1, char* smem_v0,
+                                               char* smem_v1, int L, int kb, int ke, int kind,
                                                int g, long S, long t_end) {
     constexpr int LPW = 16 / kAttnWaves;    // 1 KB load instructions per wave per K (or V) tile
     typedef typename AFrag<DT>::T FragT;
-    // smem: K ring (2 tiles) then V ring (2 tiles)
-    constexpr int kV = 2 * kTile;
+    // The two slots of the K ring and of the V ring are LDS arrays of their own, so the compiler
+    // can tell that the fragment reads of one slot do not touch the slot whose global -> LDS
+    // loads are in flight (it would otherwise wait for those loads before the reads)
 
     // The thread index goes through an opaque zero: the per-lane address arithmetic below is then
     // redone for each unit instead of being hoisted out of the persistent loop, where it would
@@ -114,7 +116,7 @@ __device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem, in
     const size_t v_rstep = (size_t)16 * a.ld_v * 2;
     // tiles starting at key j0 into ring slot `slot`; rows past the last key repeat it
     auto load_k = [&](int slot, int j0) {
-        char* dst = smem + slot * kTile;
+        char* dst = slot ? smem_k1 : smem_k0;
         if (j0 + AK <= N) {
             const char* t = reinterpret_cast<const char*>(Kg + (size_t)j0 * a.ld_k);
 #pragma unroll
@@ -131,7 +133,7 @@ __device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem, in
         }
     };
     auto load_v = [&](int slot, int j0) {
-        char* dst = smem + kV + slot * kTile;
+        char* dst = slot ? smem_v1 : smem_v0;
         if (j0 + AK <= N) {
             const char* t = reinterpret_cast<const char*>(Vg + (size_t)j0 * a.ld_v);
 #pragma unroll
@@ -164,7 +166,7 @@ __device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem, in
 
     // S^T = K Q^T for the 64 keys in K slot `slot` (two 32-key blocks)
     auto scores = [&](f32x16_v* sd, int slot) {
-        const char* kt = smem + slot * kTile;
+        const char* kt = slot ? smem_k1 : smem_k0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -256,7 +258,7 @@ __device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem, in
                 for (int q = 0; q < 16; ++q) o[i][q] *= corr;
         }
         // ---- region 2: O^T += V^T P^T; key step ks covers keys 16 ks .. +15 of the tile
-        const char* vt = smem + kV + P * kTile;
+        const char* vt = P ? smem_v1 : smem_v0;
         auto read_v = [&](FragT* vf, int ks) {
 #pragma unroll
             for (int eb = 0; eb < 4; ++eb) {
@@ -372,7 +374,10 @@ __device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem, in
 // piece last, after the workgroups holding the other pieces computed theirs first.
 template <int DT, bool NEG>
 __device__ __forceinline__ void attention_mfma_body(const AttnArgs& a) {
-    __shared__ __attribute__((aligned(1024))) char smem[4 * kTile];
+    __shared__ __attribute__((aligned(1024))) char smem_k0[kTile];
+    __shared__ __attribute__((aligned(1024))) char smem_k1[kTile];
+    __shared__ __attribute__((aligned(1024))) char smem_v0[kTile];
+    __shared__ __attribute__((aligned(1024))) char smem_v1[kTile];
     const int g = xcd_remap(blockIdx.x, gridDim.x);
     const int G = a.sk_grid, I = a.k_tiles;
     const long S = G ? (long)(a.units - a.dp_units) * I : 0;          // stream-K key tiles
@@ -398,7 +403,7 @@ __device__ __forceinline__ void attention_mfma_body(const AttnArgs& a) {
             it = (long)t * I + ke;
         }
         if (w > 0) __syncthreads();                 // the K / V rings are reused by the next unit
-        attention_unit<DT, NEG>(a, smem, L, kb, ke, kind, g, S, t_end);
+        attention_unit<DT, NEG>(a, smem_k0, smem_k1, smem_v0, smem_v1, L, kb, ke, kind, g, S, t_end);
     }
 }
 
