@@ -10,6 +10,7 @@ constexpr int AK = 64;       // keys per tile
 constexpr int HD = 128;      // head dim
 constexpr int kTile = AK * HD * 2;          // bytes of one K (or V) tile: 64 rows of 256 B
 constexpr float kLazyMax = 8.0f;            // log2 of the largest unnormalised probability
+constexpr float kLazyP = 256.0f;             // 2^kLazyMax
 
 
 typedef __attribute__((address_space(3))) void lds_void;

@@ -204,43 +204,56 @@ __device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem_k0,
                 for (int q = 0; q < 16; ++q)
                     if (masked(kb, q)) SC[kb][q] = NEG ? INFINITY : -INFINITY;
         }
-        float e0 = SC[0][0], e1 = SC[1][0];
-#pragma unroll
-        for (int q = 1; q < 16; ++q) {
-            e0 = NEG ? fminf(e0, SC[0][q]) : fmaxf(e0, SC[0][q]);
-            e1 = NEG ? fminf(e1, SC[1][q]) : fmaxf(e1, SC[1][q]);
-        }
-        const float mt = (NEG ? -half_swap_max(-fminf(e0, e1)) : half_swap_max(fmaxf(e0, e1))) * c2;
-        // raise the running max only when this tile's max exceeds it by more than 2^kLazyMax
-        const bool raise = mt > m_run + kLazyMax;
-        const float m_new = raise ? mt : m_run;
-        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);    // 1 unless raised; 0 on tile 0
-        m_run = m_new;
-        const float nm = -m_new;
-        // probabilities, packed as the PV operand: word 4 ks + t of ph (pl) holds keys
-        // 16 ks + 8 h32 + 2t, +1 (registers 8 (ks & 1) + 2t, +1 of block ks >> 1)
+        // probabilities against running max nm = -m, packed as the PV operand: word 4 ks + t of ph
+        // (pl) holds keys 16 ks + 8 h32 + 2t, +1 (registers 8 (ks & 1) + 2t, +1 of block ks >> 1)
         uint32_t ph[16], pl[DT == BF16 ? 16 : 1];
-        float lsum = 0.0f;
+        float lsum;
+        auto probs = [&](float nm) {
+            lsum = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int q = 0; q < 16; q += 2) {
-                float p0 = __builtin_amdgcn_exp2f(fmaf(SC[kb][q], c2, nm));
-                float p1 = __builtin_amdgcn_exp2f(fmaf(SC[kb][q + 1], c2, nm));
-                if constexpr (LAST) {
-                    if (masked(kb, q)) p0 = 0.0f;
-                    if (masked(kb, q + 1)) p1 = 0.0f;
+                for (int q = 0; q < 16; q += 2) {
+                    float p0 = __builtin_amdgcn_exp2f(fmaf(SC[kb][q], c2, nm));
+                    float p1 = __builtin_amdgcn_exp2f(fmaf(SC[kb][q + 1], c2, nm));
+                    if constexpr (LAST) {
+                        if (masked(kb, q)) p0 = 0.0f;
+                        if (masked(kb, q + 1)) p1 = 0.0f;
+                    }
+                    lsum += p0 + p1;
+                    const int w = 8 * kb + (q >> 1);
+                    if constexpr (DT == BF16) {
+                        const uint32_t u0 = __float_as_uint(p0) & 0xffff0000u, u1 = __float_as_uint(p1) & 0xffff0000u;
+                        ph[w] = (u0 >> 16) | u1;
+                        pl[w] = pack_bf16x2(p0 - __uint_as_float(u0), p1 - __uint_as_float(u1));
+                    } else {
+                        ph[w] = pack_f16x2(p0, p1);
+                    }
                 }
-                lsum += p0 + p1;
-                const int w = 8 * kb + (q >> 1);
-                if constexpr (DT == BF16) {
-                    const uint32_t u0 = __float_as_uint(p0) & 0xffff0000u, u1 = __float_as_uint(p1) & 0xffff0000u;
-                    ph[w] = (u0 >> 16) | u1;
-                    pl[w] = pack_bf16x2(p0 - __uint_as_float(u0), p1 - __uint_as_float(u1));
-                } else {
-                    ph[w] = pack_f16x2(p0, p1);
-                }
+        };
+        // First against the running max as it stands.  A lane whose sum stays below 2^kLazyMax has
+        // every probability below it, so no score of its query exceeds the running max by
+        // kLazyMax and the max is not raised; only when some lane of the wave reaches it (a large
+        // score, or the first tile: running max -inf) does the wave take the tile's max and
+        // recompute, which gives the same values as taking the max first.
+        probs(-m_run);
+        float corr = 1.0f;
+        bool raise = false;
+        if (__builtin_amdgcn_ballot_w64(!(lsum < kLazyP))) {
+            float e0 = SC[0][0], e1 = SC[1][0];
+#pragma unroll
+            for (int q = 1; q < 16; ++q) {
+                e0 = NEG ? fminf(e0, SC[0][q]) : fmaxf(e0, SC[0][q]);
+                e1 = NEG ? fminf(e1, SC[1][q]) : fmaxf(e1, SC[1][q]);
             }
+            const float mt = (NEG ? -half_swap_max(-fminf(e0, e1)) : half_swap_max(fmaxf(e0, e1))) * c2;
+            // raise the running max only when this tile's max exceeds it by more than kLazyMax
+            raise = mt > m_run + kLazyMax;
+            const float m_new = raise ? mt : m_run;
+            corr = __builtin_amdgcn_exp2f(m_run - m_new);    // 1 unless raised; 0 on tile 0
+            m_run = m_new;
+            if (__builtin_amdgcn_ballot_w64(raise)) probs(-m_new);
+        }
         // keep the probabilities next to the score MFMAs of the following tile (they would
         // otherwise sink past the rescale branch below, into the PV phase); emits no code
         asm volatile("" ::"v"(ph[0]), "v"(ph[1]), "v"(ph[2]), "v"(ph[3]), "v"(ph[4]), "v"(ph[5]), "v"(ph[6]),
