@@ -110,6 +110,13 @@ __device__ __forceinline__ void store4(char* p, const float* f) {
     }
 }
 
+// One element (RNE for 16-bit types).
+template <int DT>
+__device__ __forceinline__ void store1(char* p, float f) {
+    if (DT == F32) *reinterpret_cast<float*>(p) = f;
+    else *reinterpret_cast<unsigned short*>(p) = (unsigned short)(pack2<DT>(f, 0.0f) & 0xffffu);
+}
+
 // Wave-wide reductions (64 lanes).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

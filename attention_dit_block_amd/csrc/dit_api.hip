@@ -1247,8 +1247,8 @@ static int conv_impl(const char* name, int dtype, void* stream, const void* x, i
     if (y_dtype != DIT_BF16 && y_dtype != DIT_F32) return fail(DIT_ERR_INVALID_ARG, "y_dtype must be DIT_BF16 or DIT_F32");
     if (batch < 0 || frames < 1 || height < 1 || width < 1)
         return fail(DIT_ERR_INVALID_ARG, "batch = %d, %d frames of %d x %d", batch, frames, height, width);
-    if (c_in < 64 || c_in % 64) return fail(DIT_ERR_UNSUPPORTED, "c_in = %d must be a positive multiple of 64", c_in);
-    if (c_out < 8 || c_out % 8) return fail(DIT_ERR_UNSUPPORTED, "c_out = %d must be a positive multiple of 8", c_out);
+    if (c_in < 8 || c_in % 8) return fail(DIT_ERR_UNSUPPORTED, "c_in = %d must be a positive multiple of 8", c_in);
+    if (c_out < 1) return fail(DIT_ERR_INVALID_ARG, "c_out = %d must be positive", c_out);
     if (kh < 1 || kw < 1 || kh % 2 == 0 || kw % 2 == 0 || kh > 7 || kw > 7)
         return fail(DIT_ERR_UNSUPPORTED, "kernel %d x %d: odd sizes up to 7", kh, kw);
     if (kt < 1 || kt > 7) return fail(DIT_ERR_UNSUPPORTED, "temporal kernel %d: 1 to 7 frames", kt);

@@ -2,7 +2,8 @@
 // the decoder page measures its convolutions at length, those of a video VAE with causal 3-D
 // kernels) on gfx950 as an implicit GEMM: no column buffer is materialised -- the page's point
 // against im2col -- each k-step stages 64 input channels of one kernel tap for 256 output pixels
-// straight from the channels-last input.
+// straight from the channels-last input (the last block of a tap zero-filled where Cin is not a
+// multiple of 64: the 96-channel layers of the decoder's last stage).
 //
 //   y[b, t, h, w, co] = bias[co] + sum_{s, i, j, ci} x[b, t + s - (KT-1), h + i - KH/2, w + j - KW/2, ci]
 //                                                  W[co, s, i, j, ci]
@@ -13,7 +14,8 @@
 // GEMM's geometry: 256 x 256 tiles, 64-channel k-steps (rows of 128 B, XOR-swizzled chunks), both
 // operands global -> LDS with global_load_lds_dwordx4 into two stages, 8 waves of 128 x 64 on
 // v_mfma_f32_32x32x16_bf16.  A row whose tap falls outside the image writes zeros to its LDS bytes
-// (ds_write) instead of loading them.
+// (ds_write) instead of loading them, and so do the A and B chunks past Cin.  Outputs go out four
+// channels per store when Cout is a multiple of 4, one by one otherwise (the 96 -> 3 head).
 #include "dev_common.h"
 #include "launch.h"
 
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
     const int m0 = tm * CBM, n0 = tn * CBN;
     const int KHW = a.KH * a.KW;
     const int K = a.KT * KHW * a.Cin;
-    const int ncb = a.Cin / CBK;                 // channel blocks per tap
+    const int ncb = (a.Cin + CBK - 1) / CBK;     // channel blocks per tap (the last one zero-padded)
     const int nk = a.KT * KHW * ncb;
     const int ph = a.KH / 2, pw = a.KW / 2;
 
@@ -71,6 +73,7 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
         ph_[i] = (p / a.W) % a.H;
         pt_[i] = (p / HW) % a.T;
         gB[i] = reinterpret_cast<const bf16_t*>(a.w) + (size_t)min(n0 + row, a.Cout - 1) * K + chunk[i] * 8;
+        // (chunk[i] * 8 < Cin checked per k-step below)
     }
     const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
     auto issue = [&](int buf, int kk) {
@@ -79,18 +82,23 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
         const int ti = tr / a.KW, tj = tr - ti * a.KW;
         const int dt = ts - (a.KT - 1), dh = ti - ph, dw = tj - pw;
         char* sa = smem + buf * kCStage;
+        const int c0 = cb * CBK;                                // first channel of the block
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             char* dst = sa + (wave * LPW + i) * 1024;
+            char* dstb = sa + CBM * CBK * 2 + (wave * LPW + i) * 1024;
+            const bool cv = c0 + chunk[i] * 8 < a.Cin;          // this lane's 8 channels exist
             const int ih = ph_[i] + dh, iw = pw_[i] + dw;
-            if (pt_[i] + dt >= 0 && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W) {
-                const bf16_t* src = X + ((long)pix[i] + (long)dt * HW + (long)dh * a.W + dw) * a.Cin + cb * CBK + chunk[i] * 8;
+            if (cv && pt_[i] + dt >= 0 && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W) {
+                const bf16_t* src = X + ((long)pix[i] + (long)dt * HW + (long)dh * a.W + dw) * a.Cin + c0 + chunk[i] * 8;
                 __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
             } else {
                 *reinterpret_cast<u32x4_v*>(dst + lane * 16) = u32x4_v{0u, 0u, 0u, 0u};
             }
-            __builtin_amdgcn_global_load_lds(gB[i] + (size_t)kk * CBK, (lds_void*)(sa + CBM * CBK * 2 + (wave * LPW + i) * 1024),
-                                             16, 0, 0);
+            if (cv)
+                __builtin_amdgcn_global_load_lds(gB[i] + (size_t)tap * a.Cin + c0, (lds_void*)dstb, 16, 0, 0);
+            else
+                *reinterpret_cast<u32x4_v*>(dstb + lane * 16) = u32x4_v{0u, 0u, 0u, 0u};
         }
     };
     const int h = lane >> 5;
@@ -151,12 +159,19 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
                 float o[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) o[j] = acc[nb][mb][4 * i + j];
-                if (a.bias) {
-                    const f32x4_v bv = ldf4(a.bias + col);
+                char* yp = reinterpret_cast<char*>(a.y) + ((size_t)m * a.Cout + col) * (OT == F32 ? 4 : 2);
+                if ((a.Cout & 3) == 0) {
+                    if (a.bias) {
+                        const f32x4_v bv = ldf4(a.bias + col);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) o[j] += bv[j];
+                        for (int j = 0; j < 4; ++j) o[j] += bv[j];
+                    }
+                    store4<OT>(yp, o);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (col + j < a.Cout) store1<OT>(yp + j * (OT == F32 ? 4 : 2), o[j] + (a.bias ? a.bias[col + j] : 0.0f));
                 }
-                store4<OT>(reinterpret_cast<char*>(a.y) + ((size_t)m * a.Cout + col) * (OT == F32 ? 4 : 2), o);
             }
     }
 }

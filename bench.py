@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--fp8-block", action="store_true",
                    help="time the fp8 double-stream block (its four weight products on e4m3 codes) at the "
                         "workload's size (one JSON line of its own)")
+    p.add_argument("--conv", action="store_true",
+                   help="time the causal 3-D convolution on the video decoder's stage shapes at 832 x 480 "
+                        "(one JSON line of its own)")
     p.add_argument("--shared-mod", action="store_true",
                    help="multi-block workloads: one AdaLN weight set per block kind, computed once per step")
     p.add_argument("--gemm-weights", default="f16", choices=["bf16", "f16"],
@@ -123,6 +126,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.fp8_gemm:
         return fp8_gemm_bench(args, cfg, dit, torch)
+    if args.conv:
+        return conv_bench(args, dit, torch)
     if args.fp8_block:
         return fp8_block_bench(args, cfg, dit, torch)
     t = cfg.dtype
@@ -439,6 +444,56 @@ def fp8_block_bench(args, cfg, dit, torch):
                       "products": "e4m3 weights (per-row scales, quantised once) x e4m3 activations (per row, "
                                   "every step)"},
            "kernels": kernels}
+    print(json.dumps(out), flush=True)
+
+
+# Causal 3-D convolutions at the video decoder's stage resolutions for an 832 x 480 output (the
+# decoder page's measurement size): latent 104 x 60 doubled three times, 384 channels at the two
+# coarsest stages, then 192 and 96, and the 96 -> 3 head; 3 x 3 x 3 taps over 3-frame clips.
+CONV_LAYERS = [
+    ("384ch_60x104", 60, 104, 384, 384), ("384ch_120x208", 120, 208, 384, 384),
+    ("192ch_240x416", 240, 416, 192, 192), ("96ch_480x832", 480, 832, 96, 96), ("head_96to3_480x832", 480, 832, 96, 3),
+]
+
+
+def conv_bench(args, dit, torch):
+    """dit_conv3d_causal on the layer shapes above (one clip of 3 frames each, bf16 in and out, fp32
+    bias), timed with HIP events on the launch stream.  Flop: 2 x outputs x Cout x taps x Cin
+    (no padded work counted)."""
+    import dit_inputs as di
+    T, KT, K = 3, 3, 3
+    s = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(args.steps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+    per, tot, flops = {}, 0.0, 0.0
+    for name, H, W, cin, cout in CONV_LAYERS:
+        x = torch.from_numpy(di.draw((T * H * W * cin,), 1.0, "bf16", args.seed, "x").view("int16")).view(
+            torch.bfloat16).to("cuda").view(1, T, H, W, cin)
+        w = torch.from_numpy(di.draw((cout * KT * K * K * cin,), 0.02, "bf16", args.seed, "w_1").view("int16")).view(
+            torch.bfloat16).to("cuda").view(cout, KT, K, K, cin)
+        b = torch.zeros(cout, dtype=torch.float32, device="cuda")
+        y = torch.empty(1, T, H, W, cout, dtype=torch.bfloat16, device="cuda")
+        t = timed(lambda: dit.conv3d_causal(x, w, y, bias=b))
+        f = 2.0 * T * H * W * cout * KT * K * K * cin
+        per[name] = {"us_per_clip": round(t * 1e3, 1), "us_per_frame": round(t * 1e3 / T, 1),
+                     "tflops": round(f / t / 1e9, 1)}
+        tot, flops = tot + t, flops + f
+        del x, w, b, y
+    out = {"metric": "causal 3-D convolution TFLOP/s on the video decoder's stage shapes", "value": round(flops / tot / 1e9, 1),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(tot, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "video_decoder_conv3d_832x480", "frames_per_clip": T, "taps": [KT, K, K]},
+           "frac_mfma_peak": round(flops / tot / 1e9 / 2500.0, 4), "layers": per}
     print(json.dumps(out), flush=True)
 
 

@@ -491,8 +491,8 @@ int dit_block_forward_fp8(const dit_block_config* cfg,
  *  weight    [c_out, kh, kw, c_in], contiguous;  bias fp32 [c_out] or NULL
  *  y         [batch, height, width, c_out] of y_dtype (DIT_BF16 or DIT_F32);
  *            must not overlap x, weight or bias
- * Limits: c_in a multiple of 64, c_out a multiple of 8, kh and kw odd <= 7.
- * One launch.
+ * Limits: c_in a multiple of 8 (a multiple of 64 wastes no matrix work), c_out >= 1
+ * (a multiple of 4 stores four channels at a time), kh and kw odd <= 7.  One launch.
  */
 int dit_conv2d(int dtype, void* stream, const void* x, int batch, int height, int width,
                int c_in, const void* weight, int c_out, int kh, int kw, const float* bias,

@@ -390,3 +390,17 @@ def test_linear_row_stride_limit(dit):
     y = FakeDev(0x300000, shape=(2, 8))
     e = _no_launch(dit, lambda: dit.linear(x, w, y, stream=FakeStream()))
     assert e.status == "DIT_ERR_UNSUPPORTED" and "2^22" in str(e)
+
+
+def test_conv_channel_limits(dit):
+    """Input channels must come in 8s (16-byte chunks of a pixel); any positive output count works."""
+    x = FakeDev(0x100000, shape=(1, 4, 4, 60))
+    w = FakeDev(0x200000, shape=(8, 3, 3, 60))
+    y = FakeDev(0x300000, shape=(1, 4, 4, 8), esize=4)
+    e = _no_launch(dit, lambda: dit.conv2d(x, w, y, stream=FakeStream()))
+    assert e.status == "DIT_ERR_UNSUPPORTED" and "multiple of 8" in str(e)
+    x = FakeDev(0x100000, shape=(1, 4, 4, 64))
+    w = FakeDev(0x200000, shape=(0, 3, 3, 64))
+    y = FakeDev(0x300000, shape=(1, 4, 4, 0), esize=4)
+    e = _no_launch(dit, lambda: dit.conv2d(x, w, y, stream=FakeStream()))
+    assert e.status == "DIT_ERR_INVALID_ARG" and "c_out" in str(e)

@@ -57,6 +57,9 @@ def test_vae_like_3x3(dit):
     (1, 32, 32, 128, 64, 1, False, torch.float32),      # 1x1 (a per-pixel linear layer)
     (1, 9, 11, 64, 16, 5, True, torch.float32),         # 5x5 with borders wider than the image rows
     (3, 1, 7, 64, 8, 3, False, torch.bfloat16),         # one-row images
+    (1, 11, 13, 96, 96, 3, True, torch.bfloat16),      # 96 channels: each tap's second block half zeros
+    (2, 7, 9, 24, 3, 3, True, torch.float32),          # fewer channels than one block, three outputs
+    (1, 6, 10, 200, 5, 1, False, torch.bfloat16),      # 200 channels (3 blocks + 8), five outputs
 ])
 def test_shapes(dit, B, H, W, cin, cout, k, bias, ydt):
     run(dit, B, H, W, cin, cout, k, bias, ydt, 62)
@@ -117,6 +120,8 @@ def run3(dit, B, T, H, W, cin, cout, kt, k, bias, ydt, seed, sample=None):
     (2, 3, 5, 7, 64, 40, 3, 3, True, torch.float32),     # ragged, clips of 3 frames
     (1, 5, 9, 6, 128, 72, 2, 3, False, torch.bfloat16),  # kt = 2
     (1, 2, 4, 4, 64, 16, 3, 1, True, torch.float32),     # more taps than frames: the first reach before 0
+    (1, 3, 8, 12, 96, 3, 3, 3, True, torch.float32),     # the decoder head's shape: 96 -> 3, 3x3x3
+    (2, 2, 5, 6, 192, 192, 3, 3, False, torch.bfloat16),  # 192 channels (the 240 x 416 stage)
 ])
 def test_conv3d_causal_shapes(dit, B, T, H, W, cin, cout, kt, k, bias, ydt):
     run3(dit, B, T, H, W, cin, cout, kt, k, bias, ydt, 64)
@@ -140,3 +145,9 @@ def test_conv3d_video_vae_layer_sampled_frames(dit):
     # causal taps over 5 frames; frames 0 (taps before the clip) and 4 checked in full
     for t in (0, 4):
         run3(dit, 1, 5, 120, 208, 256, 256, 3, 3, True, torch.float32, 66, sample=t)
+
+
+def test_conv3d_video_vae_head_sampled_frame(dit):
+    # the decoder head, 96 -> 3 channels with 3x3x3 causal taps, at half of 832 x 480 (240 x 416
+    # pixels): frame 1 of a 2-frame clip (its first tap reaches before the clip)
+    run3(dit, 1, 2, 240, 416, 96, 3, 3, 3, True, torch.bfloat16, 67, sample=1)
