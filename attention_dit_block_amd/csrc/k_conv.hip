@@ -11,11 +11,12 @@
 // with zeros before the first frame and outside the image (stride 1, "same" spatial padding,
 // causal in time; KT = T = 1 is the 2-D convolution).  GEMM view: M = B*T*H*W output pixels,
 // N = Cout, K = KT*KH*KW*Cin in tap-major order, W read as a [Cout, K] row-major matrix.  The bf16
-// GEMM's geometry: 256 x 256 tiles, 64-channel k-steps (rows of 128 B, XOR-swizzled chunks), both
-// operands global -> LDS with global_load_lds_dwordx4 into two stages, 8 waves of 128 x 64 on
-// v_mfma_f32_32x32x16_bf16.  A row whose tap falls outside the image writes zeros to its LDS bytes
-// (ds_write) instead of loading them, and so do the A and B chunks past Cin.  Outputs go out four
-// channels per store when Cout is a multiple of 4, one by one otherwise (the 96 -> 3 head).
+// GEMM's geometry: 256-row tiles, 64-channel k-steps (rows of 128 B, XOR-swizzled chunks), both
+// operands global -> LDS with global_load_lds_dwordx4 into two stages, 8 waves on
+// v_mfma_f32_32x32x16_bf16; 256-, 128- or 32-wide output-channel tiles by the layer's width.  A
+// row whose tap falls outside the image writes zeros to its LDS bytes (ds_write) instead of
+// loading them, and so do the A and B chunks past Cin.  Outputs go out four channels per store
+// when Cout is a multiple of 4, one by one otherwise (the 96 -> 3 head).
 #include "dev_common.h"
 #include "launch.h"
 
@@ -23,9 +24,20 @@ namespace dit {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int CBM = 256, CBN = 256, CBK = 64;
-constexpr int kCStage = (CBM + CBN) * CBK * 2;      // 64 KB: A then B
-constexpr int kCLds = 2 * kCStage;
+constexpr int CBM = 256, CBK = 64;
+
+// Output-channel tile width by wave layout: WM waves along M (of 8), each a (256 / WM) x (NB * 32)
+// sub-tile.  WM = 2: 256-wide tiles (wave tiles 128 x 64); WM = 4: 128-wide (64 x 64) for layers
+// of up to 128 channels; WM = 8: 32-wide (32 x 32) for the narrow head.
+template <int WM> struct ConvGeom {
+    static constexpr int WN = 8 / WM;                 // waves along N
+    static constexpr int MB = CBM / (WM * 32);        // 32-row m-blocks per wave
+    static constexpr int NB = WM == 8 ? 1 : 2;        // 32-column n-blocks per wave
+    static constexpr int BN = WN * NB * 32;           // tile columns
+    static constexpr int kStage = (CBM + BN) * CBK * 2;
+    static constexpr int kBLoads = BN / 8;            // 1 KB B-load instructions per stage
+    static constexpr int BPW = kBLoads >= 8 ? kBLoads / 8 : 1;   // per wave (waves past kBLoads idle)
+};
 
 __device__ __forceinline__ int cswz(int row) { return (row >> 1) & 7; }
 
@@ -37,10 +49,11 @@ __device__ __forceinline__ f32x16_v cmfma(const u32x4_v& a, const u32x4_v& b, co
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_v, a), __builtin_bit_cast(bf16x8_v, b), c, 0, 0, 0);
 }
 
-template <int DT, int OT>
-__global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
-    constexpr int NW = 8, WN = 4, NB = 2, LPW = 32 / NW;
-    __shared__ __attribute__((aligned(1024))) char smem[kCLds];
+template <int DT, int OT, int WM>
+__device__ __forceinline__ void conv_body(const ConvArgs& a, char* smem) {
+    typedef ConvGeom<WM> G;
+    constexpr int LPW = 32 / 8;                       // A-load instructions per wave (256 rows)
+    constexpr int WN = G::WN, MB = G::MB, NB = G::NB, BPW = G::BPW;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -51,18 +64,17 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
     const int tm = first_m + rr % gsize, tn = rr / gsize;
     const int HW = a.H * a.W;
     const int M = a.B * a.T * HW;
-    const int m0 = tm * CBM, n0 = tn * CBN;
+    const int m0 = tm * CBM, n0 = tn * G::BN;
     const int KHW = a.KH * a.KW;
     const int K = a.KT * KHW * a.Cin;
     const int ncb = (a.Cin + CBK - 1) / CBK;     // channel blocks per tap (the last one zero-padded)
     const int nk = a.KT * KHW * ncb;
     const int ph = a.KH / 2, pw = a.KW / 2;
 
-    // load plan: instruction i of wave w covers tile rows (w*LPW+i)*8 .. +7; lane l writes LDS
-    // bytes l*16 .. +15 of the 1 KB block = row l/8, position l%8, holding chunk (l%8) ^ swz(row)
-    int pix[LPW], ph_[LPW], pw_[LPW], pt_[LPW];
-    const bf16_t* gB[LPW];
-    int chunk[LPW];
+    // load plan: A instruction i of wave w covers tile rows (w*LPW+i)*8 .. +7, B instruction
+    // j = w*BPW + r rows j*8 .. +7; lane l writes LDS bytes l*16 .. +15 of the 1 KB block = row
+    // l/8, position l%8, holding chunk (l%8) ^ swz(row)
+    int pix[LPW], ph_[LPW], pw_[LPW], pt_[LPW], chunk[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int row = (wave * LPW + i) * 8 + (lane >> 3);
@@ -72,8 +84,14 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
         pw_[i] = p % a.W;
         ph_[i] = (p / a.W) % a.H;
         pt_[i] = (p / HW) % a.T;
-        gB[i] = reinterpret_cast<const bf16_t*>(a.w) + (size_t)min(n0 + row, a.Cout - 1) * K + chunk[i] * 8;
-        // (chunk[i] * 8 < Cin checked per k-step below)
+    }
+    const bf16_t* gB[BPW];
+    int chunkb[BPW];
+#pragma unroll
+    for (int r = 0; r < BPW; ++r) {
+        const int row = (wave * BPW + r) * 8 + (lane >> 3);
+        chunkb[r] = (lane & 7) ^ cswz(row);
+        gB[r] = reinterpret_cast<const bf16_t*>(a.w) + (size_t)min(n0 + row, a.Cout - 1) * K + chunkb[r] * 8;
     }
     const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
     auto issue = [&](int buf, int kk) {
@@ -81,12 +99,11 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
         const int ts = tap / KHW, tr = tap - ts * KHW;
         const int ti = tr / a.KW, tj = tr - ti * a.KW;
         const int dt = ts - (a.KT - 1), dh = ti - ph, dw = tj - pw;
-        char* sa = smem + buf * kCStage;
+        char* sa = smem + buf * G::kStage;
         const int c0 = cb * CBK;                                // first channel of the block
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             char* dst = sa + (wave * LPW + i) * 1024;
-            char* dstb = sa + CBM * CBK * 2 + (wave * LPW + i) * 1024;
             const bool cv = c0 + chunk[i] * 8 < a.Cin;          // this lane's 8 channels exist
             const int ih = ph_[i] + dh, iw = pw_[i] + dw;
             if (cv && pt_[i] + dt >= 0 && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W) {
@@ -95,28 +112,34 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
             } else {
                 *reinterpret_cast<u32x4_v*>(dst + lane * 16) = u32x4_v{0u, 0u, 0u, 0u};
             }
-            if (cv)
-                __builtin_amdgcn_global_load_lds(gB[i] + (size_t)tap * a.Cin + c0, (lds_void*)dstb, 16, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < BPW; ++r) {
+            const int j = wave * BPW + r;
+            if (j >= G::kBLoads) break;                         // wave-uniform
+            char* dstb = sa + CBM * CBK * 2 + j * 1024;
+            if (c0 + chunkb[r] * 8 < a.Cin)
+                __builtin_amdgcn_global_load_lds(gB[r] + (size_t)tap * a.Cin + c0, (lds_void*)dstb, 16, 0, 0);
             else
                 *reinterpret_cast<u32x4_v*>(dstb + lane * 16) = u32x4_v{0u, 0u, 0u, 0u};
         }
     };
     const int h = lane >> 5;
-    int a_row[4], b_row[NB];
+    int a_row[MB], b_row[NB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a_row[j] = wm * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < MB; ++j) a_row[j] = wm * (MB * 32) + j * 32 + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) b_row[j] = wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < NB; ++j) b_row[j] = wn * (NB * 32) + j * 32 + (lane & 31);
     auto frag = [&](const char* base, int row, int s) -> u32x4_v {
         const int c = 2 * s + h;
         return *reinterpret_cast<const u32x4_v*>(base + row * 128 + ((c ^ cswz(row)) << 4));
     };
 
-    f32x16_v acc[NB][4];
+    f32x16_v acc[NB][MB];
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < MB; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
@@ -126,35 +149,35 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
     for (int it = 0; it < nk; ++it) {
         const int buf = it & 1;
         if (it + 1 < nk) issue(buf ^ 1, it + 1);
-        const char* la = smem + buf * kCStage;
+        const char* la = smem + buf * G::kStage;
         const char* lb = la + CBM * CBK * 2;
 #pragma unroll
         for (int s = 0; s < CBK / 16; ++s) {
-            u32x4_v fa[4], fb[NB];
+            u32x4_v fa[MB], fb[NB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) fa[j] = frag(la, a_row[j], s);
+            for (int j = 0; j < MB; ++j) fa[j] = frag(la, a_row[j], s);
 #pragma unroll
             for (int j = 0; j < NB; ++j) fb[j] = frag(lb, b_row[j], s);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = cmfma<DT>(fb[nb], fa[mb], acc[nb][mb]);
+                for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = cmfma<DT>(fb[nb], fa[mb], acc[nb][mb]);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
-    // epilogue: acc[nb][mb][q] -> pixel m0 + wm*128 + mb*32 + (lane & 31), channel
-    // n0 + wn*64 + nb*32 + 8 (q >> 2) + 4 h + (q & 3)
+    // epilogue: acc[nb][mb][q] -> pixel m0 + wm*MB*32 + mb*32 + (lane & 31), channel
+    // n0 + wn*NB*32 + nb*32 + 8 (q >> 2) + 4 h + (q & 3)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
+    for (int mb = 0; mb < MB; ++mb) {
+        const int m = m0 + wm * (MB * 32) + mb * 32 + (lane & 31);
         if (m >= M) continue;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int col = n0 + wn * 64 + nb * 32 + 8 * i + 4 * h;
+                const int col = n0 + wn * (NB * 32) + nb * 32 + 8 * i + 4 * h;
                 if (col >= a.Cout) continue;
                 float o[4];
 #pragma unroll
@@ -176,14 +199,49 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel(ConvArgs a) {
     }
 }
 
+// One kernel per tile width, each with its own LDS size (hipcc emits no host launch stub for a kernel
+// template whose static LDS array is sized by a template parameter).
+template <int OT>
+__global__ __launch_bounds__(512, 1) void conv2d_kernel_w256(ConvArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * ConvGeom<2>::kStage];
+    conv_body<BF16, OT, 2>(a, smem);
+}
+template <int OT>
+__global__ __launch_bounds__(512, 1) void conv2d_kernel_w128(ConvArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * ConvGeom<4>::kStage];
+    conv_body<BF16, OT, 4>(a, smem);
+}
+template <int OT>
+__global__ __launch_bounds__(512, 1) void conv2d_kernel_w32(ConvArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * ConvGeom<8>::kStage];
+    conv_body<BF16, OT, 8>(a, smem);
+}
+
+template <int WM>
+static void launch_conv_w(ConvArgs& a, long M, hipStream_t s) {
+    a.tiles_m = (int)((M + CBM - 1) / CBM);
+    a.tiles_n = (a.Cout + ConvGeom<WM>::BN - 1) / ConvGeom<WM>::BN;
+    const dim3 grid(a.tiles_m * a.tiles_n), block(512);
+    const bool f32 = a.y_dtype == F32;
+    if constexpr (WM == 2) {
+        if (f32) hipLaunchKernelGGL((conv2d_kernel_w256<F32>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((conv2d_kernel_w256<BF16>), grid, block, 0, s, a);
+    } else if constexpr (WM == 4) {
+        if (f32) hipLaunchKernelGGL((conv2d_kernel_w128<F32>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((conv2d_kernel_w128<BF16>), grid, block, 0, s, a);
+    } else {
+        if (f32) hipLaunchKernelGGL((conv2d_kernel_w32<F32>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((conv2d_kernel_w32<BF16>), grid, block, 0, s, a);
+    }
+}
+
 hipError_t launch_conv2d(ConvArgs& a, hipStream_t s) {
     const long M = (long)a.B * a.T * a.H * a.W;
     if (M == 0) return hipSuccess;
-    a.tiles_m = (int)((M + CBM - 1) / CBM);
-    a.tiles_n = (a.Cout + CBN - 1) / CBN;
-    const dim3 grid(a.tiles_m * a.tiles_n), block(512);
-    if (a.y_dtype == F32) hipLaunchKernelGGL((conv2d_kernel<BF16, F32>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((conv2d_kernel<BF16, BF16>), grid, block, 0, s, a);
+    // the narrowest tile that covers the output channels (fewer idle MFMA columns)
+    if (a.Cout <= 32) launch_conv_w<8>(a, M, s);
+    else if (a.Cout <= 128) launch_conv_w<4>(a, M, s);
+    else launch_conv_w<2>(a, M, s);
     return hipGetLastError();
 }
 
