@@ -94,46 +94,42 @@ hipError_t launch_adaln_gemv(const GemvBatch& b, hipStream_t s) {
 
 // ------------------------------------------------------------------------------------------
 // Modulate: out = (1 + scale) * x * rstd + shift with rstd = 1/sqrt(mean(x^2) + eps).
-// One wave per row; the row stays in registers between the reduction and the write.
+// One wave per row, four rows per workgroup, the row kept in registers between the reduction and
+// the write.  Workgroups are laid out per problem (text rows, then image rows), and each stages
+// its problem's shift and scale vectors in LDS once for its four rows: read per row from L2 they
+// would be twice the row's own HBM bytes, and kept in registers they would cap occupancy.
 // Bound: HBM bytes  rows * d * (sizeof(x) + sizeof(out)).
 // ------------------------------------------------------------------------------------------
 template <int XT, int OT, int NC>
 __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int total = b.p[0].rows + (b.n > 1 ? b.p[1].rows : 0);
-    if (row >= total) return;
-    const int pi = row >= b.p[0].rows ? 1 : 0;
+    extern __shared__ float s_mod[];               // shift [d], then scale [d]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nb0 = (b.p[0].rows + 3) / 4;         // workgroups of problem 0
+    const int pi = (b.n > 1 && (int)blockIdx.x >= nb0) ? 1 : 0;
     const ModProblem& P = b.p[pi];
-    const int r = row - (pi ? b.p[0].rows : 0);
+    const int r = ((int)blockIdx.x - (pi ? nb0 : 0)) * 4 + wave;
+    const bool active = r < P.rows;                // wave-uniform
     const int d = b.d;
-    const char* xrow = reinterpret_cast<const char*>(P.x) + (size_t)r * P.ld_x * ESize<XT>::v;
+    const char* xrow = reinterpret_cast<const char*>(P.x) + (size_t)min(r, P.rows - 1) * P.ld_x * ESize<XT>::v;
     char* orow = reinterpret_cast<char*>(P.out) + (size_t)r * P.ld_out * ESize<OT>::v;
 
-    // Up to 8 chunks per lane, the shift / scale slices are loaded together with the row (they
-    // are independent of it), so their L2 latency overlaps the row's HBM latency; wider rows load
-    // them after the reduction to keep the register count down.
-    constexpr bool kEarly = NC <= 8;
     float v[NC][8];
-    f32x4_v sh[kEarly ? NC : 1][2], sc[kEarly ? NC : 1][2];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int c = (lane + 64 * i) * 8;        // first element of this 8-element chunk
-        if (c < d) {
+        if (active && c < d) {
             load8<XT>(xrow + (size_t)c * ESize<XT>::v, v[i]);
         } else {
 #pragma unroll
             for (int t = 0; t < 8; ++t) v[i][t] = 0.0f;
         }
     }
-    if constexpr (kEarly) {
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            const int c = min((lane + 64 * i) * 8, d - 8);    // chunks past the row: any valid slice
-            sh[i][0] = ldf4(P.shift + c); sh[i][1] = ldf4(P.shift + c + 4);
-            sc[i][0] = ldf4(P.scale + c); sc[i][1] = ldf4(P.scale + c + 4);
-        }
+    for (int c = threadIdx.x * 4; c < d; c += 1024) {
+        stf4(s_mod + c, ldf4(P.shift + c));
+        stf4(s_mod + d + c, ldf4(P.scale + c));
     }
+    __syncthreads();
+    if (!active) return;
     float ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < NC; ++i)
@@ -148,16 +144,11 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             const int c = min((lane + 64 * i) * 8, d - 8);
+            const f32x4_v sh0 = ldf4(s_mod + c), sh1 = ldf4(s_mod + c + 4);
+            const f32x4_v sc0 = ldf4(s_mod + d + c), sc1 = ldf4(s_mod + d + c + 4);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                float shv, scv;
-                if constexpr (kEarly) {
-                    shv = sh[i][t >> 2][t & 3];
-                    scv = sc[i][t >> 2][t & 3];
-                } else {
-                    shv = P.shift[c + t];
-                    scv = P.scale[c + t];
-                }
+                const float shv = t < 4 ? sh0[t] : sh1[t - 4], scv = t < 4 ? sc0[t] : sc1[t - 4];
                 v[i][t] = fmaf(1.0f + scv, v[i][t] * rstd, shv);
                 if ((lane + 64 * i) * 8 < d) amax = fmaxf(amax, fabsf(v[i][t]));
             }
@@ -186,13 +177,8 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
     for (int i = 0; i < NC; ++i) {
         const int c = (lane + 64 * i) * 8;
         if (c < d) {
-            f32x4_v sh0, sh1, sc0, sc1;
-            if constexpr (kEarly) {
-                sh0 = sh[i][0]; sh1 = sh[i][1]; sc0 = sc[i][0]; sc1 = sc[i][1];
-            } else {
-                sh0 = ldf4(P.shift + c); sh1 = ldf4(P.shift + c + 4);
-                sc0 = ldf4(P.scale + c); sc1 = ldf4(P.scale + c + 4);
-            }
+            const f32x4_v sh0 = ldf4(s_mod + c), sh1 = ldf4(s_mod + c + 4);
+            const f32x4_v sc0 = ldf4(s_mod + d + c), sc1 = ldf4(s_mod + d + c + 4);
             float o[8];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -207,11 +193,12 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
 template <int XT, int OT>
 static hipError_t launch_mod_nc(const ModBatch& b, hipStream_t s, dim3 grid) {
     const int nc = (b.d + 511) / 512;
-    if (nc <= 2) hipLaunchKernelGGL((modulate_kernel<XT, OT, 2>), grid, dim3(256), 0, s, b);
-    else if (nc <= 4) hipLaunchKernelGGL((modulate_kernel<XT, OT, 4>), grid, dim3(256), 0, s, b);
-    else if (nc <= 6) hipLaunchKernelGGL((modulate_kernel<XT, OT, 6>), grid, dim3(256), 0, s, b);
-    else if (nc <= 8) hipLaunchKernelGGL((modulate_kernel<XT, OT, 8>), grid, dim3(256), 0, s, b);
-    else hipLaunchKernelGGL((modulate_kernel<XT, OT, 16>), grid, dim3(256), 0, s, b);
+    const size_t lds = (size_t)2 * b.d * sizeof(float);
+    if (nc <= 2) hipLaunchKernelGGL((modulate_kernel<XT, OT, 2>), grid, dim3(256), lds, s, b);
+    else if (nc <= 4) hipLaunchKernelGGL((modulate_kernel<XT, OT, 4>), grid, dim3(256), lds, s, b);
+    else if (nc <= 6) hipLaunchKernelGGL((modulate_kernel<XT, OT, 6>), grid, dim3(256), lds, s, b);
+    else if (nc <= 8) hipLaunchKernelGGL((modulate_kernel<XT, OT, 8>), grid, dim3(256), lds, s, b);
+    else hipLaunchKernelGGL((modulate_kernel<XT, OT, 16>), grid, dim3(256), lds, s, b);
     return hipGetLastError();
 }
 
@@ -224,8 +211,9 @@ static hipError_t launch_mod_x(const ModBatch& b, hipStream_t s, dim3 grid) {
 }
 
 hipError_t launch_modulate(const ModBatch& b, hipStream_t s) {
-    const int total = b.p[0].rows + (b.n > 1 ? b.p[1].rows : 0);
-    const dim3 grid((total + 3) / 4);
+    // four rows per workgroup, each problem's rows in workgroups of their own
+    const dim3 grid((b.p[0].rows + 3) / 4 + (b.n > 1 ? (b.p[1].rows + 3) / 4 : 0));
+    if (grid.x == 0) return hipSuccess;
     // All problems of one batch share x_dtype (the caller builds them so).
     return b.p[0].x_dtype == BF16 ? launch_mod_x<BF16>(b, s, grid) : launch_mod_x<F32>(b, s, grid);
 }
