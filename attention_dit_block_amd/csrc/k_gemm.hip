@@ -688,8 +688,13 @@ hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
         else same_k &= b.p[i].K / BK == b.k_steps;
     }
     const int G = device_cu_count();
-    if (DIT_GEMM_STREAMK && mfma && b.sk_scratch && same_k && G > 0 && total >= 2 * G && total % G != 0 &&
-        4 * (total % G) <= G) {
+    // Fewer tiles than half the CUs with long k-loops (512 + 1024 tokens: the 72 tiles of FFN-down,
+    // K = 9216) split every tile's k-steps over all CUs.  The hand-over of fp32 partials past the
+    // L2s is slow, so this pays only when each workgroup still gets 32 or more k-steps: the
+    // out-projection at the same size (K = 3072, 13.5 k-steps each) ran 98 -> 130 us split.
+    if (DIT_GEMM_STREAMK && mfma && b.sk_scratch && same_k && G > 0 &&
+        ((total >= 2 * G && total % G != 0 && 4 * (total % G) <= G) ||
+         (2 * total <= G && (long)total * b.k_steps >= 32L * G))) {
         const int D = total / G;
         b.sk_grid = G;
         b.dp_tiles = D >= 1 ? (D - 1) * G : 0;
