@@ -141,27 +141,26 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
 
 // ---- stream-K plumbing.  A persistent grid of G workgroups splits S work steps evenly; a piece
 // of a work unit that some workgroup does not finish itself is handed over through a partial
-// result and a 64-bit flag.  Partials and flags move with relaxed device-scope atomics: on gfx950
-// these are sc1 loads and stores that go to the coherence point past the XCD-private L2s, so no
-// cache-wide writeback or invalidate (which a release / acquire fence would issue, for the whole
-// XCD's L2) is needed.  Ordering comes from waiting for the partial's stores to be acknowledged
-// before the flag is raised.
+// result and a 64-bit flag.  Partials move as 16-byte sc1 buffer loads and stores and flags as
+// relaxed device-scope atomics (sc1 accesses as well): on gfx950 these go to the coherence point
+// past the XCD-private L2s, so no cache-wide writeback or invalidate (which a release / acquire
+// fence would issue, for the whole XCD's L2) is needed.  Ordering comes from waiting for the
+// partial's stores to be acknowledged before the flag is raised.
 // First step of workgroup g's share.
 __device__ __forceinline__ long sk_begin(long S, int g, int G) { return S * g / G; }
 
-__device__ __forceinline__ void sk_store(float4* p, float a, float b, float c, float d) {
-    unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
-    const unsigned long long lo = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
-    const unsigned long long hi = (unsigned long long)__float_as_uint(c) | ((unsigned long long)__float_as_uint(d) << 32);
-    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+constexpr int kCachePolicySc1 = 16;      // cache-policy operand of the buffer builtins: sc1
+// A partial slot (workgroup-uniform base) as a raw buffer; offsets in bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_slot(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
 }
-__device__ __forceinline__ float4 sk_load(const float4* p) {
-    unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<float4*>(p));
-    const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_float4(__uint_as_float((unsigned)lo), __uint_as_float((unsigned)(lo >> 32)),
-                       __uint_as_float((unsigned)hi), __uint_as_float((unsigned)(hi >> 32)));
+__device__ __forceinline__ void sk_store(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d) {
+    const u32x4_v v = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCachePolicySc1);
+}
+__device__ __forceinline__ float4 sk_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicySc1);
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
 }
 // Publish: every thread's partial stores acknowledged, then thread 0 raises the flag.
 __device__ __forceinline__ void sk_raise(unsigned long long* flag, unsigned long long tag) {

@@ -324,13 +324,15 @@ __device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem_k0,
     }
 
     if (kind == UNIT_PARTIAL) {
-        float4* dst = attn_partial(a, g) + wave * kPartF4 * 64 + lane;
+        const __amdgpu_buffer_rsrc_t dst = sk_slot(attn_partial(a, g));
+        const uint32_t off = (uint32_t)((wave * kPartF4 * 64 + lane) * 16);
 #pragma unroll
         for (int eb = 0; eb < 4; ++eb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                sk_store(dst + (4 * eb + i) * 64, o[eb][4 * i], o[eb][4 * i + 1], o[eb][4 * i + 2], o[eb][4 * i + 3]);
-        sk_store(dst + 16 * 64, m_run, l_run, 0.0f, 0.0f);
+                sk_store(dst, off + (4 * eb + i) * 64 * 16, o[eb][4 * i], o[eb][4 * i + 1], o[eb][4 * i + 2],
+                         o[eb][4 * i + 3]);
+        sk_store(dst, off + 16 * 64 * 16, m_run, l_run, 0.0f, 0.0f);
         sk_raise(attn_flag(a, g), a.epoch);
         return;
     }
@@ -342,8 +344,9 @@ __device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem_k0,
         for (int jg = g + 1; jg < G && sk_begin(S, jg, G) < t_end; ++jg) {
             if (sk_begin(S, jg + 1, G) == sk_begin(S, jg, G)) continue;     // empty share
             sk_take(attn_flag(a, jg), a.epoch);
-            const float4* src = attn_partial(a, jg) + wave * kPartF4 * 64 + lane;
-            const float4 ml = sk_load(src + 16 * 64);
+            const __amdgpu_buffer_rsrc_t src = sk_slot(attn_partial(a, jg));
+            const uint32_t off = (uint32_t)((wave * kPartF4 * 64 + lane) * 16);
+            const float4 ml = sk_load(src, off + 16 * 64 * 16);
             const float m_new = fmaxf(m_run, ml.x);
             const float ca = __builtin_amdgcn_exp2f(m_run - m_new), cb = __builtin_amdgcn_exp2f(ml.x - m_new);
             m_run = m_new;
@@ -353,7 +356,7 @@ __device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem_k0,
             for (int eb = 0; eb < 4; ++eb) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float4 v = sk_load(src + (4 * eb + i) * 64);
+                    const float4 v = sk_load(src, off + (4 * eb + i) * 64 * 16);
                     o[eb][4 * i] = fmaf(o[eb][4 * i], ca, v.x * cb);
                     o[eb][4 * i + 1] = fmaf(o[eb][4 * i + 1], ca, v.y * cb);
                     o[eb][4 * i + 2] = fmaf(o[eb][4 * i + 2], ca, v.z * cb);

@@ -375,7 +375,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
     // (w * NB*16 + c) * 64 + l of its workgroup's slot.
     constexpr int kF4 = NB * 16;                   // float4s of accumulators per lane
     if (kind == TILE_PARTIAL) {
-        float4* dst = sk_partial(b, g);
+        const __amdgpu_buffer_rsrc_t dst = sk_slot(sk_partial(b, g));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -383,7 +383,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int c = (nb * 4 + mb) * 4 + q;
-                    sk_store(dst + (wave * kF4 + c) * 64 + lane, acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
+                    sk_store(dst, (uint32_t)(((wave * kF4 + c) * 64 + lane) * 16), acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
                              acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
                 }
         sk_raise(sk_flag(b, g), b.epoch);
@@ -396,7 +396,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
         for (int j = g + 1; j < G && sk_begin(S, j, G) < t_end; ++j) {
             if (sk_begin(S, j + 1, G) == sk_begin(S, j, G)) continue;     // empty share
             sk_take(sk_flag(b, j), b.epoch);
-            const float4* src = sk_partial(b, j);
+            const __amdgpu_buffer_rsrc_t src = sk_slot(sk_partial(b, j));
             // 4 loads in flight at a time: the accumulators already fill the register file
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
@@ -405,7 +405,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int c = (nb * 4 + mb) * 4 + q;
-                        const float4 v = sk_load(src + (wave * kF4 + c) * 64 + lane);
+                        const float4 v = sk_load(src, (uint32_t)(((wave * kF4 + c) * 64 + lane) * 16));
                         acc[nb][mb][4 * q] += v.x;
                         acc[nb][mb][4 * q + 1] += v.y;
                         acc[nb][mb][4 * q + 2] += v.z;
