@@ -688,13 +688,14 @@ hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
         else same_k &= b.p[i].K / BK == b.k_steps;
     }
     const int G = device_cu_count();
-    // Fewer tiles than half the CUs with long k-loops (512 + 1024 tokens: the 72 tiles of FFN-down,
-    // K = 9216) split every tile's k-steps over all CUs.  The hand-over of fp32 partials past the
-    // L2s is slow, so this pays only when each workgroup still gets 32 or more k-steps: the
-    // out-projection at the same size (K = 3072, 13.5 k-steps each) ran 98 -> 130 us split.
+    // Fewer tiles than half the CUs (512 + 1024 tokens: the 72 tiles of the d-output GEMMs) split
+    // every tile's k-steps over all CUs when each workgroup still gets 12 or more k-steps (the
+    // fp32 partials' hand-over past the L2s costs about as much as a few k-steps).  A single
+    // partly filled round (216 tiles at 512 + 4096 tokens) stays unsplit: there the split put
+    // co-resident workgroups at different k-offsets and ran 114 -> 147 us (out-proj).
     if (DIT_GEMM_STREAMK && mfma && b.sk_scratch && same_k && G > 0 &&
         ((total >= 2 * G && total % G != 0 && 4 * (total % G) <= G) ||
-         (2 * total <= G && (long)total * b.k_steps >= 32L * G))) {
+         (2 * total <= G && (long)total * b.k_steps >= 12L * G))) {
         const int D = total / G;
         b.sk_grid = G;
         b.dp_tiles = D >= 1 ? (D - 1) * G : 0;
