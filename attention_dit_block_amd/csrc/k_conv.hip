@@ -217,6 +217,105 @@ __global__ __launch_bounds__(512, 1) void conv2d_kernel_w32(ConvArgs a) {
     conv_body<BF16, OT, 8>(a, smem);
 }
 
+// ---- Direct convolution for narrow layers (Cout <= 32: the decoder head, 96 -> 3).  The implicit
+// GEMM stages every input pixel once per tap; here a workgroup stages the input window of a
+// 16 x 16-pixel output tile (KT frames of (15 + KH) x (15 + KW) pixels, zeros outside the image
+// and before the clip) once per 32-channel block and runs all taps from LDS.  Pixels are 80 bytes
+// apart in LDS (32 channels + 16 bytes), so the 16 lanes of a fragment read, 16 consecutive pixels,
+// hit distinct banks.  8 waves of 32 pixels x 32 output channels (rows past Cout are zeros) on
+// v_mfma_f32_32x32x16_bf16; weight fragments come from global memory (L1 / L2: the weights are a
+// few KB), one tap ahead.
+constexpr int kDirTile = 16;                       // output tile: 16 x 16 pixels of one frame
+constexpr int kDirPix = 80;                        // LDS bytes per staged pixel
+constexpr int kDirLds = 80 * 1024;                 // two workgroups per CU
+// Staged window of a layer, in bytes (the launcher uses the direct kernel when it fits).
+inline long conv_direct_lds(int KT, int KH, int KW) { return (long)KT * (kDirTile - 1 + KH) * (kDirTile - 1 + KW) * kDirPix; }
+
+template <int OT>
+__global__ __launch_bounds__(512, 2) void conv_direct_kernel(ConvArgs a) {
+    __shared__ __attribute__((aligned(16))) char win[kDirLds];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+    const int tiles_w = (a.W + kDirTile - 1) / kDirTile, tiles_h = (a.H + kDirTile - 1) / kDirTile;
+    int L = blockIdx.x;
+    const int tx = L % tiles_w; L /= tiles_w;
+    const int ty = L % tiles_h; L /= tiles_h;
+    const int t = L % a.T, b = L / a.T;               // output frame t of clip b
+    const int y0 = ty * kDirTile, x0 = tx * kDirTile;
+    const int TH2 = kDirTile - 1 + a.KH, TW2 = kDirTile - 1 + a.KW;
+    const int nwin = a.KT * TH2 * TW2;                 // staged pixels
+    const int ph = a.KH / 2, pw = a.KW / 2;
+    const int KHW = a.KH * a.KW, taps = a.KT * KHW;
+    const long K = (long)taps * a.Cin;                 // weight row length
+    const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
+    const bf16_t* Wt = reinterpret_cast<const bf16_t*>(a.w);
+
+    // this lane's output pixel (A rows) and weight row (B rows)
+    const int pp = wave * 32 + (lane & 31);
+    const int py = pp >> 4, px = pp & 15;
+    const int wr = lane & 31;                          // output channel of the B fragment
+    f32x16_v acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+
+    for (int c0 = 0; c0 < a.Cin; c0 += 32) {
+        if (c0 > 0) __syncthreads();                   // every wave is done with the last block
+        // stage the window: chunk c = pixel * 4 + quarter (8 channels); at most 1024 pixels, so at
+        // most 8 chunks per thread, all loaded before the first LDS write
+        constexpr int kMaxChunks = kDirLds / kDirPix * 4 / 512;
+        u32x4_v v[kMaxChunks];
+#pragma unroll
+        for (int r = 0; r < kMaxChunks; ++r) {
+            const int c = tid + 512 * r;
+            v[r] = u32x4_v{0u, 0u, 0u, 0u};
+            if (c < nwin * 4) {
+                const int pix = c >> 2, qq = c & 3;
+                const int xs = pix % TW2, rr = pix / TW2;
+                const int ys = rr % TH2, s = rr / TH2;
+                const int tt = t + s - (a.KT - 1), yy = y0 + ys - ph, xx = x0 + xs - pw;
+                const int ch = c0 + qq * 8;
+                if (tt >= 0 && (unsigned)yy < (unsigned)a.H && (unsigned)xx < (unsigned)a.W && ch < a.Cin)
+                    v[r] = ld16(X + ((((long)b * a.T + tt) * a.H + yy) * a.W + xx) * a.Cin + ch);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kMaxChunks; ++r) {
+            const int c = tid + 512 * r;
+            if (c < nwin * 4) *reinterpret_cast<u32x4_v*>(win + (c >> 2) * kDirPix + (c & 3) * 16) = v[r];
+        }
+        __syncthreads();
+        // weight fragment of tap k, k16 step ks: row wr, channels c0 + 16 ks + 8 h .. +7
+        auto wfrag = [&](int k, int ks) -> u32x4_v {
+            const int ch = c0 + 16 * ks + 8 * h;
+            if (wr < a.Cout && ch < a.Cin) return ld16(Wt + (long)wr * K + (long)k * a.Cin + ch);
+            return u32x4_v{0u, 0u, 0u, 0u};
+        };
+        u32x4_v wb0 = wfrag(0, 0), wb1 = wfrag(0, 1);
+        for (int k = 0; k < taps; ++k) {
+            u32x4_v nb0 = wb0, nb1 = wb1;
+            if (k + 1 < taps) { nb0 = wfrag(k + 1, 0); nb1 = wfrag(k + 1, 1); }
+            const int s = k / KHW, rk = k - s * KHW, i = rk / a.KW, j = rk - i * a.KW;
+            const char* ap = win + ((s * TH2 + py + i) * TW2 + px + j) * kDirPix + 16 * h;
+            const u32x4_v fa0 = *reinterpret_cast<const u32x4_v*>(ap);
+            const u32x4_v fa1 = *reinterpret_cast<const u32x4_v*>(ap + 32);
+            acc = cmfma<BF16>(wb0, fa0, acc);
+            acc = cmfma<BF16>(wb1, fa1, acc);
+            wb0 = nb0; wb1 = nb1;
+        }
+    }
+
+    // acc[q] -> pixel pp, output channel 8 (q >> 2) + 4 h + (q & 3)
+    const int yo = y0 + py, xo = x0 + px;
+    if (yo >= a.H || xo >= a.W) return;
+    const long m = (((long)b * a.T + t) * a.H + yo) * a.W + xo;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int co = 8 * (q >> 2) + 4 * h + (q & 3);
+        if (co < a.Cout)
+            store1<OT>(reinterpret_cast<char*>(a.y) + (m * a.Cout + co) * (OT == F32 ? 4 : 2),
+                       acc[q] + (a.bias ? a.bias[co] : 0.0f));
+    }
+}
+
 template <int WM>
 static void launch_conv_w(ConvArgs& a, long M, hipStream_t s) {
     a.tiles_m = (int)((M + CBM - 1) / CBM);
@@ -238,8 +337,15 @@ static void launch_conv_w(ConvArgs& a, long M, hipStream_t s) {
 hipError_t launch_conv2d(ConvArgs& a, hipStream_t s) {
     const long M = (long)a.B * a.T * a.H * a.W;
     if (M == 0) return hipSuccess;
-    // the narrowest tile that covers the output channels (fewer idle MFMA columns)
-    if (a.Cout <= 32) launch_conv_w<8>(a, M, s);
+    // narrow layers whose staged window fits: the direct kernel; otherwise the narrowest implicit-GEMM
+    // tile that covers the output channels (fewer idle MFMA columns)
+    if (a.Cout <= 32 && conv_direct_lds(a.KT, a.KH, a.KW) <= kDirLds) {
+        const long tiles = (long)a.B * a.T * ((a.H + kDirTile - 1) / kDirTile) * ((a.W + kDirTile - 1) / kDirTile);
+        if (tiles > 0x7fffffffL) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)tiles), block(512);
+        if (a.y_dtype == F32) hipLaunchKernelGGL((conv_direct_kernel<F32>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((conv_direct_kernel<BF16>), grid, block, 0, s, a);
+    } else if (a.Cout <= 32) launch_conv_w<8>(a, M, s);
     else if (a.Cout <= 128) launch_conv_w<4>(a, M, s);
     else launch_conv_w<2>(a, M, s);
     return hipGetLastError();
