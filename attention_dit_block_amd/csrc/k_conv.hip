@@ -243,6 +243,7 @@ __global__ __launch_bounds__(512, 2) void conv_direct_kernel(ConvArgs a) {
     const int y0 = ty * kDirTile, x0 = tx * kDirTile;
     const int TH2 = kDirTile - 1 + a.KH, TW2 = kDirTile - 1 + a.KW;
     const int nwin = a.KT * TH2 * TW2;                 // staged pixels
+    const float inv_tw = 1.0f / (float)TW2, inv_th = 1.0f / (float)TH2;
     const int ph = a.KH / 2, pw = a.KW / 2;
     const int KHW = a.KH * a.KW, taps = a.KT * KHW;
     const long K = (long)taps * a.Cin;                 // weight row length
@@ -268,9 +269,11 @@ __global__ __launch_bounds__(512, 2) void conv_direct_kernel(ConvArgs a) {
             const int c = tid + 512 * r;
             v[r] = u32x4_v{0u, 0u, 0u, 0u};
             if (c < nwin * 4) {
+                // quotients of numbers below 2^10 by divisors below 32: (n + 0.5) / d is at least
+                // 0.5 / d from an integer, far above the float error, so truncation is exact
                 const int pix = c >> 2, qq = c & 3;
-                const int xs = pix % TW2, rr = pix / TW2;
-                const int ys = rr % TH2, s = rr / TH2;
+                const int rr = (int)(((float)pix + 0.5f) * inv_tw), xs = pix - rr * TW2;
+                const int s = (int)(((float)rr + 0.5f) * inv_th), ys = rr - s * TH2;
                 const int tt = t + s - (a.KT - 1), yy = y0 + ys - ph, xx = x0 + xs - pw;
                 const int ch = c0 + qq * 8;
                 if (tt >= 0 && (unsigned)yy < (unsigned)a.H && (unsigned)xx < (unsigned)a.W && ch < a.Cin)
@@ -289,18 +292,23 @@ __global__ __launch_bounds__(512, 2) void conv_direct_kernel(ConvArgs a) {
             if (wr < a.Cout && ch < a.Cin) return ld16(Wt + (long)wr * K + (long)k * a.Cin + ch);
             return u32x4_v{0u, 0u, 0u, 0u};
         };
+        // taps frame by frame, row by row (no division in the loop), the next tap's weight
+        // fragments loaded while this one runs
         u32x4_v wb0 = wfrag(0, 0), wb1 = wfrag(0, 1);
-        for (int k = 0; k < taps; ++k) {
-            u32x4_v nb0 = wb0, nb1 = wb1;
-            if (k + 1 < taps) { nb0 = wfrag(k + 1, 0); nb1 = wfrag(k + 1, 1); }
-            const int s = k / KHW, rk = k - s * KHW, i = rk / a.KW, j = rk - i * a.KW;
-            const char* ap = win + ((s * TH2 + py + i) * TW2 + px + j) * kDirPix + 16 * h;
-            const u32x4_v fa0 = *reinterpret_cast<const u32x4_v*>(ap);
-            const u32x4_v fa1 = *reinterpret_cast<const u32x4_v*>(ap + 32);
-            acc = cmfma<BF16>(wb0, fa0, acc);
-            acc = cmfma<BF16>(wb1, fa1, acc);
-            wb0 = nb0; wb1 = nb1;
-        }
+        int k = 0;
+        for (int sf = 0; sf < a.KT; ++sf)
+            for (int i = 0; i < a.KH; ++i) {
+                const char* rowp = win + ((sf * TH2 + py + i) * TW2 + px) * kDirPix + 16 * h;
+                for (int j = 0; j < a.KW; ++j, ++k) {
+                    u32x4_v nb0 = wb0, nb1 = wb1;
+                    if (k + 1 < taps) { nb0 = wfrag(k + 1, 0); nb1 = wfrag(k + 1, 1); }
+                    const u32x4_v fa0 = *reinterpret_cast<const u32x4_v*>(rowp + j * kDirPix);
+                    const u32x4_v fa1 = *reinterpret_cast<const u32x4_v*>(rowp + j * kDirPix + 32);
+                    acc = cmfma<BF16>(wb0, fa0, acc);
+                    acc = cmfma<BF16>(wb1, fa1, acc);
+                    wb0 = nb0; wb1 = nb1;
+                }
+            }
     }
 
     // acc[q] -> pixel pp, output channel 8 (q >> 2) + 4 h + (q & 3)
