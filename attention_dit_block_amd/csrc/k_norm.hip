@@ -21,11 +21,42 @@ constexpr int kGemvWaves = 4;
 template <int DT>
 __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
     extern __shared__ float s_act[];
+    constexpr int kES = ESize<DT>::v;
+    constexpr int kElems = 16 / kES;                       // elements per 16-byte slice
+    constexpr int kQ = kElems / 4;                         // float4s of SiLU(c) per slice
     const int tid = threadIdx.x;
-    for (int i = tid; i < b.d_cond; i += 256) {
-        const float c = DT == BF16 ? bf2f(reinterpret_cast<const bf16_t*>(b.cond)[i])
-                                   : reinterpret_cast<const float*>(b.cond)[i];
-        s_act[i] = c / (1.0f + expf(-c));
+    // SiLU(c) in LDS, interleaved so that the float4s a lane needs for one slice sit 16 bytes
+    // apart across lanes (bank-conflict-free reads): element e = (it * 64 + l) * kElems + 4 q + j
+    // goes to ((it * kQ + q) * 64 + l) * 4 + j.  Staged 4 elements per thread per step, all of a
+    // pass's loads issued before the first SiLU.
+    for (int base = 0; base < b.d_cond; base += 4 * 1024) {
+        float cv[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = base + (tid + 256 * r) * 4;
+            if (e < b.d_cond) {
+                if constexpr (DT == BF16) {
+                    const u32x2_v w = *reinterpret_cast<const u32x2_v*>(reinterpret_cast<const bf16_t*>(b.cond) + e);
+                    cv[r][0] = bf_lo(w[0]); cv[r][1] = bf_hi(w[0]); cv[r][2] = bf_lo(w[1]); cv[r][3] = bf_hi(w[1]);
+                } else {
+                    const f32x4_v w = ldf4(reinterpret_cast<const float*>(b.cond) + e);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) cv[r][j] = w[j];
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = base + (tid + 256 * r) * 4;
+            if (e < b.d_cond) {
+                const int slice = e / kElems, q = (e - slice * kElems) >> 2;
+                const int it = slice >> 6, l = slice & 63;
+                f32x4_v o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = cv[r][j] / (1.0f + expf(-cv[r][j]));
+                stf4(s_act + ((it * kQ + q) * 64 + l) * 4, o);
+            }
+        }
     }
     __syncthreads();
 
@@ -33,8 +64,6 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
     const int wave = tid >> 6;
     const int total = b.p[0].rows + (b.n > 1 ? b.p[1].rows : 0);
     const int row0 = (blockIdx.x * kGemvWaves + wave) * kGemvRowsPerWave;
-    constexpr int kES = ESize<DT>::v;
-    constexpr int kElems = 16 / kES;                       // elements per 16-byte slice
     const char* wrow[kGemvRowsPerWave];
     float acc[kGemvRowsPerWave];
     bool ok[kGemvRowsPerWave];
@@ -48,26 +77,43 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
         wrow[r] = reinterpret_cast<const char*>(b.p[pi].w) + (size_t)lr * b.d_cond * kES;
         acc[r] = 0.0f;
     }
-    for (int k0 = lane * kElems; k0 < b.d_cond; k0 += 64 * kElems) {
-        float sa[8];
+    // slices of 64 lanes x kElems elements; the next slice's weights load while this one is summed
+    const int iters = (b.d_cond + 64 * kElems - 1) / (64 * kElems);
+    u32x4_v w[kGemvRowsPerWave], wn[kGemvRowsPerWave];
+    auto load = [&](u32x4_v* dst, int it) {
+        const int k0 = (it * 64 + lane) * kElems;
 #pragma unroll
-        for (int t = 0; t < kElems; ++t) sa[t] = s_act[k0 + t];
-        u32x4_v w[kGemvRowsPerWave];
+        for (int r = 0; r < kGemvRowsPerWave; ++r)
+            dst[r] = k0 < b.d_cond ? ld16(wrow[r] + (size_t)k0 * kES) : u32x4_v{0u, 0u, 0u, 0u};
+    };
+    load(w, 0);
+    for (int it = 0; it < iters; ++it) {
+        if (it + 1 < iters) load(wn, it + 1);
+        const int k0 = (it * 64 + lane) * kElems;
+        if (k0 < b.d_cond) {
+            float sa[8];
 #pragma unroll
-        for (int r = 0; r < kGemvRowsPerWave; ++r) w[r] = ld16(wrow[r] + (size_t)k0 * kES);
+            for (int q = 0; q < kQ; ++q) {
+                const f32x4_v v = ldf4(s_act + ((it * kQ + q) * 64 + lane) * 4);
 #pragma unroll
-        for (int r = 0; r < kGemvRowsPerWave; ++r) {
-            if (DT == BF16) {
+                for (int j = 0; j < 4; ++j) sa[4 * q + j] = v[j];
+            }
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    acc[r] = fmaf(bf_lo(w[r][t]), sa[2 * t], acc[r]);
-                    acc[r] = fmaf(bf_hi(w[r][t]), sa[2 * t + 1], acc[r]);
+            for (int r = 0; r < kGemvRowsPerWave; ++r) {
+                if (DT == BF16) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        acc[r] = fmaf(bf_lo(w[r][t]), sa[2 * t], acc[r]);
+                        acc[r] = fmaf(bf_hi(w[r][t]), sa[2 * t + 1], acc[r]);
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) acc[r] = fmaf(__uint_as_float(w[r][t]), sa[t], acc[r]);
                 }
-            } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) acc[r] = fmaf(__uint_as_float(w[r][t]), sa[t], acc[r]);
             }
         }
+#pragma unroll
+        for (int r = 0; r < kGemvRowsPerWave; ++r) w[r] = wn[r];
     }
 #pragma unroll
     for (int r = 0; r < kGemvRowsPerWave; ++r) {
@@ -84,7 +130,9 @@ hipError_t launch_adaln_gemv(const GemvBatch& b, hipStream_t s) {
     const int total = b.p[0].rows + (b.n > 1 ? b.p[1].rows : 0);
     const int per_block = kGemvWaves * kGemvRowsPerWave;
     const dim3 grid((total + per_block - 1) / per_block);
-    const size_t lds = (size_t)b.d_cond * sizeof(float);
+    // SiLU(c), rounded up to whole 64-lane slices (the interleaved layout spans them)
+    const int slice = 64 * (b.dtype == BF16 ? 8 : 4);
+    const size_t lds = (size_t)((b.d_cond + slice - 1) / slice) * slice * sizeof(float);
     if (b.dtype == BF16)
         hipLaunchKernelGGL(adaln_gemv_kernel<BF16>, grid, dim3(256), lds, s, b);
     else
