@@ -160,6 +160,21 @@ def test_adaln_gemv_only(dit):
     assert metric(host(mod), ref) <= 1e-5
 
 
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+def test_adaln_gemv_long_cond(dit, wdt):
+    """A conditioning vector longer than one staging pass of SiLU(c) (4096 values) and not a whole
+    number of 64-lane slices: the GEMV's multi-pass staging and partial last slice."""
+    say(f"adaln_modulate GEMV, 9000-long cond, {wdt}")
+    d_cond, d = 9000, 264
+    cond = di.draw((d_cond,), 1.0, wdt, 11, "cond")
+    w = di.draw((2 * d, d_cond), 0.02, wdt, 11, "w_mod")
+    mod = torch.empty(2 * d, dtype=torch.float32, device="cuda")
+    dit.adaln_modulate(dev(cond, wdt), dev(w, wdt), 2, d, mod)
+    torch.cuda.synchronize()
+    ref = o.adaln_modulation(o.widen(w, wdt), o.widen(cond, wdt))
+    assert metric(host(mod), ref) <= 1e-5
+
+
 ATTN_CASES = [
     ("f32", 80, 2),
     ("f32", 333, 1),
