@@ -122,6 +122,8 @@ ADALN_CASES = [
     ("bf16", "bf16", "bf16", 3072, 6, 512),
     ("bf16", "bf16", "f16", 3072, 3, 37),     # single-stream block: 3 chunks, ragged rows
     ("bf16", "bf16", "f16", 264, 6, 5),       # d not a multiple of 512
+    ("bf16", "bf16", "f16", 8192, 3, 3),      # the widest rows (16 chunks per lane, 64 KB of LDS)
+    ("bf16", "f32", "bf16", 4104, 3, 9),      # 16 chunks per lane, the last partly filled
 ]
 
 
