@@ -122,6 +122,8 @@ def run3(dit, B, T, H, W, cin, cout, kt, k, bias, ydt, seed, sample=None):
     (1, 2, 4, 4, 64, 16, 3, 1, True, torch.float32),     # more taps than frames: the first reach before 0
     (1, 3, 8, 12, 96, 3, 3, 3, True, torch.float32),     # the decoder head's shape: 96 -> 3, 3x3x3
     (2, 2, 5, 6, 192, 192, 3, 3, False, torch.bfloat16),  # 192 channels (the 240 x 416 stage)
+    (1, 3, 6, 7, 64, 16, 3, 5, True, torch.float32),     # narrow, but its 3x20x20-pixel window exceeds
+                                                         # the direct kernel's LDS: 32-wide implicit GEMM
 ])
 def test_conv3d_causal_shapes(dit, B, T, H, W, cin, cout, kt, k, bias, ydt):
     run3(dit, B, T, H, W, cin, cout, kt, k, bias, ydt, 64)
