@@ -18,7 +18,7 @@
 // reads are bank-conflict free.  The MFMA computes D[n][m], so each lane ends with four
 // consecutive output columns of one row and the epilogue reads / writes 8-16 B per lane.
 // Workgroups are remapped so each XCD gets a contiguous range of tiles, rastered in groups of
-// 8 M-tiles.
+// 4 M-tiles (8 and 16 were slower at 512 + 16384 tokens, the same at 512 + 4096).
 //
 // fp32 path: a plain LDS-tiled FMA kernel (no reduced-precision matrix math).
 #include <atomic>
@@ -42,7 +42,7 @@ __device__ __forceinline__ void tile_of(const GemmBatch& b, int L, int& pi, int&
     // block of about G x (32 / G) tiles, whose A and B tiles L2 shares.
     pi = (b.n > 1 && L >= b.p[1].tile_begin) ? 1 : 0;
     const GemmProblem& P = b.p[pi];
-    const int G0 = b.group_m > 0 ? b.group_m : 8;
+    const int G0 = b.group_m > 0 ? b.group_m : 4;
     const int t = L - P.tile_begin;
     const int per_group = G0 * P.tiles_n;
     const int g = t / per_group;

@@ -88,7 +88,7 @@ struct GemmBatch {
     int a_dtype;        // F32 (fp32 path, fp32 weights), BF16 (bf16 weights) or F16 (bf16 weights,
                         // converted to fp16 while they are staged)
     bool b_f16;         // F16 activations only: the weights are fp16 copies, staged as they are
-    int group_m;        // tile raster: groups of group_m M-tiles, N-major inside a group (0: 8)
+    int group_m;        // tile raster: groups of group_m M-tiles, N-major inside a group (0: 4)
     int total_tiles;    // filled by the launcher
     // Stream-K scratch (16-B-aligned device memory of gemm_sk_scratch_bytes(), or null: one
     // workgroup per tile).  The launcher fills the rest: a persistent grid of sk_grid
