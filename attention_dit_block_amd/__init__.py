@@ -25,11 +25,12 @@ __all__ = [
     "StreamWeightsFp8", "block_fp8_workspace_size", "block_forward_fp8", "SingleWeightsFp8",
     "single_block_fp8_workspace_size", "single_block_forward_fp8", "conv2d", "conv3d_causal",
     "convert_bf16_to_f16",
-    "last_error", "launch_count", "abi_version",
+    "last_error", "launch_count", "abi_version", "workspace_flags", "set_split_wait_limit", "DIT_RANGE_F16",
     "timing_begin", "timing_end", "timing_read",
 ]
 
 DIT_F32, DIT_BF16, DIT_F16 = 0, 1, 2
+DIT_RANGE_F16 = 1
 DIT_OK, DIT_ERR_INVALID_ARG, DIT_ERR_UNSUPPORTED, DIT_ERR_WORKSPACE, DIT_ERR_HIP = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "DIT_OK", 1: "DIT_ERR_INVALID_ARG", 2: "DIT_ERR_UNSUPPORTED",
                 3: "DIT_ERR_WORKSPACE", 4: "DIT_ERR_HIP"}
@@ -114,6 +115,8 @@ _conv = _sig("dit_conv2d", _i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _
 _last_error = _sig("dit_last_error", ctypes.c_char_p, [])
 _launch_count = _sig("dit_launch_count", ctypes.c_uint64, [])
 _abi = _sig("dit_abi_version", _i, [])
+_wsflags = _sig("dit_workspace_flags", _i, [_vp, _vp, ctypes.POINTER(ctypes.c_uint32)])
+_split_wait = _sig("dit_set_split_wait_limit", None, [_i])
 _tbegin = _sig("dit_timing_begin", _i, [_i])
 _tend = _sig("dit_timing_end", _i, [])
 _tread = _sig("dit_timing_read", _i, [_i, ctypes.c_char_p, _i, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_double)])
@@ -126,7 +129,7 @@ EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", 
             "dit_quantize_fp8", "dit_linear_fp8", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
             "dit_single_block_fp8_workspace_size", "dit_single_block_forward_fp8",
             "dit_conv2d", "dit_conv3d_causal", "dit_convert_bf16_to_f16",
-            "dit_last_error", "dit_launch_count",
+            "dit_last_error", "dit_launch_count", "dit_workspace_flags", "dit_set_split_wait_limit",
             "dit_abi_version", "dit_timing_begin", "dit_timing_end", "dit_timing_read"]
 
 
@@ -147,6 +150,22 @@ def launch_count() -> int:
 
 def abi_version() -> int:
     return int(_abi())
+
+
+def workspace_flags(workspace) -> int:
+    """Range flags of the last block / step call that used ``workspace`` (waits for the current
+    stream's work): DIT_RANGE_F16 set when an fp16 activation left fp16's finite range."""
+    import torch
+    out = ctypes.c_uint32(0)
+    _check(_wsflags(_ptr(workspace, "workspace"), torch.cuda.current_stream().cuda_stream, ctypes.byref(out)),
+           "dit_workspace_flags")
+    return int(out.value)
+
+
+def set_split_wait_limit(polls: int) -> None:
+    """Test hook: bound on a split unit's owner waiting for a piece before it computes the piece
+    itself (this thread's later calls; < 0 restores the default)."""
+    _split_wait(int(polls))
 
 
 def _check(rc: int, fn: str) -> None:

@@ -117,6 +117,18 @@ __device__ __forceinline__ void store1(char* p, float f) {
     else *reinterpret_cast<unsigned short*>(p) = (unsigned short)(pack2<DT>(f, 0.0f) & 0xffffu);
 }
 
+// fp16 range check of an fp32 result about to be rounded to fp16: true when it is NaN or
+// |x| > 65504 (it would not stay a finite fp16 value).
+__device__ __forceinline__ bool f16_out_of_range(float x) { return !(fabsf(x) <= 65504.0f); }
+__device__ __forceinline__ bool f16_out_of_range4(const float* x) {
+    return (int)f16_out_of_range(x[0]) + (int)f16_out_of_range(x[1]) + (int)f16_out_of_range(x[2]) +
+           (int)f16_out_of_range(x[3]) != 0;
+}
+// OR kRangeF16 into the range-flag word (vector atomic; only lanes that saw a bad value write).
+__device__ __forceinline__ void raise_range_flag(unsigned* flag, bool bad) {
+    if (bad && flag) __hip_atomic_fetch_or(flag, kRangeF16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Wave-wide reductions (64 lanes).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -141,45 +153,94 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
 
 // ---- stream-K plumbing.  A persistent grid of G workgroups splits S work steps evenly; a piece
 // of a work unit that some workgroup does not finish itself is handed over through a partial
-// result and a 64-bit flag.  Partials move as 16-byte sc1 buffer loads and stores and flags as
+// result and a 32-bit flag.  Partials move as 16-byte sc1 buffer loads and stores and flags as
 // relaxed device-scope atomics (sc1 accesses as well): on gfx950 these go to the coherence point
 // past the XCD-private L2s, so no cache-wide writeback or invalidate (which a release / acquire
 // fence would issue, for the whole XCD's L2) is needed.  Ordering comes from waiting for the
 // partial's stores to be acknowledged before the flag is raised.
+//
+// Hand-over protocol.  A flag holding anything but this launch's tag or tag | kSkAbandoned means
+// "not published" (the workspace is never zeroed: a fresh one holds arbitrary bits, a reused one
+// whatever earlier launches left):
+//   producer: partial stored, then the flag swapped from its current value to tag -- unless it
+//             reads tag | kSkAbandoned, i.e. the owner has given up on the piece: then it resets the
+//             flag to 0.
+//   owner:    waits (bounded) for flag == tag, then takes the partial and resets the flag to 0.  When
+//             the wait expires it swaps the flag from its current value to tag | kSkAbandoned and
+//             computes the piece itself -- unless it reads tag, i.e. the partial arrived meanwhile:
+//             then it takes it as usual.
+// Both swaps are compare-and-swaps on the value just read; apart from the owner's final reset, each
+// side writes the flag at most once, so a failed swap means the other side's swap came first.
+// Exactly one side wins: a piece is never dropped nor counted twice, a late producer never leaves a raised flag behind (a replay
+// of a captured launch reuses its tag), and the result does not depend on every workgroup of the
+// grid being resident at once.
+// A wait bound of 0 turns the hand-over off: producers do not publish and owners compute every
+// piece themselves, touching no flag (a host-side test setting that exercises the owners' path).
 // First step of workgroup g's share.
 __device__ __forceinline__ long sk_begin(long S, int g, int G) { return S * g / G; }
 
+constexpr unsigned kSkAbandoned = 1u << 31;   // launch tags stay below 2^31
 constexpr int kCachePolicySc1 = 16;      // cache-policy operand of the buffer builtins: sc1
-// A partial slot (workgroup-uniform base) as a raw buffer; offsets in bytes.
+// A partial slot (workgroup-uniform base) as a raw buffer; offsets in bytes: a per-lane part `off`
+// and a uniform part `soff` (a constant in a scalar register; per-lane offsets are then one VGPR for
+// a whole tile's accesses).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_slot(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
 }
-__device__ __forceinline__ void sk_store(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d) {
+__device__ __forceinline__ void sk_store(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff, float a, float b,
+                                         float c, float d) {
     const u32x4_v v = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCachePolicySc1);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, soff, kCachePolicySc1);
 }
-__device__ __forceinline__ float4 sk_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4_v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicySc1);
+__device__ __forceinline__ float4 sk_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    const u32x4_v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kCachePolicySc1);
     return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
 }
-// Publish: every thread's partial stores acknowledged, then thread 0 raises the flag.
-__device__ __forceinline__ void sk_raise(unsigned long long* flag, unsigned long long tag) {
+// Publish: every thread's partial stores acknowledged, then thread 0 raises the flag (or, if the
+// owner has given up on the piece, resets it).
+__device__ __forceinline__ void sk_raise(unsigned* flag, unsigned tag, int spins) {
+    if (spins == 0) return;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(flag, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Take: thread 0 waits for the flag (bounded: every workgroup of the grid is resident, so the
-// piece is being computed; on expiry the unit is finished without it), then clears it, so a replay
-// of the same launch (same tag, e.g. from a captured graph) waits for the new piece.
-__device__ __forceinline__ void sk_take(unsigned long long* flag, unsigned long long tag) {
     if (threadIdx.x == 0) {
-        for (int spin = 0; spin < (1 << 22); ++spin) {
-            if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) break;
+        unsigned v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v == (tag | kSkAbandoned) ||
+            !__hip_atomic_compare_exchange_strong(flag, &v, tag, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT))
+            __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);     // the owner gave up
+    }
+}
+// Take (every thread of the workgroup calls it): true = the piece's partial is published and may be
+// read (the flag is reset already: the partial stays in place until this launch ends); false = the
+// owner claimed the piece and computes it itself.  `spins` bounds the wait (0: give up at once).
+// Thread 0 decides; the rest of the workgroup reads the decision from the flag itself between two
+// barriers (tag: taken; anything else: claimed -- after a claim only the producer writes the flag,
+// and only from tag | kSkAbandoned to 0).  The kernels avoid plain LDS stores (an LDS broadcast here
+// would make the compiler wait for every in-flight global -> LDS load before any LDS read).
+__device__ __forceinline__ bool sk_take(unsigned* flag, unsigned tag, int spins) {
+    if (spins == 0) return false;
+    if (threadIdx.x == 0) {
+        bool got = false;
+        for (int spin = 0;; ++spin) {
+            if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) { got = true; break; }
+            if (spin >= spins) break;
             __builtin_amdgcn_s_sleep(2);
+        }
+        if (!got) {
+            // claim the piece, unless the producer published in between (the swap then fails)
+            unsigned v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (v != tag)
+                __hip_atomic_compare_exchange_strong(flag, &v, tag | kSkAbandoned, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // workgroup-uniform; readfirstlane tells the compiler so (a branch on it stays scalar)
+    const bool ok = __builtin_amdgcn_readfirstlane(
+                        (int)(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag)) != 0;
+    __syncthreads();
+    if (ok && threadIdx.x == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return ok;
 }
 
 }  // namespace dit

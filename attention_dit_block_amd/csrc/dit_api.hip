@@ -141,7 +141,7 @@ int validate_config(const dit_block_config* c) {
 
 // Workspace plan: 256-byte aligned sub-buffers.
 struct WsPlan {
-    size_t mod, act, qkv, o, h, f, of, sk, sk_bytes, ask, ask_bytes, q8, sq, total;
+    size_t flags, mod, act, qkv, o, h, f, of, sk, sk_bytes, ask, ask_bytes, q8, sq, total;
 };
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 WsPlan plan_workspace(const dit_block_config* c, int single, bool fp8 = false) {
@@ -149,6 +149,7 @@ WsPlan plan_workspace(const dit_block_config* c, int single, bool fp8 = false) {
     WsPlan p{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
+    p.flags = take(4);          // the call's range-flag word, first in every plan (offset 0)
     if (!single) {
         p.mod = take(2 * 6 * d * 4);
         p.act = take(n * d * es);
@@ -184,6 +185,21 @@ extern "C" {
 
 const char* dit_last_error(void) { return tl_err; }
 uint64_t dit_launch_count(void) { return tl_launches; }
+
+void dit_set_split_wait_limit(int polls) { set_sk_spin_limit(polls); }
+
+int dit_workspace_flags(const void* workspace, void* stream, uint32_t* flags) {
+    clear_err();
+    if (!flags) return fail(DIT_ERR_INVALID_ARG, "flags is NULL");
+    DIT_TRY(check_ptr(workspace, "workspace"));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint32_t v = 0;
+    hipError_t e = hipMemcpyAsync(&v, workspace, sizeof v, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(DIT_ERR_HIP, "reading the flag word failed: %s", hipGetErrorString(e));
+    *flags = v;
+    return DIT_OK;
+}
 int dit_abi_version(void) { return DIT_ABI_VERSION; }
 
 int dit_adaln_modulate(int dtype, void* stream, const void* cond, int d_cond, const void* w_mod, int n_chunks,
@@ -349,7 +365,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
                               const dit_stream_weights* img, const void* cond, const int32_t* pos, const void* x_txt,
                               const void* x_img, void* y_txt, void* y_img, void* workspace, size_t ws_bytes,
                               void* stream, const float* mod_pre, const dit_stream_weights_fp8* t8 = nullptr,
-                              const dit_stream_weights_fp8* i8 = nullptr) {
+                              const dit_stream_weights_fp8* i8 = nullptr, bool clear_flags = true) {
     clear_err();
     const bool fp8 = t8 != nullptr;
     DIT_TRY(fp8 ? validate_fp8_config(cfg) : validate_config(cfg));
@@ -394,10 +410,11 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     char* ob = ws + W.o;
     float* h = reinterpret_cast<float*>(ws + W.h);
     char* f = ws + W.f;
+    unsigned* flag = reinterpret_cast<unsigned*>(ws + W.flags);
     const size_t es = esize(c.act_dtype);     // activation element size
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-    // 1. AdaLN vectors of both streams
+    // 1. AdaLN vectors of both streams (this first kernel also resets the range-flag word)
     if (!mod_pre) {
         GemvBatch g{};
         g.p[0] = {wmod_t, mod_t, 6 * d};
@@ -406,6 +423,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
         g.cond = cond;
         g.d_cond = c.d_cond;
         g.dtype = c.dtype;
+        g.clear_flag = clear_flags ? flag : nullptr;
         DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
     }
 
@@ -414,7 +432,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     int nm = 0;
     if (nt) m.p[nm++] = {x_txt, d, c.x_dtype, act, d, mod_t + 0 * d, mod_t + 1 * (size_t)d, nt};
     if (ni) m.p[nm++] = {x_img, d, c.x_dtype, act + (size_t)nt * d * es, d, mod_i + 0 * d, mod_i + 1 * (size_t)d, ni};
-    m.n = nm; m.d = d; m.eps = c.eps; m.out_dtype = c.act_dtype;
+    m.n = nm; m.d = d; m.eps = c.eps; m.out_dtype = c.act_dtype; m.range_flag = flag;
     // fp8 products: a goes straight to e4m3 codes with per-row scales
     uint8_t* q8 = fp8 ? reinterpret_cast<uint8_t*>(ws + W.q8) : nullptr;
     float* sq = fp8 ? reinterpret_cast<float*>(ws + W.sq) : nullptr;
@@ -452,9 +470,11 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
         if (nt) b.p[b.n++] = fp8_problem(0, nt, d, t8->w_qkv, t8->s_qkv, qkv, 3L * d, c.act_dtype, 3 * d, EPI_STORE);
         if (ni) b.p[b.n++] = fp8_problem(nt, ni, d, i8->w_qkv, i8->s_qkv, qkv + (size_t)nt * 3 * d * es, 3L * d,
                                          c.act_dtype, 3 * d, EPI_STORE);
+        b.range_flag = flag;
         DIT_TRY(launch("gemm_fp8_qkv", s, [&] { return launch_gemm_fp8(b, s); }));
     } else {
     GemmBatch gq{};
+    gq.range_flag = flag;
     gq.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     gq.a_dtype = c.act_dtype;
     gq.b_f16 = c.gemm_w_dtype == DIT_F16;
@@ -517,7 +537,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     if (nt) m2.p[nm++] = {h, d, DIT_F32, act, d, mod_t + 3 * (size_t)d, mod_t + 4 * (size_t)d, nt};
     if (ni) m2.p[nm++] = {h + (size_t)nt * d, d, DIT_F32, act + (size_t)nt * d * es, d, mod_i + 3 * (size_t)d,
                           mod_i + 4 * (size_t)d, ni};
-    m2.n = nm; m2.d = d; m2.eps = c.eps; m2.out_dtype = c.act_dtype;
+    m2.n = nm; m2.d = d; m2.eps = c.eps; m2.out_dtype = c.act_dtype; m2.range_flag = flag;
     if (fp8) to_fp8(m2);
     DIT_TRY(launch(fp8 ? "modulate_h_fp8" : "modulate_h", s, [&] { return launch_modulate(m2, s); }));
 
@@ -533,9 +553,11 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
                                    EPI_SWIGLU);
             b.p[b.n++].up_off = F;
         }
+        b.range_flag = flag;
         DIT_TRY(launch("gemm_fp8_ffn_in_swiglu", s, [&] { return launch_gemm_fp8(b, s); }));
     } else {
     GemmBatch gf{};
+    gf.range_flag = flag;
     gf.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
     gf.a_dtype = c.act_dtype;
     gf.b_f16 = c.gemm_w_dtype == DIT_F16;
@@ -609,7 +631,8 @@ int dit_block_forward_fp8(const dit_block_config* cfg, const dit_stream_weights_
 // mod_pre: the [3d] fp32 AdaLN vectors computed by the caller, or NULL (from w->w_mod and cond).
 static int single_block_impl(const dit_block_config* cfg, const dit_single_weights* w, const void* cond,
                              const int32_t* pos, const void* x, void* y, void* workspace, size_t ws_bytes,
-                             void* stream, const float* mod_pre, const dit_single_weights_fp8* w8 = nullptr) {
+                             void* stream, const float* mod_pre, const dit_single_weights_fp8* w8 = nullptr,
+                             bool clear_flags = true) {
     clear_err();
     const bool fp8 = w8 != nullptr;
     DIT_TRY(fp8 ? validate_fp8_config(cfg) : validate_config(cfg));
@@ -649,6 +672,7 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
     char* of = ws + W.of;
     uint8_t* q8 = fp8 ? reinterpret_cast<uint8_t*>(ws + W.q8) : nullptr;
     float* sq = fp8 ? reinterpret_cast<float*>(ws + W.sq) : nullptr;
+    unsigned* flag = reinterpret_cast<unsigned*>(ws + W.flags);
     const size_t es = esize(c.act_dtype);     // activation element size
     const long ldof = (long)d + F;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -657,12 +681,13 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
         GemvBatch g{};
         g.p[0] = {w_mod, mod, 3 * d};
         g.n = 1; g.cond = cond; g.d_cond = c.d_cond; g.dtype = c.dtype;
+        g.clear_flag = clear_flags ? flag : nullptr;
         DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
     }
 
     ModBatch m{};
     m.p[0] = {x, d, c.x_dtype, act, d, mod, mod + d, n};
-    m.n = 1; m.d = d; m.eps = c.eps; m.out_dtype = c.act_dtype;
+    m.n = 1; m.d = d; m.eps = c.eps; m.out_dtype = c.act_dtype; m.range_flag = flag;
     if (fp8) {
         // a goes straight to e4m3 codes with per-row scales
         m.p[0].out = q8; m.p[0].out_scale = sq; m.out_dtype = FP8_ROWS;
@@ -686,10 +711,12 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
                        of + (size_t)d * es, ldof, F, EPI_SWIGLU);
         bg.p[0].up_off = F;
         bg.n = 1;
+        bq.range_flag = bg.range_flag = flag;
         DIT_TRY(launch("gemm_fp8_linear1_qkv", s, [&] { return launch_gemm_fp8(bq, s); }));
         DIT_TRY(launch("gemm_fp8_linear1_gu", s, [&] { return launch_gemm_fp8(bg, s); }));
     } else {
         GemmBatch g1{};
+        g1.range_flag = flag;
         g1.sk_scratch = W.sk_bytes ? ws + W.sk : nullptr;
         g1.a_dtype = c.act_dtype;
         g1.b_f16 = c.gemm_w_dtype == DIT_F16;
@@ -900,9 +927,12 @@ static int step_forward_impl(const dit_block_config* cfg, int n_double, const di
         return fail(DIT_ERR_INVALID_ARG, "workspace overlaps an input or y");
     if (overlap(ry, rxt) || overlap(ry, rxi)) return fail(DIT_ERR_INVALID_ARG, "y overlaps x_txt / x_img");
 
-    // shared modulation: one AdaLN GEMV launch per block kind for the whole step
+    // shared modulation: one AdaLN GEMV launch per block kind for the whole step.  The step's first
+    // kernel resets the range-flag word (the blocks' kernels then only raise it).
     float* mod_d = nullptr;
     float* mod_s = nullptr;
+    unsigned* flag = reinterpret_cast<unsigned*>(workspace);
+    bool cleared = false;
     if (shared) {
         hipStream_t s = reinterpret_cast<hipStream_t>(stream);
         mod_d = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + up256(blocks_need));
@@ -912,12 +942,16 @@ static int step_forward_impl(const dit_block_config* cfg, int n_double, const di
             g.p[0] = {shared[0], mod_d, (int)(6 * d)};
             g.p[1] = {shared[1], mod_d + 6 * d, (int)(6 * d)};
             g.n = 2; g.cond = cond; g.d_cond = c.d_cond; g.dtype = c.dtype;
+            g.clear_flag = cleared ? nullptr : flag;
+            cleared = true;
             DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
         }
         if (n_single > 0) {
             GemvBatch g{};
             g.p[0] = {shared[2], mod_s, (int)(3 * d)};
             g.n = 1; g.cond = cond; g.d_cond = c.d_cond; g.dtype = c.dtype;
+            g.clear_flag = cleared ? nullptr : flag;
+            cleared = true;
             DIT_TRY(launch("adaln_gemv", s, [&] { return launch_adaln_gemv(g, s); }));
         }
     }
@@ -932,12 +966,14 @@ static int step_forward_impl(const dit_block_config* cfg, int n_double, const di
     for (int b = 0; b < n_double; ++b) {
         const dit_block_config* cb = b == 0 ? &c_first : &c_rest;
         DIT_TRY(block_forward_impl(cb, &txt[b], &img[b], cond, pos, b == 0 ? x_txt : y_txt, b == 0 ? x_img : y_img,
-                                   y_txt, y_img, workspace, blocks_need, stream, mod_d));
+                                   y_txt, y_img, workspace, blocks_need, stream, mod_d, nullptr, nullptr, !cleared));
+        cleared = true;
     }
     for (int b = 0; b < n_single; ++b) {
         const bool first = n_double == 0 && b == 0;
         DIT_TRY(single_block_impl(first ? &c_first : &c_rest, &single[b], cond, pos, first ? x_txt : y, y, workspace,
-                                  blocks_need, stream, mod_s));
+                                  blocks_need, stream, mod_s, nullptr, !cleared));
+        cleared = true;
     }
     return DIT_OK;
 }
@@ -974,10 +1010,10 @@ size_t dit_timestep_embedding_workspace_size(int freq_dim, int d) {
     return temb_ws(freq_dim, d);
 }
 
-int dit_timestep_embedding(int dtype, void* stream, const float* t, const float* g, const void* w_t_in,
-                           const void* w_t_out, const void* w_g_in, const void* w_g_out, int freq_dim, int d,
-                           float max_period, float time_factor, void* cond_out, void* workspace, size_t ws_bytes) {
-    clear_err();
+// Checks of the timestep embedding's arguments other than its scratch.
+static int check_temb(int dtype, const float* t, const float* g, const void* w_t_in, const void* w_t_out,
+                      const void* w_g_in, const void* w_g_out, int freq_dim, int d, float max_period,
+                      float time_factor, const void* cond_out) {
     if (!valid_wdtype(dtype)) return fail(DIT_ERR_INVALID_ARG, "dtype must be DIT_BF16 or DIT_F32");
     if (freq_dim < 8 || freq_dim % 8 || freq_dim > 16384)
         return fail(DIT_ERR_INVALID_ARG, "freq_dim = %d must be a multiple of 8 in [8, 16384]", freq_dim);
@@ -991,17 +1027,16 @@ int dit_timestep_embedding(int dtype, void* stream, const float* t, const float*
         DIT_TRY(check_ptr(w_g_in, "w_g_in"));
         DIT_TRY(check_ptr(w_g_out, "w_g_out"));
     }
-    DIT_TRY(check_ptr(cond_out, "cond_out"));
-    DIT_TRY(check_ptr(workspace, "workspace"));
-    const size_t need = temb_ws(freq_dim, d);
-    if (ws_bytes < need) return fail(DIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
-    const Range rws{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
-    if (overlap(rws, range_of(cond_out, 1, d, d, dtype))) return fail(DIT_ERR_INVALID_ARG, "cond_out overlaps the workspace");
-    char* ws = reinterpret_cast<char*>(workspace);
+    return check_ptr(cond_out, "cond_out");
+}
+
+// The launch sequence on scratch `ws` of temb_ws(freq_dim, d) bytes (arguments checked).
+static int temb_launch(int dtype, hipStream_t s, const float* t, const float* g, const void* w_t_in,
+                       const void* w_t_out, const void* w_g_in, const void* w_g_out, int freq_dim, int d,
+                       float max_period, float time_factor, void* cond_out, char* ws) {
     float* emb = reinterpret_cast<float*>(ws);
     float* hid = reinterpret_cast<float*>(ws + up256((size_t)freq_dim * 4));
     float* acc = reinterpret_cast<float*>(ws + up256((size_t)freq_dim * 4) + up256((size_t)d * 4));
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // c = W_out . SiLU(W_in . emb(value)), summed over the timestep and (optionally) the guidance
     for (int pass = 0; pass < (g ? 2 : 1); ++pass) {
         const float* val = pass ? g : t;
@@ -1011,8 +1046,21 @@ int dit_timestep_embedding(int dtype, void* stream, const float* t, const float*
         DIT_TRY(launch("embed_gemv_in", s, [&] { return launch_vec_gemv(wi, dtype, d, freq_dim, emb, false, hid, false, s); }));
         DIT_TRY(launch("embed_gemv_out", s, [&] { return launch_vec_gemv(wo, dtype, d, d, hid, true, acc, pass > 0, s); }));
     }
-    DIT_TRY(launch("cast", s, [&] { return launch_cast(acc, cond_out, d, dtype, s); }));
-    return DIT_OK;
+    return launch("cast", s, [&] { return launch_cast(acc, cond_out, d, dtype, s); });
+}
+
+int dit_timestep_embedding(int dtype, void* stream, const float* t, const float* g, const void* w_t_in,
+                           const void* w_t_out, const void* w_g_in, const void* w_g_out, int freq_dim, int d,
+                           float max_period, float time_factor, void* cond_out, void* workspace, size_t ws_bytes) {
+    clear_err();
+    DIT_TRY(check_temb(dtype, t, g, w_t_in, w_t_out, w_g_in, w_g_out, freq_dim, d, max_period, time_factor, cond_out));
+    DIT_TRY(check_ptr(workspace, "workspace"));
+    const size_t need = temb_ws(freq_dim, d);
+    if (ws_bytes < need) return fail(DIT_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+    const Range rws{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+    if (overlap(rws, range_of(cond_out, 1, d, d, dtype))) return fail(DIT_ERR_INVALID_ARG, "cond_out overlaps the workspace");
+    return temb_launch(dtype, reinterpret_cast<hipStream_t>(stream), t, g, w_t_in, w_t_out, w_g_in, w_g_out, freq_dim,
+                       d, max_period, time_factor, cond_out, reinterpret_cast<char*>(workspace));
 }
 
 int dit_linear(int dtype, void* stream, const void* x, int x_dtype, long ld_x, const void* w, int m, int n, int k,

@@ -39,39 +39,45 @@
 
 namespace dit {
 
-// waves (of 32 queries each) per workgroup: 8 (one workgroup per CU; each staged K/V tile serves
-// 256 queries, 3% faster at 4608 tokens) or 4 (two workgroups per CU)
-#ifndef DIT_ATTN_WAVES
-#define DIT_ATTN_WAVES 8
-#endif
-constexpr int kAttnWaves = DIT_ATTN_WAVES;
+// waves (of 32 queries each) per workgroup: 8, one workgroup per CU, so each staged K/V tile
+// serves 256 queries (4-wave workgroups, two per CU, measured slower: 342 against 277 us at 4608
+// tokens, 4.33 against 3.36 ms at 16896)
+constexpr int kAttnWaves = 8;
 constexpr int AQ = 32 * kAttnWaves;     // queries per workgroup
 // How a workgroup finishes a (head, query tile) unit it ran key tiles [kb, ke) of:
 enum UnitKind {
     UNIT_FULL = 0,      // all key tiles: normalise and store O
     UNIT_OWNER = 1,     // key tiles from 0: merge the partials of the workgroups holding the rest, store
-    UNIT_PARTIAL = 2    // later key tiles: publish (running max, running sum, unnormalised O)
+    UNIT_PARTIAL = 2,   // later key tiles: publish (running max, running sum, unnormalised O)
+    UNIT_OWNER_CONT = 3 // an owner's continuation: key tiles of a piece whose partial did not arrive,
+                        // merged with the owner's state from its carry slot, then as UNIT_OWNER
 };
 
-// Stream-K scratch: [sk_grid] partial slots, then [sk_grid] 64-bit flags.  In a slot, lane l of
-// wave w keeps float4 c (c < 16: its O accumulators; c = 16: running max, running sum) at index
-// (w * 17 + c) * 64 + l.
+// Stream-K scratch: [sk_grid] partial slots, [sk_grid] carry slots (an owner's state while it
+// computes a missing piece), then [sk_grid] 32-bit flags.  In a slot, lane l of wave w keeps float4
+// c (c < 16: its O accumulators; c = 16: running max, running sum) at index (w * 17 + c) * 64 + l.
 constexpr int kPartF4 = 17;
 constexpr int kSlotF4 = kAttnWaves * kPartF4 * 64;
 __device__ __forceinline__ float4* attn_partial(const AttnArgs& a, int g) {
     return reinterpret_cast<float4*>(a.sk_scratch) + (size_t)g * kSlotF4;
 }
-__device__ __forceinline__ unsigned long long* attn_flag(const AttnArgs& a, int g) {
-    return reinterpret_cast<unsigned long long*>(reinterpret_cast<float4*>(a.sk_scratch) +
-                                                 (size_t)a.sk_grid * kSlotF4) + g;
+__device__ __forceinline__ float4* attn_carry(const AttnArgs& a, int g) {
+    return reinterpret_cast<float4*>(a.sk_scratch) + (size_t)(a.sk_grid + g) * kSlotF4;
+}
+__device__ __forceinline__ unsigned* attn_flag(const AttnArgs& a, int g) {
+    return reinterpret_cast<unsigned*>(reinterpret_cast<float4*>(a.sk_scratch) +
+                                                 (size_t)2 * a.sk_grid * kSlotF4) + g;
 }
 
 // One (head, query tile) unit L = head * nq + query tile over key tiles [kb, ke).
 // NEG: softmax_scale < 0 (the row max of the scaled scores is then the min of the raw ones).
+// Returns -1, or (an owner whose piece jn did not arrive; its state is in its carry slot) the index
+// jn of the next workgroup whose piece is still to be merged, with the missing piece's key tiles in
+// [ckb, cke): the driver then runs that continuation as the workgroup's next item.
 template <int DT, bool NEG>
-__device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem_k0, char* smem_k1, char* smem_v0,
-                                               char* smem_v1, int L, int kb, int ke, int kind,
-                                               int g, long S, long t_end) {
+__device__ __forceinline__ int attention_unit(const AttnArgs& a, char* smem_k0, char* smem_k1, char* smem_v0,
+                                              char* smem_v1, int L, int kb, int ke, int kind,
+                                              int g, long S, long t_end, int jn0, int& ckb, int& cke) {
     constexpr int LPW = 16 / kAttnWaves;    // 1 KB load instructions per wave per K (or V) tile
     typedef typename AFrag<DT>::T FragT;
     // The two slots of the K ring and of the V ring are LDS arrays of their own, so the compiler
@@ -323,48 +329,82 @@ __device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem_k0,
         step.template operator()<0, true>(j, sA, sB);
     }
 
-    if (kind == UNIT_PARTIAL) {
-        const __amdgpu_buffer_rsrc_t dst = sk_slot(attn_partial(a, g));
-        const uint32_t off = (uint32_t)((wave * kPartF4 * 64 + lane) * 16);
+    // per-lane byte offset of float4 0 in a stream-K slot (computed where it is used, so it is not
+    // held in a register across the pipeline above)
+    auto slot_lane = [&]() { return (uint32_t)((wave * kPartF4 * 64 + lane) * 16); };
+    // merges the state in a stream-K slot (a piece's partial or the carry): m = max(m_a, m_b),
+    // O = O_a 2^(m_a - m) + O_b 2^(m_b - m), the same for the running sum
+    auto merge_slot = [&](const float4* slot) {
+        const __amdgpu_buffer_rsrc_t src = sk_slot(slot);
+        const uint32_t slot_off = slot_lane();
+        const float4 ml = sk_load(src, slot_off + 16 * 64 * 16, 0);
+        const float m_new = fmaxf(m_run, ml.x);
+        const float ca = __builtin_amdgcn_exp2f(m_run - m_new), cb = __builtin_amdgcn_exp2f(ml.x - m_new);
+        m_run = m_new;
+        l_run = fmaf(l_run, ca, ml.y * cb);
+        // 4 loads in flight at a time: O and the pipeline state fill most of the registers
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 v = sk_load(src, slot_off + (4 * eb + i) * 64 * 16, 0);
+                o[eb][4 * i] = fmaf(o[eb][4 * i], ca, v.x * cb);
+                o[eb][4 * i + 1] = fmaf(o[eb][4 * i + 1], ca, v.y * cb);
+                o[eb][4 * i + 2] = fmaf(o[eb][4 * i + 2], ca, v.z * cb);
+                o[eb][4 * i + 3] = fmaf(o[eb][4 * i + 3], ca, v.w * cb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // stores the state (unnormalised O, running max, running sum) into a stream-K slot
+    auto store_slot = [&](float4* slot) {
+        const __amdgpu_buffer_rsrc_t dst = sk_slot(slot);
+        const uint32_t slot_off = slot_lane();
 #pragma unroll
         for (int eb = 0; eb < 4; ++eb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                sk_store(dst, off + (4 * eb + i) * 64 * 16, o[eb][4 * i], o[eb][4 * i + 1], o[eb][4 * i + 2],
+                sk_store(dst, slot_off + (4 * eb + i) * 64 * 16, 0, o[eb][4 * i], o[eb][4 * i + 1], o[eb][4 * i + 2],
                          o[eb][4 * i + 3]);
-        sk_store(dst, off + 16 * 64 * 16, m_run, l_run, 0.0f, 0.0f);
-        sk_raise(attn_flag(a, g), a.epoch);
-        return;
-    }
-    if (kind == UNIT_OWNER) {
-        // The rest of this unit's key tiles, up to stream-K step t_end, went to the next
-        // workgroups g+1, g+2, ...; each published its piece first thing in its share.  Merge:
-        // m = max(m_a, m_b), O = O_a 2^(m_a - m) + O_b 2^(m_b - m), the same for the running sum.
+        sk_store(dst, slot_off + 16 * 64 * 16, 0, m_run, l_run, 0.0f, 0.0f);
+    };
+
+    // The owner of a split unit has run its own key tiles (or, continuing, a missing piece's); it
+    // merges the partial states of the workgroups holding the rest of the unit, up to stream-K step
+    // t_end, which published them first thing in their shares.  When a piece's partial does not
+    // arrive in time the owner claims the piece, parks its state in its carry slot and returns; the
+    // driver runs the piece's key tiles as its next item, which resumes here.
+    if (kind == UNIT_OWNER || kind == UNIT_OWNER_CONT) {
         const int G = a.sk_grid;
-        for (int jg = g + 1; jg < G && sk_begin(S, jg, G) < t_end; ++jg) {
-            if (sk_begin(S, jg + 1, G) == sk_begin(S, jg, G)) continue;     // empty share
-            sk_take(attn_flag(a, jg), a.epoch);
-            const __amdgpu_buffer_rsrc_t src = sk_slot(attn_partial(a, jg));
-            const uint32_t off = (uint32_t)((wave * kPartF4 * 64 + lane) * 16);
-            const float4 ml = sk_load(src, off + 16 * 64 * 16);
-            const float m_new = fmaxf(m_run, ml.x);
-            const float ca = __builtin_amdgcn_exp2f(m_run - m_new), cb = __builtin_amdgcn_exp2f(ml.x - m_new);
-            m_run = m_new;
-            l_run = fmaf(l_run, ca, ml.y * cb);
-            // 4 loads in flight at a time: O and the pipeline state fill most of the registers
-#pragma unroll
-            for (int eb = 0; eb < 4; ++eb) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float4 v = sk_load(src, off + (4 * eb + i) * 64 * 16);
-                    o[eb][4 * i] = fmaf(o[eb][4 * i], ca, v.x * cb);
-                    o[eb][4 * i + 1] = fmaf(o[eb][4 * i + 1], ca, v.y * cb);
-                    o[eb][4 * i + 2] = fmaf(o[eb][4 * i + 2], ca, v.z * cb);
-                    o[eb][4 * i + 3] = fmaf(o[eb][4 * i + 3], ca, v.w * cb);
+        int miss = -1;
+        // jn = -1: the state parked in the carry slot (a continuation), then pieces from jn0
+        for (int jn = kind == UNIT_OWNER_CONT ? -1 : jn0; jn < G && (jn < 0 || sk_begin(S, jn, G) < t_end);
+             jn = jn < 0 ? jn0 : jn + 1) {
+            const float4* src = attn_carry(a, g);
+            if (jn >= 0) {
+                if (sk_begin(S, jn + 1, G) == sk_begin(S, jn, G)) continue;     // empty share
+                if (!sk_take(attn_flag(a, jn), a.epoch, a.sk_spins)) {
+                    miss = jn;
+                    break;
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                src = attn_partial(a, jn);
             }
+            merge_slot(src);
         }
+        if (miss >= 0) {
+            store_slot(attn_carry(a, g));
+            __builtin_amdgcn_s_waitcnt(0);
+            const long t_first = t_end - a.k_tiles;        // stream-K step of this unit's key tile 0
+            ckb = (int)(sk_begin(S, miss, G) - t_first);
+            cke = (int)(min(sk_begin(S, miss + 1, G), t_end) - t_first);
+            return miss + 1;
+        }
+    }
+
+    if (kind == UNIT_PARTIAL) {
+        store_slot(attn_partial(a, g));
+        sk_raise(attn_flag(a, g), a.epoch, a.sk_spins);
+        return -1;
     }
 
     const float inv = 1.0f / half_swap_sum(l_run);
@@ -380,6 +420,7 @@ __device__ __forceinline__ void attention_unit(const AttnArgs& a, char* smem_k0,
                 *reinterpret_cast<u32x2_v*>(op + e) = w;
             }
     }
+    return -1;
 }
 
 // Persistent stream-K driver (sk_grid > 0) or one unit per workgroup.  Workgroup g (XCD-remapped,
@@ -399,11 +440,15 @@ __device__ __forceinline__ void attention_mfma_body(const AttnArgs& a) {
     const long S = G ? (long)(a.units - a.dp_units) * I : 0;          // stream-K key tiles
     const long e = G ? sk_begin(S, g + 1, G) : 0;
     long it = G ? sk_begin(S, g, G) : 0;
+    int cont = -1, ckb = 0, cke = 0, cL = 0;     // an owner's continuation (attention_unit's return)
+    long ct_end = 0;
     // one work item per pass, so the unit code is generated once
     for (int w = 0;; ++w) {
-        int L, kb = 0, ke = I, kind = UNIT_FULL;
+        int L, kb = 0, ke = I, kind = UNIT_FULL, jn0 = g + 1;
         long t_end = 0;
-        if (G == 0) {
+        if (cont >= 0) {
+            L = cL; kb = ckb; ke = cke; kind = UNIT_OWNER_CONT; t_end = ct_end; jn0 = cont;
+        } else if (G == 0) {
             if (w > 0) break;
             L = g;
         } else if ((long)g + (long)w * G < a.dp_units) {
@@ -419,7 +464,10 @@ __device__ __forceinline__ void attention_mfma_body(const AttnArgs& a) {
             it = (long)t * I + ke;
         }
         if (w > 0) __syncthreads();                 // the K / V rings are reused by the next unit
-        attention_unit<DT, NEG>(a, smem_k0, smem_k1, smem_v0, smem_v1, L, kb, ke, kind, g, S, t_end);
+        cont = attention_unit<DT, NEG>(a, smem_k0, smem_k1, smem_v0, smem_v1, L, kb, ke, kind, g, S, t_end, jn0, ckb,
+                                       cke);
+        cL = L;
+        ct_end = t_end;
     }
 }
 
@@ -486,12 +534,9 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(AttnArgs a) {
     }
 }
 
-#ifndef DIT_ATTN_STREAMK
-#define DIT_ATTN_STREAMK 1
-#endif
 size_t attention_sk_scratch_bytes() {
     const int G = device_cu_count();
-    return G > 0 ? (size_t)G * ((size_t)kSlotF4 * 16 + 8) : 0;
+    return G > 0 ? (size_t)G * (2 * (size_t)kSlotF4 * 16 + 8) : 0;
 }
 
 hipError_t launch_attention(AttnArgs& a, hipStream_t s) {
@@ -507,7 +552,7 @@ hipError_t launch_attention(AttnArgs& a, hipStream_t s) {
         a.k_tiles = (a.n_tok + AK - 1) / AK;
         a.sk_grid = 0;
         a.dp_units = 0;
-        if (DIT_ATTN_STREAMK && a.sk_scratch && G > 0 && a.units % G != 0) {
+        if (a.sk_scratch && G > 0 && a.units % G != 0) {
             const long rounds = (a.units + G - 1) / G;
             const long work = (long)a.units * a.k_tiles;
             const long idle = rounds * G * a.k_tiles - work;
@@ -516,6 +561,7 @@ hipError_t launch_attention(AttnArgs& a, hipStream_t s) {
                 a.sk_grid = G;
                 a.dp_units = D >= 1 ? (D - 1) * G : 0;
                 a.epoch = next_launch_tag();
+                a.sk_spins = sk_spin_limit();
             }
         }
         const dim3 grid(a.sk_grid ? a.sk_grid : a.units), block(64 * kAttnWaves);

@@ -192,6 +192,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmBatch bt) {
 
     // epilogue: acc[nb][mb][q] -> row m0 + wm*128 + mb*32 + (lane & 31); B row b_row[nb] - (lane & 31)
     // + 8 (q >> 2) + 4 h + (q & 3) of the tile
+    bool bad = false;              // an fp16 output out of fp16's range
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
         const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
@@ -207,6 +208,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmBatch bt) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     o[j] = silu_f8(acc[0][mb][4 * i + j] * sa * sg[j]) * (acc[1][mb][4 * i + j] * sa * su[j]);
+                if (g.c_dtype == F16)
+                    bad |= f16_out_of_range4(o);
                 store4_any(g.c, (size_t)m * g.ldc + col, g.c_dtype, o);
             }
         } else {
@@ -229,10 +232,13 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmBatch bt) {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) o[j] = fmaf(gt[j], o[j], r[j]);
                     }
+                    if (g.c_dtype == F16)
+                        bad |= f16_out_of_range4(o);
                     store4_any(g.c, (size_t)m * g.ldc + col, g.c_dtype, o);
                 }
         }
     }
+    raise_range_flag(bt.range_flag, bad);
 }
 
 hipError_t launch_gemm_fp8(Fp8GemmBatch& bt, hipStream_t s) {

@@ -9,8 +9,9 @@
 // single-stream block's first linear).
 //
 // MFMA path (bf16 weights): a 256 x 256 x 64 block tile, 8 waves (2 along M x 4 along N), each a
-// 128 x 64 sub-tile of 4 x 2 v_mfma_f32_32x32x16 tiles with fp32 accumulators (a 4-wave layout
-// of 128 x 128 sub-tiles is kept as an alternative).  Activations are bf16 or fp16; with fp16
+// 128 x 64 sub-tile of 4 x 2 v_mfma_f32_32x32x16 tiles with fp32 accumulators (two waves per SIMD:
+// one issues MFMAs while the other waits on LDS; a 4-wave layout of 128 x 128 sub-tiles, one wave
+// per SIMD, measured 8-10% slower).  Activations are bf16 or fp16; with fp16
 // activations the bf16 weight tile is converted to fp16 while it is staged (the MFMA needs one
 // operand type; the conversion is exact).  Operands go global -> LDS with global_load_lds_dwordx4
 // (no VGPR staging) where no conversion is needed, double-buffered.
@@ -90,10 +91,7 @@ template <int AT> constexpr int mfma_type() { return AT == BF16 ? BF16 : F16; }
 // goes the same way when AT is BF16 or F16W; when AT == F16 it is loaded into VGPRs, converted to fp16
 // (exact: bf16 values are fp16 values in fp16's normal range) and written to the same LDS
 // layout, so both operands of the fp16 MFMA come from one swizzled layout.
-//
-// WN = waves along N.  WN = 2: 4 waves (one per SIMD), each a 128 x 128 sub-tile (4 x 4 MFMA
-// tiles, 256 accumulators).  WN = 4: 8 waves (two per SIMD), each 128 x 64 (4 x 2 MFMA tiles,
-// 128 accumulators) -- the second wave on a SIMD issues MFMAs while the first waits on LDS.
+constexpr int WN = 4;                                  // waves along N (2 along M)
 constexpr int kGemmLds = 2 * (BM + BN) * BK * 2;      // two A+B stages: 128 KB, one workgroup per CU
 constexpr int kPartialF4 = BM * BN / 4;               // float4s of one fp32 partial tile (256 KB)
 
@@ -101,21 +99,30 @@ constexpr int kPartialF4 = BM * BN / 4;               // float4s of one fp32 par
 enum TileKind {
     TILE_FULL = 0,      // all k-steps: epilogue
     TILE_OWNER = 1,     // k-steps from 0: add the partials of the workgroups holding the rest, epilogue
-    TILE_PARTIAL = 2    // a later run of k-steps: publish the fp32 partial for the owner
+    TILE_PARTIAL = 2,   // a later run of k-steps: publish the fp32 partial for the owner
+    TILE_OWNER_CONT = 3 // an owner's continuation: k-steps of a piece whose partial did not arrive,
+                        // plus the owner's running sum from its carry slot, then as TILE_OWNER
 };
 
-// Stream-K scratch: [sk_grid] partial tiles, then [sk_grid] 64-bit flags.
+// Stream-K scratch: [sk_grid] partial tiles, [sk_grid] carry tiles (an owner's running sum while it
+// computes a missing piece), then [sk_grid] 32-bit flags.
 __device__ __forceinline__ float4* sk_partial(const GemmBatch& b, int g) {
     return reinterpret_cast<float4*>(b.sk_scratch) + (size_t)g * kPartialF4;
 }
-__device__ __forceinline__ unsigned long long* sk_flag(const GemmBatch& b, int g) {
-    return reinterpret_cast<unsigned long long*>(reinterpret_cast<float4*>(b.sk_scratch) +
-                                                 (size_t)b.sk_grid * kPartialF4) + g;
+__device__ __forceinline__ float4* sk_carry(const GemmBatch& b, int g) {
+    return reinterpret_cast<float4*>(b.sk_scratch) + (size_t)(b.sk_grid + g) * kPartialF4;
+}
+__device__ __forceinline__ unsigned* sk_flag(const GemmBatch& b, int g) {
+    return reinterpret_cast<unsigned*>(reinterpret_cast<float4*>(b.sk_scratch) +
+                                                 (size_t)2 * b.sk_grid * kPartialF4) + g;
 }
 
-template <int MODE, int AT, int WN>
-__device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L, int kb, int ke, int kind, int g,
-                                          long S, long t_end) {
+// Returns -1, or (an owner whose piece jn did not arrive; its running sum is in its carry slot) the
+// index jn of the next workgroup whose piece is still to be merged, with the missing piece's k-steps
+// in [ckb, cke): the driver then runs that continuation as the workgroup's next item.
+template <int MODE, int AT>
+__device__ __forceinline__ int gemm_tile(const GemmBatch& b, char* smem, int L, int kb, int ke, int kind, int g,
+                                         long S, long t_end, int jn0, int& ckb, int& cke) {
     constexpr int NW = 2 * WN;                     // waves per workgroup
     constexpr int NB = 4 / (WN / 2);               // 32-wide n-blocks per wave (4 or 2)
     constexpr int LPW = 32 / NW;                   // 1 KB load instructions per wave per operand
@@ -237,7 +244,6 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-    const int nk = ke - kb;                        // k-steps of this run
     // Fragments for k16 sub-step s of a staged tile (LDS byte offset `base` of its A tile).
     auto read_frags = [&](FragT* fa, FragT* fb, int base, int s) {
         const int c = 2 * s + khalf;
@@ -251,16 +257,11 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
             fb[j] = *reinterpret_cast<const FragT*>(lb + b_row[j] * 128 + ((c ^ swz(b_row[j])) << 4));
     };
 
-    issue_loads(0, kb * BK);
-    store_b(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
     FragT fa[2][4], fb[2][NB];
     // One k-step on the staged tile `buf`.  MORE: the next tile exists -- issue its loads
     // and (fp16) write its converted weight tile; the body is then one basic block, so the
     // scheduling groups below apply to all of it.
-    auto kstep = [&]<bool MORE>(int it) {
+    auto kstep = [&]<bool MORE>(int k0, int it) {
         constexpr int kMFMA = 0x008, kVALU = 0x002, kDSR = 0x100, kDSW = 0x200, kVMEM = 0x020;
         constexpr int kReads = 4 + NB, kMfmas = 4 * NB;
         const int buf = it & 1;
@@ -273,7 +274,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
             const int cur = s & 1;
             if (s + 1 < BK / 16) read_frags(fa[cur ^ 1], fb[cur ^ 1], buf * kStage, s + 1);
             if constexpr (MORE) {
-                if (s == 0) issue_loads(buf ^ 1, (kb + it + 1) * BK);
+                if (s == 0) issue_loads(buf ^ 1, (k0 + it + 1) * BK);
                 if constexpr (AT == F16) {
                     if (s == BK / 16 - 1) store_b(buf ^ 1);
                 }
@@ -313,7 +314,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
     // MFMAs (whose fragments are already in registers) cover their latency.  The loads of tile
     // it + 2 go into the stage tile it was read from: every wave finished reading it before the
     // barrier.  MORE: 2 = tiles it + 1 and it + 2 exist, 1 = only it + 1, 0 = last tile.
-    auto kstep_rot = [&]<int MORE>(int it) {
+    auto kstep_rot = [&]<int MORE>(int k0, int it) {
         constexpr int kMFMA = 0x008, kDSR = 0x100;
         constexpr int kReads = 4 + NB, kMfmas = 4 * NB;
         const int buf = it & 1;
@@ -351,31 +352,64 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
             if constexpr (MORE > 1) {
                 if (q < LPW) {
                     __builtin_amdgcn_sched_barrier(0);
-                    issue_load_pair(buf, (kb + it + 2) * BK, q);
+                    issue_load_pair(buf, (k0 + it + 2) * BK, q);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    if constexpr (AT != F16) {
-        read_frags(fa[0], fb[0], 0, 0);
-        if (nk > 1) issue_loads(1, (kb + 1) * BK);
-        int it = 0;
-        for (; it < nk - 2; ++it) kstep_rot.template operator()<2>(it);
-        if (nk > 1) kstep_rot.template operator()<1>(it++);
-        kstep_rot.template operator()<0>(it);
-    } else {
-        read_frags(fa[0], fb[0], 0, 0);
-        for (int it = 0; it < nk - 1; ++it) kstep.template operator()<true>(it);
-        kstep.template operator()<false>(nk - 1);
-    }
+    // k-steps [k0, k1) of the tile, accumulated into acc
+    // k-steps [k0, k1) of the tile, accumulated into acc
+    auto kloop = [&](int k0, int k1) {
+        const int nk = k1 - k0;
+        issue_loads(0, k0 * BK);
+        store_b(0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if constexpr (AT != F16) {
+            read_frags(fa[0], fb[0], 0, 0);
+            if (nk > 1) issue_loads(1, (k0 + 1) * BK);
+            int it = 0;
+            for (; it < nk - 2; ++it) kstep_rot.template operator()<2>(k0, it);
+            if (nk > 1) kstep_rot.template operator()<1>(k0, it++);
+            kstep_rot.template operator()<0>(k0, it);
+        } else {
+            read_frags(fa[0], fb[0], 0, 0);
+            for (int it = 0; it < nk - 1; ++it) kstep.template operator()<true>(k0, it);
+            kstep.template operator()<false>(k0, nk - 1);
+        }
+    };
 
     // Partial tiles: lane l of wave w keeps float4 c of its accumulators at index
     // (w * NB*16 + c) * 64 + l of its workgroup's slot.
     constexpr int kF4 = NB * 16;                   // float4s of accumulators per lane
-    if (kind == TILE_PARTIAL) {
-        const __amdgpu_buffer_rsrc_t dst = sk_slot(sk_partial(b, g));
+    kloop(kb, ke);
+
+    const uint32_t slot_off = (uint32_t)((wave * kF4 * 64 + lane) * 16);     // float4 c at + c * 1024
+    // adds the fp32 tile in a stream-K slot (partial or carry) to acc
+    auto add_slot = [&](const float4* slot) {
+        const __amdgpu_buffer_rsrc_t src = sk_slot(slot);
+        // 4 loads in flight at a time: the accumulators already fill the register file
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = (nb * 4 + mb) * 4 + q;
+                    const float4 v = sk_load(src, slot_off, (uint32_t)c * 1024u);
+                    acc[nb][mb][4 * q] += v.x;
+                    acc[nb][mb][4 * q + 1] += v.y;
+                    acc[nb][mb][4 * q + 2] += v.z;
+                    acc[nb][mb][4 * q + 3] += v.w;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    };
+    // stores acc into a stream-K slot
+    auto store_slot = [&](float4* slot) {
+        const __amdgpu_buffer_rsrc_t dst = sk_slot(slot);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -383,42 +417,53 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int c = (nb * 4 + mb) * 4 + q;
-                    sk_store(dst, (uint32_t)(((wave * kF4 + c) * 64 + lane) * 16), acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
+                    sk_store(dst, slot_off, (uint32_t)c * 1024u, acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
                              acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
                 }
-        sk_raise(sk_flag(b, g), b.epoch);
-        return;
-    }
-    if (kind == TILE_OWNER) {
-        // The rest of this tile, up to k-step t_end (stream-K relative), was split over the next
-        // workgroups g+1, g+2, ...; each published its piece first thing in its share.
+    };
+
+    // The owner of a split tile has run its own k-steps (or, continuing, a missing piece's); it adds
+    // the partials of the workgroups holding the rest of the tile, up to k-step t_end (stream-K
+    // relative), which published them first thing in their shares.  When a piece's partial does
+    // not arrive in time the owner claims the piece, parks its running sum in its carry slot and
+    // returns; the driver runs the piece's k-steps as its next item, which resumes here.
+    if (kind == TILE_OWNER || kind == TILE_OWNER_CONT) {
         const int G = b.sk_grid;
-        for (int j = g + 1; j < G && sk_begin(S, j, G) < t_end; ++j) {
-            if (sk_begin(S, j + 1, G) == sk_begin(S, j, G)) continue;     // empty share
-            sk_take(sk_flag(b, j), b.epoch);
-            const __amdgpu_buffer_rsrc_t src = sk_slot(sk_partial(b, j));
-            // 4 loads in flight at a time: the accumulators already fill the register file
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int c = (nb * 4 + mb) * 4 + q;
-                        const float4 v = sk_load(src, (uint32_t)(((wave * kF4 + c) * 64 + lane) * 16));
-                        acc[nb][mb][4 * q] += v.x;
-                        acc[nb][mb][4 * q + 1] += v.y;
-                        acc[nb][mb][4 * q + 2] += v.z;
-                        acc[nb][mb][4 * q + 3] += v.w;
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+        int miss = -1;
+        // jn = -1: the running sum parked in the carry slot (a continuation), then pieces from jn0
+        for (int jn = kind == TILE_OWNER_CONT ? -1 : jn0; jn < G && (jn < 0 || sk_begin(S, jn, G) < t_end);
+             jn = jn < 0 ? jn0 : jn + 1) {
+            const float4* src = sk_carry(b, g);
+            if (jn >= 0) {
+                if (sk_begin(S, jn + 1, G) == sk_begin(S, jn, G)) continue;     // empty share
+                if (!sk_take(sk_flag(b, jn), b.epoch, b.sk_spins)) {
+                    miss = jn;
+                    break;
                 }
+                src = sk_partial(b, jn);
+            }
+            add_slot(src);
         }
+        if (miss >= 0) {
+            store_slot(sk_carry(b, g));
+            __builtin_amdgcn_s_waitcnt(0);
+            const long t_first = t_end - b.k_steps;        // stream-K step of this tile's k-step 0
+            ckb = (int)(sk_begin(S, miss, G) - t_first);
+            cke = (int)(min(sk_begin(S, miss + 1, G), t_end) - t_first);
+            return miss + 1;
+        }
+    }
+
+    if (kind == TILE_PARTIAL) {
+        store_slot(sk_partial(b, g));
+        sk_raise(sk_flag(b, g), b.epoch, b.sk_spins);
+        return -1;
     }
 
     // ---- epilogue.  acc[nb][mb][q]: row m = m0 + wm*128 + mb*32 + (lane & 31),
     //      B-row offset within the n-block: 8*(q>>2) + 4*khalf + (q&3).
     const int mlane = lane & 31;
+    bool bad = false;              // an fp16 output out of fp16's range
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
         const int m = m0 + wm * 128 + mb * 32 + mlane;
@@ -437,6 +482,8 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
                         const float u = acc[nb + NB / 2][mb][4 * i + j];
                         f[j] = silu_acc(g) * u;
                     }
+                    if (P.c_dtype == F16)
+                        bad |= f16_out_of_range4(f);
                     store4_dt(P.C, (size_t)m * P.ldc + col, P.c_dtype, f);
                 }
             }
@@ -459,11 +506,15 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
 #pragma unroll
                         for (int j = 0; j < 4; ++j) o[j] = fmaf(gt[j], o[j], r[j]);
                     }
+                    if (P.c_dtype == F16)
+                        bad |= f16_out_of_range4(o);
                     store4_dt(P.C, (size_t)m * P.ldc + col, P.c_dtype, o);
                 }
             }
         }
     }
+    raise_range_flag(b.range_flag, bad);
+    return -1;
 }
 
 // Persistent stream-K driver (sk_grid > 0) or one tile per workgroup.  Workgroup g (XCD-remapped,
@@ -472,7 +523,7 @@ __device__ __forceinline__ void gemm_tile(const GemmBatch& b, char* smem, int L,
 // (published as a partial), whole tiles, and the start of a tile later workgroups finish (it
 // owns that one and adds their partials).  A tile's owner computes its piece last, after the
 // workgroups holding the other pieces computed theirs first.
-template <int MODE, int AT, int WN>
+template <int MODE, int AT>
 __device__ __forceinline__ void gemm_mfma_body(const GemmBatch& b) {
     __shared__ __attribute__((aligned(1024))) char smem[kGemmLds];
     const int g = xcd_remap(blockIdx.x, gridDim.x);
@@ -480,11 +531,15 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmBatch& b) {
     const long S = G ? (long)(b.total_tiles - b.dp_tiles) * I : 0;     // stream-K k-steps
     const long e = G ? sk_begin(S, g + 1, G) : 0;
     long it = G ? sk_begin(S, g, G) : 0;
+    int cont = -1, ckb = 0, cke = 0, cL = 0;     // an owner's continuation (gemm_tile's return)
+    long ct_end = 0;
     // one work item per pass, so the tile code is generated once
     for (int w = 0;; ++w) {
-        int L, kb = 0, ke = I, kind = TILE_FULL;
+        int L, kb = 0, ke = I, kind = TILE_FULL, jn0 = g + 1;
         long t_end = 0;
-        if (G == 0) {
+        if (cont >= 0) {
+            L = cL; kb = ckb; ke = cke; kind = TILE_OWNER_CONT; t_end = ct_end; jn0 = cont;
+        } else if (G == 0) {
             if (w > 0) break;
             L = g;
         } else if ((long)g + (long)w * G < b.dp_tiles) {
@@ -500,16 +555,14 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmBatch& b) {
             it = (long)t * I + ke;
         }
         if (w > 0) __syncthreads();                 // LDS stages are reused by the next tile
-        gemm_tile<MODE, AT, WN>(b, smem, L, kb, ke, kind, g, S, t_end);
+        cont = gemm_tile<MODE, AT>(b, smem, L, kb, ke, kind, g, S, t_end, jn0, ckb, cke);
+        cL = L;
+        ct_end = t_end;
     }
 }
 
-// The two workgroup layouts as kernels (launch bounds must not depend on a template parameter:
-// hipcc then emits no host launch stub).
 template <int MODE, int AT>
-__global__ __launch_bounds__(256, 1) void gemm_mfma_w4(GemmBatch b) { gemm_mfma_body<MODE, AT, 2>(b); }
-template <int MODE, int AT>
-__global__ __launch_bounds__(512, 1) void gemm_mfma_w8(GemmBatch b) { gemm_mfma_body<MODE, AT, 4>(b); }
+__global__ __launch_bounds__(512, 1) void gemm_mfma_w8(GemmBatch b) { gemm_mfma_body<MODE, AT>(b); }
 
 // ------------------------------------------------------------------------------------------
 // fp32 GEMM: 64 x 64 block tile, K step 16, 256 threads each owning a 4 x 4 output patch.
@@ -591,31 +644,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmBatch b) {
     else gemm_f32_tile<false>(P, tm, tn);
 }
 
-#ifndef DIT_GEMM_WN
-#define DIT_GEMM_WN 4
-#endif
-template <int AT, bool W8>
-static void launch_mfma_w(GemmBatch& b, hipStream_t s, bool all_store, bool all_res, bool all_swiglu) {
-    const dim3 grid(b.sk_grid ? b.sk_grid : b.total_tiles), block(W8 ? 512 : 256);
-#define DIT_LAUNCH(MODE)                                                                          \
-    do {                                                                                          \
-        if constexpr (W8) hipLaunchKernelGGL((gemm_mfma_w8<MODE, AT>), grid, block, 0, s, b);     \
-        else hipLaunchKernelGGL((gemm_mfma_w4<MODE, AT>), grid, block, 0, s, b);                  \
-    } while (0)
-    if (all_store) DIT_LAUNCH(MODE_STORE);
-    else if (all_res) DIT_LAUNCH(MODE_RES);
-    else if (all_swiglu) DIT_LAUNCH(MODE_SWIGLU);
-    else DIT_LAUNCH(MODE_MIXED);
-#undef DIT_LAUNCH
-}
 template <int AT>
 static void launch_mfma(GemmBatch& b, hipStream_t s, bool all_store, bool all_res, bool all_swiglu) {
-    launch_mfma_w<AT, DIT_GEMM_WN == 4>(b, s, all_store, all_res, all_swiglu);
+    const dim3 grid(b.sk_grid ? b.sk_grid : b.total_tiles), block(512);
+    if (all_store) hipLaunchKernelGGL((gemm_mfma_w8<MODE_STORE, AT>), grid, block, 0, s, b);
+    else if (all_res) hipLaunchKernelGGL((gemm_mfma_w8<MODE_RES, AT>), grid, block, 0, s, b);
+    else if (all_swiglu) hipLaunchKernelGGL((gemm_mfma_w8<MODE_SWIGLU, AT>), grid, block, 0, s, b);
+    else hipLaunchKernelGGL((gemm_mfma_w8<MODE_MIXED, AT>), grid, block, 0, s, b);
 }
-
-#ifndef DIT_GEMM_STREAMK
-#define DIT_GEMM_STREAMK 1
-#endif
 
 // Compute units of the current device (the stream-K grid: one 128 KB-LDS workgroup per CU, all
 // resident at once); 0 if unknown.
@@ -633,19 +669,23 @@ int device_cu_count() {
 
 size_t gemm_sk_scratch_bytes() {
     const int G = device_cu_count();
-    return G > 0 ? (size_t)G * ((size_t)kPartialF4 * 16 + 8) : 0;
+    return G > 0 ? (size_t)G * (2 * (size_t)kPartialF4 * 16 + 8) : 0;
 }
 
 // Launch tags for the stream-K flags: nonzero, unique per launch in this process and started from a
 // time-derived value, so flags left in a reused workspace never match a new launch.  An owner
 // clears each flag it consumed, so replays of one launch (one tag) work too.
-static std::atomic<unsigned long long> g_epoch{
-    ((unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() << 20) | 1ull};
-unsigned long long next_launch_tag() {
-    unsigned long long e;
-    do e = g_epoch.fetch_add(1, std::memory_order_relaxed); while (e == 0);
+static std::atomic<unsigned> g_epoch{
+    (unsigned)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
+unsigned next_launch_tag() {
+    unsigned e;
+    do e = g_epoch.fetch_add(1, std::memory_order_relaxed) & ~kSkAbandoned; while (e == 0);
     return e;
 }
+
+static thread_local int tl_sk_spins = kSkSpinsDefault;
+int sk_spin_limit() { return tl_sk_spins; }
+void set_sk_spin_limit(int spins) { tl_sk_spins = spins < 0 ? kSkSpinsDefault : spins; }
 
 hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
     int total = 0;
@@ -693,13 +733,14 @@ hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
     // fp32 partials' hand-over past the L2s costs about as much as a few k-steps).  A single
     // partly filled round (216 tiles at 512 + 4096 tokens) stays unsplit: there the split put
     // co-resident workgroups at different k-offsets and ran 114 -> 147 us (out-proj).
-    if (DIT_GEMM_STREAMK && mfma && b.sk_scratch && same_k && G > 0 &&
+    if (mfma && b.sk_scratch && same_k && G > 0 &&
         ((total >= 2 * G && total % G != 0 && 4 * (total % G) <= G) ||
          (2 * total <= G && (long)total * b.k_steps >= 12L * G))) {
         const int D = total / G;
         b.sk_grid = G;
         b.dp_tiles = D >= 1 ? (D - 1) * G : 0;
         b.epoch = next_launch_tag();
+        b.sk_spins = sk_spin_limit();
     }
     if (b.a_dtype == F16 && b.b_f16) launch_mfma<F16W>(b, s, all_store, all_res, all_swiglu);
     else if (b.a_dtype == F16) launch_mfma<F16>(b, s, all_store, all_res, all_swiglu);

@@ -22,6 +22,7 @@ template <int DT>
 __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
     extern __shared__ float s_act[];
     constexpr int kES = ESize<DT>::v;
+    if (b.clear_flag && blockIdx.x == 0 && threadIdx.x == 0) *b.clear_flag = 0u;
     constexpr int kElems = 16 / kES;                       // elements per 16-byte slice
     constexpr int kQ = kElems / 4;                         // float4s of SiLU(c) per slice
     const int tid = threadIdx.x;
@@ -221,6 +222,7 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
         }
         return;
     }
+    bool bad = false;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int c = (lane + 64 * i) * 8;
@@ -233,9 +235,14 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
                 o[t] = fmaf(1.0f + sc0[t], v[i][t] * rstd, sh0[t]);
                 o[4 + t] = fmaf(1.0f + sc1[t], v[i][4 + t] * rstd, sh1[t]);
             }
+            if constexpr (OT == F16) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) bad |= f16_out_of_range(o[t]);
+            }
             store8<OT>(orow + (size_t)c * ESize<OT>::v, o);
         }
     }
+    if constexpr (OT == F16) raise_range_flag(b.range_flag, bad);
 }
 
 template <int XT, int OT>

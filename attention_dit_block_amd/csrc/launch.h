@@ -9,6 +9,10 @@
 namespace dit {
 
 enum DType { F32 = 0, BF16 = 1, F16 = 2 };
+// Bits of a call's range-flag word (device memory; the entry points keep it in their workspace).
+// Kernels that round fp32 results to fp16 OR in kRangeF16 when a value is outside fp16's finite
+// range (|x| > 65504) or NaN, so it would reach the next step as inf or NaN.
+constexpr unsigned kRangeF16 = 1u;
 // Output type of the modulate kernel only: OCP e4m3 codes with a per-row fp32 scale.
 constexpr int FP8_ROWS = 3;
 
@@ -24,6 +28,7 @@ struct GemvBatch {
     const void* cond;   // [d_cond]
     int d_cond;
     int dtype;          // dtype of w and cond (F32 or BF16)
+    unsigned* clear_flag;   // range-flag word to reset to 0 (the first kernel of a call), or null
 };
 hipError_t launch_adaln_gemv(const GemvBatch& b, hipStream_t s);
 
@@ -42,6 +47,7 @@ struct ModBatch {
     float eps;
     int out_dtype;      // F32, BF16, F16, or FP8_ROWS: e4m3 codes (bytes, row stride ld_out) quantised per
                         // row as launch_quantize_fp8 does, from the fp32 results
+    unsigned* range_flag;   // or null: kRangeF16 when an F16 output is out of range
 };
 hipError_t launch_modulate(const ModBatch& b, hipStream_t s);
 
@@ -95,7 +101,9 @@ struct GemmBatch {
     // workgroups runs tiles [0, dp_tiles) whole and splits the k-steps of the others evenly.
     void* sk_scratch;
     int sk_grid, dp_tiles, k_steps;
-    unsigned long long epoch;
+    unsigned epoch;
+    int sk_spins;       // bound on an owner's wait for a piece (then it computes the piece itself)
+    unsigned* range_flag;   // or null: kRangeF16 when an F16 output is out of range
 };
 // Row strides (lda, ldb) of the 16-bit GEMMs are below this many elements (launch_gemm returns
 // hipErrorInvalidValue otherwise; the entry points reject such strides first).
@@ -117,7 +125,8 @@ struct AttnArgs {
     // one workgroup per (head, query tile) unit).  The launcher fills the rest.
     void* sk_scratch;
     int sk_grid, dp_units, units, k_tiles;
-    unsigned long long epoch;
+    unsigned epoch;
+    int sk_spins;       // bound on an owner's wait for a piece (then it computes the piece itself)
 };
 hipError_t launch_attention(AttnArgs& a, hipStream_t s);
 size_t attention_sk_scratch_bytes();
@@ -161,6 +170,7 @@ struct Fp8GemmBatch {
     Fp8GemmProblem p[2];
     int n;              // every problem has p[0].epi
     int total_tiles;    // filled by the launcher
+    unsigned* range_flag;   // or null: kRangeF16 when an F16 output is out of range
 };
 hipError_t launch_gemm_fp8(Fp8GemmBatch& g, hipStream_t s);
 
@@ -193,8 +203,13 @@ hipError_t launch_layernorm_modulate(const void* x, int x_dtype, long ld_x, void
                                      hipStream_t s);
 
 // Compute units of the current device (0 if unknown), and nonzero launch tags unique in the
-// process, for the stream-K grids.
+// process (below 2^31), for the stream-K grids.
 int device_cu_count();
-unsigned long long next_launch_tag();
+unsigned next_launch_tag();
+// The calling thread's bound on a stream-K owner's wait for a piece, in polls of the flag
+// (default kSkSpinsDefault; 0: owners compute every piece whose partial is not already there).
+constexpr int kSkSpinsDefault = 1 << 22;
+int sk_spin_limit();
+void set_sk_spin_limit(int spins);
 
 }  // namespace dit

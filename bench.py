@@ -282,13 +282,26 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(cfg.name, dom, (args.act + ("/f16w" if f16w else "")) if t == "bf16" else "f32")
 
+    # the arithmetic type of the matrix products: fp16 operands when the activations are fp16 (bf16
+    # weights converted to fp16 copies, or while they are staged), bf16 operands otherwise
+    if t != "bf16":
+        mfma_dtype, arithmetic = "f32", "fp32 storage and FMA arithmetic"
+    elif args.act == "f16":
+        mfma_dtype = "f16"
+        arithmetic = ("fp16-operand MFMA with fp32 accumulation (bf16 model weights, fp16 activations), fp32 "
+                      "residual stream, softmax and norms")
+    else:
+        mfma_dtype, arithmetic = "bf16", "bf16-operand MFMA with fp32 accumulation, fp32 residual stream"
     out = {
         "metric": METRIC, "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if t == "bf16" else "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": mfma_dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name, "activations": args.act if t == "bf16" else "f32",
-                   "product_weights": "f16 copies of the bf16 weights (converted once, exact)" if f16w else t, "blocks": cfg.n_double + cfg.n_single, "d": cfg.d, "heads": cfg.n_heads,
+        "config": {"workload": cfg.name, "model_dtype": t, "activations": args.act if t == "bf16" else "f32",
+                   "product_weights": ("f16 copies of the bf16 weights, converted once at setup (round to nearest "
+                                       "even; |w| < 2^-14 become fp16 subnormals)") if f16w else t,
+                   "arithmetic": arithmetic,
+                   "blocks": cfg.n_double + cfg.n_single, "d": cfg.d, "heads": cfg.n_heads,
                    "ffn_inner": cfg.ffn_inner, "n_txt": cfg.n_txt, "n_img": cfg.n_img, "tokens": cfg.n_tok,
                    "gflop_per_step": round(flops / 1e9, 1),
                    "modulation": "shared" if shared else "per_block"},

@@ -208,7 +208,10 @@ size_t dit_block_workspace_size(const dit_block_config* cfg, int single_stream);
  *  workspace >= dit_block_workspace_size(cfg, 0) bytes, scratch (never
  *            zeroed, contents undefined afterwards); must not overlap any
  *            other argument.  Calls sharing a workspace must be ordered on
- *            one stream.
+ *            one stream.  Its first 4 bytes are the call's range-flag word
+ *            (dit_workspace_flags): the call resets it in its first kernel and
+ *            sets DIT_RANGE_F16 when an fp16 activation (act_dtype DIT_F16)
+ *            leaves fp16's finite range, so the output is not to be trusted.
  */
 int dit_block_forward(const dit_block_config* cfg,
                       const dit_stream_weights* txt, const dit_stream_weights* img,
@@ -324,6 +327,7 @@ int dit_timestep_embedding(int dtype, void* stream, const float* t, const float*
                            const void* w_g_in, const void* w_g_out,
                            int freq_dim, int d, float max_period, float time_factor,
                            void* cond_out, void* workspace, size_t ws_bytes);
+
 
 /*
  * y = x W^T on the block's GEMM kernel: the patch embedding of the image
@@ -531,6 +535,40 @@ uint64_t dit_launch_count(void);
 
 /* DIT_ABI_VERSION of the built library. */
 int dit_abi_version(void);
+
+/*
+ * Range flags of the last block / step call that used `workspace` (the word at
+ * its first 4 bytes): waits for the work queued on `stream`, then copies the
+ * word to *flags (host).  The one call of the library that synchronises.
+ *   DIT_RANGE_F16: an fp32 result rounded to an fp16 activation (a, qkv, b, f,
+ *   and the fp8 blocks' fp16 products; act_dtype DIT_F16) was NaN or larger than
+ *   65504 in magnitude, so it became inf or NaN.  q and k after QK-norm + RoPE
+ *   are not checked: each is a unit-RMS 128-vector times the QK-norm weight, so
+ *   its magnitude is at most sqrt(128) max|w_qk|, and they stay finite for QK-norm
+ *   weights below 5792 in magnitude (a precondition of DIT_F16 activations).
+ *   Attention's output is a convex combination of v rows and cannot leave the
+ *   range either.  fp16 activations keep bf16 models' block outputs closer to
+ *   exact arithmetic but have a narrower range than bf16; a model whose
+ *   activations leave it needs act_dtype DIT_BF16.
+ * Reentrant; returns DIT_ERR_HIP if the copy or the wait fails.
+ */
+#define DIT_RANGE_F16 1u
+int dit_workspace_flags(const void* workspace, void* stream, uint32_t* flags);
+
+/*
+ * Test hook of the split-work hand-over.  When a launch splits its last round of
+ * work units over a persistent grid of one workgroup per compute unit (the GEMMs'
+ * k-steps, attention's key tiles), the workgroup owning a unit adds the partial
+ * results the other workgroups publish for their pieces of it.  It polls a
+ * piece's flag at most `polls` times; then it computes that piece itself (the
+ * result equals the split one up to the summation order), so no piece is ever
+ * dropped, whether or not every workgroup of the grid is resident.  Default
+ * 2^22 polls (a value < 0 restores it).  0 turns the hand-over off: no
+ * partial is published and every owner computes all the pieces of its unit
+ * itself (for tests of that path).  Thread-local: applies to the calling
+ * thread's later calls.
+ */
+void dit_set_split_wait_limit(int polls);
 
 /*
  * Kernel timing for measurement tools.  dit_timing_begin(capacity) makes the

@@ -58,8 +58,21 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def upload_stream_weights(w: dict, dtype: str) -> dict:
-    return {k: dev(v, dtype) for k, v in w.items()}
+PRODUCT_WEIGHTS = ("w_qkv", "w_o", "w_ffn_in", "w_ffn_out", "w_1", "w_2")
+
+
+def upload_stream_weights(w: dict, dtype: str, f16_products: bool = False) -> dict:
+    """Weights to the GPU; f16_products: the matrix-product weights as fp16 copies of the bf16
+    weights made by dit_convert_bf16_to_f16 (the block's gemm_w_dtype = DIT_F16 format)."""
+    out = {k: dev(v, dtype) for k, v in w.items()}
+    if f16_products:
+        import attention_dit_block_amd as dit
+        for k in PRODUCT_WEIGHTS:
+            if k in out:
+                f = torch.empty(out[k].shape, dtype=torch.float16, device="cuda")
+                dit.convert_bf16_to_f16(out[k], f)
+                out[k] = f
+    return out
 
 
 def shape_of(cfg: di.BlockConfig, mod, x_dtype=None, y_dtype=None, n_txt=None, n_img=None, act_dtype=None):

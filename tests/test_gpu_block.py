@@ -26,22 +26,26 @@ def dit():
     return m
 
 
-def run_double(dit, cfg, inp, x_dtype="same", y_dtype="f32", act=None):
-    """Run dit_block_forward on generator inputs; returns (y_txt, y_img) as float64."""
+def run_double(dit, cfg, inp, x_dtype="same", y_dtype="f32", act=None, f16w=False):
+    """Run dit_block_forward on generator inputs; returns (y_txt, y_img) as float64.  f16w: the
+    matrix-product weights as fp16 copies (gemm_w_dtype = DIT_F16, the bench's format)."""
     t = cfg.dtype
     xdt = t if x_dtype == "same" else x_dtype
     sh = shape_of(cfg, dit, x_dtype=dit.DIT_BF16 if xdt == "bf16" else dit.DIT_F32,
                   y_dtype=dit.DIT_BF16 if y_dtype == "bf16" else dit.DIT_F32,
                   act_dtype={None: None, "bf16": dit.DIT_BF16, "f16": dit.DIT_F16}[act])
+    if f16w:
+        sh.gemm_w_dtype = dit.DIT_F16
     ws = torch.empty(dit.block_workspace_size(sh), dtype=torch.uint8, device="cuda")
     yt = torch.empty(cfg.n_txt, cfg.d, dtype=torch.float32 if y_dtype == "f32" else torch.bfloat16, device="cuda")
     yi = torch.empty(cfg.n_img, cfg.d, dtype=yt.dtype, device="cuda")
+    wt, wi = upload_stream_weights(inp["txt"], t, f16w), upload_stream_weights(inp["img"], t, f16w)
     before = dit.launch_count()
-    dit.block_forward(sh, upload_stream_weights(inp["txt"], t), upload_stream_weights(inp["img"], t),
-                      dev(inp["cond"], t), dev(inp["pos"], "i32"), dev(inp["x_txt"], xdt), dev(inp["x_img"], xdt),
-                      yt, yi, ws)
+    dit.block_forward(sh, wt, wi, dev(inp["cond"], t), dev(inp["pos"], "i32"), dev(inp["x_txt"], xdt),
+                      dev(inp["x_img"], xdt), yt, yi, ws)
     torch.cuda.synchronize()
     assert dit.launch_count() == before + 9
+    assert dit.workspace_flags(ws) == 0, "an fp16 activation left fp16's range"
     return host(yt), host(yi)
 
 
@@ -97,13 +101,16 @@ def test_double_block_c1_bf16_activations_drift(dit):
     report(cfg, "y_img (bf16 act)", yi, ref["y_img"], bar=0.1)
 
 
-def test_double_block_c2(dit):
+@pytest.mark.parametrize("f16w", [False, True], ids=["bf16_weights", "f16_weight_copies"])
+def test_double_block_c2(dit, f16w):
+    # f16_weight_copies is the configuration bench.py times (its FFN-in GEMM takes the stream-K
+    # split of a mostly empty last round on the rotated k-loop)
     cfg = di.CONFIGS[2]
-    say(f"double block {cfg.name}")
+    say(f"double block {cfg.name} f16w={f16w}")
     inp = di.double_block_inputs(cfg, seed=0)
-    yt, yi = run_double(dit, cfg, inp)
+    yt, yi = run_double(dit, cfg, inp, f16w=f16w)
     # bit-identical on a second run (the split-K reduction of the FFN-in GEMM has a fixed order)
-    yt2, yi2 = run_double(dit, cfg, inp)
+    yt2, yi2 = run_double(dit, cfg, inp, f16w=f16w)
     np.testing.assert_array_equal(yt, yt2)
     np.testing.assert_array_equal(yi, yi2)
     ref = o.double_block(cfg, inp)
@@ -116,11 +123,12 @@ def _sample_rows(n, k, seed):
     return np.unique(np.concatenate([[0, n - 1], r]))
 
 
-def test_double_block_c4_sampled_rows(dit):
+@pytest.mark.parametrize("f16w", [False, True], ids=["bf16_weights", "f16_weight_copies"])
+def test_double_block_c4_sampled_rows(dit, f16w):
     cfg = di.CONFIGS[4]
-    say(f"double block {cfg.name} (sampled rows)")
+    say(f"double block {cfg.name} (sampled rows) f16w={f16w}")
     inp = di.double_block_inputs(cfg, seed=0)
-    yt, yi = run_double(dit, cfg, inp)
+    yt, yi = run_double(dit, cfg, inp, f16w=f16w)
     rt, ri = _sample_rows(cfg.n_txt, 128, 1), _sample_rows(cfg.n_img, 256, 2)
     ref = o.double_block(cfg, inp, rows_txt=rt, rows_img=ri)
     report(cfg, "y_txt[sampled]", yt[rt], ref["y_txt"])
@@ -298,12 +306,13 @@ def test_c3_step_chain_teacher_forced(dit):
 
 # ---- the step entry point ----------------------------------------------------------------------
 
-def _step_weights(cfg, nd, ns, seed, qk="random"):
+def _step_weights(cfg, nd, ns, seed, qk="random", f16w=False):
     t = cfg.dtype
     dbl = [di.double_block_inputs(cfg, seed=seed, block=b, qk_norm=qk) for b in range(nd)]
     sgl = [di.single_weights(cfg, seed, nd + b, qk_norm=qk) for b in range(ns)]
-    return dbl, sgl, ([upload_stream_weights(x["txt"], t) for x in dbl], [upload_stream_weights(x["img"], t) for x in dbl],
-                      [upload_stream_weights(w, t) for w in sgl])
+    return dbl, sgl, ([upload_stream_weights(x["txt"], t, f16w) for x in dbl],
+                      [upload_stream_weights(x["img"], t, f16w) for x in dbl],
+                      [upload_stream_weights(w, t, f16w) for w in sgl])
 
 
 def test_step_matches_blocks_and_oracle_chain(dit):
@@ -350,18 +359,21 @@ def test_step_matches_blocks_and_oracle_chain(dit):
     report(cfg, "stack output", host(y), st)
 
 
-def test_step_graph_capture_replays(dit):
+@pytest.mark.parametrize("f16w", [False, True], ids=["bf16_weights", "f16_weight_copies"])
+def test_step_graph_capture_replays(dit, f16w):
     """The c2-shaped step (1 double + 1 single block; its FFN-in GEMM runs split-K) captured
     into a graph: every replay, with eager work of the program between replays, is bit-identical
     to the eager step."""
     cfg = di.CONFIGS[2]
-    say("step forward under graph capture (c2 shape, 1 double + 1 single)")
-    dbl, sgl, (wt, wi, ws_) = _step_weights(cfg, 1, 1, seed=0, qk="ones")
+    say(f"step forward under graph capture (c2 shape, 1 double + 1 single) f16w={f16w}")
+    dbl, sgl, (wt, wi, ws_) = _step_weights(cfg, 1, 1, seed=0, qk="ones", f16w=f16w)
     act = dbl[0]
     t = cfg.dtype
     cond, pos = dev(act["cond"], t), dev(act["pos"], "i32")
     xt, xi = dev(act["x_txt"], t), dev(act["x_img"], t)
     sh = shape_of(cfg, dit)
+    if f16w:
+        sh.gemm_w_dtype = dit.DIT_F16
     ws = torch.empty(dit.step_workspace_size(sh, 1, 1), dtype=torch.uint8, device="cuda")
     y = torch.empty(cfg.n_tok, cfg.d, dtype=torch.float32, device="cuda")
     dit.step_forward(sh, wt, wi, ws_, cond, pos, xt, xi, y, ws)

@@ -183,3 +183,58 @@ def test_fp8_single_block_c3_shape_sampled(dit):
     y = run_single_fp8(dit, cfg, inp)
     rows = np.unique(np.concatenate([[0, cfg.n_tok - 1], np.random.default_rng(9).choice(cfg.n_tok, 64, replace=False)]))
     check_single(cfg, inp, y[rows], rows=rows, wide=True)
+
+
+def test_fp8_block_c2_last_product_elementwise(dit):
+    """Element-wise check of the full-width fp8 block (512 + 4096 tokens, d = 3072, F = 9216), every
+    output tile: its last product y = h + gate2 (f W_down^T) on e4m3 codes, teacher-forced on the
+    GPU's own fp32 residual h, AdaLN gates and e4m3 codes / row scales of f, read back from the
+    workspace after the call.  Given those, the result is fixed up to fp32 rounding: the e4m3
+    products are exact in fp32, a sum of K of them in any order is within (K - 1) 2^-24 sum|terms|
+    (2^-23 with truncating adds), the two scale products add 2^-24 each, and the fused
+    gate * acc + h rounds once more (2^-24 |y|).  Workspace layout: the range-flag word (256 bytes),
+    the AdaLN vectors [2][6d] fp32, a, qkv, O (fp16), h (fp32), ...; the last two buffers are the
+    current product's activation codes [n, max(d, F)] and row scales [n]."""
+    cfg = di.CONFIGS[2]
+    say(f"fp8 double block {cfg.name}: last product element-wise, teacher-forced")
+    inp = di.double_block_inputs(cfg, seed=0)
+    n, d, F = cfg.n_tok, cfg.d, cfg.ffn_inner
+    sh = shape_of(cfg, dit)
+    total = dit.block_fp8_workspace_size(sh)
+    ws = torch.empty(total, dtype=torch.uint8, device="cuda")
+    yt = torch.empty(cfg.n_txt, d, dtype=torch.float32, device="cuda")
+    yi = torch.empty(cfg.n_img, d, dtype=torch.float32, device="cuda")
+    wt, wi = fp8_weights(dit, inp["txt"]), fp8_weights(dit, inp["img"])
+    dit.block_forward_fp8(sh, wt, wi, dev(inp["cond"], "bf16"), dev(inp["pos"], "i32"), dev(inp["x_txt"], "bf16"),
+                          dev(inp["x_img"], "bf16"), yt, yi, ws)
+    torch.cuda.synchronize()
+
+    def up(x):
+        return (x + 255) // 256 * 256
+    wsh = ws.cpu().numpy()
+    off_mod = 256
+    off_h = off_mod + up(12 * d * 4) + up(n * d * 2) + up(n * 3 * d * 2) + up(n * d * 2)
+    off_sq = total - up(n * 4)
+    off_q8 = off_sq - up(n * max(d, F))
+    mod = wsh[off_mod:off_mod + 12 * d * 4].view(np.float32).reshape(2, 6, d).astype(np.float64)
+    h = wsh[off_h:off_h + n * d * 4].view(np.float32).reshape(n, d).astype(np.float64)
+    fq = wsh[off_q8:off_q8 + n * F].reshape(n, F)
+    sf = wsh[off_sq:off_sq + n * 4].view(np.float32)
+    rng = np.random.default_rng(17)
+    worst = 0.0
+    for si, (s, y, w, rows0, nrows) in enumerate((("txt", yt, wt, 0, cfg.n_txt), ("img", yi, wi, cfg.n_txt, cfg.n_img))):
+        # two rows of every 256-row tile of this stream's problem, and its first and last rows
+        r = np.unique(np.concatenate([[0, nrows - 1]] + [t * 256 + rng.choice(min(256, nrows - t * 256), 2, replace=False)
+                                                         for t in range((nrows + 255) // 256)]))
+        wq, sw = w["w_ffn_out"].cpu().numpy(), w["s_ffn_out"].cpu().numpy()
+        acc = o.linear_fp8(fq[rows0 + r], sf[rows0 + r], wq, sw)
+        abs_sum = o.linear_fp8(fq[rows0 + r] & 0x7F, sf[rows0 + r], wq & 0x7F, sw)
+        gate = mod[si, 5]
+        ref = h[rows0 + r] + gate * acc
+        bound = np.abs(gate) * (F * 2.0 ** -23 + 2.0 ** -22) * abs_sum + 2.0 ** -23 * np.abs(ref) + 1e-30
+        err = np.abs(host(y)[r] - ref)
+        worst = max(worst, float(np.max(err / bound)))
+        say(f"  y_{s}: {len(r)} rows x {d}: max err / bound {np.max(err / bound):.3f}, max|gpu - ref|/RMS "
+            f"{metric(host(y)[r], ref):.2e}")
+        assert np.all(err <= bound), f"y_{s}: {np.sum(err > bound)} elements beyond the bound"
+    assert worst > 0.0

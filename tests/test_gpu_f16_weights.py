@@ -50,7 +50,8 @@ def _f16_weights(dit, w: dict, names) -> dict:
 
 
 @pytest.mark.parametrize("cfg", [di.BlockConfig("ragged_bf16_d384", "bf16", d=384, n_heads=3, ffn_inner=1152, n_txt=7,
-                                                grid_h=5, grid_w=9), di.CONFIGS[1]], ids=["ragged", "c1"])
+                                                grid_h=5, grid_w=9), di.CONFIGS[1], di.CONFIGS[2]],
+                         ids=["ragged", "c1", "c2"])
 def test_double_block_f16_weights_bit_identical(dit, cfg):
     say(f"double block {cfg.name}: fp16 product weights")
     inp = di.double_block_inputs(cfg, seed=2, qk_norm="random")

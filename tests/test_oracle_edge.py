@@ -55,13 +55,29 @@ def test_mlp_embedder_brute_force_and_identity():
     np.testing.assert_allclose(o.mlp_embedder(v, eye, eye), [x / (1.0 + math.exp(-x)) for x in v], rtol=1e-14)
 
 
-def test_conditioning_vector_sums_time_and_guidance():
-    rng = np.random.default_rng(2)
-    wi, wo = rng.standard_normal((8, 16)), rng.standard_normal((8, 8))
-    ct = o.conditioning_vector(0.25, wi, wo, 16)
-    np.testing.assert_allclose(ct, o.mlp_embedder(o.timestep_embedding(0.25, 16), wi, wo), rtol=1e-14)
-    both = o.conditioning_vector(0.25, wi, wo, 16, g=0.25, w_g_in=wi, w_g_out=wo)
-    np.testing.assert_allclose(both, 2 * ct, rtol=1e-14)
+def test_conditioning_vector_closed_forms():
+    """Closed forms of c = W_t,out SiLU(W_t,in emb(t)) [+ W_g,out SiLU(W_g,in emb(g))]."""
+    sig1 = 1.0 / (1.0 + math.exp(-1.0))               # SiLU(1) = sigma(1) = 0.7310585786300049
+    # t = 0: emb = [1, 1, 0, 0] (cosines of 0 first); W_in picks emb[0] and emb[2] -> hidden (1, 0)
+    w_in = np.array([[1.0, 0, 0, 0], [0, 0, 1.0, 0]])
+    w_out = np.array([[2.0, 0], [0, 3.0]])
+    np.testing.assert_allclose(o.conditioning_vector(0.0, w_in, w_out, 4), [2.0 * sig1, 0.0], rtol=0, atol=1e-15)
+    # t = 0.25, factor 1000, max_period 100, dim 4: s = 250, frequencies 1 and 0.1
+    # emb = [cos 250, cos 25, sin 250, sin 25]; identity MLP weights give SiLU(emb) itself
+    e = [math.cos(250.0), math.cos(25.0), math.sin(250.0), math.sin(25.0)]
+    eye = np.eye(4)
+    ct = o.conditioning_vector(0.25, eye, eye, 4, max_period=100.0)
+    # (the oracle's frequency 100^(-1/2) carries a rounding of ~1e-17, times s = 250: atol 1e-12)
+    np.testing.assert_allclose(ct, [v / (1.0 + math.exp(-v)) for v in e], rtol=0, atol=1e-12)
+    # guidance g = 0.5 (s = 500) through its own weights: W_g,in selects sin(500 * 0.1) = sin 50 into
+    # hidden 0, W_g,out doubles it into output 3
+    wg_in = np.zeros((4, 4)); wg_in[0, 3] = 1.0
+    wg_out = np.zeros((4, 4)); wg_out[3, 0] = 2.0
+    both = o.conditioning_vector(0.25, eye, eye, 4, g=0.5, w_g_in=wg_in, w_g_out=wg_out, max_period=100.0)
+    s50 = math.sin(50.0)
+    want = [v / (1.0 + math.exp(-v)) for v in e]
+    want[3] += 2.0 * s50 / (1.0 + math.exp(-s50))
+    np.testing.assert_allclose(both, want, rtol=0, atol=1e-12)
 
 
 def test_linear_brute_force_and_one_hot_rows():
