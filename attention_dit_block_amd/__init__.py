@@ -20,7 +20,7 @@ __all__ = [
     "adaln_modulate", "qk_rmsnorm_rope", "joint_attention",
     "block_workspace_size", "block_forward", "single_block_forward",
     "step_workspace_size", "step_forward", "step_shared_mod_workspace_size", "step_forward_shared_mod",
-    "timestep_embedding_workspace_size", "timestep_embedding", "linear",
+    "timestep_embedding_workspace_size", "timestep_embedding", "timestep_embedding_noalloc", "linear",
     "final_layer_workspace_size", "final_layer", "neighborhood_attention", "quantize_fp8", "linear_fp8",
     "StreamWeightsFp8", "block_fp8_workspace_size", "block_forward_fp8", "SingleWeightsFp8",
     "single_block_fp8_workspace_size", "single_block_forward_fp8", "conv2d", "conv3d_causal",
@@ -95,6 +95,7 @@ _step_sm = _sig("dit_step_forward_shared_mod", _i, [ctypes.POINTER(BlockConfig),
                                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
 _temb_wsize = _sig("dit_timestep_embedding_workspace_size", _sz, [_i, _i])
 _temb = _sig("dit_timestep_embedding", _i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _f, _vp, _vp, _sz])
+_temb_na = _sig("dit_timestep_embedding_noalloc", _i, [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _f, _vp])
 _linear = _sig("dit_linear", _i, [_i, _vp, _vp, _i, _l, _vp, _i, _i, _i, _vp, _i, _l])
 _final_wsize = _sig("dit_final_layer_workspace_size", _sz, [_i, _i, _i])
 _final = _sig("dit_final_layer", _i, [_i, _i, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _i, _f, _vp, _i, _vp, _sz])
@@ -124,7 +125,8 @@ _tread = _sig("dit_timing_read", _i, [_i, ctypes.c_char_p, _i, ctypes.POINTER(_i
 EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", "dit_block_workspace_size",
             "dit_block_forward", "dit_single_block_forward", "dit_step_workspace_size", "dit_step_forward",
             "dit_step_shared_mod_workspace_size", "dit_step_forward_shared_mod",
-            "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_linear",
+            "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_timestep_embedding_noalloc",
+            "dit_linear",
             "dit_final_layer_workspace_size", "dit_final_layer", "dit_neighborhood_attention",
             "dit_quantize_fp8", "dit_linear_fp8", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
             "dit_single_block_fp8_workspace_size", "dit_single_block_forward_fp8",
@@ -487,6 +489,26 @@ def timestep_embedding(t, w_t_in, w_t_out, cond_out, workspace, g=None, w_g_in=N
                fd, d, max_period, time_factor, _ptr(cond_out, "cond_out"), _ptr(workspace, "workspace"),
                workspace.numel() * workspace.element_size())
     _check(rc, "dit_timestep_embedding")
+
+
+def timestep_embedding_noalloc(t, w_t_in, w_t_out, cond_out, g=None, w_g_in=None, w_g_out=None,
+                               max_period: float = 1e4, time_factor: float = 1000.0, stream=None) -> None:
+    """timestep_embedding with the library's static per-GPU scratch instead of a workspace (no
+    allocation; calls that overlap on one GPU race -- see include/dit.h)."""
+    import torch
+    d, fd = w_t_in.shape[0], w_t_in.shape[1]
+    _need(w_t_in, d * fd, "w_t_in")
+    _need(w_t_out, d * d, "w_t_out")
+    _need(cond_out, d, "cond_out")
+    _need(t, 1, "t")
+    if g is not None:
+        _need(g, 1, "g")
+        _need(w_g_in, d * fd, "w_g_in")
+        _need(w_g_out, d * d, "w_g_out")
+    rc = _temb_na(_dt(w_t_in), _stream(stream), _ptr(t, "t", torch.float32), _ptr(g, "g", torch.float32),
+                  _ptr(w_t_in, "w_t_in"), _ptr(w_t_out, "w_t_out"), _ptr(w_g_in, "w_g_in"), _ptr(w_g_out, "w_g_out"),
+                  fd, d, max_period, time_factor, _ptr(cond_out, "cond_out"))
+    _check(rc, "dit_timestep_embedding_noalloc")
 
 
 def linear(x, w, y, stream=None) -> None:

@@ -6,7 +6,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -1061,6 +1063,58 @@ int dit_timestep_embedding(int dtype, void* stream, const float* t, const float*
     if (overlap(rws, range_of(cond_out, 1, d, d, dtype))) return fail(DIT_ERR_INVALID_ARG, "cond_out overlaps the workspace");
     return temb_launch(dtype, reinterpret_cast<hipStream_t>(stream), t, g, w_t_in, w_t_out, w_g_in, w_g_out, freq_dim,
                        d, max_period, time_factor, cond_out, reinterpret_cast<char*>(workspace));
+}
+
+// ---- the allocation-free variant: its scratch is a file-scope device array --------------------
+// Each GPU holds its own copy of `scratch` (DIT_TEMB_STATIC_SCRATCH bytes) until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: its device address on the
+// current device comes from hipGetSymbolAddress, once per device, and only that address is handed
+// to kernels.
+static __device__ __align__(256) char scratch[DIT_TEMB_STATIC_SCRATCH];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (nullptr + error message on failure).
+void* static_scratch(int& err) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        err = fail(DIT_ERR_HIP, "hipGetDevice failed or device %d out of range", dev);
+        return nullptr;
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            err = fail(DIT_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+}  // namespace
+
+int dit_timestep_embedding_noalloc(int dtype, void* stream, const float* t, const float* g, const void* w_t_in,
+                                   const void* w_t_out, const void* w_g_in, const void* w_g_out, int freq_dim, int d,
+                                   float max_period, float time_factor, void* cond_out) {
+    clear_err();
+    DIT_TRY(check_temb(dtype, t, g, w_t_in, w_t_out, w_g_in, w_g_out, freq_dim, d, max_period, time_factor, cond_out));
+    const size_t need = temb_ws(freq_dim, d);
+    if (need > (size_t)DIT_TEMB_STATIC_SCRATCH)
+        return fail(DIT_ERR_UNSUPPORTED, "freq_dim = %d, d = %d need %zu bytes of scratch; the static scratch holds %d",
+                    freq_dim, d, need, DIT_TEMB_STATIC_SCRATCH);
+    int err = DIT_OK;
+    void* ws = static_scratch(err);
+    if (!ws) return err;
+    return temb_launch(dtype, reinterpret_cast<hipStream_t>(stream), t, g, w_t_in, w_t_out, w_g_in, w_g_out, freq_dim,
+                       d, max_period, time_factor, cond_out, reinterpret_cast<char*>(ws));
 }
 
 int dit_linear(int dtype, void* stream, const void* x, int x_dtype, long ld_x, const void* w, int m, int n, int k,

@@ -328,6 +328,24 @@ int dit_timestep_embedding(int dtype, void* stream, const float* t, const float*
                            int freq_dim, int d, float max_period, float time_factor,
                            void* cond_out, void* workspace, size_t ws_bytes);
 
+/*
+ * dit_timestep_embedding for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * kernels and result, with the scratch in a static device array of the library
+ * (DIT_TEMB_STATIC_SCRATCH bytes per GPU, held until the process ends) instead of a
+ * caller workspace.  The call allocates nothing.
+ * Limit: dit_timestep_embedding_workspace_size(freq_dim, d) <= DIT_TEMB_STATIC_SCRATCH
+ * (e.g. freq_dim 256 with d up to 8064); larger sizes return DIT_ERR_UNSUPPORTED.
+ * Every call on one GPU shares that GPU's array: calls that can overlap on one GPU
+ * (different streams without ordering, different threads) race and must not be
+ * issued; calls ordered on one stream are fine.  Other arguments as above.
+ */
+#define DIT_TEMB_STATIC_SCRATCH 65536
+int dit_timestep_embedding_noalloc(int dtype, void* stream, const float* t, const float* g,
+                                   const void* w_t_in, const void* w_t_out,
+                                   const void* w_g_in, const void* w_g_out,
+                                   int freq_dim, int d, float max_period, float time_factor,
+                                   void* cond_out);
 
 /*
  * y = x W^T on the block's GEMM kernel: the patch embedding of the image
