@@ -30,7 +30,10 @@
 // Work units are (head, 256-query tile) pairs.  With a stream-K scratch buffer (the block path) and
 // a partly filled last round of units, a persistent grid of one workgroup per CU splits the
 // remaining units' key tiles evenly; a unit's pieces are combined exactly like two halves of the
-// online softmax (running max, running sum, unnormalised O), in a fixed order.
+// online softmax (running max, running sum, unnormalised O), in a fixed order.  The split is local
+// to each XCD: the XCD's workgroups take a contiguous block of units (a few heads), run their full
+// rounds in step, then split only the rest of their block, so the K and V they read at any time
+// are about one head's, which the XCD's L2 holds.
 //
 // fp32 kernel: LDS-tiled, 4 threads per query, fp32 FMA throughout.
 #include "attn_common.h"
@@ -71,13 +74,15 @@ __device__ __forceinline__ unsigned* attn_flag(const AttnArgs& a, int g) {
 
 // One (head, query tile) unit L = head * nq + query tile over key tiles [kb, ke).
 // NEG: softmax_scale < 0 (the row max of the scaled scores is then the min of the raw ones).
-// Returns -1, or (an owner whose piece jn did not arrive; its state is in its carry slot) the index
-// jn of the next workgroup whose piece is still to be merged, with the missing piece's key tiles in
-// [ckb, cke): the driver then runs that continuation as the workgroup's next item.
+// Split units: g is the workgroup, gb the first workgroup of its segment (its XCD), Gs the
+// segment's workgroups and S its stream-K key tiles; pieces are indexed within the segment.
+// Returns -1, or (an owner whose piece jn did not arrive; its state is in its carry slot) the
+// segment index jn of the next workgroup whose piece is still to be merged, with the missing
+// piece's key tiles in [ckb, cke): the driver then runs that continuation as its next item.
 template <int DT, bool NEG>
 __device__ __forceinline__ int attention_unit(const AttnArgs& a, char* smem_k0, char* smem_k1, char* smem_v0,
-                                              char* smem_v1, int L, int kb, int ke, int kind,
-                                              int g, long S, long t_end, int jn0, int& ckb, int& cke) {
+                                              char* smem_v1, int L, int kb, int ke, int kind, int g, int gb, int Gs,
+                                              long S, long t_end, int jn0, int& ckb, int& cke) {
     constexpr int LPW = 16 / kAttnWaves;    // 1 KB load instructions per wave per K (or V) tile
     typedef typename AFrag<DT>::T FragT;
     // The two slots of the K ring and of the V ring are LDS arrays of their own, so the compiler
@@ -375,19 +380,18 @@ __device__ __forceinline__ int attention_unit(const AttnArgs& a, char* smem_k0, 
     // arrive in time the owner claims the piece, parks its state in its carry slot and returns; the
     // driver runs the piece's key tiles as its next item, which resumes here.
     if (kind == UNIT_OWNER || kind == UNIT_OWNER_CONT) {
-        const int G = a.sk_grid;
         int miss = -1;
         // jn = -1: the state parked in the carry slot (a continuation), then pieces from jn0
-        for (int jn = kind == UNIT_OWNER_CONT ? -1 : jn0; jn < G && (jn < 0 || sk_begin(S, jn, G) < t_end);
+        for (int jn = kind == UNIT_OWNER_CONT ? -1 : jn0; jn < Gs && (jn < 0 || sk_begin(S, jn, Gs) < t_end);
              jn = jn < 0 ? jn0 : jn + 1) {
             const float4* src = attn_carry(a, g);
             if (jn >= 0) {
-                if (sk_begin(S, jn + 1, G) == sk_begin(S, jn, G)) continue;     // empty share
-                if (!sk_take(attn_flag(a, jn), a.epoch, a.sk_spins)) {
+                if (sk_begin(S, jn + 1, Gs) == sk_begin(S, jn, Gs)) continue;     // empty share
+                if (!sk_take(attn_flag(a, gb + jn), a.epoch, a.sk_spins)) {
                     miss = jn;
                     break;
                 }
-                src = attn_partial(a, jn);
+                src = attn_partial(a, gb + jn);
             }
             merge_slot(src);
         }
@@ -395,8 +399,8 @@ __device__ __forceinline__ int attention_unit(const AttnArgs& a, char* smem_k0, 
             store_slot(attn_carry(a, g));
             __builtin_amdgcn_s_waitcnt(0);
             const long t_first = t_end - a.k_tiles;        // stream-K step of this unit's key tile 0
-            ckb = (int)(sk_begin(S, miss, G) - t_first);
-            cke = (int)(min(sk_begin(S, miss + 1, G), t_end) - t_first);
+            ckb = (int)(sk_begin(S, miss, Gs) - t_first);
+            cke = (int)(min(sk_begin(S, miss + 1, Gs), t_end) - t_first);
             return miss + 1;
         }
     }
@@ -424,11 +428,12 @@ __device__ __forceinline__ int attention_unit(const AttnArgs& a, char* smem_k0, 
 }
 
 // Persistent stream-K driver (sk_grid > 0) or one unit per workgroup.  Workgroup g (XCD-remapped,
-// so consecutive g, which share heads, share an L2) runs units g, g + G, ... below dp_units, then
-// its even share of the remaining units' key tiles in order: the end of a unit some earlier
-// workgroup started (published as a partial), whole units, and the start of a unit later
-// workgroups finish (it owns that one and merges their partials).  A unit's owner computes its
-// piece last, after the workgroups holding the other pieces computed theirs first.
+// so the Gs workgroups of a segment share an XCD and its L2) runs its segment's units gl, gl + Gs,
+// ... below dp (gl = its index in the segment), then its even share of the segment's remaining
+// key tiles in order: the end of a unit some earlier workgroup started (published as a partial),
+// whole units, and the start of a unit later workgroups finish (it owns that one and merges their
+// partials).  A unit's owner computes its piece last, after the workgroups holding the other
+// pieces computed theirs first.
 template <int DT, bool NEG>
 __device__ __forceinline__ void attention_mfma_body(const AttnArgs& a) {
     __shared__ __attribute__((aligned(1024))) char smem_k0[kTile];
@@ -437,35 +442,42 @@ __device__ __forceinline__ void attention_mfma_body(const AttnArgs& a) {
     __shared__ __attribute__((aligned(1024))) char smem_v1[kTile];
     const int g = xcd_remap(blockIdx.x, gridDim.x);
     const int G = a.sk_grid, I = a.k_tiles;
-    const long S = G ? (long)(a.units - a.dp_units) * I : 0;          // stream-K key tiles
-    const long e = G ? sk_begin(S, g + 1, G) : 0;
-    long it = G ? sk_begin(S, g, G) : 0;
+    // the segment (XCD) of workgroup g: workgroups [gb, gb + Gs), units [u0, u0 + Us), of which the
+    // first dp run whole (full rounds but one) and the rest, S key tiles, are split evenly
+    const int Gs = G ? G / a.sk_segs : 0;
+    const int x = G ? g / Gs : 0, gb = x * Gs, gl = g - gb;
+    const int u0 = G ? (int)((long)a.units * x / a.sk_segs) : 0;
+    const int Us = G ? (int)((long)a.units * (x + 1) / a.sk_segs) - u0 : 0;
+    const int dp = G && Us >= Gs ? (Us / Gs - 1) * Gs : 0;
+    const long S = G ? (long)(Us - dp) * I : 0;
+    const long e = G ? sk_begin(S, gl + 1, Gs) : 0;
+    long it = G ? sk_begin(S, gl, Gs) : 0;
     int cont = -1, ckb = 0, cke = 0, cL = 0;     // an owner's continuation (attention_unit's return)
     long ct_end = 0;
     // one work item per pass, so the unit code is generated once
     for (int w = 0;; ++w) {
-        int L, kb = 0, ke = I, kind = UNIT_FULL, jn0 = g + 1;
+        int L, kb = 0, ke = I, kind = UNIT_FULL, jn0 = gl + 1;
         long t_end = 0;
         if (cont >= 0) {
             L = cL; kb = ckb; ke = cke; kind = UNIT_OWNER_CONT; t_end = ct_end; jn0 = cont;
         } else if (G == 0) {
             if (w > 0) break;
             L = g;
-        } else if ((long)g + (long)w * G < a.dp_units) {
-            L = g + w * G;
+        } else if ((long)gl + (long)w * Gs < dp) {
+            L = u0 + gl + w * Gs;
         } else {
             if (it >= e) break;
             const int t = (int)(it / I);
             kb = (int)(it - (long)t * I);
             ke = (int)min((long)I, e - (long)t * I);
             kind = kb > 0 ? UNIT_PARTIAL : (ke == I ? UNIT_FULL : UNIT_OWNER);
-            L = a.dp_units + t;
+            L = u0 + dp + t;
             t_end = (long)(t + 1) * I;
             it = (long)t * I + ke;
         }
         if (w > 0) __syncthreads();                 // the K / V rings are reused by the next unit
-        cont = attention_unit<DT, NEG>(a, smem_k0, smem_k1, smem_v0, smem_v1, L, kb, ke, kind, g, S, t_end, jn0, ckb,
-                                       cke);
+        cont = attention_unit<DT, NEG>(a, smem_k0, smem_k1, smem_v0, smem_v1, L, kb, ke, kind, g, gb, Gs, S, t_end,
+                                       jn0, ckb, cke);
         cL = L;
         ct_end = t_end;
     }
@@ -551,15 +563,16 @@ hipError_t launch_attention(AttnArgs& a, hipStream_t s) {
         a.units = nq * a.n_heads;
         a.k_tiles = (a.n_tok + AK - 1) / AK;
         a.sk_grid = 0;
-        a.dp_units = 0;
+        a.sk_segs = 1;
         if (a.sk_scratch && G > 0 && a.units % G != 0) {
             const long rounds = (a.units + G - 1) / G;
             const long work = (long)a.units * a.k_tiles;
             const long idle = rounds * G * a.k_tiles - work;
             if (idle >= 4L * G && work >= 8L * G) {
-                const int D = a.units / G;
                 a.sk_grid = G;
-                a.dp_units = D >= 1 ? (D - 1) * G : 0;
+                // one segment per XCD (8 on gfx950; the remapped workgroup ids of an XCD are
+                // contiguous), or one for the whole grid if the CUs do not divide evenly
+                a.sk_segs = G % 8 == 0 ? 8 : 1;
                 a.epoch = next_launch_tag();
                 a.sk_spins = sk_spin_limit();
             }

@@ -124,7 +124,7 @@ struct AttnArgs {
     // Stream-K scratch (16-B-aligned device memory of attention_sk_scratch_bytes(), or null:
     // one workgroup per (head, query tile) unit).  The launcher fills the rest.
     void* sk_scratch;
-    int sk_grid, dp_units, units, k_tiles;
+    int sk_grid, sk_segs, units, k_tiles;
     unsigned epoch;
     int sk_spins;       // bound on an owner's wait for a piece (then it computes the piece itself)
 };
