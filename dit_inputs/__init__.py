@@ -36,7 +36,7 @@ __all__ = [
     "BlockConfig", "CONFIGS", "config_by_name", "positions",
     "bf16_bits_from_f32", "f32_from_bf16_bits",
     "draw", "double_block_inputs", "single_block_inputs",
-    "activation_inputs", "TENSOR_IDS",
+    "activation_inputs", "TENSOR_IDS", "fp8_attention_inputs",
 ]
 
 
@@ -147,7 +147,7 @@ TENSOR_IDS: Dict[str, int] = {
     "cond": 1, "x_txt": 2, "x_img": 3, "x": 4,
     "w_mod": 10, "w_qkv": 11, "qk_norm_w": 12, "w_o": 13, "w_ffn_in": 14, "w_ffn_out": 15,
     "w_1": 16, "w_2": 17,
-    "q": 20, "k": 21, "v": 22,
+    "q": 20, "k": 21, "v": 22, "q_scale": 23, "k_scale": 24, "v_scale": 25,
     "w_t_in": 30, "w_t_out": 31, "w_g_in": 32, "w_g_out": 33, "w_patch": 34, "latent": 35,
     "w_final_mod": 36, "w_final_out": 37, "w_mod_shared": 38,
 }
@@ -263,6 +263,32 @@ def qkv_inputs(cfg: BlockConfig, seed: int = 0, std: float = 1.0) -> Dict[str, n
     shape = (cfg.n_tok, cfg.d)
     return {"q": draw(shape, std, t, seed, "q"), "k": draw(shape, std, t, seed, "k"),
             "v": draw(shape, std, t, seed, "v")}
+
+
+def fp8_attention_inputs(n_tok: int, n_heads: int, head_dim: int = 128, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Operands of the fp8 attention call, drawn directly as e4m3 codes (no rounding involved).
+    q8, k8, v8 [n_tok, n_heads*head_dim] uint8: magnitude codes uniform over 0x30 .. 0x77 (values
+    0.5 .. 240, log-uniformly spread, rms about 68) with a random sign bit, 1% of them zeros.
+    Scales float32: sq [n_tok, n_heads] = f_h * U(0.5, 1.5) / 68 with a per-head sharpness
+    f_h ~ U(0.5, 2.5); sk [n_heads] and sv [n_heads] = U(0.8, 1.2) / 68.  The scaled scores
+    q.k / sqrt(head_dim) then have a standard deviation of about f_h (diffuse to peaked rows)."""
+    shape = (n_tok, n_heads * head_dim)
+    out = {}
+    for name in ("q", "k", "v"):
+        rng = np.random.default_rng([int(seed), 0, STREAM_IDS["none"], TENSOR_IDS[name], 8])
+        mag = rng.integers(0x30, 0x78, size=shape, dtype=np.uint8)
+        sign = (rng.integers(0, 2, size=shape, dtype=np.uint8) << 7).astype(np.uint8)
+        codes = (mag | sign).astype(np.uint8)
+        codes[rng.random(shape) < 0.01] = 0
+        out[name + "8"] = codes
+    rng = np.random.default_rng([int(seed), 0, STREAM_IDS["none"], TENSOR_IDS["q_scale"], 8])
+    sharp = rng.uniform(0.5, 2.5, n_heads)
+    out["sq"] = (sharp[None, :] * rng.uniform(0.5, 1.5, (n_tok, n_heads)) / 68.0).astype(np.float32)
+    rng = np.random.default_rng([int(seed), 0, STREAM_IDS["none"], TENSOR_IDS["k_scale"], 8])
+    out["sk"] = (rng.uniform(0.8, 1.2, n_heads) / 68.0).astype(np.float32)
+    rng = np.random.default_rng([int(seed), 0, STREAM_IDS["none"], TENSOR_IDS["v_scale"], 8])
+    out["sv"] = (rng.uniform(0.8, 1.2, n_heads) / 68.0).astype(np.float32)
+    return out
 
 
 def edge_inputs(cfg: BlockConfig, seed: int = 0, freq_dim: int = 256, patch: int = 64) -> Dict[str, np.ndarray]:

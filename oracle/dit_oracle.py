@@ -27,8 +27,9 @@ a per-stream weight, RoPE frequency theta^(-2j/dim_axis) with theta = 1e4 and
 rotation by +angle on interleaved pairs, softmax scale 1/sqrt(head_dim), no
 mask, text tokens first, SwiGLU with the gate half first.
 
-Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` or
-``tests/test_oracle_edge.py`` (closed forms, invariants, library special cases, brute force) except the
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_oracle_edge.py`` or ``tests/test_oracle_fp8.py`` (closed forms, invariants, library
+special cases, brute force) except the
 composition of the whole block, which is pinned only through its stages and
 block-level special cases (identity modulation, constant scores, zero FFN).
 """
@@ -466,6 +467,39 @@ def quantize_fp8_rows(x: np.ndarray):
 def linear_fp8(xq, sx, wq, sw) -> np.ndarray:
     """y = diag(sx) (dec(xq) dec(wq)^T) diag(sw), exact in float64."""
     return (np.asarray(sx, F64)[:, None] * (e4m3_decode(xq) @ e4m3_decode(wq).T)) * np.asarray(sw, F64)[None, :]
+
+
+def joint_attention_fp8(q8, sq, k8, sk, v8, sv, n_heads: int, head_dim: int, scale: Optional[float] = None,
+                        q_rows: Optional[np.ndarray] = None, round_p: bool = False) -> np.ndarray:
+    """Joint attention with e4m3 operands (the fp8 variant of the attention's two products).
+    q8, k8, v8 are [n, n_heads*head_dim] e4m3 codes, head h in columns h*head_dim ..; the scales are
+    float32: sq [n, n_heads] one per token and head, sk [n_heads] and sv [n_heads] one per head.  The
+    operands are Q_h = diag(sq[:, h]) dec(q8_h), K_h = sk[h] dec(k8_h), V_h = sv[h] dec(v8_h),
+    exactly, and O_h = softmax(Q_h K_h^T * scale) V_h in float64.
+
+    round_p adds a model of the probabilities passing through e4m3 on their way into the PV product:
+    with s the scaled scores of a row and w_j = exp(s_j - max s) (the largest weight is 1), the
+    weights become dec(e4m3(w_j)) while the normaliser stays the exact sum:
+    O = sum_j dec(e4m3(w_j)) V_j / sum_j w_j.  Weights below 2^-6 land on e4m3's subnormal grid
+    (steps of 2^-9)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    q = e4m3_decode(q8)
+    k = e4m3_decode(k8)
+    v = e4m3_decode(v8)
+    sq = np.asarray(sq, F64).reshape(q.shape[0], n_heads)
+    sk = np.asarray(sk, F64).reshape(n_heads)
+    sv = np.asarray(sv, F64).reshape(n_heads)
+    if q_rows is not None:
+        q, sq = q[q_rows], sq[q_rows]
+    out = np.empty((q.shape[0], n_heads * head_dim), dtype=F64)
+    for h in range(n_heads):
+        c = slice(h * head_dim, (h + 1) * head_dim)
+        s = (sq[:, h:h + 1] * q[:, c]) @ (sk[h] * k[:, c]).T * scale
+        w = np.exp(s - np.max(s, axis=1, keepdims=True))
+        wq = e4m3_decode(e4m3_encode(w)) if round_p else w
+        out[:, c] = (wq @ (sv[h] * v[:, c])) / np.sum(w, axis=1, keepdims=True)
+    return out
 
 
 # --- 2-D convolution (the diffusion-VAE decoder's layers) ----------------------------------------

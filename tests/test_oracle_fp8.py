@@ -102,3 +102,130 @@ def test_fp8_product_error_within_e4m3_rounding_bound():
     # and the fp8 block differs from the exact block only through these products
     y = o._product(x, w, True)
     assert not np.allclose(y, x @ w.T, rtol=1e-3)
+
+
+# --- fp8 joint attention -------------------------------------------------------------------------
+
+def _codes(rng, shape, lo=0x30, hi=0x78):
+    return (rng.integers(lo, hi, size=shape) | (rng.integers(0, 2, size=shape) << 7)).astype(np.uint8)
+
+
+def test_fp8_attention_brute_force():
+    # plain loops with math.exp on the decoded values: per-token q scales, per-head k and v scales,
+    # head slicing, the softmax scale -- a scale applied on the wrong axis or head fails here
+    import math
+    rng = np.random.default_rng(11)
+    n, H, D = 5, 2, 4
+    q8, k8, v8 = _codes(rng, (n, H * D)), _codes(rng, (n, H * D)), _codes(rng, (n, H * D))
+    sq = rng.uniform(0.001, 0.01, (n, H)).astype(np.float32)
+    sk = np.array([0.004, 0.007], np.float32)
+    sv = np.array([0.5, 0.25], np.float32)
+    scale = 0.37
+    dec = o.e4m3_decode
+    want = np.zeros((n, H * D))
+    for h in range(H):
+        for i in range(n):
+            s = [sum(float(sq[i, h]) * dec(q8[i, h * D + c]) * float(sk[h]) * dec(k8[j, h * D + c])
+                     for c in range(D)) * scale for j in range(n)]
+            mx = max(s)
+            w = [math.exp(x - mx) for x in s]
+            for c in range(D):
+                want[i, h * D + c] = sum(w[j] * float(sv[h]) * dec(v8[j, h * D + c]) for j in range(n)) / sum(w)
+    got = o.joint_attention_fp8(q8, sq, k8, sk, v8, sv, H, D, scale=scale)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
+    rows = np.array([3, 0])
+    np.testing.assert_allclose(o.joint_attention_fp8(q8, sq, k8, sk, v8, sv, H, D, scale=scale, q_rows=rows),
+                               want[rows], rtol=1e-12, atol=1e-15)
+
+
+def test_fp8_attention_equal_scores_give_the_mean_of_v():
+    # identical keys: every weight is exactly 1 (e4m3 holds 1), so both forms return mean(V)
+    rng = np.random.default_rng(12)
+    n, H, D = 9, 2, 8
+    q8, v8 = _codes(rng, (n, H * D)), _codes(rng, (n, H * D))
+    k8 = np.repeat(_codes(rng, (1, H * D)), n, axis=0)
+    sq = rng.uniform(0.001, 0.01, (n, H))
+    sk, sv = np.array([0.01, 0.02]), np.array([0.5, 3.0])
+    v = o.e4m3_decode(v8) * np.repeat(sv, D)[None, :]
+    for round_p in (False, True):
+        got = o.joint_attention_fp8(q8, sq, k8, sk, v8, sv, H, D, round_p=round_p)
+        np.testing.assert_allclose(got, np.broadcast_to(v.mean(axis=0), got.shape), rtol=1e-14)
+
+
+def test_fp8_attention_dominant_key_and_constant_v():
+    rng = np.random.default_rng(13)
+    n, H, D = 6, 1, 8
+    # key 2 equals the query direction scaled up: its score exceeds every other by > 30, so its
+    # weight is 1 and every other weight is below 2^-40 -- O is V_2 (exact form), and the rounded
+    # model drops the others entirely (they round to 0): O = V_2 / (1 + tiny)
+    q8 = np.full((n, D), 0x38, np.uint8)                      # all ones
+    k8 = _codes(rng, (n, D), 0x30, 0x38)                      # |k| in [0.5, 1)
+    k8 &= 0x7F                                                # positive
+    k8[2] = 0x58                                              # 8.0
+    v8 = _codes(rng, (n, D))
+    sq, sk, sv = np.ones((n, 1)), np.array([1.0]), np.array([0.125])
+    for rp in (False, True):
+        got = o.joint_attention_fp8(q8, sq, k8, sk, v8, sv, H, D, scale=1.0, round_p=rp)
+        np.testing.assert_allclose(got, np.broadcast_to(0.125 * o.e4m3_decode(v8[2]), got.shape), rtol=1e-12)
+    # V constant per feature: the exact form returns that row for every query, whatever the scores
+    v8c = np.repeat(_codes(rng, (1, D)), n, axis=0)
+    got = o.joint_attention_fp8(_codes(rng, (n, D)), rng.uniform(0.01, 0.1, (n, 1)), _codes(rng, (n, D)),
+                                np.array([0.05]), v8c, np.array([2.0]), H, D)
+    np.testing.assert_allclose(got, np.broadcast_to(2.0 * o.e4m3_decode(v8c[0]), got.shape), rtol=1e-13)
+
+
+def test_fp8_attention_rounded_weights_closed_form():
+    # two keys with scaled scores 0 and ln 0.3: weights 1 and 0.3; e4m3 holds 1 and rounds 0.3 =
+    # 1.2 * 2^-2 to 1.25 * 2^-2 = 0.3125, the normaliser stays 1.3:
+    # O = (V_1 + 0.3125 V_2) / 1.3 for the rounded model, (V_1 + 0.3 V_2) / 1.3 exactly
+    import math
+    rng = np.random.default_rng(15)
+    D = 8
+    q8 = np.full((2, D), 0x38, np.uint8)                      # ones
+    k8 = np.zeros((2, D), np.uint8)
+    k8[1] = 0x38                                              # key 1: q.k = 8, key 0: 0
+    v8 = _codes(rng, (2, D))
+    v = 0.5 * o.e4m3_decode(v8)
+    args = (q8, np.ones((2, 1)), k8, np.array([1.0]), v8, np.array([0.5]), 1, D)
+    scale = math.log(0.3) / 8
+    got = o.joint_attention_fp8(*args, scale=scale, round_p=True, q_rows=np.array([0]))
+    np.testing.assert_allclose(got[0], (v[0] + 0.3125 * v[1]) / 1.3, rtol=1e-13)
+    got = o.joint_attention_fp8(*args, scale=scale, q_rows=np.array([0]))
+    np.testing.assert_allclose(got[0], (v[0] + 0.3 * v[1]) / 1.3, rtol=1e-13)
+
+
+def test_fp8_attention_scale_moves_between_factors():
+    # s = sq sk scale q.k: moving a factor of 2 from sk to scale, or from sq to sk, changes nothing
+    rng = np.random.default_rng(14)
+    n, H, D = 7, 2, 16
+    q8, k8, v8 = _codes(rng, (n, H * D)), _codes(rng, (n, H * D)), _codes(rng, (n, H * D))
+    sq = rng.uniform(0.001, 0.01, (n, H))
+    sk, sv = np.array([0.01, 0.02]), np.array([0.5, 3.0])
+    a = o.joint_attention_fp8(q8, sq, k8, sk, v8, sv, H, D, scale=0.3)
+    np.testing.assert_allclose(o.joint_attention_fp8(q8, sq, k8, sk * 2, v8, sv, H, D, scale=0.15), a, rtol=1e-12)
+    np.testing.assert_allclose(o.joint_attention_fp8(q8, sq * 2, k8, sk / 2, v8, sv, H, D, scale=0.3), a,
+                               rtol=1e-12)
+
+
+def test_fp8_attention_rounded_weights_within_the_e4m3_bound():
+    # each weight w in (0, 1] moves by at most max(2^-4 w, 2^-10) (half a step, normal or
+    # subnormal), so |O_round - O| <= sum_j max(2^-4 w_j, 2^-10) |V_j| / sum_j w_j per element
+    import dit_inputs as di
+    x = di.fp8_attention_inputs(96, 2, seed=3)
+    H, D = 2, 128
+    exact = o.joint_attention_fp8(x["q8"], x["sq"], x["k8"], x["sk"], x["v8"], x["sv"], H, D)
+    rnd = o.joint_attention_fp8(x["q8"], x["sq"], x["k8"], x["sk"], x["v8"], x["sv"], H, D, round_p=True)
+    q = o.e4m3_decode(x["q8"]) * np.repeat(x["sq"].astype(np.float64), D, axis=1)
+    k = o.e4m3_decode(x["k8"]) * np.repeat(x["sk"].astype(np.float64), D)[None, :]
+    v = o.e4m3_decode(x["v8"]) * np.repeat(x["sv"].astype(np.float64), D)[None, :]
+    worst = 0.0
+    for h in range(H):
+        c = slice(h * D, (h + 1) * D)
+        s = q[:, c] @ k[:, c].T / np.sqrt(D)
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        bound = np.maximum(2.0 ** -4 * w, 2.0 ** -10) @ np.abs(v[:, c]) / w.sum(axis=1, keepdims=True)
+        err = np.abs(rnd[:, c] - exact[:, c])
+        assert np.all(err <= bound * (1 + 1e-9))
+        worst = max(worst, float(np.max(err / bound)))
+    assert worst > 0.05                    # the bound is not vacuous
+    assert not np.allclose(rnd, exact, rtol=1e-3)

@@ -46,6 +46,10 @@ MUTANTS = {
     "qk_weights_swapped": ("for which, t in ((0, q), (1, k)):", "for which, t in ((1, q), (0, k)):"),
     "single_ffn_rows": ("gu = _product(a[r], w1[3 * d:], fp8)", "gu = _product(a[r], w1[2 * d:2 * d + 2 * F], fp8)"),
     "fp8_product_drops_weight_scales": ("return linear_fp8(xq, sx, wq, sw)", "return linear_fp8(xq, sx, wq, np.ones_like(sw))"),
+    "fp8_attn_k_scale_for_v": ("out[:, c] = (wq @ (sv[h] * v[:, c]))", "out[:, c] = (wq @ (sk[h] * v[:, c]))"),
+    "fp8_attn_q_scale_per_head": ("s = (sq[:, h:h + 1] * q[:, c])", "s = (sq[0, h] * q[:, c])"),
+    "fp8_attn_no_softmax_scale": ("@ (sk[h] * k[:, c]).T * scale", "@ (sk[h] * k[:, c]).T"),
+    "fp8_attn_normalise_rounded": ("/ np.sum(w, axis=1, keepdims=True)", "/ np.sum(wq, axis=1, keepdims=True)"),
     "single_o_f_order": ("np.concatenate([o, f], axis=1)", "np.concatenate([f, o], axis=1)"),
     "v_from_k_block": ('v = np.concatenate([qkv["txt"][:, 2 * d:], qkv["img"][:, 2 * d:]], axis=0)',
                        'v = np.concatenate([qkv["txt"][:, d:2 * d], qkv["img"][:, d:2 * d]], axis=0)'),
