@@ -103,6 +103,8 @@ _natten = _sig("dit_neighborhood_attention", _i, [_i, _vp, _vp, _l, _vp, _l, _vp
                                                  ctypes.POINTER(_i), _i, _i, _f])
 _quant8 = _sig("dit_quantize_fp8", _i, [_i, _vp, _vp, _l, _i, _i, _vp, _l, _vp])
 _linear8 = _sig("dit_linear_fp8", _i, [_vp, _vp, _l, _vp, _vp, _l, _vp, _i, _i, _i, _vp, _i, _l])
+_attn8 = _sig("dit_joint_attention_fp8", _i, [_vp, _vp, _l, _vp, _vp, _l, _vp, _vp, _l, _vp, _vp, _i, _l, _i, _i, _i,
+                                               _f])
 _wsize8 = _sig("dit_block_fp8_workspace_size", _sz, [ctypes.POINTER(BlockConfig)])
 _block8 = _sig("dit_block_forward_fp8", _i, [ctypes.POINTER(BlockConfig), ctypes.POINTER(StreamWeightsFp8),
                                              ctypes.POINTER(StreamWeightsFp8), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
@@ -128,7 +130,7 @@ EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", 
             "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_timestep_embedding_noalloc",
             "dit_linear",
             "dit_final_layer_workspace_size", "dit_final_layer", "dit_neighborhood_attention",
-            "dit_quantize_fp8", "dit_linear_fp8", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
+            "dit_quantize_fp8", "dit_linear_fp8", "dit_joint_attention_fp8", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
             "dit_single_block_fp8_workspace_size", "dit_single_block_forward_fp8",
             "dit_conv2d", "dit_conv3d_causal", "dit_convert_bf16_to_f16",
             "dit_last_error", "dit_launch_count", "dit_workspace_flags", "dit_set_split_wait_limit",
@@ -591,6 +593,26 @@ def linear_fp8(xq, sx, wq, sw, y, stream=None) -> None:
                   _ptr(wq, "wq", torch.uint8), _ld(wq, "wq"), _ptr(sw, "sw", torch.float32), m, n, k, _ptr(y, "y"),
                   _dt(y), _ld(y, "y"))
     _check(rc, "dit_linear_fp8")
+
+
+def joint_attention_fp8(q8, sq, k8, sk, v8, sv, o, n_heads: int, softmax_scale: Optional[float] = None,
+                        head_dim: int = 128, stream=None) -> None:
+    """Joint attention on e4m3 codes (uint8 tensors [n, n_heads*head_dim]) with per token-and-head
+    q scales sq [n, n_heads] and per-head k / v scales sk, sv [n_heads]; see include/dit.h."""
+    import torch
+    if softmax_scale is None:
+        softmax_scale = head_dim ** -0.5
+    n = q8.shape[0]
+    for t, what in ((q8, "q8"), (k8, "k8"), (v8, "v8"), (o, "o")):
+        _rows(t, n, n_heads * head_dim, what)
+    _need(sq, n * n_heads, "sq")
+    _need(sk, n_heads, "sk")
+    _need(sv, n_heads, "sv")
+    rc = _attn8(_stream(stream), _ptr(q8, "q8", torch.uint8), _ld(q8, "q8"), _ptr(sq, "sq", torch.float32),
+                _ptr(k8, "k8", torch.uint8), _ld(k8, "k8"), _ptr(sk, "sk", torch.float32),
+                _ptr(v8, "v8", torch.uint8), _ld(v8, "v8"), _ptr(sv, "sv", torch.float32),
+                _ptr(o, "o"), _dt(o), _ld(o, "o"), n, n_heads, head_dim, softmax_scale)
+    _check(rc, "dit_joint_attention_fp8")
 
 
 def block_fp8_workspace_size(shape: Shape) -> int:

@@ -1338,6 +1338,50 @@ int dit_linear_fp8(void* stream, const void* xq, long ld_x, const float* sx, con
     return launch("gemm_fp8", s, [&] { return launch_gemm_fp8(g, s); });
 }
 
+int dit_joint_attention_fp8(void* stream, const void* q8, long ld_q, const float* q_scale, const void* k8, long ld_k,
+                            const float* k_scale, const void* v8, long ld_v, const float* v_scale, void* o,
+                            int o_dtype, long ld_o, int n_tok, int n_heads, int head_dim, float softmax_scale) {
+    clear_err();
+    if (!valid_dtype(o_dtype)) return fail(DIT_ERR_INVALID_ARG, "o_dtype must be DIT_F32, DIT_BF16 or DIT_F16");
+    if (head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim = %d (only 128 is supported)", head_dim);
+    if (n_heads < 1) return fail(DIT_ERR_INVALID_ARG, "n_heads = %d", n_heads);
+    if (n_tok < 0) return fail(DIT_ERR_INVALID_ARG, "n_tok = %d", n_tok);
+    if (!std::isfinite(softmax_scale)) return fail(DIT_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (n_tok == 0) return DIT_OK;          // nothing is read or written
+    DIT_TRY(check_ptr(q8, "q"));
+    DIT_TRY(check_ptr(k8, "k"));
+    DIT_TRY(check_ptr(v8, "v"));
+    DIT_TRY(check_ptr(q_scale, "q_scale"));
+    DIT_TRY(check_ptr(k_scale, "k_scale"));
+    DIT_TRY(check_ptr(v_scale, "v_scale"));
+    DIT_TRY(check_ptr(o, "o"));
+    const long width = (long)n_heads * head_dim;
+    const long* lds[3] = {&ld_q, &ld_k, &ld_v};
+    const char* names[3] = {"ld_q", "ld_k", "ld_v"};
+    for (int i = 0; i < 3; ++i)
+        if (*lds[i] < width || *lds[i] % 16 || *lds[i] >= (1L << 25))
+            return fail(DIT_ERR_INVALID_ARG, "%s = %ld must be >= n_heads * 128, a multiple of 16 and below 2^25",
+                        names[i], *lds[i]);
+    if (reinterpret_cast<uintptr_t>(q8) % 16 || reinterpret_cast<uintptr_t>(k8) % 16 ||
+        reinterpret_cast<uintptr_t>(v8) % 16)
+        return fail(DIT_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
+    DIT_TRY(check_ld(ld_o, width, o_dtype, "ld_o"));
+    if ((long)n_tok * n_heads > (1L << 30)) return fail(DIT_ERR_UNSUPPORTED, "n_tok * n_heads too large");
+    const Range ro = range_of(o, n_tok, ld_o, width, o_dtype);
+    auto codes = [&](const void* p, long ld) {
+        return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (uintptr_t)((n_tok - 1) * ld + width)};
+    };
+    if (overlap(ro, codes(q8, ld_q)) || overlap(ro, codes(k8, ld_k)) || overlap(ro, codes(v8, ld_v)) ||
+        overlap(ro, range_of(q_scale, n_tok, n_heads, n_heads, DIT_F32)) ||
+        overlap(ro, range_of(k_scale, 1, n_heads, n_heads, DIT_F32)) ||
+        overlap(ro, range_of(v_scale, 1, n_heads, n_heads, DIT_F32)))
+        return fail(DIT_ERR_INVALID_ARG, "o overlaps an input");
+    AttnFp8Args a{q8, ld_q, q_scale, k8, ld_k, k_scale, v8, ld_v, v_scale, o, ld_o, o_dtype, n_tok, n_heads,
+                  softmax_scale};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("joint_attention_fp8", s, [&] { return launch_attention_fp8(a, s); });
+}
+
 // =========================================================================================
 // 2-D convolution (NHWC), implicit GEMM.
 // =========================================================================================

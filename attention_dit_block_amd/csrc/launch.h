@@ -131,6 +131,21 @@ struct AttnArgs {
 hipError_t launch_attention(AttnArgs& a, hipStream_t s);
 size_t attention_sk_scratch_bytes();
 
+// ---- joint attention on e4m3 operands ----------------------------------------------------
+struct AttnFp8Args {
+    const void* q; long ld_q;           // e4m3 codes; strides in bytes (multiples of 16)
+    const float* q_scale;               // [n_tok, n_heads]
+    const void* k; long ld_k;
+    const float* k_scale;               // [n_heads]
+    const void* v; long ld_v;
+    const float* v_scale;               // [n_heads]
+    void* o; long ld_o;                 // o_dtype elements
+    int o_dtype;                        // F32, BF16 or F16
+    int n_tok, n_heads;
+    float scale;
+};
+hipError_t launch_attention_fp8(const AttnFp8Args& a, hipStream_t s);
+
 // ---- windowed (neighborhood) attention over a [T, H, W] token grid --------------------------
 struct WinAttnArgs {
     const void* q; long ld_q;

@@ -433,6 +433,37 @@ int dit_linear_fp8(void* stream, const void* xq, long ld_x, const float* sx,
                    void* y, int y_dtype, long ld_y);
 
 /*
+ * Joint attention with e4m3 operands: dit_joint_attention's softmax attention
+ * with both products (the scores and the PV product) on fp8 MFMA.
+ *
+ *   O_h = softmax(diag(sq_h) dec(Q_h) dec(K_h)^T sk_h * softmax_scale)
+ *         dec(V_h) sv_h                                      for every head h
+ *
+ *  q8, k8, v8  e4m3 codes [n_tok rows, byte strides ld_q/ld_k/ld_v]; head h
+ *              = columns h*128 .. h*128 + 127.  Strides multiples of 16 and
+ *              below 2^25, base pointers 16-byte aligned.
+ *  q_scale     fp32 [n_tok, n_heads] (sq_h = column h): one scale per token
+ *              and head, as dit_quantize_fp8 writes for the rows of one head
+ *  k_scale, v_scale  fp32 [n_heads]: one scale per head (sk_h, sv_h)
+ *  o           [n_tok rows, stride ld_o elements] of o_dtype (DIT_F32,
+ *              DIT_BF16 or DIT_F16); must not overlap the inputs
+ * Scores and softmax are fp32; the probabilities enter the PV product rounded
+ * to e4m3 (each within 2^-4 of its value relative to the tile's running max,
+ * or 2^-10 absolutely below e4m3's normal range); the normaliser is the
+ * fp32 sum of the unrounded probabilities.  Codes 0x7f / 0xff (NaN) and
+ * non-finite scales give non-finite outputs.
+ * Limits: head_dim == 128, n_heads >= 1, n_tok >= 0 (n_tok == 0: nothing is
+ * read or written), n_tok * n_heads <= 2^30.  One launch, one workgroup per
+ * (head, 256 queries).
+ */
+int dit_joint_attention_fp8(void* stream,
+                            const void* q8, long ld_q, const float* q_scale,
+                            const void* k8, long ld_k, const float* k_scale,
+                            const void* v8, long ld_v, const float* v_scale,
+                            void* o, int o_dtype, long ld_o,
+                            int n_tok, int n_heads, int head_dim, float softmax_scale);
+
+/*
  * fp8 double-stream block: dit_block_forward with its four weight products
  * (QKV, out-projection, FFN-in, FFN-down) on e4m3 codes.  Before each product
  * the block quantises the product's activations per row by dit_quantize_fp8's

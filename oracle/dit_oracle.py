@@ -470,7 +470,8 @@ def linear_fp8(xq, sx, wq, sw) -> np.ndarray:
 
 
 def joint_attention_fp8(q8, sq, k8, sk, v8, sv, n_heads: int, head_dim: int, scale: Optional[float] = None,
-                        q_rows: Optional[np.ndarray] = None, round_p: bool = False) -> np.ndarray:
+                        q_rows: Optional[np.ndarray] = None, round_p: bool = False,
+                        p_shift: Optional[np.ndarray] = None) -> np.ndarray:
     """Joint attention with e4m3 operands (the fp8 variant of the attention's two products).
     q8, k8, v8 are [n, n_heads*head_dim] e4m3 codes, head h in columns h*head_dim ..; the scales are
     float32: sq [n, n_heads] one per token and head, sk [n_heads] and sv [n_heads] one per head.  The
@@ -481,7 +482,9 @@ def joint_attention_fp8(q8, sq, k8, sk, v8, sv, n_heads: int, head_dim: int, sca
     with s the scaled scores of a row and w_j = exp(s_j - max s) (the largest weight is 1), the
     weights become dec(e4m3(w_j)) while the normaliser stays the exact sum:
     O = sum_j dec(e4m3(w_j)) V_j / sum_j w_j.  Weights below 2^-6 land on e4m3's subnormal grid
-    (steps of 2^-9)."""
+    (steps of 2^-9).  p_shift [rows, n_heads] (log2 units, 0 <= shift <= 8) rounds the weights of
+    a row relative to a max lower than the row's by that much instead: dec(e4m3(w_j 2^shift)) 2^-shift
+    -- an online softmax whose running max lags the row max by shift."""
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     q = e4m3_decode(q8)
@@ -497,7 +500,11 @@ def joint_attention_fp8(q8, sq, k8, sk, v8, sv, n_heads: int, head_dim: int, sca
         c = slice(h * head_dim, (h + 1) * head_dim)
         s = (sq[:, h:h + 1] * q[:, c]) @ (sk[h] * k[:, c]).T * scale
         w = np.exp(s - np.max(s, axis=1, keepdims=True))
-        wq = e4m3_decode(e4m3_encode(w)) if round_p else w
+        if round_p:
+            f = np.ones((w.shape[0], 1)) if p_shift is None else np.exp2(np.asarray(p_shift, F64)[:, h:h + 1])
+            wq = e4m3_decode(e4m3_encode(w * f)) / f
+        else:
+            wq = w
         out[:, c] = (wq @ (sv[h] * v[:, c])) / np.sum(w, axis=1, keepdims=True)
     return out
 

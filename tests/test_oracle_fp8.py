@@ -194,6 +194,28 @@ def test_fp8_attention_rounded_weights_closed_form():
     np.testing.assert_allclose(got[0], (v[0] + 0.3 * v[1]) / 1.3, rtol=1e-13)
 
 
+def test_fp8_attention_rounding_shift():
+    # a whole shift is a power-of-two scaling, exact in e4m3's normal range: shift 3 rounds the
+    # closed-form pair above the same way (0.3 * 8 = 2.4 -> 2.5 = 0.3125 * 8); a shift of
+    # log2(1.25) turns the largest weight 1 into 1.25 (exact) and 0.3 into 0.375 (exact): no
+    # rounding at all, so the model equals the exact form
+    import math
+    rng = np.random.default_rng(16)
+    D = 8
+    q8 = np.full((2, D), 0x38, np.uint8)
+    k8 = np.zeros((2, D), np.uint8)
+    k8[1] = 0x38
+    v8 = _codes(rng, (2, D))
+    v = 0.5 * o.e4m3_decode(v8)
+    args = (q8, np.ones((2, 1)), k8, np.array([1.0]), v8, np.array([0.5]), 1, D)
+    scale = math.log(0.3) / 8
+    got = o.joint_attention_fp8(*args, scale=scale, round_p=True, q_rows=np.array([0]), p_shift=np.array([[3.0]]))
+    np.testing.assert_allclose(got[0], (v[0] + 0.3125 * v[1]) / 1.3, rtol=1e-13)
+    got = o.joint_attention_fp8(*args, scale=scale, round_p=True, q_rows=np.array([0]),
+                                p_shift=np.array([[math.log2(1.25)]]))
+    np.testing.assert_allclose(got[0], (v[0] + 0.3 * v[1]) / 1.3, rtol=1e-13)
+
+
 def test_fp8_attention_scale_moves_between_factors():
     # s = sq sk scale q.k: moving a factor of 2 from sk to scale, or from sq to sk, changes nothing
     rng = np.random.default_rng(14)
