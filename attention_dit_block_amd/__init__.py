@@ -103,6 +103,7 @@ _natten = _sig("dit_neighborhood_attention", _i, [_i, _vp, _vp, _l, _vp, _l, _vp
                                                  ctypes.POINTER(_i), _i, _i, _f])
 _quant8 = _sig("dit_quantize_fp8", _i, [_i, _vp, _vp, _l, _i, _i, _vp, _l, _vp])
 _linear8 = _sig("dit_linear_fp8", _i, [_vp, _vp, _l, _vp, _vp, _l, _vp, _i, _i, _i, _vp, _i, _l])
+_mfma_loop = _sig("dit_mfma_loop", _i, [_vp, _i, _i, _vp])
 _attn8 = _sig("dit_joint_attention_fp8", _i, [_vp, _vp, _l, _vp, _vp, _l, _vp, _vp, _l, _vp, _vp, _i, _l, _i, _i, _i,
                                                _f])
 _wsize8 = _sig("dit_block_fp8_workspace_size", _sz, [ctypes.POINTER(BlockConfig)])
@@ -130,7 +131,7 @@ EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", 
             "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_timestep_embedding_noalloc",
             "dit_linear",
             "dit_final_layer_workspace_size", "dit_final_layer", "dit_neighborhood_attention",
-            "dit_quantize_fp8", "dit_linear_fp8", "dit_joint_attention_fp8", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
+            "dit_quantize_fp8", "dit_linear_fp8", "dit_joint_attention_fp8", "dit_mfma_loop", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
             "dit_single_block_fp8_workspace_size", "dit_single_block_forward_fp8",
             "dit_conv2d", "dit_conv3d_causal", "dit_convert_bf16_to_f16",
             "dit_last_error", "dit_launch_count", "dit_workspace_flags", "dit_set_split_wait_limit",
@@ -613,6 +614,13 @@ def joint_attention_fp8(q8, sq, k8, sk, v8, sv, o, n_heads: int, softmax_scale: 
                 _ptr(v8, "v8", torch.uint8), _ld(v8, "v8"), _ptr(sv, "sv", torch.float32),
                 _ptr(o, "o"), _dt(o), _ld(o, "o"), n, n_heads, head_dim, softmax_scale)
     _check(rc, "dit_joint_attention_fp8")
+
+
+def mfma_loop(workgroups: int, iters: int, out, stream=None) -> None:
+    """Calibration: workgroups x 4 waves x 4 chains x iters fp16 32x32x16 MFMAs (32768 flop each)."""
+    import torch
+    _need(out, workgroups * 256, "out")
+    _check(_mfma_loop(_stream(stream), workgroups, iters, _ptr(out, "out", torch.float32)), "dit_mfma_loop")
 
 
 def block_fp8_workspace_size(shape: Shape) -> int:

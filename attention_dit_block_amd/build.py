@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdit.so")
-SOURCES = ["dit_api.hip", "k_norm.hip", "k_gemm.hip", "k_attention.hip", "k_edge.hip", "k_window.hip", "k_fp8.hip", "k_conv.hip", "k_attn_fp8.hip"]
+SOURCES = ["dit_api.hip", "k_norm.hip", "k_gemm.hip", "k_attention.hip", "k_edge.hip", "k_window.hip", "k_fp8.hip", "k_conv.hip", "k_attn_fp8.hip", "k_calib.hip"]
 HEADERS = ["dev_common.h", "launch.h", "attn_common.h"]
 
 ARCH = "gfx950"

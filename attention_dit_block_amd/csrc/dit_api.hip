@@ -1382,6 +1382,15 @@ int dit_joint_attention_fp8(void* stream, const void* q8, long ld_q, const float
     return launch("joint_attention_fp8", s, [&] { return launch_attention_fp8(a, s); });
 }
 
+int dit_mfma_loop(void* stream, int workgroups, int iters, float* out) {
+    clear_err();
+    if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24))
+        return fail(DIT_ERR_INVALID_ARG, "workgroups = %d, iters = %d", workgroups, iters);
+    DIT_TRY(check_ptr(out, "out"));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("mfma_loop", s, [&] { return launch_mfma_loop(workgroups, iters, out, s); });
+}
+
 // =========================================================================================
 // 2-D convolution (NHWC), implicit GEMM.
 // =========================================================================================

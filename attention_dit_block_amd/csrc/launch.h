@@ -146,6 +146,9 @@ struct AttnFp8Args {
 };
 hipError_t launch_attention_fp8(const AttnFp8Args& a, hipStream_t s);
 
+// ---- calibration: a loop of fp16 MFMAs, 4 waves x 4 chains x iters per workgroup ----------
+hipError_t launch_mfma_loop(int workgroups, int iters, float* out, hipStream_t s);
+
 // ---- windowed (neighborhood) attention over a [T, H, W] token grid --------------------------
 struct WinAttnArgs {
     const void* q; long ld_q;

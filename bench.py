@@ -13,14 +13,25 @@ weights; ``--gemm-weights bf16`` times the weights as given).
 
 ``roofline`` covers the kernel with the largest total time, timed with HIP
 events the library records on the launch stream around each of its launches
-(dit_timing_*).  ``cpu_baseline`` times the fp64 oracle on one block of the same
-workload on the host cores.
+(dit_timing_*).  Its ``traffic`` is measured in this run: before the bench
+touches the GPU it runs its own step twice more as child processes under
+``rocprofv3 --pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``, each after three plain
+device copies of a known size that scale the counters to bytes (``--no-traffic``
+skips this).  ``calibration`` holds the launch floor, a measured MFMA-loop peak
+and copy bandwidth, and ``cold_hbm`` the AdaLN GEMV, modulation and QK-norm +
+RoPE kernels on buffers rotated over more than 512 MB (every launch reads HBM).
+``cpu_baseline`` times the fp64 oracle on one block of the same workload on the
+host cores.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
+import signal
+import tempfile
 import os
 import subprocess
 import sys
@@ -66,6 +77,11 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="first run a plain device-to-device copy of BYTES (3 times), to scale HBM "
                         "byte counters against a kernel of known traffic")
+    p.add_argument("--no-traffic", action="store_true",
+                   help="skip the two rocprofv3 counter passes that measure the kernels' HBM bytes")
+    p.add_argument("--no-calibration", action="store_true",
+                   help="skip the launch-floor, MFMA-loop, copy and cold-buffer measurements")
+    p.add_argument("--traffic-child", action="store_true", help=argparse.SUPPRESS)
     return p.parse_args()
 
 
@@ -111,6 +127,232 @@ def kernel_work(cfg, name, shared_mod=False):
     return (f / cnt if f else None), (b / cnt if b else None), bound
 
 
+CALIB_BYTES = 1 << 28            # plain copy that scales the byte counters
+TRAFFIC_COUNTERS = ("FETCH_SIZE", "WRITE_SIZE")
+
+
+def provenance():
+    """Where the numbers come from (no GPU use): git revision and dirty flag when the tree is a git
+    checkout, a hash of the sources the library is built from, the ROCm version."""
+    info = {"git_rev": None, "git_dirty": None}
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=20)
+        if r.returncode == 0:
+            info["git_rev"] = r.stdout.strip()
+            st = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
+                                capture_output=True, text=True, timeout=20)
+            info["git_dirty"] = bool(st.stdout.strip()) if st.returncode == 0 else None
+    except Exception:
+        pass
+    h = hashlib.sha256()
+    srcs = sorted(glob.glob(os.path.join(ROOT, "attention_dit_block_amd", "csrc", "*")) +
+                  [os.path.join(ROOT, "include", "dit.h")])
+    for path in srcs:
+        h.update(os.path.relpath(path, ROOT).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    info["source_sha256"] = h.hexdigest()[:16]
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    return info
+
+
+def _run_child(cmd, timeout_s):
+    """Run cmd in its own process group; kill the whole group if it outlives timeout_s."""
+    proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
+                            start_new_session=True)
+    try:
+        out, _ = proc.communicate(timeout=timeout_s)
+    except subprocess.TimeoutExpired:
+        os.killpg(proc.pid, signal.SIGKILL)
+        out, _ = proc.communicate()
+        return -9, out
+    return proc.returncode, out
+
+
+def _read_counter_csv(path, counter):
+    """[(dispatch id, kernel name, counter value summed over its instances)] in dispatch order."""
+    vals, names = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"]
+    return [(d, names[d], vals[d]) for d in sorted(vals)]
+
+
+def counters_from_csv(path, counter):
+    """One counter pass -> {"scale": bytes per counted byte, "values": bytes of each library launch
+    after setup, in order, "symbols": their kernels}, or a reason string.  The scale is the median
+    over the three largest non-library dispatches before the first library launch (the calibration
+    copies of CALIB_BYTES each way); the library's setup conversions (bf16 -> fp16 weight copies) are
+    skipped."""
+    rows = _read_counter_csv(path, counter)
+    lib = [i for i, (_, n, _) in enumerate(rows) if "dit::" in n and "bf16_to_f16" not in n]
+    if not lib:
+        return f"{counter}: no library dispatches"
+    copies = sorted((v for _, n, v in rows[:lib[0]] if "dit::" not in n), reverse=True)[:3]
+    if len(copies) < 3 or min(copies) <= 0:
+        return f"{counter}: calibration copies not found"
+    scale = CALIB_BYTES / (sorted(copies)[1] * 1024.0)
+    return {"scale": scale, "values": [rows[i][2] * 1024.0 * scale for i in lib], "symbols": [rows[i][1] for i in lib]}
+
+
+def counter_passes(args):
+    """The step's HBM bytes per launch, measured: the bench runs its own step (3 steps, after three
+    plain copies of CALIB_BYTES) as a child process under rocprofv3 --pmc FETCH_SIZE, then under
+    --pmc WRITE_SIZE.  Both counters are in KiB per dispatch; each is scaled by what it reads for
+    the copies (the copy moves CALIB_BYTES each way).  Runs before this process uses the GPU.
+    Returns ({counter: {"scale": bytes per counted byte, "per_step": [bytes of launch i of a step],
+    "symbols": [...]}}, command) or (None, reason)."""
+    child = [sys.executable, os.path.abspath(__file__), "--traffic-child", "--workload", args.workload,
+             "--steps", "3", "--warmup", "0", "--seed", str(args.seed), "--act", args.act,
+             "--gemm-weights", args.gemm_weights, "--copy-calibration", str(CALIB_BYTES)]
+    res = {}
+    with tempfile.TemporaryDirectory(prefix="dit_counters_") as tmp:
+        for ctr in TRAFFIC_COUNTERS:
+            d = os.path.join(tmp, ctr)
+            cmd = ["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", d, "-o", "c", "--"] + child
+            print(f"traffic: rocprofv3 --pmc {ctr} pass", file=sys.stderr, flush=True)
+            try:
+                rc, out = _run_child(cmd, 400)
+            except OSError as e:
+                return None, f"rocprofv3 not runnable: {e}"
+            files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+            if rc != 0 or not files:
+                return None, f"{ctr} pass failed (rc {rc}): {out[-300:]}"
+            res[ctr] = counters_from_csv(files[0], ctr)
+            if isinstance(res[ctr], str):
+                return None, res[ctr]
+    cmd_text = "rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <dir> -o c -- " + " ".join(
+        ["python3", "bench.py"] + child[2:])
+    return res, cmd_text
+
+
+def traffic_of(counters, order, name):
+    """Bytes per launch of launch site `name` (position order.index(name) in a step of len(order)
+    launches), averaged over the child's last two steps; None if the dispatches do not line up."""
+    if not counters or name not in order:
+        return None
+    L, p = len(order), order.index(name)
+    total, detail = 0.0, {}
+    for ctr, c in counters.items():
+        v, sym = c["values"], c["symbols"]
+        if len(v) % L or len(v) < 2 * L:
+            return None
+        idx = [len(v) - 2 * L + p, len(v) - L + p]
+        if sym[idx[0]] != sym[idx[1]]:
+            return None
+        b = sum(v[i] for i in idx) / 2
+        detail[ctr.lower() + "_bytes"] = int(b)
+        detail[ctr.lower() + "_scale"] = round(c["scale"], 4)
+        total += b
+    detail["bytes"] = int(total)
+    return detail
+
+
+def calibration(dit, torch, dev):
+    """Launch floor (the library's smallest launch, back to back), measured MFMA-loop rate and
+    device copy bandwidth: the ceilings this box reaches, next to the published peaks."""
+    s = torch.cuda.current_stream()
+
+    def ev_ms(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(reps):
+            fn()
+        b.record(s)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    out = {}
+    src = torch.zeros(8, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty(8, dtype=torch.float16, device=dev)
+    ev_ms(lambda: dit.convert_bf16_to_f16(src, dst), 200)
+    out["launch_floor_us"] = round(min(ev_ms(lambda: dit.convert_bf16_to_f16(src, dst), 2000) for _ in range(3))
+                                   / 2000 * 1e3, 2)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg, iters = 8 * cus, 4000
+    buf = torch.empty(wg * 256, dtype=torch.float32, device=dev)
+    ev_ms(lambda: dit.mfma_loop(wg, iters, buf), 3)
+    best = min(ev_ms(lambda: dit.mfma_loop(wg, iters, buf), 5) / 5 for _ in range(3))
+    out["mfma_loop_f16_tflops"] = round(wg * 4 * iters * 4 * 32768.0 / (best * 1e-3) / 1e12, 1)
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    ev_ms(lambda: b.copy_(a), 2)
+    best = min(ev_ms(lambda: b.copy_(a), 10) / 10 for _ in range(3))
+    out["copy_gbs"] = round(2.0 * n * 4 / (best * 1e-3) / 1e9, 1)
+    out["copy_bytes"] = 2 * n * 4
+    return out
+
+
+def cold_hbm(cfg, dit, torch, dev):
+    """The HBM-bound kernels of the block, one standalone launch after another on inputs rotated
+    over more than 512 MB (more than the MI355X's 8 x 4 MB L2 and 256 MB MALL), so every launch
+    reads HBM: the AdaLN GEMV (both streams' 12 d x d_cond weights), the modulation of x (bf16 in)
+    and of h (fp32 in) to fp16, and QK-norm + RoPE in place on fp16 q and k of a [n, 3d] buffer.
+    Algorithmic bytes per launch: weights + vectors (GEMV), n d (in + out) (modulation), 4 n d 2 +
+    16 n (QK-norm + RoPE: q and k read and written, positions)."""
+    n, d, dc, H = cfg.n_tok, cfg.d, cfg.dc, cfg.n_heads
+    rot = 600 << 20
+    out = {}
+
+    def measure(site, make, call, nbytes):
+        sets = [make() for _ in range(max(2, -(-rot // nbytes)))]
+        for st in sets:
+            call(st)
+        torch.cuda.synchronize()
+        reps = 3
+        dit.timing_begin(8 * reps * len(sets))
+        for _ in range(reps):
+            for st in sets:
+                call(st)
+        dit.timing_end()
+        torch.cuda.synchronize()
+        cnt, tot = dit.timing_read()[site]
+        us = tot / cnt * 1e3
+        out[site if site != "modulate" else make.__name__] = {
+            "us": round(us, 2), "bytes": int(nbytes), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "rotated_sets": len(sets)}
+        del sets
+        torch.cuda.empty_cache()
+
+    cond = torch.randn(dc, device=dev).to(torch.bfloat16)
+    mod = torch.empty(12 * d, dtype=torch.float32, device=dev)
+
+    def gemv_set():
+        return torch.randn(12 * d, dc, device=dev).mul_(0.02).to(torch.bfloat16)
+    measure("adaln_gemv", gemv_set, lambda w: dit.adaln_modulate(cond, w, 12, d, mod), 12 * d * dc * 2 + dc * 2 + 12 * d * 4)
+
+    w2 = torch.randn(2 * d, dc, device=dev).mul_(0.02).to(torch.bfloat16)
+    mod2 = torch.empty(2 * d, dtype=torch.float32, device=dev)
+
+    def modulate_x():
+        return (torch.randn(n, d, device=dev).to(torch.bfloat16), torch.empty(n, d, dtype=torch.float16, device=dev))
+
+    def modulate_h():
+        return (torch.randn(n, d, device=dev), torch.empty(n, d, dtype=torch.float16, device=dev))
+    for mk, es in ((modulate_x, 2), (modulate_h, 4)):
+        measure("modulate", mk, lambda xs: dit.adaln_modulate(cond, w2, 2, d, mod2, x=xs[0], x_out=xs[1]),
+                n * d * (es + 2))
+
+    import dit_inputs as di
+    pos = torch.from_numpy(di.positions(cfg.n_txt, cfg.grid_h, cfg.grid_w)).to(dev)
+    qk_w = torch.ones(2, 2, 128, dtype=torch.bfloat16, device=dev)
+
+    def qkv_set():
+        return torch.randn(n, 3 * d, device=dev).to(torch.float16)
+    measure("qk_rmsnorm_rope", qkv_set,
+            lambda b: dit.qk_rmsnorm_rope(b[:, :d], b[:, d:2 * d], H, qk_w, cfg.n_txt, pos), 4 * n * d * 2 + 16 * n)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -123,6 +365,14 @@ def main():
     import attention_dit_block_amd as dit
 
     cfg = di.config_by_name(args.workload)
+    # everything that starts another program runs here, before this process uses the GPU
+    prov = provenance() if not args.traffic_child else None
+    counters, counters_cmd = None, None
+    single_block = cfg.n_double == 1 and cfg.n_single == 0
+    if not (args.traffic_child or args.no_traffic or args.fp8_gemm or args.conv or args.fp8_block) and single_block:
+        counters, counters_cmd = counter_passes(args)
+        if counters is None:
+            print(f"traffic: not measured ({counters_cmd})", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     if args.fp8_gemm:
         return fp8_gemm_bench(args, cfg, dit, torch)
@@ -210,20 +460,27 @@ def main():
         for f in step_blocks:
             f()
 
+    if args.traffic_child:
+        # a counter pass: the steps only (the parent reads the counters of their launches)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        return
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_start = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
-    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    ev_ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     flops = cfg.flops_step()
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
@@ -257,12 +514,17 @@ def main():
     dit.timing_end()
     torch.cuda.synchronize()
     kt = dit.timing_read()
+    # launch sites in the order of a step (first appearance), when each runs once per step
+    order = list(kt) if all(c == args.steps for c, _ in kt.values()) else []
     kernels = {}
     for name, (cnt, tot) in kt.items():
         avg = tot / cnt
         fl, by, bound = kernel_work(cfg, name, shared)
         e = {"launches_per_step": cnt / args.steps, "avg_ms": round(avg, 5),
              "share": round(tot / sum(v[1] for v in kt.values()), 4), "bound": bound}
+        tr = traffic_of(counters, order, name)
+        if tr:
+            e["traffic_bytes"] = tr["bytes"]
         if fl:
             e["tflops"] = round(fl / (avg * 1e-3) / 1e12, 1)
             e["frac_mfma"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
@@ -280,7 +542,19 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(by / (avg * 1e-3) / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(cfg.name, dom, (args.act + ("/f16w" if f16w else "")) if t == "bf16" else "f32")
+    roof["avg_us"] = round(avg * 1e3, 2)
+    roof["algorithmic"] = {"flops": fl} if fl else {"bytes": by}
+    tr = traffic_of(counters, order, dom)
+    roof["traffic"] = tr["bytes"] if tr else None
+    if tr:
+        roof["traffic_detail"] = tr
+        roof["traffic_source"] = counters_cmd
+    else:
+        roof["traffic_note"] = ("counter passes skipped (--no-traffic)" if args.no_traffic else
+                                counters_cmd if counters is None else
+                                "the counter passes' launches did not line up with the step's launch sites")
+    calib = None if args.no_calibration else calibration(dit, torch, dev)
+    cold = None if args.no_calibration or t != "bf16" else cold_hbm(cfg, dit, torch, dev)
 
     # the arithmetic type of the matrix products: fp16 operands when the activations are fp16 (bf16
     # weights converted to fp16 copies, or while they are staged), bf16 operands otherwise
@@ -307,48 +581,20 @@ def main():
                    "modulation": "shared" if shared else "per_block"},
         "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "ms_per_step_hip_events": round(ev_ms, 4),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 4),
+        "ms_per_step_min": round(step_ms[0], 4),
         "ms_per_step_graph_replay": None if ms_graph is None else round(ms_graph, 4),
         "roofline": roof,
         "kernels": kernels,
+        "calibration": calib,
+        "cold_hbm": cold,
+        "provenance": prov,
         "setup_s": round(setup_s, 1),
     }
 
     if not args.no_cpu_baseline and cfg.n_single == 0:
         out["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(out), flush=True)
-
-
-# HBM bytes per launch, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) over this
-# bench, each counter scaled by what it reads for a plain device copy of known size (FETCH_SIZE
-# x2.0, WRITE_SIZE x1.0).  Keyed by workload, activation type (/f16w: fp16 product weights) and
-# kernel; each entry holds the
-# SHA-256 prefix of the kernel's source at the time of the counters and is reported only while
-# that source is unchanged.
-_C2 = "c2_bf16_d3072_t512_i4096"
-MEASURED_TRAFFIC = {
-    (_C2, "f16/f16w", "gemm_ffn_in_swiglu"): {"bytes": 1580828858, "sha256": "e7e540b5a969d75f"},
-    (_C2, "f16/f16w", "gemm_qkv"): {"bytes": 565891338, "sha256": "e7e540b5a969d75f"},
-    (_C2, "f16/f16w", "gemm_ffn_down"): {"bytes": 648753813, "sha256": "e7e540b5a969d75f"},
-    (_C2, "f16/f16w", "gemm_out_proj"): {"bytes": 275804369, "sha256": "e7e540b5a969d75f"},
-    (_C2, "f16/f16w", "joint_attention"): {"bytes": 879978277, "sha256": "6bf54797b33b7fdd"},
-    (_C2, "f16/f16w", "adaln_gemv"): {"bytes": 226856195, "sha256": "9ba2a8c38ca8bc15"},
-    (_C2, "f16/f16w", "qk_rmsnorm_rope"): {"bytes": 113904479, "sha256": "9ba2a8c38ca8bc15"},
-    (_C2, "f16/f16w", "modulate_h"): {"bytes": 85400691, "sha256": "9ba2a8c38ca8bc15"},
-    (_C2, "f16/f16w", "modulate_x"): {"bytes": 57093561, "sha256": "9ba2a8c38ca8bc15"},
-}
-
-KERNEL_SOURCE = {"gemm": "k_gemm.hip", "joint_attention": "k_attention.hip"}
-
-
-def measured_traffic(workload, kernel, act):
-    e = MEASURED_TRAFFIC.get((workload, act, kernel))
-    if e is None:
-        return None
-    src = next((v for k, v in KERNEL_SOURCE.items() if kernel.startswith(k)), "k_norm.hip")
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "attention_dit_block_amd", "csrc", src)
-    with open(path, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    return e["bytes"] if sha.startswith(e["sha256"]) else None
 
 
 def fp8_block_bench(args, cfg, dit, torch):

@@ -464,6 +464,15 @@ int dit_joint_attention_fp8(void* stream,
                             int n_tok, int n_heads, int head_dim, float softmax_scale);
 
 /*
+ * Calibration for measurements (not part of the block): `workgroups`
+ * workgroups of 4 waves each run iters x 4 independent
+ * v_mfma_f32_32x32x16_f16 (32768 flop each) with no memory traffic, then
+ * write one float per thread to out [workgroups * 256].  Its rate is the
+ * matrix cores' sustained fp16 throughput at the device's present clock.
+ */
+int dit_mfma_loop(void* stream, int workgroups, int iters, float* out);
+
+/*
  * fp8 double-stream block: dit_block_forward with its four weight products
  * (QKV, out-projection, FFN-in, FFN-down) on e4m3 codes.  Before each product
  * the block quantises the product's activations per row by dit_quantize_fp8's

@@ -62,3 +62,48 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def _fake_counter_csv(path, counter, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for d, name, v in rows:
+            # two instances per dispatch: the reader sums them
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v / 2})
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v / 2})
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": "OTHER", "Counter_Value": 1e9})
+
+
+def test_counter_bytes_per_launch_site(tmp_path):
+    # a counter pass: a fill, 3 calibration copies (counted at half their bytes), setup conversions,
+    # then 3 steps of 3 library launches; the bytes of launch site i come from its dispatches in the
+    # last two steps, scaled by the copies
+    kib = bench.CALIB_BYTES / 1024
+    rows = [(1, "at::fill", kib), (2, "at::copy", kib / 2), (3, "at::copy", kib / 2), (4, "at::copy", kib / 2),
+            (5, "dit::bf16_to_f16_kernel(unsigned short const*, unsigned short*, unsigned long)", 7.0)]
+    sites = ["void dit::gemv()", "void dit::gemm<0>()", "void dit::attn()"]
+    d = 6
+    for stepi in range(3):
+        for i, name in enumerate(sites):
+            rows.append((d, name, 100.0 * (i + 1) + (50.0 if stepi == 0 else 0.0)))   # the first step is cold
+            d += 1
+    p = tmp_path / "c_counter_collection.csv"
+    _fake_counter_csv(p, "FETCH_SIZE", rows)
+    parsed = bench._read_counter_csv(str(p), "FETCH_SIZE")
+    assert [r[0] for r in parsed] == list(range(1, d)) and parsed[5][2] == 150.0
+    c = bench.counters_from_csv(str(p), "FETCH_SIZE")
+    # the median of the three largest dispatches before the library's: a copy (the fill, counted
+    # differently here, is outvoted)
+    assert c["scale"] == 2.0
+    assert c["symbols"] == sites * 3 and c["values"][1] == 250.0 * 1024 * 2.0 and c["values"][4] == 200.0 * 1024 * 2.0
+    counters = {"FETCH_SIZE": c}
+    order = ["adaln_gemv", "gemm_qkv", "joint_attention"]
+    tr = bench.traffic_of(counters, order, "gemm_qkv")
+    assert tr["bytes"] == int(200.0 * 1024 * 2.0) and tr["fetch_size_scale"] == 2.0
+    assert bench.traffic_of(counters, order, "joint_attention")["bytes"] == int(300.0 * 1024 * 2.0)
+    # a step whose launches do not line up with the site order gives no figure
+    assert bench.traffic_of(counters, order + ["modulate_h"], "gemm_qkv") is None
+    assert bench.traffic_of(counters, order, "not_a_site") is None
+    assert bench.traffic_of(None, order, "gemm_qkv") is None
