@@ -224,9 +224,10 @@ def double_block(cfg, inputs: Dict[str, object], rows_txt=None, rows_img=None,
     stream); all tokens still enter the keys and values.  ``mods`` replaces
     the AdaLN vectors by given [6, d] arrays (special-case pins).  ``keep``
     returns the intermediates too.  ``fp8`` quantises both operands of the four weight
-    products (QKV, out-projection, FFN-in, FFN-down) to e4m3 per row (``_product``); the
-    activations are rounded to float32 just before (the quantiser's input precision), everything
-    else stays exact."""
+    products (QKV, out-projection, FFN-in, FFN-down) to e4m3 per row (``_product``) and runs the
+    attention on e4m3 q, k, v (``fp8_attention_operands``, ``joint_attention_fp8``); the
+    values are rounded to float32 just before each quantisation (the quantisers' input
+    precision), everything else stays exact."""
     t = cfg.dtype
     d, H, D, F = cfg.d, cfg.n_heads, cfg.head_dim, cfg.ffn_inner
     nt, ni = cfg.n_txt, cfg.n_img
@@ -254,7 +255,11 @@ def double_block(cfg, inputs: Dict[str, object], rows_txt=None, rows_img=None,
     rows = {"txt": np.arange(nt) if rows_txt is None else np.asarray(rows_txt),
             "img": np.arange(ni) if rows_img is None else np.asarray(rows_img)}
     q_rows = np.concatenate([rows["txt"], nt + rows["img"]])
-    o = joint_attention(q, k, v, H, D, q_rows=q_rows)
+    if fp8:
+        kmax = float(np.max(np.abs(qk_w[:, 1, :])))
+        o = joint_attention_fp8(*fp8_attention_operands(q, k, v, H, D, kmax), H, D, q_rows=q_rows)
+    else:
+        o = joint_attention(q, k, v, H, D, q_rows=q_rows)
     o_s = {"txt": o[:len(rows["txt"])], "img": o[len(rows["txt"]):]}
     out: Dict[str, np.ndarray] = {}
     for s in ("txt", "img"):
@@ -284,7 +289,8 @@ def single_block(cfg, inputs: Dict[str, object], rows=None, mods=None,
 
     Exact float64 arithmetic as in ``double_block``; x is read in ``x_dtype``.  ``fp8``
     quantises both operands of the two weight products (W_1 per output row, each activation row
-    over its full width) to e4m3, as ``double_block(fp8=True)`` does."""
+    over its full width) to e4m3 and runs the attention on e4m3 q, k, v, as
+    ``double_block(fp8=True)`` does."""
     t = cfg.dtype
     d, H, D, F = cfg.d, cfg.n_heads, cfg.head_dim, cfg.ffn_inner
     n = cfg.n_tok
@@ -303,7 +309,11 @@ def single_block(cfg, inputs: Dict[str, object], rows=None, mods=None,
     qk_w = widen(ws["qk_norm_w"], t).reshape(1, 2, D)
     q, k = qk_rmsnorm_rope(q, k, H, D, qk_w, n, cfg.eps_qk, pos, cfg.axes_dim, cfg.theta)
     r = np.arange(n) if rows is None else np.asarray(rows)
-    o = joint_attention(q, k, v, H, D, q_rows=r)
+    if fp8:
+        kmax = float(np.max(np.abs(qk_w[:, 1, :])))
+        o = joint_attention_fp8(*fp8_attention_operands(q, k, v, H, D, kmax), H, D, q_rows=r)
+    else:
+        o = joint_attention(q, k, v, H, D, q_rows=r)
     gu = _product(a[r], w1[3 * d:], fp8)
     f = swiglu(gu[:, :F], gu[:, F:])
     y = x[r] + m[2] * _product(np.concatenate([o, f], axis=1), _w(ws, "w_2", t), fp8)
@@ -507,6 +517,34 @@ def joint_attention_fp8(q8, sq, k8, sk, v8, sv, n_heads: int, head_dim: int, sca
             wq = w
         out[:, c] = (wq @ (sv[h] * v[:, c])) / np.sum(w, axis=1, keepdims=True)
     return out
+
+
+# Bound of a QK-normed, rotated head vector's elements relative to its weight: after RMSNorm the
+# 128 values have sum of squares 128 * ms / (ms + eps) < 128, so each has |x| < sqrt(128); the
+# weight multiplies it by at most max|w|, and a rotation of a pair (x, y) keeps sqrt(x^2 + y^2).
+K_BOUND_PER_WEIGHT = np.float32(math.sqrt(128.0) / E4M3_MAX)
+
+
+def fp8_attention_operands(q, k, v, n_heads: int, head_dim: int, k_weight_absmax: float):
+    """The e4m3 operands of the fp8 blocks' attention (float32 decisions, as the kernels take them):
+    q per (token, head) row by ``quantize_fp8_rows``; k per head with the static scale
+    s_k = float32(max|w_k| * float32(sqrt(128) / 448)), max over the k-norm weights the block uses
+    (every |k| stays below 448 s_k, see K_BOUND_PER_WEIGHT), codes e4m3(float32(k) / s_k); v per
+    head with s_v = max over the head's |v| / 448 (1 for an all-zero head), codes
+    e4m3(float32(v) / s_v).  Returns (q8, sq [n, H], k8, sk [H], v8, sv [H])."""
+    n, D, H = q.shape[0], head_dim, n_heads
+    q32, k32, v32 = (np.asarray(t, F64).astype(np.float32) for t in (q, k, v))
+    q8 = np.empty((n, H * D), np.uint8)
+    sq = np.empty((n, H), np.float32)
+    for h in range(H):
+        q8[:, h * D:(h + 1) * D], sq[:, h] = quantize_fp8_rows(q32[:, h * D:(h + 1) * D])
+    s_k = np.float32(np.float32(k_weight_absmax) * K_BOUND_PER_WEIGHT)
+    sk = np.full(H, s_k, np.float32)
+    k8 = e4m3_encode((k32 / s_k).astype(np.float32))
+    vmax = np.max(np.abs(v32).reshape(n, H, D), axis=(0, 2))
+    sv = np.where(vmax > 0, vmax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    v8 = e4m3_encode((v32 / np.repeat(sv, D)[None, :]).astype(np.float32))
+    return q8, sq, k8, sk, v8, sv
 
 
 # --- 2-D convolution (the diffusion-VAE decoder's layers) ----------------------------------------

@@ -251,3 +251,61 @@ def test_fp8_attention_rounded_weights_within_the_e4m3_bound():
         worst = max(worst, float(np.max(err / bound)))
     assert worst > 0.05                    # the bound is not vacuous
     assert not np.allclose(rnd, exact, rtol=1e-3)
+
+
+# --- the fp8 blocks' attention operands -----------------------------------------------------------
+
+def test_fp8_attention_operands_scales_and_codes():
+    rng = np.random.default_rng(21)
+    n, H, D = 10, 3, 16
+    q = rng.standard_normal((n, H * D)) * np.exp(rng.uniform(-2, 2, (n, 1)))
+    k = rng.standard_normal((n, H * D)) * 0.3
+    v = rng.standard_normal((n, H * D)) * np.repeat(np.array([0.5, 0.0, 7.0]), D)[None, :]
+    kmax = 1.25
+    q8, sq, k8, sk, v8, sv = o.fp8_attention_operands(q, k, v, H, D, kmax)
+    for h in range(H):
+        c = slice(h * D, (h + 1) * D)
+        # q: every (token, head) row's largest magnitude lands on +-448
+        np.testing.assert_array_equal(np.max(np.abs(o.e4m3_decode(q8[:, c])), axis=1), 448.0)
+        np.testing.assert_allclose(sq[:, h], np.max(np.abs(q[:, c]), axis=1) / 448.0, rtol=1e-6)
+    # k: one static scale per head from the weight bound
+    np.testing.assert_array_equal(sk, np.float32(np.float32(1.25) * np.float32(np.sqrt(128.0) / 448.0)))
+    # v: the zero head gets scale 1 and zero codes, the others map their max to 448
+    assert sv[1] == 1.0 and np.all(o.e4m3_decode(v8[:, D:2 * D]) == 0.0)
+    for h in (0, 2):
+        c = slice(h * D, (h + 1) * D)
+        assert np.max(np.abs(o.e4m3_decode(v8[:, c]))) == 448.0
+    # every operand within half an e4m3 step of its value (normal range) or of the scale's subnormal step
+    for x, codes, scale in ((q, q8, np.repeat(sq, D, axis=1)), (k, k8, sk[0]), (v, v8, np.repeat(sv, D)[None, :])):
+        back = o.e4m3_decode(codes) * scale
+        tol = np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * scale) * (1 + 1e-5)
+        assert np.all(np.abs(back - x) <= tol)
+
+
+def test_fp8_attention_k_bound_is_tight():
+    # the worst case of the bound: a one-hot head vector, RMS-normed at position 0 (no rotation),
+    # times the largest weight, reaches sqrt(128) * max|w| (less eps): its code is 448 (0x7E)
+    H, D = 1, 128
+    w = np.ones((1, 2, D))
+    w[0, 1, 0] = 1.5                        # k weight, dim 0 the largest
+    x = np.zeros((1, D))
+    x[0, 0] = 3.0
+    pos = np.zeros((1, 4), np.int32)
+    q, k = o.qk_rmsnorm_rope(x.copy(), x.copy(), H, D, w, 1, 1e-6, pos, (32, 32, 32, 32), 1e4)
+    assert abs(k[0, 0] - np.sqrt(128.0) * 1.5) < 1e-3        # eps shaves 7e-6 relative
+    _, _, k8, sk, _, _ = o.fp8_attention_operands(q, k, np.zeros((1, D)), H, D, 1.5)
+    assert k8[0, 0] == 0x7E
+    # random normed, rotated k never leaves the range
+    rng = np.random.default_rng(22)
+    n = 64
+    wr = 1.0 + 0.3 * rng.standard_normal((1, 2, D))
+    kk = rng.standard_normal((n, D)) * np.exp(rng.uniform(-3, 3, (n, 1)))
+    kk[np.arange(n) % 7 == 0] *= 0
+    kk[np.arange(n) % 7 == 0, rng.integers(0, D, (n + 6) // 7)] = 1.0       # one-hot rows
+    posr = rng.integers(0, 64, (n, 4)).astype(np.int32)
+    _, kn = o.qk_rmsnorm_rope(kk.copy(), kk.copy(), H, D, wr, n, 1e-6, posr, (32, 32, 32, 32), 1e4)
+    kw = float(np.max(np.abs(wr[0, 1])))
+    s_k = np.float32(np.float32(kw) * o.K_BOUND_PER_WEIGHT)
+    assert np.max(np.abs(kn)) / s_k <= 448.0 * (1 + 1e-6)
+    _, _, k8r, _, _, _ = o.fp8_attention_operands(kn, kn, np.zeros_like(kn), H, D, kw)
+    assert not np.any(np.isnan(o.e4m3_decode(k8r)))

@@ -50,6 +50,10 @@ MUTANTS = {
     "fp8_attn_q_scale_per_head": ("s = (sq[:, h:h + 1] * q[:, c])", "s = (sq[0, h] * q[:, c])"),
     "fp8_attn_no_softmax_scale": ("@ (sk[h] * k[:, c]).T * scale", "@ (sk[h] * k[:, c]).T"),
     "fp8_attn_normalise_rounded": ("/ np.sum(w, axis=1, keepdims=True)", "/ np.sum(wq, axis=1, keepdims=True)"),
+    "fp8_attn_k_bound_head_dim_64": ("K_BOUND_PER_WEIGHT = np.float32(math.sqrt(128.0) / E4M3_MAX)",
+                                     "K_BOUND_PER_WEIGHT = np.float32(math.sqrt(64.0) / E4M3_MAX)"),
+    "fp8_attn_v_scale_per_token": ("vmax = np.max(np.abs(v32).reshape(n, H, D), axis=(0, 2))",
+                                   "vmax = np.max(np.abs(v32).reshape(n, H, D), axis=(1, 2))[:H]"),
     "single_o_f_order": ("np.concatenate([o, f], axis=1)", "np.concatenate([f, o], axis=1)"),
     "v_from_k_block": ('v = np.concatenate([qkv["txt"][:, 2 * d:], qkv["img"][:, 2 * d:]], axis=0)',
                        'v = np.concatenate([qkv["txt"][:, d:2 * d], qkv["img"][:, d:2 * d]], axis=0)'),
