@@ -104,6 +104,7 @@ _natten = _sig("dit_neighborhood_attention", _i, [_i, _vp, _vp, _l, _vp, _l, _vp
 _quant8 = _sig("dit_quantize_fp8", _i, [_i, _vp, _vp, _l, _i, _i, _vp, _l, _vp])
 _linear8 = _sig("dit_linear_fp8", _i, [_vp, _vp, _l, _vp, _vp, _l, _vp, _i, _i, _i, _vp, _i, _l])
 _mfma_loop = _sig("dit_mfma_loop", _i, [_vp, _i, _i, _vp])
+_stream_probe = _sig("dit_stream_probe", _i, [_vp, _i, _vp, _vp, _sz, _i, _vp])
 _attn8 = _sig("dit_joint_attention_fp8", _i, [_vp, _vp, _l, _vp, _vp, _l, _vp, _vp, _l, _vp, _vp, _i, _l, _i, _i, _i,
                                                _f])
 _wsize8 = _sig("dit_block_fp8_workspace_size", _sz, [ctypes.POINTER(BlockConfig)])
@@ -131,7 +132,7 @@ EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", 
             "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_timestep_embedding_noalloc",
             "dit_linear",
             "dit_final_layer_workspace_size", "dit_final_layer", "dit_neighborhood_attention",
-            "dit_quantize_fp8", "dit_linear_fp8", "dit_joint_attention_fp8", "dit_mfma_loop", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
+            "dit_quantize_fp8", "dit_linear_fp8", "dit_joint_attention_fp8", "dit_mfma_loop", "dit_stream_probe", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
             "dit_single_block_fp8_workspace_size", "dit_single_block_forward_fp8",
             "dit_conv2d", "dit_conv3d_causal", "dit_convert_bf16_to_f16",
             "dit_last_error", "dit_launch_count", "dit_workspace_flags", "dit_set_split_wait_limit",
@@ -621,6 +622,22 @@ def mfma_loop(workgroups: int, iters: int, out, stream=None) -> None:
     import torch
     _need(out, workgroups * 256, "out")
     _check(_mfma_loop(_stream(stream), workgroups, iters, _ptr(out, "out", torch.float32)), "dit_mfma_loop")
+
+
+def stream_probe(mode: int, src, dst=None, sink=None, workgroups: int = 2048, stream=None) -> None:
+    """Calibration: stream src (mode 0: read into sink [workgroups*256] fp32; mode 1: copy to dst)."""
+    import torch
+    nbytes = src.numel() * src.element_size()
+    _need(src, src.numel(), "src")
+    if mode == 1:
+        _need(dst, src.numel(), "dst")
+        if dst.element_size() != src.element_size():
+            raise ValueError("dst must have src's element size")
+    else:
+        _need(sink, workgroups * 256, "sink")
+    rc = _stream_probe(_stream(stream), mode, _ptr(src, "src"), _ptr(dst, "dst") if mode == 1 else None, nbytes,
+                       workgroups, _ptr(sink, "sink", torch.float32) if mode == 0 else None)
+    _check(rc, "dit_stream_probe")
 
 
 def block_fp8_workspace_size(shape: Shape) -> int:

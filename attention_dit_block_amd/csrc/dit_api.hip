@@ -143,7 +143,7 @@ int validate_config(const dit_block_config* c) {
 
 // Workspace plan: 256-byte aligned sub-buffers.
 struct WsPlan {
-    size_t flags, mod, act, qkv, o, h, f, of, sk, sk_bytes, ask, ask_bytes, q8, sq, total;
+    size_t flags, mod, act, qkv, o, h, f, of, sk, sk_bytes, ask, ask_bytes, a8, a8s, q8, sq, total;
 };
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 WsPlan plan_workspace(const dit_block_config* c, int single, bool fp8 = false) {
@@ -171,8 +171,13 @@ WsPlan plan_workspace(const dit_block_config* c, int single, bool fp8 = false) {
     // attention's stream-K scratch (16-bit paths)
     p.ask_bytes = c->dtype == DIT_BF16 ? attention_sk_scratch_bytes() : 0;
     p.ask = take(p.ask_bytes);
-    // fp8 products: the e4m3 codes and per-row scales of the current product's activations
+    // fp8: the attention's e4m3 operands [n, 3d] (q | k | v codes) and their scales (q per token
+    // and head, k and v per head) with the per-head |v| maxima; then the codes and per-row scales
+    // of the current product's activations
     if (fp8) {
+        const size_t H = c->n_heads;
+        p.a8 = take(n * 3 * d);
+        p.a8s = take((n * H + 3 * H) * 4);
         p.q8 = take(n * (single ? d + F : std::max(d, F)));
         p.sq = take(n * 4);
     }
@@ -438,6 +443,12 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     // fp8 products: a goes straight to e4m3 codes with per-row scales
     uint8_t* q8 = fp8 ? reinterpret_cast<uint8_t*>(ws + W.q8) : nullptr;
     float* sq = fp8 ? reinterpret_cast<float*>(ws + W.sq) : nullptr;
+    // fp8 attention operands: codes, scales, and the per-head |v| maxima (zeroed by the modulation)
+    uint8_t* a8 = fp8 ? reinterpret_cast<uint8_t*>(ws + W.a8) : nullptr;
+    float* a8_sq = fp8 ? reinterpret_cast<float*>(ws + W.a8s) : nullptr;
+    float* a8_sk = fp8 ? a8_sq + (size_t)n * c.n_heads : nullptr;
+    float* a8_sv = fp8 ? a8_sk + c.n_heads : nullptr;
+    unsigned* a8_vmax = fp8 ? reinterpret_cast<unsigned*>(a8_sv + c.n_heads) : nullptr;
     auto to_fp8 = [&](ModBatch& mb) {
         int r0 = 0;
         for (int i = 0; i < mb.n; ++i) {
@@ -447,7 +458,10 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
         }
         mb.out_dtype = FP8_ROWS;
     };
-    if (fp8) to_fp8(m);
+    if (fp8) {
+        to_fp8(m);
+        m.clear = a8_vmax; m.clear_n = c.n_heads;
+    }
     DIT_TRY(launch(fp8 ? "modulate_x_fp8" : "modulate_x", s, [&] { return launch_modulate(m, s); }));
 
     // fp8 products: quantise the activations [n, k] (row stride k) per row (a and b come quantised
@@ -473,6 +487,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
         if (ni) b.p[b.n++] = fp8_problem(nt, ni, d, i8->w_qkv, i8->s_qkv, qkv + (size_t)nt * 3 * d * es, 3L * d,
                                          c.act_dtype, 3 * d, EPI_STORE);
         b.range_flag = flag;
+        b.vmax = a8_vmax; b.vmax_col0 = 2 * d;
         DIT_TRY(launch("gemm_fp8_qkv", s, [&] { return launch_gemm_fp8(b, s); }));
     } else {
     GemmBatch gq{};
@@ -496,13 +511,24 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     r.q = qkv; r.ld_q = 3L * d; r.k = qkv + (size_t)d * es; r.ld_k = 3L * d;
     r.n_tok = n; r.n_heads = c.n_heads; r.qk_w0 = qkw_t; r.qk_w1 = qkw_i; r.n_first = nt;
     r.eps = c.eps_qk; r.pos = pos; r.n_axes = c.n_axes; r.dtype = c.act_dtype; r.w_dtype = c.dtype;
-    DIT_TRY(launch("qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(r, s); }));
+    if (fp8) {
+        // e4m3 q, k, v for the attention (q, k in qkv stay unrotated)
+        r.qkv8 = a8; r.ld8 = 3L * d; r.sq = a8_sq; r.sk = a8_sk; r.sv = a8_sv;
+        r.v = qkv + (size_t)2 * d * es; r.ld_v = 3L * d; r.vmax = a8_vmax;
+    }
+    DIT_TRY(launch(fp8 ? "qk_rmsnorm_rope_fp8" : "qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(r, s); }));
 
     // 5. O = joint attention over all n tokens
-    AttnArgs at{qkv, 3L * d, qkv + (size_t)d * es, 3L * d, qkv + (size_t)2 * d * es, 3L * d, ob, d, n, c.n_heads,
-                1.0f / std::sqrt((float)c.head_dim), c.act_dtype};
-    at.sk_scratch = W.ask_bytes ? ws + W.ask : nullptr;
-    DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
+    if (fp8) {
+        AttnFp8Args af{a8, 3L * d, a8_sq, a8 + d, 3L * d, a8_sk, a8 + 2 * (size_t)d, 3L * d, a8_sv, ob, d,
+                       c.act_dtype, n, c.n_heads, 1.0f / std::sqrt((float)c.head_dim)};
+        DIT_TRY(launch("joint_attention_fp8", s, [&] { return launch_attention_fp8(af, s); }));
+    } else {
+        AttnArgs at{qkv, 3L * d, qkv + (size_t)d * es, 3L * d, qkv + (size_t)2 * d * es, 3L * d, ob, d, n, c.n_heads,
+                    1.0f / std::sqrt((float)c.head_dim), c.act_dtype};
+        at.sk_scratch = W.ask_bytes ? ws + W.ask : nullptr;
+        DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
+    }
 
     // 6. h = x + gate1 * (O W_o^T)   (fp32)
     if (fp8) {
@@ -674,6 +700,12 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
     char* of = ws + W.of;
     uint8_t* q8 = fp8 ? reinterpret_cast<uint8_t*>(ws + W.q8) : nullptr;
     float* sq = fp8 ? reinterpret_cast<float*>(ws + W.sq) : nullptr;
+    // fp8 attention operands: codes, scales, and the per-head |v| maxima (zeroed by the modulation)
+    uint8_t* a8 = fp8 ? reinterpret_cast<uint8_t*>(ws + W.a8) : nullptr;
+    float* a8_sq = fp8 ? reinterpret_cast<float*>(ws + W.a8s) : nullptr;
+    float* a8_sk = fp8 ? a8_sq + (size_t)n * c.n_heads : nullptr;
+    float* a8_sv = fp8 ? a8_sk + c.n_heads : nullptr;
+    unsigned* a8_vmax = fp8 ? reinterpret_cast<unsigned*>(a8_sv + c.n_heads) : nullptr;
     unsigned* flag = reinterpret_cast<unsigned*>(ws + W.flags);
     const size_t es = esize(c.act_dtype);     // activation element size
     const long ldof = (long)d + F;
@@ -693,6 +725,7 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
     if (fp8) {
         // a goes straight to e4m3 codes with per-row scales
         m.p[0].out = q8; m.p[0].out_scale = sq; m.out_dtype = FP8_ROWS;
+        m.clear = a8_vmax; m.clear_n = c.n_heads;
     }
     DIT_TRY(launch(fp8 ? "modulate_x_fp8" : "modulate_x", s, [&] { return launch_modulate(m, s); }));
 
@@ -714,6 +747,7 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
         bg.p[0].up_off = F;
         bg.n = 1;
         bq.range_flag = bg.range_flag = flag;
+        bq.vmax = a8_vmax; bq.vmax_col0 = 2 * d;
         DIT_TRY(launch("gemm_fp8_linear1_qkv", s, [&] { return launch_gemm_fp8(bq, s); }));
         DIT_TRY(launch("gemm_fp8_linear1_gu", s, [&] { return launch_gemm_fp8(bg, s); }));
     } else {
@@ -735,12 +769,22 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
     r.n_tok = n; r.n_heads = c.n_heads; r.qk_w0 = qk_norm_w; r.qk_w1 = qk_norm_w; r.n_first = n;
     r.eps = c.eps_qk;
     r.pos = pos; r.n_axes = c.n_axes; r.dtype = c.act_dtype; r.w_dtype = c.dtype;
-    DIT_TRY(launch("qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(r, s); }));
+    if (fp8) {
+        r.qkv8 = a8; r.ld8 = 3L * d; r.sq = a8_sq; r.sk = a8_sk; r.sv = a8_sv;
+        r.v = qkv + (size_t)2 * d * es; r.ld_v = 3L * d; r.vmax = a8_vmax;
+    }
+    DIT_TRY(launch(fp8 ? "qk_rmsnorm_rope_fp8" : "qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(r, s); }));
 
-    AttnArgs at{qkv, 3L * d, qkv + (size_t)d * es, 3L * d, qkv + (size_t)2 * d * es, 3L * d, of, ldof, n, c.n_heads,
-                1.0f / std::sqrt((float)c.head_dim), c.act_dtype};
-    at.sk_scratch = W.ask_bytes ? ws + W.ask : nullptr;
-    DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
+    if (fp8) {
+        AttnFp8Args af{a8, 3L * d, a8_sq, a8 + d, 3L * d, a8_sk, a8 + 2 * (size_t)d, 3L * d, a8_sv, of, ldof,
+                       c.act_dtype, n, c.n_heads, 1.0f / std::sqrt((float)c.head_dim)};
+        DIT_TRY(launch("joint_attention_fp8", s, [&] { return launch_attention_fp8(af, s); }));
+    } else {
+        AttnArgs at{qkv, 3L * d, qkv + (size_t)d * es, 3L * d, qkv + (size_t)2 * d * es, 3L * d, of, ldof, n,
+                    c.n_heads, 1.0f / std::sqrt((float)c.head_dim), c.act_dtype};
+        at.sk_scratch = W.ask_bytes ? ws + W.ask : nullptr;
+        DIT_TRY(launch("joint_attention", s, [&] { return launch_attention(at, s); }));
+    }
 
     if (fp8) {
         DIT_TRY(launch("quantize_of", s, [&] {
@@ -1389,6 +1433,26 @@ int dit_mfma_loop(void* stream, int workgroups, int iters, float* out) {
     DIT_TRY(check_ptr(out, "out"));
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     return launch("mfma_loop", s, [&] { return launch_mfma_loop(workgroups, iters, out, s); });
+}
+
+int dit_stream_probe(void* stream, int mode, const void* src, void* dst, size_t bytes, int workgroups, float* sink) {
+    clear_err();
+    if (mode != 0 && mode != 1) return fail(DIT_ERR_INVALID_ARG, "mode = %d", mode);
+    if (bytes == 0 || bytes % 16384) return fail(DIT_ERR_INVALID_ARG, "bytes = %zu must be a positive multiple of 16384", bytes);
+    if (workgroups < 1 || workgroups > (1 << 20)) return fail(DIT_ERR_INVALID_ARG, "workgroups = %d", workgroups);
+    DIT_TRY(check_ptr(src, "src"));
+    if (reinterpret_cast<uintptr_t>(src) % 16) return fail(DIT_ERR_INVALID_ARG, "src must be 16-byte aligned");
+    if (mode == 1) {
+        DIT_TRY(check_ptr(dst, "dst"));
+        if (reinterpret_cast<uintptr_t>(dst) % 16) return fail(DIT_ERR_INVALID_ARG, "dst must be 16-byte aligned");
+        const Range a{reinterpret_cast<uintptr_t>(src), reinterpret_cast<uintptr_t>(src) + bytes};
+        const Range b{reinterpret_cast<uintptr_t>(dst), reinterpret_cast<uintptr_t>(dst) + bytes};
+        if (overlap(a, b)) return fail(DIT_ERR_INVALID_ARG, "dst overlaps src");
+    } else {
+        DIT_TRY(check_ptr(sink, "sink"));
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("stream_probe", s, [&] { return launch_stream_probe(src, dst, bytes, mode, workgroups, sink, s); });
 }
 
 // =========================================================================================

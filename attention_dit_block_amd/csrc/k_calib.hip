@@ -33,3 +33,37 @@ hipError_t launch_mfma_loop(int workgroups, int iters, float* out, hipStream_t s
 }
 
 }  // namespace dit
+
+namespace dit {
+
+// Streaming probes: every thread moves 64 B per iteration (four 16-byte accesses, unrolled, all
+// loads issued before any use), grid-stride over the buffer.  mode 0 reads src and writes one
+// float per thread (the HBM read ceiling); mode 1 copies src to dst (read + write).
+__global__ __launch_bounds__(256) void stream_probe_kernel(const u32x4_v* __restrict__ src, u32x4_v* __restrict__ dst,
+                                                           size_t n16, int mode, float* sink) {
+    const size_t stride = (size_t)gridDim.x * 256 * 4;
+    size_t i = ((size_t)blockIdx.x * 256) * 4 + threadIdx.x;
+    u32x4_v acc = {0u, 0u, 0u, 0u};
+    for (; i + 3 * 256 < n16; i += stride) {
+        u32x4_v v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(src + i + j * 256);
+        if (mode == 1) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(v[j], dst + i + j * 256);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc ^= v[j];
+        }
+    }
+    if (mode == 0) sink[(size_t)blockIdx.x * 256 + threadIdx.x] = __uint_as_float(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+}
+
+hipError_t launch_stream_probe(const void* src, void* dst, size_t bytes, int mode, int workgroups, float* sink,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(stream_probe_kernel, dim3(workgroups), dim3(256), 0, s, reinterpret_cast<const u32x4_v*>(src),
+                       reinterpret_cast<u32x4_v*>(dst), bytes / 16, mode, sink);
+    return hipGetLastError();
+}
+
+}  // namespace dit

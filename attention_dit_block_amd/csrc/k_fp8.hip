@@ -193,6 +193,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmBatch bt) {
     // epilogue: acc[nb][mb][q] -> row m0 + wm*128 + mb*32 + (lane & 31); B row b_row[nb] - (lane & 31)
     // + 8 (q >> 2) + 4 h + (q & 3) of the tile
     bool bad = false;              // an fp16 output out of fp16's range
+    float vm = 0.0f;               // EPI_STORE with vmax: largest |stored value| of this lane
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
         const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
@@ -234,11 +235,29 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmBatch bt) {
                     }
                     if (g.c_dtype == F16)
                         bad |= f16_out_of_range4(o);
+                    if constexpr (MODE == EPI_STORE) {
+                        if (bt.vmax) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                vm = fmaxf(vm, fabsf(g.c_dtype == F16 ? (float)(_Float16)o[j] : o[j]));
+                        }
+                    }
                     store4_any(g.c, (size_t)m * g.ldc + col, g.c_dtype, o);
                 }
         }
     }
     raise_range_flag(bt.range_flag, bad);
+    if constexpr (MODE == EPI_STORE) {
+        // a wave's 64 columns lie inside one 128-column head: one atomic max per wave
+        const int cb = n0 + wn * 64;
+        if (bt.vmax && cb >= bt.vmax_col0 && cb < g.N) {
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) vm = fmaxf(vm, __shfl_xor(vm, off, 64));
+            if (lane == 0)
+                __hip_atomic_fetch_max(bt.vmax + (cb - bt.vmax_col0) / 128, __float_as_uint(vm), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 hipError_t launch_gemm_fp8(Fp8GemmBatch& bt, hipStream_t s) {

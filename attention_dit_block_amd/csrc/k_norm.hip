@@ -153,6 +153,8 @@ template <int XT, int OT, int NC>
 __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
     extern __shared__ float s_mod[];               // shift [d], then scale [d]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (b.clear && blockIdx.x == 0)
+        for (int i = threadIdx.x; i < b.clear_n; i += 256) b.clear[i] = 0u;
     const int nb0 = (b.p[0].rows + 3) / 4;         // workgroups of problem 0
     const int pi = (b.n > 1 && (int)blockIdx.x >= nb0) ? 1 : 0;
     const ModProblem& P = b.p[pi];
@@ -328,6 +330,120 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkRopeArgs a) {
     }
 }
 
+// e4m3 variant for the attention of the fp8 blocks: the same norm and rotation of q and k, then
+// codes instead of the rotated values -- q per (token, head) with s = max|y| / 448 (1 for a zero
+// row), k per head with the static scale max|w_k| * sqrt(128) / 448 (a normed, rotated element never
+// exceeds sqrt(128) times the largest weight), v per head with s = max|v| / 448 from the maxima the
+// QKV epilogue raised; codes e4m3(y / s), correctly rounded fp32 division, nearest-even conversion.
+constexpr float kKBound = 0x1.9dc22cp-6f;   // sqrt(128) / 448 rounded to fp32
+
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int m = G / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+
+template <int DT, int WT>
+__global__ __launch_bounds__(256) void qk_norm_rope_fp8_kernel(QkRopeArgs a) {
+    __shared__ float s_cos[64], s_sin[64], s_kw[4];
+    const int n = blockIdx.x;
+    const int tid = threadIdx.x;
+    constexpr int ES = ESize<DT>::v, WS = ESize<WT>::v;
+    if (tid < 64) {
+        const int ax = a.tab.axis[tid];
+        const double phi = (double)a.pos[(size_t)n * a.n_axes + ax] * a.tab.omega_d[tid];
+        const double two_pi = 6.283185307179586476925286766559;
+        const float red = (float)(phi - two_pi * rint(phi / two_pi));
+        s_cos[tid] = cosf(red);
+        s_sin[tid] = sinf(red);
+    }
+    {
+        // the largest |k weight| of both sets: thread tid reads dim tid % 128 of set tid / 128
+        const char* wk = reinterpret_cast<const char*>(tid < 128 ? a.qk_w0 : a.qk_w1);
+        float wv = 0.0f;
+        if (wk) {
+            float w8[8];
+            load8<WT>(wk + (size_t)(128 + (tid & 127 & ~7)) * WS, w8);
+            wv = fabsf(w8[tid & 7]);
+        }
+        wv = group_max<64>(wv);
+        if ((tid & 63) == 0) s_kw[tid >> 6] = wv;
+    }
+    __syncthreads();
+    const float s_k = fmaxf(fmaxf(s_kw[0], s_kw[1]), fmaxf(s_kw[2], s_kw[3])) * kKBound;
+    auto v_scale = [&](int h) {
+        const float m = __uint_as_float(a.vmax[h]);
+        return m > 0.0f ? m / 448.0f : 1.0f;
+    };
+    const int H = a.n_heads;
+    if (n == 0 && tid < H) {
+        a.sk[tid] = s_k;
+        a.sv[tid] = v_scale(tid);
+    }
+    const int set = n < a.n_first ? 0 : 1;
+    const int g = tid >> 4;           // 16 groups of 16 lanes
+    const int t = tid & 15;           // dims 8t .. 8t+7 of the head
+    for (int vec = g; vec < 3 * H; vec += 16) {
+        const int which = vec / H;    // 0 q, 1 k, 2 v
+        const int h = vec - which * H;
+        const char* src = which == 0 ? reinterpret_cast<const char*>(a.q) + (size_t)n * a.ld_q * ES
+                        : which == 1 ? reinterpret_cast<const char*>(a.k) + (size_t)n * a.ld_k * ES
+                                     : reinterpret_cast<const char*>(a.v) + (size_t)n * a.ld_v * ES;
+        float y[8];
+        load8<DT>(src + (size_t)(h * 128 + t * 8) * ES, y);
+        float sc;
+        if (which < 2) {
+            float w[8];
+            load8<WT>(reinterpret_cast<const char*>(set ? a.qk_w1 : a.qk_w0) + (size_t)(which * 128 + t * 8) * WS, w);
+            float ss = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fmaf(y[i], y[i], ss);
+            ss = group_sum<16>(ss);
+            const float rstd = 1.0f / sqrtf(ss * (1.0f / 128.0f) + a.eps);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] = y[i] * rstd * w[i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float c = s_cos[4 * t + i], s = s_sin[4 * t + i];
+                const float u0 = y[2 * i], u1 = y[2 * i + 1];
+                y[2 * i] = u0 * c - u1 * s;
+                y[2 * i + 1] = u0 * s + u1 * c;
+            }
+            if (which == 0) {
+                float m = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[i]));
+                m = group_max<16>(m);
+                sc = m > 0.0f ? m / 448.0f : 1.0f;
+                if (t == 0) a.sq[(size_t)n * H + h] = sc;
+            } else {
+                sc = s_k;
+            }
+        } else {
+            sc = v_scale(h);
+        }
+        float z[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z[i] = y[i] / sc;
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(z[4], z[5], 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(z[6], z[7], w1, true);
+        uint8_t* dst = a.qkv8 + (size_t)n * a.ld8 + (size_t)which * H * 128 + h * 128 + t * 8;
+        *reinterpret_cast<u32x2_v*>(dst) = u32x2_v{(uint32_t)w0, (uint32_t)w1};
+    }
+}
+
+template <int DT>
+static hipError_t launch_rope_fp8_w(const QkRopeArgs& a, hipStream_t s) {
+    const dim3 grid(a.n_tok), block(256);
+    if (a.w_dtype == F16) hipLaunchKernelGGL((qk_norm_rope_fp8_kernel<DT, F16>), grid, block, 0, s, a);
+    else if (a.w_dtype == BF16) hipLaunchKernelGGL((qk_norm_rope_fp8_kernel<DT, BF16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((qk_norm_rope_fp8_kernel<DT, F32>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
 template <int DT>
 static hipError_t launch_rope_w(const QkRopeArgs& a, hipStream_t s) {
     const dim3 grid(a.n_tok), block(256);
@@ -338,6 +454,12 @@ static hipError_t launch_rope_w(const QkRopeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_qk_rmsnorm_rope(const QkRopeArgs& a, hipStream_t s) {
+    if (a.qkv8) {
+        if (a.n_heads > 256) return hipErrorInvalidValue;
+        if (a.dtype == F16) return launch_rope_fp8_w<F16>(a, s);
+        if (a.dtype == BF16) return launch_rope_fp8_w<BF16>(a, s);
+        return hipErrorInvalidValue;
+    }
     if (a.dtype == F16) return launch_rope_w<F16>(a, s);
     if (a.dtype == BF16) return launch_rope_w<BF16>(a, s);
     return launch_rope_w<F32>(a, s);

@@ -48,6 +48,7 @@ struct ModBatch {
     int out_dtype;      // F32, BF16, F16, or FP8_ROWS: e4m3 codes (bytes, row stride ld_out) quantised per
                         // row as launch_quantize_fp8 does, from the fp32 results
     unsigned* range_flag;   // or null: kRangeF16 when an F16 output is out of range
+    unsigned* clear; int clear_n;   // or null: words the kernel sets to 0 (a later kernel's maxima)
 };
 hipError_t launch_modulate(const ModBatch& b, hipStream_t s);
 
@@ -59,6 +60,15 @@ struct RopeTable {
 struct QkRopeArgs {
     void* q; long ld_q;
     void* k; long ld_k;
+    // e4m3 output (qkv8 non-null): q, k stay as they are; the kernel writes codes into qkv8 rows
+    // (stride ld8 bytes; q in columns 0 .. d-1, k in d .. 2d-1, v in 2d .. 3d-1, d = n_heads * 128):
+    // q per token and head (scales sq [n_tok, n_heads]), k per head with the static scale of the
+    // k-norm weights (sk [n_heads]), v (read from v) per head from the maxima vmax (sv [n_heads]);
+    // sk and sv are written by workgroup 0.  n_heads <= 256.
+    uint8_t* qkv8; long ld8;
+    float* sq; float* sk; float* sv;
+    const void* v; long ld_v;
+    const unsigned* vmax;
     int n_tok, n_heads;
     const void* qk_w0;      // [2 (q, k)][128] for rows n < n_first
     const void* qk_w1;      // [2 (q, k)][128] for rows n >= n_first
@@ -148,6 +158,9 @@ hipError_t launch_attention_fp8(const AttnFp8Args& a, hipStream_t s);
 
 // ---- calibration: a loop of fp16 MFMAs, 4 waves x 4 chains x iters per workgroup ----------
 hipError_t launch_mfma_loop(int workgroups, int iters, float* out, hipStream_t s);
+// ---- calibration: streaming read (mode 0, one float per thread into sink) or copy (mode 1) ----
+hipError_t launch_stream_probe(const void* src, void* dst, size_t bytes, int mode, int workgroups, float* sink,
+                               hipStream_t s);
 
 // ---- windowed (neighborhood) attention over a [T, H, W] token grid --------------------------
 struct WinAttnArgs {
@@ -189,6 +202,10 @@ struct Fp8GemmBatch {
     int n;              // every problem has p[0].epi
     int total_tiles;    // filled by the launcher
     unsigned* range_flag;   // or null: kRangeF16 when an F16 output is out of range
+    // EPI_STORE only, or null: for output columns from vmax_col0 on (a multiple of 128), the largest
+    // |stored value| of each 128-column head, as fp32 bits, raised by atomic max (every problem of
+    // the batch into the same words; the caller zeroes them first)
+    unsigned* vmax; int vmax_col0;
 };
 hipError_t launch_gemm_fp8(Fp8GemmBatch& g, hipStream_t s);
 

@@ -18,7 +18,7 @@ touches the GPU it runs its own step twice more as child processes under
 ``rocprofv3 --pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``, each after three plain
 device copies of a known size that scale the counters to bytes (``--no-traffic``
 skips this).  ``calibration`` holds the launch floor, a measured MFMA-loop peak
-and copy bandwidth, and ``cold_hbm`` the AdaLN GEMV, modulation and QK-norm +
+and streaming read / copy bandwidth, and ``cold_hbm`` the AdaLN GEMV, modulation and QK-norm +
 RoPE kernels on buffers rotated over more than 512 MB (every launch reads HBM).
 ``cpu_baseline`` times the fp64 oracle on one block of the same workload on the
 host cores.
@@ -287,8 +287,16 @@ def calibration(dit, torch, dev):
     b = torch.empty_like(a)
     ev_ms(lambda: b.copy_(a), 2)
     best = min(ev_ms(lambda: b.copy_(a), 10) / 10 for _ in range(3))
-    out["copy_gbs"] = round(2.0 * n * 4 / (best * 1e-3) / 1e9, 1)
+    out["copy_gbs"] = round(2.0 * n * 4 / (best * 1e-3) / 1e9, 1)      # the runtime's device copy
     out["copy_bytes"] = 2 * n * 4
+    # the library's own streaming probe (16-byte nontemporal accesses, 8 workgroups per CU)
+    sink = torch.empty(8 * cus * 256, dtype=torch.float32, device=dev)
+    for mode, key, moved in ((0, "stream_read_gbs", n * 4), (1, "stream_copy_gbs", 2 * n * 4)):
+        fn = (lambda: dit.stream_probe(0, a, sink=sink, workgroups=8 * cus)) if mode == 0 else \
+             (lambda: dit.stream_probe(1, a, dst=b, workgroups=8 * cus))
+        ev_ms(fn, 2)
+        best = min(ev_ms(fn, 10) / 10 for _ in range(3))
+        out[key] = round(moved / (best * 1e-3) / 1e9, 1)
     return out
 
 
@@ -680,7 +688,9 @@ def fp8_block_bench(args, cfg, dit, torch):
             "gemm_fp8_linear1_qkv": 6.0 * n * d * d, "gemm_fp8_linear1_gu": 4.0 * n * d * F,
             "gemm_fp8_linear2": 2.0 * n * (d + F) * d}
     quant = {"quantize_o": n * d * 3.0, "quantize_f": n * F * 3.0, "quantize_of": n * (d + F) * 3.0,
-             "modulate_h_fp8": n * d * 5.0}              # 16-bit / fp32 read + code written
+             "modulate_h_fp8": n * d * 5.0,              # 16-bit / fp32 read + code written
+             "qk_rmsnorm_rope_fp8": n * 3 * d * 3.0}     # q, k, v read (16-bit), their codes written
+    gemm["joint_attention_fp8"] = 4.0 * n * n * d
     kernels = {}
     for name, (cnt, tot) in kt.items():
         avg = tot / cnt

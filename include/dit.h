@@ -473,25 +473,43 @@ int dit_joint_attention_fp8(void* stream,
 int dit_mfma_loop(void* stream, int workgroups, int iters, float* out);
 
 /*
+ * Calibration for measurements (not part of the block): a grid-stride stream
+ * over `bytes` (a positive multiple of 16384) of src with 16-byte nontemporal
+ * accesses, `workgroups` workgroups of 256 threads.  mode 0 reads src and
+ * writes one float per thread to sink [workgroups * 256] (the HBM read
+ * ceiling); mode 1 copies src to dst (read + write ceiling), dst not
+ * overlapping src.  src, dst 16-byte aligned.
+ */
+int dit_stream_probe(void* stream, int mode, const void* src, void* dst, size_t bytes, int workgroups,
+                     float* sink);
+
+/*
  * fp8 double-stream block: dit_block_forward with its four weight products
  * (QKV, out-projection, FFN-in, FFN-down) on e4m3 codes.  Before each product
  * the block quantises the product's activations per row by dit_quantize_fp8's
  * rule (a and b from their fp32 values, inside the modulation kernel; O and f
  * from their act_dtype values); the
  * weights come quantised per output row (w[j, :] = s[j] * dec(codes[j, :]), as
- * dit_quantize_fp8 writes them from the 16-bit weights).  The AdaLN GEMV, the
- * norms, RoPE, attention and the epilogues (gated residual, SwiGLU) are those
- * of the 16-bit block, so the only extra error is the e4m3 rounding of both
- * operands of each product (up to 2^-4 relative per element).
+ * dit_quantize_fp8 writes them from the 16-bit weights).  The attention runs
+ * as dit_joint_attention_fp8 on e4m3 q, k, v written by the QK-norm + RoPE
+ * kernel: q per token and head by dit_quantize_fp8's rule, k per head with the
+ * static scale max|w_k| * sqrt(128) / 448 (max over both streams' k-norm
+ * weights: a normed, rotated element never exceeds sqrt(128) * max|w_k|), v
+ * per head with s = max|v| / 448 over all tokens (the QKV epilogue raises the
+ * maxima).  The AdaLN GEMV, the norms, RoPE and the epilogues (gated residual,
+ * SwiGLU) are those of the 16-bit block, so the extra error is the e4m3
+ * rounding of both operands of each product (up to 2^-4 relative per element)
+ * and of the attention's probabilities.
  *  cfg       dtype DIT_BF16; act_dtype DIT_F16 or DIT_BF16
  *  txt, img  (host) fp8 weights of each stream (below); every pointer 16-byte
  *            aligned
  *  workspace >= dit_block_fp8_workspace_size(cfg) bytes (the 16-bit block's
- *            plus n * max(d, F) code bytes and n fp32 scales)
+ *            plus n * 3d attention code bytes, (n + 3) * n_heads fp32 words,
+ *            n * max(d, F) product code bytes and n fp32 scales)
  * Other arguments, aliasing rules and errors as for dit_block_forward.
- * Launches (11): GEMV, modulate x (to e4m3), QKV, QK-norm + RoPE, attention,
- * quantise O, out-projection, modulate h (to e4m3), FFN-in, quantise f,
- * FFN-down.
+ * Launches (11): GEMV, modulate x (to e4m3), QKV, QK-norm + RoPE (to e4m3),
+ * attention (e4m3), quantise O, out-projection, modulate h (to e4m3), FFN-in,
+ * quantise f, FFN-down.
  */
 typedef struct dit_stream_weights_fp8 {
     const void* w_mod;          /* [6d, d_cond] of dtype (shift1, scale1, gate1, shift2, scale2, gate2) */
@@ -524,9 +542,10 @@ size_t dit_single_block_fp8_workspace_size(const dit_block_config* cfg);
  * fp8 single-stream block: dit_single_block_forward with its two weight products on e4m3 codes:
  * a is quantised per row inside the modulation kernel, [O | f] per row (width d + F) by a
  * separate pass; W_1 and W_2 come quantised per output row.  Arguments, aliasing and errors as for
- * dit_single_block_forward; cfg as for dit_block_forward_fp8.  Launches (8): GEMV, modulate x (to
- * e4m3), linear1 q|k|v, linear1 gate|up (SwiGLU), QK-norm + RoPE, attention, quantise [O | f],
- * linear2.
+ * dit_single_block_forward; cfg as for dit_block_forward_fp8; the attention on e4m3 q, k, v as in
+ * dit_block_forward_fp8 (k scale from the block's one k-norm weight).  Launches (8): GEMV,
+ * modulate x (to e4m3), linear1 q|k|v, linear1 gate|up (SwiGLU), QK-norm + RoPE (to e4m3),
+ * attention (e4m3), quantise [O | f], linear2.
  */
 int dit_single_block_forward_fp8(const dit_block_config* cfg, const dit_single_weights_fp8* w,
                                  const void* cond, const int32_t* pos, const void* x, void* y,

@@ -238,3 +238,76 @@ def test_fp8_block_c2_last_product_elementwise(dit):
             f"{metric(host(y)[r], ref):.2e}")
         assert np.all(err <= bound), f"y_{s}: {np.sum(err > bound)} elements beyond the bound"
     assert worst > 0.0
+
+
+@pytest.mark.parametrize("cfg", [di.BlockConfig("ragged_fp8attn", "bf16", d=384, n_heads=3, ffn_inner=1152, n_txt=7,
+                                                grid_h=5, grid_w=9), di.CONFIGS[1]], ids=["ragged", "c1"])
+def test_fp8_block_attention_operands_and_output(dit, cfg):
+    """The fp8 block's attention, teacher-forced on the GPU's own values read back from the
+    workspace: from its fp16 q, k, v (QKV product output), the oracle's QK-norm + RoPE (exact) and
+    fp8_attention_operands give the codes and scales the e4m3 mode of the QK-norm + RoPE kernel must
+    write -- k and v scales bit-identical (the same fp32 operations on the same values), v codes
+    bit-identical, q and k codes equal or one e4m3 step apart (the GPU rotates in fp32; the oracle
+    exactly), q scales within 1e-5.  The attention output O is then held to the fp8 attention bound
+    (tests/test_gpu_attention_fp8.py) against the oracle's fp8 attention on the GPU's own codes.
+    Workspace layout from the end: ... | attention codes [n, 3d] | scales sq [n, H], sk [H],
+    sv [H], |v| maxima [H] | product codes [n, max(d, F)] | product scales [n]."""
+    import test_gpu_attention_fp8 as ta
+    say(f"fp8 double block {cfg.name}: attention operands and output, teacher-forced")
+    inp = di.double_block_inputs(cfg, seed=4, qk_norm="random")
+    n, d, F, H, D = cfg.n_tok, cfg.d, cfg.ffn_inner, cfg.n_heads, 128
+    sh = shape_of(cfg, dit)
+    total = dit.block_fp8_workspace_size(sh)
+    ws = torch.empty(total, dtype=torch.uint8, device="cuda")
+    yt = torch.empty(cfg.n_txt, d, dtype=torch.float32, device="cuda")
+    yi = torch.empty(cfg.n_img, d, dtype=torch.float32, device="cuda")
+    wt, wi = fp8_weights(dit, inp["txt"]), fp8_weights(dit, inp["img"])
+    dit.block_forward_fp8(sh, wt, wi, dev(inp["cond"], "bf16"), dev(inp["pos"], "i32"), dev(inp["x_txt"], "bf16"),
+                          dev(inp["x_img"], "bf16"), yt, yi, ws)
+    torch.cuda.synchronize()
+
+    def up(x):
+        return (x + 255) // 256 * 256
+    wsh = ws.cpu().numpy()
+    off_qkv = 256 + up(12 * d * 4) + up(n * d * 2)
+    off_o = off_qkv + up(n * 3 * d * 2)
+    off_sq = total - up(n * 4)
+    off_q8 = off_sq - up(n * max(d, F))
+    off_a8s = off_q8 - up((n * H + 3 * H) * 4)
+    off_a8 = off_a8s - up(n * 3 * d)
+    qkv = wsh[off_qkv:off_qkv + n * 3 * d * 2].view(np.float16).reshape(n, 3 * d).astype(np.float64)
+    o_gpu = wsh[off_o:off_o + n * d * 2].view(np.float16).reshape(n, d).astype(np.float64)
+    a8 = wsh[off_a8:off_a8 + n * 3 * d].reshape(n, 3 * d)
+    sc = wsh[off_a8s:off_a8s + (n * H + 3 * H) * 4].view(np.float32)
+    sq, sk, sv = sc[:n * H].reshape(n, H), sc[n * H:n * H + H], sc[n * H + H:n * H + 2 * H]
+    # the oracle's rotation of the GPU's q, k and its operands (k bound from both streams' k weights)
+    qk_w = np.stack([o.widen(inp["txt"]["qk_norm_w"], "bf16").reshape(2, D),
+                     o.widen(inp["img"]["qk_norm_w"], "bf16").reshape(2, D)])
+    q, k = o.qk_rmsnorm_rope(qkv[:, :d], qkv[:, d:2 * d], H, D, qk_w, cfg.n_txt, cfg.eps_qk, inp["pos"],
+                             cfg.axes_dim, cfg.theta)
+    v = qkv[:, 2 * d:]
+    q8r, sqr, k8r, skr, v8r, svr = o.fp8_attention_operands(q, k, v, H, D, float(np.max(np.abs(qk_w[:, 1]))))
+    np.testing.assert_array_equal(sk, skr)
+    np.testing.assert_array_equal(sv, svr)
+    np.testing.assert_array_equal(a8[:, 2 * d:], v8r)
+    np.testing.assert_allclose(sq, sqr, rtol=1e-5)
+
+    def step_apart(got, ref):
+        # e4m3 codes of one sign are ordered like their values: equal, or neighbours
+        g, r = got.astype(np.int32), ref.astype(np.int32)
+        same_sign = (g & 0x80) == (r & 0x80)
+        near = same_sign & (np.abs((g & 0x7F) - (r & 0x7F)) <= 1)
+        zero = ((g & 0x7F) <= 1) & ((r & 0x7F) <= 1)          # -0 / +0 / smallest subnormals
+        return near | zero, float(np.mean(g == r))
+    for name, got, ref in (("q", a8[:, :d], q8r), ("k", a8[:, d:2 * d], k8r)):
+        ok, agree = step_apart(got, ref)
+        say(f"  {name} codes: {agree:.4%} identical")
+        assert np.all(ok), f"{name}: {np.sum(~ok)} codes more than one step from the oracle's"
+        assert agree > 0.99
+    # O against the oracle's fp8 attention on the GPU's own codes
+    x = {"q8": a8[:, :d], "sq": sq, "k8": a8[:, d:2 * d], "sk": sk, "v8": a8[:, 2 * d:], "sv": sv}
+    rows = np.arange(n) if n <= 256 else np.unique(np.concatenate(
+        [[0, cfg.n_txt - 1, cfg.n_txt, n - 1], np.random.default_rng(3).choice(n, 60, replace=False)]))
+    full = np.zeros((n, d))
+    full[rows] = o_gpu[rows]
+    ta._check(full, x, H, rows, "f16")
