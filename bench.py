@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--fp8-block", action="store_true",
                    help="time the fp8 double-stream block (its four weight products on e4m3 codes) at the "
                         "workload's size (one JSON line of its own)")
+    p.add_argument("--fp8-attention", action="store_true",
+                   help="time dit_joint_attention_fp8 (e4m3 q, k, v) at the workload's joint sequence and heads, "
+                        "next to the fp16 kernel on the same shape")
     p.add_argument("--conv", action="store_true",
                    help="time the causal 3-D convolution on the video decoder's stage shapes at 832 x 480 "
                         "(one JSON line of its own)")
@@ -377,7 +380,8 @@ def main():
     prov = provenance() if not args.traffic_child else None
     counters, counters_cmd = None, None
     single_block = cfg.n_double == 1 and cfg.n_single == 0
-    if not (args.traffic_child or args.no_traffic or args.fp8_gemm or args.conv or args.fp8_block) and single_block:
+    if not (args.traffic_child or args.no_traffic or args.fp8_gemm or args.conv or args.fp8_block or
+            args.fp8_attention) and single_block:
         counters, counters_cmd = counter_passes(args)
         if counters is None:
             print(f"traffic: not measured ({counters_cmd})", file=sys.stderr, flush=True)
@@ -388,6 +392,8 @@ def main():
         return conv_bench(args, dit, torch)
     if args.fp8_block:
         return fp8_block_bench(args, cfg, dit, torch)
+    if args.fp8_attention:
+        return fp8_attention_bench(args, cfg, dit, torch)
     t = cfg.dtype
     if args.copy_calibration:
         n = args.copy_calibration // 4
@@ -713,6 +719,51 @@ def fp8_block_bench(args, cfg, dit, torch):
                       "products": "e4m3 weights (per-row scales, quantised once) x e4m3 activations (per row, "
                                   "every step)"},
            "kernels": kernels}
+    print(json.dumps(out), flush=True)
+
+
+def fp8_attention_bench(args, cfg, dit, torch):
+    """dit_joint_attention_fp8 over the workload's joint sequence (n_txt + n_img tokens, its heads)
+    on seeded e4m3 codes and scales (dit_inputs.fp8_attention_inputs), and dit_joint_attention on
+    fp16 q, k, v of the same shape; both one workgroup per (head, 256 queries), timed with HIP
+    events around K launches after W warm-up launches.  Flop: 4 N^2 d (QK^T and PV)."""
+    import dit_inputs as di
+    n, H = cfg.n_tok, cfg.n_heads
+    x = di.fp8_attention_inputs(n, H, seed=args.seed)
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
+    o8 = torch.empty(n, H * 128, dtype=torch.float16, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(args.seed)
+    q16, k16, v16 = (torch.randn(n, H * 128, device="cuda", generator=g).half() for _ in range(3))
+    o16 = torch.empty_like(q16)
+    s = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(args.steps):
+            fn()
+        b.record(s)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+    ms8 = timed(lambda: dit.joint_attention_fp8(t["q8"], t["sq"], t["k8"], t["sk"], t["v8"], t["sv"], o8, H))
+    ms16 = timed(lambda: dit.joint_attention(q16, k16, v16, o16, H))
+    flops = 4.0 * n * n * H * 128
+    tf8, tf16 = flops / (ms8 * 1e-3) / 1e12, flops / (ms16 * 1e-3) / 1e12
+    out = {"metric": "fp8 joint attention ms & TFLOP/s (e4m3 q, k, v; scores and PV on fp8 MFMA)",
+           "value": round(tf8, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms8, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp8_e4m3", "data": "synthetic",
+           "config": {"workload": cfg.name, "tokens": n, "heads": H, "head_dim": 128,
+                      "inputs": "e4m3 codes drawn directly (dit_inputs.fp8_attention_inputs), per token-and-head q "
+                                "scales, per-head k and v scales"},
+           "roofline": {"bound": "mfma", "achieved": round(tf8, 1), "peak": 5000.0, "unit": "TFLOP/s",
+                        "frac": round(tf8 / 5000.0, 4), "frac_of_bf16_peak": round(tf8 / PEAK_BF16_TFLOPS, 4)},
+           "fp16_same_shape": {"ms": round(ms16, 4), "tflops": round(tf16, 1),
+                               "frac_bf16_peak": round(tf16 / PEAK_BF16_TFLOPS, 4)},
+           "speedup_over_fp16": round(ms16 / ms8, 3)}
     print(json.dumps(out), flush=True)
 
 
