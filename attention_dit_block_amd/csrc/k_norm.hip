@@ -26,6 +26,35 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
     constexpr int kElems = 16 / kES;                       // elements per 16-byte slice
     constexpr int kQ = kElems / 4;                         // float4s of SiLU(c) per slice
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int total = b.p[0].rows + (b.n > 1 ? b.p[1].rows : 0);
+    const int row0 = (blockIdx.x * kGemvWaves + wave) * kGemvRowsPerWave;
+    const char* wrow[kGemvRowsPerWave];
+    float acc[kGemvRowsPerWave];
+    bool ok[kGemvRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kGemvRowsPerWave; ++r) {
+        const int g = row0 + r;
+        ok[r] = g < total;
+        int pi = (g >= b.p[0].rows) ? 1 : 0;
+        int lr = g - (pi ? b.p[0].rows : 0);
+        if (!ok[r]) { pi = 0; lr = 0; }
+        wrow[r] = reinterpret_cast<const char*>(b.p[pi].w) + (size_t)lr * b.d_cond * kES;
+        acc[r] = 0.0f;
+    }
+    // slices of 64 lanes x kElems elements; the next slice's weights load while this one is summed
+    // (nontemporal: every weight is read once)
+    const int iters = (b.d_cond + 64 * kElems - 1) / (64 * kElems);
+    u32x4_v w[kGemvRowsPerWave], wn[kGemvRowsPerWave];
+    auto load = [&](u32x4_v* dst, int it) {
+        const int k0 = (it * 64 + lane) * kElems;
+#pragma unroll
+        for (int r = 0; r < kGemvRowsPerWave; ++r)
+            dst[r] = k0 < b.d_cond ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_v*>(wrow[r] + (size_t)k0 * kES))
+                                  : u32x4_v{0u, 0u, 0u, 0u};
+    };
+    load(w, 0);       // the first slice's HBM latency overlaps the SiLU(c) staging below
     // SiLU(c) in LDS, interleaved so that the float4s a lane needs for one slice sit 16 bytes
     // apart across lanes (bank-conflict-free reads): element e = (it * 64 + l) * kElems + 4 q + j
     // goes to ((it * kQ + q) * 64 + l) * 4 + j.  Staged 4 elements per thread per step, all of a
@@ -61,33 +90,6 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
     }
     __syncthreads();
 
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int total = b.p[0].rows + (b.n > 1 ? b.p[1].rows : 0);
-    const int row0 = (blockIdx.x * kGemvWaves + wave) * kGemvRowsPerWave;
-    const char* wrow[kGemvRowsPerWave];
-    float acc[kGemvRowsPerWave];
-    bool ok[kGemvRowsPerWave];
-#pragma unroll
-    for (int r = 0; r < kGemvRowsPerWave; ++r) {
-        const int g = row0 + r;
-        ok[r] = g < total;
-        int pi = (g >= b.p[0].rows) ? 1 : 0;
-        int lr = g - (pi ? b.p[0].rows : 0);
-        if (!ok[r]) { pi = 0; lr = 0; }
-        wrow[r] = reinterpret_cast<const char*>(b.p[pi].w) + (size_t)lr * b.d_cond * kES;
-        acc[r] = 0.0f;
-    }
-    // slices of 64 lanes x kElems elements; the next slice's weights load while this one is summed
-    const int iters = (b.d_cond + 64 * kElems - 1) / (64 * kElems);
-    u32x4_v w[kGemvRowsPerWave], wn[kGemvRowsPerWave];
-    auto load = [&](u32x4_v* dst, int it) {
-        const int k0 = (it * 64 + lane) * kElems;
-#pragma unroll
-        for (int r = 0; r < kGemvRowsPerWave; ++r)
-            dst[r] = k0 < b.d_cond ? ld16(wrow[r] + (size_t)k0 * kES) : u32x4_v{0u, 0u, 0u, 0u};
-    };
-    load(w, 0);
     for (int it = 0; it < iters; ++it) {
         if (it + 1 < iters) load(wn, it + 1);
         const int k0 = (it * 64 + lane) * kElems;
