@@ -238,8 +238,12 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmBatch bt) {
                     if constexpr (MODE == EPI_STORE) {
                         if (bt.vmax) {
 #pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                vm = fmaxf(vm, fabsf(g.c_dtype == F16 ? (float)(_Float16)o[j] : o[j]));
+                            for (int j = 0; j < 4; ++j) {
+                                // the value as stored (the QK-norm + RoPE pass quantises that)
+                                const float st = g.c_dtype == F16 ? (float)(_Float16)o[j]
+                                               : g.c_dtype == BF16 ? bf_lo(pack_bf16x2(o[j], 0.0f)) : o[j];
+                                vm = fmaxf(vm, fabsf(st));
+                            }
                         }
                     }
                     store4_any(g.c, (size_t)m * g.ldc + col, g.c_dtype, o);

@@ -139,6 +139,16 @@ def test_fp8_attention_full_size_sampled_rows(dit):
     _check(got, x, H, rows, "bf16")
 
 
+def test_fp8_attention_16896_tokens_sampled_rows(dit):
+    # 512 text + 16384 image tokens (the largest single-GPU block workload), sampled query rows
+    n, H = 16896, 24
+    say(f"fp8 attention n={n} H={H}: sampled rows")
+    x = di.fp8_attention_inputs(n, H, seed=31)
+    got = _run(dit, x, n, H, "f16")
+    rows = np.unique(np.concatenate([[0, 511, 512, n - 1], np.random.default_rng(1).integers(0, n, 28)]))
+    _check(got, x, H, rows, "f16")
+
+
 def test_fp8_attention_rejects_bad_arguments(dit):
     n, H = 64, 1
     x = _to_gpu(di.fp8_attention_inputs(n, H, seed=1))

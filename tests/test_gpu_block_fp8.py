@@ -240,9 +240,12 @@ def test_fp8_block_c2_last_product_elementwise(dit):
     assert worst > 0.0
 
 
-@pytest.mark.parametrize("cfg", [di.BlockConfig("ragged_fp8attn", "bf16", d=384, n_heads=3, ffn_inner=1152, n_txt=7,
-                                                grid_h=5, grid_w=9), di.CONFIGS[1]], ids=["ragged", "c1"])
-def test_fp8_block_attention_operands_and_output(dit, cfg):
+_RAGGED_FP8ATTN = di.BlockConfig("ragged_fp8attn", "bf16", d=384, n_heads=3, ffn_inner=1152, n_txt=7, grid_h=5, grid_w=9)
+
+
+@pytest.mark.parametrize("cfg, act", [(_RAGGED_FP8ATTN, "f16"), (_RAGGED_FP8ATTN, "bf16"), (di.CONFIGS[1], "f16")],
+                         ids=["ragged", "ragged_bf16_act", "c1"])
+def test_fp8_block_attention_operands_and_output(dit, cfg, act):
     """The fp8 block's attention, teacher-forced on the GPU's own values read back from the
     workspace: from its fp16 q, k, v (QKV product output), the oracle's QK-norm + RoPE (exact) and
     fp8_attention_operands give the codes and scales the e4m3 mode of the QK-norm + RoPE kernel must
@@ -256,7 +259,7 @@ def test_fp8_block_attention_operands_and_output(dit, cfg):
     say(f"fp8 double block {cfg.name}: attention operands and output, teacher-forced")
     inp = di.double_block_inputs(cfg, seed=4, qk_norm="random")
     n, d, F, H, D = cfg.n_tok, cfg.d, cfg.ffn_inner, cfg.n_heads, 128
-    sh = shape_of(cfg, dit)
+    sh = shape_of(cfg, dit, act_dtype=dit.DIT_BF16 if act == "bf16" else None)
     total = dit.block_fp8_workspace_size(sh)
     ws = torch.empty(total, dtype=torch.uint8, device="cuda")
     yt = torch.empty(cfg.n_txt, d, dtype=torch.float32, device="cuda")
@@ -275,8 +278,12 @@ def test_fp8_block_attention_operands_and_output(dit, cfg):
     off_q8 = off_sq - up(n * max(d, F))
     off_a8s = off_q8 - up((n * H + 3 * H) * 4)
     off_a8 = off_a8s - up(n * 3 * d)
-    qkv = wsh[off_qkv:off_qkv + n * 3 * d * 2].view(np.float16).reshape(n, 3 * d).astype(np.float64)
-    o_gpu = wsh[off_o:off_o + n * d * 2].view(np.float16).reshape(n, d).astype(np.float64)
+    def act16(buf, shape):
+        if act == "bf16":
+            return di.f32_from_bf16_bits(buf.view(np.uint16)).reshape(shape).astype(np.float64)
+        return buf.view(np.float16).reshape(shape).astype(np.float64)
+    qkv = act16(wsh[off_qkv:off_qkv + n * 3 * d * 2], (n, 3 * d))
+    o_gpu = act16(wsh[off_o:off_o + n * d * 2], (n, d))
     a8 = wsh[off_a8:off_a8 + n * 3 * d].reshape(n, 3 * d)
     sc = wsh[off_a8s:off_a8s + (n * H + 3 * H) * 4].view(np.float32)
     sq, sk, sv = sc[:n * H].reshape(n, H), sc[n * H:n * H + H], sc[n * H + H:n * H + 2 * H]
@@ -310,4 +317,4 @@ def test_fp8_block_attention_operands_and_output(dit, cfg):
         [[0, cfg.n_txt - 1, cfg.n_txt, n - 1], np.random.default_rng(3).choice(n, 60, replace=False)]))
     full = np.zeros((n, d))
     full[rows] = o_gpu[rows]
-    ta._check(full, x, H, rows, "f16")
+    ta._check(full, x, H, rows, act)
