@@ -522,6 +522,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     if (fp8) {
         AttnFp8Args af{a8, 3L * d, a8_sq, a8 + d, 3L * d, a8_sk, a8 + 2 * (size_t)d, 3L * d, a8_sv, ob, d,
                        c.act_dtype, n, c.n_heads, 1.0f / std::sqrt((float)c.head_dim)};
+        af.sk_scratch = W.ask_bytes ? ws + W.ask : nullptr;
         DIT_TRY(launch("joint_attention_fp8", s, [&] { return launch_attention_fp8(af, s); }));
     } else {
         AttnArgs at{qkv, 3L * d, qkv + (size_t)d * es, 3L * d, qkv + (size_t)2 * d * es, 3L * d, ob, d, n, c.n_heads,
@@ -778,6 +779,7 @@ static int single_block_impl(const dit_block_config* cfg, const dit_single_weigh
     if (fp8) {
         AttnFp8Args af{a8, 3L * d, a8_sq, a8 + d, 3L * d, a8_sk, a8 + 2 * (size_t)d, 3L * d, a8_sv, of, ldof,
                        c.act_dtype, n, c.n_heads, 1.0f / std::sqrt((float)c.head_dim)};
+        af.sk_scratch = W.ask_bytes ? ws + W.ask : nullptr;
         DIT_TRY(launch("joint_attention_fp8", s, [&] { return launch_attention_fp8(af, s); }));
     } else {
         AttnArgs at{qkv, 3L * d, qkv + (size_t)d * es, 3L * d, qkv + (size_t)2 * d * es, 3L * d, of, ldof, n,

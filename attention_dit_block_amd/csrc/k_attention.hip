@@ -37,40 +37,11 @@
 //
 // fp32 kernel: LDS-tiled, 4 threads per query, fp32 FMA throughout.
 #include "attn_common.h"
+#include "attn_split.h"
 #include "dev_common.h"
 #include "launch.h"
 
 namespace dit {
-
-// waves (of 32 queries each) per workgroup: 8, one workgroup per CU, so each staged K/V tile
-// serves 256 queries (4-wave workgroups, two per CU, measured slower: 342 against 277 us at 4608
-// tokens, 4.33 against 3.36 ms at 16896)
-constexpr int kAttnWaves = 8;
-constexpr int AQ = 32 * kAttnWaves;     // queries per workgroup
-// How a workgroup finishes a (head, query tile) unit it ran key tiles [kb, ke) of:
-enum UnitKind {
-    UNIT_FULL = 0,      // all key tiles: normalise and store O
-    UNIT_OWNER = 1,     // key tiles from 0: merge the partials of the workgroups holding the rest, store
-    UNIT_PARTIAL = 2,   // later key tiles: publish (running max, running sum, unnormalised O)
-    UNIT_OWNER_CONT = 3 // an owner's continuation: key tiles of a piece whose partial did not arrive,
-                        // merged with the owner's state from its carry slot, then as UNIT_OWNER
-};
-
-// Stream-K scratch: [sk_grid] partial slots, [sk_grid] carry slots (an owner's state while it
-// computes a missing piece), then [sk_grid] 32-bit flags.  In a slot, lane l of wave w keeps float4
-// c (c < 16: its O accumulators; c = 16: running max, running sum) at index (w * 17 + c) * 64 + l.
-constexpr int kPartF4 = 17;
-constexpr int kSlotF4 = kAttnWaves * kPartF4 * 64;
-__device__ __forceinline__ float4* attn_partial(const AttnArgs& a, int g) {
-    return reinterpret_cast<float4*>(a.sk_scratch) + (size_t)g * kSlotF4;
-}
-__device__ __forceinline__ float4* attn_carry(const AttnArgs& a, int g) {
-    return reinterpret_cast<float4*>(a.sk_scratch) + (size_t)(a.sk_grid + g) * kSlotF4;
-}
-__device__ __forceinline__ unsigned* attn_flag(const AttnArgs& a, int g) {
-    return reinterpret_cast<unsigned*>(reinterpret_cast<float4*>(a.sk_scratch) +
-                                                 (size_t)2 * a.sk_grid * kSlotF4) + g;
-}
 
 // One (head, query tile) unit L = head * nq + query tile over key tiles [kb, ke).
 // NEG: softmax_scale < 0 (the row max of the scaled scores is then the min of the raw ones).
@@ -334,82 +305,8 @@ __device__ __forceinline__ int attention_unit(const AttnArgs& a, char* smem_k0, 
         step.template operator()<0, true>(j, sA, sB);
     }
 
-    // per-lane byte offset of float4 0 in a stream-K slot (computed where it is used, so it is not
-    // held in a register across the pipeline above)
-    auto slot_lane = [&]() { return (uint32_t)((wave * kPartF4 * 64 + lane) * 16); };
-    // merges the state in a stream-K slot (a piece's partial or the carry): m = max(m_a, m_b),
-    // O = O_a 2^(m_a - m) + O_b 2^(m_b - m), the same for the running sum
-    auto merge_slot = [&](const float4* slot) {
-        const __amdgpu_buffer_rsrc_t src = sk_slot(slot);
-        const uint32_t slot_off = slot_lane();
-        const float4 ml = sk_load(src, slot_off + 16 * 64 * 16, 0);
-        const float m_new = fmaxf(m_run, ml.x);
-        const float ca = __builtin_amdgcn_exp2f(m_run - m_new), cb = __builtin_amdgcn_exp2f(ml.x - m_new);
-        m_run = m_new;
-        l_run = fmaf(l_run, ca, ml.y * cb);
-        // 4 loads in flight at a time: O and the pipeline state fill most of the registers
-#pragma unroll
-        for (int eb = 0; eb < 4; ++eb) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 v = sk_load(src, slot_off + (4 * eb + i) * 64 * 16, 0);
-                o[eb][4 * i] = fmaf(o[eb][4 * i], ca, v.x * cb);
-                o[eb][4 * i + 1] = fmaf(o[eb][4 * i + 1], ca, v.y * cb);
-                o[eb][4 * i + 2] = fmaf(o[eb][4 * i + 2], ca, v.z * cb);
-                o[eb][4 * i + 3] = fmaf(o[eb][4 * i + 3], ca, v.w * cb);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    // stores the state (unnormalised O, running max, running sum) into a stream-K slot
-    auto store_slot = [&](float4* slot) {
-        const __amdgpu_buffer_rsrc_t dst = sk_slot(slot);
-        const uint32_t slot_off = slot_lane();
-#pragma unroll
-        for (int eb = 0; eb < 4; ++eb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sk_store(dst, slot_off + (4 * eb + i) * 64 * 16, 0, o[eb][4 * i], o[eb][4 * i + 1], o[eb][4 * i + 2],
-                         o[eb][4 * i + 3]);
-        sk_store(dst, slot_off + 16 * 64 * 16, 0, m_run, l_run, 0.0f, 0.0f);
-    };
-
-    // The owner of a split unit has run its own key tiles (or, continuing, a missing piece's); it
-    // merges the partial states of the workgroups holding the rest of the unit, up to stream-K step
-    // t_end, which published them first thing in their shares.  When a piece's partial does not
-    // arrive in time the owner claims the piece, parks its state in its carry slot and returns; the
-    // driver runs the piece's key tiles as its next item, which resumes here.
-    if (kind == UNIT_OWNER || kind == UNIT_OWNER_CONT) {
-        int miss = -1;
-        // jn = -1: the state parked in the carry slot (a continuation), then pieces from jn0
-        for (int jn = kind == UNIT_OWNER_CONT ? -1 : jn0; jn < Gs && (jn < 0 || sk_begin(S, jn, Gs) < t_end);
-             jn = jn < 0 ? jn0 : jn + 1) {
-            const float4* src = attn_carry(a, g);
-            if (jn >= 0) {
-                if (sk_begin(S, jn + 1, Gs) == sk_begin(S, jn, Gs)) continue;     // empty share
-                if (!sk_take(attn_flag(a, gb + jn), a.epoch, a.sk_spins)) {
-                    miss = jn;
-                    break;
-                }
-                src = attn_partial(a, gb + jn);
-            }
-            merge_slot(src);
-        }
-        if (miss >= 0) {
-            store_slot(attn_carry(a, g));
-            __builtin_amdgcn_s_waitcnt(0);
-            const long t_first = t_end - a.k_tiles;        // stream-K step of this unit's key tile 0
-            ckb = (int)(sk_begin(S, miss, Gs) - t_first);
-            cke = (int)(min(sk_begin(S, miss + 1, Gs), t_end) - t_first);
-            return miss + 1;
-        }
-    }
-
-    if (kind == UNIT_PARTIAL) {
-        store_slot(attn_partial(a, g));
-        sk_raise(attn_flag(a, g), a.epoch, a.sk_spins);
-        return -1;
-    }
+    const int fin = attn_split_finish(a, o, m_run, l_run, kind, g, gb, Gs, S, t_end, jn0, ckb, cke, wave, lane);
+    if (fin != kAttnStore) return fin;
 
     const float inv = 1.0f / half_swap_sum(l_run);
     if (qrow < N) {
@@ -427,60 +324,18 @@ __device__ __forceinline__ int attention_unit(const AttnArgs& a, char* smem_k0, 
     return -1;
 }
 
-// Persistent stream-K driver (sk_grid > 0) or one unit per workgroup.  Workgroup g (XCD-remapped,
-// so the Gs workgroups of a segment share an XCD and its L2) runs its segment's units gl, gl + Gs,
-// ... below dp (gl = its index in the segment), then its even share of the segment's remaining
-// key tiles in order: the end of a unit some earlier workgroup started (published as a partial),
-// whole units, and the start of a unit later workgroups finish (it owns that one and merges their
-// partials).  A unit's owner computes its piece last, after the workgroups holding the other
-// pieces computed theirs first.
+// The split driver (attn_split.h) runs the work items of workgroup blockIdx.x.
 template <int DT, bool NEG>
 __device__ __forceinline__ void attention_mfma_body(const AttnArgs& a) {
     __shared__ __attribute__((aligned(1024))) char smem_k0[kTile];
     __shared__ __attribute__((aligned(1024))) char smem_k1[kTile];
     __shared__ __attribute__((aligned(1024))) char smem_v0[kTile];
     __shared__ __attribute__((aligned(1024))) char smem_v1[kTile];
-    const int g = xcd_remap(blockIdx.x, gridDim.x);
-    const int G = a.sk_grid, I = a.k_tiles;
-    // the segment (XCD) of workgroup g: workgroups [gb, gb + Gs), units [u0, u0 + Us), of which the
-    // first dp run whole (full rounds but one) and the rest, S key tiles, are split evenly
-    const int Gs = G ? G / a.sk_segs : 0;
-    const int x = G ? g / Gs : 0, gb = x * Gs, gl = g - gb;
-    const int u0 = G ? (int)((long)a.units * x / a.sk_segs) : 0;
-    const int Us = G ? (int)((long)a.units * (x + 1) / a.sk_segs) - u0 : 0;
-    const int dp = G && Us >= Gs ? (Us / Gs - 1) * Gs : 0;
-    const long S = G ? (long)(Us - dp) * I : 0;
-    const long e = G ? sk_begin(S, gl + 1, Gs) : 0;
-    long it = G ? sk_begin(S, gl, Gs) : 0;
-    int cont = -1, ckb = 0, cke = 0, cL = 0;     // an owner's continuation (attention_unit's return)
-    long ct_end = 0;
-    // one work item per pass, so the unit code is generated once
-    for (int w = 0;; ++w) {
-        int L, kb = 0, ke = I, kind = UNIT_FULL, jn0 = gl + 1;
-        long t_end = 0;
-        if (cont >= 0) {
-            L = cL; kb = ckb; ke = cke; kind = UNIT_OWNER_CONT; t_end = ct_end; jn0 = cont;
-        } else if (G == 0) {
-            if (w > 0) break;
-            L = g;
-        } else if ((long)gl + (long)w * Gs < dp) {
-            L = u0 + gl + w * Gs;
-        } else {
-            if (it >= e) break;
-            const int t = (int)(it / I);
-            kb = (int)(it - (long)t * I);
-            ke = (int)min((long)I, e - (long)t * I);
-            kind = kb > 0 ? UNIT_PARTIAL : (ke == I ? UNIT_FULL : UNIT_OWNER);
-            L = u0 + dp + t;
-            t_end = (long)(t + 1) * I;
-            it = (long)t * I + ke;
-        }
-        if (w > 0) __syncthreads();                 // the K / V rings are reused by the next unit
-        cont = attention_unit<DT, NEG>(a, smem_k0, smem_k1, smem_v0, smem_v1, L, kb, ke, kind, g, gb, Gs, S, t_end,
+    attn_split_driver(a, [&](int L, int kb, int ke, int kind, int g, int gb, int Gs, long S, long t_end, int jn0,
+                             int& ckb, int& cke) {
+        return attention_unit<DT, NEG>(a, smem_k0, smem_k1, smem_v0, smem_v1, L, kb, ke, kind, g, gb, Gs, S, t_end,
                                        jn0, ckb, cke);
-        cL = L;
-        ct_end = t_end;
-    }
+    });
 }
 
 // Fixed launch bounds (they must not depend on a template parameter: hipcc then emits no host
@@ -555,28 +410,10 @@ hipError_t launch_attention(AttnArgs& a, hipStream_t s) {
     if (a.n_tok == 0) return hipSuccess;
     if (a.dtype == BF16 || a.dtype == F16) {
         const int nq = (a.n_tok + AQ - 1) / AQ;
-        // Stream-K when the last round of units leaves CUs idle for at least four key tiles on
-        // average and every workgroup's share is at least eight key tiles (each piece handed over
-        // costs a pipeline fill and a partial's round trip): at 512 text + 4096 image tokens the
-        // 432 units of 72 key tiles run on 256 CUs as 121.5 key tiles each instead of 2 x 72.
         const int G = device_cu_count();
         a.units = nq * a.n_heads;
         a.k_tiles = (a.n_tok + AK - 1) / AK;
-        a.sk_grid = 0;
-        a.sk_segs = 1;
-        if (a.sk_scratch && G > 0 && a.units % G != 0) {
-            const long rounds = (a.units + G - 1) / G;
-            const long work = (long)a.units * a.k_tiles;
-            const long idle = rounds * G * a.k_tiles - work;
-            if (idle >= 4L * G && work >= 8L * G) {
-                a.sk_grid = G;
-                // one segment per XCD (8 on gfx950; the remapped workgroup ids of an XCD are
-                // contiguous), or one for the whole grid if the CUs do not divide evenly
-                a.sk_segs = G % 8 == 0 ? 8 : 1;
-                a.epoch = next_launch_tag();
-                a.sk_spins = sk_spin_limit();
-            }
-        }
+        attn_plan_split(a, G);
         const dim3 grid(a.sk_grid ? a.sk_grid : a.units), block(64 * kAttnWaves);
         // Stream-K: one workgroup per CU, all resident at once (owners wait for later workgroups).
         // The register budget already allows only one per CU; unused dynamic LDS past the 64 KB

@@ -27,8 +27,10 @@
 //     receives byte j % 8 of the 8-byte rows addressed by lanes j / 8, j / 8 + 2, .., j / 8 + 14),
 //     so four such reads give lane l feature l % 32 of keys 32 h + 0 .. 31 in byte order rho.
 // The running sum is taken over the fp32 probabilities (before their rounding to e4m3).  Each lane
-// ends with 4 consecutive output features of one query per register group.
+// ends with 4 consecutive output features of one query per register group.  With a split scratch
+// buffer (the block path) the units' key tiles are split as for the 16-bit kernel (attn_split.h).
 #include "attn_common.h"
+#include "attn_split.h"
 #include "dev_common.h"
 #include "launch.h"
 
@@ -38,8 +40,6 @@ typedef int i32x8_v __attribute__((ext_vector_type(8)));
 typedef int i32x2_v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2_v lds_i32x2;
 
-constexpr int kF8Waves = 8;
-constexpr int kF8Q = 32 * kF8Waves;         // queries per workgroup
 constexpr int kF8Tile = AK * HD;            // bytes of a K or V tile: 64 rows of 128 codes
 
 __device__ __forceinline__ f32x16_v mfma_e4m3(const i32x8_v& a, const i32x8_v& b, const f32x16_v& c) {
@@ -68,27 +68,31 @@ __device__ __forceinline__ void store4(void* o, long ld_o, int row, int col, flo
     }
 }
 
+// One (head, query tile) unit L = head * nq + query tile over key tiles [kb, ke); kind, g, gb, Gs,
+// S, t_end, jn0, ckb, cke as for the split driver (attn_split.h).  Returns -1 or an owner's
+// continuation.
 template <int OT>
-__global__ __launch_bounds__(64 * kF8Waves, 2) void attention_fp8_kernel(AttnFp8Args a) {
-    __shared__ __attribute__((aligned(1024))) char smem_k0[kF8Tile];
-    __shared__ __attribute__((aligned(1024))) char smem_k1[kF8Tile];
-    __shared__ __attribute__((aligned(1024))) char smem_v0[kF8Tile];
-    __shared__ __attribute__((aligned(1024))) char smem_v1[kF8Tile];
-    const int tid = threadIdx.x, lane = tid & 63;
+__device__ __forceinline__ int attention_unit_fp8(const AttnFp8Args& a, char* smem_k0, char* smem_k1, char* smem_v0,
+                                                  char* smem_v1, int L, int kb, int ke, int kind, int g, int gb,
+                                                  int Gs, long S, long t_end, int jn0, int& ckb, int& cke) {
+    // The thread index goes through an opaque zero: the per-lane address arithmetic below is then
+    // redone for each unit instead of being hoisted out of the persistent loop, where it would
+    // hold registers across the whole kernel.
+    int zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+    const int tid = threadIdx.x + zero, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h32 = lane >> 5, l32 = lane & 31;
     const int N = a.n_tok;
-    const int nq = (N + kF8Q - 1) / kF8Q;
-    const int g = xcd_remap(blockIdx.x, gridDim.x);      // consecutive units (one head) share an XCD
-    const int head = g / nq, qt = g % nq;
-    const int ke = (N + AK - 1) / AK;
+    const int nq = (N + AQ - 1) / AQ;
+    const int head = L / nq, qt = L % nq;
 
     const char* Qg = reinterpret_cast<const char*>(a.q) + head * HD;
     const char* Kg = reinterpret_cast<const char*>(a.k) + head * HD;
     const char* Vg = reinterpret_cast<const char*>(a.v) + head * HD;
 
     // Q fragments (B operand of S^T): query qrow, codes 64 s + 32 h32 .. +31 of slice s
-    const int qrow = qt * kF8Q + wave * 32 + l32;
+    const int qrow = qt * AQ + wave * 32 + l32;
     const int qr = min(qrow, N - 1);
     i32x8_v qf[2];
 #pragma unroll
@@ -243,16 +247,16 @@ __global__ __launch_bounds__(64 * kF8Waves, 2) void attention_fp8_kernel(AttnFp8
         __syncthreads();
     };
 
-    // prologue: K tiles 0 and 1, V tile 0; scores of tile 0
-    load_k(0, 0);
-    if (1 < ke) load_k(1, AK);
-    load_v(0, 0);
+    // prologue: K tiles kb and kb + 1, V tile kb; scores of tile kb
+    load_k(0, kb * AK);
+    if (kb + 1 < ke) load_k(1, (kb + 1) * AK);
+    load_v(0, kb * AK);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     scores(sA, 0);
     __syncthreads();        // K slot 0 is refilled by step 0
 
-    int j = 0;
+    int j = kb;
     for (; j + 2 < ke; j += 2) {
         step.template operator()<0, false>(j, sA, sB);
         step.template operator()<1, false>(j + 1, sB, sA);
@@ -264,6 +268,8 @@ __global__ __launch_bounds__(64 * kF8Waves, 2) void attention_fp8_kernel(AttnFp8
         step.template operator()<0, true>(j, sA, sB);
     }
 
+    const int fin = attn_split_finish(a, o, m_run, l_run, kind, g, gb, Gs, S, t_end, jn0, ckb, cke, wave, lane);
+    if (fin != kAttnStore) return fin;
     if (qrow < N) {
         const float inv = a.v_scale[head] / half_swap_sum(l_run);
         const int col0 = head * HD + 4 * h32;
@@ -274,18 +280,38 @@ __global__ __launch_bounds__(64 * kF8Waves, 2) void attention_fp8_kernel(AttnFp8
                 store4<OT>(a.o, a.ld_o, qrow, col0 + 32 * fb + 8 * i, o[fb][4 * i] * inv, o[fb][4 * i + 1] * inv,
                            o[fb][4 * i + 2] * inv, o[fb][4 * i + 3] * inv);
     }
+    return -1;
 }
 
-hipError_t launch_attention_fp8(const AttnFp8Args& a, hipStream_t s) {
+template <int OT>
+__global__ __launch_bounds__(64 * kAttnWaves, 2) void attention_fp8_kernel(AttnFp8Args a) {
+    __shared__ __attribute__((aligned(1024))) char smem_k0[kF8Tile];
+    __shared__ __attribute__((aligned(1024))) char smem_k1[kF8Tile];
+    __shared__ __attribute__((aligned(1024))) char smem_v0[kF8Tile];
+    __shared__ __attribute__((aligned(1024))) char smem_v1[kF8Tile];
+    attn_split_driver(a, [&](int L, int kb, int ke, int kind, int g, int gb, int Gs, long S, long t_end, int jn0,
+                             int& ckb, int& cke) {
+        return attention_unit_fp8<OT>(a, smem_k0, smem_k1, smem_v0, smem_v1, L, kb, ke, kind, g, gb, Gs, S, t_end,
+                                      jn0, ckb, cke);
+    });
+}
+
+hipError_t launch_attention_fp8(AttnFp8Args& a, hipStream_t s) {
     if (a.n_tok == 0) return hipSuccess;
     // 32-bit lane offsets: 63 rows of a tile past its start
     if (a.ld_k >= (1L << 25) || a.ld_v >= (1L << 25)) return hipErrorInvalidValue;
-    const int nq = (a.n_tok + kF8Q - 1) / kF8Q;
-    const dim3 grid(nq * a.n_heads), block(64 * kF8Waves);
+    const int nq = (a.n_tok + AQ - 1) / AQ;
+    a.units = nq * a.n_heads;
+    a.k_tiles = (a.n_tok + AK - 1) / AK;
+    attn_plan_split(a, device_cu_count());
+    const dim3 grid(a.sk_grid ? a.sk_grid : a.units), block(64 * kAttnWaves);
+    // split: one workgroup per CU (the registers already allow only one; 64 KB of dynamic LDS past
+    // the 32 KB rings makes that hold whatever the register budget)
+    const unsigned pad = a.sk_grid ? 65536u : 0u;
     switch (a.o_dtype) {
-        case F32: hipLaunchKernelGGL(attention_fp8_kernel<F32>, grid, block, 0, s, a); break;
-        case F16: hipLaunchKernelGGL(attention_fp8_kernel<F16>, grid, block, 0, s, a); break;
-        case BF16: hipLaunchKernelGGL(attention_fp8_kernel<BF16>, grid, block, 0, s, a); break;
+        case F32: hipLaunchKernelGGL(attention_fp8_kernel<F32>, grid, block, pad, s, a); break;
+        case F16: hipLaunchKernelGGL(attention_fp8_kernel<F16>, grid, block, pad, s, a); break;
+        case BF16: hipLaunchKernelGGL(attention_fp8_kernel<BF16>, grid, block, pad, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

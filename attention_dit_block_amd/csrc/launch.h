@@ -153,8 +153,14 @@ struct AttnFp8Args {
     int o_dtype;                        // F32, BF16 or F16
     int n_tok, n_heads;
     float scale;
+    // Key-split scratch (16-B-aligned device memory of attention_sk_scratch_bytes(), or null: one
+    // workgroup per (head, query tile) unit).  The launcher fills the rest.
+    void* sk_scratch;
+    int sk_grid, sk_segs, units, k_tiles;
+    unsigned epoch;
+    int sk_spins;
 };
-hipError_t launch_attention_fp8(const AttnFp8Args& a, hipStream_t s);
+hipError_t launch_attention_fp8(AttnFp8Args& a, hipStream_t s);
 
 // ---- calibration: a loop of fp16 MFMAs, 4 waves x 4 chains x iters per workgroup ----------
 hipError_t launch_mfma_loop(int workgroups, int iters, float* out, hipStream_t s);

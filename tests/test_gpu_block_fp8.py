@@ -318,3 +318,46 @@ def test_fp8_block_attention_operands_and_output(dit, cfg, act):
     full = np.zeros((n, d))
     full[rows] = o_gpu[rows]
     ta._check(full, x, H, rows, act)
+
+
+@pytest.mark.parametrize("cfg", [di.BlockConfig("attn_split_fp8", "bf16", d=256, n_heads=2, ffn_inner=768, n_txt=77,
+                                                grid_h=64, grid_w=65), di.CONFIGS[2]], ids=["attn_split", "c2"])
+@pytest.mark.parametrize("polls", [0, 1])
+def test_fp8_block_split_owners_compute_missing_pieces(dit, cfg, polls):
+    """The fp8 attention's key split on the block path (the 16-bit kernel's hand-over, attn_split.h):
+    with a wait bound of 0 every owner computes all of its unit's pieces, with 1 poll some pieces are
+    handed over and some claimed.  The block stays within the fp8 bars (small shape: 5e-2 max/RMS
+    against the oracle's fp8 block; c2: within 1% RMS of the default run, whose pieces may round
+    their probabilities against a different running max), and a later default run repeats the first
+    bit for bit (no flag left behind)."""
+    say(f"fp8 block split hand-over, wait bound {polls}: {cfg.name}")
+    inp = di.double_block_inputs(cfg, seed=6)
+    sh = shape_of(cfg, dit)
+    ws = torch.empty(dit.block_fp8_workspace_size(sh), dtype=torch.uint8, device="cuda")
+    yt = torch.empty(cfg.n_txt, cfg.d, dtype=torch.float32, device="cuda")
+    yi = torch.empty(cfg.n_img, cfg.d, dtype=torch.float32, device="cuda")
+    wt, wi = fp8_weights(dit, inp["txt"]), fp8_weights(dit, inp["img"])
+    args = (dev(inp["cond"], "bf16"), dev(inp["pos"], "i32"), dev(inp["x_txt"], "bf16"), dev(inp["x_img"], "bf16"))
+
+    def run():
+        dit.block_forward_fp8(sh, wt, wi, *args, yt, yi, ws)
+        torch.cuda.synchronize()
+        return host(yt), host(yi)
+    dit.set_split_wait_limit(-1)
+    base = run()
+    try:
+        dit.set_split_wait_limit(polls)
+        got = run()
+    finally:
+        dit.set_split_wait_limit(-1)
+    after = run()
+    ref8 = o.double_block(cfg, inp, fp8=True) if cfg.n_tok < 6000 else None
+    for i, s in enumerate(("txt", "img")):
+        assert np.all(np.isfinite(got[i]))
+        np.testing.assert_array_equal(after[i], base[i])
+        rel = rms_rel(got[i], base[i])
+        say(f"  y_{s}: RMS distance to the default run {rel:.2e}")
+        if cfg.n_tok < 6000 and cfg.d == 256:
+            assert metric(got[i], ref8["y_" + s]) <= BAR_FP8
+        else:
+            assert rel <= 1e-2
