@@ -27,6 +27,7 @@ __all__ = [
     "convert_bf16_to_f16",
     "last_error", "launch_count", "abi_version", "workspace_flags", "set_split_wait_limit", "DIT_RANGE_F16",
     "timing_begin", "timing_end", "timing_read",
+    "joint_attention_fp8", "mfma_loop", "stream_probe", "gemm_kloop_probe", "attention_step_probe",
 ]
 
 DIT_F32, DIT_BF16, DIT_F16 = 0, 1, 2
@@ -105,6 +106,8 @@ _quant8 = _sig("dit_quantize_fp8", _i, [_i, _vp, _vp, _l, _i, _i, _vp, _l, _vp])
 _linear8 = _sig("dit_linear_fp8", _i, [_vp, _vp, _l, _vp, _vp, _l, _vp, _i, _i, _i, _vp, _i, _l])
 _mfma_loop = _sig("dit_mfma_loop", _i, [_vp, _i, _i, _vp])
 _stream_probe = _sig("dit_stream_probe", _i, [_vp, _i, _vp, _vp, _sz, _i, _vp])
+_kloop_probe = _sig("dit_gemm_kloop_probe", _i, [_vp, _i, _i, _i, _vp, _sz, _vp])
+_attn_step_probe = _sig("dit_attention_step_probe", _i, [_vp, _i, _i, _i, ctypes.c_float, _vp])
 _attn8 = _sig("dit_joint_attention_fp8", _i, [_vp, _vp, _l, _vp, _vp, _l, _vp, _vp, _l, _vp, _vp, _i, _l, _i, _i, _i,
                                                _f])
 _wsize8 = _sig("dit_block_fp8_workspace_size", _sz, [ctypes.POINTER(BlockConfig)])
@@ -132,7 +135,7 @@ EXPORTED = ["dit_adaln_modulate", "dit_qk_rmsnorm_rope", "dit_joint_attention", 
             "dit_timestep_embedding_workspace_size", "dit_timestep_embedding", "dit_timestep_embedding_noalloc",
             "dit_linear",
             "dit_final_layer_workspace_size", "dit_final_layer", "dit_neighborhood_attention",
-            "dit_quantize_fp8", "dit_linear_fp8", "dit_joint_attention_fp8", "dit_mfma_loop", "dit_stream_probe", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
+            "dit_quantize_fp8", "dit_linear_fp8", "dit_joint_attention_fp8", "dit_mfma_loop", "dit_stream_probe", "dit_gemm_kloop_probe", "dit_attention_step_probe", "dit_block_fp8_workspace_size", "dit_block_forward_fp8",
             "dit_single_block_fp8_workspace_size", "dit_single_block_forward_fp8",
             "dit_conv2d", "dit_conv3d_causal", "dit_convert_bf16_to_f16",
             "dit_last_error", "dit_launch_count", "dit_workspace_flags", "dit_set_split_wait_limit",
@@ -638,6 +641,30 @@ def stream_probe(mode: int, src, dst=None, sink=None, workgroups: int = 2048, st
     rc = _stream_probe(_stream(stream), mode, _ptr(src, "src"), _ptr(dst, "dst") if mode == 1 else None, nbytes,
                        workgroups, _ptr(sink, "sink", torch.float32) if mode == 0 else None)
     _check(rc, "dit_stream_probe")
+
+
+def gemm_kloop_probe(mode: int, workgroups: int, ksteps: int, out, window=None, stream=None) -> None:
+    """Calibration: the GEMM k-loop on LDS-resident operands (mode bit 0 ping-pong, bit 1 global loads
+    from window, >= 4 MiB of fp16 2^-6); out [workgroups * 512] fp32 gets 2 * ksteps per thread."""
+    import torch
+    _need(out, workgroups * 512, "out")
+    wbytes = 0
+    if mode & 2:
+        if window is None:
+            raise ValueError("mode bit 1 needs a window")
+        wbytes = window.numel() * window.element_size()
+    rc = _kloop_probe(_stream(stream), mode, workgroups, ksteps, _ptr(window, "window") if mode & 2 else None, wbytes,
+                      _ptr(out, "out", torch.float32))
+    _check(rc, "dit_gemm_kloop_probe")
+
+
+def attention_step_probe(mode: int, workgroups: int, tiles: int, out, c2: float = 0.0, stream=None) -> None:
+    """Calibration: the attention step on LDS-resident K / V (mode 0 kernel order, 1 ping-pong);
+    out [workgroups * 512] fp32 gets 48 * tiles (+ 16 in mode 1) per thread when c2 = 0."""
+    import torch
+    _need(out, workgroups * 512, "out")
+    _check(_attn_step_probe(_stream(stream), mode, workgroups, tiles, c2, _ptr(out, "out", torch.float32)),
+           "dit_attention_step_probe")
 
 
 def block_fp8_workspace_size(shape: Shape) -> int:

@@ -1437,6 +1437,32 @@ int dit_mfma_loop(void* stream, int workgroups, int iters, float* out) {
     return launch("mfma_loop", s, [&] { return launch_mfma_loop(workgroups, iters, out, s); });
 }
 
+int dit_gemm_kloop_probe(void* stream, int mode, int workgroups, int ksteps, const void* window, size_t window_bytes,
+                         float* out) {
+    clear_err();
+    if (mode < 0 || mode > 3) return fail(DIT_ERR_INVALID_ARG, "mode = %d", mode);
+    if (workgroups < 1 || workgroups > (1 << 20) || ksteps < 1 || ksteps > (1 << 20))
+        return fail(DIT_ERR_INVALID_ARG, "workgroups = %d, ksteps = %d", workgroups, ksteps);
+    DIT_TRY(check_ptr(out, "out"));
+    if (mode & 2) {
+        DIT_TRY(check_ptr(window, "window"));
+        if (window_bytes < ((size_t)4 << 20)) return fail(DIT_ERR_INVALID_ARG, "window_bytes = %zu < 4 MiB", window_bytes);
+        if (reinterpret_cast<uintptr_t>(window) % 16) return fail(DIT_ERR_INVALID_ARG, "window must be 16-byte aligned");
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("gemm_kloop_probe", s, [&] { return launch_gemm_kloop_probe(mode, workgroups, ksteps, window, out, s); });
+}
+
+int dit_attention_step_probe(void* stream, int mode, int workgroups, int tiles, float c2, float* out) {
+    clear_err();
+    if (mode != 0 && mode != 1) return fail(DIT_ERR_INVALID_ARG, "mode = %d", mode);
+    if (workgroups < 1 || workgroups > (1 << 20) || tiles < 1 || tiles > (1 << 20))
+        return fail(DIT_ERR_INVALID_ARG, "workgroups = %d, tiles = %d", workgroups, tiles);
+    DIT_TRY(check_ptr(out, "out"));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return launch("attention_step_probe", s, [&] { return launch_attention_step_probe(mode, workgroups, tiles, c2, out, s); });
+}
+
 int dit_stream_probe(void* stream, int mode, const void* src, void* dst, size_t bytes, int workgroups, float* sink) {
     clear_err();
     if (mode != 0 && mode != 1) return fail(DIT_ERR_INVALID_ARG, "mode = %d", mode);

@@ -164,6 +164,8 @@ hipError_t launch_attention_fp8(AttnFp8Args& a, hipStream_t s);
 
 // ---- calibration: a loop of fp16 MFMAs, 4 waves x 4 chains x iters per workgroup ----------
 hipError_t launch_mfma_loop(int workgroups, int iters, float* out, hipStream_t s);
+hipError_t launch_gemm_kloop_probe(int mode, int workgroups, int ksteps, const void* win, float* out, hipStream_t s);
+hipError_t launch_attention_step_probe(int mode, int workgroups, int tiles, float c2, float* out, hipStream_t s);
 // ---- calibration: streaming read (mode 0, one float per thread into sink) or copy (mode 1) ----
 hipError_t launch_stream_probe(const void* src, void* dst, size_t bytes, int mode, int workgroups, float* sink,
                                hipStream_t s);

@@ -300,6 +300,21 @@ def calibration(dit, torch, dev):
         ev_ms(fn, 2)
         best = min(ev_ms(fn, 10) / 10 for _ in range(3))
         out[key] = round(moved / (best * 1e-3) / 1e9, 1)
+    # the GEMM's k-loop and the attention step with their operands in LDS (one workgroup per CU): what
+    # the instruction schedules reach without the kernels' global loads and epilogues
+    res = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    win = torch.full((2 << 20,), 0.015625, dtype=torch.float16, device=dev)        # 4 MiB of 2^-6
+    ks, tiles = 2000, 2000
+    for mode, key in ((0, "interleaved"), (1, "pingpong"), (2, "interleaved_l2_loads"), (3, "pingpong_l2_loads")):
+        fn = lambda: dit.gemm_kloop_probe(mode, cus, ks, res, window=win)
+        ev_ms(fn, 2)
+        best = min(ev_ms(fn, 5) / 5 for _ in range(3))
+        out.setdefault("gemm_kloop_lds_tflops", {})[key] = round(2.0 * 256 * 256 * 64 * ks * cus / (best * 1e-3) / 1e12, 1)
+    for mode, key in ((0, "kernel_order"), (1, "pingpong")):
+        fn = lambda: dit.attention_step_probe(mode, cus, tiles, res)
+        ev_ms(fn, 2)
+        best = min(ev_ms(fn, 5) / 5 for _ in range(3))
+        out.setdefault("attention_step_lds_tflops", {})[key] = round(4.0 * 256 * 64 * 128 * tiles * cus / (best * 1e-3) / 1e12, 1)
     return out
 
 

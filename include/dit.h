@@ -484,6 +484,40 @@ int dit_stream_probe(void* stream, int mode, const void* src, void* dst, size_t 
                      float* sink);
 
 /*
+ * Calibration for measurements (not part of the block): the inner loop of the
+ * block's GEMM kernel on LDS-resident operands.  `workgroups` workgroups of 8
+ * waves (128 KB of LDS each, one per CU) run `ksteps` k-steps of the 256 x 256
+ * x 64 fp16 tile: 128 v_mfma_f32_32x32x16_f16 per wave per k-step
+ * (2 * 256 * 256 * 64 flop per workgroup), fragments read from two staged
+ * tiles laid out and swizzled as the GEMM lays them out.  mode bit 0: the
+ * ping-pong schedule (the two waves of a SIMD alternate fragment-read and MFMA
+ * phases, a barrier per phase, MFMA phases at raised wave priority) instead of
+ * the GEMM's interleaved one; bit 1: also load each k-step's 64 KB global ->
+ * LDS from `window` (at least 4 MiB, 16-byte aligned, filled with the fp16
+ * value 2^-6 = 0x2400 so the staged values stay 2^-6; read only; ignored
+ * without bit 1).  Every staged element is 2^-6, so each thread writes
+ * out[w * 512 + t] = 2 * ksteps (the sum of its 128 accumulators); out holds
+ * workgroups * 512 floats.
+ */
+int dit_gemm_kloop_probe(void* stream, int mode, int workgroups, int ksteps, const void* window, size_t window_bytes,
+                         float* out);
+
+/*
+ * Calibration for measurements (not part of the block): the joint-attention
+ * kernel's pipeline step on LDS-resident K and V.  `workgroups` workgroups of
+ * 8 waves (32 queries each, 64 KB of LDS) run `tiles` 64-key tiles at head
+ * dimension 128: per wave and tile 16 score MFMAs, 32 exponentials of
+ * fma(s, c2, -1) with their sums and fp16 packing, a rarely taken branch and
+ * 16 PV MFMAs (4 * 256 * 64 * 128 flop per workgroup and tile).  mode 0: the
+ * kernel's order (next tile's scores beside this tile's softmax, then PV, a
+ * barrier per tile); mode 1: the two waves of a SIMD half a tile apart (MFMA
+ * phase at raised priority, softmax phase), a barrier per phase.  Staged
+ * values are 2^-6; with c2 = 0 every probability is 1/2 and each thread writes
+ * out[w * 512 + t] = 48 * tiles (mode 0) or 48 * tiles + 16 (mode 1).
+ */
+int dit_attention_step_probe(void* stream, int mode, int workgroups, int tiles, float c2, float* out);
+
+/*
  * fp8 double-stream block: dit_block_forward with its four weight products
  * (QKV, out-projection, FFN-in, FFN-down) on e4m3 codes.  Before each product
  * the block quantises the product's activations per row by dit_quantize_fp8's

@@ -44,3 +44,37 @@ def test_mfma_loop_runs(dit):
     dit.mfma_loop(4, 10, out)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+def test_gemm_kloop_probe_closed_form(dit, mode):
+    """Every staged element is 2^-6, so a k-step adds 64 * 2^-12 to each of a thread's 128
+    accumulators: the per-thread sum after k steps is 2 k, exactly, in every schedule."""
+    say(f"GEMM k-loop probe, mode {mode}")
+    wg, ks = 5, 37
+    out = torch.full((wg * 512,), float("nan"), dtype=torch.float32, device="cuda")
+    win = torch.full((2 << 20,), 0.015625, dtype=torch.float16, device="cuda")
+    dit.gemm_kloop_probe(mode, wg, ks, out, window=win)
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.full_like(out, 2.0 * ks))
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_attention_step_probe_closed_form(dit, mode):
+    """With c2 = 0 every probability is 2^-1: a tile adds 32 * 2^-1 to the row sum and 64 * 2^-6 * 2^-1
+    to each of a thread's 64 output accumulators, 48 per tile in all (mode 1 runs one more softmax)."""
+    say(f"attention step probe, mode {mode}")
+    wg, tiles = 3, 41
+    out = torch.full((wg * 512,), float("nan"), dtype=torch.float32, device="cuda")
+    dit.attention_step_probe(mode, wg, tiles, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.full_like(out, 48.0 * tiles + (16.0 if mode == 1 else 0.0)))
+
+
+def test_probe_arguments_rejected(dit):
+    out = torch.empty(512, dtype=torch.float32, device="cuda")
+    small = torch.zeros(1024, dtype=torch.float16, device="cuda")
+    with pytest.raises(Exception):
+        dit.gemm_kloop_probe(2, 1, 1, out, window=small)       # window under 4 MiB
+    with pytest.raises(Exception):
+        dit.attention_step_probe(2, 1, 1, out)                  # no such mode
