@@ -7,7 +7,8 @@
 // each wave 32 queries.  K and V tiles of 64 keys go from HBM straight into LDS
 // (global_load_lds, no VGPR staging) through two 2-slot rings: at step j the workgroup loads
 // K tile j+2 and V tile j+1 while it computes the scores of tile j+1 (MFMA) next to the softmax
-// of tile j (VALU), then O += V_j P_j; one barrier per step.
+// of tile j (VALU) -- one pair of probabilities between consecutive score MFMAs, an order
+// scheduling barriers hold -- then O += V_j P_j; one barrier per step.
 // Per key tile:
 //   S^T = K Q^T  with v_mfma_f32_32x32x16 (K fragment = A operand, Q fragment = B), so a lane
 //                holds 32 scores of ONE query: the row max needs one swap with lane ^ 32;
@@ -176,7 +177,6 @@ __device__ __forceinline__ int attention_unit(const AttnArgs& a, char* smem_k0, 
             load_v(P ^ 1, j0 + AK);
         }
         // ---- region 1: S(j+1) MFMAs with the softmax of tile j
-        if constexpr (!LAST) scores(SN, P ^ 1);
         // register q of block kb holds key j0 + 32 kb + 16 (q >> 3) + 8 h32 + (q & 7)
         auto masked = [&](int kb, int q) { return j0 + 32 * kb + 16 * (q >> 3) + 8 * h32 + (q & 7) >= N; };
         if constexpr (LAST) {
@@ -218,7 +218,43 @@ __device__ __forceinline__ int attention_unit(const AttnArgs& a, char* smem_k0, 
         // kLazyMax and the max is not raised; only when some lane of the wave reaches it (a large
         // score, or the first tile: running max -inf) does the wave take the tile's max and
         // recompute, which gives the same values as taking the max first.
-        probs(-m_run);
+        if constexpr (LAST) {
+            probs(-m_run);
+        } else {
+            // the 16 score MFMAs of tile j + 1 (the two 32-key chains alternating, each in feature
+            // order), each K fragment read one MFMA ahead, and between consecutive MFMAs one pair of
+            // tile j's probabilities (in probs' order); the scheduling barriers keep this order, so
+            // the exponentials issue while the matrix pipe works
+            const char* kt = (P ^ 1) ? smem_k1 : smem_k0;
+            auto kfrag = [&](int i) {
+                const int kb = i & 1, es = i >> 1;
+                return *reinterpret_cast<const FragT*>(kt + (es >> 1) * 4096 + kb * 32 * 64 + k_off[es & 1]);
+            };
+            const float nm = -m_run;
+            lsum = 0.0f;
+            FragT kf_next = kfrag(0), kf_next2 = kfrag(1);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const FragT kf = kf_next;
+                kf_next = kf_next2;
+                if (i < 14) kf_next2 = kfrag(i + 2);
+                const int kb = i & 1, es = i >> 1;
+                SN[kb] = es == 0 ? amfma<DT>(kf, qf[es], f32x16_v{}) : amfma<DT>(kf, qf[es], SN[kb]);
+                const int kc = i >> 3, q = 2 * (i & 7);
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(SC[kc][q], c2, nm));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(SC[kc][q + 1], c2, nm));
+                lsum += p0 + p1;
+                const int w = 8 * kc + (q >> 1);
+                if constexpr (DT == BF16) {
+                    const uint32_t u0 = __float_as_uint(p0) & 0xffff0000u, u1 = __float_as_uint(p1) & 0xffff0000u;
+                    ph[w] = (u0 >> 16) | u1;
+                    pl[w] = pack_bf16x2(p0 - __uint_as_float(u0), p1 - __uint_as_float(u1));
+                } else {
+                    ph[w] = pack_f16x2(p0, p1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
         float corr = 1.0f;
         bool raise = false;
         if (__builtin_amdgcn_ballot_w64(!(lsum < kLazyP))) {
@@ -254,29 +290,29 @@ __device__ __forceinline__ int attention_unit(const AttnArgs& a, char* smem_k0, 
         }
         // ---- region 2: O^T += V^T P^T; key step ks covers keys 16 ks .. +15 of the tile
         const char* vt = P ? smem_v1 : smem_v0;
-        auto read_v = [&](FragT* vf, int ks) {
-#pragma unroll
-            for (int eb = 0; eb < 4; ++eb) {
-                const char* vp = vt + v_off + eb * 4096 + ks * 16 * 64;
-                const s16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-                const s16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * 64));
-                const s16x8_v w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                vf[eb] = __builtin_bit_cast(FragT, w);
-            }
+        // one V^T fragment read ahead of its MFMA
+        auto read_v1 = [&](int i) {
+            const int ks = i >> 2, eb = i & 3;
+            const char* vp = vt + v_off + eb * 4096 + ks * 16 * 64;
+            const s16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+            const s16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * 64));
+            const s16x8_v w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(FragT, w);
         };
-        FragT vf[2][4];
-        read_v(vf[0], 0);
+        FragT vn = read_v1(0), vn2 = read_v1(1);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (ks < 3) read_v(vf[(ks + 1) & 1], ks + 1);
+        for (int i = 0; i < 16; ++i) {
+            const FragT vc = vn;
+            vn = vn2;
+            if (i < 14) vn2 = read_v1(i + 2);
+            const int ks = i >> 2, eb = i & 3;
             const u32x4_v hv = {ph[4 * ks], ph[4 * ks + 1], ph[4 * ks + 2], ph[4 * ks + 3]};
-#pragma unroll
-            for (int eb = 0; eb < 4; ++eb) o[eb] = amfma<DT>(vf[ks & 1][eb], __builtin_bit_cast(FragT, hv), o[eb]);
+            o[eb] = amfma<DT>(vc, __builtin_bit_cast(FragT, hv), o[eb]);
             if constexpr (DT == BF16) {
                 const u32x4_v lv = {pl[4 * ks], pl[4 * ks + 1], pl[4 * ks + 2], pl[4 * ks + 3]};
-#pragma unroll
-                for (int eb = 0; eb < 4; ++eb) o[eb] = amfma<DT>(vf[ks & 1][eb], __builtin_bit_cast(FragT, lv), o[eb]);
+                o[eb] = amfma<DT>(vc, __builtin_bit_cast(FragT, lv), o[eb]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // the loads issued above have landed (own: waitcnt; every wave's: barrier), and every
         // wave is done with the slots the next step's loads overwrite
