@@ -69,6 +69,10 @@ __device__ __forceinline__ int attention_unit(const AttnArgs& a, char* smem_k0, 
     const int tid = threadIdx.x + zero, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h32 = lane >> 5, l32 = lane & 31;
+    // the key range is wave-uniform (an owner's continuation takes it from a flag word every lane
+    // read): scalar loop control and scalar tile addresses
+    kb = __builtin_amdgcn_readfirstlane(kb);
+    ke = __builtin_amdgcn_readfirstlane(ke);
     const int nq = (a.n_tok + AQ - 1) / AQ;
     const int head = L / nq, qt = L % nq;
     const int N = a.n_tok;
