@@ -133,6 +133,10 @@ __device__ __forceinline__ int gemm_tile(const GemmBatch& b, char* smem, int L, 
     constexpr int MT = mfma_type<AT>();           // MFMA operand type
     typedef typename Frag<MT>::T FragT;
 
+    // An owner's continuation takes its k-range from a flag word every lane read: make the range
+    // wave-uniform so the k-loop runs on scalar control.
+    kb = __builtin_amdgcn_readfirstlane(kb);
+    ke = __builtin_amdgcn_readfirstlane(ke);
     int pi, tm, tn;
     tile_of(b, L, pi, tm, tn);
     const GemmProblem& P = b.p[pi];
