@@ -645,7 +645,8 @@ def stream_probe(mode: int, src, dst=None, sink=None, workgroups: int = 2048, st
 
 def gemm_kloop_probe(mode: int, workgroups: int, ksteps: int, out, window=None, stream=None) -> None:
     """Calibration: the GEMM k-loop on LDS-resident operands (mode bit 0 ping-pong, bit 1 global loads
-    from window, >= 4 MiB of fp16 2^-6); out [workgroups * 512] fp32 gets 2 * ksteps per thread."""
+    from window, >= 4 MiB of fp16; bit 2 random operands); out [workgroups * 512] fp32 gets 2 * ksteps
+    per thread with the constant operands (window of fp16 2^-6)."""
     import torch
     _need(out, workgroups * 512, "out")
     wbytes = 0
@@ -659,8 +660,9 @@ def gemm_kloop_probe(mode: int, workgroups: int, ksteps: int, out, window=None, 
 
 
 def attention_step_probe(mode: int, workgroups: int, tiles: int, out, c2: float = 0.0, stream=None) -> None:
-    """Calibration: the attention step on LDS-resident K / V (mode 0 kernel order, 1 ping-pong);
-    out [workgroups * 512] fp32 gets 48 * tiles (+ 16 in mode 1) per thread when c2 = 0."""
+    """Calibration: the attention step on LDS-resident K / V (mode bit 0 ping-pong, bit 1 random
+    operands); out [workgroups * 512] fp32 gets 48 * tiles (+ 16 with bit 0) per thread when c2 = 0
+    and the operands are constant."""
     import torch
     _need(out, workgroups * 512, "out")
     _check(_attn_step_probe(_stream(stream), mode, workgroups, tiles, c2, _ptr(out, "out", torch.float32)),

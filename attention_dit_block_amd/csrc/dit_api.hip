@@ -1440,7 +1440,8 @@ int dit_mfma_loop(void* stream, int workgroups, int iters, float* out) {
 int dit_gemm_kloop_probe(void* stream, int mode, int workgroups, int ksteps, const void* window, size_t window_bytes,
                          float* out) {
     clear_err();
-    if (mode < 0 || mode > 3) return fail(DIT_ERR_INVALID_ARG, "mode = %d", mode);
+    if (mode < 0 || mode > 15 || ((mode & 8) && (mode & 2)))
+        return fail(DIT_ERR_INVALID_ARG, "mode = %d (bit 3, registers only, excludes bit 1, global loads)", mode);
     if (workgroups < 1 || workgroups > (1 << 20) || ksteps < 1 || ksteps > (1 << 20))
         return fail(DIT_ERR_INVALID_ARG, "workgroups = %d, ksteps = %d", workgroups, ksteps);
     DIT_TRY(check_ptr(out, "out"));
@@ -1455,7 +1456,7 @@ int dit_gemm_kloop_probe(void* stream, int mode, int workgroups, int ksteps, con
 
 int dit_attention_step_probe(void* stream, int mode, int workgroups, int tiles, float c2, float* out) {
     clear_err();
-    if (mode != 0 && mode != 1) return fail(DIT_ERR_INVALID_ARG, "mode = %d", mode);
+    if (mode < 0 || mode > 3) return fail(DIT_ERR_INVALID_ARG, "mode = %d", mode);
     if (workgroups < 1 || workgroups > (1 << 20) || tiles < 1 || tiles > (1 << 20))
         return fail(DIT_ERR_INVALID_ARG, "workgroups = %d, tiles = %d", workgroups, tiles);
     DIT_TRY(check_ptr(out, "out"));

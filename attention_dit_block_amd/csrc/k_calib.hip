@@ -76,6 +76,25 @@ hipError_t launch_stream_probe(const void* src, void* dst, size_t bytes, int mod
 typedef __attribute__((address_space(3))) void calib_lds_void;
 constexpr uint32_t kHalf2Pow6 = 0x24002400u;      // two fp16 2^-6
 
+// 16 bytes of staged operand number i: eight fp16 2^-6, or (rnd) eight hashed fp16 values of random
+// sign, magnitude in [2^-6, 2^-2), so that the matrix cores switch realistic bit patterns (constant
+// operands let the chip hold a higher clock)
+__device__ __forceinline__ u32x4_v calib_fill(int i, int rnd) {
+    if (!rnd) return u32x4_v{kHalf2Pow6, kHalf2Pow6, kHalf2Pow6, kHalf2Pow6};
+    u32x4_v w;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        uint32_t h = (uint32_t)(4 * i + t) * 2654435761u;
+        h ^= h >> 13;
+        h *= 0x5bd1e995u;
+        h ^= h >> 15;
+        const uint32_t a = ((h & 1u) << 15) | ((9u + ((h >> 1) & 3u)) << 10) | ((h >> 3) & 0x3ffu);
+        const uint32_t b = (((h >> 13) & 1u) << 15) | ((9u + ((h >> 14) & 3u)) << 10) | ((h >> 16) & 0x3ffu);
+        w[t] = a | (b << 16);
+    }
+    return w;
+}
+
 __device__ __forceinline__ void calib_barrier() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
@@ -90,16 +109,17 @@ __device__ __forceinline__ void calib_barrier() {
 // alternate 32-deep fragment-read phases and 16-MFMA phases a phase apart, a barrier per phase, the
 // MFMA phase at raised wave priority) instead of the kernel's interleaved one (each k16 sub-step's
 // MFMAs beside the next sub-step's reads, a barrier per k-step).  Bit 1: also load each k-step's
-// 64 KB global -> LDS (8 KB per wave) from a 4 MiB window of 2^-6 values, as the GEMM does.
+// 64 KB global -> LDS (8 KB per wave) from a 4 MiB window of 2^-6 values, as the GEMM does.  Bit 3:
+// the fragments are read once before the loop and the MFMAs run on them from registers (the
+// matrix cores' rate in this layout, without LDS).
 // out[w * 512 + t] = the sum of thread t's 128 accumulators = 2 * ksteps.
 template <int MODE>
-__global__ __launch_bounds__(512, 1) void gemm_kloop_kernel(int n, const char* win, float* out) {
+__global__ __launch_bounds__(512, 1) void gemm_kloop_kernel(int n, const char* win, float* out, int rnd) {
     __shared__ __attribute__((aligned(1024))) char smem[131072];
-    constexpr bool PP = MODE & 1, GL = (MODE & 2) != 0;
+    constexpr bool PP = MODE & 1, GL = (MODE & 2) != 0, REGS = (MODE & 8) != 0;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / 4, wn = wave % 4, khalf = lane >> 5;
-    for (int i = tid; i < 131072 / 16; i += 512)
-        reinterpret_cast<u32x4_v*>(smem)[i] = u32x4_v{kHalf2Pow6, kHalf2Pow6, kHalf2Pow6, kHalf2Pow6};
+    for (int i = tid; i < 131072 / 16; i += 512) reinterpret_cast<u32x4_v*>(smem)[i] = calib_fill(i, rnd);
     __syncthreads();
     int a_row[4], b_row[2];
 #pragma unroll
@@ -137,14 +157,18 @@ __global__ __launch_bounds__(512, 1) void gemm_kloop_kernel(int n, const char* w
             for (int mb = 0; mb < 4; ++mb)
                 acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[s][nb], fa[s][mb], acc[nb][mb], 0, 0, 0);
     };
-    if constexpr (!PP) {
+    if constexpr (REGS) {
         rd(fa[0], fb[0], 0, 0);
+        rd(fa[1], fb[1], 0, 1);
+    }
+    if constexpr (!PP) {
+        if constexpr (!REGS) rd(fa[0], fb[0], 0, 0);
         for (int t = 0; t < n; ++t) {
             const int base = (t & 1) * 65536;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int cur = s & 1;
-                if (s < 3) rd(fa[cur ^ 1], fb[cur ^ 1], base, s + 1);
+                if (!REGS && s < 3) rd(fa[cur ^ 1], fb[cur ^ 1], base, s + 1);
                 if (GL && s == 0 && t + 1 < n)
 #pragma unroll
                     for (int i = 0; i < 8; ++i) gl(t + 1, i);
@@ -162,14 +186,16 @@ __global__ __launch_bounds__(512, 1) void gemm_kloop_kernel(int n, const char* w
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            rd(fa[0], fb[0], ((t + 1) & 1) * 65536, 0);
+            if (!REGS) rd(fa[0], fb[0], ((t + 1) & 1) * 65536, 0);
         }
     } else {
         // group 0 (waves 0-3) reads half h while group 1 (waves 4-7, one per SIMD beside them)
         // runs the MFMAs of its previous half, then the other way round
         auto mph = [&](int t, int h) {
-            rd(fa[0], fb[0], (t & 1) * 65536, 2 * h);
-            rd(fa[1], fb[1], (t & 1) * 65536, 2 * h + 1);
+            if (!REGS) {
+                rd(fa[0], fb[0], (t & 1) * 65536, 2 * h);
+                rd(fa[1], fb[1], (t & 1) * 65536, 2 * h + 1);
+            }
             __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0)
         };
         auto cph = [&]() {
@@ -213,18 +239,18 @@ __global__ __launch_bounds__(512, 1) void gemm_kloop_kernel(int n, const char* w
 // scores j + 1 and PV j, at raised priority; a softmax phase), a barrier per phase.  With c2 = 0
 // every probability is 1/2 and out[w * 512 + t] = 48 * tiles (+ 16 in MODE 1, one more softmax).
 template <int MODE>
-__global__ __launch_bounds__(512, 2) void attention_step_kernel(int n, float c2, float* out) {
+__global__ __launch_bounds__(512, 2) void attention_step_kernel(int n, float c2, float* out, int rnd) {
     // 96 KB so that, like the kernel it stands for, one workgroup holds a CU (64 KB are used)
     __shared__ __attribute__((aligned(1024))) char smem[98304];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    for (int i = tid; i < 65536 / 16; i += 512)
-        reinterpret_cast<u32x4_v*>(smem)[i] = u32x4_v{kHalf2Pow6, kHalf2Pow6, kHalf2Pow6, kHalf2Pow6};
+    for (int i = tid; i < 65536 / 16; i += 512) reinterpret_cast<u32x4_v*>(smem)[i] = calib_fill(i, rnd);
     __syncthreads();
     f16x8_v qf[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[i][e] = (_Float16)0.015625f;
+    for (int i = 0; i < 8; ++i) {
+        const u32x4_v w = calib_fill(4096 + 64 * i + lane, rnd);
+        qf[i] = __builtin_bit_cast(f16x8_v, w);
+    }
     f32x16_v o[4], S[2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -322,18 +348,22 @@ __global__ __launch_bounds__(512, 2) void attention_step_kernel(int n, float c2,
 
 hipError_t launch_gemm_kloop_probe(int mode, int workgroups, int ksteps, const void* win, float* out, hipStream_t s) {
     const char* w = reinterpret_cast<const char*>(win);
-    switch (mode) {
-    case 0: hipLaunchKernelGGL(gemm_kloop_kernel<0>, dim3(workgroups), dim3(512), 0, s, ksteps, w, out); break;
-    case 1: hipLaunchKernelGGL(gemm_kloop_kernel<1>, dim3(workgroups), dim3(512), 0, s, ksteps, w, out); break;
-    case 2: hipLaunchKernelGGL(gemm_kloop_kernel<2>, dim3(workgroups), dim3(512), 0, s, ksteps, w, out); break;
-    default: hipLaunchKernelGGL(gemm_kloop_kernel<3>, dim3(workgroups), dim3(512), 0, s, ksteps, w, out); break;
+    const int rnd = (mode >> 2) & 1;
+    switch (mode & 11) {
+    case 0: hipLaunchKernelGGL(gemm_kloop_kernel<0>, dim3(workgroups), dim3(512), 0, s, ksteps, w, out, rnd); break;
+    case 1: hipLaunchKernelGGL(gemm_kloop_kernel<1>, dim3(workgroups), dim3(512), 0, s, ksteps, w, out, rnd); break;
+    case 2: hipLaunchKernelGGL(gemm_kloop_kernel<2>, dim3(workgroups), dim3(512), 0, s, ksteps, w, out, rnd); break;
+    case 3: hipLaunchKernelGGL(gemm_kloop_kernel<3>, dim3(workgroups), dim3(512), 0, s, ksteps, w, out, rnd); break;
+    case 8: hipLaunchKernelGGL(gemm_kloop_kernel<8>, dim3(workgroups), dim3(512), 0, s, ksteps, w, out, rnd); break;
+    default: hipLaunchKernelGGL(gemm_kloop_kernel<9>, dim3(workgroups), dim3(512), 0, s, ksteps, w, out, rnd); break;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_attention_step_probe(int mode, int workgroups, int tiles, float c2, float* out, hipStream_t s) {
-    if (mode == 0) hipLaunchKernelGGL(attention_step_kernel<0>, dim3(workgroups), dim3(512), 0, s, tiles, c2, out);
-    else hipLaunchKernelGGL(attention_step_kernel<1>, dim3(workgroups), dim3(512), 0, s, tiles, c2, out);
+    const int rnd = (mode >> 1) & 1;
+    if ((mode & 1) == 0) hipLaunchKernelGGL(attention_step_kernel<0>, dim3(workgroups), dim3(512), 0, s, tiles, c2, out, rnd);
+    else hipLaunchKernelGGL(attention_step_kernel<1>, dim3(workgroups), dim3(512), 0, s, tiles, c2, out, rnd);
     return hipGetLastError();
 }
 

@@ -304,14 +304,18 @@ def calibration(dit, torch, dev):
     # the instruction schedules reach without the kernels' global loads and epilogues
     res = torch.empty(cus * 512, dtype=torch.float32, device=dev)
     win = torch.full((2 << 20,), 0.015625, dtype=torch.float16, device=dev)        # 4 MiB of 2^-6
+    # random-valued operands as well: constant ones let the device hold a higher clock
+    win_r = (torch.rand(2 << 20, device=dev) * 0.25 - 0.125).to(torch.float16)
     ks, tiles = 2000, 2000
-    for mode, key in ((0, "interleaved"), (1, "pingpong"), (2, "interleaved_l2_loads"), (3, "pingpong_l2_loads")):
-        fn = lambda: dit.gemm_kloop_probe(mode, cus, ks, res, window=win)
+    for mode, key in ((0, "interleaved"), (1, "pingpong"), (2, "interleaved_l2_loads"), (3, "pingpong_l2_loads"),
+                      (8, "registers"), (12, "registers_random"), (4, "interleaved_random"), (5, "pingpong_random"),
+                      (6, "interleaved_l2_loads_random"), (7, "pingpong_l2_loads_random")):
+        fn = lambda: dit.gemm_kloop_probe(mode, cus, ks, res, window=win_r if mode & 4 else win)
         ev_ms(fn, 2)
         best = min(ev_ms(fn, 5) / 5 for _ in range(3))
         out.setdefault("gemm_kloop_lds_tflops", {})[key] = round(2.0 * 256 * 256 * 64 * ks * cus / (best * 1e-3) / 1e12, 1)
-    for mode, key in ((0, "kernel_order"), (1, "pingpong")):
-        fn = lambda: dit.attention_step_probe(mode, cus, tiles, res)
+    for mode, key in ((0, "kernel_order"), (1, "pingpong"), (2, "kernel_order_random")):
+        fn = lambda: dit.attention_step_probe(mode, cus, tiles, res, c2=0.18 if mode & 2 else 0.0)
         ev_ms(fn, 2)
         best = min(ev_ms(fn, 5) / 5 for _ in range(3))
         out.setdefault("attention_step_lds_tflops", {})[key] = round(4.0 * 256 * 64 * 128 * tiles * cus / (best * 1e-3) / 1e12, 1)

@@ -497,7 +497,11 @@ int dit_stream_probe(void* stream, int mode, const void* src, void* dst, size_t 
  * value 2^-6 = 0x2400 so the staged values stay 2^-6; read only; ignored
  * without bit 1).  Every staged element is 2^-6, so each thread writes
  * out[w * 512 + t] = 2 * ksteps (the sum of its 128 accumulators); out holds
- * workgroups * 512 floats.
+ * workgroups * 512 floats.  Bit 2: the LDS tiles start as hashed fp16 values
+ * of random sign and magnitude in [2^-6, 2^-2) instead (operands whose bits
+ * switch as real data do; the device holds a lower clock on them), and out is
+ * the sums they give.  Bit 3 (not with bit 1): the fragments are read once and
+ * the k-steps run their MFMAs from registers, without LDS reads.
  */
 int dit_gemm_kloop_probe(void* stream, int mode, int workgroups, int ksteps, const void* window, size_t window_bytes,
                          float* out);
@@ -508,12 +512,14 @@ int dit_gemm_kloop_probe(void* stream, int mode, int workgroups, int ksteps, con
  * 8 waves (32 queries each, 64 KB of LDS) run `tiles` 64-key tiles at head
  * dimension 128: per wave and tile 16 score MFMAs, 32 exponentials of
  * fma(s, c2, -1) with their sums and fp16 packing, a rarely taken branch and
- * 16 PV MFMAs (4 * 256 * 64 * 128 flop per workgroup and tile).  mode 0: the
- * kernel's order (next tile's scores beside this tile's softmax, then PV, a
- * barrier per tile); mode 1: the two waves of a SIMD half a tile apart (MFMA
- * phase at raised priority, softmax phase), a barrier per phase.  Staged
+ * 16 PV MFMAs (4 * 256 * 64 * 128 flop per workgroup and tile).  mode bit 0
+ * clear: the kernel's order (next tile's scores beside this tile's softmax,
+ * then PV, a barrier per tile); set: the two waves of a SIMD half a tile apart
+ * (MFMA phase at raised priority, softmax phase), a barrier per phase.  Staged
  * values are 2^-6; with c2 = 0 every probability is 1/2 and each thread writes
- * out[w * 512 + t] = 48 * tiles (mode 0) or 48 * tiles + 16 (mode 1).
+ * out[w * 512 + t] = 48 * tiles (bit 0 clear) or 48 * tiles + 16 (set).  Bit
+ * 1: K, V and Q start as hashed fp16 values of random sign and magnitude in
+ * [2^-6, 2^-2) instead (see dit_gemm_kloop_probe).
  */
 int dit_attention_step_probe(void* stream, int mode, int workgroups, int tiles, float c2, float* out);
 

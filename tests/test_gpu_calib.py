@@ -46,7 +46,7 @@ def test_mfma_loop_runs(dit):
     assert torch.isfinite(out).all()
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 8, 9])
 def test_gemm_kloop_probe_closed_form(dit, mode):
     """Every staged element is 2^-6, so a k-step adds 64 * 2^-12 to each of a thread's 128
     accumulators: the per-thread sum after k steps is 2 k, exactly, in every schedule."""
@@ -71,10 +71,28 @@ def test_attention_step_probe_closed_form(dit, mode):
     assert torch.equal(out, torch.full_like(out, 48.0 * tiles + (16.0 if mode == 1 else 0.0)))
 
 
+def test_probes_random_operands_deterministic(dit):
+    """With random operands (mode bit 2 / bit 1) the probes give finite sums, the same on every run."""
+    say("probes with random operands")
+    out = torch.empty(4 * 512, dtype=torch.float32, device="cuda")
+    win = (torch.rand(2 << 20, device="cuda") * 0.25 - 0.125).to(torch.float16)
+    for run in (lambda: dit.gemm_kloop_probe(6, 4, 9, out, window=win), lambda: dit.gemm_kloop_probe(4, 4, 9, out),
+                lambda: dit.attention_step_probe(2, 4, 7, out, c2=0.18)):
+        run()
+        torch.cuda.synchronize()
+        first = out.clone()
+        assert torch.isfinite(first).all()
+        run()
+        torch.cuda.synchronize()
+        assert torch.equal(out, first)
+
+
 def test_probe_arguments_rejected(dit):
     out = torch.empty(512, dtype=torch.float32, device="cuda")
     small = torch.zeros(1024, dtype=torch.float16, device="cuda")
     with pytest.raises(Exception):
         dit.gemm_kloop_probe(2, 1, 1, out, window=small)       # window under 4 MiB
     with pytest.raises(Exception):
-        dit.attention_step_probe(2, 1, 1, out)                  # no such mode
+        dit.attention_step_probe(4, 1, 1, out)                  # no such mode
+    with pytest.raises(Exception):
+        dit.gemm_kloop_probe(10, 1, 1, out, window=small)       # registers only with global loads
