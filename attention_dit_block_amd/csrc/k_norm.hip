@@ -279,7 +279,7 @@ hipError_t launch_modulate(const ModBatch& b, hipStream_t s) {
 
 // ------------------------------------------------------------------------------------------
 // QK RMSNorm + 4-axis RoPE, in place.  One 256-thread block per token: the first wave computes
-// the token's 64 rotation angles once (double-precision angle and range reduction, fp32 sin/cos)
+// the token's 64 rotation angles once (double-precision angle reduced in revolutions, hardware sin/cos)
 // into LDS; then groups of 16 lanes each take one 128-dim head vector of q or k (16 B per lane
 // for 16-bit types), reduce its mean square across the 16 lanes, scale by the QK-norm weight
 // and rotate the four interleaved pairs they hold.
