@@ -143,6 +143,29 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Reductions over aligned groups of 16 lanes by DPP moves (no LDS round trip).  Every lane of a
+// group ends with the same bits: after the quad steps each lane holds its quad's value S_q, then
+// row_mirror adds quad 3 - q and row_half_mirror the neighbouring quad's pair, so each lane forms
+// (S_0 + S_3) + (S_1 + S_2) up to the order of two commutative operands.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f32<0xB1>(v);      // quad_perm [1, 0, 3, 2]
+    v += dpp_f32<0x4E>(v);      // quad_perm [2, 3, 0, 1]
+    v += dpp_f32<0x140>(v);     // row_mirror: lane 15 - j of the row of 16
+    v += dpp_f32<0x141>(v);     // row_half_mirror: lane 7 - j of the half row
+    return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    return v;
+}
+
 // XCD-aware remap: consecutive workgroup ids go round-robin over the 8 XCDs; give each XCD a
 // contiguous range of work indices instead (workgroups sharing operands then share one L2).
 __device__ __forceinline__ int xcd_remap(int bid, int nwg) {

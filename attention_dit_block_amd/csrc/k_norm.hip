@@ -319,8 +319,8 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkRopeArgs a) {
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
-        ss = group_sum<16>(ss);
-        const float rstd = 1.0f / sqrtf(ss * (1.0f / 128.0f) + a.eps);
+        ss = row16_sum(ss);
+        const float rstd = __builtin_amdgcn_rsqf(ss * (1.0f / 128.0f) + a.eps);
         float y[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = v[i] * rstd * w[i];
@@ -339,7 +339,8 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkRopeArgs a) {
 // codes instead of the rotated values -- q per (token, head) with s = max|y| / 448 (1 for a zero
 // row), k per head with the static scale max|w_k| * sqrt(128) / 448 (a normed, rotated element never
 // exceeds sqrt(128) times the largest weight), v per head with s = max|v| / 448 from the maxima the
-// QKV epilogue raised; codes e4m3(y / s), correctly rounded fp32 division, nearest-even conversion.
+// QKV epilogue raised; codes e4m3(y / s) of the correctly rounded fp32 quotient, nearest-even
+// conversion.
 constexpr float kKBound = 0x1.9dc22cp-6f;   // sqrt(128) / 448 rounded to fp32
 
 template <int G>
@@ -349,65 +350,83 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
+// x / s correctly rounded to fp32, from r = 1 / (double)s (correctly rounded): the double product
+// x * r is within 2^-52 (relative) of x / s, while a quotient of two fp32 values in the normal range
+// lies more than 2^-49 (relative) from every midpoint between neighbouring fp32 values, so the
+// product rounds to the same fp32 value as the quotient.  (Quotients below the normal range are far
+// below e4m3's smallest step and give the same zero code either way.)  Three instructions instead of
+// the division's ten.
+__device__ __forceinline__ float div_by_rcp(float x, double r) { return (float)((double)x * r); }
+
 template <int DT, int WT>
 __global__ __launch_bounds__(256) void qk_norm_rope_fp8_kernel(QkRopeArgs a) {
     __shared__ float s_cos[64], s_sin[64], s_kw[4];
+    __shared__ double s_rv[256];        // 1 / (double)(v scale) per head
+    constexpr int ES = ESize<DT>::v, WS = ESize<WT>::v;
     const int n = blockIdx.x;
     const int tid = threadIdx.x;
-    constexpr int ES = ESize<DT>::v, WS = ESize<WT>::v;
+    const int H = a.n_heads;
+    const int set = n < a.n_first ? 0 : 1;
+    const int g = tid >> 4;           // 16 groups of 16 lanes
+    const int t = tid & 15;           // dims 8t .. 8t+7 of the head
+    // this lane's dims of the q- and k-norm weights
+    float wq[8], wk[8];
+    {
+        const char* wrow = reinterpret_cast<const char*>(set ? a.qk_w1 : a.qk_w0);
+        load8<WT>(wrow + (size_t)(t * 8) * WS, wq);
+        load8<WT>(wrow + (size_t)(128 + t * 8) * WS, wk);
+    }
     if (tid < 64) {
+        // the angle in revolutions reduced in double precision, hardware sine and cosine (as in
+        // the 16-bit pass)
         const int ax = a.tab.axis[tid];
-        const double phi = (double)a.pos[(size_t)n * a.n_axes + ax] * a.tab.omega_d[tid];
-        const double two_pi = 6.283185307179586476925286766559;
-        const float red = (float)(phi - two_pi * rint(phi / two_pi));
-        s_cos[tid] = cosf(red);
-        s_sin[tid] = sinf(red);
+        const double inv_two_pi = 0.15915494309189533576888376337251;
+        const double rev = (double)a.pos[(size_t)n * a.n_axes + ax] * a.tab.omega_d[tid] * inv_two_pi;
+        const float fr = (float)(rev - rint(rev));
+        s_cos[tid] = __builtin_amdgcn_cosf(fr);
+        s_sin[tid] = __builtin_amdgcn_sinf(fr);
     }
     {
         // the largest |k weight| of both sets: thread tid reads dim tid % 128 of set tid / 128
-        const char* wk = reinterpret_cast<const char*>(tid < 128 ? a.qk_w0 : a.qk_w1);
+        const char* wkp = reinterpret_cast<const char*>(tid < 128 ? a.qk_w0 : a.qk_w1);
         float wv = 0.0f;
-        if (wk) {
+        if (wkp) {
             float w8[8];
-            load8<WT>(wk + (size_t)(128 + (tid & 127 & ~7)) * WS, w8);
+            load8<WT>(wkp + (size_t)(128 + (tid & 127 & ~7)) * WS, w8);
             wv = fabsf(w8[tid & 7]);
         }
         wv = group_max<64>(wv);
         if ((tid & 63) == 0) s_kw[tid >> 6] = wv;
     }
+    if (tid < H) {
+        const float m = __uint_as_float(a.vmax[tid]);
+        const float sv = m > 0.0f ? m / 448.0f : 1.0f;
+        s_rv[tid] = 1.0 / (double)sv;
+        if (n == 0) a.sv[tid] = sv;
+    }
     __syncthreads();
     const float s_k = fmaxf(fmaxf(s_kw[0], s_kw[1]), fmaxf(s_kw[2], s_kw[3])) * kKBound;
-    auto v_scale = [&](int h) {
-        const float m = __uint_as_float(a.vmax[h]);
-        return m > 0.0f ? m / 448.0f : 1.0f;
-    };
-    const int H = a.n_heads;
-    if (n == 0 && tid < H) {
-        a.sk[tid] = s_k;
-        a.sv[tid] = v_scale(tid);
-    }
-    const int set = n < a.n_first ? 0 : 1;
-    const int g = tid >> 4;           // 16 groups of 16 lanes
-    const int t = tid & 15;           // dims 8t .. 8t+7 of the head
-    for (int vec = g; vec < 3 * H; vec += 16) {
-        const int which = vec / H;    // 0 q, 1 k, 2 v
-        const int h = vec - which * H;
-        const char* src = which == 0 ? reinterpret_cast<const char*>(a.q) + (size_t)n * a.ld_q * ES
-                        : which == 1 ? reinterpret_cast<const char*>(a.k) + (size_t)n * a.ld_k * ES
-                                     : reinterpret_cast<const char*>(a.v) + (size_t)n * a.ld_v * ES;
+    const double r_k = 1.0 / (double)s_k;
+    if (n == 0 && tid < H) a.sk[tid] = s_k;
+    const char* rows[3] = {reinterpret_cast<const char*>(a.q) + (size_t)n * a.ld_q * ES,
+                           reinterpret_cast<const char*>(a.k) + (size_t)n * a.ld_k * ES,
+                           reinterpret_cast<const char*>(a.v) + (size_t)n * a.ld_v * ES};
+    uint8_t* dst_row = a.qkv8 + (size_t)n * a.ld8;
+    // vectors g, g + 16, ... of the token's 3H (q heads, then k heads, then v heads), as (which, h)
+    int which = 0, h = g;
+    while (which < 3 && h >= H) { h -= H; ++which; }
+    while (which < 3) {
         float y[8];
-        load8<DT>(src + (size_t)(h * 128 + t * 8) * ES, y);
-        float sc;
+        load8<DT>(rows[which] + (size_t)(h * 128 + t * 8) * ES, y);
+        double r;
         if (which < 2) {
-            float w[8];
-            load8<WT>(reinterpret_cast<const char*>(set ? a.qk_w1 : a.qk_w0) + (size_t)(which * 128 + t * 8) * WS, w);
             float ss = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) ss = fmaf(y[i], y[i], ss);
-            ss = group_sum<16>(ss);
-            const float rstd = 1.0f / sqrtf(ss * (1.0f / 128.0f) + a.eps);
+            ss = row16_sum(ss);
+            const float rstd = __builtin_amdgcn_rsqf(ss * (1.0f / 128.0f) + a.eps);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) y[i] = y[i] * rstd * w[i];
+            for (int i = 0; i < 8; ++i) y[i] = y[i] * rstd * (which == 0 ? wq[i] : wk[i]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float c = s_cos[4 * t + i], s = s_sin[4 * t + i];
@@ -419,24 +438,23 @@ __global__ __launch_bounds__(256) void qk_norm_rope_fp8_kernel(QkRopeArgs a) {
                 float m = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(y[i]));
-                m = group_max<16>(m);
-                sc = m > 0.0f ? m / 448.0f : 1.0f;
+                m = row16_max(m);
+                const float sc = m > 0.0f ? m / 448.0f : 1.0f;
                 if (t == 0) a.sq[(size_t)n * H + h] = sc;
+                r = 1.0 / (double)sc;
             } else {
-                sc = s_k;
+                r = r_k;
             }
         } else {
-            sc = v_scale(h);
+            r = s_rv[h];
         }
-        float z[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) z[i] = y[i] / sc;
-        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
-        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], w0, true);
-        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(z[4], z[5], 0, false);
-        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(z[6], z[7], w1, true);
-        uint8_t* dst = a.qkv8 + (size_t)n * a.ld8 + (size_t)which * H * 128 + h * 128 + t * 8;
-        *reinterpret_cast<u32x2_v*>(dst) = u32x2_v{(uint32_t)w0, (uint32_t)w1};
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_rcp(y[0], r), div_by_rcp(y[1], r), 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_rcp(y[2], r), div_by_rcp(y[3], r), w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_rcp(y[4], r), div_by_rcp(y[5], r), 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_rcp(y[6], r), div_by_rcp(y[7], r), w1, true);
+        *reinterpret_cast<u32x2_v*>(dst_row + (which * H + h) * 128 + t * 8) = u32x2_v{(uint32_t)w0, (uint32_t)w1};
+        h += 16;
+        while (which < 3 && h >= H) { h -= H; ++which; }
     }
 }
 
