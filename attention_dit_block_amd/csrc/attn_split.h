@@ -63,23 +63,24 @@ __device__ __forceinline__ void attn_merge_slot(const float4* slot, f32x16_v (&o
     const __amdgpu_buffer_rsrc_t src = sk_slot(slot);
     const uint32_t slot_off = attn_slot_lane(wave, lane);
     const float4 ml = sk_load(src, slot_off + 16 * 64 * 16, 0);
+    // all 16 loads in flight at once: after the key loop only O and a few addresses are live
+    float4 v[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) v[c] = sk_load(src, slot_off + c * 64 * 16, 0);
     const float m_new = fmaxf(m_run, ml.x);
     const float ca = __builtin_amdgcn_exp2f(m_run - m_new), cb = __builtin_amdgcn_exp2f(ml.x - m_new);
     m_run = m_new;
     l_run = fmaf(l_run, ca, ml.y * cb);
-    // 4 loads in flight at a time: O and the pipeline state fill most of the registers
 #pragma unroll
-    for (int eb = 0; eb < 4; ++eb) {
+    for (int eb = 0; eb < 4; ++eb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float4 v = sk_load(src, slot_off + (4 * eb + i) * 64 * 16, 0);
-            o[eb][4 * i] = fmaf(o[eb][4 * i], ca, v.x * cb);
-            o[eb][4 * i + 1] = fmaf(o[eb][4 * i + 1], ca, v.y * cb);
-            o[eb][4 * i + 2] = fmaf(o[eb][4 * i + 2], ca, v.z * cb);
-            o[eb][4 * i + 3] = fmaf(o[eb][4 * i + 3], ca, v.w * cb);
+            const float4 w = v[4 * eb + i];
+            o[eb][4 * i] = fmaf(o[eb][4 * i], ca, w.x * cb);
+            o[eb][4 * i + 1] = fmaf(o[eb][4 * i + 1], ca, w.y * cb);
+            o[eb][4 * i + 2] = fmaf(o[eb][4 * i + 2], ca, w.z * cb);
+            o[eb][4 * i + 3] = fmaf(o[eb][4 * i + 3], ca, w.w * cb);
         }
-        __builtin_amdgcn_sched_barrier(0);
-    }
 }
 
 // stores the state (unnormalised O, running max, running sum) into a slot

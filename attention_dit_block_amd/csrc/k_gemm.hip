@@ -396,19 +396,23 @@ __device__ __forceinline__ int gemm_tile(const GemmBatch& b, char* smem, int L, 
     // adds the fp32 tile in a stream-K slot (partial or carry) to acc
     auto add_slot = [&](const float4* slot) {
         const __amdgpu_buffer_rsrc_t src = sk_slot(slot);
-        // 4 loads in flight at a time: the accumulators already fill the register file
+        // batches of 8 loads, all issued before the batch's adds (written load-then-add, the
+        // scheduler placed each load just before its add and waited for it there: one round trip
+        // past the L2 per float4); the k-loop's operand registers are free by now
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
+            for (int hm = 0; hm < 2; ++hm) {
+                float4 v[8];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int c = (nb * 4 + mb) * 4 + q;
-                    const float4 v = sk_load(src, slot_off, (uint32_t)c * 1024u);
-                    acc[nb][mb][4 * q] += v.x;
-                    acc[nb][mb][4 * q + 1] += v.y;
-                    acc[nb][mb][4 * q + 2] += v.z;
-                    acc[nb][mb][4 * q + 3] += v.w;
+                for (int k = 0; k < 8; ++k) v[k] = sk_load(src, slot_off, (uint32_t)((nb * 4 + 2 * hm) * 4 + k) * 1024u);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int mb = 2 * hm + (k >> 2), q = k & 3;
+                    acc[nb][mb][4 * q] += v[k].x;
+                    acc[nb][mb][4 * q + 1] += v[k].y;
+                    acc[nb][mb][4 * q + 2] += v[k].z;
+                    acc[nb][mb][4 * q + 3] += v[k].w;
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
