@@ -474,11 +474,11 @@ __device__ __forceinline__ int gemm_tile(const GemmBatch& b, char* smem, int L, 
     //      B-row offset within the n-block: 8*(q>>2) + 4*khalf + (q&3).
     const int mlane = lane & 31;
     bool bad = false;              // an fp16 output out of fp16's range
+    if (swiglu) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        const int m = m0 + wm * 128 + mb * 32 + mlane;
-        if (m >= M) continue;
-        if (swiglu) {
+        for (int mb = 0; mb < 4; ++mb) {
+            const int m = m0 + wm * 128 + mb * 32 + mlane;
+            if (m >= M) continue;
 #pragma unroll
             for (int nb = 0; nb < NB / 2; ++nb) {
 #pragma unroll
@@ -497,30 +497,63 @@ __device__ __forceinline__ int gemm_tile(const GemmBatch& b, char* smem, int L, 
                     store4_dt(P.C, (size_t)m * P.ldc + col, P.c_dtype, f);
                 }
             }
-        } else {
+        }
+    } else {
+        // Store (and gated residual): the types are dispatched once, outside the row loop, and a
+        // row's residual loads are all issued before its first store -- with a type switch or a
+        // bounds test around each load, every load was followed by a wait at the branch's join,
+        // one round trip per 4 outputs.  Loads clamp their row and column into the problem (N is
+        // a multiple of 8); the stores test them.
+        const bool res = epi == EPI_GATED_RES;
+        auto rows = [&]<int RT, int CT>() {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
+            for (int mb = 0; mb < 4; ++mb) {
+                const int m = m0 + wm * 128 + mb * 32 + mlane;
+                const char* rrow = reinterpret_cast<const char*>(P.R) + (size_t)min(m, M - 1) * P.ldr * ESize<RT>::v;
+                char* crow = reinterpret_cast<char*>(P.C) + (size_t)m * P.ldc * ESize<CT>::v;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int col = n0 + wn * WNR + nb * 32 + 8 * i + 4 * khalf;
-                    if (col >= P.N) continue;
-                    float o[4];
+                for (int nb = 0; nb < NB; ++nb) {
+                    float r[4][4];
+                    f32x4_v gate[4];
+                    if (res) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) o[j] = acc[nb][mb][4 * i + j];
-                    if (epi == EPI_GATED_RES) {
-                        const f32x4_v gt = ldf4(P.gate + col);
-                        float r[4];
-                        const size_t roff = (size_t)m * P.ldr + col;
-                        if (P.r_dtype == BF16) load4<BF16>(reinterpret_cast<const char*>(P.R) + roff * 2, r);
-                        else load4<F32>(reinterpret_cast<const char*>(P.R) + roff * 4, r);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) o[j] = fmaf(gt[j], o[j], r[j]);
+                        for (int i = 0; i < 4; ++i) {
+                            const int col = min(n0 + wn * WNR + nb * 32 + 8 * i + 4 * khalf, P.N - 4);
+                            gate[i] = ldf4(P.gate + col);
+                            load4<RT>(rrow + (size_t)col * ESize<RT>::v, r[i]);
+                        }
                     }
-                    if (P.c_dtype == F16)
-                        bad |= f16_out_of_range4(o);
-                    store4_dt(P.C, (size_t)m * P.ldc + col, P.c_dtype, o);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int col = n0 + wn * WNR + nb * 32 + 8 * i + 4 * khalf;
+                        float o[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            o[j] = res ? fmaf(gate[i][j], acc[nb][mb][4 * i + j], r[i][j]) : acc[nb][mb][4 * i + j];
+                        if (m < M && col < P.N) {
+                            if constexpr (CT == F16) bad |= f16_out_of_range4(o);
+                            store4<CT>(crow + (size_t)col * ESize<CT>::v, o);
+                        }
+                    }
+                    // the next batch's loads stay below this one's stores (hoisted, they raised
+                    // the register pressure past the file)
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
+        };
+        // gated residual outputs are F32 or BF16 (h, y), store outputs F32, F16 or BF16
+        if (res) {
+            if (P.r_dtype == BF16) {
+                if (P.c_dtype == BF16) rows.template operator()<BF16, BF16>();
+                else rows.template operator()<BF16, F32>();
+            } else {
+                if (P.c_dtype == BF16) rows.template operator()<F32, BF16>();
+                else rows.template operator()<F32, F32>();
+            }
+        } else {
+            if (P.c_dtype == F32) rows.template operator()<F32, F32>();
+            else if (P.c_dtype == F16) rows.template operator()<F32, F16>();
+            else rows.template operator()<F32, BF16>();
         }
     }
     raise_range_flag(b.range_flag, bad);
@@ -715,6 +748,10 @@ hipError_t launch_gemm(GemmBatch& b, hipStream_t s) {
             P.tiles_n = (P.N + FBN - 1) / FBN;
         }
         if (P.M == 0) P.tiles_m = 0;
+        // the MFMA epilogue handles gated-residual outputs of F32 or BF16 over BF16 or F32 residuals
+        if (mfma && P.epi == EPI_GATED_RES && P.M > 0 &&
+            ((P.c_dtype != F32 && P.c_dtype != BF16) || (P.r_dtype != F32 && P.r_dtype != BF16)))
+            return hipErrorInvalidValue;
         // the MFMA kernel addresses a tile's rows by 32-bit byte offsets from the tile's first row
         if (mfma && P.M > 0 && (P.lda >= kGemmMaxLd || P.ldb >= kGemmMaxLd)) return hipErrorInvalidValue;
         P.tile_begin = total;
