@@ -47,12 +47,14 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
     // (nontemporal: every weight is read once)
     const int iters = (b.d_cond + 64 * kElems - 1) / (64 * kElems);
     u32x4_v w[kGemvRowsPerWave], wn[kGemvRowsPerWave];
+    // (loads clamped into the row, d_cond >= 8 and a multiple of 8; a lane past the row's end skips
+    // the sums below.  Loaded under a per-lane branch or zeroed right after, each slice waited for
+    // its loads at once, and the next slice's loads no longer overlapped this one's sums.)
     auto load = [&](u32x4_v* dst, int it) {
-        const int k0 = (it * 64 + lane) * kElems;
+        const int kc = min((it * 64 + lane) * kElems, b.d_cond - kElems);
 #pragma unroll
         for (int r = 0; r < kGemvRowsPerWave; ++r)
-            dst[r] = k0 < b.d_cond ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_v*>(wrow[r] + (size_t)k0 * kES))
-                                  : u32x4_v{0u, 0u, 0u, 0u};
+            dst[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_v*>(wrow[r] + (size_t)kc * kES));
     };
     load(w, 0);       // the first slice's HBM latency overlaps the SiLU(c) staging below
     // SiLU(c) in LDS, interleaved so that the float4s a lane needs for one slice sit 16 bytes
@@ -90,8 +92,7 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
     }
     __syncthreads();
 
-    for (int it = 0; it < iters; ++it) {
-        if (it + 1 < iters) load(wn, it + 1);
+    auto sums = [&](const u32x4_v* wv, int it) {
         const int k0 = (it * 64 + lane) * kElems;
         if (k0 < b.d_cond) {
             float sa[8];
@@ -106,17 +107,33 @@ __global__ __launch_bounds__(256) void adaln_gemv_kernel(GemvBatch b) {
                 if (DT == BF16) {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        acc[r] = fmaf(bf_lo(w[r][t]), sa[2 * t], acc[r]);
-                        acc[r] = fmaf(bf_hi(w[r][t]), sa[2 * t + 1], acc[r]);
+                        acc[r] = fmaf(bf_lo(wv[r][t]), sa[2 * t], acc[r]);
+                        acc[r] = fmaf(bf_hi(wv[r][t]), sa[2 * t + 1], acc[r]);
                     }
                 } else {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) acc[r] = fmaf(__uint_as_float(w[r][t]), sa[t], acc[r]);
+                    for (int t = 0; t < 4; ++t) acc[r] = fmaf(__uint_as_float(wv[r][t]), sa[t], acc[r]);
                 }
             }
         }
-#pragma unroll
-        for (int r = 0; r < kGemvRowsPerWave; ++r) w[r] = wn[r];
+    };
+    // Two buffers in alternating roles, and no load under a branch inside the loop: a copy from the
+    // prefetch buffer into the working one at the end of each slice, or a conditional prefetch
+    // (whose two paths leave different loads outstanding), made every slice wait for the next
+    // slice's loads.
+    int it = 0;
+    for (; it + 2 < iters; it += 2) {
+        load(wn, it + 1);
+        sums(w, it);
+        load(w, it + 2);
+        sums(wn, it + 1);
+    }
+    if (it + 1 < iters) {
+        load(wn, it + 1);
+        sums(w, it);
+        sums(wn, it + 1);
+    } else {
+        sums(w, it);
     }
 #pragma unroll
     for (int r = 0; r < kGemvRowsPerWave; ++r) {
@@ -166,17 +183,19 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
     const char* xrow = reinterpret_cast<const char*>(P.x) + (size_t)min(r, P.rows - 1) * P.ld_x * ESize<XT>::v;
     char* orow = reinterpret_cast<char*>(P.out) + (size_t)r * P.ld_out * ESize<OT>::v;
 
+    // every chunk's load issued unconditionally (column clamped into the row, d >= 8 and a multiple
+    // of 8; rows past the problem read its last row), chunks past d zeroed after the loads: a load
+    // under a per-chunk branch waited at the branch's join, one round trip per chunk
     float v[NC][8];
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-        const int c = (lane + 64 * i) * 8;        // first element of this 8-element chunk
-        if (active && c < d) {
-            load8<XT>(xrow + (size_t)c * ESize<XT>::v, v[i]);
-        } else {
+    for (int i = 0; i < NC; ++i)
+        load8<XT>(xrow + (size_t)min((lane + 64 * i) * 8, d - 8) * ESize<XT>::v, v[i]);
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+        if ((lane + 64 * i) * 8 >= d) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) v[i][t] = 0.0f;
         }
-    }
     for (int c = threadIdx.x * 4; c < d; c += 1024) {
         stf4(s_mod + c, ldf4(P.shift + c));
         stf4(s_mod + d + c, ldf4(P.scale + c));
