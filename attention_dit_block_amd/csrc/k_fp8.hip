@@ -196,61 +196,99 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_kernel(Fp8GemmBatch bt) {
     // + 8 (q >> 2) + 4 h + (q & 3) of the tile
     bool bad = false;              // an fp16 output out of fp16's range
     float vm = 0.0f;               // EPI_STORE with vmax: largest |stored value| of this lane
+    // Output type CT and residual type RT dispatched once per tile; each 32-column block's scale,
+    // gate and residual loads issue together before its stores, rows and columns clamped into the
+    // problem (N is a multiple of 8) and the stores tested -- under a type switch or a bounds test
+    // each load waited at the branch's join, one round trip per 4 outputs.
+    auto tile_out = [&]<int CT, int RT>() {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
-        if (m >= g.M) continue;
-        const float sa = g.sa[m];
-        if constexpr (kSwiglu) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int col = n0 + wn * 32 + 8 * i + 4 * h;
-                if (col >= g.N) continue;
-                const f32x4_v sg = ldf4(g.sb + col), su = ldf4(g.sb + g.up_off + col);
-                float o[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    o[j] = silu_f8(acc[0][mb][4 * i + j] * sa * sg[j]) * (acc[1][mb][4 * i + j] * sa * su[j]);
-                if (g.c_dtype == F16)
-                    bad |= f16_out_of_range4(o);
-                store4_any(g.c, (size_t)m * g.ldc + col, g.c_dtype, o);
-            }
-        } else {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+        for (int mb = 0; mb < 4; ++mb) {
+            const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
+            const int mc = min(m, g.M - 1);
+            const float sa = g.sa[mc];
+            char* crow = reinterpret_cast<char*>(g.c) + (size_t)m * g.ldc * ESize<CT>::v;
+            if constexpr (kSwiglu) {
+                f32x4_v sg[4], su[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int col = n0 + wn * 64 + nb * 32 + 8 * i + 4 * h;
-                    if (col >= g.N) continue;
-                    const f32x4_v sb = ldf4(g.sb + col);
+                    const int cc = min(n0 + wn * 32 + 8 * i + 4 * h, g.N - 4);
+                    sg[i] = ldf4(g.sb + cc);
+                    su[i] = ldf4(g.sb + g.up_off + cc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int col = n0 + wn * 32 + 8 * i + 4 * h;
                     float o[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) o[j] = acc[nb][mb][4 * i + j] * sa * sb[j];
-                    if constexpr (MODE == EPI_GATED_RES) {
-                        const f32x4_v gt = ldf4(g.gate + col);
-                        float r[4];
-                        const size_t roff = (size_t)m * g.ldr + col;
-                        if (g.r_dtype == BF16) load4<BF16>(reinterpret_cast<const char*>(g.r) + roff * 2, r);
-                        else load4<F32>(reinterpret_cast<const char*>(g.r) + roff * 4, r);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) o[j] = fmaf(gt[j], o[j], r[j]);
+                    for (int j = 0; j < 4; ++j)
+                        o[j] = silu_f8(acc[0][mb][4 * i + j] * sa * sg[i][j]) * (acc[1][mb][4 * i + j] * sa * su[i][j]);
+                    if (m < g.M && col < g.N) {
+                        if constexpr (CT == F16) bad |= f16_out_of_range4(o);
+                        store4<CT>(crow + (size_t)col * ESize<CT>::v, o);
                     }
-                    if (g.c_dtype == F16)
-                        bad |= f16_out_of_range4(o);
-                    if constexpr (MODE == EPI_STORE) {
-                        if (bt.vmax) {
+                }
+            } else {
+                const char* rrow = MODE == EPI_GATED_RES
+                                       ? reinterpret_cast<const char*>(g.r) + (size_t)mc * g.ldr * ESize<RT>::v
+                                       : nullptr;
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                // the value as stored (the QK-norm + RoPE pass quantises that)
-                                const float st = g.c_dtype == F16 ? (float)(_Float16)o[j]
-                                               : g.c_dtype == BF16 ? bf_lo(pack_bf16x2(o[j], 0.0f)) : o[j];
-                                vm = fmaxf(vm, fabsf(st));
-                            }
+                for (int hb = 0; hb < 2 * NB; ++hb) {      // 16-column halves of the 32-column blocks
+                    const int nb = hb >> 1, i0 = 2 * (hb & 1);
+                    f32x4_v sb[4], gt[4];
+                    float r[4][4];
+#pragma unroll
+                    for (int i = i0; i < i0 + 2; ++i) {
+                        const int cc = min(n0 + wn * 64 + nb * 32 + 8 * i + 4 * h, g.N - 4);
+                        sb[i] = ldf4(g.sb + cc);
+                        if constexpr (MODE == EPI_GATED_RES) {
+                            gt[i] = ldf4(g.gate + cc);
+                            load4<RT>(rrow + (size_t)cc * ESize<RT>::v, r[i]);
                         }
                     }
-                    store4_any(g.c, (size_t)m * g.ldc + col, g.c_dtype, o);
+#pragma unroll
+                    for (int i = i0; i < i0 + 2; ++i) {
+                        const int col = n0 + wn * 64 + nb * 32 + 8 * i + 4 * h;
+                        float o[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) o[j] = acc[nb][mb][4 * i + j] * sa * sb[i][j];
+                        if constexpr (MODE == EPI_GATED_RES) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) o[j] = fmaf(gt[i][j], o[j], r[i][j]);
+                        }
+                        if (m < g.M && col < g.N) {
+                            if constexpr (CT == F16) bad |= f16_out_of_range4(o);
+                            if constexpr (MODE == EPI_STORE) {
+                                if (bt.vmax) {
+#pragma unroll
+                                    for (int j = 0; j < 4; ++j) {
+                                        // the value as stored (the QK-norm + RoPE pass quantises that)
+                                        const float st = CT == F16 ? (float)(_Float16)o[j]
+                                                       : CT == BF16 ? bf_lo(pack_bf16x2(o[j], 0.0f)) : o[j];
+                                        vm = fmaxf(vm, fabsf(st));
+                                    }
+                                }
+                            }
+                            store4<CT>(crow + (size_t)col * ESize<CT>::v, o);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+            }
         }
+    };
+    if constexpr (MODE == EPI_GATED_RES) {
+        // gated-residual outputs are F32 or BF16 over BF16 or F32 residuals (checked on the host)
+        if (g.r_dtype == BF16) {
+            if (g.c_dtype == BF16) tile_out.template operator()<BF16, BF16>();
+            else tile_out.template operator()<F32, BF16>();
+        } else {
+            if (g.c_dtype == BF16) tile_out.template operator()<BF16, F32>();
+            else tile_out.template operator()<F32, F32>();
+        }
+    } else {
+        if (g.c_dtype == F32) tile_out.template operator()<F32, F32>();
+        else if (g.c_dtype == F16) tile_out.template operator()<F16, F32>();
+        else tile_out.template operator()<BF16, F32>();
     }
     raise_range_flag(bt.range_flag, bad);
     if constexpr (MODE == EPI_STORE) {
@@ -271,6 +309,9 @@ hipError_t launch_gemm_fp8(Fp8GemmBatch& bt, hipStream_t s) {
     for (int i = 0; i < bt.n; ++i) {
         Fp8GemmProblem& g = bt.p[i];
         const bool sw = g.epi == EPI_SWIGLU;
+        if (g.M > 0 && g.epi == EPI_GATED_RES &&
+            ((g.c_dtype != F32 && g.c_dtype != BF16) || (g.r_dtype != F32 && g.r_dtype != BF16)))
+            return hipErrorInvalidValue;
         g.tiles_m = g.M > 0 ? (g.M + QBM - 1) / QBM : 0;
         g.tiles_n = sw ? (g.N + QBN / 2 - 1) / (QBN / 2) : (g.N + QBN - 1) / QBN;
         g.tile_begin = total;
