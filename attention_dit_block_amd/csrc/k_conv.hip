@@ -168,7 +168,22 @@ __device__ __forceinline__ void conv_body(const ConvArgs& a, char* smem) {
     }
 
     // epilogue: acc[nb][mb][q] -> pixel m0 + wm*MB*32 + mb*32 + (lane & 31), channel
-    // n0 + wn*NB*32 + nb*32 + 8 (q >> 2) + 4 h + (q & 3)
+    // n0 + wn*NB*32 + nb*32 + 8 (q >> 2) + 4 h + (q & 3).  With Cout a multiple of 4 the bias of the
+    // lane's columns is loaded once, up front (clamped into Cout; loaded per store group under the
+    // bounds test, each load waited at the branch's join).
+    const bool c4 = (a.Cout & 3) == 0;
+    f32x4_v bv[NB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bv[nb][i] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+    if (c4 && a.bias) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                bv[nb][i] = ldf4(a.bias + min(n0 + wn * (NB * 32) + nb * 32 + 8 * i + 4 * h, a.Cout - 4));
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int m = m0 + wm * (MB * 32) + mb * 32 + (lane & 31);
@@ -183,12 +198,9 @@ __device__ __forceinline__ void conv_body(const ConvArgs& a, char* smem) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) o[j] = acc[nb][mb][4 * i + j];
                 char* yp = reinterpret_cast<char*>(a.y) + ((size_t)m * a.Cout + col) * (OT == F32 ? 4 : 2);
-                if ((a.Cout & 3) == 0) {
-                    if (a.bias) {
-                        const f32x4_v bv = ldf4(a.bias + col);
+                if (c4) {
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) o[j] += bv[j];
-                    }
+                    for (int j = 0; j < 4; ++j) o[j] += bv[nb][i][j];
                     store4<OT>(yp, o);
                 } else {
 #pragma unroll
@@ -286,41 +298,52 @@ __global__ __launch_bounds__(512, 2) void conv_direct_kernel(ConvArgs a) {
             if (c < nwin * 4) *reinterpret_cast<u32x4_v*>(win + (c >> 2) * kDirPix + (c & 3) * 16) = v[r];
         }
         __syncthreads();
-        // weight fragment of tap k, k16 step ks: row wr, channels c0 + 16 ks + 8 h .. +7
+        // weight fragment of tap k, k16 step ks: row wr, channels c0 + 16 ks + 8 h .. +7, the row and
+        // channel clamped into the weights (rows past Cout feed outputs that are not stored; channels
+        // past Cin meet the window's zeros), so every load is unconditional
+        const bf16_t* wrow = Wt + (long)min(wr, a.Cout - 1) * K;
         auto wfrag = [&](int k, int ks) -> u32x4_v {
-            const int ch = c0 + 16 * ks + 8 * h;
-            if (wr < a.Cout && ch < a.Cin) return ld16(Wt + (long)wr * K + (long)k * a.Cin + ch);
-            return u32x4_v{0u, 0u, 0u, 0u};
+            return ld16(wrow + (long)k * a.Cin + min(c0 + 16 * ks + 8 * h, a.Cin - 8));
         };
-        // taps frame by frame, row by row (no division in the loop), the next tap's weight
-        // fragments loaded while this one runs
-        u32x4_v wb0 = wfrag(0, 0), wb1 = wfrag(0, 1);
-        int k = 0;
-        for (int sf = 0; sf < a.KT; ++sf)
-            for (int i = 0; i < a.KH; ++i) {
-                const char* rowp = win + ((sf * TH2 + py + i) * TW2 + px) * kDirPix + 16 * h;
-                for (int j = 0; j < a.KW; ++j, ++k) {
-                    u32x4_v nb0 = wb0, nb1 = wb1;
-                    if (k + 1 < taps) { nb0 = wfrag(k + 1, 0); nb1 = wfrag(k + 1, 1); }
-                    const u32x4_v fa0 = *reinterpret_cast<const u32x4_v*>(rowp + j * kDirPix);
-                    const u32x4_v fa1 = *reinterpret_cast<const u32x4_v*>(rowp + j * kDirPix + 32);
-                    acc = cmfma<BF16>(wb0, fa0, acc);
-                    acc = cmfma<BF16>(wb1, fa1, acc);
-                    wb0 = nb0; wb1 = nb1;
-                }
+        // taps frame by frame, row by row (no division in the loop), two taps per pass with the
+        // weight fragments in two register pairs of alternating roles: each pair loads while the
+        // other pair's tap runs (one pair copied into the other after every tap, or loaded under
+        // a branch, made every tap wait for the next tap's weights)
+        int sf = 0, ti = 0, tj = 0;                    // the next tap to run
+        auto run_tap = [&](const u32x4_v& w0, const u32x4_v& w1) {
+            const char* p = win + ((sf * TH2 + py + ti) * TW2 + px + tj) * kDirPix + 16 * h;
+            const u32x4_v fa0 = *reinterpret_cast<const u32x4_v*>(p);
+            const u32x4_v fa1 = *reinterpret_cast<const u32x4_v*>(p + 32);
+            acc = cmfma<BF16>(w0, fa0, acc);
+            acc = cmfma<BF16>(w1, fa1, acc);
+            if (++tj == a.KW) {
+                tj = 0;
+                if (++ti == a.KH) { ti = 0; ++sf; }
             }
+        };
+        u32x4_v wa0 = wfrag(0, 0), wa1 = wfrag(0, 1);
+        for (int k = 0; k < taps; k += 2) {
+            const int k1 = min(k + 1, taps - 1), k2 = min(k + 2, taps - 1);
+            const u32x4_v wb0 = wfrag(k1, 0), wb1 = wfrag(k1, 1);
+            run_tap(wa0, wa1);
+            wa0 = wfrag(k2, 0);
+            wa1 = wfrag(k2, 1);
+            if (k + 1 < taps) run_tap(wb0, wb1);
+        }
     }
 
     // acc[q] -> pixel pp, output channel 8 (q >> 2) + 4 h + (q & 3)
     const int yo = y0 + py, xo = x0 + px;
     if (yo >= a.H || xo >= a.W) return;
     const long m = (((long)b * a.T + t) * a.H + yo) * a.W + xo;
+    float bias[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) bias[q] = a.bias ? a.bias[min(8 * (q >> 2) + 4 * h + (q & 3), a.Cout - 1)] : 0.0f;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int co = 8 * (q >> 2) + 4 * h + (q & 3);
         if (co < a.Cout)
-            store1<OT>(reinterpret_cast<char*>(a.y) + (m * a.Cout + co) * (OT == F32 ? 4 : 2),
-                       acc[q] + (a.bias ? a.bias[co] : 0.0f));
+            store1<OT>(reinterpret_cast<char*>(a.y) + (m * a.Cout + co) * (OT == F32 ? 4 : 2), acc[q] + bias[q]);
     }
 }
 
