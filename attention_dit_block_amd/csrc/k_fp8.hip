@@ -23,6 +23,68 @@ namespace dit {
 
 constexpr float kE4M3Max = 448.0f;
 
+// One wave per row.  x / s goes through the double reciprocal of s: the double product is within
+// 2^-52 (relative) of the quotient, and a quotient of two fp32 values in the normal range lies more
+// than 2^-49 from every midpoint between neighbouring fp32 values, so the product rounds to the
+// correctly rounded quotient (results below the normal range are e4m3 zeros of the same sign either
+// way) -- three instructions instead of a division's ten.
+__device__ __forceinline__ float div_by_rcp8(float x, double r) { return (float)((double)x * r); }
+
+template <int XT>
+__device__ __forceinline__ void quant_store8(uint8_t* dst, const float* f, double r) {
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_rcp8(f[0], r), div_by_rcp8(f[1], r), 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_rcp8(f[2], r), div_by_rcp8(f[3], r), w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_rcp8(f[4], r), div_by_rcp8(f[5], r), 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_rcp8(f[6], r), div_by_rcp8(f[7], r), w1, true);
+    *reinterpret_cast<u32x2_v*>(dst) = u32x2_v{(uint32_t)w0, (uint32_t)w1};
+}
+
+// 16-bit rows of up to 512 * NC columns: the row is loaded once, all its chunks in flight together
+// (columns clamped into the row, cols >= 8 and a multiple of 8), and kept packed in registers
+// between the max and the codes.
+template <int XT, int NC>
+__global__ __launch_bounds__(256) void quantize_fp8_rows_kernel(const void* x, long ld_x, int rows, int cols,
+                                                                uint8_t* q, long ld_q, float* scales) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + wave;
+    if (r >= rows) return;
+    const char* xr = reinterpret_cast<const char*>(x) + (size_t)r * ld_x * 2;
+    u32x4_v raw[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+        raw[i] = *reinterpret_cast<const u32x4_v*>(xr + (size_t)min((lane + 64 * i) * 8, cols - 8) * 2);
+    auto unpack = [&](const u32x4_v& w, float* f) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) unpack2<XT>(w[t], f[2 * t], f[2 * t + 1]);
+    };
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        if ((lane + 64 * i) * 8 < cols) {
+            float f[8];
+            unpack(raw[i], f);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    const float s = amax > 0.0f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
+    if (lane == 0) scales[r] = s;
+    const double rs = 1.0 / (double)s;
+    uint8_t* qr = q + (size_t)r * ld_q;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int k0 = (lane + 64 * i) * 8;
+        if (k0 < cols) {
+            float f[8];
+            unpack(raw[i], f);
+            quant_store8<XT>(qr + k0, f, rs);
+        }
+    }
+}
+
+// Any row length and fp32 rows: two passes over the row, four chunks in flight per pass step.
 template <int XT>
 __global__ __launch_bounds__(256) void quantize_fp8_kernel(const void* x, long ld_x, int rows, int cols, uint8_t* q,
                                                            long ld_q, float* scales) {
@@ -31,38 +93,54 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const void* x, long l
     if (r >= rows) return;
     constexpr int XS = XT == F32 ? 4 : 2;
     const char* xr = reinterpret_cast<const char*>(x) + (size_t)r * ld_x * XS;
-    float f[8];
     float amax = 0.0f;
-    for (int k0 = lane * 8; k0 < cols; k0 += 512) {
-        load8<XT>(xr + (size_t)k0 * XS, f);
+    for (int k0 = lane * 8; k0 < cols; k0 += 4 * 512) {
+        float f[4][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+        for (int u = 0; u < 4; ++u) load8<XT>(xr + (size_t)min(k0 + 512 * u, cols - 8) * XS, f[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (k0 + 512 * u < cols) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[u][j]));
+            }
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
     const float s = amax > 0.0f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
     if (lane == 0) scales[r] = s;
+    const double rs = 1.0 / (double)s;
     uint8_t* qr = q + (size_t)r * ld_q;
-    for (int k0 = lane * 8; k0 < cols; k0 += 512) {
-        load8<XT>(xr + (size_t)k0 * XS, f);
-        float y[8];
+    for (int k0 = lane * 8; k0 < cols; k0 += 4 * 512) {
+        float f[4][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) y[j] = __fdiv_rn(f[j], s);
-        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
-        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
-        const u32x2_v w = {(uint32_t)w0, (uint32_t)w1};
-        *reinterpret_cast<u32x2_v*>(qr + k0) = w;
+        for (int u = 0; u < 4; ++u) load8<XT>(xr + (size_t)min(k0 + 512 * u, cols - 8) * XS, f[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (k0 + 512 * u < cols) quant_store8<XT>(qr + k0 + 512 * u, f[u], rs);
     }
+}
+
+template <int XT>
+static void launch_quant_rows(const void* x, long ld_x, int rows, int cols, uint8_t* q, long ld_q, float* scales,
+                              hipStream_t s, dim3 grid) {
+    const int nc = (cols + 511) / 512;
+    if (nc <= 2) hipLaunchKernelGGL((quantize_fp8_rows_kernel<XT, 2>), grid, dim3(256), 0, s, x, ld_x, rows, cols, q, ld_q, scales);
+    else if (nc <= 6) hipLaunchKernelGGL((quantize_fp8_rows_kernel<XT, 6>), grid, dim3(256), 0, s, x, ld_x, rows, cols, q, ld_q, scales);
+    else if (nc <= 12) hipLaunchKernelGGL((quantize_fp8_rows_kernel<XT, 12>), grid, dim3(256), 0, s, x, ld_x, rows, cols, q, ld_q, scales);
+    else if (nc <= 18) hipLaunchKernelGGL((quantize_fp8_rows_kernel<XT, 18>), grid, dim3(256), 0, s, x, ld_x, rows, cols, q, ld_q, scales);
+    else hipLaunchKernelGGL((quantize_fp8_rows_kernel<XT, 24>), grid, dim3(256), 0, s, x, ld_x, rows, cols, q, ld_q, scales);
 }
 
 hipError_t launch_quantize_fp8(const void* x, int x_dtype, long ld_x, int rows, int cols, uint8_t* q, long ld_q,
                                float* scales, hipStream_t s) {
     if (rows == 0) return hipSuccess;
     const dim3 grid((rows + 3) / 4), block(256);
+    const bool in_regs = cols <= 512 * 24;
     if (x_dtype == F32) hipLaunchKernelGGL((quantize_fp8_kernel<F32>), grid, block, 0, s, x, ld_x, rows, cols, q, ld_q, scales);
+    else if (x_dtype == F16 && in_regs) launch_quant_rows<F16>(x, ld_x, rows, cols, q, ld_q, scales, s, grid);
     else if (x_dtype == F16) hipLaunchKernelGGL((quantize_fp8_kernel<F16>), grid, block, 0, s, x, ld_x, rows, cols, q, ld_q, scales);
+    else if (in_regs) launch_quant_rows<BF16>(x, ld_x, rows, cols, q, ld_q, scales, s, grid);
     else hipLaunchKernelGGL((quantize_fp8_kernel<BF16>), grid, block, 0, s, x, ld_x, rows, cols, q, ld_q, scales);
     return hipGetLastError();
 }

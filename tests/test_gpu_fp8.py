@@ -21,7 +21,12 @@ def dit():
     return m
 
 
-@pytest.mark.parametrize("dtype, rows, cols", [("bf16", 64, 3072), ("f16", 37, 200), ("f32", 10, 9216)])
+@pytest.mark.parametrize("dtype, rows, cols", [("bf16", 64, 3072), ("f16", 37, 200), ("f32", 10, 9216),
+                                               # rows kept in registers: the FFN-down input, the single
+                                               # block's linear2 input (d + F), one-chunk rows
+                                               ("f16", 20, 9216), ("bf16", 9, 12288), ("f16", 3, 8),
+                                               # longer 16-bit rows and ragged fp32 rows: two passes
+                                               ("bf16", 7, 13320), ("f32", 7, 1000)])
 def test_quantize_matches_oracle_bit_for_bit(dit, dtype, rows, cols):
     x = di.draw((rows, cols), 1.0, dtype, 51, "x")
     xf = o.widen(x, dtype).astype(np.float32)
