@@ -143,7 +143,7 @@ int validate_config(const dit_block_config* c) {
 
 // Workspace plan: 256-byte aligned sub-buffers.
 struct WsPlan {
-    size_t flags, mod, act, qkv, o, h, f, of, sk, sk_bytes, ask, ask_bytes, a8, a8s, q8, sq, total;
+    size_t flags, mod, act, qkv, o, h, f, of, cs, cs_bytes, sk, sk_bytes, ask, ask_bytes, a8, a8s, q8, sq, total;
 };
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 WsPlan plan_workspace(const dit_block_config* c, int single, bool fp8 = false) {
@@ -159,6 +159,10 @@ WsPlan plan_workspace(const dit_block_config* c, int single, bool fp8 = false) {
         p.o = take(n * d * es);
         p.h = take(n * d * 4);
         p.f = take(n * F * es);
+        // the rotation angles' (cos, sin) per token for the QKV product's fused QK RMSNorm + RoPE
+        // (16-bit path, every 256-column tile two whole heads)
+        p.cs_bytes = !fp8 && c->dtype == DIT_BF16 && d % 256 == 0 ? n * 64 * 2 * 4 : 0;
+        p.cs = take(p.cs_bytes);
     } else {
         p.mod = take(3 * d * 4);
         p.act = take(n * d * es);
@@ -480,7 +484,9 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
         return P;
     };
 
-    // 3. qkv = a W_qkv^T
+    // 3. qkv = a W_qkv^T; in the 16-bit path with whole heads per tile, QK RMSNorm + RoPE in its
+    //    epilogue, from a table of the angles' (cos, sin) computed first
+    const bool fuse_rope = !fp8 && W.cs_bytes > 0;
     if (fp8) {
         Fp8GemmBatch b{};
         if (nt) b.p[b.n++] = fp8_problem(0, nt, d, t8->w_qkv, t8->s_qkv, qkv, 3L * d, c.act_dtype, 3 * d, EPI_STORE);
@@ -502,10 +508,20 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
                              nullptr, 0, 0, nullptr, 0, ni, 3 * d, d, EPI_STORE};
         gq.n = k;
     }
+    if (fuse_rope) {
+        float* cs = reinterpret_cast<float*>(ws + W.cs);
+        RopeTable tab;
+        DIT_TRY(build_rope_table(c.head_dim, c.n_axes, c.axes_dim, c.theta, tab));
+        DIT_TRY(launch("rope_table", s, [&] { return launch_rope_table(pos, n, c.n_axes, tab, cs, s); }));
+        gq.rope_cs = cs; gq.rope_d = d; gq.rope_eps = c.eps_qk;
+        int k = 0;
+        if (nt) { gq.rope_w[k] = qkw_t; gq.rope_row0[k++] = 0; }
+        if (ni) { gq.rope_w[k] = qkw_i; gq.rope_row0[k++] = nt; }
+    }
     DIT_TRY(launch("gemm_qkv", s, [&] { return launch_gemm(gq, s); }));
     }
 
-    // 4. QK RMSNorm + RoPE in place (text rows use the text weights)
+    // 4. QK RMSNorm + RoPE in place (text rows use the text weights), unless fused above
     QkRopeArgs r{};
     DIT_TRY(build_rope_table(c.head_dim, c.n_axes, c.axes_dim, c.theta, r.tab));
     r.q = qkv; r.ld_q = 3L * d; r.k = qkv + (size_t)d * es; r.ld_k = 3L * d;
@@ -516,7 +532,8 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
         r.qkv8 = a8; r.ld8 = 3L * d; r.sq = a8_sq; r.sk = a8_sk; r.sv = a8_sv;
         r.v = qkv + (size_t)2 * d * es; r.ld_v = 3L * d; r.vmax = a8_vmax;
     }
-    DIT_TRY(launch(fp8 ? "qk_rmsnorm_rope_fp8" : "qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(r, s); }));
+    if (!fuse_rope)
+        DIT_TRY(launch(fp8 ? "qk_rmsnorm_rope_fp8" : "qk_rmsnorm_rope", s, [&] { return launch_qk_rmsnorm_rope(r, s); }));
 
     // 5. O = joint attention over all n tokens
     if (fp8) {

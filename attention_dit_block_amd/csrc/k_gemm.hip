@@ -119,6 +119,67 @@ __device__ __forceinline__ unsigned* sk_flag(const GemmBatch& b, int g) {
                                                  (size_t)2 * b.sk_grid * kPartialF4) + g;
 }
 
+// QK RMSNorm + 4-axis RoPE on the fp32 accumulators of a q or k tile of the QKV product, before they
+// are stored (the separate pass's arithmetic on the unrounded products: per-head mean square, rsq,
+// times the norm weight, then each interleaved pair rotated by the (cos, sin) of its angle from
+// the token's row of the angle table).  Wave (wm, wn) holds rows wm*128 + mb*32 + lane%32 and
+// columns wn*64 + nb*32 + 8 i + 4 (lane/32) + j of the tile; a head's 128 columns are waves wn and
+// wn ^ 1, whose partial sums of squares meet in LDS, where the tile's 128 norm weights wait too.
+__device__ __forceinline__ void qk_rope_tile(const GemmBatch& b, int pi, char* smem, f32x16_v (&acc)[2][4], int m0,
+                                             int n0, int M, int wm, int wn, int lane) {
+    const int khalf = lane >> 5, mlane = lane & 31;
+    const int which = n0 >= b.rope_d ? 1 : 0;        // q or k
+    const int hd0 = (wn & 1) * 64;                   // this wave's first dimension of the head
+    float ss[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        float s = 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) s = fmaf(acc[nb][mb][q], acc[nb][mb][q], s);
+        ss[mb] = s + __shfl_xor(s, 32, kWave);
+    }
+    __syncthreads();                                 // every wave is done with the last stage
+    float* red = reinterpret_cast<float*>(smem);     // [2 wm][4 wn][128 rows], then the 128 weights
+    if (khalf == 0) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) red[(wm * 4 + wn) * 128 + mb * 32 + mlane] = ss[mb];
+    }
+    const int tid = (wm * 4 + wn) * 64 + lane;
+    if (tid < 128) red[1024 + tid] = bf_lo(reinterpret_cast<const uint16_t*>(b.rope_w[pi])[which * 128 + tid]);
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) ss[mb] += red[(wm * 4 + (wn ^ 1)) * 128 + mb * 32 + mlane];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int tok = b.rope_row0[pi] + min(m0 + wm * 128 + mb * 32 + mlane, M - 1);
+        const float* crow = b.rope_cs + (size_t)tok * 128;
+        // the row's 16 pairs: (cos, sin) of pairs p0, p0 + 1 in one 16-byte load per 4 values
+        f32x4_v cs[2][4];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cs[nb][i] = ldf4(crow + (hd0 + nb * 32 + 8 * i + 4 * khalf));
+        const float rstd = __builtin_amdgcn_rsqf(ss[mb] * (1.0f / 128.0f) + b.rope_eps);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float* wp = red + 1024 + hd0 + nb * 32 + 8 * i + 4 * khalf;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const float c = cs[nb][i][2 * t], sn = cs[nb][i][2 * t + 1];
+                    const float u0 = acc[nb][mb][4 * i + 2 * t] * rstd * wp[2 * t];
+                    const float u1 = acc[nb][mb][4 * i + 2 * t + 1] * rstd * wp[2 * t + 1];
+                    acc[nb][mb][4 * i + 2 * t] = u0 * c - u1 * sn;
+                    acc[nb][mb][4 * i + 2 * t + 1] = u0 * sn + u1 * c;
+                }
+            }
+        __builtin_amdgcn_sched_barrier(0);          // one row's table values live at a time
+    }
+}
+
 // Returns -1, or (an owner whose piece jn did not arrive; its running sum is in its carry slot) the
 // index jn of the next workgroup whose piece is still to be merged, with the missing piece's k-steps
 // in [ckb, cke): the driver then runs that continuation as the workgroup's next item.
@@ -499,6 +560,10 @@ __device__ __forceinline__ int gemm_tile(const GemmBatch& b, char* smem, int L, 
             }
         }
     } else {
+        if constexpr (MODE == MODE_STORE) {
+            // fused QK RMSNorm + RoPE on a q or k tile (two whole heads: rope_d is a multiple of 256)
+            if (b.rope_cs && n0 < 2 * b.rope_d) qk_rope_tile(b, pi, smem, acc, m0, n0, M, wm, wn, lane);
+        }
         // Store (and gated residual): the types are dispatched once, outside the row loop, and a
         // row's residual loads are all issued before its first store -- with a type switch or a
         // bounds test around each load, every load was followed by a wait at the branch's join,

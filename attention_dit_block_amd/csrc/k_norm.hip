@@ -499,6 +499,28 @@ static hipError_t launch_rope_w(const QkRopeArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// One thread per (token, pair): the angle in revolutions reduced in double precision, then the
+// hardware cosine and sine -- the arithmetic of qk_norm_rope_kernel's angle phase.
+__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* pos, int n_tok, int n_axes, RopeTable tab,
+                                                         float* cs) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long)n_tok * 64) return;
+    const int tok = (int)(i >> 6), p = (int)(i & 63);
+    const double inv_two_pi = 0.15915494309189533576888376337251;
+    const double rev = (double)pos[(size_t)tok * n_axes + tab.axis[p]] * tab.omega_d[p] * inv_two_pi;
+    const float fr = (float)(rev - rint(rev));
+    *reinterpret_cast<f32x2_v*>(cs + 2 * i) = f32x2_v{__builtin_amdgcn_cosf(fr), __builtin_amdgcn_sinf(fr)};
+}
+
+hipError_t launch_rope_table(const int32_t* pos, int n_tok, int n_axes, const RopeTable& tab, float* cs,
+                             hipStream_t s) {
+    if (n_tok == 0) return hipSuccess;
+    const long threads = (long)n_tok * 64;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, pos, n_tok, n_axes,
+                       tab, cs);
+    return hipGetLastError();
+}
+
 hipError_t launch_qk_rmsnorm_rope(const QkRopeArgs& a, hipStream_t s) {
     if (a.qkv8) {
         if (a.n_heads > 256) return hipErrorInvalidValue;

@@ -80,6 +80,10 @@ struct QkRopeArgs {
     int w_dtype;            // QK-norm weights: F32, BF16 or F16
 };
 hipError_t launch_qk_rmsnorm_rope(const QkRopeArgs& a, hipStream_t s);
+// (cos, sin) of the 64 rotation angles of every token, [n_tok][64][2] fp32, the same values the
+// QK RMSNorm + RoPE pass uses
+hipError_t launch_rope_table(const int32_t* pos, int n_tok, int n_axes, const RopeTable& tab, float* cs,
+                             hipStream_t s);
 
 // ---- grouped GEMM  C = epilogue(A . B^T) -----------------------------------------
 enum Epilogue {
@@ -114,6 +118,13 @@ struct GemmBatch {
     unsigned epoch;
     int sk_spins;       // bound on an owner's wait for a piece (then it computes the piece itself)
     unsigned* range_flag;   // or null: kRangeF16 when an F16 output is out of range
+    // QK RMSNorm + 4-axis RoPE applied to the accumulators of EPI_STORE tiles before they are
+    // stored (MFMA batches, rope_cs non-null): output columns [0, rope_d) of each problem are q,
+    // [rope_d, 2 rope_d) k, 128 per head (rope_d a multiple of 256), normalised with the
+    // problem's bf16 weights rope_w[p] ([2 (q, k)][128]) and rotated by the (cos, sin) pairs of
+    // token rope_row0[p] + row in rope_cs ([n_tok][64 pairs][2], from launch_rope_table).
+    const float* rope_cs; int rope_d; float rope_eps;
+    const void* rope_w[2]; int rope_row0[2];
 };
 // Row strides (lda, ldb) of the 16-bit GEMMs are below this many elements (launch_gemm returns
 // hipErrorInvalidValue otherwise; the entry points reject such strides first).

@@ -107,7 +107,11 @@ def step_work(cfg, shared_mod=False):
         if not shared_mod or blk in (0, cfg.n_double):
             add("adaln_gemv", nbytes=(12 if double else 3) * d * dc * es, bound="hbm")
         add("modulate_x", nbytes=n * d * (ex + es), bound="hbm")
-        add("qk_rmsnorm_rope", nbytes=4.0 * n * d * es + 16.0 * n, bound="hbm")
+        if double and cfg.dtype == "bf16" and d % 256 == 0:
+            # QK RMSNorm + RoPE in the QKV product's epilogue; the angles' (cos, sin) table first
+            add("rope_table", nbytes=n * 64 * 8.0 + 16.0 * n, bound="hbm")
+        else:
+            add("qk_rmsnorm_rope", nbytes=4.0 * n * d * es + 16.0 * n, bound="hbm")
         add("joint_attention", flops=4.0 * n * n * d)
         if double:
             add("gemm_qkv", flops=2.0 * n * d * 3 * d)

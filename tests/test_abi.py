@@ -68,7 +68,9 @@ def test_workspace_size_matches_plan(dit):
     def up(x):
         return (x + 255) // 256 * 256
     # the 4-byte range-flag word (first, 256-byte slot), then the buffers of the block
-    want = up(4) + up(2 * 6 * d * 4) + up(n * d * 2) + up(n * 3 * d * 2) + up(n * d * 2) + up(n * d * 4) + up(n * F * 2)
+    # ... and the (cos, sin) table of the 64 rotation angles per token for the fused QK RMSNorm + RoPE
+    want = (up(4) + up(2 * 6 * d * 4) + up(n * d * 2) + up(n * 3 * d * 2) + up(n * d * 2) + up(n * d * 4) +
+            up(n * F * 2) + up(n * 64 * 2 * 4))
     assert dit.block_workspace_size(s) == want
     want1 = up(4) + up(3 * d * 4) + up(n * d * 2) + up(n * 3 * d * 2) + up(n * (d + F) * 2)
     assert dit.block_workspace_size(s, single_stream=True) == want1

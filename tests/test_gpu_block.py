@@ -12,7 +12,7 @@ import torch
 
 import dit_inputs as di
 from oracle import dit_oracle as o
-from gpu_util import bf16_ulp, dev, host, metric, say, shape_of, upload_stream_weights
+from gpu_util import bf16_ulp, dev, host, metric, say, shape_of, ulp, upload_stream_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -430,3 +430,62 @@ def test_single_block_degenerate_streams(dit, n_txt, grid):
     inp = di.single_block_inputs(cfg, seed=4, qk_norm="random")
     y = run_single(dit, cfg, inp)
     report(cfg, "y", y, o.single_block(cfg, inp)["y"])
+
+
+def test_double_block_fused_qk_rope_teacher_forced(dit):
+    """The QKV product's epilogue applies QK RMSNorm + RoPE when every 256-column tile holds two whole
+    heads (here d = 3072, fp16 activations).  Teacher-forced on the GPU's own modulated activations a
+    (read back from the workspace): the exact product a W_qkv^T, then the oracle's QK RMSNorm + RoPE,
+    against the stored q and k.  The epilogue normalises the fp32 accumulators (exact up to fp32
+    accumulation, ~1e-6 of a head's RMS here), so each value is its fp16 rounding: within 0.6 ulp
+    plus 2e-5 of the RMS.  Sampled rows: the first and last text and image rows and 60 others.
+    a comes from dit_adaln_modulate on each stream (the block's kernels, row by row the same
+    arithmetic; the block's own a buffer is reused later in the block).  Workspace layout:
+    range-flag word (256 bytes), AdaLN vectors [2][6d] fp32, a [n, d], qkv [n, 3d]."""
+    cfg = di.CONFIGS[2]
+    say(f"fused QK RMSNorm + RoPE: {cfg.name}, teacher-forced")
+    inp = di.double_block_inputs(cfg, seed=9, qk_norm="random")
+    n, d, H = cfg.n_tok, cfg.d, cfg.n_heads
+    sh = shape_of(cfg, dit, act_dtype=dit.DIT_F16)
+    ws = torch.empty(dit.block_workspace_size(sh), dtype=torch.uint8, device="cuda")
+    yt = torch.empty(cfg.n_txt, d, dtype=torch.float32, device="cuda")
+    yi = torch.empty(cfg.n_img, d, dtype=torch.float32, device="cuda")
+    wt, wi = upload_stream_weights(inp["txt"], "bf16"), upload_stream_weights(inp["img"], "bf16")
+    dit.block_forward(sh, wt, wi, dev(inp["cond"], "bf16"), dev(inp["pos"], "i32"), dev(inp["x_txt"], "bf16"),
+                      dev(inp["x_img"], "bf16"), yt, yi, ws)
+    torch.cuda.synchronize()
+
+    def up(x):
+        return (x + 255) // 256 * 256
+    off_qkv = 256 + up(12 * d * 4) + up(n * d * 2)
+    rows = np.unique(np.concatenate([[0, cfg.n_txt - 1, cfg.n_txt, n - 1],
+                                     np.random.default_rng(5).choice(n, 60, replace=False)]))
+    wsh = ws.cpu().numpy()
+    a_all = np.empty((n, d))
+    for s, r0, r1 in (("txt", 0, cfg.n_txt), ("img", cfg.n_txt, n)):
+        mod = torch.empty(6 * d, dtype=torch.float32, device="cuda")
+        xo = torch.empty(r1 - r0, d, dtype=torch.float16, device="cuda")
+        dit.adaln_modulate(dev(inp["cond"], "bf16"), dev(inp[s]["w_mod"], "bf16"), 6, d, mod,
+                           x=dev(inp["x_" + s], "bf16"), x_out=xo, shift_chunk=0, scale_chunk=1, eps=cfg.eps)
+        torch.cuda.synchronize()
+        a_all[r0:r1] = xo.cpu().numpy().astype(np.float64)
+    a = a_all[rows]
+    qk = wsh[off_qkv:off_qkv + n * 3 * d * 2].view(np.float16).reshape(n, 3 * d)[rows, :2 * d].astype(np.float64)
+    ref = np.empty((len(rows), 2 * d))
+    qk_w = np.stack([o.widen(inp["txt"]["qk_norm_w"], "bf16").reshape(2, 128),
+                     o.widen(inp["img"]["qk_norm_w"], "bf16").reshape(2, 128)])
+    for s, sel in (("txt", rows < cfg.n_txt), ("img", rows >= cfg.n_txt)):
+        if not sel.any():
+            continue
+        w = o.widen(inp[s]["w_qkv"], "bf16")[:2 * d]            # q and k rows of W_qkv
+        prod = a[sel] @ w.T
+        set_w = qk_w[0] if s == "txt" else qk_w[1]
+        q, k = o.qk_rmsnorm_rope(prod[:, :d], prod[:, d:], H, 128, np.stack([set_w, set_w]), len(rows), cfg.eps_qk,
+                                 inp["pos"][rows[sel]], cfg.axes_dim, cfg.theta)
+        ref[sel] = np.concatenate([q, k], axis=1)
+    rms = np.sqrt(np.mean(ref ** 2))
+    err = np.abs(qk - ref)
+    bound = 0.6 * ulp(ref, "f16") + 2e-5 * rms
+    say(f"  q, k: {len(rows)} rows x {2 * d}: max err / bound {np.max(err / bound):.3f}, "
+        f"max|gpu - ref|/RMS {metric(qk, ref):.2e}")
+    assert np.all(err <= bound), f"{np.sum(err > bound)} values beyond the bound"
