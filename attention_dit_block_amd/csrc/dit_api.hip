@@ -444,6 +444,14 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
     if (nt) m.p[nm++] = {x_txt, d, c.x_dtype, act, d, mod_t + 0 * d, mod_t + 1 * (size_t)d, nt};
     if (ni) m.p[nm++] = {x_img, d, c.x_dtype, act + (size_t)nt * d * es, d, mod_i + 0 * d, mod_i + 1 * (size_t)d, ni};
     m.n = nm; m.d = d; m.eps = c.eps; m.out_dtype = c.act_dtype; m.range_flag = flag;
+    // 16-bit path with whole heads per 256-column tile: QK RMSNorm + RoPE in the QKV product's
+    // epilogue, from a table of the angles' (cos, sin) that this modulation writes as well
+    const bool fuse_rope = !fp8 && W.cs_bytes > 0;
+    float* rope_cs = fuse_rope ? reinterpret_cast<float*>(ws + W.cs) : nullptr;
+    if (fuse_rope) {
+        DIT_TRY(build_rope_table(c.head_dim, c.n_axes, c.axes_dim, c.theta, m.rope_tab));
+        m.rope_cs = rope_cs; m.rope_pos = pos; m.rope_n = n; m.rope_n_axes = c.n_axes;
+    }
     // fp8 products: a goes straight to e4m3 codes with per-row scales
     uint8_t* q8 = fp8 ? reinterpret_cast<uint8_t*>(ws + W.q8) : nullptr;
     float* sq = fp8 ? reinterpret_cast<float*>(ws + W.sq) : nullptr;
@@ -484,9 +492,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
         return P;
     };
 
-    // 3. qkv = a W_qkv^T; in the 16-bit path with whole heads per tile, QK RMSNorm + RoPE in its
-    //    epilogue, from a table of the angles' (cos, sin) computed first
-    const bool fuse_rope = !fp8 && W.cs_bytes > 0;
+    // 3. qkv = a W_qkv^T (with QK RMSNorm + RoPE in its epilogue when fuse_rope)
     if (fp8) {
         Fp8GemmBatch b{};
         if (nt) b.p[b.n++] = fp8_problem(0, nt, d, t8->w_qkv, t8->s_qkv, qkv, 3L * d, c.act_dtype, 3 * d, EPI_STORE);
@@ -509,11 +515,7 @@ static int block_forward_impl(const dit_block_config* cfg, const dit_stream_weig
         gq.n = k;
     }
     if (fuse_rope) {
-        float* cs = reinterpret_cast<float*>(ws + W.cs);
-        RopeTable tab;
-        DIT_TRY(build_rope_table(c.head_dim, c.n_axes, c.axes_dim, c.theta, tab));
-        DIT_TRY(launch("rope_table", s, [&] { return launch_rope_table(pos, n, c.n_axes, tab, cs, s); }));
-        gq.rope_cs = cs; gq.rope_d = d; gq.rope_eps = c.eps_qk;
+        gq.rope_cs = rope_cs; gq.rope_d = d; gq.rope_eps = c.eps_qk;
         int k = 0;
         if (nt) { gq.rope_w[k] = qkw_t; gq.rope_row0[k++] = 0; }
         if (ni) { gq.rope_w[k] = qkw_i; gq.rope_row0[k++] = nt; }

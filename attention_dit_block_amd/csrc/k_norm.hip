@@ -160,6 +160,17 @@ hipError_t launch_adaln_gemv(const GemvBatch& b, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Entry i = token * 64 + pair of the rotation-angle table: the angle in revolutions reduced in double
+// precision, then the hardware cosine and sine (the QK RMSNorm + RoPE pass's angle arithmetic).
+__device__ __forceinline__ void rope_table_entry(const int32_t* pos, int n_axes, const RopeTable& tab, float* cs,
+                                                 long i) {
+    const int tok = (int)(i >> 6), p = (int)(i & 63);
+    const double inv_two_pi = 0.15915494309189533576888376337251;
+    const double rev = (double)pos[(size_t)tok * n_axes + tab.axis[p]] * tab.omega_d[p] * inv_two_pi;
+    const float fr = (float)(rev - rint(rev));
+    *reinterpret_cast<f32x2_v*>(cs + 2 * i) = f32x2_v{__builtin_amdgcn_cosf(fr), __builtin_amdgcn_sinf(fr)};
+}
+
 // ------------------------------------------------------------------------------------------
 // Modulate: out = (1 + scale) * x * rstd + shift with rstd = 1/sqrt(mean(x^2) + eps).
 // One wave per row, four rows per workgroup, the row kept in registers between the reduction and
@@ -174,6 +185,12 @@ __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (b.clear && blockIdx.x == 0)
         for (int i = threadIdx.x; i < b.clear_n; i += 256) b.clear[i] = 0u;
+    if (b.rope_cs) {
+        // the QKV product's rotation table, one entry per thread (its own launch cost as much as
+        // computing it here)
+        const long i = (long)blockIdx.x * 256 + threadIdx.x;
+        if (i < (long)b.rope_n * 64) rope_table_entry(b.rope_pos, b.rope_n_axes, b.rope_tab, b.rope_cs, i);
+    }
     const int nb0 = (b.p[0].rows + 3) / 4;         // workgroups of problem 0
     const int pi = (b.n > 1 && (int)blockIdx.x >= nb0) ? 1 : 0;
     const ModProblem& P = b.p[pi];
@@ -496,28 +513,6 @@ static hipError_t launch_rope_w(const QkRopeArgs& a, hipStream_t s) {
     if (a.w_dtype == F16) hipLaunchKernelGGL((qk_norm_rope_kernel<DT, F16>), grid, block, 0, s, a);
     else if (a.w_dtype == BF16) hipLaunchKernelGGL((qk_norm_rope_kernel<DT, BF16>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((qk_norm_rope_kernel<DT, F32>), grid, block, 0, s, a);
-    return hipGetLastError();
-}
-
-// One thread per (token, pair): the angle in revolutions reduced in double precision, then the
-// hardware cosine and sine -- the arithmetic of qk_norm_rope_kernel's angle phase.
-__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* pos, int n_tok, int n_axes, RopeTable tab,
-                                                         float* cs) {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (long)n_tok * 64) return;
-    const int tok = (int)(i >> 6), p = (int)(i & 63);
-    const double inv_two_pi = 0.15915494309189533576888376337251;
-    const double rev = (double)pos[(size_t)tok * n_axes + tab.axis[p]] * tab.omega_d[p] * inv_two_pi;
-    const float fr = (float)(rev - rint(rev));
-    *reinterpret_cast<f32x2_v*>(cs + 2 * i) = f32x2_v{__builtin_amdgcn_cosf(fr), __builtin_amdgcn_sinf(fr)};
-}
-
-hipError_t launch_rope_table(const int32_t* pos, int n_tok, int n_axes, const RopeTable& tab, float* cs,
-                             hipStream_t s) {
-    if (n_tok == 0) return hipSuccess;
-    const long threads = (long)n_tok * 64;
-    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, pos, n_tok, n_axes,
-                       tab, cs);
     return hipGetLastError();
 }
 

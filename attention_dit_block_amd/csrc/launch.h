@@ -40,6 +40,10 @@ struct ModProblem {
     int rows;
     float* out_scale;                         // FP8_ROWS: [rows] per-row scales
 };
+struct RopeTable {
+    double omega_d[64];     // frequency of pair p
+    int8_t axis[64];        // position axis of pair p
+};
 struct ModBatch {
     ModProblem p[2];
     int n;
@@ -49,14 +53,16 @@ struct ModBatch {
                         // row as launch_quantize_fp8 does, from the fp32 results
     unsigned* range_flag;   // or null: kRangeF16 when an F16 output is out of range
     unsigned* clear; int clear_n;   // or null: words the kernel sets to 0 (a later kernel's maxima)
+    // or null: the kernel also writes the (cos, sin) table of the 64 rotation angles of rope_n
+    // tokens, [rope_n][64][2] fp32, with the QK RMSNorm + RoPE pass's angle arithmetic (one angle
+    // per thread of the grid, which has at least 64 threads per modulated row; rope_n must not
+    // exceed the rows)
+    float* rope_cs; const int32_t* rope_pos; int rope_n, rope_n_axes;
+    RopeTable rope_tab;
 };
 hipError_t launch_modulate(const ModBatch& b, hipStream_t s);
 
 // ---- QK RMSNorm + RoPE, in place -----------------------------------------------
-struct RopeTable {
-    double omega_d[64];     // frequency of pair p
-    int8_t axis[64];        // position axis of pair p
-};
 struct QkRopeArgs {
     void* q; long ld_q;
     void* k; long ld_k;
@@ -80,10 +86,6 @@ struct QkRopeArgs {
     int w_dtype;            // QK-norm weights: F32, BF16 or F16
 };
 hipError_t launch_qk_rmsnorm_rope(const QkRopeArgs& a, hipStream_t s);
-// (cos, sin) of the 64 rotation angles of every token, [n_tok][64][2] fp32, the same values the
-// QK RMSNorm + RoPE pass uses
-hipError_t launch_rope_table(const int32_t* pos, int n_tok, int n_axes, const RopeTable& tab, float* cs,
-                             hipStream_t s);
 
 // ---- grouped GEMM  C = epilogue(A . B^T) -----------------------------------------
 enum Epilogue {
@@ -122,7 +124,7 @@ struct GemmBatch {
     // stored (MFMA batches, rope_cs non-null): output columns [0, rope_d) of each problem are q,
     // [rope_d, 2 rope_d) k, 128 per head (rope_d a multiple of 256), normalised with the
     // problem's bf16 weights rope_w[p] ([2 (q, k)][128]) and rotated by the (cos, sin) pairs of
-    // token rope_row0[p] + row in rope_cs ([n_tok][64 pairs][2], from launch_rope_table).
+    // token rope_row0[p] + row in rope_cs ([n_tok][64 pairs][2], written by the modulation).
     const float* rope_cs; int rope_d; float rope_eps;
     const void* rope_w[2]; int rope_row0[2];
 };

@@ -106,11 +106,12 @@ def step_work(cfg, shared_mod=False):
         ex = es if blk == 0 else 4                   # block input: workload type, then fp32 stream
         if not shared_mod or blk in (0, cfg.n_double):
             add("adaln_gemv", nbytes=(12 if double else 3) * d * dc * es, bound="hbm")
-        add("modulate_x", nbytes=n * d * (ex + es), bound="hbm")
         if double and cfg.dtype == "bf16" and d % 256 == 0:
-            # QK RMSNorm + RoPE in the QKV product's epilogue; the angles' (cos, sin) table first
-            add("rope_table", nbytes=n * 64 * 8.0 + 16.0 * n, bound="hbm")
+            # QK RMSNorm + RoPE in the QKV product's epilogue, from a table of the angles' (cos, sin)
+            # that the modulation writes as well (positions read, 64 pairs of fp32 written per token)
+            add("modulate_x", nbytes=n * d * (ex + es) + n * 64 * 8.0 + 16.0 * n, bound="hbm")
         else:
+            add("modulate_x", nbytes=n * d * (ex + es), bound="hbm")
             add("qk_rmsnorm_rope", nbytes=4.0 * n * d * es + 16.0 * n, bound="hbm")
         add("joint_attention", flops=4.0 * n * n * d)
         if double:

@@ -37,8 +37,8 @@ def test_step_launch_counts_and_bounds():
     blocks = cfg.n_double + cfg.n_single
     for name in ("modulate_x", "joint_attention", "adaln_gemv"):
         assert work[name][3] == blocks
-    # double blocks: QK RMSNorm + RoPE in the QKV product's epilogue after a table of the angles
-    assert work["rope_table"][3] == cfg.n_double
+    # double blocks: QK RMSNorm + RoPE in the QKV product's epilogue (the angle table comes with the
+    # modulation), single blocks: the separate pass
     assert work["qk_rmsnorm_rope"][3] == cfg.n_single
     for name in ("gemm_qkv", "gemm_out_proj", "modulate_h", "gemm_ffn_in_swiglu", "gemm_ffn_down"):
         assert work[name][3] == cfg.n_double

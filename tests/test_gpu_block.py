@@ -44,7 +44,9 @@ def run_double(dit, cfg, inp, x_dtype="same", y_dtype="f32", act=None, f16w=Fals
     dit.block_forward(sh, wt, wi, dev(inp["cond"], t), dev(inp["pos"], "i32"), dev(inp["x_txt"], xdt),
                       dev(inp["x_img"], xdt), yt, yi, ws)
     torch.cuda.synchronize()
-    assert dit.launch_count() == before + 9
+    # 9 launches, 8 when QK RMSNorm + RoPE runs in the QKV product's epilogue (bf16 model, d a
+    # multiple of 256)
+    assert dit.launch_count() == before + (8 if t == "bf16" and cfg.d % 256 == 0 else 9)
     assert dit.workspace_flags(ws) == 0, "an fp16 activation left fp16's range"
     return host(yt), host(yi)
 
