@@ -197,7 +197,10 @@ size_t dit_block_workspace_size(const dit_block_config* cfg, int single_stream);
  *   b_s = (1+scale2) RMSNorm(h_s) + shift2;  [g|u] = b_s W_in,s^T
  *   y_s = h_s + gate2 ((SiLU(g) * u) W_down,s^T)
  * Storage: the AdaLN vectors and h are fp32; a, qkv, O, b and f are
- * act_dtype; x is x_dtype and y is y_dtype.
+ * act_dtype; x is x_dtype and y is y_dtype.  With bf16 weights and d a
+ * multiple of 256 the QK RMSNorm + RoPE is applied to the q and k products'
+ * fp32 values before they are stored (otherwise to the stored act_dtype
+ * values, by a pass of its own).
  *
  *  cfg, txt, img (host)
  *  cond      [d_cond] of dtype (shared by both streams)
@@ -258,8 +261,9 @@ size_t dit_step_workspace_size(const dit_block_config* cfg, int n_double, int n_
  *  workspace >= dit_step_workspace_size(cfg, n_double, n_single) bytes, as for
  *            the blocks.
  * All arguments of all blocks are validated before the first launch; an error
- * launches nothing.  9 launches per double-stream block, 6 per single-stream
- * block.
+ * launches nothing.  9 launches per double-stream block (8 when its QK RMSNorm
+ * + RoPE runs in the QKV product's epilogue: bf16 weights, d a multiple of
+ * 256), 6 per single-stream block.
  */
 int dit_step_forward(const dit_block_config* cfg, int n_double,
                      const dit_stream_weights* txt, const dit_stream_weights* img,
@@ -284,7 +288,8 @@ size_t dit_step_shared_mod_workspace_size(const dit_block_config* cfg, int n_dou
  *  w_mod_single          [3d, d_cond] of dtype (needed when n_single > 0)
  *  workspace >= dit_step_shared_mod_workspace_size(cfg, n_double, n_single)
  * Other arguments and guarantees as for dit_step_forward; 8 launches per
- * double-stream block and 5 per single-stream block, plus 1 per block kind.
+ * double-stream block (7 with the QK RMSNorm + RoPE in the QKV product) and 5
+ * per single-stream block, plus 1 per block kind.
  * With every block's w_mod equal to the shared matrix the result is
  * bit-identical to dit_step_forward's.
  */
