@@ -3,6 +3,8 @@
 // (QKV projections, FFN; the "CUDA codepath !" thread, antirez/iris.c issue #15), with the
 // per-block elementwise work fused into the epilogue:
 //   EPI_STORE     C = acc                                   (QKV)
+//                 with QK RMSNorm + RoPE applied to the q and k columns first when the batch
+//                 carries an angle table (the block's QKV product, whole heads per tile)
 //   EPI_GATED_RES C = R + gate[col] * acc                   (out-proj, FFN-down: gated residual)
 //   EPI_SWIGLU    C = SiLU(acc_gate) * acc_up               (FFN-in)
 // One launch covers several problems (text and image streams, or the two halves of the

@@ -176,8 +176,10 @@ __device__ __forceinline__ void rope_table_entry(const int32_t* pos, int n_axes,
 // One wave per row, four rows per workgroup, the row kept in registers between the reduction and
 // the write.  Workgroups are laid out per problem (text rows, then image rows), and each stages
 // its problem's shift and scale vectors in LDS once for its four rows: read per row from L2 they
-// would be twice the row's own HBM bytes, and kept in registers they would cap occupancy.
-// Bound: HBM bytes  rows * d * (sizeof(x) + sizeof(out)).
+// would be twice the row's own HBM bytes, and kept in registers they would cap occupancy.  On
+// request the grid also writes the RoPE angle table of the QKV product's fused QK RMSNorm + RoPE,
+// one entry per thread.
+// Bound: HBM bytes  rows * d * (sizeof(x) + sizeof(out)) (+ 512 per row with the table).
 // ------------------------------------------------------------------------------------------
 template <int XT, int OT, int NC>
 __global__ __launch_bounds__(256) void modulate_kernel(ModBatch b) {
