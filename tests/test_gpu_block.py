@@ -434,7 +434,8 @@ def test_single_block_degenerate_streams(dit, n_txt, grid):
     report(cfg, "y", y, o.single_block(cfg, inp)["y"])
 
 
-def test_double_block_fused_qk_rope_teacher_forced(dit):
+@pytest.mark.parametrize("f16w", [False, True], ids=["bf16_weights", "f16_weight_copies"])
+def test_double_block_fused_qk_rope_teacher_forced(dit, f16w):
     """The QKV product's epilogue applies QK RMSNorm + RoPE when every 256-column tile holds two whole
     heads (here d = 3072, fp16 activations).  Teacher-forced on the GPU's own modulated activations a
     (read back from the workspace): the exact product a W_qkv^T, then the oracle's QK RMSNorm + RoPE,
@@ -445,14 +446,16 @@ def test_double_block_fused_qk_rope_teacher_forced(dit):
     arithmetic; the block's own a buffer is reused later in the block).  Workspace layout:
     range-flag word (256 bytes), AdaLN vectors [2][6d] fp32, a [n, d], qkv [n, 3d]."""
     cfg = di.CONFIGS[2]
-    say(f"fused QK RMSNorm + RoPE: {cfg.name}, teacher-forced")
+    say(f"fused QK RMSNorm + RoPE: {cfg.name}, teacher-forced, f16w={f16w}")
     inp = di.double_block_inputs(cfg, seed=9, qk_norm="random")
     n, d, H = cfg.n_tok, cfg.d, cfg.n_heads
     sh = shape_of(cfg, dit, act_dtype=dit.DIT_F16)
+    if f16w:                                   # the bench's format: fp16 copies of the product weights
+        sh.gemm_w_dtype = dit.DIT_F16
     ws = torch.empty(dit.block_workspace_size(sh), dtype=torch.uint8, device="cuda")
     yt = torch.empty(cfg.n_txt, d, dtype=torch.float32, device="cuda")
     yi = torch.empty(cfg.n_img, d, dtype=torch.float32, device="cuda")
-    wt, wi = upload_stream_weights(inp["txt"], "bf16"), upload_stream_weights(inp["img"], "bf16")
+    wt, wi = upload_stream_weights(inp["txt"], "bf16", f16w), upload_stream_weights(inp["img"], "bf16", f16w)
     dit.block_forward(sh, wt, wi, dev(inp["cond"], "bf16"), dev(inp["pos"], "i32"), dev(inp["x_txt"], "bf16"),
                       dev(inp["x_img"], "bf16"), yt, yi, ws)
     torch.cuda.synchronize()
